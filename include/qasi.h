@@ -1,0 +1,185 @@
+/*
+ * qasi -- query-aware sparse index for MI355X (gfx950).
+ *
+ * C ABI of the decode-step hot path shared by TokenSelect and TokenButler (query-aware
+ * token-level KV selection followed by sparse attention over the selected tokens, for one
+ * attention layer) and of SnapKV prefill-end compression.
+ *
+ * Sources (cited by page title and section):
+ *   [TS] "論文解説: TokenSelect — 動的トークンレベルKVキャッシュ選択による長文推論の高速化"
+ *   [TB] "Technische Zusammenfassung: TokenButler"
+ *   [SK] "NeurIPS 2024論文解説: SnapKV — 生成前にKVキャッシュの重要トークンを選択する手法"
+ *
+ * Common conventions
+ *   - d = 128 (head dimension) and d' = 32 (index dimension) are fixed; Hkv must be 1, 2,
+ *     4 or 8 and G = Hq / Hkv an integer in 1..8 (query head h reads KV head h / G).
+ *   - bf16 tensors are passed as uint16_t bit patterns.  All device pointers must be
+ *     16-byte aligned.
+ *   - Caches are token-major and packed over a ragged batch: K[t][g][128], V[t][g][128],
+ *     K_index[t][g][32], where sequence b owns rows [offsets[b], offsets[b+1]).  Functions
+ *     that size launches take the same offsets twice: `offsets_dev` (device, read by the
+ *     kernels) and `offsets_host` (host, read synchronously to size grids; no device sync).
+ *   - Token positions inside index lists are sequence-local (0 .. n_b - 1).
+ *   - The caller owns every buffer.  Nothing is allocated or freed by any call; scratch
+ *     comes from a caller workspace sized by the *_workspace_bytes queries.  No pointer is
+ *     kept after the enqueued work completes.  All work is enqueued asynchronously on the
+ *     caller's stream; calls on different streams with different workspaces are independent.
+ *   - Return codes: 0 success; QASI_ERR_INVALID (null or misaligned pointer, bad count,
+ *     non-monotone offsets, out-of-range parameters); QASI_ERR_UNSUPPORTED (shape outside
+ *     the supported set); QASI_ERR_WORKSPACE (workspace too small); QASI_ERR_HIP (a launch
+ *     failed).  Validation is synchronous and happens before any HIP call, so a non-zero
+ *     return other than QASI_ERR_HIP enqueues nothing.  Device faults are asynchronous and
+ *     surface at the caller's next synchronisation.  ts_last_error() returns a
+ *     thread-local message for the last failing call.  Inputs are assumed finite.
+ */
+#ifndef QASI_H
+#define QASI_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QASI_OK 0
+#define QASI_ERR_INVALID (-1)
+#define QASI_ERR_UNSUPPORTED (-2)
+#define QASI_ERR_WORKSPACE (-3)
+#define QASI_ERR_HIP (-4)
+
+#define QASI_MODE_VOTE 0
+#define QASI_MODE_PER_HEAD 1
+
+/* Selection parameters ([TS] "基本的な統合パターン", TokenSelectConfig).
+ *   budget = budget_num / budget_den of the n_b cached tokens; the list length is
+ *            K_b = min(n_b, max(floor(n_b * budget), sink + local)) ([TS] same listing).
+ *   sink, local: the first `sink` and last `local` tokens are always selected
+ *            ([TS] "Token-Level Selection と Sparse Attention", always-included table).
+ *   v_min:   vote mode only; tokens with Vote < v_min rank below every candidate but
+ *            remain fillable ([TS] "Voting Mechanism").
+ *   theta_num / theta_den: vote mode only; the head threshold is the nearest-rank order
+ *            statistic s_(r), r = ceil(n_b * theta_num / theta_den) (9/10: 90th
+ *            percentile; 1/2: the median of the page's listing).                       */
+typedef struct {
+    int32_t mode;          /* QASI_MODE_VOTE or QASI_MODE_PER_HEAD */
+    int32_t reserved;
+    int64_t budget_num, budget_den;
+    int64_t sink, local;
+    int64_t v_min;
+    int64_t theta_num, theta_den;
+} ts_select_params;
+
+/* Thread-local description of the last error (never NULL). */
+const char* ts_last_error(void);
+
+/* K_b for one sequence of n tokens under `p` (host-only helper; -1 if p is invalid). */
+int64_t ts_budget_tokens(int64_t n, const ts_select_params* p);
+
+/* Append T tokens to the compressed key index ([TS] "Query-Key Dot Product Index": the
+ * d' = d/4 index is built incrementally during inference; [TB] "Kernarchitektur": keys are
+ * projected by a fixed matrix into the low-dimensional space):
+ *   k_index[pos + t][g][c] = bf16_rne( sum_j k_new[t][g][j] * P[j][c] )
+ * with the sum formed in fp64 and rounded once to bf16 (nearest-even).
+ *   k_new   device bf16 [T][Hkv][128]
+ *   P       device fp32 [128][32] (one projection shared by all KV heads)
+ *   k_index device bf16 [>= pos + T][Hkv][32]; rows pos .. pos+T-1 are written.
+ * T = 1 per decode step; T = n rebuilds the index of a whole cache.                   */
+int ts_index_append(const uint16_t* k_new, const float* P, uint16_t* k_index, int64_t pos,
+                    int64_t T, int32_t Hkv, hipStream_t stream);
+
+/* Index scores for every query head and cached token ([TS] "Query-Key Dot Product
+ * Index", eq. Score_h(i) = q_h . k_index,h(i) / sqrt(d')):  q'_h = P^T q_h (fp32) and
+ *   scores[h][t] = (q'_h / sqrt(32)) . k_index[t][h / G]    (fp32, t packed over the batch)
+ *   q       device bf16 [B][Hq][128] (one decode query per sequence)
+ *   k_index device bf16 [Ntot][Hkv][32]
+ *   scores  device fp32 [Hq][Ntot], Ntot = offsets[B].                                */
+int ts_score(const uint16_t* q, const float* P, const uint16_t* k_index,
+             const int64_t* offsets_dev, const int64_t* offsets_host, int32_t B, int32_t Hq,
+             int32_t Hkv, float* scores, hipStream_t stream);
+
+/* Workspace for ts_select. */
+size_t ts_select_workspace_bytes(const int64_t* offsets_host, int32_t B, int32_t Hq,
+                                 const ts_select_params* p);
+
+/* Token selection per sequence.
+ * Vote mode ([TS] "Voting Mechanism" and "Token-Level Selection", with the listing of
+ * "基本的な統合パターン"): theta_h = s_(r) per (sequence, head); Vote(t) = #{h : scores[h][t]
+ * > theta_h} (strict); key(t) = Vote(t) if Vote(t) >= v_min else -1; the list is the forced
+ * tokens F = [0, sink) U [n_b - local, n_b) plus the K_b - |F| non-forced tokens of highest
+ * key, ties to the lower position, in ascending order:  idx_out[kpre_b + j], j < K_b, with
+ * kpre_b = sum_{b' < b} K_b'.
+ * Per-head mode ([TS] "主要な貢献" per-head selection, the "w/o Voting" ablation; [TB]
+ * "Kernarchitektur"): the same rule per query head with key = scores[h][t]; -0 and +0 tie:
+ * idx_out[Hq * kpre_b + h * K_b + j].
+ *   scores     device fp32 [Hq][Ntot] (as written by ts_score)
+ *   idx_out    device int32 (layout above)
+ *   count_out  device int64 [B] (receives K_b)
+ *   theta_out  nullable device fp32 [B][Hq] (vote mode: theta_h)
+ *   votes_out  nullable device uint8 [Ntot] (vote mode: Vote(t))
+ *   ws         device workspace of at least ts_select_workspace_bytes(...) bytes.     */
+int ts_select(const float* scores, const int64_t* offsets_dev, const int64_t* offsets_host,
+              int32_t B, int32_t Hq, int32_t Hkv, const ts_select_params* p, int32_t* idx_out,
+              int64_t* count_out, float* theta_out, uint8_t* votes_out, void* ws,
+              size_t ws_bytes, hipStream_t stream);
+
+/* Workspace for ts_sparse_decode (counts_host = the per-sequence list lengths) and for
+ * ts_dense_decode (counts_host = NULL). */
+size_t ts_decode_workspace_bytes(const int64_t* offsets_host, const int64_t* counts_host,
+                                 int32_t B, int32_t Hq, int32_t Hkv, int32_t mode);
+
+/* Sparse decode attention over the selected tokens ([TS] eq. Attention(Q, K_S, V_S) =
+ * softmax(Q K_S^T / sqrt(d)) V_S; the lists already hold the sink and local tokens, so the
+ * page's "output merge" of sparse and local attention is one softmax over their union):
+ *   out[b][h][:] = sum_{t in S} softmax_t(q[b][h] . K[t][h/G] / sqrt(128)) V[t][h/G]
+ * computed as a gathered split-K flash decode (fp32 accumulation) with a log-sum-exp
+ * merge of the partial results.
+ *   q           device bf16 [B][Hq][128]
+ *   K, V        device bf16 [Ntot][Hkv][128]
+ *   idx         device int32 lists in the ts_select layout for `mode`; positions must be
+ *               < n_b (unchecked on the device: out-of-range entries are a caller error)
+ *   counts_host host int64 [B]: list length per sequence (0 < count_b <= n_b)
+ *   out         device fp32 [B][Hq][128].                                             */
+int ts_sparse_decode(const uint16_t* q, const uint16_t* K, const uint16_t* V,
+                     const int64_t* offsets_dev, const int64_t* offsets_host, const int32_t* idx,
+                     const int64_t* counts_host, int32_t mode, int32_t B, int32_t Hq,
+                     int32_t Hkv, float* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Dense decode attention over all n_b tokens of each sequence (the comparison baseline,
+ * [TS] eq. S_i = q . k_i / sqrt(d) for every cached token).  Same layouts as above.   */
+int ts_dense_decode(const uint16_t* q, const uint16_t* K, const uint16_t* V,
+                    const int64_t* offsets_dev, const int64_t* offsets_host, int32_t B,
+                    int32_t Hq, int32_t Hkv, float* out, void* ws, size_t ws_bytes,
+                    hipStream_t stream);
+
+/* Workspace for snapkv_compress. */
+size_t snapkv_workspace_bytes(int64_t n, int32_t w, int32_t Hq, int32_t Hkv, int64_t c);
+
+/* SnapKV prefill-end compression of one sequence ([SK] "Attention Score計算とPooling",
+ * "Top-k SelectionとCluster-based Retention" and the listing of "アルゴリズム"):
+ *   for each KV head g, rows r = (query head h of group g, window position t):
+ *     A_r = softmax_j(q_obs[t][h] . K[j][g] / sqrt(128)) over all n keys (no mask),
+ *     imp[g][j] = mean over the G*w rows of A_r[j]   (the page's inter-head average),
+ *     pooled[g][j] = (imp[g][j-1] + imp[g][j] + imp[g][j+1]) / 3 (zero padding, kernel 3),
+ *     idx_out[g][:] = the ce = min(c, n) positions of largest pooled value, ties to the
+ *                     lower position, ascending;
+ *     K_out[s][g][:] = K[idx_out[g][s]][g][:], V_out likewise (bit copies).
+ * QK^T runs on bf16 MFMA with fp32 accumulation; softmax statistics are fp32.
+ *   q_obs          device bf16 [w][Hq][128] (the last w prompt queries)
+ *   K, V           device bf16 [n][Hkv][128]
+ *   pool_kernel    must be 3 (odd kernels keep the length; only 3 is built)
+ *   idx_out        device int32 [Hkv][ce]
+ *   K_out, V_out   device bf16 [ce][Hkv][128]
+ *   importance_out nullable device fp32 [Hkv][n] (imp)
+ *   pooled_out     nullable device fp32 [Hkv][n] (pooled)                             */
+int snapkv_compress(const uint16_t* q_obs, const uint16_t* K, const uint16_t* V, int64_t n,
+                    int32_t w, int32_t Hq, int32_t Hkv, int64_t c, int32_t pool_kernel,
+                    int32_t* idx_out, uint16_t* K_out, uint16_t* V_out, float* importance_out,
+                    float* pooled_out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QASI_H */

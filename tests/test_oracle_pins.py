@@ -1,0 +1,457 @@
+"""Pins of the fp64 CPU oracle against what the pages and mathematics fix.
+
+Each test checks the oracle against something other than itself: a closed form, a
+special case that reduces to a textbook or library routine (NumPy / torch-CPU fp64), an
+invariant, exact rational arithmetic, or a brute-force recount on tiny inputs.  Together
+they are chosen so that a dropped term, a wrong sign or index, a transposed operand or a
+wrong tie-break in the oracle fails at least one of them.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from query_aware_sparse_index_amd import synth
+
+D, DP = 128, 32
+
+
+def bf(x):
+    return synth.f32_to_bf16_bits(np.asarray(x, np.float32))
+
+
+def unbf(b):
+    a = np.asarray(b, np.uint16)
+    return synth.bf16_bits_to_f32(a.reshape(-1)).astype(np.float64).reshape(a.shape)
+
+
+# --------------------------------------------------------------- bf16 rounding
+
+def _nearest_bf16_exact(x: float) -> float:
+    """Brute force with exact rationals: the nearest finite bf16 value, ties to the even
+    significand (the oracle must agree on every sampled double)."""
+    if x == 0.0:
+        return x
+    fx = Fraction(x)
+    a = abs(fx)
+    e = 0
+    while a >= 2:
+        a /= 2
+        e += 1
+    while a < 1:
+        a *= 2
+        e -= 1
+    q = max(e - 7, -133)
+    quantum = Fraction(2) ** q
+    lo = (abs(fx) // quantum) * quantum
+    hi = lo + quantum
+    dlo, dhi = abs(fx) - lo, hi - abs(fx)
+    if dlo < dhi:
+        r = lo
+    elif dhi < dlo:
+        r = hi
+    else:
+        r = lo if (lo / quantum) % 2 == 0 else hi
+    return float(r if fx > 0 else -r)
+
+
+def test_bf16_round_ties_and_edges():
+    # textbook ties: 1 + 2^-8 is halfway between 1 and 1 + 2^-7 -> even (1.0)
+    assert O.bf16_round(1.0 + 2.0 ** -8) == 0x3F80
+    assert O.bf16_round(1.0 + 3 * 2.0 ** -8) == 0x3F82
+    assert O.bf16_round(-(1.0 + 2.0 ** -8)) == 0xBF80
+    assert O.bf16_round(1.0 + 2.0 ** -8 + 2.0 ** -40) == 0x3F81  # just above the tie
+    # subnormal quantum 2^-133: 1.5 quanta ties to 2 quanta, 0.5 quanta ties to 0
+    assert O.bf16_round(1.5 * 2.0 ** -133) == 0x0002
+    assert O.bf16_round(0.5 * 2.0 ** -133) == 0x0000
+    assert O.bf16_round(2.0 ** -126) == 0x0080
+    # overflow to infinity; largest finite survives
+    assert O.bf16_round(3.5e38) == 0x7F80
+    assert O.bf16_round(float(np.float32(unbf(np.uint16(0x7F7F))))) == 0x7F7F
+    assert O.bf16_round(-0.0) == 0x8000 and O.bf16_round(0.0) == 0
+
+
+def test_bf16_round_matches_exact_rationals():
+    rng = np.random.default_rng(11)
+    xs = np.concatenate([rng.standard_normal(300) * 10.0 ** rng.integers(-6, 6, 300),
+                         rng.standard_normal(50) * 2.0 ** -128])
+    for x in xs:
+        want = _nearest_bf16_exact(float(x))
+        got = unbf(np.uint16(O.bf16_round(float(x))))
+        assert got == want, (x, got, want)
+
+
+def test_bf16_round_roundtrip_and_fp32_route():
+    rng = np.random.default_rng(5)
+    bits = rng.integers(0, 0x7F80, 2000).astype(np.uint16)
+    for b in bits[:400]:
+        assert O.bf16_round(float(unbf(b))) == int(b)
+    # for fp32-representable inputs one rounding fp32 -> bf16 is exact RNE: NumPy route
+    x = rng.standard_normal(2000).astype(np.float32)
+    want = bf(x)
+    got = np.array([O.bf16_round(float(v)) for v in x], np.uint16)
+    assert np.array_equal(got, want)
+
+
+# --------------------------------------------------------------- index append
+
+def _signed_perm_P(rng):
+    perm = rng.permutation(D)[:DP]
+    sign = rng.choice([-1.0, 1.0], DP)
+    P = np.zeros((D, DP), np.float32)
+    P[perm, np.arange(DP)] = sign
+    return P, perm, sign
+
+
+def test_index_project_signed_permutation_is_exact_gather():
+    rng = np.random.default_rng(1)
+    P, perm, sign = _signed_perm_P(rng)
+    k = bf(rng.standard_normal((7, 3, D)))
+    out = O.index_project(k, P)
+    want = bf(unbf(k)[:, :, perm] * sign[None, None, :])
+    assert np.array_equal(out, want)
+
+
+def test_index_project_vs_library_matmul_and_exact_rounding():
+    rng = synth.rng_for(1)
+    P = synth.projection(rng)
+    k = synth.normal_bf16(rng, (40, 2, D))
+    out, exact, mag = O.index_project(k, P, with_exact=True)
+    ref = np.einsum("tgj,jc->tgc", unbf(k), P.astype(np.float64))
+    assert np.allclose(exact, ref, rtol=1e-12, atol=1e-12)
+    assert np.all(mag >= np.abs(exact))
+    flat = exact.reshape(-1)
+    for i in range(0, flat.size, 7):
+        assert unbf(out.reshape(-1)[i]) == _nearest_bf16_exact(float(flat[i]))
+
+
+def test_index_project_orthonormal_contracts_norm():
+    rng = synth.rng_for(2)
+    P = synth.projection(rng)
+    assert np.abs(P.astype(np.float64).T @ P.astype(np.float64) - np.eye(DP)).max() < 1e-6
+    k = synth.normal_bf16(rng, (64, 4, D))
+    kp = unbf(O.index_project(k, P))
+    nk = np.linalg.norm(unbf(k), axis=-1)
+    nkp = np.linalg.norm(kp, axis=-1)
+    assert np.all(nkp <= nk * (1 + 2.0 ** -8) + 1e-12)
+
+
+# ---------------------------------------------------------------------- score
+
+def _offsets(lengths):
+    o = np.zeros(len(lengths) + 1, np.int64)
+    o[1:] = np.cumsum(lengths)
+    return o
+
+
+def test_score_closed_form_in_span_of_P():
+    """q, k in span(P) with a signed-permutation P: q'.k' equals the full q.k."""
+    rng = np.random.default_rng(3)
+    P, perm, sign = _signed_perm_P(rng)
+    Hq, Hkv, n = 4, 2, 33
+    qf = np.zeros((1, Hq, D))
+    kf = np.zeros((n, Hkv, D))
+    qf[..., perm] = rng.standard_normal((1, Hq, DP))
+    kf[..., perm] = rng.standard_normal((n, Hkv, DP))
+    q, k = bf(qf), bf(kf)
+    kidx = O.index_project(k, P)
+    s = O.score(q, P, kidx, _offsets([n]), Hq, Hkv)
+    G = Hq // Hkv
+    for h in range(Hq):
+        want = unbf(k)[:, h // G, :] @ unbf(q)[0, h, :] / np.sqrt(DP)
+        assert np.allclose(s[h], want, rtol=1e-13, atol=1e-13)
+
+
+def test_score_gqa_mapping_and_ragged_batches():
+    rng = np.random.default_rng(4)
+    P = synth.projection(rng)
+    Hq, Hkv, lengths = 8, 2, [5, 9]
+    offs = _offsets(lengths)
+    kidx = np.zeros((14, Hkv, DP), np.uint16)
+    kidx[5 + 3, 1, :] = bf(rng.standard_normal(DP))          # sequence 1, token 3, KV head 1
+    q = bf(rng.standard_normal((2, Hq, D)))
+    s = O.score(q, P, kidx, offs, Hq, Hkv)
+    nz = np.argwhere(s != 0)
+    assert set(map(tuple, nz)) == {(h, 8) for h in range(4, 8)}
+    # query of sequence 0 does not leak into sequence 1
+    q2 = q.copy()
+    q2[0] = 0
+    s2 = O.score(q2, P, kidx, offs, Hq, Hkv)
+    assert np.array_equal(s2[:, 5:], s[:, 5:]) and np.all(s2[:, :5] == 0)
+
+
+def test_score_library_einsum_and_exact_doubling():
+    x = synth.config1()
+    n = int(x.offsets[-1])
+    kidx = O.index_project(x.K[:512], x.P)
+    offs = _offsets([512])
+    s = O.score(x.q, x.P, kidx, offs, 8, 2)
+    qp = np.einsum("hj,jc->hc", unbf(x.q)[0], x.P.astype(np.float64))
+    ref = np.einsum("hc,thc->ht", qp, unbf(kidx)[:, np.arange(8) // 4, :]) / np.sqrt(DP)
+    assert np.allclose(s, ref, rtol=1e-12, atol=1e-12)
+    q2 = bf(unbf(x.q) * 2.0)
+    assert np.array_equal(O.score(q2, x.P, kidx, offs, 8, 2), 2.0 * s)
+    assert n == 4096
+
+
+# ---------------------------------------------------------------------- theta
+
+@pytest.mark.parametrize("n,num,den", [(1, 9, 10), (10, 9, 10), (11, 9, 10), (4096, 9, 10), (7, 1, 2), (8, 1, 2)])
+def test_theta_is_nearest_rank_order_statistic(n, num, den):
+    rng = np.random.default_rng(n)
+    sc = rng.standard_normal((3, n))
+    th = O.theta(sc, _offsets([n]), num, den)
+    r = -(-n * num // den)
+    assert O.theta_rank(n, num, den) == r
+    for h in range(3):
+        assert th[0, h] == np.sort(sc[h])[r - 1]
+        assert np.sum(sc[h] > th[0, h]) == n - r        # distinct scores
+    if num * 2 == den and n % 2 == 1:
+        assert np.allclose(th[0], np.median(sc, axis=1))
+
+
+def test_theta_ties_and_signed_zero():
+    sc = np.array([[0.0, -0.0, 0.0, 1.0, -1.0, -0.0, 2.0, 0.0, 0.0, 0.0]])
+    th = O.theta(sc, _offsets([10]), 9, 10)
+    assert th[0, 0] == 1.0
+    th = O.theta(sc, _offsets([10]), 1, 2)
+    assert th[0, 0] == 0.0
+
+
+# ----------------------------------------------------------------------- vote
+
+def test_votes_bruteforce_recount_tiny():
+    rng = np.random.default_rng(7)
+    for trial in range(20):
+        Hq, n = int(rng.integers(1, 9)), int(rng.integers(1, 65))
+        sc = rng.integers(-3, 4, (Hq, n)).astype(np.float64)   # many ties on purpose
+        offs = _offsets([n])
+        th = O.theta(sc, offs, 9, 10)
+        v = O.votes(sc, th, offs)
+        for i in range(n):
+            cnt = 0
+            for h in range(Hq):
+                if sc[h, i] > th[0, h]:
+                    cnt += 1
+            assert v[i] == cnt
+        assert v.sum() == sum(int(np.sum(sc[h] > th[0, h])) for h in range(Hq))
+
+
+def test_votes_ragged_use_own_thresholds():
+    sc = np.array([[1.0, 2.0, 3.0, 10.0, 20.0], [3.0, 2.0, 1.0, 5.0, 5.0]])
+    offs = _offsets([3, 2])
+    th = np.array([[2.0, 2.0], [10.0, 4.0]])
+    v = O.votes(sc, th, offs)
+    assert list(v) == [1, 0, 1, 1, 2]
+
+
+# ------------------------------------------------------------------- selection
+
+def _ref_select(key, n, k, sink, local):
+    """Library stable sort on (-key, index) over the non-forced tokens."""
+    forced = np.zeros(n, bool)
+    forced[:min(sink, n)] = True
+    forced[max(0, n - local):] = True
+    cand = np.nonzero(~forced)[0]
+    order = np.lexsort((cand, -key[cand]))
+    take = cand[order[:max(0, k - forced.sum())]]
+    return np.sort(np.concatenate([np.nonzero(forced)[0], take])).astype(np.int32)
+
+
+def test_budget_tokens():
+    assert O.budget_tokens(4096, 1, 10, 4, 256) == 409
+    assert O.budget_tokens(131072, 1, 5, 4, 256) == 26214
+    assert O.budget_tokens(2000, 1, 10, 4, 256) == 260
+    assert O.budget_tokens(100, 1, 10, 4, 256) == 100
+    assert O.budget_tokens(4097, 1, 1, 4, 256) == 4097
+
+
+def test_select_vote_matches_library_sort_and_invariants():
+    rng = np.random.default_rng(9)
+    for trial in range(30):
+        n = int(rng.integers(1, 400))
+        sink, local = int(rng.integers(0, 6)), int(rng.integers(0, 40))
+        vmin = int(rng.integers(0, 3))
+        votes = rng.integers(0, 6, n).astype(np.int32)
+        bnum, bden = int(rng.integers(1, 5)), 10
+        idx, cnt = O.select_vote(votes, _offsets([n]), bnum, bden, sink, local, vmin)
+        k = O.budget_tokens(n, bnum, bden, sink, local)
+        key = np.where(votes >= vmin, votes, -1).astype(np.float64)
+        assert cnt[0] == k
+        assert np.array_equal(idx, _ref_select(key, n, k, sink, local))
+        assert np.all(np.diff(idx) > 0) and idx.min() >= 0 and idx.max() < n
+        forced = set(range(min(sink, n))) | set(range(max(0, n - local), n))
+        assert forced <= set(idx.tolist())
+
+
+def test_select_vote_vmin_makes_low_votes_fillable_minus_one():
+    # votes 1 and 0 are both below vmin=2: they tie at -1 and fill by lowest index
+    votes = np.array([9, 0, 1, 0, 2, 1, 0, 9], np.int32)
+    idx, _ = O.select_vote(votes, _offsets([8]), 5, 8, 1, 1, 2)   # k = 5
+    assert list(idx) == [0, 1, 2, 4, 7]
+
+
+def test_select_special_cases():
+    n = 1000
+    offs = _offsets([n])
+    # all votes zero (the q = 0 case): forced plus the lowest non-forced indices
+    idx, cnt = O.select_vote(np.zeros(n, np.int32), offs, 1, 2, 4, 256, 1)
+    assert list(idx) == list(range(0, 500 - 256)) + list(range(n - 256, n))
+    # full budget: everything
+    idx, _ = O.select_vote(np.arange(n, dtype=np.int32) % 7, offs, 1, 1, 4, 256, 1)
+    assert np.array_equal(idx, np.arange(n))
+    # n <= sink + local: everything
+    idx, _ = O.select_vote(np.zeros(200, np.int32), _offsets([200]), 1, 10, 4, 256, 1)
+    assert np.array_equal(idx, np.arange(200))
+
+
+def test_select_per_head_is_plain_sort_and_ties():
+    rng = np.random.default_rng(12)
+    n = 300
+    sc = rng.standard_normal((3, n))
+    sc[1, 10] = -0.0
+    sc[1, 11] = 0.0
+    sc[1, 12:40] = 0.0
+    idx, cnt = O.select_per_head(sc, _offsets([n]), 1, 2, 4, 16)
+    k = int(cnt[0])
+    assert k == 150
+    for h in range(3):
+        assert np.array_equal(idx[h * k:(h + 1) * k], _ref_select(sc[h], n, k, 4, 16))
+    # one head, no forced tokens: a plain descending stable sort, re-sorted ascending
+    one = sc[:1]
+    idx1, _ = O.select_per_head(one, _offsets([n]), 1, 3, 0, 0)
+    want = np.sort(np.argsort(-one[0], kind="stable")[:100])
+    assert np.array_equal(idx1, want)
+
+
+def test_select_ragged_layout():
+    votes = np.array([0, 5, 0, 0, 0, 0, 7, 0, 0, 0], np.int32)
+    offs = _offsets([4, 6])
+    idx, cnt = O.select_vote(votes, offs, 1, 2, 1, 1, 1)
+    assert list(cnt) == [2, 3]
+    assert list(idx) == [0, 3] + [0, 2, 5]
+
+
+# ---------------------------------------------------------------------- decode
+
+def _torch_attention(q, K, V, sel, g):
+    qt = torch.tensor(unbf(q), dtype=torch.float64)
+    kt = torch.tensor(unbf(K[sel, g, :]), dtype=torch.float64)
+    vt = torch.tensor(unbf(V[sel, g, :]), dtype=torch.float64)
+    w = torch.softmax(kt @ qt / np.sqrt(D), dim=0)
+    return (w @ vt).numpy()
+
+
+def test_dense_decode_matches_library_softmax_attention():
+    rng = np.random.default_rng(13)
+    Hq, Hkv, lengths = 4, 2, [37, 50]
+    offs = _offsets(lengths)
+    q = bf(rng.standard_normal((2, Hq, D)))
+    K = bf(rng.standard_normal((87, Hkv, D)))
+    V = bf(rng.standard_normal((87, Hkv, D)))
+    out = O.dense_decode(q, K, V, offs, Hq, Hkv)
+    for b in range(2):
+        sel = np.arange(offs[b], offs[b + 1])
+        for h in range(Hq):
+            ref = _torch_attention(q[b, h], K, V, sel, h // 2)
+            assert np.allclose(out[b, h], ref, rtol=1e-12, atol=1e-13)
+
+
+def test_sparse_full_budget_equals_dense_and_modes_agree():
+    x = synth.config1()
+    n = 4096
+    offs = _offsets([n])
+    idx = np.arange(n, dtype=np.int32)
+    sp = O.decode(x.q, x.K, x.V, offs, idx, np.array([n]), 0, 8, 2)
+    de = O.dense_decode(x.q, x.K, x.V, offs, 8, 2)
+    assert np.allclose(sp, de, rtol=0, atol=1e-14)
+    sel = np.sort(np.random.default_rng(1).choice(n, 300, replace=False)).astype(np.int32)
+    a = O.decode(x.q, x.K, x.V, offs, sel, np.array([300]), 0, 8, 2)
+    b = O.decode(x.q, x.K, x.V, offs, np.tile(sel, 8), np.array([300]), 1, 8, 2)
+    assert np.array_equal(a, b)
+    perm = np.random.default_rng(2).permutation(sel)
+    c = O.decode(x.q, x.K, x.V, offs, perm, np.array([300]), 0, 8, 2)
+    assert np.allclose(a, c, rtol=0, atol=1e-13)
+
+
+def test_decode_single_token_and_constant_values():
+    rng = np.random.default_rng(14)
+    Hq, Hkv, n = 4, 1, 20
+    q = bf(rng.standard_normal((1, Hq, D)))
+    K = bf(rng.standard_normal((n, Hkv, D)))
+    V = bf(rng.standard_normal((n, Hkv, D)))
+    out = O.decode(q, K, V, _offsets([n]), np.array([7], np.int32), np.array([1]), 0, Hq, Hkv)
+    assert np.array_equal(out[0], np.repeat(unbf(V[7, 0])[None], Hq, 0))
+    Vc = np.repeat(V[3:4], n, 0)
+    out = O.dense_decode(q, K, Vc, _offsets([n]), Hq, Hkv)
+    assert np.allclose(out[0], unbf(Vc[0, 0])[None], rtol=1e-14, atol=1e-14)
+
+
+def test_decode_per_head_lists_use_own_rows():
+    rng = np.random.default_rng(15)
+    Hq, Hkv, n = 2, 1, 10
+    q = bf(rng.standard_normal((1, Hq, D)))
+    K = bf(rng.standard_normal((n, Hkv, D)))
+    V = bf(rng.standard_normal((n, Hkv, D)))
+    idx = np.array([1, 2, 5, 8], np.int32)        # head 0: {1, 2}; head 1: {5, 8}
+    out = O.decode(q, K, V, _offsets([n]), idx, np.array([2]), 1, Hq, Hkv)
+    assert np.allclose(out[0, 0], _torch_attention(q[0, 0], K, V, np.array([1, 2]), 0), atol=1e-13)
+    assert np.allclose(out[0, 1], _torch_attention(q[0, 1], K, V, np.array([5, 8]), 0), atol=1e-13)
+
+
+# ---------------------------------------------------------------------- SnapKV
+
+def test_snapkv_rows_sum_to_one_and_pool_closed_form():
+    x = synth.make_snap(9, 300, 4, 4, 2, 5)
+    imp = O.snapkv_importance(x.q_obs, x.K, 4, 2)
+    assert np.allclose(imp.sum(axis=1), 1.0, rtol=0, atol=1e-13)
+    pooled = O.avg_pool1d(imp, 3)
+    assert np.allclose(pooled.sum(axis=1), 1.0 - (imp[:, 0] + imp[:, -1]) / 3.0, atol=1e-13)
+
+
+def test_snapkv_matches_library_softmax_pool_and_sort():
+    x = synth.make_snap(10, 257, 3, 6, 2, 7)
+    imp = O.snapkv_importance(x.q_obs, x.K, 6, 2)
+    q = torch.tensor(unbf(x.q_obs), dtype=torch.float64)        # [w][Hq][D]
+    k = torch.tensor(unbf(x.K), dtype=torch.float64)            # [n][Hkv][D]
+    for g in range(2):
+        rows = q[:, 3 * g:3 * g + 3, :].reshape(-1, D)
+        a = torch.softmax(rows @ k[:, g, :].T / np.sqrt(D), dim=-1).mean(dim=0)
+        assert np.allclose(imp[g], a.numpy(), rtol=1e-12, atol=1e-15)
+    pooled = O.avg_pool1d(imp, 3)
+    ref = torch.nn.functional.avg_pool1d(torch.tensor(imp)[None], 3, stride=1, padding=1)[0].numpy()
+    assert np.allclose(pooled, ref, rtol=1e-14, atol=1e-16)
+    idx = O.topc(pooled, 40)
+    for g in range(2):
+        order = np.lexsort((np.arange(257), -pooled[g]))[:40]
+        assert np.array_equal(idx[g], np.sort(order))
+
+
+def test_snapkv_zero_keys_tie_break_and_capacity():
+    n = 50
+    q = bf(np.random.default_rng(1).standard_normal((2, 2, D)))
+    K = np.zeros((n, 1, D), np.uint16)
+    imp = O.snapkv_importance(q, K, 2, 1)
+    assert np.allclose(imp, 1.0 / n, rtol=1e-14)
+    pooled = O.avg_pool1d(imp, 3)
+    assert np.allclose(pooled[0, 1:-1], 1.0 / n) and np.allclose(pooled[0, [0, -1]], 2.0 / (3 * n))
+    idx = O.topc(pooled, 10)
+    assert list(idx[0]) == list(range(1, 11))
+    assert np.array_equal(O.topc(pooled, 4096)[0], np.arange(n))
+
+
+def test_snapkv_single_row_is_one_softmax_and_gather_bits():
+    rng = np.random.default_rng(3)
+    n = 40
+    q = bf(rng.standard_normal((1, 1, D)))
+    K = bf(rng.standard_normal((n, 1, D)))
+    V = bf(rng.standard_normal((n, 1, D)))
+    imp = O.snapkv_importance(q, K, 1, 1)
+    s = unbf(K[:, 0]) @ unbf(q[0, 0]) / np.sqrt(D)
+    e = np.exp(s - s.max())
+    assert np.allclose(imp[0], e / e.sum(), rtol=1e-13)
+    idx = O.topc(O.avg_pool1d(imp, 3), 5)
+    Ko, Vo = O.gather_rows(K, V, idx)
+    assert np.array_equal(Ko[:, 0], K[idx[0], 0]) and np.array_equal(Vo[:, 0], V[idx[0], 0])
