@@ -138,13 +138,16 @@ size_t ts_decode_workspace_bytes(const int64_t* offsets_host, const int64_t* cou
  *   q           device bf16 [B][Hq][128]
  *   K, V        device bf16 [Ntot][Hkv][128]
  *   idx         device int32 lists in the ts_select layout for `mode`; positions must be
- *               < n_b (unchecked on the device: out-of-range entries are a caller error)
- *   counts_host host int64 [B]: list length per sequence (0 < count_b <= n_b)
+ *               in [0, n_b) (out-of-range entries are a caller error; the kernel clamps
+ *               them into range so that a bad list cannot read outside the cache)
+ *   counts_dev  device int64 [B] and counts_host host int64 [B]: the same list lengths
+ *               (0 < count_b <= n_b; e.g. count_out of ts_select and ts_budget_tokens)
  *   out         device fp32 [B][Hq][128].                                             */
 int ts_sparse_decode(const uint16_t* q, const uint16_t* K, const uint16_t* V,
                      const int64_t* offsets_dev, const int64_t* offsets_host, const int32_t* idx,
-                     const int64_t* counts_host, int32_t mode, int32_t B, int32_t Hq,
-                     int32_t Hkv, float* out, void* ws, size_t ws_bytes, hipStream_t stream);
+                     const int64_t* counts_dev, const int64_t* counts_host, int32_t mode,
+                     int32_t B, int32_t Hq, int32_t Hkv, float* out, void* ws, size_t ws_bytes,
+                     hipStream_t stream);
 
 /* Dense decode attention over all n_b tokens of each sequence (the comparison baseline,
  * [TS] eq. S_i = q . k_i / sqrt(d) for every cached token).  Same layouts as above.   */

@@ -239,3 +239,21 @@ def snapkv(q_obs, K, V, Hq, Hkv, c=4096, kernel=3):
     idx = topc(pooled, c)
     Ko, Vo = gather_rows(K, V, idx)
     return imp, pooled, idx, Ko, Vo
+
+
+def snapkv_importance_matmul(q_obs, K, Hq, Hkv, groups=None):
+    """The same importance as qo_snapkv_importance, with NumPy fp64 matmul as the QK^T step
+    (for full-size checks where the plain loops are too slow).  Returns {g: imp[n]}."""
+    w = q_obs.shape[0]
+    G = Hq // Hkv
+    qf = (np.ascontiguousarray(q_obs, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    out = {}
+    for g in (range(Hkv) if groups is None else groups):
+        kf = (np.ascontiguousarray(K[:, g, :], np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        rows = qf[:, g * G:(g + 1) * G, :].transpose(1, 0, 2).reshape(G * w, D)
+        s = rows @ kf.T / np.sqrt(D)
+        s -= s.max(axis=1, keepdims=True)
+        np.exp(s, out=s)
+        s /= s.sum(axis=1, keepdims=True)
+        out[g] = s.mean(axis=0)
+    return out

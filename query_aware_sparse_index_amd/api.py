@@ -1,0 +1,176 @@
+"""Python binding of the qasi C ABI (argument marshalling only).
+
+Every function takes torch tensors that live on the HIP device, passes their raw pointers
+and the current stream to libqasi.so, and returns the tensors the library wrote.  Torch is
+used for device memory and streams; every step of the computation runs in the library's
+gfx950 kernels.  bf16 tensors may be torch.bfloat16 or int16/uint16 bit patterns.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+
+MODE_VOTE = 0
+MODE_PER_HEAD = 1
+
+
+class QasiError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"qasi error {code}: {msg}")
+        self.code = code
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise QasiError(rc, _lib.load().ts_last_error().decode())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _p(t):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _host_i64(arr):
+    a = (ctypes.c_int64 * len(arr))(*[int(x) for x in arr])
+    return a
+
+
+def _bf16_check(*ts):
+    for t in ts:
+        if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+            raise TypeError(f"expected bf16 bits, got {t.dtype}")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def params(mode=MODE_VOTE, budget=(1, 5), sink=4, local=256, v_min=1, theta=(9, 10)) -> _lib.SelectParams:
+    return _lib.SelectParams(mode, 0, int(budget[0]), int(budget[1]), int(sink), int(local), int(v_min),
+                             int(theta[0]), int(theta[1]))
+
+
+def budget_tokens(n: int, p: _lib.SelectParams) -> int:
+    return int(_lib.load().ts_budget_tokens(int(n), ctypes.byref(p)))
+
+
+class Offsets:
+    """Sequence offsets held twice, on the device (for kernels) and on the host (for sizing)."""
+
+    def __init__(self, offsets, device="cuda"):
+        self.host_list = [int(x) for x in offsets]
+        self.host = _host_i64(self.host_list)
+        self.dev = torch.tensor(self.host_list, dtype=torch.int64, device=device)
+        self.B = len(self.host_list) - 1
+        self.ntot = self.host_list[-1]
+
+
+def index_append(k_new, P, k_index, pos: int):
+    _bf16_check(k_new, k_index)
+    T, Hkv, _ = k_new.shape
+    _check(_lib.load().ts_index_append(_p(k_new), _p(P), _p(k_index), int(pos), int(T), int(Hkv), _stream()))
+    return k_index
+
+
+def score(q, P, k_index, offs: Offsets, Hkv: int, out=None):
+    _bf16_check(q, k_index)
+    Hq = q.shape[1]
+    if out is None:
+        out = torch.empty((Hq, offs.ntot), dtype=torch.float32, device=q.device)
+    _check(_lib.load().ts_score(_p(q), _p(P), _p(k_index), _p(offs.dev), offs.host, offs.B, Hq, int(Hkv),
+                                _p(out), _stream()))
+    return out
+
+
+def select_workspace_bytes(offs: Offsets, Hq: int, p) -> int:
+    return int(_lib.load().ts_select_workspace_bytes(offs.host, offs.B, int(Hq), ctypes.byref(p)))
+
+
+def select(scores, offs: Offsets, Hkv: int, p, want_theta=False, want_votes=False, ws=None, idx=None, count=None):
+    Hq = scores.shape[0]
+    ks = [budget_tokens(offs.host_list[b + 1] - offs.host_list[b], p) for b in range(offs.B)]
+    total = sum(ks) * (Hq if p.mode == MODE_PER_HEAD else 1)
+    dev = scores.device
+    if idx is None:
+        idx = torch.empty(max(total, 4), dtype=torch.int32, device=dev)
+    if count is None:
+        count = torch.empty(offs.B, dtype=torch.int64, device=dev)
+    theta = torch.empty((offs.B, Hq), dtype=torch.float32, device=dev) if want_theta else None
+    votes = torch.empty(max(offs.ntot, 16), dtype=torch.uint8, device=dev) if want_votes else None
+    need = select_workspace_bytes(offs, Hq, p)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _check(_lib.load().ts_select(_p(scores), _p(offs.dev), offs.host, offs.B, Hq, int(Hkv), ctypes.byref(p),
+                                 _p(idx), _p(count), _p(theta), _p(votes), _p(ws), ws.numel(), _stream()))
+    res = {"idx": idx[:total], "count": count, "counts_host": ks}
+    if want_theta:
+        res["theta"] = theta
+    if want_votes:
+        res["votes"] = votes[:offs.ntot]
+    return res
+
+
+def decode_workspace_bytes(offs: Offsets, counts_host, Hq: int, Hkv: int, mode: int) -> int:
+    ch = _host_i64(counts_host) if counts_host is not None else None
+    return int(_lib.load().ts_decode_workspace_bytes(offs.host, ch, offs.B, int(Hq), int(Hkv), int(mode)))
+
+
+def sparse_decode(q, K, V, offs: Offsets, idx, counts_dev, counts_host, mode: int, ws=None, out=None):
+    _bf16_check(q, K, V)
+    B, Hq, _ = q.shape
+    Hkv = K.shape[1]
+    if out is None:
+        out = torch.empty((B, Hq, 128), dtype=torch.float32, device=q.device)
+    need = decode_workspace_bytes(offs, counts_host, Hq, Hkv, mode)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _check(_lib.load().ts_sparse_decode(_p(q), _p(K), _p(V), _p(offs.dev), offs.host, _p(idx), _p(counts_dev),
+                                        _host_i64(counts_host), int(mode), B, Hq, Hkv, _p(out), _p(ws), ws.numel(),
+                                        _stream()))
+    return out
+
+
+def dense_decode(q, K, V, offs: Offsets, ws=None, out=None):
+    _bf16_check(q, K, V)
+    B, Hq, _ = q.shape
+    Hkv = K.shape[1]
+    if out is None:
+        out = torch.empty((B, Hq, 128), dtype=torch.float32, device=q.device)
+    need = decode_workspace_bytes(offs, None, Hq, Hkv, MODE_VOTE)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _check(_lib.load().ts_dense_decode(_p(q), _p(K), _p(V), _p(offs.dev), offs.host, B, Hq, Hkv, _p(out), _p(ws),
+                                       ws.numel(), _stream()))
+    return out
+
+
+def snapkv_workspace_bytes(n: int, w: int, Hq: int, Hkv: int, c: int) -> int:
+    return int(_lib.load().snapkv_workspace_bytes(int(n), int(w), int(Hq), int(Hkv), int(c)))
+
+
+def snapkv_compress(q_obs, K, V, c: int = 4096, pool_kernel: int = 3, want_importance=False, ws=None):
+    _bf16_check(q_obs, K, V)
+    w, Hq, _ = q_obs.shape
+    n, Hkv, _ = K.shape
+    ce = min(c, n)
+    dev = K.device
+    idx = torch.empty((Hkv, ce), dtype=torch.int32, device=dev)
+    K_out = torch.empty((ce, Hkv, 128), dtype=K.dtype, device=dev)
+    V_out = torch.empty((ce, Hkv, 128), dtype=V.dtype, device=dev)
+    imp = torch.empty((Hkv, n), dtype=torch.float32, device=dev) if want_importance else None
+    pooled = torch.empty((Hkv, n), dtype=torch.float32, device=dev) if want_importance else None
+    need = snapkv_workspace_bytes(n, w, Hq, Hkv, c)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _check(_lib.load().snapkv_compress(_p(q_obs), _p(K), _p(V), int(n), int(w), int(Hq), int(Hkv), int(c),
+                                       int(pool_kernel), _p(idx), _p(K_out), _p(V_out), _p(imp), _p(pooled), _p(ws),
+                                       ws.numel(), _stream()))
+    res = {"idx": idx, "K": K_out, "V": V_out}
+    if want_importance:
+        res["importance"] = imp
+        res["pooled"] = pooled
+    return res

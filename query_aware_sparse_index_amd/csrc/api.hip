@@ -1,0 +1,237 @@
+// C-ABI layer: synchronous host-side validation, workspace sizing and launch orchestration.
+// Every check runs before the first HIP call of an entry point, so a validation failure
+// enqueues nothing.  No entry point allocates or frees memory.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "../../include/qasi.h"
+#include "qasi_internal.h"
+
+namespace qasi {
+hipError_t init_score_kernels();
+hipError_t init_snap_kernels();
+hipError_t init_kernels() {
+    hipError_t e = init_score_kernels();
+    if (e != hipSuccess) return e;
+    return init_snap_kernels();
+}
+}  // namespace qasi
+
+namespace {
+
+thread_local std::string g_last_error = "no error";
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+int hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return QASI_OK;
+    return fail(QASI_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int init_once() {
+    static std::once_flag flag;
+    static hipError_t status = hipSuccess;
+    std::call_once(flag, [] { status = qasi::init_kernels(); });
+    return hip_status(status, "kernel initialisation");
+}
+
+bool hkv_ok(int32_t Hkv) { return Hkv == 1 || Hkv == 2 || Hkv == 4 || Hkv == 8; }
+
+int check_heads(int32_t Hq, int32_t Hkv) {
+    if (Hq <= 0 || Hkv <= 0) return fail(QASI_ERR_INVALID, "Hq=%d and Hkv=%d must be positive", Hq, Hkv);
+    if (!hkv_ok(Hkv)) return fail(QASI_ERR_UNSUPPORTED, "Hkv=%d not in {1,2,4,8}", Hkv);
+    if (Hq % Hkv != 0) return fail(QASI_ERR_UNSUPPORTED, "Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+    int G = Hq / Hkv;
+    if (G != 1 && G != 2 && G != 4 && G != 8) return fail(QASI_ERR_UNSUPPORTED, "G=Hq/Hkv=%d not in {1,2,4,8}", G);
+    if (Hq > 64) return fail(QASI_ERR_UNSUPPORTED, "Hq=%d exceeds 64", Hq);
+    return QASI_OK;
+}
+
+// offsets_host: B+1 entries, starts at 0, non-decreasing, each length below 2^31.
+int check_offsets(const int64_t* offsets_dev, const int64_t* offsets_host, int32_t B, bool nonempty) {
+    if (B <= 0) return fail(QASI_ERR_INVALID, "B=%d must be positive", B);
+    if (!offsets_dev || !offsets_host) return fail(QASI_ERR_INVALID, "offsets pointers must be non-null");
+    if ((reinterpret_cast<uintptr_t>(offsets_dev) & 7u) != 0) return fail(QASI_ERR_INVALID, "offsets_dev must be 8-byte aligned");
+    if (offsets_host[0] != 0) return fail(QASI_ERR_INVALID, "offsets[0]=%lld must be 0", (long long)offsets_host[0]);
+    for (int b = 0; b < B; ++b) {
+        int64_t n = offsets_host[b + 1] - offsets_host[b];
+        if (n < 0) return fail(QASI_ERR_INVALID, "offsets not monotone at %d", b);
+        if (nonempty && n == 0) return fail(QASI_ERR_INVALID, "sequence %d is empty", b);
+        if (n >= ((int64_t)1 << 31)) return fail(QASI_ERR_UNSUPPORTED, "sequence %d longer than 2^31-1", b);
+    }
+    return QASI_OK;
+}
+
+int to_cfg(const ts_select_params* p, qasi::SelectConfig* c) {
+    if (!p) return fail(QASI_ERR_INVALID, "params must be non-null");
+    if (p->mode != QASI_MODE_VOTE && p->mode != QASI_MODE_PER_HEAD) return fail(QASI_ERR_INVALID, "mode=%d", p->mode);
+    if (p->budget_den <= 0 || p->budget_num < 0 || p->budget_num > ((int64_t)1 << 31) || p->budget_den > ((int64_t)1 << 31))
+        return fail(QASI_ERR_INVALID, "budget %lld/%lld invalid", (long long)p->budget_num, (long long)p->budget_den);
+    if (p->sink < 0 || p->local < 0 || p->sink > ((int64_t)1 << 31) || p->local > ((int64_t)1 << 31))
+        return fail(QASI_ERR_INVALID, "sink/local must be in [0, 2^31]");
+    if (p->mode == QASI_MODE_VOTE) {
+        if (p->theta_den <= 0 || p->theta_num < 0 || p->theta_num > p->theta_den)
+            return fail(QASI_ERR_INVALID, "theta %lld/%lld must be in [0, 1]", (long long)p->theta_num, (long long)p->theta_den);
+        if (p->v_min < 0) return fail(QASI_ERR_INVALID, "v_min must be >= 0");
+    }
+    c->mode = p->mode;
+    c->bnum = p->budget_num;
+    c->bden = p->budget_den;
+    c->sink = p->sink;
+    c->local = p->local;
+    c->vmin = p->v_min < 255 ? p->v_min : 255;
+    c->tnum = p->theta_num;
+    c->tden = p->theta_den > 0 ? p->theta_den : 1;
+    return QASI_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ts_last_error(void) { return g_last_error.c_str(); }
+
+int64_t ts_budget_tokens(int64_t n, const ts_select_params* p) {
+    qasi::SelectConfig c;
+    if (n < 0 || to_cfg(p, &c) != QASI_OK) return -1;
+    return qasi::budget_tokens(n, c);
+}
+
+int ts_index_append(const uint16_t* k_new, const float* P, uint16_t* k_index, int64_t pos, int64_t T, int32_t Hkv,
+                    hipStream_t stream) {
+    if (!aligned16(k_new) || !aligned16(P) || !aligned16(k_index))
+        return fail(QASI_ERR_INVALID, "k_new, P and k_index must be non-null and 16-byte aligned");
+    if (pos < 0 || T < 0) return fail(QASI_ERR_INVALID, "pos=%lld and T=%lld must be >= 0", (long long)pos, (long long)T);
+    if (!hkv_ok(Hkv)) return fail(QASI_ERR_UNSUPPORTED, "Hkv=%d not in {1,2,4,8}", Hkv);
+    if (T == 0) return QASI_OK;
+    if (int r = init_once()) return r;
+    return hip_status(qasi::launch_index_append(k_new, P, k_index, pos, T, Hkv, stream), "ts_index_append launch");
+}
+
+int ts_score(const uint16_t* q, const float* P, const uint16_t* k_index, const int64_t* offsets_dev,
+             const int64_t* offsets_host, int32_t B, int32_t Hq, int32_t Hkv, float* scores, hipStream_t stream) {
+    if (!aligned16(q) || !aligned16(P) || !aligned16(k_index) || !aligned16(scores))
+        return fail(QASI_ERR_INVALID, "q, P, k_index and scores must be non-null and 16-byte aligned");
+    if (int r = check_heads(Hq, Hkv)) return r;
+    if (int r = check_offsets(offsets_dev, offsets_host, B, false)) return r;
+    if (int r = init_once()) return r;
+    return hip_status(qasi::launch_score(q, P, k_index, offsets_dev, offsets_host, B, Hq, Hkv, scores, stream),
+                      "ts_score launch");
+}
+
+size_t ts_select_workspace_bytes(const int64_t* offsets_host, int32_t B, int32_t Hq, const ts_select_params* p) {
+    qasi::SelectConfig c;
+    if (!offsets_host || B <= 0 || Hq <= 0 || to_cfg(p, &c) != QASI_OK) return 0;
+    return qasi::select_workspace(offsets_host, B, Hq, c);
+}
+
+int ts_select(const float* scores, const int64_t* offsets_dev, const int64_t* offsets_host, int32_t B, int32_t Hq,
+              int32_t Hkv, const ts_select_params* p, int32_t* idx_out, int64_t* count_out, float* theta_out,
+              uint8_t* votes_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (!aligned16(scores) || !aligned16(idx_out) || !aligned16(ws))
+        return fail(QASI_ERR_INVALID, "scores, idx_out and ws must be non-null and 16-byte aligned");
+    if (!count_out || (reinterpret_cast<uintptr_t>(count_out) & 7u))
+        return fail(QASI_ERR_INVALID, "count_out must be non-null and 8-byte aligned");
+    if (theta_out && (reinterpret_cast<uintptr_t>(theta_out) & 3u)) return fail(QASI_ERR_INVALID, "theta_out misaligned");
+    if (int r = check_heads(Hq, Hkv)) return r;
+    if (int r = check_offsets(offsets_dev, offsets_host, B, true)) return r;
+    qasi::SelectConfig c;
+    if (int r = to_cfg(p, &c)) return r;
+    size_t need = qasi::select_workspace(offsets_host, B, Hq, c);
+    if (ws_bytes < need) return fail(QASI_ERR_WORKSPACE, "ts_select needs %zu workspace bytes, got %zu", need, ws_bytes);
+    if (int r = init_once()) return r;
+    return hip_status(qasi::launch_select(scores, offsets_dev, offsets_host, B, Hq, c, idx_out, count_out, theta_out,
+                                          votes_out, ws, ws_bytes, stream),
+                      "ts_select launch");
+}
+
+size_t ts_decode_workspace_bytes(const int64_t* offsets_host, const int64_t* counts_host, int32_t B, int32_t Hq,
+                                 int32_t Hkv, int32_t mode) {
+    if (!offsets_host || B <= 0 || Hq <= 0 || Hkv <= 0) return 0;
+    return qasi::decode_workspace(offsets_host, counts_host, B, Hq, Hkv, mode);
+}
+
+int ts_sparse_decode(const uint16_t* q, const uint16_t* K, const uint16_t* V, const int64_t* offsets_dev,
+                     const int64_t* offsets_host, const int32_t* idx, const int64_t* counts_dev,
+                     const int64_t* counts_host, int32_t mode, int32_t B, int32_t Hq, int32_t Hkv, float* out, void* ws,
+                     size_t ws_bytes, hipStream_t stream) {
+    if (!aligned16(q) || !aligned16(K) || !aligned16(V) || !aligned16(out) || !aligned16(ws))
+        return fail(QASI_ERR_INVALID, "q, K, V, out and ws must be non-null and 16-byte aligned");
+    if (!idx || (reinterpret_cast<uintptr_t>(idx) & 3u)) return fail(QASI_ERR_INVALID, "idx must be non-null and aligned");
+    if (!counts_dev || !counts_host || (reinterpret_cast<uintptr_t>(counts_dev) & 7u))
+        return fail(QASI_ERR_INVALID, "counts_dev / counts_host must be non-null (counts_dev 8-byte aligned)");
+    if (mode != QASI_MODE_VOTE && mode != QASI_MODE_PER_HEAD) return fail(QASI_ERR_INVALID, "mode=%d", mode);
+    if (int r = check_heads(Hq, Hkv)) return r;
+    if (int r = check_offsets(offsets_dev, offsets_host, B, true)) return r;
+    for (int b = 0; b < B; ++b) {
+        int64_t n = offsets_host[b + 1] - offsets_host[b];
+        if (counts_host[b] < 1 || counts_host[b] > n)
+            return fail(QASI_ERR_INVALID, "counts[%d]=%lld outside [1, n_b=%lld]", b, (long long)counts_host[b], (long long)n);
+    }
+    size_t need = qasi::decode_workspace(offsets_host, counts_host, B, Hq, Hkv, mode);
+    if (ws_bytes < need) return fail(QASI_ERR_WORKSPACE, "ts_sparse_decode needs %zu workspace bytes, got %zu", need, ws_bytes);
+    if (int r = init_once()) return r;
+    return hip_status(qasi::launch_sparse_decode(q, K, V, offsets_dev, offsets_host, idx, counts_dev, counts_host, mode,
+                                                 B, Hq, Hkv, out, ws, ws_bytes, stream),
+                      "ts_sparse_decode launch");
+}
+
+int ts_dense_decode(const uint16_t* q, const uint16_t* K, const uint16_t* V, const int64_t* offsets_dev,
+                    const int64_t* offsets_host, int32_t B, int32_t Hq, int32_t Hkv, float* out, void* ws,
+                    size_t ws_bytes, hipStream_t stream) {
+    if (!aligned16(q) || !aligned16(K) || !aligned16(V) || !aligned16(out) || !aligned16(ws))
+        return fail(QASI_ERR_INVALID, "q, K, V, out and ws must be non-null and 16-byte aligned");
+    if (int r = check_heads(Hq, Hkv)) return r;
+    if (int r = check_offsets(offsets_dev, offsets_host, B, true)) return r;
+    size_t need = qasi::decode_workspace(offsets_host, nullptr, B, Hq, Hkv, 2);
+    if (ws_bytes < need) return fail(QASI_ERR_WORKSPACE, "ts_dense_decode needs %zu workspace bytes, got %zu", need, ws_bytes);
+    if (int r = init_once()) return r;
+    return hip_status(qasi::launch_dense_decode(q, K, V, offsets_dev, offsets_host, B, Hq, Hkv, out, ws, ws_bytes, stream),
+                      "ts_dense_decode launch");
+}
+
+size_t snapkv_workspace_bytes(int64_t n, int32_t w, int32_t Hq, int32_t Hkv, int64_t c) {
+    if (n <= 0 || w <= 0 || Hq <= 0 || Hkv <= 0 || c <= 0 || Hq % Hkv) return 0;
+    return qasi::snapkv_workspace(n, w, Hq, Hkv, c);
+}
+
+int snapkv_compress(const uint16_t* q_obs, const uint16_t* K, const uint16_t* V, int64_t n, int32_t w, int32_t Hq,
+                    int32_t Hkv, int64_t c, int32_t pool_kernel, int32_t* idx_out, uint16_t* K_out, uint16_t* V_out,
+                    float* importance_out, float* pooled_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (!aligned16(q_obs) || !aligned16(K) || !aligned16(V) || !aligned16(idx_out) || !aligned16(K_out) ||
+        !aligned16(V_out) || !aligned16(ws))
+        return fail(QASI_ERR_INVALID, "q_obs, K, V, idx_out, K_out, V_out and ws must be non-null and 16-byte aligned");
+    if ((importance_out && (reinterpret_cast<uintptr_t>(importance_out) & 3u)) ||
+        (pooled_out && (reinterpret_cast<uintptr_t>(pooled_out) & 3u)))
+        return fail(QASI_ERR_INVALID, "importance_out / pooled_out misaligned");
+    if (n <= 0 || n >= ((int64_t)1 << 31)) return fail(QASI_ERR_INVALID, "n=%lld outside [1, 2^31)", (long long)n);
+    if (w <= 0 || c <= 0) return fail(QASI_ERR_INVALID, "w=%d and c=%lld must be positive", w, (long long)c);
+    if (int r = check_heads(Hq, Hkv)) return r;
+    if (pool_kernel != 3) return fail(QASI_ERR_UNSUPPORTED, "pool_kernel=%d (only 3 is built)", pool_kernel);
+    const int R = (Hq / Hkv) * w;
+    if (R > 256 || R % 16 != 0)
+        return fail(QASI_ERR_UNSUPPORTED, "(Hq/Hkv)*w=%d must be a multiple of 16 and at most 256", R);
+    size_t need = qasi::snapkv_workspace(n, w, Hq, Hkv, c);
+    if (ws_bytes < need) return fail(QASI_ERR_WORKSPACE, "snapkv_compress needs %zu workspace bytes, got %zu", need, ws_bytes);
+    if (int r = init_once()) return r;
+    return hip_status(qasi::launch_snapkv(q_obs, K, V, n, w, Hq, Hkv, c, idx_out, K_out, V_out, importance_out,
+                                          pooled_out, ws, ws_bytes, stream),
+                      "snapkv_compress launch");
+}
+
+}  // extern "C"

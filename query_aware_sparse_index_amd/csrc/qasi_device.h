@@ -1,0 +1,118 @@
+// Device-side helpers shared by the gfx950 kernels of the qasi library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qasi {
+
+constexpr int kD = 128;   // head dimension
+constexpr int kDP = 32;   // index dimension d' = d / 4
+
+// bf16 bit pattern -> fp32 (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// fp64 -> bf16 with one rounding, nearest-even.  Normal range: drop 45 mantissa bits of the
+// double with round-half-even integer arithmetic (a carry into the exponent is the correct
+// result).  Below 2^-126: count quanta of the subnormal grid 2^-133 and round that count
+// with rint (nearest-even in the default mode); 128 quanta is the smallest normal 0x0080.
+__device__ __forceinline__ uint16_t f64_to_bf16_rne(double x) {
+    uint64_t u = (uint64_t)__double_as_longlong(x);
+    uint32_t sign = (uint32_t)(u >> 63) << 15;
+    uint64_t a = u & 0x7fffffffffffffffull;
+    if (a == 0) return (uint16_t)sign;
+    uint32_t bexp = (uint32_t)(a >> 52);
+    if (bexp >= 1023 - 126) {
+        a += 0x00000fffffffffffull + ((a >> 45) & 1ull);
+        uint32_t e = (uint32_t)(a >> 52);
+        if (e > 1023 + 127) return (uint16_t)(sign | 0x7f80u);
+        uint32_t mant = (uint32_t)((a >> 45) & 0x7full);
+        return (uint16_t)(sign | ((e - 1023 + 127) << 7) | mant);
+    }
+    double q = rint(__longlong_as_double((long long)a) * 0x1p133);
+    return (uint16_t)(sign | (uint32_t)q);
+}
+
+// Order-preserving map fp32 -> uint32 (ascending keys <=> ascending values); -0 maps to
+// the key of +0 so the two tie.
+__device__ __forceinline__ uint32_t order_key(float s) {
+    uint32_t b = __float_as_uint(s);
+    if (b == 0x80000000u) b = 0u;
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float key_to_float(uint32_t k) {
+    uint32_t b = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+    return __uint_as_float(b);
+}
+
+// Butterfly sums across lanes with DPP (no LDS traffic).  xor1 / xor2 stay inside a quad;
+// half-mirror and mirror pair 4-lane and 8-lane groups inside a 16-lane row.
+__device__ __forceinline__ float dpp_quad_xor1(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xb1, 0xf, 0xf, true));  // [1,0,3,2]
+}
+__device__ __forceinline__ float dpp_quad_xor2(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4e, 0xf, 0xf, true));  // [2,3,0,1]
+}
+__device__ __forceinline__ float dpp_row_half_mirror(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float dpp_row_mirror(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xf, 0xf, true));
+}
+// Sum over each group of 4 lanes (result in every lane of the quad).
+__device__ __forceinline__ float sum_quad(float v) {
+    v += dpp_quad_xor1(v);
+    v += dpp_quad_xor2(v);
+    return v;
+}
+// Sum over each 16-lane row (result in every lane of the row).
+__device__ __forceinline__ float sum_row16(float v) {
+    v += dpp_quad_xor1(v);
+    v += dpp_quad_xor2(v);
+    v += dpp_row_half_mirror(v);
+    v += dpp_row_mirror(v);
+    return v;
+}
+
+// Wave-wide reductions (64 lanes) through shuffles.
+__device__ __forceinline__ float wave_max(float v) {
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+__device__ __forceinline__ int wave_sum_i(int v) {
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+// Inclusive prefix sum of one int per thread over a block of NT threads (NT multiple of 64,
+// at most 1024).  `tmp` holds NT/64 ints.  Returns the inclusive value; *total the sum.
+template <int NT>
+__device__ __forceinline__ int block_inclusive_scan(int v, int* tmp, int* total) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        int y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) tmp[wid] = x;
+    __syncthreads();
+    int base = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) {
+        int t = tmp[w];
+        if (w < wid) base += t;
+        tot += t;
+    }
+    __syncthreads();
+    *total = tot;
+    return x + base;
+}
+
+}  // namespace qasi

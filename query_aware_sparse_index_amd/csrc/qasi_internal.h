@@ -1,0 +1,66 @@
+// Internal launcher interface between the C-ABI layer and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qasi {
+
+// ---- index and score
+hipError_t launch_index_append(const uint16_t* k_new, const float* P, uint16_t* k_index, int64_t pos, int64_t T,
+                               int Hkv, hipStream_t stream);
+hipError_t launch_score(const uint16_t* q, const float* P, const uint16_t* k_index, const int64_t* offsets_dev,
+                        const int64_t* offsets_host, int B, int Hq, int Hkv, float* scores, hipStream_t stream);
+
+// ---- selection
+struct SelectConfig {
+    int mode;
+    int64_t bnum, bden, sink, local, vmin, tnum, tden;
+};
+size_t select_workspace(const int64_t* offsets_host, int B, int Hq, const SelectConfig& c);
+hipError_t launch_select(const float* scores, const int64_t* offsets_dev, const int64_t* offsets_host, int B, int Hq,
+                         const SelectConfig& c, int32_t* idx_out, int64_t* count_out, float* theta_out,
+                         uint8_t* votes_out, void* ws, size_t ws_bytes, hipStream_t stream);
+int64_t budget_tokens(int64_t n, const SelectConfig& c);
+// Top-k per row of a [rows][n] fp32 array, ties to the lower position, ascending output
+// idx_out[r * k + j] (the per-head selection with no forced tokens).
+size_t rows_topk_workspace(int rows, int64_t n, int64_t k);
+hipError_t launch_rows_topk(const float* vals, int rows, int64_t n, int64_t k, int32_t* idx_out, void* ws,
+                            size_t ws_bytes, hipStream_t stream);
+
+// ---- decode
+size_t decode_workspace(const int64_t* offsets_host, const int64_t* counts_host, int B, int Hq, int Hkv, int mode);
+hipError_t launch_sparse_decode(const uint16_t* q, const uint16_t* K, const uint16_t* V, const int64_t* offsets_dev,
+                                const int64_t* offsets_host, const int32_t* idx, const int64_t* counts_dev,
+                                const int64_t* counts_host, int mode,
+                                int B, int Hq, int Hkv, float* out, void* ws, size_t ws_bytes, hipStream_t stream);
+hipError_t launch_dense_decode(const uint16_t* q, const uint16_t* K, const uint16_t* V, const int64_t* offsets_dev,
+                               const int64_t* offsets_host, int B, int Hq, int Hkv, float* out, void* ws,
+                               size_t ws_bytes, hipStream_t stream);
+
+// ---- SnapKV
+size_t snapkv_workspace(int64_t n, int w, int Hq, int Hkv, int64_t c);
+hipError_t launch_snapkv(const uint16_t* q_obs, const uint16_t* K, const uint16_t* V, int64_t n, int w, int Hq,
+                         int Hkv, int64_t c, int32_t* idx_out, uint16_t* K_out, uint16_t* V_out, float* imp_out,
+                         float* pooled_out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+// One-time per-process set-up (kernel attributes); returns the first error.
+hipError_t init_kernels();
+
+// Workspace carving: 256-byte aligned sub-buffers.
+struct WsCarver {
+    char* base;
+    size_t off = 0;
+    explicit WsCarver(void* p) : base(static_cast<char*>(p)) {}
+    template <class T>
+    T* take(size_t count) {
+        off = (off + 255) & ~(size_t)255;
+        T* p = reinterpret_cast<T*>(base ? base + off : nullptr);
+        off += count * sizeof(T);
+        return p;
+    }
+    size_t size() const { return (off + 255) & ~(size_t)255; }
+};
+
+}  // namespace qasi

@@ -1,0 +1,122 @@
+"""The C-ABI library loads, exports every function include/qasi.h declares, and rejects
+invalid or unsupported calls synchronously, before any HIP call (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from query_aware_sparse_index_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = ctypes.c_void_p(4096)          # aligned, never dereferenced: validation fails first
+MIS = ctypes.c_void_p(4097)           # misaligned
+
+
+def header_functions():
+    txt = open(os.path.join(ROOT, "include", "qasi.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", txt, flags=re.M)))
+
+
+def test_exports_match_header():
+    lib = _lib.load()
+    names = header_functions()
+    assert len(names) == 11, names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.SIGNATURES)
+
+
+def _offs(vals):
+    return (ctypes.c_int64 * len(vals))(*vals)
+
+
+def _params(mode=0, bnum=1, bden=5, sink=4, local=256, vmin=1, tn=9, td=10):
+    return _lib.SelectParams(mode, 0, bnum, bden, sink, local, vmin, tn, td)
+
+
+def err():
+    return _lib.load().ts_last_error().decode()
+
+
+def test_budget_helper():
+    L = _lib.load()
+    p = _params()
+    assert L.ts_budget_tokens(131072, ctypes.byref(p)) == 26214
+    assert L.ts_budget_tokens(100, ctypes.byref(p)) == 100
+    bad = _params(bden=0)
+    assert L.ts_budget_tokens(100, ctypes.byref(bad)) == -1
+
+
+def test_index_append_validation():
+    L = _lib.load()
+    assert L.ts_index_append(None, FAKE, FAKE, 0, 1, 8, None) == -1
+    assert L.ts_index_append(MIS, FAKE, FAKE, 0, 1, 8, None) == -1
+    assert L.ts_index_append(FAKE, FAKE, FAKE, -1, 1, 8, None) == -1
+    assert L.ts_index_append(FAKE, FAKE, FAKE, 0, 1, 3, None) == -2
+    assert L.ts_index_append(FAKE, FAKE, FAKE, 0, 0, 8, None) == 0   # nothing to do, no HIP call
+
+
+@pytest.mark.parametrize("Hq,Hkv,code", [(32, 3, -2), (30, 8, -2), (24, 8, -2), (128, 8, -2), (0, 8, -1)])
+def test_score_head_validation(Hq, Hkv, code):
+    L = _lib.load()
+    o = _offs([0, 100])
+    assert L.ts_score(FAKE, FAKE, FAKE, FAKE, o, 1, Hq, Hkv, FAKE, None) == code
+    assert err()
+
+
+def test_offsets_validation():
+    L = _lib.load()
+    assert L.ts_score(FAKE, FAKE, FAKE, FAKE, _offs([1, 100]), 1, 32, 8, FAKE, None) == -1
+    assert L.ts_score(FAKE, FAKE, FAKE, FAKE, _offs([0, 100, 50]), 2, 32, 8, FAKE, None) == -1
+    assert L.ts_score(FAKE, FAKE, FAKE, FAKE, _offs([0, 100]), 0, 32, 8, FAKE, None) == -1
+    p = _params()
+    assert L.ts_select(FAKE, FAKE, _offs([0, 0]), 1, 32, 8, ctypes.byref(p), FAKE, FAKE, None, None, FAKE, 1 << 40,
+                       None) == -1  # empty sequence
+
+
+def test_select_validation():
+    L = _lib.load()
+    o = _offs([0, 4096])
+    for p, code in [(_params(mode=2), -1), (_params(bden=0), -1), (_params(tn=11, td=10), -1), (_params(sink=-1), -1),
+                    (_params(vmin=-1), -1)]:
+        assert L.ts_select(FAKE, FAKE, o, 1, 8, 2, ctypes.byref(p), FAKE, FAKE, None, None, FAKE, 1 << 40, None) == code
+    p = _params()
+    need = L.ts_select_workspace_bytes(o, 1, 8, ctypes.byref(p))
+    assert need > 0
+    assert L.ts_select(FAKE, FAKE, o, 1, 8, 2, ctypes.byref(p), FAKE, FAKE, None, None, FAKE, need - 1, None) == -3
+    assert "workspace" in err()
+    assert L.ts_select(FAKE, FAKE, o, 1, 8, 2, None, FAKE, FAKE, None, None, FAKE, need, None) == -1
+
+
+def test_decode_validation():
+    L = _lib.load()
+    o = _offs([0, 1000])
+    c_ok, c_bad0, c_big = _offs([100]), _offs([0]), _offs([1001])
+    ws = 1 << 40
+    assert L.ts_sparse_decode(FAKE, FAKE, FAKE, FAKE, o, FAKE, FAKE, c_bad0, 0, 1, 32, 8, FAKE, FAKE, ws, None) == -1
+    assert L.ts_sparse_decode(FAKE, FAKE, FAKE, FAKE, o, FAKE, FAKE, c_big, 0, 1, 32, 8, FAKE, FAKE, ws, None) == -1
+    assert L.ts_sparse_decode(FAKE, FAKE, FAKE, FAKE, o, FAKE, FAKE, c_ok, 7, 1, 32, 8, FAKE, FAKE, ws, None) == -1
+    assert L.ts_sparse_decode(FAKE, FAKE, FAKE, FAKE, o, None, FAKE, c_ok, 0, 1, 32, 8, FAKE, FAKE, ws, None) == -1
+    need = L.ts_decode_workspace_bytes(o, c_ok, 1, 32, 8, 0)
+    assert L.ts_sparse_decode(FAKE, FAKE, FAKE, FAKE, o, FAKE, FAKE, c_ok, 0, 1, 32, 8, FAKE, FAKE, need - 1, None) == -3
+    assert L.ts_dense_decode(FAKE, MIS, FAKE, FAKE, o, 1, 32, 8, FAKE, FAKE, ws, None) == -1
+    need = L.ts_decode_workspace_bytes(o, None, 1, 32, 8, 0)
+    assert L.ts_dense_decode(FAKE, FAKE, FAKE, FAKE, o, 1, 32, 8, FAKE, FAKE, need - 1, None) == -3
+
+
+def test_snapkv_validation():
+    L = _lib.load()
+    ws = 1 << 40
+    args = lambda n, w, Hq, Hkv, c, k: (FAKE, FAKE, FAKE, n, w, Hq, Hkv, c, k, FAKE, FAKE, FAKE, None, None, FAKE, ws, None)
+    assert L.snapkv_compress(*args(1000, 32, 64, 8, 4096, 5)) == -2
+    assert L.snapkv_compress(*args(1000, 3, 64, 8, 4096, 3)) == -2      # G*w = 24
+    assert L.snapkv_compress(*args(1000, 64, 64, 8, 4096, 3)) == -2     # G*w = 512
+    assert L.snapkv_compress(*args(0, 32, 64, 8, 4096, 3)) == -1
+    assert L.snapkv_compress(*args(1000, 32, 64, 8, 0, 3)) == -1
+    need = L.snapkv_workspace_bytes(1000, 32, 64, 8, 4096)
+    assert need > 0
+    a = list(args(1000, 32, 64, 8, 4096, 3))
+    a[-2] = need - 1
+    assert L.snapkv_compress(*a) == -3

@@ -1,0 +1,138 @@
+"""GPU parity of the HIP path against the fp64 CPU oracle (staged).
+
+Rules (each stage is compared on the GPU's own inputs to that stage, so that legal fp32
+vs fp64 near-ties cannot cascade):
+  * index append: the GPU index equals the oracle's bf16 values bit for bit (both sum the
+    fp64 products in the same order and round once);
+  * scores: |gpu - oracle(gpu index)| <= 2 x the fp32 dot-product error bound;
+  * theta: the exact nearest-rank order statistic of the GPU scores;
+  * votes and selections: bit-exact against the oracle run on the GPU scores / votes;
+  * decode: max abs error <= 2e-3 against the oracle run on the GPU index lists.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from query_aware_sparse_index_amd import api, synth
+
+from gpu_util import Step, bits, check_staged, dev, f64, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+
+
+def test_c1_vote_step():
+    r = check_staged(Step(synth.config1()).run())
+    print("c1 vote", r)
+
+
+def test_c1_per_head_step():
+    r = check_staged(Step(synth.config1(), mode=api.MODE_PER_HEAD).run())
+    print("c1 per-head", r)
+
+
+@pytest.mark.parametrize("mode", [api.MODE_VOTE, api.MODE_PER_HEAD])
+def test_c2_step(mode):
+    r = check_staged(Step(synth.config2(), mode=mode).run())
+    print("c2", mode, r)
+
+
+@pytest.mark.parametrize("lengths,budget", [([5000, 1234, 300, 4097], (3, 20)), ([70000, 20000], (1, 5))])
+@pytest.mark.parametrize("mode", [api.MODE_VOTE, api.MODE_PER_HEAD])
+def test_ragged_batch(lengths, budget, mode):
+    x = synth.make_decode(4, lengths, 32, 8, lambda n: n // 100, False, budget, 3)
+    check_staged(Step(x, mode=mode).run())
+
+
+@pytest.mark.parametrize("mode", [api.MODE_VOTE, api.MODE_PER_HEAD])
+def test_full_budget_equals_dense(mode):
+    x = synth.make_decode(1, [3000], 8, 2, 16, False, (1, 1), 5)
+    st = Step(x, mode=mode).run()
+    idx = st.sel["idx"].cpu().numpy()
+    reps = 1 if mode == api.MODE_VOTE else 8
+    assert np.array_equal(idx, np.tile(np.arange(3000), reps))
+    dense = api.dense_decode(st.q, st.K, st.V, st.offs)
+    torch.cuda.synchronize()
+    ref = O.dense_decode(x.q, x.K, x.V, x.offsets, 8, 2)
+    assert np.abs(f64(dense) - ref).max() <= 2e-3
+    assert np.abs(f64(st.out) - ref).max() <= 2e-3
+
+
+def test_short_sequences_take_everything():
+    for n in (1, 5, 259, 260, 261):
+        x = synth.make_decode(1, [n], 8, 2, 0, False, (1, 10), n)
+        st = Step(x).run()
+        k = O.budget_tokens(n, 1, 10, 4, 256)
+        idx = st.sel["idx"].cpu().numpy()
+        assert len(idx) == k
+        if n <= 260:
+            assert np.array_equal(idx, np.arange(n))
+        check_staged(st)
+
+
+def test_zero_query_ties_to_lowest_positions():
+    x = synth.make_decode(1, [5000], 8, 2, 0, False, (1, 10), 2)
+    x.q[:] = 0
+    for mode in (api.MODE_VOTE, api.MODE_PER_HEAD):
+        st = Step(x, mode=mode).run()
+        assert np.all(f64(st.scores) == 0)
+        check_staged(st)
+        idx = st.sel["idx"].cpu().numpy()[:500]
+        assert np.array_equal(idx, np.r_[0:244, 4744:5000])
+
+
+def test_median_threshold_and_vmin():
+    x = synth.config1()
+    check_staged(Step(x, theta=(1, 2)).run())
+    check_staged(Step(x, vmin=3).run())
+    check_staged(Step(x, sink=0, local=0).run())
+
+
+def test_incremental_append_equals_batch_build():
+    x = synth.config1()
+    n = 4096
+    K = to_dev(x.K)
+    P = to_dev(x.P)
+    a = torch.empty((n, 2, 32), dtype=torch.int16, device=dev())
+    b = torch.empty_like(a)
+    api.index_append(K, P, a, 0)
+    api.index_append(K[:4000], P, b, 0)
+    for t in range(4000, n):
+        api.index_append(K[t:t + 1], P, b, t)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_repeat_is_deterministic():
+    x = synth.config2()
+    s1 = Step(x).run()
+    s2 = Step(x).run()
+    assert torch.equal(s1.scores, s2.scores)
+    assert torch.equal(s1.sel["idx"], s2.sel["idx"])
+    assert torch.equal(s1.out, s2.out)
+
+
+def test_dense_decode_c2():
+    x = synth.config2()
+    q, K, V = to_dev(x.q), to_dev(x.K), to_dev(x.V)
+    out = api.dense_decode(q, K, V, api.Offsets(x.offsets, dev()))
+    torch.cuda.synchronize()
+    ref = O.dense_decode(x.q, x.K, x.V, x.offsets, 32, 8)
+    assert np.abs(f64(out) - ref).max() <= 2e-3
+
+
+def test_error_codes_on_device_calls():
+    x = synth.config1()
+    st = Step(x)
+    with pytest.raises(api.QasiError) as e:
+        api.score(st.q[:, :6].contiguous(), st.P, torch.empty((4096, 2, 32), dtype=torch.int16, device=dev()), st.offs, 4)
+    assert e.value.code in (-1, -2)
+    with pytest.raises(api.QasiError) as e:
+        api.snapkv_compress(st.q[:1], st.K, st.V, 64, pool_kernel=5)
+    assert e.value.code == -2
