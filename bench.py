@@ -1,0 +1,331 @@
+"""Decode-step benchmark: query-aware selection + sparse attention on one MI355X.
+
+Workload: one LLaMA-3-8B-shaped attention layer (32 query / 8 KV heads, d = 128, index
+d' = 32) with n = 131072 cached tokens, a 20 % selection budget and voting mode.  A step is
+the whole hot path: ts_index_append (T = 1) + ts_score + ts_select + ts_sparse_decode,
+with the cache, the index and the step's query already resident in HBM.  The last-level
+cache is flushed (a 512 MiB read) before every timed step, outside the timed region, so
+the figure is HBM-cold.  Time is measured with HIP events on the stream the kernels run on.
+
+Prints one JSON line (see the fields below); --out also writes it to a file.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_GBPS = 8000.0       # MI355X HBM3E peak
+METRIC = "µs/decode step + HBM GB/s (% peak), 128K ctx, 20% budget, 1 MI355X"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--n", type=int, default=131072)
+    ap.add_argument("--budget", type=int, default=20, help="percent (5, 10, 15, 20, 30)")
+    ap.add_argument("--mode", choices=["vote", "per-head"], default="vote")
+    ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extra", action="store_true", help="skip dense / warm / graph side measurements")
+    ap.add_argument("--cpu-steps", type=int, default=10)
+    ap.add_argument("--isolate", action="store_true", help="also time each call alone after a flush")
+    ap.add_argument("--out", default=None)
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the decode-step path of one attention layer runs on a single "
+              "MI355X (see DESIGN.md for how it would shard); run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from query_aware_sparse_index_amd import api, synth
+
+    dev = torch.device("cuda:0")
+    n0, steps, warm = args.n, args.steps, args.warmup
+    total_steps = steps + warm
+    mode = api.MODE_VOTE if args.mode == "vote" else api.MODE_PER_HEAD
+    bnum, bden = synth.BUDGETS[args.budget]
+    print(f"bench: building inputs n={n0} budget={bnum}/{bden} mode={args.mode} steps={steps} warmup={warm}",
+          file=sys.stderr, flush=True)
+
+    x = synth.config3(args.budget, n0)
+    Hq, Hkv = x.Hq, x.Hkv
+    cap = n0 + total_steps
+    # cache arrays with room for the decode steps; the new rows are drawn per step
+    K = torch.empty((cap, Hkv, 128), dtype=torch.int16, device=dev)
+    V = torch.empty((cap, Hkv, 128), dtype=torch.int16, device=dev)
+    K[:n0] = torch.from_numpy(x.K.view(np.int16)).to(dev)
+    V[:n0] = torch.from_numpy(x.V.view(np.int16)).to(dev)
+    qs = []
+    for s in range(total_steps):
+        q_s, k_new, v_new = synth.config3_step(s + 1, x.q, Hkv)
+        K[n0 + s] = torch.from_numpy(k_new[0].view(np.int16)).to(dev)
+        V[n0 + s] = torch.from_numpy(v_new[0].view(np.int16)).to(dev)
+        qs.append(q_s)
+    Q = torch.from_numpy(np.stack(qs).view(np.int16)).to(dev)          # [steps][1][Hq][128]
+    P = torch.from_numpy(x.P).to(dev)
+    kidx = torch.empty((cap, Hkv, 32), dtype=torch.int16, device=dev)
+    api.index_append(K[:n0], P, kidx, 0)
+    p = api.params(mode, (bnum, bden))
+    offs = [api.Offsets([0, n0 + s + 1], dev) for s in range(total_steps)]
+    nmax = cap
+    scores = torch.empty((Hq, api.score_stride(offs[-1])), dtype=torch.float32, device=dev)
+    kmax = api.budget_tokens(nmax, p)
+    idx = torch.empty(kmax * (Hq if mode == api.MODE_PER_HEAD else 1) + 16, dtype=torch.int32, device=dev)
+    count = torch.empty(1, dtype=torch.int64, device=dev)
+    ws_sel = torch.empty(max(api.select_workspace_bytes(offs[-1], Hq, p), 256), dtype=torch.uint8, device=dev)
+    ws_dec = torch.empty(max(api.decode_workspace_bytes(offs[-1], [kmax], Hq, Hkv, mode), 256), dtype=torch.uint8,
+                         device=dev)
+    out = torch.empty((1, Hq, 128), dtype=torch.float32, device=dev)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
+    flush_sink = torch.empty((), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def do_flush():
+        torch.sum(flush.view(torch.float32), dim=0, out=flush_sink)
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    # argument tuples for the four C-ABI calls of every step, built before timing so that
+    # the host enqueues a step in a few microseconds
+    import ctypes
+    from query_aware_sparse_index_amd import _lib
+    L = _lib.load()
+    vp = lambda t: ctypes.c_void_p(t.data_ptr())
+    pref = ctypes.byref(p)
+    stream_of = lambda: ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    calls = []
+    for s in range(total_steps):
+        n = n0 + s + 1
+        o = offs[s]
+        kb = api.budget_tokens(n, p)
+        ch = (ctypes.c_int64 * 1)(kb)
+        qp = ctypes.c_void_p(Q[s].data_ptr())
+        calls.append(((vp(K) .value + (n - 1) * Hkv * 128 * 2, n - 1),
+                      (qp, vp(o.dev), o.host), ch, kb))
+    Kp, Pp, kip, scp, idp, cnp = vp(K), vp(P), vp(kidx), vp(scores), vp(idx), vp(count)
+    Vp, outp, wsp, wdp = vp(V), vp(out), vp(ws_sel), vp(ws_dec)
+    ws_sel_n, ws_dec_n = ws_sel.numel(), ws_dec.numel()
+
+    def chk(rc):
+        if rc != 0:
+            raise RuntimeError(L.ts_last_error().decode())
+
+    def step(s, marks=None):
+        (kaddr, pos), (qp, od, oh), ch, kb = calls[s]
+        st = stream_of()
+        chk(L.ts_index_append(ctypes.c_void_p(kaddr), Pp, kip, pos, 1, Hkv, st))
+        if marks: marks[1].record()
+        chk(L.ts_score(qp, Pp, kip, od, oh, 1, Hq, Hkv, scp, st))
+        if marks: marks[2].record()
+        chk(L.ts_select(scp, od, oh, 1, Hq, Hkv, pref, idp, cnp, None, None, wsp, ws_sel_n, st))
+        if marks: marks[3].record()
+        chk(L.ts_sparse_decode(qp, Kp, Vp, od, oh, idp, cnp, ch, mode, 1, Hq, Hkv, outp, wdp, ws_dec_n, st))
+        return kb
+
+    # warm-up
+    for s in range(warm):
+        if not args.no_flush:
+            do_flush()
+        step(s)
+    torch.cuda.synchronize()
+    print("bench: warm-up done", file=sys.stderr, flush=True)
+
+    # timed steps: events per step and per call; flushes between steps are not timed
+    marks = [[ev() for _ in range(5)] for _ in range(steps)]
+    ktot = []
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    for i in range(steps):
+        s = warm + i
+        if not args.no_flush:
+            do_flush()
+        m = marks[i]
+        m[0].record()
+        ktot.append(step(s, m))
+        m[4].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    step_us = np.array([m[0].elapsed_time(m[4]) * 1e3 for m in marks])
+    parts = {
+        "index_append": np.array([m[0].elapsed_time(m[1]) * 1e3 for m in marks]),
+        "score": np.array([m[1].elapsed_time(m[2]) * 1e3 for m in marks]),
+        "select": np.array([m[2].elapsed_time(m[3]) * 1e3 for m in marks]),
+        "sparse_decode": np.array([m[3].elapsed_time(m[4]) * 1e3 for m in marks]),
+    }
+    print(f"bench: timed {steps} steps, mean {step_us.mean():.1f} us", file=sys.stderr, flush=True)
+
+    # algorithmic bytes (what the method must move): index read + selected K/V rows
+    n_mean = n0 + warm + (steps + 1) / 2.0
+    k_mean = float(np.mean(ktot))
+    if mode == api.MODE_VOTE:
+        kv_bytes = k_mean * Hkv * 128 * 2 * 2          # one K and V row per KV head per selected token
+    else:
+        kv_bytes = k_mean * Hq * 128 * 2 * 2           # every query head reads its own list's rows
+    idx_bytes = n_mean * Hkv * 32 * 2
+    small = Hq * 128 * 2 + 128 * 32 * 4 + Hq * 128 * 4 + k_mean * 4
+    step_bytes = idx_bytes + kv_bytes + small
+    mean_us = float(step_us.mean())
+    gbps = step_bytes / (mean_us * 1e-6) / 1e9
+    dec_us = float(parts["sparse_decode"].mean())
+    dec_bytes = kv_bytes + Hq * 128 * 2 + k_mean * 4
+    dec_gbps = dec_bytes / (dec_us * 1e-6) / 1e9
+
+    extra = {}
+    if args.isolate:
+        # each call alone: flush, event, call, event (inputs from the last timed step)
+        s_iso = warm + steps - 1
+        (kaddr, pos), (qp, od, oh), ch, kb = calls[s_iso]
+        st = stream_of()
+        iso_calls = {
+            "index_append": lambda: chk(L.ts_index_append(ctypes.c_void_p(kaddr), Pp, kip, pos, 1, Hkv, st)),
+            "score": lambda: chk(L.ts_score(qp, Pp, kip, od, oh, 1, Hq, Hkv, scp, st)),
+            "select": lambda: chk(L.ts_select(scp, od, oh, 1, Hq, Hkv, pref, idp, cnp, None, None, wsp, ws_sel_n, st)),
+            "sparse_decode": lambda: chk(L.ts_sparse_decode(qp, Kp, Vp, od, oh, idp, cnp, ch, mode, 1, Hq, Hkv, outp,
+                                                            wdp, ws_dec_n, st)),
+        }
+        iso = {}
+        for name, fn in iso_calls.items():
+            for flushed in (True, False):
+                evs = []
+                for r in range(12):
+                    if flushed:
+                        do_flush()
+                    a, b2 = ev(), ev()
+                    a.record()
+                    fn()
+                    b2.record()
+                    evs.append((a, b2))
+                torch.cuda.synchronize()
+                iso[f"{name}{'' if flushed else '_warm'}"] = round(float(np.mean([a.elapsed_time(b2) * 1e3 for a, b2 in evs[2:]])), 2)
+        extra["isolated_us"] = iso
+    if not args.no_extra:
+        # dense flash-decode over all n under the same protocol
+        n_d = n0
+        od = api.Offsets([0, n_d], dev)
+        ws_dd = torch.empty(max(api.decode_workspace_bytes(od, None, Hq, Hkv, api.MODE_VOTE), 256), dtype=torch.uint8,
+                            device=dev)
+        dts = []
+        for i in range(20):
+            do_flush()
+            a, b = ev(), ev()
+            a.record()
+            api.dense_decode(Q[0], K, V, od, ws=ws_dd, out=out)
+            b.record()
+            dts.append((a, b))
+        torch.cuda.synchronize()
+        dense_us = float(np.mean([a.elapsed_time(b) * 1e3 for a, b in dts[2:]]))
+        extra["dense_decode_us"] = round(dense_us, 2)
+        extra["dense_gbps"] = round(n_d * Hkv * 128 * 4 / (dense_us * 1e-6) / 1e9, 1)
+        # warm last-level cache (no flush), same steps
+        w_us = []
+        for i in range(min(steps, 30)):
+            a, b = ev(), ev()
+            a.record()
+            step(warm + i)
+            b.record()
+            w_us.append((a, b))
+        torch.cuda.synchronize()
+        extra["warm_llc_us"] = round(float(np.mean([a.elapsed_time(b) * 1e3 for a, b in w_us])), 2)
+        # hipGraph capture of one step at a fixed n, replayed with flushes in between
+        try:
+            s_fix = warm
+            g = torch.cuda.CUDAGraph()
+            cs = torch.cuda.Stream()
+            cs.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(cs):
+                step(s_fix)
+            torch.cuda.current_stream().wait_stream(cs)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g):
+                step(s_fix)
+            g_us = []
+            for i in range(30):
+                do_flush()
+                a, b = ev(), ev()
+                a.record()
+                g.replay()
+                b.record()
+                g_us.append((a, b))
+            torch.cuda.synchronize()
+            extra["graph_step_us"] = round(float(np.mean([a.elapsed_time(b) * 1e3 for a, b in g_us[3:]])), 2)
+        except Exception as e:  # capture is an optional side measurement
+            extra["graph_step_us"] = f"unavailable: {type(e).__name__}"
+
+    cpu = None
+    if not args.no_cpu:
+        from oracle import oracle as O
+        print("bench: timing the CPU oracle", file=sys.stderr, flush=True)
+        Kh, Vh = K[:n0 + args.cpu_steps].cpu().numpy().view(np.uint16), V[:n0 + args.cpu_steps].cpu().numpy().view(np.uint16)
+        kidx_h = O.index_project(Kh[:n0], x.P)
+        qs_h = Q.cpu().numpy().view(np.uint16)
+        t0 = time.perf_counter()
+        for s in range(args.cpu_steps):
+            n = n0 + s + 1
+            kidx_h = np.concatenate([kidx_h, O.index_project(Kh[n - 1:n], x.P)])
+            o = np.array([0, n], np.int64)
+            sc = O.score(qs_h[s], x.P, kidx_h, o, Hq, Hkv)
+            if mode == api.MODE_VOTE:
+                th = O.theta(sc, o, 9, 10)
+                vt = O.votes(sc, th, o)
+                il, cnt = O.select_vote(vt, o, bnum, bden)
+            else:
+                il, cnt = O.select_per_head(sc, o, bnum, bden)
+            O.decode(qs_h[s], Kh, Vh, o, il, cnt, mode, Hq, Hkv)
+        cpu_s = (time.perf_counter() - t0) / args.cpu_steps
+        cpu = {"value": round(cpu_s * 1e6, 1), "unit": "us/step", "cores": 1, "kind": "oracle",
+               "sample": f"{args.cpu_steps} full decode steps of the same workload (n={n0}+s, fp64 C oracle, "
+                         f"single thread, {os.cpu_count()} host cores visible)"}
+
+    res = {
+        "metric": METRIC,
+        "value": round(mean_us, 2),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warm,
+        "ms_per_step": round(mean_us / 1e3, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"LLaMA-3-8B-shaped decode layer, n={n0} cached tokens, 32 query / 8 KV heads, "
+                               f"d=128, d'=32, budget {args.budget}%, {args.mode} mode, sink 4 + local 256",
+                   "n": n0, "Hq": Hq, "Hkv": Hkv, "budget": f"{bnum}/{bden}", "mode": args.mode,
+                   "inputs": "bf16", "llc": "warm" if args.no_flush else "flushed before each step"},
+        "median_us": round(float(np.median(step_us)), 2),
+        "hbm_gbps": round(gbps, 1),
+        "pct_peak": round(100 * gbps / PEAK_GBPS, 1),
+        "algorithmic_bytes_per_step": int(step_bytes),
+        "breakdown_us": {k: round(float(v.mean()), 2) for k, v in parts.items()},
+        "roofline": {"bound": "hbm", "kernel": "ts_sparse_decode (gather decode + LSE merge)",
+                     "achieved": round(dec_gbps, 1), "peak": PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(dec_gbps / PEAK_GBPS, 4), "traffic": None,
+                     "algorithmic_bytes": int(dec_bytes), "avg_us": round(dec_us, 2)},
+        "cpu_baseline": cpu,
+        "wall_s_timed_loop": round(wall, 4),
+    }
+    res.update(extra)
+    line = json.dumps(res)
+    print(line, flush=True)
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(line + "\n")
+
+
+if __name__ == "__main__":
+    main()

@@ -74,6 +74,9 @@ typedef struct {
 /* Thread-local description of the last error (never NULL). */
 const char* ts_last_error(void);
 
+/* Row stride S of the score array: offsets[B] rounded up to a multiple of 64 (-1 if invalid). */
+int64_t ts_score_stride(const int64_t* offsets_host, int32_t B);
+
 /* K_b for one sequence of n tokens under `p` (host-only helper; -1 if p is invalid). */
 int64_t ts_budget_tokens(int64_t n, const ts_select_params* p);
 
@@ -91,10 +94,12 @@ int ts_index_append(const uint16_t* k_new, const float* P, uint16_t* k_index, in
 
 /* Index scores for every query head and cached token ([TS] "Query-Key Dot Product
  * Index", eq. Score_h(i) = q_h . k_index,h(i) / sqrt(d')):  q'_h = P^T q_h (fp32) and
- *   scores[h][t] = (q'_h / sqrt(32)) . k_index[t][h / G]    (fp32, t packed over the batch)
+ *   scores[h * S + t] = (q'_h / sqrt(32)) . k_index[t][h / G]   (fp32, t packed over the batch)
  *   q       device bf16 [B][Hq][128] (one decode query per sequence)
  *   k_index device bf16 [Ntot][Hkv][32]
- *   scores  device fp32 [Hq][Ntot], Ntot = offsets[B].                                */
+ *   scores  device fp32 [Hq][S]: row stride S = ts_score_stride(offsets_host, B), i.e.
+ *           Ntot = offsets[B] rounded up to a multiple of 64 so that rows start on 256-byte
+ *           boundaries; entries t >= Ntot of a row are not written.                       */
 int ts_score(const uint16_t* q, const float* P, const uint16_t* k_index,
              const int64_t* offsets_dev, const int64_t* offsets_host, int32_t B, int32_t Hq,
              int32_t Hkv, float* scores, hipStream_t stream);
@@ -105,15 +110,15 @@ size_t ts_select_workspace_bytes(const int64_t* offsets_host, int32_t B, int32_t
 
 /* Token selection per sequence.
  * Vote mode ([TS] "Voting Mechanism" and "Token-Level Selection", with the listing of
- * "基本的な統合パターン"): theta_h = s_(r) per (sequence, head); Vote(t) = #{h : scores[h][t]
+ * "基本的な統合パターン"): theta_h = s_(r) per (sequence, head); Vote(t) = #{h : score_h(t)
  * > theta_h} (strict); key(t) = Vote(t) if Vote(t) >= v_min else -1; the list is the forced
  * tokens F = [0, sink) U [n_b - local, n_b) plus the K_b - |F| non-forced tokens of highest
  * key, ties to the lower position, in ascending order:  idx_out[kpre_b + j], j < K_b, with
  * kpre_b = sum_{b' < b} K_b'.
  * Per-head mode ([TS] "主要な貢献" per-head selection, the "w/o Voting" ablation; [TB]
- * "Kernarchitektur"): the same rule per query head with key = scores[h][t]; -0 and +0 tie:
+ * "Kernarchitektur"): the same rule per query head with key = score_h(t); -0 and +0 tie:
  * idx_out[Hq * kpre_b + h * K_b + j].
- *   scores     device fp32 [Hq][Ntot] (as written by ts_score)
+ *   scores     device fp32 [Hq][S] (as written by ts_score, S = ts_score_stride)
  *   idx_out    device int32 (layout above)
  *   count_out  device int64 [B] (receives K_b)
  *   theta_out  nullable device fp32 [B][Hq] (vote mode: theta_h)

@@ -19,6 +19,7 @@ _i64p = ctypes.POINTER(ctypes.c_int64)
 SIGNATURES = {
     "ts_last_error": (ctypes.c_char_p, []),
     "ts_budget_tokens": (_i64, [_i64, _vp]),
+    "ts_score_stride": (_i64, [_i64p, _i32]),
     "ts_index_append": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i32, _vp]),
     "ts_score": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64p, _i32, _i32, _i32, _vp, _vp]),
     "ts_select_workspace_bytes": (_sz, [_i64p, _i32, _i32, _vp]),

@@ -76,11 +76,16 @@ def index_append(k_new, P, k_index, pos: int):
     return k_index
 
 
+def score_stride(offs: Offsets) -> int:
+    return int(_lib.load().ts_score_stride(offs.host, offs.B))
+
+
 def score(q, P, k_index, offs: Offsets, Hkv: int, out=None):
+    """Returns the [Hq][S] score array (row stride S = score_stride(offs) >= Ntot)."""
     _bf16_check(q, k_index)
     Hq = q.shape[1]
     if out is None:
-        out = torch.empty((Hq, offs.ntot), dtype=torch.float32, device=q.device)
+        out = torch.empty((Hq, score_stride(offs)), dtype=torch.float32, device=q.device)
     _check(_lib.load().ts_score(_p(q), _p(P), _p(k_index), _p(offs.dev), offs.host, offs.B, Hq, int(Hkv),
                                 _p(out), _stream()))
     return out

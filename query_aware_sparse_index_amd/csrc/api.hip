@@ -106,6 +106,11 @@ extern "C" {
 
 const char* ts_last_error(void) { return g_last_error.c_str(); }
 
+int64_t ts_score_stride(const int64_t* offsets_host, int32_t B) {
+    if (!offsets_host || B <= 0) return -1;
+    return ((offsets_host[B] + 63) / 64) * 64;
+}
+
 int64_t ts_budget_tokens(int64_t n, const ts_select_params* p) {
     qasi::SelectConfig c;
     if (n < 0 || to_cfg(p, &c) != QASI_OK) return -1;
@@ -150,13 +155,16 @@ int ts_select(const float* scores, const int64_t* offsets_dev, const int64_t* of
     if (theta_out && (reinterpret_cast<uintptr_t>(theta_out) & 3u)) return fail(QASI_ERR_INVALID, "theta_out misaligned");
     if (int r = check_heads(Hq, Hkv)) return r;
     if (int r = check_offsets(offsets_dev, offsets_host, B, true)) return r;
+    for (int b = 0; b < B; ++b)
+        if (offsets_host[b + 1] - offsets_host[b] > ((int64_t)1 << 24))
+            return fail(QASI_ERR_UNSUPPORTED, "sequence %d longer than 2^24 tokens (selection limit)", b);
     qasi::SelectConfig c;
     if (int r = to_cfg(p, &c)) return r;
     size_t need = qasi::select_workspace(offsets_host, B, Hq, c);
     if (ws_bytes < need) return fail(QASI_ERR_WORKSPACE, "ts_select needs %zu workspace bytes, got %zu", need, ws_bytes);
     if (int r = init_once()) return r;
-    return hip_status(qasi::launch_select(scores, offsets_dev, offsets_host, B, Hq, c, idx_out, count_out, theta_out,
-                                          votes_out, ws, ws_bytes, stream),
+    return hip_status(qasi::launch_select(scores, ts_score_stride(offsets_host, B), offsets_dev, offsets_host, B, Hq, c,
+                                          idx_out, count_out, theta_out, votes_out, ws, ws_bytes, stream),
                       "ts_select launch");
 }
 

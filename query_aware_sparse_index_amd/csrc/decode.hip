@@ -3,27 +3,26 @@
 // [TS] "Token-Level Selection と Sparse Attention", eq. Attention(Q, K_S, V_S) =
 // softmax(Q K_S^T / sqrt(d)) V_S over the selected tokens, which include the sink and local
 // tokens; the "output merge" of the five-step integration is the log-sum-exp merge of the
-// partial softmax results of disjoint token chunks.
+// partial softmax results of disjoint chunks of the list.
 //
 // Work item = (sequence b, chunk of kDecCH list entries) [vote / dense] or (b, KV head g,
-// chunk) [per-head].  A block has 8 waves (vote) or G waves (per-head).  In vote mode the
-// wave is tied to a KV head g and handles the G query heads of g, so each gathered K/V row
-// is read once for the whole GQA group.  A wave splits into 4 rows of 16 lanes; a row takes
-// one token at a time and each lane holds 8 of the 128 dims (one 16-byte load of K and V).
-//   phase 1: z = q . k * log2(e)/sqrt(128) for every token of the chunk (row butterfly)
-//   phase 2: per-head chunk max m and p = exp2(z - m), l = sum p (LDS)
+// chunk) [per-head].  Items are dispatched in list order, so the chip sweeps the sorted lists
+// front to back.  A block has 8 waves (vote / dense) or G waves (per-head).  In vote mode a
+// wave is tied to a KV head g and serves the G query heads of g, so each gathered K/V row is
+// read once for the whole GQA group.  A wave is 4 rows of 16 lanes; a row takes one entry at
+// a time and lane p holds dims [8p, 8p+8) (one 16-byte load of K or V).
+//   phase 1: z = q . k * log2(e)/sqrt(128) for every entry of the chunk (row butterfly)
+//   phase 2: per-head chunk max m, p = exp2(z - m), l = sum p (LDS)
 //   phase 3: acc += p * v
-// The chunk's partial (m, l, acc[128]) per head goes to the workspace; the merge kernel
+// The partial (m, l, acc[128]) of every chunk and head goes to the workspace; the merge kernel
 // combines the chunks of a sequence: out = sum_c acc_c 2^(m_c - M) / sum_c l_c 2^(m_c - M).
 #include "qasi_device.h"
 #include "qasi_internal.h"
 
 namespace qasi {
 
-constexpr int kDecCH = 64;          // list entries per chunk
-constexpr int kPartStride = 2 + kD; // m, l, acc[128]
+constexpr int kDecCH = 64;            // list entries per chunk
 constexpr float kLog2eOverSqrtD = 1.4426950408889634f / 11.313708498984761f;
-
 __device__ __forceinline__ bool find_list_chunk(const int64_t* __restrict__ counts, int B, int64_t item, int& b,
                                                 int64_t& first, int64_t& nch, int64_t& j0, int64_t& len,
                                                 int64_t& kpre) {
@@ -55,7 +54,8 @@ __global__ __launch_bounds__(512) void decode_partial_kernel(const uint16_t* __r
                                                             const int64_t* __restrict__ offsets,
                                                             const int32_t* __restrict__ idx,
                                                             const int64_t* __restrict__ counts, int B, int Hq,
-                                                            int Hkv, float* __restrict__ part) {
+                                                            int Hkv, float* __restrict__ part_acc,
+                                                            float2* __restrict__ part_ml) {
     constexpr int GH = (MODE == 1) ? 1 : G;          // query heads per wave
     constexpr int NW = (MODE == 1) ? G : 8;          // waves per block
     __shared__ float zb[((MODE == 1) ? G : 64) * kDecCH];   // [head slot][entry]
@@ -211,9 +211,9 @@ __global__ __launch_bounds__(512) void decode_partial_kernel(const uint16_t* __r
         for (int o = threadIdx.x; o < G * kD; o += NW * 64) {
             int w = o / kD, d = o % kD;
             int h = g * G + w;
-            float* dst = part + ((int64_t)blockIdx.x * Hq + h) * kPartStride;
-            dst[2 + d] = red[w * kD + d];
-            if (d == 0) { dst[0] = stat[w * 2]; dst[1] = stat[w * 2 + 1]; }
+            const int64_t slot = (int64_t)blockIdx.x * Hq + h;
+            part_acc[slot * kD + d] = red[w * kD + d];
+            if (d == 0) part_ml[slot] = make_float2(stat[w * 2], stat[w * 2 + 1]);
         }
     } else {
         for (int o = threadIdx.x; o < Hq * kD; o += NW * 64) {
@@ -221,42 +221,64 @@ __global__ __launch_bounds__(512) void decode_partial_kernel(const uint16_t* __r
             int gg = h / G, hh = h % G;
             float s = 0.f;
             for (int sb = 0; sb < nsub; ++sb) s += red[((sb * Hkv + gg) * GH + hh) * kD + d];
-            float* dst = part + ((int64_t)blockIdx.x * Hq + h) * kPartStride;
-            dst[2 + d] = s;
-            if (d == 0) { dst[0] = stat[h * 2]; dst[1] = stat[h * 2 + 1]; }
+            const int64_t slot = (int64_t)blockIdx.x * Hq + h;
+            part_acc[slot * kD + d] = s;
+            if (d == 0) part_ml[slot] = make_float2(stat[h * 2], stat[h * 2 + 1]);
         }
     }
 }
 
-// Merge of the chunk partials of each (sequence, head); block = (b, h, 16-dim slice).
-__global__ __launch_bounds__(64) void decode_merge_kernel(const float* __restrict__ part,
-                                                         const int64_t* __restrict__ counts, int B, int Hq,
-                                                         float* __restrict__ out) {
-    __shared__ float sm[4][16];
-    __shared__ float sl[4];
+// Merge of the chunk partials of each (sequence, head).  Block = (b * Hq + h, 16-dim slice);
+// its 1024 threads are (chunk group cg < 64, dim dl < 16): each thread walks every 64th chunk
+// of the sequence with independent loads, then the 64 groups are summed in LDS.
+__global__ __launch_bounds__(1024) void decode_merge_kernel(const float* __restrict__ part_acc,
+                                                           const float2* __restrict__ part_ml,
+                                                           const int64_t* __restrict__ counts, int B, int Hq,
+                                                           float* __restrict__ out) {
+    __shared__ float sa[64][17];
+    __shared__ float sl[64];
+    __shared__ float smax[16];
     const int bh = blockIdx.x, b = bh / Hq, h = bh % Hq, ds = blockIdx.y;
     int64_t first = 0;
     for (int i = 0; i < b; ++i) first += (counts[i] + kDecCH - 1) / kDecCH;
     const int64_t nch = (counts[b] + kDecCH - 1) / kDecCH;
-    const int lane = threadIdx.x;
     float M = -INFINITY;
-    for (int64_t c = lane; c < nch; c += 64) M = fmaxf(M, part[((first + c) * Hq + h) * kPartStride]);
+    for (int64_t c = threadIdx.x; c < nch; c += 1024) M = fmaxf(M, part_ml[(first + c) * Hq + h].x);
     M = wave_max(M);
-    const int ig = lane >> 4, d = ds * 16 + (lane & 15);
-    float a = 0.f, l = 0.f;
-    for (int64_t c = ig; c < nch; c += 4) {
-        const float* src = part + ((first + c) * Hq + h) * kPartStride;
-        float w = exp2f(src[0] - M);
-        a = fmaf(src[2 + d], w, a);
-        l = fmaf(src[1], w, l);
-    }
-    sm[ig][lane & 15] = a;
-    if ((lane & 15) == 0) sl[ig] = l;
+    if ((threadIdx.x & 63) == 0) smax[threadIdx.x >> 6] = M;
     __syncthreads();
-    if (lane < 16) {
-        float A = sm[0][lane] + sm[1][lane] + sm[2][lane] + sm[3][lane];
-        float L = sl[0] + sl[1] + sl[2] + sl[3];
-        out[((int64_t)b * Hq + h) * kD + ds * 16 + lane] = A / L;
+    M = smax[0];
+#pragma unroll
+    for (int w = 1; w < 16; ++w) M = fmaxf(M, smax[w]);
+    const int cg = threadIdx.x >> 4, dl = threadIdx.x & 15, d = ds * 16 + dl;
+    float a = 0.f, l = 0.f;
+    for (int64_t c0 = cg; c0 < nch; c0 += 64 * 8) {
+        float x[8], mm[8], ll[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int64_t c = c0 + 64 * u;
+            const int64_t slot = (first + (c < nch ? c : 0)) * Hq + h;
+            x[u] = part_acc[slot * kD + d];
+            const float2 ml = part_ml[slot];
+            mm[u] = ml.x;
+            ll[u] = ml.y;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if (c0 + 64 * u < nch) {
+                const float w = exp2f(mm[u] - M);
+                a = fmaf(x[u], w, a);
+                l = fmaf(ll[u], w, l);
+            }
+        }
+    }
+    sa[cg][dl] = a;
+    if (dl == 0) sl[cg] = l;
+    __syncthreads();
+    if (threadIdx.x < 16) {
+        float A = 0.f, L = 0.f;
+        for (int k = 0; k < 64; ++k) { A += sa[k][threadIdx.x]; L += sl[k]; }
+        out[((int64_t)b * Hq + h) * kD + ds * 16 + threadIdx.x] = A / L;
     }
 }
 
@@ -275,20 +297,21 @@ size_t decode_workspace(const int64_t* offsets_host, const int64_t* counts_host,
         for (int b = 0; b < B; ++b) items += (offsets_host[b + 1] - offsets_host[b] + kDecCH - 1) / kDecCH;
     WsCarver w(nullptr);
     w.take<int64_t>((size_t)B + 1);   // dense: per-sequence lengths
-    w.take<float>((size_t)items * Hq * kPartStride);
+    w.take<float>((size_t)items * Hq * kD);
+    w.take<float2>((size_t)items * Hq);
     return w.size();
 }
 
 template <int MODE>
 static hipError_t launch_partial_G(int G, dim3 grid, hipStream_t stream, const uint16_t* q, const uint16_t* K,
                                    const uint16_t* V, const int64_t* offsets, const int32_t* idx,
-                                   const int64_t* counts, int B, int Hq, int Hkv, float* part) {
+                                   const int64_t* counts, int B, int Hq, int Hkv, float* part, float2* ml) {
     dim3 block(MODE == 1 ? 64 * G : 512);
     switch (G) {
-        case 1: hipLaunchKernelGGL((decode_partial_kernel<1, MODE>), grid, block, 0, stream, q, K, V, offsets, idx, counts, B, Hq, Hkv, part); break;
-        case 2: hipLaunchKernelGGL((decode_partial_kernel<2, MODE>), grid, block, 0, stream, q, K, V, offsets, idx, counts, B, Hq, Hkv, part); break;
-        case 4: hipLaunchKernelGGL((decode_partial_kernel<4, MODE>), grid, block, 0, stream, q, K, V, offsets, idx, counts, B, Hq, Hkv, part); break;
-        case 8: hipLaunchKernelGGL((decode_partial_kernel<8, MODE>), grid, block, 0, stream, q, K, V, offsets, idx, counts, B, Hq, Hkv, part); break;
+        case 1: hipLaunchKernelGGL((decode_partial_kernel<1, MODE>), grid, block, 0, stream, q, K, V, offsets, idx, counts, B, Hq, Hkv, part, ml); break;
+        case 2: hipLaunchKernelGGL((decode_partial_kernel<2, MODE>), grid, block, 0, stream, q, K, V, offsets, idx, counts, B, Hq, Hkv, part, ml); break;
+        case 4: hipLaunchKernelGGL((decode_partial_kernel<4, MODE>), grid, block, 0, stream, q, K, V, offsets, idx, counts, B, Hq, Hkv, part, ml); break;
+        case 8: hipLaunchKernelGGL((decode_partial_kernel<8, MODE>), grid, block, 0, stream, q, K, V, offsets, idx, counts, B, Hq, Hkv, part, ml); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -306,14 +329,15 @@ hipError_t launch_sparse_decode(const uint16_t* q, const uint16_t* K, const uint
     if (decode_workspace(offsets_host, counts_host, B, Hq, Hkv, mode) > ws_bytes) return hipErrorInvalidValue;
     WsCarver w(ws);
     w.take<int64_t>((size_t)B + 1);
-    float* part = w.take<float>((size_t)list_items(counts_host, B) * Hq * kPartStride);
-    const int G = Hq / Hkv;
     const int64_t items = list_items(counts_host, B);
+    float* part = w.take<float>((size_t)items * Hq * kD);
+    float2* ml = w.take<float2>((size_t)items * Hq);
+    const int G = Hq / Hkv;
     hipError_t e;
-    if (mode == 0) e = launch_partial_G<0>(G, dim3((unsigned)items), stream, q, K, V, offsets_dev, idx, counts_dev, B, Hq, Hkv, part);
-    else e = launch_partial_G<1>(G, dim3((unsigned)items, Hkv), stream, q, K, V, offsets_dev, idx, counts_dev, B, Hq, Hkv, part);
+    if (mode == 0) e = launch_partial_G<0>(G, dim3((unsigned)items), stream, q, K, V, offsets_dev, idx, counts_dev, B, Hq, Hkv, part, ml);
+    else e = launch_partial_G<1>(G, dim3((unsigned)items, Hkv), stream, q, K, V, offsets_dev, idx, counts_dev, B, Hq, Hkv, part, ml);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_merge_kernel, dim3(B * Hq, kD / 16), dim3(64), 0, stream, part, counts_dev, B, Hq, out);
+    hipLaunchKernelGGL(decode_merge_kernel, dim3(B * Hq, kD / 16), dim3(1024), 0, stream, part, ml, counts_dev, B, Hq, out);
     return hipGetLastError();
 }
 
@@ -325,12 +349,13 @@ hipError_t launch_dense_decode(const uint16_t* q, const uint16_t* K, const uint1
     for (int b = 0; b < B; ++b) items += (offsets_host[b + 1] - offsets_host[b] + kDecCH - 1) / kDecCH;
     WsCarver w(ws);
     int64_t* lens = w.take<int64_t>((size_t)B + 1);
-    float* part = w.take<float>((size_t)items * Hq * kPartStride);
+    float* part = w.take<float>((size_t)items * Hq * kD);
+    float2* ml = w.take<float2>((size_t)items * Hq);
     hipLaunchKernelGGL(lengths_kernel, dim3(1), dim3(256), 0, stream, offsets_dev, B, lens);
     hipError_t e = launch_partial_G<2>(Hq / Hkv, dim3((unsigned)items), stream, q, K, V, offsets_dev, nullptr, lens,
-                                       B, Hq, Hkv, part);
+                                       B, Hq, Hkv, part, ml);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_merge_kernel, dim3(B * Hq, kD / 16), dim3(64), 0, stream, part, lens, B, Hq, out);
+    hipLaunchKernelGGL(decode_merge_kernel, dim3(B * Hq, kD / 16), dim3(1024), 0, stream, part, ml, lens, B, Hq, out);
     return hipGetLastError();
 }
 

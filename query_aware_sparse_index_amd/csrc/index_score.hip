@@ -9,10 +9,10 @@
 namespace qasi {
 
 // ---------------------------------------------------------------------------------------
-// Index append.  One block owns a run of (token, KV head) rows; each of its 256 threads is
-// (row slot r = tid / 32, output column c = tid % 32).  The k row is staged in LDS and the
-// projection is summed in fp64 in order j = 0..127 with fma (the bf16 x fp32 product is
-// exact in fp64), then rounded once to bf16.
+// Index append.  A block owns runs of 8 (token, KV head) rows; thread (r, c) = (tid / 32,
+// tid % 32) forms the projection of row r onto column c of P: the k row is staged in LDS, the
+// 128 entries P[j][c] are loaded up front (fully unrolled), and the sum is formed in fp64 in
+// order j = 0..127 with fma (the bf16 x fp32 product is exact in fp64), then rounded once.
 // ---------------------------------------------------------------------------------------
 constexpr int kAppendThreads = 256;
 constexpr int kAppendRows = kAppendThreads / kDP;   // 8 rows per pass
@@ -20,28 +20,30 @@ constexpr int kAppendRows = kAppendThreads / kDP;   // 8 rows per pass
 __global__ __launch_bounds__(kAppendThreads) void index_append_kernel(
     const uint16_t* __restrict__ k_new, const float* __restrict__ P, uint16_t* __restrict__ k_index,
     int64_t pos, int64_t rows, int Hkv) {
-    __shared__ float sP[kD * kDP];
-    __shared__ double sk[kAppendRows][kD];
-    for (int i = threadIdx.x; i < kD * kDP; i += kAppendThreads) sP[i] = P[i];
+    __shared__ float sk[kAppendRows][kD];
     const int r = threadIdx.x / kDP, c = threadIdx.x % kDP;
+    float pc[kD];
+#pragma unroll
+    for (int j = 0; j < kD; ++j) pc[j] = P[j * kDP + c];
     for (int64_t base = (int64_t)blockIdx.x * kAppendRows; base < rows; base += (int64_t)gridDim.x * kAppendRows) {
         __syncthreads();
-        // 8 rows x 128 bf16 = 512 uint32 pairs; 2 pairs per thread
-        for (int i = threadIdx.x; i < kAppendRows * kD / 2; i += kAppendThreads) {
-            int rr = i / (kD / 2), jj = (i % (kD / 2)) * 2;
-            int64_t row = base + rr;
-            uint32_t pr = 0;
-            if (row < rows) pr = *reinterpret_cast<const uint32_t*>(k_new + row * kD + jj);
-            sk[rr][jj] = (double)bf16_lo(pr);
-            sk[rr][jj + 1] = (double)bf16_hi(pr);
+        {   // 8 rows x 128 bf16 = 2 KiB: one 8-byte piece per thread
+            const int rr = threadIdx.x / 32, jj = (threadIdx.x % 32) * 4;
+            const int64_t row = base + rr;
+            uint2 w = make_uint2(0, 0);
+            if (row < rows) w = *reinterpret_cast<const uint2*>(k_new + row * kD + jj);
+            sk[rr][jj] = bf16_lo(w.x);
+            sk[rr][jj + 1] = bf16_hi(w.x);
+            sk[rr][jj + 2] = bf16_lo(w.y);
+            sk[rr][jj + 3] = bf16_hi(w.y);
         }
         __syncthreads();
-        int64_t row = base + r;
+        const int64_t row = base + r;
         if (row < rows) {
             double acc = 0.0;
-#pragma unroll 8
-            for (int j = 0; j < kD; ++j) acc = fma(sk[r][j], (double)sP[j * kDP + c], acc);
-            int64_t t = row / Hkv, g = row % Hkv;
+#pragma unroll
+            for (int j = 0; j < kD; ++j) acc = fma((double)sk[r][j], (double)pc[j], acc);
+            const int64_t t = row / Hkv, g = row % Hkv;
             k_index[((pos + t) * Hkv + g) * kDP + c] = f64_to_bf16_rne(acc);
         }
     }
@@ -51,7 +53,7 @@ hipError_t launch_index_append(const uint16_t* k_new, const float* P, uint16_t* 
                                int64_t T, int Hkv, hipStream_t stream) {
     int64_t rows = T * Hkv;
     int64_t blocks = (rows + kAppendRows - 1) / kAppendRows;
-    if (blocks > 4096) blocks = 4096;
+    if (blocks > 2048) blocks = 2048;
     hipLaunchKernelGGL(index_append_kernel, dim3((unsigned)blocks), dim3(kAppendThreads), 0, stream, k_new, P,
                        k_index, pos, rows, Hkv);
     return hipGetLastError();
@@ -59,15 +61,15 @@ hipError_t launch_index_append(const uint16_t* k_new, const float* P, uint16_t* 
 
 // ---------------------------------------------------------------------------------------
 // Index scores.  Work item = (sequence b, block of kScoreTB tokens of b).  The block first
-// projects the sequence's queries (q'_h = P^T q_h / sqrt(32), fp32) into LDS while its first
-// index loads are in flight.  A token's index row (Hkv x 32 bf16 = Hkv x 64 B) is read by
-// LPT = 4*Hkv lanes with one 16-byte load each: lane (g, part) holds 8 index values of KV
-// head g and forms the partial dot products of the G heads of g; a quad butterfly (DPP)
-// completes each dot product.  Scores are staged in LDS as an [Hq][kScoreTB] tile and
-// written row by row (coalesced) into scores[h][t].
+// issues its first index loads, then projects the sequence's queries (q'_h = P^T q_h /
+// sqrt(32), fp32, P and q staged in LDS).  A token's index row (Hkv x 32 bf16 = Hkv x 64 B)
+// is read by LPT = 4*Hkv lanes with one 16-byte non-temporal load each: lane (g, part)
+// holds 8 index values of KV head g and forms the partial dot products of the G heads of g;
+// a quad butterfly (DPP) completes each dot product.  Scores are staged in LDS as an
+// [Hq][kScoreTB] tile and written row by row (coalesced) into scores[h][t].
 // ---------------------------------------------------------------------------------------
-constexpr int kScoreThreads = 256;
-constexpr int kScoreTB = 256;
+constexpr int kScoreThreads = 512;
+constexpr int kScoreTB = 512;
 
 __device__ __forceinline__ bool find_item(const int64_t* __restrict__ offsets, int B, int64_t item, int tb, int& b,
                                           int64_t& t0, int64_t& len) {
@@ -99,12 +101,14 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(const uint16_t* __
     constexpr int UNR = ITERS < 8 ? ITERS : 8;
     extern __shared__ float smem[];
     float* sq = smem;                       // [Hq][32] projected queries
-    float* tile = smem + Hq * kDP;          // [Hq][kScoreTB]
+    float* sP = sq + Hq * kDP;              // [128][32]        } staging, dead once q' is formed
+    float* sqf = sP + kD * kDP;             // [Hq][128] queries }
+    float* tile = sP;                       // [Hq][kScoreTB] score tile, overlays the staging
 
     int b;
     int64_t t0, len;
     if (!find_item(offsets, B, blockIdx.x, kScoreTB, b, t0, len)) return;
-    const int64_t Ntot = offsets[B];
+    const int64_t S = score_stride(offsets[B]);
     const int64_t base_tok = offsets[b] + t0;
     const int G = Hq / HKV;
 
@@ -118,19 +122,25 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(const uint16_t* __
     for (int u = 0; u < UNR; ++u) {
         int tl = u * TPB + slot;
         kv[u] = make_uint4(0, 0, 0, 0);
-        if (tl < len) kv[u] = *reinterpret_cast<const uint4*>(k_index + ((base_tok + tl) * HKV + g) * kDP + part * 8);
+        if (tl < len) kv[u] = ld16(k_index + ((base_tok + tl) * HKV + g) * kDP + part * 8);
     }
-
+    // stage P (16 KB) and the queries of sequence b
+    for (int i = threadIdx.x; i < kD * kDP / 4; i += kScoreThreads)
+        reinterpret_cast<float4*>(sP)[i] = reinterpret_cast<const float4*>(P)[i];
+    for (int i = threadIdx.x; i < Hq * kD / 8; i += kScoreThreads) {
+        uint4 w = reinterpret_cast<const uint4*>(q + (int64_t)b * Hq * kD)[i];
+        float* d = sqf + i * 8;
+        d[0] = bf16_lo(w.x); d[1] = bf16_hi(w.x); d[2] = bf16_lo(w.y); d[3] = bf16_hi(w.y);
+        d[4] = bf16_lo(w.z); d[5] = bf16_hi(w.z); d[6] = bf16_lo(w.w); d[7] = bf16_hi(w.w);
+    }
+    __syncthreads();
     // q'_h[c] = sum_j q[b][h][j] P[j][c] / sqrt(32)
     for (int o = threadIdx.x; o < Hq * kDP; o += kScoreThreads) {
-        int h = o / kDP, c = o % kDP;
-        const uint16_t* qh = q + ((int64_t)b * Hq + h) * kD;
+        const int h = o / kDP, c = o % kDP;
+        const float* qh = sqf + h * kD;
         float acc = 0.f;
-        for (int j = 0; j < kD; j += 2) {
-            uint32_t pr = *reinterpret_cast<const uint32_t*>(qh + j);
-            acc = fmaf(bf16_lo(pr), P[j * kDP + c], acc);
-            acc = fmaf(bf16_hi(pr), P[(j + 1) * kDP + c], acc);
-        }
+#pragma unroll 16
+        for (int j = 0; j < kD; ++j) acc = fmaf(qh[j], sP[j * kDP + c], acc);
         sq[o] = acc * 0.17677669529663688f;
     }
     __syncthreads();
@@ -149,7 +159,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(const uint16_t* __
             int tn = (it0 + UNR + u) * TPB + slot;
             if (it0 + UNR < ITERS) {
                 kv[u] = make_uint4(0, 0, 0, 0);
-                if (tn < len) kv[u] = *reinterpret_cast<const uint4*>(k_index + ((base_tok + tn) * HKV + g) * kDP + part * 8);
+                if (tn < len) kv[u] = ld16(k_index + ((base_tok + tn) * HKV + g) * kDP + part * 8);
             }
             float kf[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
                            bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
@@ -168,8 +178,13 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(const uint16_t* __
     __syncthreads();
     for (int o = threadIdx.x; o < Hq * kScoreTB; o += kScoreThreads) {
         int h = o / kScoreTB, tl = o % kScoreTB;
-        if (tl < len) scores[(int64_t)h * Ntot + base_tok + tl] = tile[o];
+        if (tl < len) scores[(int64_t)h * S + base_tok + tl] = tile[o];
     }
+}
+
+static size_t score_shm(int Hq) {
+    size_t stage = (size_t)kD * kDP + (size_t)Hq * kD, tile = (size_t)Hq * kScoreTB;
+    return ((size_t)Hq * kDP + (stage > tile ? stage : tile)) * sizeof(float);
 }
 
 int64_t score_items(const int64_t* offsets_host, int B) {
@@ -182,7 +197,7 @@ hipError_t launch_score(const uint16_t* q, const float* P, const uint16_t* k_ind
                         const int64_t* offsets_host, int B, int Hq, int Hkv, float* scores, hipStream_t stream) {
     int64_t items = score_items(offsets_host, B);
     if (items == 0) return hipSuccess;
-    size_t shm = (size_t)Hq * (kDP + kScoreTB) * sizeof(float);
+    size_t shm = score_shm(Hq);
     dim3 grid((unsigned)items), block(kScoreThreads);
     switch (Hkv) {
         case 1: hipLaunchKernelGGL(score_kernel<1>, grid, block, shm, stream, q, P, k_index, offsets_dev, B, Hq, scores); break;
@@ -198,7 +213,7 @@ hipError_t launch_score(const uint16_t* q, const float* P, const uint16_t* k_ind
 
 namespace qasi {
 hipError_t init_score_kernels() {
-    const int bytes = 64 * (kDP + kScoreTB) * (int)sizeof(float);
+    const int bytes = (int)score_shm(64);
     hipError_t e = hipSuccess;
     if ((e = hipFuncSetAttribute((const void*)score_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize, bytes))) return e;
     if ((e = hipFuncSetAttribute((const void*)score_kernel<2>, hipFuncAttributeMaxDynamicSharedMemorySize, bytes))) return e;

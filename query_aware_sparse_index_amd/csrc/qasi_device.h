@@ -9,6 +9,10 @@ namespace qasi {
 constexpr int kD = 128;   // head dimension
 constexpr int kDP = 32;   // index dimension d' = d / 4
 
+// Row stride of the [Hq][S] score array: the packed token count rounded up to 64 floats, so
+// that every row starts on a 256-byte boundary.
+__host__ __device__ __forceinline__ int64_t score_stride(int64_t ntot) { return ((ntot + 63) / 64) * 64; }
+
 // bf16 bit pattern -> fp32 (exact).
 __device__ __forceinline__ float bf16_lo(uint32_t pair) { return __uint_as_float(pair << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t pair) { return __uint_as_float(pair & 0xffff0000u); }
@@ -33,6 +37,44 @@ __device__ __forceinline__ uint16_t f64_to_bf16_rne(double x) {
     }
     double q = rint(__longlong_as_double((long long)a) * 0x1p133);
     return (uint16_t)(sign | (uint32_t)q);
+}
+
+// 16-byte load of streamed data.
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// Calls f(t, value, ok) for every t in [lo, hi) of a fp32 row, with 16-byte loads for the aligned
+// body (U loads in flight per thread) and scalar loads for the unaligned head and tail.  All
+// NT threads of the block take part.
+template <int NT, int U, class F>
+__device__ __forceinline__ void for_each_f32(const float* __restrict__ row, int64_t lo, int64_t hi, F f) {
+    if (lo >= hi) return;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(row + lo);
+    int64_t head = (int64_t)(((16u - (a & 15u)) & 15u) / 4u);
+    if (head > hi - lo) head = hi - lo;
+    if (threadIdx.x < head) f(lo + threadIdx.x, row[lo + threadIdx.x], true);
+    const int64_t b0 = lo + head;
+    const int64_t nv = (hi - b0) / 4;
+    const float4* body = reinterpret_cast<const float4*>(row + b0);
+    for (int64_t v0 = threadIdx.x; v0 - threadIdx.x < nv; v0 += (int64_t)U * NT) {
+        float4 x[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t v = v0 + (int64_t)u * NT;
+            x[u] = v < nv ? body[v] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t v = v0 + (int64_t)u * NT;
+            const bool ok = v < nv;
+            const int64_t t = b0 + 4 * v;
+            f(t, x[u].x, ok);
+            f(t + 1, x[u].y, ok);
+            f(t + 2, x[u].z, ok);
+            f(t + 3, x[u].w, ok);
+        }
+    }
+    const int64_t tail0 = b0 + 4 * nv;
+    if (threadIdx.x < hi - tail0) f(tail0 + threadIdx.x, row[tail0 + threadIdx.x], true);
 }
 
 // Order-preserving map fp32 -> uint32 (ascending keys <=> ascending values); -0 maps to

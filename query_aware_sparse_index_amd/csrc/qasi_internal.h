@@ -19,15 +19,15 @@ struct SelectConfig {
     int64_t bnum, bden, sink, local, vmin, tnum, tden;
 };
 size_t select_workspace(const int64_t* offsets_host, int B, int Hq, const SelectConfig& c);
-hipError_t launch_select(const float* scores, const int64_t* offsets_dev, const int64_t* offsets_host, int B, int Hq,
-                         const SelectConfig& c, int32_t* idx_out, int64_t* count_out, float* theta_out,
+hipError_t launch_select(const float* scores, int64_t S, const int64_t* offsets_dev, const int64_t* offsets_host,
+                         int B, int Hq, const SelectConfig& c, int32_t* idx_out, int64_t* count_out, float* theta_out,
                          uint8_t* votes_out, void* ws, size_t ws_bytes, hipStream_t stream);
 int64_t budget_tokens(int64_t n, const SelectConfig& c);
-// Top-k per row of a [rows][n] fp32 array, ties to the lower position, ascending output
-// idx_out[r * k + j] (the per-head selection with no forced tokens).
+// Top-k per row of a [rows][stride] fp32 array (n valid entries per row), ties to the lower
+// position, ascending output idx_out[r * k + j] (the per-head selection with no forced tokens).
 size_t rows_topk_workspace(int rows, int64_t n, int64_t k);
-hipError_t launch_rows_topk(const float* vals, int rows, int64_t n, int64_t k, int32_t* idx_out, void* ws,
-                            size_t ws_bytes, hipStream_t stream);
+hipError_t launch_rows_topk(const float* vals, int64_t stride, int rows, int64_t n, int64_t k, int32_t* idx_out,
+                            void* ws, size_t ws_bytes, hipStream_t stream);
 
 // ---- decode
 size_t decode_workspace(const int64_t* offsets_host, const int64_t* counts_host, int B, int Hq, int Hkv, int mode);

@@ -23,9 +23,9 @@
 namespace qasi {
 
 constexpr int kOsSlice = 16384;     // keys per radix slice
-constexpr int kOsThreads = 256;
+constexpr int kOsThreads = 1024;
+constexpr int kOsMaxSL = 1024;      // slices per instance (n up to 16M tokens)
 constexpr int kChunk = 1024;        // tokens per vote / compaction block
-constexpr int kChunkThreads = 256;
 constexpr int kVoteBins = 72;       // vote keys 0 .. Hq + 1 (Hq <= 64)
 
 enum : int64_t { kFlagActive = 0, kFlagTakeNone = 1, kFlagTakeAll = 2 };
@@ -97,8 +97,8 @@ __device__ __forceinline__ int64_t forced_before(int64_t x, int64_t n, int64_t s
 // ------------------------------------------------------------------------ os_hist
 __global__ __launch_bounds__(kOsThreads) void os_hist_kernel(const float* __restrict__ scores,
                                                             const int64_t* __restrict__ offsets, int B, int Hq,
-                                                            DevCfg cfg, int SL, uint32_t* __restrict__ part1) {
-    // 4 per-wave sub-histograms, two 16-bit bins per word
+                                                            DevCfg cfg, int SL, int64_t S, uint32_t* __restrict__ part1) {
+    // 4 sub-histograms (one per group of 4 waves), two 16-bit bins per word
     __shared__ uint32_t sub[4][2048];
     const int inst = blockIdx.y, s = blockIdx.x;
     const int b = inst / Hq, h = inst % Hq;
@@ -106,17 +106,18 @@ __global__ __launch_bounds__(kOsThreads) void os_hist_kernel(const float* __rest
     OsInst oi = os_instance(offsets[b + 1] - off, cfg);
     for (int i = threadIdx.x; i < 4 * 2048; i += kOsThreads) (&sub[0][0])[i] = 0;
     __syncthreads();
-    const int64_t Ntot = offsets[B];
     int64_t lo = oi.beg + (int64_t)s * kOsSlice, hi = lo + kOsSlice;
     if (hi > oi.end) hi = oi.end;
     const bool act = oi.flag == kFlagActive && lo < hi;
     if (act) {
-        const float* row = scores + (int64_t)h * Ntot + off;
-        uint32_t* mine = sub[threadIdx.x >> 6];
-        for (int64_t t = lo + threadIdx.x; t < hi; t += kOsThreads) {
-            uint32_t d = order_key(row[t]) >> 20;
-            atomicAdd(&mine[d >> 1], (d & 1) ? 0x10000u : 1u);
-        }
+        const float* row = scores + (int64_t)h * S + off;
+        uint32_t* mine = sub[threadIdx.x >> 8];
+        for_each_f32<kOsThreads, 4>(row, lo, hi, [&](int64_t, float v, bool ok) {
+            if (ok) {
+                const uint32_t d = order_key(v) >> 20;
+                atomicAdd(&mine[d >> 1], (d & 1) ? 0x10000u : 1u);
+            }
+        });
     }
     __syncthreads();
     uint32_t* dst = part1 + ((size_t)inst * SL + s) * 2048;
@@ -126,26 +127,26 @@ __global__ __launch_bounds__(kOsThreads) void os_hist_kernel(const float* __rest
 // Finds the digit whose cumulative count (ascending) first reaches `rank` in the 4096-bin
 // LDS histogram `hist`.  Returns the digit; *below = count of keys in smaller digits.
 __device__ int find_digit_4096(const uint32_t* hist, int64_t rank, int64_t* below, int64_t* sbuf, int* tmp) {
-    // each thread owns 16 consecutive bins
+    constexpr int PER = 4096 / kOsThreads;   // consecutive bins owned by a thread
     const int tid = threadIdx.x;
     if (tid == 0) { sbuf[0] = 0; sbuf[1] = 0; }
     __syncthreads();
     int64_t local = 0;
-    for (int i = 0; i < 16; ++i) local += hist[tid * 16 + i];
-    // inclusive scan of 64-bit locals through the int scan (counts fit in 31 bits here)
+#pragma unroll
+    for (int i = 0; i < PER; ++i) local += hist[tid * PER + i];
     int total;
-    int inc = block_inclusive_scan<kOsThreads>((int)local, tmp, &total);
-    int64_t excl = inc - local;
+    const int inc = block_inclusive_scan<kOsThreads>((int)local, tmp, &total);
+    const int64_t excl = inc - local;
     if (excl < rank && rank <= inc) {
         int64_t c = excl;
-        for (int i = 0; i < 16; ++i) {
-            int64_t nc = c + hist[tid * 16 + i];
-            if (rank <= nc) { sbuf[0] = tid * 16 + i; sbuf[1] = c; break; }
+        for (int i = 0; i < PER; ++i) {
+            const int64_t nc = c + hist[tid * PER + i];
+            if (rank <= nc) { sbuf[0] = tid * PER + i; sbuf[1] = c; break; }
             c = nc;
         }
     }
     __syncthreads();
-    int d = (int)sbuf[0];
+    const int d = (int)sbuf[0];
     *below = sbuf[1];
     __syncthreads();
     return d;
@@ -154,7 +155,7 @@ __device__ int find_digit_4096(const uint32_t* hist, int64_t rank, int64_t* belo
 // --------------------------------------------------------------------- os_collect
 __global__ __launch_bounds__(kOsThreads) void os_collect_kernel(const float* __restrict__ scores,
                                                                const int64_t* __restrict__ offsets, int B, int Hq,
-                                                               DevCfg cfg, int SL, const uint32_t* __restrict__ part1,
+                                                               DevCfg cfg, int SL, int64_t S, const uint32_t* __restrict__ part1,
                                                                uint32_t* __restrict__ cand, uint32_t* __restrict__ cand_cnt,
                                                                int64_t* __restrict__ state) {
     __shared__ uint32_t hist[4096];
@@ -173,15 +174,29 @@ __global__ __launch_bounds__(kOsThreads) void os_collect_kernel(const float* __r
         return;
     }
     // sum the slice histograms (two 16-bit bins per word)
-    for (int i = threadIdx.x; i < 2048; i += kOsThreads) {
-        uint32_t a = 0, c = 0;
-        for (int k = 0; k < SL; ++k) {
-            uint32_t w = part1[((size_t)inst * SL + k) * 2048 + i];
-            a += w & 0xffffu;
-            c += w >> 16;
+    for (int i0 = threadIdx.x; i0 < 2048; i0 += 8 * kOsThreads) {
+        uint32_t a[8], c[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) { a[u] = 0; c[u] = 0; }
+        for (int k0 = 0; k0 < SL; k0 += 4) {
+            uint32_t w[4][8];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int i = i0 + u * kOsThreads;
+                    w[kk][u] = (k0 + kk < SL && i < 2048) ? part1[((size_t)inst * SL + k0 + kk) * 2048 + i] : 0u;
+                }
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                for (int u = 0; u < 8; ++u) { a[u] += w[kk][u] & 0xffffu; c[u] += w[kk][u] >> 16; }
         }
-        hist[2 * i] = a;
-        hist[2 * i + 1] = c;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int i = i0 + u * kOsThreads;
+            if (i < 2048) { hist[2 * i] = a[u]; hist[2 * i + 1] = c[u]; }
+        }
     }
     if (threadIdx.x == 0) lcnt = 0;
     __syncthreads();
@@ -195,18 +210,23 @@ __global__ __launch_bounds__(kOsThreads) void os_collect_kernel(const float* __r
         state[inst * 8 + kStR1] = oi.rank - below;
         state[inst * 8 + kStGtBin] = m - below - hist[d1];
     }
-    const int64_t Ntot = offsets[B];
     int64_t lo = oi.beg + (int64_t)s * kOsSlice, hi = lo + kOsSlice;
     if (hi > oi.end) hi = oi.end;
-    const float* row = scores + (int64_t)h * Ntot + off;
+    const float* row = scores + (int64_t)h * S + off;
     uint32_t* dst = cand + ((size_t)inst * SL + s) * kOsSlice;
-    for (int64_t t = lo + threadIdx.x; t < hi; t += kOsThreads) {
-        uint32_t k = order_key(row[t]);
-        if ((int)(k >> 20) == d1) {
-            uint32_t p = atomicAdd(&lcnt, 1u);
-            dst[p] = k;
+    const int lane = threadIdx.x & 63;
+    for_each_f32<kOsThreads, 4>(row, lo, hi, [&](int64_t, float v, bool ok) {
+        const uint32_t k = order_key(v);
+        const bool hit = ok && (int)(k >> 20) == d1;
+        const uint64_t mask = __ballot(hit);
+        if (mask) {
+            uint32_t basep = 0;
+            const int leader = __ffsll((unsigned long long)mask) - 1;
+            if (lane == leader) basep = atomicAdd(&lcnt, (uint32_t)__popcll(mask));
+            basep = __shfl(basep, leader, 64);
+            if (hit) dst[basep + __popcll(mask & ((1ull << lane) - 1ull))] = k;
         }
-    }
+    });
     __syncthreads();
     if (threadIdx.x == 0) cand_cnt[(size_t)inst * SL + s] = (lo < hi) ? lcnt : 0u;
 }
@@ -218,6 +238,7 @@ __global__ __launch_bounds__(kOsThreads) void os_final_kernel(int B, int Hq, int
     __shared__ uint32_t hist[4096];
     __shared__ int64_t sbuf[2];
     __shared__ int tmp[kOsThreads / 64];
+    __shared__ uint32_t scnt[kOsMaxSL], spre[kOsMaxSL + 1];
     const int inst = blockIdx.x;
     int64_t* st = state + inst * 8;
     if (st[kStFlag] != kFlagActive) {
@@ -227,13 +248,34 @@ __global__ __launch_bounds__(kOsThreads) void os_final_kernel(int B, int Hq, int
     const uint32_t d1 = (uint32_t)st[kStD1];
     int64_t r = st[kStR1];
     int64_t gt = st[kStGtBin];
+    // candidate counts of all slices, and their prefix, in LDS
+    for (int k = threadIdx.x; k < SL; k += kOsThreads) scnt[k] = cand_cnt[(size_t)inst * SL + k];
     // digit 2: bits 19..8
     for (int i = threadIdx.x; i < 4096; i += kOsThreads) hist[i] = 0;
     __syncthreads();
-    for (int k = 0; k < SL; ++k) {
-        const uint32_t* src = cand + ((size_t)inst * SL + k) * kOsSlice;
-        uint32_t cnt = cand_cnt[(size_t)inst * SL + k];
-        for (uint32_t j = threadIdx.x; j < cnt; j += kOsThreads) atomicAdd(&hist[(src[j] >> 8) & 0xfffu], 1u);
+    if (threadIdx.x == 0) {
+        uint32_t acc = 0;
+        for (int k = 0; k < SL; ++k) { spre[k] = acc; acc += scnt[k]; }
+        spre[SL] = acc;
+    }
+    __syncthreads();
+    const uint32_t total = spre[SL];
+    const uint32_t* cbase = cand + (size_t)inst * SL * kOsSlice;
+    auto cand_at = [&](uint32_t gi) {   // global candidate index -> key
+        int lo2 = 0, hi2 = SL - 1;
+        while (lo2 < hi2) {
+            const int mid = (lo2 + hi2 + 1) >> 1;
+            if (spre[mid] <= gi) lo2 = mid; else hi2 = mid - 1;
+        }
+        return cbase[(size_t)lo2 * kOsSlice + (gi - spre[lo2])];
+    };
+    for (uint32_t j0 = threadIdx.x; j0 < total; j0 += 8 * kOsThreads) {
+        uint32_t key[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) key[u] = (j0 + u * kOsThreads < total) ? cand_at(j0 + u * kOsThreads) : 0u;
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (j0 + u * kOsThreads < total) atomicAdd(&hist[(key[u] >> 8) & 0xfffu], 1u);
     }
     __syncthreads();
     int64_t below;
@@ -255,13 +297,13 @@ __global__ __launch_bounds__(kOsThreads) void os_final_kernel(int B, int Hq, int
     // digit 3: bits 7..0 among keys with prefix (d1, d2)
     for (int i = threadIdx.x; i < 4096; i += kOsThreads) hist[i] = 0;
     __syncthreads();
-    for (int k = 0; k < SL; ++k) {
-        const uint32_t* src = cand + ((size_t)inst * SL + k) * kOsSlice;
-        uint32_t cnt = cand_cnt[(size_t)inst * SL + k];
-        for (uint32_t j = threadIdx.x; j < cnt; j += kOsThreads) {
-            uint32_t key = src[j];
-            if ((int)((key >> 8) & 0xfffu) == d2) atomicAdd(&hist[key & 0xffu], 1u);
-        }
+    for (uint32_t j0 = threadIdx.x; j0 < total; j0 += 8 * kOsThreads) {
+        uint32_t key[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) key[u] = (j0 + u * kOsThreads < total) ? cand_at(j0 + u * kOsThreads) : 0u;
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (j0 + u * kOsThreads < total && (int)((key[u] >> 8) & 0xfffu) == d2) atomicAdd(&hist[key[u] & 0xffu], 1u);
     }
     __syncthreads();
     const int d3 = find_digit_4096(hist, r, &below, sbuf, tmp);   // bins >= 256 are empty
@@ -311,228 +353,237 @@ __device__ __forceinline__ int64_t kpre_of(const int64_t* __restrict__ offsets, 
 }
 
 // -------------------------------------------------------------------------- votes
-// Vote(t) = #{h : scores[h][t] > theta_h} (strict, IEEE compare so -0 == +0); the key of a
-// non-forced token is Vote + 1 if Vote >= v_min, else 0 (the listing's -1); forced tokens
-// get 255.  Each block also counts the keys of its non-forced tokens.
-__global__ __launch_bounds__(kChunkThreads) void vote_kernel(const float* __restrict__ scores,
-                                                            const int64_t* __restrict__ offsets, int B, int Hq,
-                                                            DevCfg cfg, const int64_t* __restrict__ state,
-                                                            uint8_t* __restrict__ votes, uint8_t* __restrict__ keys,
-                                                            uint32_t* __restrict__ hist) {
+// One thread per token (1024-token blocks).  Vote(t) = #{h : scores[h][t] > theta_h}
+// (strict, IEEE compare so -0 == +0).  The key of a non-forced token is Vote + 1 if
+// Vote >= v_min, else 0 (the listing's -1); forced tokens get 255.  Each block also counts
+// the keys of its non-forced tokens (one histogram per block).
+__global__ __launch_bounds__(kChunk) void vote_kernel(const float* __restrict__ scores,
+                                                     const int64_t* __restrict__ offsets, int B, int Hq,
+                                                     DevCfg cfg, int64_t S, const int64_t* __restrict__ state,
+                                                     uint8_t* __restrict__ votes, uint8_t* __restrict__ keys,
+                                                     uint32_t* __restrict__ hist) {
     __shared__ float th[64];
-    __shared__ uint32_t lh[kVoteBins];
+    __shared__ uint32_t lh[kChunk / 64][kVoteBins];
     int b;
     int64_t first, nch, t0, len;
     if (!find_chunk(offsets, B, blockIdx.x, b, first, nch, t0, len)) return;
-    const int64_t off = offsets[b], n = offsets[b + 1] - off, Ntot = offsets[B];
-    for (int h = threadIdx.x; h < Hq; h += kChunkThreads) th[h] = key_to_float((uint32_t)state[((int64_t)b * Hq + h) * 8 + kStKey]);
-    for (int i = threadIdx.x; i < kVoteBins; i += kChunkThreads) lh[i] = 0;
+    const int64_t off = offsets[b], n = offsets[b + 1] - off;
+    for (int h = threadIdx.x; h < Hq; h += kChunk) th[h] = key_to_float((uint32_t)state[((int64_t)b * Hq + h) * 8 + kStKey]);
+    for (int i = threadIdx.x; i < (kChunk / 64) * kVoteBins; i += kChunk) (&lh[0][0])[i] = 0;
     __syncthreads();
-    for (int i = threadIdx.x; i < len; i += kChunkThreads) {
-        int64_t t = t0 + i;
+    const int64_t i = threadIdx.x;
+    const int64_t t = t0 + i;
+    if (i < len) {
+        const float* col = scores + off + t;
         int v = 0;
-        for (int h = 0; h < Hq; ++h) v += scores[(int64_t)h * Ntot + off + t] > th[h] ? 1 : 0;
+        for (int h0 = 0; h0 < Hq; h0 += 16) {
+            float sv[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) sv[u] = (h0 + u < Hq) ? col[(int64_t)(h0 + u) * S] : 0.f;
+#pragma unroll
+            for (int u = 0; u < 16; ++u) v += (h0 + u < Hq && sv[u] > th[h0 + u]) ? 1 : 0;
+        }
         votes[off + t] = (uint8_t)v;
         uint8_t key;
         if (is_forced(t, n, cfg.sink, cfg.local)) key = 255;
         else {
             key = (uint8_t)(v >= cfg.vmin ? v + 1 : 0);
-            atomicAdd(&lh[key], 1u);
+            atomicAdd(&lh[threadIdx.x >> 6][key], 1u);
         }
         keys[off + t] = key;
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < kVoteBins; i += kChunkThreads) hist[(size_t)blockIdx.x * kVoteBins + i] = lh[i];
+    for (int k = threadIdx.x; k < kVoteBins; k += kChunk) {
+        uint32_t a = 0;
+#pragma unroll
+        for (int w = 0; w < kChunk / 64; ++w) a += lh[w][k];
+        hist[(size_t)blockIdx.x * kVoteBins + k] = a;
+    }
+}
+
+// Sums the key histograms of the blocks of sequence b into tot[] and those of the blocks
+// before block c into bef[] (rows staged through LDS, 128 blocks at a time).
+__device__ void sum_block_hists(const uint32_t* __restrict__ hist, int64_t first, int64_t nch, int64_t c,
+                                uint32_t (*stage)[kVoteBins], uint32_t* tot, uint32_t* bef) {
+    if (threadIdx.x < kVoteBins) { tot[threadIdx.x] = 0; bef[threadIdx.x] = 0; }
+    for (int64_t k0 = 0; k0 < nch; k0 += 128) {
+        const int64_t rows = nch - k0 < 128 ? nch - k0 : 128;
+        __syncthreads();
+        const int64_t ne = rows * kVoteBins;
+        for (int64_t e0 = threadIdx.x; e0 < ne; e0 += 16 * (int64_t)blockDim.x) {
+            uint32_t x[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const int64_t e = e0 + (int64_t)u * blockDim.x;
+                x[u] = e < ne ? hist[(size_t)(first + k0) * kVoteBins + e] : 0u;
+            }
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const int64_t e = e0 + (int64_t)u * blockDim.x;
+                if (e < ne) stage[e / kVoteBins][e % kVoteBins] = x[u];
+            }
+        }
+        __syncthreads();
+        if (threadIdx.x < kVoteBins) {
+            uint32_t a = 0, p = 0;
+            for (int64_t r = 0; r < rows; ++r) {
+                const uint32_t x = stage[r][threadIdx.x];
+                a += x;
+                if (k0 + r < c) p += x;
+            }
+            tot[threadIdx.x] += a;
+            bef[threadIdx.x] += p;
+        }
+    }
+    __syncthreads();
 }
 
 // ------------------------------------------------------------ vote compaction
-__global__ __launch_bounds__(kChunkThreads) void compact_vote_kernel(const int64_t* __restrict__ offsets, int B,
-                                                                    DevCfg cfg, const uint8_t* __restrict__ keys,
-                                                                    const uint32_t* __restrict__ hist,
-                                                                    int32_t* __restrict__ idx_out,
-                                                                    int64_t* __restrict__ count_out) {
+// One thread per token.  The boundary key v* is the largest key whose suffix count reaches
+// need = K - |F|; every non-forced token above v*, the first (need - #above) tokens equal to
+// v* in position order and every forced token are written, ascending, at their rank.
+__global__ __launch_bounds__(kChunk) void compact_vote_kernel(const int64_t* __restrict__ offsets, int B,
+                                                             DevCfg cfg, const uint8_t* __restrict__ keys,
+                                                             const uint32_t* __restrict__ hist,
+                                                             int32_t* __restrict__ idx_out,
+                                                             int64_t* __restrict__ count_out) {
+    __shared__ uint32_t stage[128][kVoteBins];
     __shared__ uint32_t tot[kVoteBins], bef[kVoteBins];
     __shared__ int64_t sh[4];
-    __shared__ int tmp[kChunkThreads / 64];
+    __shared__ int tmp[kChunk / 64];
     int b;
     int64_t first, nch, t0, len;
     if (!find_chunk(offsets, B, blockIdx.x, b, first, nch, t0, len)) return;
     const int64_t off = offsets[b], n = offsets[b + 1] - off;
     const int64_t c = blockIdx.x - first;
-    for (int v = threadIdx.x; v < kVoteBins; v += kChunkThreads) {
-        uint32_t a = 0, p = 0;
-        for (int64_t k = 0; k < nch; ++k) {
-            uint32_t x = hist[(size_t)(first + k) * kVoteBins + v];
-            a += x;
-            if (k < c) p += x;
-        }
-        tot[v] = a;
-        bef[v] = p;
+    sum_block_hists(hist, first, nch, c, stage, tot, bef);
+    const int64_t K = budget_k(n, cfg.bnum, cfg.bden, cfg.sink, cfg.local);
+    const int64_t need = K - forced_before(n, n, cfg.sink, cfg.local);
+    // suffix counts over the keys (thread t holds key kVoteBins - 1 - t); v* is the largest
+    // key whose suffix count reaches `need` (none when need == 0)
+    {
+        const int t = threadIdx.x;
+        const int v = kVoteBins - 1 - t;
+        const int cnt = (t < kVoteBins) ? (int)tot[v] : 0;
+        int all;
+        const int incl = block_inclusive_scan<kChunk>(cnt, tmp, &all);
+        if (t == 0) { sh[0] = kVoteBins; sh[1] = 0; }
+        __syncthreads();
+        if (need > 0 && t < kVoteBins && incl >= need && incl - cnt < need) { sh[0] = v; sh[1] = incl - cnt; }
+        __syncthreads();
     }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const int64_t K = budget_k(n, cfg.bnum, cfg.bden, cfg.sink, cfg.local);
-        const int64_t fb = forced_before(n, n, cfg.sink, cfg.local);
-        const int64_t need = K - fb;
-        int vs = kVoteBins;   // no non-forced token is taken when need == 0
-        int64_t gt = 0;
-        if (need > 0) {
-            int64_t cum = 0;
-            for (int v = kVoteBins - 1; v >= 0; --v) {
-                if (cum + tot[v] >= need) { vs = v; break; }
-                cum += tot[v];
-            }
-            gt = cum;
-        }
-        int64_t gtb = 0;
-        for (int v = vs + 1; v < kVoteBins; ++v) gtb += bef[v];
-        int64_t eqb = vs < kVoteBins ? bef[vs] : 0;
-        int64_t need_eq = need - gt;
-        sh[0] = vs;
-        sh[1] = need_eq;
-        sh[2] = eqb;
-        sh[3] = forced_before(t0, n, cfg.sink, cfg.local) + gtb + (eqb < need_eq ? eqb : need_eq);
-        if (c == 0) count_out[b] = K;
-    }
-    __syncthreads();
     const int vs = (int)sh[0];
-    const int64_t need_eq = sh[1], eqb = sh[2], base = sh[3];
-    const int64_t kpre = kpre_of(offsets, b, cfg);
-    // each thread owns 4 consecutive tokens of the chunk
-    uint8_t kk[4];
-    int eqf[4];
-    int neq = 0;
-    for (int j = 0; j < 4; ++j) {
-        int64_t i = (int64_t)threadIdx.x * 4 + j;
-        kk[j] = i < len ? keys[off + t0 + i] : 0;
-        eqf[j] = (i < len && kk[j] != 255 && kk[j] == vs) ? 1 : 0;
-        neq += eqf[j];
-    }
-    int tot_eq;
-    int eq_inc = block_inclusive_scan<kChunkThreads>(neq, tmp, &tot_eq);
-    int eq_rank = eq_inc - neq;
-    int self[4];
-    int nsel = 0;
-    for (int j = 0; j < 4; ++j) {
-        int64_t i = (int64_t)threadIdx.x * 4 + j;
-        int s = 0;
-        if (i < len) {
-            if (kk[j] == 255) s = 1;
-            else if (kk[j] > vs && vs < kVoteBins) s = 1;
-            else if (eqf[j]) { s = (eqb + eq_rank < need_eq) ? 1 : 0; ++eq_rank; }
+    const int64_t gt = sh[1];
+    {
+        const int t = threadIdx.x;
+        const int x = (t < kVoteBins && t > vs) ? (int)bef[t] : 0;
+        int gtb;
+        block_inclusive_scan<kChunk>(x, tmp, &gtb);
+        if (t == 0) {
+            const int64_t eqb = vs < kVoteBins ? bef[vs] : 0;
+            const int64_t need_eq = need - gt;
+            sh[1] = need_eq;
+            sh[2] = eqb;
+            sh[3] = forced_before(t0, n, cfg.sink, cfg.local) + gtb + (eqb < need_eq ? eqb : need_eq);
+            if (c == 0) count_out[b] = K;
         }
-        self[j] = s;
-        nsel += s;
+    }
+    __syncthreads();
+    const int64_t need_eq = sh[1], eqb = sh[2], base = sh[3];
+    const int64_t i = threadIdx.x;
+    const uint8_t kk = i < len ? keys[off + t0 + i] : 0;
+    const int eqf = (i < len && kk != 255 && kk == vs) ? 1 : 0;
+    int tot_eq;
+    const int eq_rank = block_inclusive_scan<kChunk>(eqf, tmp, &tot_eq) - eqf;
+    int sel = 0;
+    if (i < len) {
+        if (kk == 255) sel = 1;
+        else if (vs < kVoteBins && kk > vs) sel = 1;
+        else if (eqf) sel = (eqb + eq_rank < need_eq) ? 1 : 0;
     }
     int tot_sel;
-    int sel_inc = block_inclusive_scan<kChunkThreads>(nsel, tmp, &tot_sel);
-    int64_t p = base + sel_inc - nsel;
-    const int64_t K = budget_k(n, cfg.bnum, cfg.bden, cfg.sink, cfg.local);
-    for (int j = 0; j < 4; ++j) {
-        if (self[j] && p < K) idx_out[kpre + p] = (int32_t)(t0 + (int64_t)threadIdx.x * 4 + j);
-        p += self[j];
-    }
+    const int64_t p = base + block_inclusive_scan<kChunk>(sel, tmp, &tot_sel) - sel;
+    const int64_t kpre = kpre_of(offsets, b, cfg);
+    if (sel && p < K) idx_out[kpre + p] = (int32_t)(t0 + i);
 }
 
 // --------------------------------------------------------- per-head compaction
-// cnt[(h * nitems + item) * 2 + {0: above, 1: equal}] for the non-forced tokens of a chunk.
-__global__ __launch_bounds__(kChunkThreads) void ph_count_kernel(const float* __restrict__ scores,
-                                                                const int64_t* __restrict__ offsets, int B, int Hq,
-                                                                DevCfg cfg, const int64_t* __restrict__ state,
-                                                                int64_t nitems, uint32_t* __restrict__ cnt) {
-    __shared__ int tmp[kChunkThreads / 64];
+// cnt[(h * nitems + item) * 2 + {0: above, 1: equal}] for the non-forced tokens of a block.
+__global__ __launch_bounds__(kChunk) void ph_count_kernel(const float* __restrict__ scores,
+                                                         const int64_t* __restrict__ offsets, int B, int Hq,
+                                                         DevCfg cfg, int64_t S, const int64_t* __restrict__ state,
+                                                         int64_t nitems, uint32_t* __restrict__ cnt) {
+    __shared__ int tmp[kChunk / 64];
     int b;
     int64_t first, nch, t0, len;
     if (!find_chunk(offsets, B, blockIdx.x, b, first, nch, t0, len)) return;
     const int h = blockIdx.y;
-    const int64_t off = offsets[b], n = offsets[b + 1] - off, Ntot = offsets[B];
+    const int64_t off = offsets[b], n = offsets[b + 1] - off;
     const int64_t* st = state + ((int64_t)b * Hq + h) * 8;
     const uint32_t ks = (uint32_t)st[kStKey];
     const bool act = st[kStFlag] == kFlagActive;
+    const int64_t i = threadIdx.x, t = t0 + i;
     int gt = 0, eq = 0;
-    if (act) {
-        for (int64_t i = threadIdx.x; i < len; i += kChunkThreads) {
-            int64_t t = t0 + i;
-            if (is_forced(t, n, cfg.sink, cfg.local)) continue;
-            uint32_t k = order_key(scores[(int64_t)h * Ntot + off + t]);
-            gt += k > ks;
-            eq += k == ks;
-        }
+    if (act && i < len && !is_forced(t, n, cfg.sink, cfg.local)) {
+        const uint32_t k = order_key(scores[(int64_t)h * S + off + t]);
+        gt = k > ks;
+        eq = k == ks;
     }
     int tg, te;
-    block_inclusive_scan<kChunkThreads>(gt, tmp, &tg);
-    block_inclusive_scan<kChunkThreads>(eq, tmp, &te);
+    block_inclusive_scan<kChunk>(gt, tmp, &tg);
+    block_inclusive_scan<kChunk>(eq, tmp, &te);
     if (threadIdx.x == 0) {
         cnt[((size_t)h * nitems + blockIdx.x) * 2 + 0] = (uint32_t)tg;
         cnt[((size_t)h * nitems + blockIdx.x) * 2 + 1] = (uint32_t)te;
     }
 }
 
-__global__ __launch_bounds__(kChunkThreads) void ph_compact_kernel(const float* __restrict__ scores,
-                                                                  const int64_t* __restrict__ offsets, int B, int Hq,
-                                                                  DevCfg cfg, const int64_t* __restrict__ state,
-                                                                  int64_t nitems, const uint32_t* __restrict__ cnt,
-                                                                  int32_t* __restrict__ idx_out,
-                                                                  int64_t* __restrict__ count_out) {
-    __shared__ int64_t sh[2];
-    __shared__ int tmp[kChunkThreads / 64];
+__global__ __launch_bounds__(kChunk) void ph_compact_kernel(const float* __restrict__ scores,
+                                                           const int64_t* __restrict__ offsets, int B, int Hq,
+                                                           DevCfg cfg, int64_t S, const int64_t* __restrict__ state,
+                                                           int64_t nitems, const uint32_t* __restrict__ cnt,
+                                                           int32_t* __restrict__ idx_out,
+                                                           int64_t* __restrict__ count_out) {
+    __shared__ int tmp[kChunk / 64];
     int b;
     int64_t first, nch, t0, len;
     if (!find_chunk(offsets, B, blockIdx.x, b, first, nch, t0, len)) return;
     const int h = blockIdx.y;
-    const int64_t off = offsets[b], n = offsets[b + 1] - off, Ntot = offsets[B];
+    const int64_t off = offsets[b], n = offsets[b + 1] - off;
     const int64_t c = blockIdx.x - first;
     const int64_t* st = state + ((int64_t)b * Hq + h) * 8;
     const int64_t flag = st[kStFlag];
     const uint32_t ks = (uint32_t)st[kStKey];
     const int64_t K = budget_k(n, cfg.bnum, cfg.bden, cfg.sink, cfg.local);
     const int64_t need_eq = flag == kFlagActive ? st[kStNeed] - st[kStGt] : 0;
-    if (threadIdx.x == 0) {
-        int64_t gtb = 0, eqb = 0;
-        for (int64_t k = 0; k < c; ++k) {
-            gtb += cnt[((size_t)h * nitems + first + k) * 2 + 0];
-            eqb += cnt[((size_t)h * nitems + first + k) * 2 + 1];
-        }
-        int64_t fb = forced_before(t0, n, cfg.sink, cfg.local);
-        int64_t base;
-        if (flag == kFlagTakeAll) base = t0;
-        else if (flag == kFlagTakeNone) base = fb;
-        else base = fb + gtb + (eqb < need_eq ? eqb : need_eq);
-        sh[0] = base;
-        sh[1] = eqb;
-        if (c == 0 && h == 0) count_out[b] = K;
+    // counts of the blocks before this one (one block per thread, then a block sum)
+    int gtb_i = 0, eqb_i = 0;
+    for (int64_t k = threadIdx.x; k < c; k += kChunk) {
+        gtb_i += (int)cnt[((size_t)h * nitems + first + k) * 2 + 0];
+        eqb_i += (int)cnt[((size_t)h * nitems + first + k) * 2 + 1];
     }
-    __syncthreads();
-    const int64_t base = sh[0], eqb = sh[1];
-    int sel[4], eqf[4];
-    uint32_t kk[4];
-    int neq = 0;
-    for (int j = 0; j < 4; ++j) {
-        int64_t i = (int64_t)threadIdx.x * 4 + j;
-        int64_t t = t0 + i;
-        bool in = i < len;
-        bool f = in && is_forced(t, n, cfg.sink, cfg.local);
-        kk[j] = (in && !f) ? order_key(scores[(int64_t)h * Ntot + off + t]) : 0u;
-        eqf[j] = (in && !f && flag == kFlagActive && kk[j] == ks) ? 1 : 0;
-        neq += eqf[j];
-        sel[j] = in ? (f ? 1 : (flag == kFlagTakeAll ? 1 : (flag == kFlagActive && kk[j] > ks ? 1 : 0))) : 0;
-    }
+    int gtb, eqb;
+    block_inclusive_scan<kChunk>(gtb_i, tmp, &gtb);
+    block_inclusive_scan<kChunk>(eqb_i, tmp, &eqb);
+    const int64_t fb = forced_before(t0, n, cfg.sink, cfg.local);
+    int64_t base;
+    if (flag == kFlagTakeAll) base = t0;
+    else if (flag == kFlagTakeNone) base = fb;
+    else base = fb + gtb + ((int64_t)eqb < need_eq ? (int64_t)eqb : need_eq);
+    if (c == 0 && h == 0 && threadIdx.x == 0) count_out[b] = K;
+
+    const int64_t i = threadIdx.x, t = t0 + i;
+    const bool in = i < len;
+    const bool f = in && is_forced(t, n, cfg.sink, cfg.local);
+    const uint32_t kk = (in && !f) ? order_key(scores[(int64_t)h * S + off + t]) : 0u;
+    const int eqf = (in && !f && flag == kFlagActive && kk == ks) ? 1 : 0;
     int tot;
-    int eq_inc = block_inclusive_scan<kChunkThreads>(neq, tmp, &tot);
-    int eq_rank = eq_inc - neq;
-    int nsel = 0;
-    for (int j = 0; j < 4; ++j) {
-        if (eqf[j]) { sel[j] = (eqb + eq_rank < need_eq) ? 1 : 0; ++eq_rank; }
-        nsel += sel[j];
-    }
-    int sel_inc = block_inclusive_scan<kChunkThreads>(nsel, tmp, &tot);
-    int64_t p = base + sel_inc - nsel;
+    const int eq_rank = block_inclusive_scan<kChunk>(eqf, tmp, &tot) - eqf;
+    int sel = in ? (f ? 1 : (flag == kFlagTakeAll ? 1 : (flag == kFlagActive && kk > ks ? 1 : 0))) : 0;
+    if (eqf) sel = ((int64_t)eqb + eq_rank < need_eq) ? 1 : 0;
+    const int64_t p = base + block_inclusive_scan<kChunk>(sel, tmp, &tot) - sel;
     const int64_t kpre = kpre_of(offsets, b, cfg);
-    int32_t* dst = idx_out + Hq * kpre + (int64_t)h * K;
-    for (int j = 0; j < 4; ++j) {
-        if (sel[j] && p < K) dst[p] = (int32_t)(t0 + (int64_t)threadIdx.x * 4 + j);
-        p += sel[j];
-    }
+    if (sel && p < K) idx_out[Hq * kpre + (int64_t)h * K + p] = (int32_t)t;
 }
 
 // ------------------------------------------------------------------- host side
@@ -590,31 +641,31 @@ size_t select_workspace(const int64_t* offsets_host, int B, int Hq, const Select
     return select_layout(nullptr, offsets_host, B, Hq, c).bytes;
 }
 
-hipError_t launch_select(const float* scores, const int64_t* offsets_dev, const int64_t* offsets_host, int B, int Hq,
-                         const SelectConfig& c, int32_t* idx_out, int64_t* count_out, float* theta_out,
+hipError_t launch_select(const float* scores, int64_t S, const int64_t* offsets_dev, const int64_t* offsets_host,
+                         int B, int Hq, const SelectConfig& c, int32_t* idx_out, int64_t* count_out, float* theta_out,
                          uint8_t* votes_out, void* ws, size_t ws_bytes, hipStream_t stream) {
     SelectLayout L = select_layout(ws, offsets_host, B, Hq, c);
     if (L.bytes > ws_bytes) return hipErrorInvalidValue;
     DevCfg d = dev_cfg(c);
     const unsigned inst = (unsigned)(B * Hq);
     hipLaunchKernelGGL(os_hist_kernel, dim3(L.SL, inst), dim3(kOsThreads), 0, stream, scores, offsets_dev, B, Hq, d,
-                       L.SL, L.part1);
+                       L.SL, S, L.part1);
     hipLaunchKernelGGL(os_collect_kernel, dim3(L.SL, inst), dim3(kOsThreads), 0, stream, scores, offsets_dev, B, Hq, d,
-                       L.SL, L.part1, L.cand, L.cand_cnt, L.state);
+                       L.SL, S, L.part1, L.cand, L.cand_cnt, L.state);
     hipLaunchKernelGGL(os_final_kernel, dim3(inst), dim3(kOsThreads), 0, stream, B, Hq, L.SL, L.cand, L.cand_cnt,
                        L.state, c.mode == 0 ? theta_out : nullptr);
     if (L.nitems == 0) return hipGetLastError();
     if (c.mode == 0) {
         uint8_t* votes = votes_out ? votes_out : L.votes;
-        hipLaunchKernelGGL(vote_kernel, dim3((unsigned)L.nitems), dim3(kChunkThreads), 0, stream, scores, offsets_dev,
-                           B, Hq, d, L.state, votes, L.keys, L.hist);
-        hipLaunchKernelGGL(compact_vote_kernel, dim3((unsigned)L.nitems), dim3(kChunkThreads), 0, stream, offsets_dev,
+        hipLaunchKernelGGL(vote_kernel, dim3((unsigned)L.nitems), dim3(kChunk), 0, stream, scores, offsets_dev,
+                           B, Hq, d, S, L.state, votes, L.keys, L.hist);
+        hipLaunchKernelGGL(compact_vote_kernel, dim3((unsigned)L.nitems), dim3(kChunk), 0, stream, offsets_dev,
                            B, d, L.keys, L.hist, idx_out, count_out);
     } else {
-        hipLaunchKernelGGL(ph_count_kernel, dim3((unsigned)L.nitems, Hq), dim3(kChunkThreads), 0, stream, scores,
-                           offsets_dev, B, Hq, d, L.state, L.nitems, L.phcnt);
-        hipLaunchKernelGGL(ph_compact_kernel, dim3((unsigned)L.nitems, Hq), dim3(kChunkThreads), 0, stream, scores,
-                           offsets_dev, B, Hq, d, L.state, L.nitems, L.phcnt, idx_out, count_out);
+        hipLaunchKernelGGL(ph_count_kernel, dim3((unsigned)L.nitems, Hq), dim3(kChunk), 0, stream, scores,
+                           offsets_dev, B, Hq, d, S, L.state, L.nitems, L.phcnt);
+        hipLaunchKernelGGL(ph_compact_kernel, dim3((unsigned)L.nitems, Hq), dim3(kChunk), 0, stream, scores,
+                           offsets_dev, B, Hq, d, S, L.state, L.nitems, L.phcnt, idx_out, count_out);
     }
     return hipGetLastError();
 }
@@ -646,8 +697,8 @@ size_t rows_topk_workspace(int rows, int64_t n, int64_t k) {
     return w.size();
 }
 
-hipError_t launch_rows_topk(const float* vals, int rows, int64_t n, int64_t k, int32_t* idx_out, void* ws,
-                            size_t ws_bytes, hipStream_t stream) {
+hipError_t launch_rows_topk(const float* vals, int64_t stride, int rows, int64_t n, int64_t k, int32_t* idx_out,
+                            void* ws, size_t ws_bytes, hipStream_t stream) {
     if (rows_topk_workspace(rows, n, k) > ws_bytes) return hipErrorInvalidValue;
     int64_t oh[2] = {0, n};
     SelectConfig c = rows_cfg(n, k);
@@ -657,7 +708,7 @@ hipError_t launch_rows_topk(const float* vals, int rows, int64_t n, int64_t k, i
     size_t sb = select_workspace(oh, 1, rows, c);
     void* sws = w.take<char>(sb);
     hipLaunchKernelGGL(set_offsets_kernel, dim3(1), dim3(64), 0, stream, od, n);
-    return launch_select(vals, od, oh, 1, rows, c, idx_out, cnt, nullptr, nullptr, sws, sb, stream);
+    return launch_select(vals, stride, od, oh, 1, rows, c, idx_out, cnt, nullptr, nullptr, sws, sb, stream);
 }
 
 }  // namespace qasi

@@ -168,15 +168,19 @@ __global__ void snap_lse_kernel(const float2* __restrict__ pstat, int64_t nblk, 
     lse[gr] = M + log2f(L);
 }
 
-// pooled[g][j] = ((imp[j-1] + imp[j]) + imp[j+1]) / 3, zero outside [0, n)
-__global__ void snap_pool_kernel(const float* __restrict__ imp, int64_t n, int Hkv, float* __restrict__ pooled) {
+// pooled[g][j] = ((imp[j-1] + imp[j]) + imp[j+1]) / 3, zero outside [0, n); written with row
+// stride `ps` into the workspace and, when requested, densely into pooled_out.
+__global__ void snap_pool_kernel(const float* __restrict__ imp, int64_t n, int Hkv, int64_t ps,
+                                 float* __restrict__ pooled, float* __restrict__ pooled_out) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= n * Hkv) return;
     const int64_t g = i / n, j = i % n;
     const float* row = imp + g * n;
     float a = j > 0 ? row[j - 1] : 0.f;
     float c = j + 1 < n ? row[j + 1] : 0.f;
-    pooled[i] = ((a + row[j]) + c) / 3.0f;
+    const float v = ((a + row[j]) + c) / 3.0f;
+    pooled[g * ps + j] = v;
+    if (pooled_out) pooled_out[i] = v;
 }
 
 // K_out[s][g] = K[idx[g][s]][g]; one 16-byte piece per thread
@@ -211,7 +215,7 @@ static SnapLayout snap_layout(void* ws, int64_t n, int w, int Hq, int Hkv, int64
     L.pstat = wc.take<float2>((size_t)Hkv * L.nblk * R);
     L.lse = wc.take<float>((size_t)Hkv * R);
     L.imp = wc.take<float>((size_t)Hkv * n);
-    L.pooled = wc.take<float>((size_t)Hkv * n);
+    L.pooled = wc.take<float>((size_t)Hkv * score_stride(n));
     int64_t ce = c < n ? c : n;
     L.sel_bytes = rows_topk_workspace(Hkv, n, ce);
     L.sel_ws = wc.take<char>(L.sel_bytes);
@@ -230,7 +234,7 @@ hipError_t launch_snapkv(const uint16_t* q_obs, const uint16_t* K, const uint16_
     if (L.bytes > ws_bytes) return hipErrorInvalidValue;
     const int R = (Hq / Hkv) * w;
     float* imp = imp_out ? imp_out : L.imp;
-    float* pooled = pooled_out ? pooled_out : L.pooled;
+    float* pooled = L.pooled;
     const size_t shq = (size_t)R * kD * 2;
     dim3 grid(Hkv, (unsigned)L.nblk);
     hipLaunchKernelGGL(snap_pass_kernel<1>, grid, dim3(kSnapThreads), shq, stream, q_obs, K, n, w, Hq, Hkv, L.pstat,
@@ -240,9 +244,10 @@ hipError_t launch_snapkv(const uint16_t* q_obs, const uint16_t* K, const uint16_
     hipLaunchKernelGGL(snap_pass_kernel<2>, grid, dim3(kSnapThreads), shq, stream, q_obs, K, n, w, Hq, Hkv, nullptr,
                        L.lse, imp);
     const int64_t tot = n * Hkv;
-    hipLaunchKernelGGL(snap_pool_kernel, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, stream, imp, n, Hkv, pooled);
+    hipLaunchKernelGGL(snap_pool_kernel, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, stream, imp, n, Hkv,
+                       score_stride(n), pooled, pooled_out);
     const int64_t ce = c < n ? c : n;
-    hipError_t e = launch_rows_topk(pooled, Hkv, n, ce, idx_out, L.sel_ws, L.sel_bytes, stream);
+    hipError_t e = launch_rows_topk(pooled, score_stride(n), Hkv, n, ce, idx_out, L.sel_ws, L.sel_bytes, stream);
     if (e != hipSuccess) return e;
     const int64_t pieces = ce * Hkv * 16;
     hipLaunchKernelGGL(snap_gather_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, stream, K, V, idx_out,

@@ -22,7 +22,7 @@ def header_functions():
 def test_exports_match_header():
     lib = _lib.load()
     names = header_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.SIGNATURES)
@@ -38,6 +38,13 @@ def _params(mode=0, bnum=1, bden=5, sink=4, local=256, vmin=1, tn=9, td=10):
 
 def err():
     return _lib.load().ts_last_error().decode()
+
+
+def test_score_stride():
+    L = _lib.load()
+    assert L.ts_score_stride(_offs([0, 131073]), 1) == 131136
+    assert L.ts_score_stride(_offs([0, 64, 128]), 2) == 128
+    assert L.ts_score_stride(None, 1) == -1
 
 
 def test_budget_helper():
