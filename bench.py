@@ -87,6 +87,7 @@ def main():
     idx = torch.empty(kmax * (Hq if mode == api.MODE_PER_HEAD else 1) + 16, dtype=torch.int32, device=dev)
     count = torch.empty(1, dtype=torch.int64, device=dev)
     ws_sel = torch.empty(max(api.select_workspace_bytes(offs[-1], Hq, p), 256), dtype=torch.uint8, device=dev)
+    ws_sc = torch.empty(max(api.score_workspace_bytes(1, Hq), 256), dtype=torch.uint8, device=dev)
     ws_dec = torch.empty(max(api.decode_workspace_bytes(offs[-1], [kmax], Hq, Hkv, mode), 256), dtype=torch.uint8,
                          device=dev)
     out = torch.empty((1, Hq, 128), dtype=torch.float32, device=dev)
@@ -117,8 +118,8 @@ def main():
         calls.append(((vp(K) .value + (n - 1) * Hkv * 128 * 2, n - 1),
                       (qp, vp(o.dev), o.host), ch, kb))
     Kp, Pp, kip, scp, idp, cnp = vp(K), vp(P), vp(kidx), vp(scores), vp(idx), vp(count)
-    Vp, outp, wsp, wdp = vp(V), vp(out), vp(ws_sel), vp(ws_dec)
-    ws_sel_n, ws_dec_n = ws_sel.numel(), ws_dec.numel()
+    Vp, outp, wsp, wdp, wsc = vp(V), vp(out), vp(ws_sel), vp(ws_dec), vp(ws_sc)
+    ws_sel_n, ws_dec_n, ws_sc_n = ws_sel.numel(), ws_dec.numel(), ws_sc.numel()
 
     def chk(rc):
         if rc != 0:
@@ -129,7 +130,7 @@ def main():
         st = stream_of()
         chk(L.ts_index_append(ctypes.c_void_p(kaddr), Pp, kip, pos, 1, Hkv, st))
         if marks: marks[1].record()
-        chk(L.ts_score(qp, Pp, kip, od, oh, 1, Hq, Hkv, scp, st))
+        chk(L.ts_score(qp, Pp, kip, od, oh, 1, Hq, Hkv, scp, wsc, ws_sc_n, st))
         if marks: marks[2].record()
         chk(L.ts_select(scp, od, oh, 1, Hq, Hkv, pref, idp, cnp, None, None, wsp, ws_sel_n, st))
         if marks: marks[3].record()
@@ -192,7 +193,7 @@ def main():
         st = stream_of()
         iso_calls = {
             "index_append": lambda: chk(L.ts_index_append(ctypes.c_void_p(kaddr), Pp, kip, pos, 1, Hkv, st)),
-            "score": lambda: chk(L.ts_score(qp, Pp, kip, od, oh, 1, Hq, Hkv, scp, st)),
+            "score": lambda: chk(L.ts_score(qp, Pp, kip, od, oh, 1, Hq, Hkv, scp, wsc, ws_sc_n, st)),
             "select": lambda: chk(L.ts_select(scp, od, oh, 1, Hq, Hkv, pref, idp, cnp, None, None, wsp, ws_sel_n, st)),
             "sparse_decode": lambda: chk(L.ts_sparse_decode(qp, Kp, Vp, od, oh, idp, cnp, ch, mode, 1, Hq, Hkv, outp,
                                                             wdp, ws_dec_n, st)),

@@ -92,6 +92,9 @@ int64_t ts_budget_tokens(int64_t n, const ts_select_params* p);
 int ts_index_append(const uint16_t* k_new, const float* P, uint16_t* k_index, int64_t pos,
                     int64_t T, int32_t Hkv, hipStream_t stream);
 
+/* Workspace for ts_score (the projected queries q'_h, B * Hq * 32 fp32 values). */
+size_t ts_score_workspace_bytes(int32_t B, int32_t Hq);
+
 /* Index scores for every query head and cached token ([TS] "Query-Key Dot Product
  * Index", eq. Score_h(i) = q_h . k_index,h(i) / sqrt(d')):  q'_h = P^T q_h (fp32) and
  *   scores[h * S + t] = (q'_h / sqrt(32)) . k_index[t][h / G]   (fp32, t packed over the batch)
@@ -99,10 +102,12 @@ int ts_index_append(const uint16_t* k_new, const float* P, uint16_t* k_index, in
  *   k_index device bf16 [Ntot][Hkv][32]
  *   scores  device fp32 [Hq][S]: row stride S = ts_score_stride(offsets_host, B), i.e.
  *           Ntot = offsets[B] rounded up to a multiple of 64 so that rows start on 256-byte
- *           boundaries; entries t >= Ntot of a row are not written.                       */
+ *           boundaries; entries t >= Ntot of a row are not written.
+ *   ws      device workspace of at least ts_score_workspace_bytes(B, Hq) bytes (holds
+ *           q'_h / sqrt(32) between the two kernels of the call).                       */
 int ts_score(const uint16_t* q, const float* P, const uint16_t* k_index,
              const int64_t* offsets_dev, const int64_t* offsets_host, int32_t B, int32_t Hq,
-             int32_t Hkv, float* scores, hipStream_t stream);
+             int32_t Hkv, float* scores, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Workspace for ts_select. */
 size_t ts_select_workspace_bytes(const int64_t* offsets_host, int32_t B, int32_t Hq,

@@ -21,7 +21,8 @@ SIGNATURES = {
     "ts_budget_tokens": (_i64, [_i64, _vp]),
     "ts_score_stride": (_i64, [_i64p, _i32]),
     "ts_index_append": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i64, _i32, _vp]),
-    "ts_score": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64p, _i32, _i32, _i32, _vp, _vp]),
+    "ts_score_workspace_bytes": (_sz, [_i32, _i32]),
+    "ts_score": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64p, _i32, _i32, _i32, _vp, _vp, _sz, _vp]),
     "ts_select_workspace_bytes": (_sz, [_i64p, _i32, _i32, _vp]),
     "ts_select": (ctypes.c_int, [_vp, _vp, _i64p, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "ts_decode_workspace_bytes": (_sz, [_i64p, _i64p, _i32, _i32, _i32, _i32]),

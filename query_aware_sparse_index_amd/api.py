@@ -80,14 +80,21 @@ def score_stride(offs: Offsets) -> int:
     return int(_lib.load().ts_score_stride(offs.host, offs.B))
 
 
-def score(q, P, k_index, offs: Offsets, Hkv: int, out=None):
+def score_workspace_bytes(B: int, Hq: int) -> int:
+    return int(_lib.load().ts_score_workspace_bytes(int(B), int(Hq)))
+
+
+def score(q, P, k_index, offs: Offsets, Hkv: int, out=None, ws=None):
     """Returns the [Hq][S] score array (row stride S = score_stride(offs) >= Ntot)."""
     _bf16_check(q, k_index)
     Hq = q.shape[1]
     if out is None:
         out = torch.empty((Hq, score_stride(offs)), dtype=torch.float32, device=q.device)
+    need = score_workspace_bytes(offs.B, Hq)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     _check(_lib.load().ts_score(_p(q), _p(P), _p(k_index), _p(offs.dev), offs.host, offs.B, Hq, int(Hkv),
-                                _p(out), _stream()))
+                                _p(out), _p(ws), ws.numel(), _stream()))
     return out
 
 

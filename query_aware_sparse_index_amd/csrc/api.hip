@@ -128,14 +128,23 @@ int ts_index_append(const uint16_t* k_new, const float* P, uint16_t* k_index, in
     return hip_status(qasi::launch_index_append(k_new, P, k_index, pos, T, Hkv, stream), "ts_index_append launch");
 }
 
+size_t ts_score_workspace_bytes(int32_t B, int32_t Hq) {
+    if (B <= 0 || Hq <= 0 || Hq > 64) return 0;
+    return qasi::score_workspace(B, Hq);
+}
+
 int ts_score(const uint16_t* q, const float* P, const uint16_t* k_index, const int64_t* offsets_dev,
-             const int64_t* offsets_host, int32_t B, int32_t Hq, int32_t Hkv, float* scores, hipStream_t stream) {
-    if (!aligned16(q) || !aligned16(P) || !aligned16(k_index) || !aligned16(scores))
-        return fail(QASI_ERR_INVALID, "q, P, k_index and scores must be non-null and 16-byte aligned");
+             const int64_t* offsets_host, int32_t B, int32_t Hq, int32_t Hkv, float* scores, void* ws,
+             size_t ws_bytes, hipStream_t stream) {
+    if (!aligned16(q) || !aligned16(P) || !aligned16(k_index) || !aligned16(scores) || !aligned16(ws))
+        return fail(QASI_ERR_INVALID, "q, P, k_index, scores and ws must be non-null and 16-byte aligned");
     if (int r = check_heads(Hq, Hkv)) return r;
     if (int r = check_offsets(offsets_dev, offsets_host, B, false)) return r;
+    size_t need = qasi::score_workspace(B, Hq);
+    if (ws_bytes < need) return fail(QASI_ERR_WORKSPACE, "ts_score needs %zu workspace bytes, got %zu", need, ws_bytes);
     if (int r = init_once()) return r;
-    return hip_status(qasi::launch_score(q, P, k_index, offsets_dev, offsets_host, B, Hq, Hkv, scores, stream),
+    return hip_status(qasi::launch_score(q, P, k_index, offsets_dev, offsets_host, B, Hq, Hkv, scores, ws, ws_bytes,
+                                         stream),
                       "ts_score launch");
 }
 

@@ -60,16 +60,21 @@ hipError_t launch_index_append(const uint16_t* k_new, const float* P, uint16_t* 
 }
 
 // ---------------------------------------------------------------------------------------
-// Index scores.  Work item = (sequence b, block of kScoreTB tokens of b).  The block first
-// issues its first index loads, then projects the sequence's queries (q'_h = P^T q_h /
-// sqrt(32), fp32, P and q staged in LDS).  A token's index row (Hkv x 32 bf16 = Hkv x 64 B)
-// is read by LPT = 4*Hkv lanes with one 16-byte non-temporal load each: lane (g, part)
-// holds 8 index values of KV head g and forms the partial dot products of the G heads of g;
-// a quad butterfly (DPP) completes each dot product.  Scores are staged in LDS as an
-// [Hq][kScoreTB] tile and written row by row (coalesced) into scores[h][t].
+// Index scores, two kernels:
+//   qproj_kernel : q'_h = P^T q_h / sqrt(32) in fp32 for every (sequence, query head), into
+//                  the workspace (one block per sequence);
+//   score_kernel : work item = (sequence b, block of kScoreTB tokens of b), dispatched in
+//                  token order.  A token's index row (Hkv x 32 bf16 = Hkv x 64 B) is read by
+//                  LPT = 4*Hkv lanes with one 16-byte load each: lane (g, part) holds 8 index
+//                  values of KV head g and forms the partial dot products of the G heads of g.
+//                  A transposed quad butterfly (DPP) leaves lane `part` with the complete
+//                  scores of the heads h = part (mod 4) of its group, so every lane stores
+//                  whole scores.  Scores are staged in a padded LDS tile [Hq][kScoreTB + 1]
+//                  (conflict-free) and written row by row into scores[h * S + t].
 // ---------------------------------------------------------------------------------------
 constexpr int kScoreThreads = 512;
-constexpr int kScoreTB = 512;
+constexpr int kScoreTB = 128;
+constexpr int kTileLd = kScoreTB + 1;
 
 __device__ __forceinline__ bool find_item(const int64_t* __restrict__ offsets, int B, int64_t item, int tb, int& b,
                                           int64_t& t0, int64_t& len) {
@@ -89,102 +94,146 @@ __device__ __forceinline__ bool find_item(const int64_t* __restrict__ offsets, i
     return false;
 }
 
-template <int HKV>
-__global__ __launch_bounds__(kScoreThreads) void score_kernel(const uint16_t* __restrict__ q, const float* __restrict__ P,
+// qp[(b * Hq + h) * 32 + c] = sum_j q[b][h][j] P[j][c] / sqrt(32): P and the block's
+// queries are staged in LDS with one round trip to memory, then thread (h, c) forms its
+// 128-term sum.
+__global__ __launch_bounds__(1024) void qproj_kernel(const uint16_t* __restrict__ q, const float* __restrict__ P,
+                                                    int Hq, float* __restrict__ qp) {
+    __shared__ float sP[kD * kDP];
+    __shared__ uint4 sq[64 * kD / 8];
+    const int b = blockIdx.x;
+    const uint4* qb = reinterpret_cast<const uint4*>(q + (int64_t)b * Hq * kD);
+    for (int i = threadIdx.x; i < kD * kDP / 4; i += 1024)
+        reinterpret_cast<float4*>(sP)[i] = reinterpret_cast<const float4*>(P)[i];
+    for (int i = threadIdx.x; i < Hq * kD / 8; i += 1024) sq[i] = qb[i];
+    __syncthreads();
+    for (int o = threadIdx.x; o < Hq * kDP; o += 1024) {
+        const int h = o / kDP, c = o % kDP;
+        float acc = 0.f;
+#pragma unroll 4
+        for (int j8 = 0; j8 < kD / 8; ++j8) {
+            const uint4 w = sq[h * (kD / 8) + j8];
+            const float qv[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
+                                 bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc = fmaf(qv[e], sP[(j8 * 8 + e) * kDP + c], acc);
+        }
+        qp[(int64_t)b * Hq * kDP + o] = acc * 0.17677669529663688f;
+    }
+}
+
+// Transposed quad reduction: v[hh] (hh < G) are this lane's partial sums; afterwards
+// v[k] of lane `part` holds the full sum of head hh = part + 4k (G >= 4), of head
+// hh = part & 1 (G == 2, lanes part and part^2 agree) or of head 0 (G == 1).
+template <int G>
+__device__ __forceinline__ void quad_transpose_sum(float (&v)[G], int part) {
+    if constexpr (G == 1) {
+        v[0] = sum_quad(v[0]);
+    } else if constexpr (G == 2) {
+        const bool odd = part & 1;
+        const float send = odd ? v[0] : v[1];
+        const float keep = odd ? v[1] : v[0];
+        const float r = keep + dpp_quad_xor1(send);
+        v[0] = r + dpp_quad_xor2(r);
+    } else {
+        // step 1 (partner part^1): keep heads with (hh & 1) == (part & 1)
+        constexpr int H1 = G / 2;
+        float k1[H1];
+        const bool odd = part & 1;
+#pragma unroll
+        for (int i = 0; i < H1; ++i) {
+            const float a = v[2 * i], c = v[2 * i + 1];
+            const float send = odd ? a : c;
+            const float keep = odd ? c : a;
+            k1[i] = keep + dpp_quad_xor1(send);     // head 2i + (part & 1)
+        }
+        // step 2 (partner part^2): keep heads with (hh & 3) == part
+        const bool hi2 = part & 2;
+#pragma unroll
+        for (int i = 0; i < H1 / 2; ++i) {
+            const float a = k1[2 * i], c = k1[2 * i + 1];   // heads 4i + (part&1), 4i + 2 + (part&1)
+            const float send = hi2 ? a : c;
+            const float keep = hi2 ? c : a;
+            v[i] = keep + dpp_quad_xor2(send);        // head 4i + part
+        }
+    }
+}
+
+template <int HKV, int G>
+__global__ __launch_bounds__(kScoreThreads) void score_kernel(const float* __restrict__ qp,
                                                              const uint16_t* __restrict__ k_index,
-                                                             const int64_t* __restrict__ offsets, int B, int Hq,
+                                                             const int64_t* __restrict__ offsets, int B,
                                                              float* __restrict__ scores) {
+    constexpr int Hq = HKV * G;
     constexpr int LPT = 4 * HKV;          // lanes per token
     constexpr int TPW = 64 / LPT;         // tokens per wave per load
     constexpr int TPB = TPW * (kScoreThreads / 64);  // tokens per block per load
     constexpr int ITERS = kScoreTB / TPB;
     constexpr int UNR = ITERS < 8 ? ITERS : 8;
-    extern __shared__ float smem[];
-    float* sq = smem;                       // [Hq][32] projected queries
-    float* sP = sq + Hq * kDP;              // [128][32]        } staging, dead once q' is formed
-    float* sqf = sP + kD * kDP;             // [Hq][128] queries }
-    float* tile = sP;                       // [Hq][kScoreTB] score tile, overlays the staging
+    constexpr int NOUT = G >= 4 ? G / 4 : 1;          // complete heads per lane
+    __shared__ float tile[Hq * kTileLd];
 
     int b;
     int64_t t0, len;
     if (!find_item(offsets, B, blockIdx.x, kScoreTB, b, t0, len)) return;
     const int64_t S = score_stride(offsets[B]);
     const int64_t base_tok = offsets[b] + t0;
-    const int G = Hq / HKV;
 
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const int lit = lane % LPT, g = lit / 4, part = lit % 4;
     const int slot = wid * TPW + lane / LPT;
 
-    // first batch of index loads, issued before the query projection
     uint4 kv[UNR];
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
-        int tl = u * TPB + slot;
+        const int tl = u * TPB + slot;
         kv[u] = make_uint4(0, 0, 0, 0);
         if (tl < len) kv[u] = ld16(k_index + ((base_tok + tl) * HKV + g) * kDP + part * 8);
     }
-    // stage P (16 KB) and the queries of sequence b
-    for (int i = threadIdx.x; i < kD * kDP / 4; i += kScoreThreads)
-        reinterpret_cast<float4*>(sP)[i] = reinterpret_cast<const float4*>(P)[i];
-    for (int i = threadIdx.x; i < Hq * kD / 8; i += kScoreThreads) {
-        uint4 w = reinterpret_cast<const uint4*>(q + (int64_t)b * Hq * kD)[i];
-        float* d = sqf + i * 8;
-        d[0] = bf16_lo(w.x); d[1] = bf16_hi(w.x); d[2] = bf16_lo(w.y); d[3] = bf16_hi(w.y);
-        d[4] = bf16_lo(w.z); d[5] = bf16_hi(w.z); d[6] = bf16_lo(w.w); d[7] = bf16_hi(w.w);
-    }
-    __syncthreads();
-    // q'_h[c] = sum_j q[b][h][j] P[j][c] / sqrt(32)
-    for (int o = threadIdx.x; o < Hq * kDP; o += kScoreThreads) {
-        const int h = o / kDP, c = o % kDP;
-        const float* qh = sqf + h * kD;
-        float acc = 0.f;
-#pragma unroll 16
-        for (int j = 0; j < kD; ++j) acc = fmaf(qh[j], sP[j * kDP + c], acc);
-        sq[o] = acc * 0.17677669529663688f;
-    }
-    __syncthreads();
-    float qr[8][8];   // [head in group][element]
+    float qr[G][8];
 #pragma unroll
-    for (int hh = 0; hh < 8; ++hh)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qr[hh][e] = (hh < G) ? sq[(g * G + hh) * kDP + part * 8 + e] : 0.f;
+    for (int hh = 0; hh < G; ++hh) {
+        const float4* src = reinterpret_cast<const float4*>(qp + ((int64_t)b * Hq + g * G + hh) * kDP + part * 8);
+        const float4 a = src[0], c = src[1];
+        qr[hh][0] = a.x; qr[hh][1] = a.y; qr[hh][2] = a.z; qr[hh][3] = a.w;
+        qr[hh][4] = c.x; qr[hh][5] = c.y; qr[hh][6] = c.z; qr[hh][7] = c.w;
+    }
+    // rows of the tile this lane writes: heads g*G + part + 4k (G >= 4), g*G + (part&1) (G == 2), g*G (G == 1)
+    const bool writer = (G >= 4) || (G == 2 ? part < 2 : part == 0);
+    const int hrow = g * G + (G >= 4 ? part : (G == 2 ? (part & 1) : 0));
 
     for (int it0 = 0; it0 < ITERS; it0 += UNR) {
 #pragma unroll
         for (int u = 0; u < UNR; ++u) {
-            int tl = (it0 + u) * TPB + slot;
-            uint4 w = kv[u];
-            // prefetch the next batch into the same register
-            int tn = (it0 + UNR + u) * TPB + slot;
+            const int tl = (it0 + u) * TPB + slot;
+            const uint4 w = kv[u];
             if (it0 + UNR < ITERS) {
+                const int tn = (it0 + UNR + u) * TPB + slot;
                 kv[u] = make_uint4(0, 0, 0, 0);
                 if (tn < len) kv[u] = ld16(k_index + ((base_tok + tn) * HKV + g) * kDP + part * 8);
             }
-            float kf[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
-                           bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
+            const float kf[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
+                                 bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
+            float v[G];
 #pragma unroll
-            for (int hh = 0; hh < 8; ++hh) {
-                if (hh < G) {
-                    float s = 0.f;
+            for (int hh = 0; hh < G; ++hh) {
+                float s = 0.f;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) s = fmaf(qr[hh][e], kf[e], s);
-                    s = sum_quad(s);
-                    if ((hh & 3) == part && tl < len) tile[(g * G + hh) * kScoreTB + tl] = s;
-                }
+                for (int e = 0; e < 8; ++e) s = fmaf(qr[hh][e], kf[e], s);
+                v[hh] = s;
+            }
+            quad_transpose_sum<G>(v, part);
+            if (writer && tl < len) {
+#pragma unroll
+                for (int k = 0; k < NOUT; ++k) tile[(hrow + 4 * k) * kTileLd + tl] = v[k];
             }
         }
     }
     __syncthreads();
     for (int o = threadIdx.x; o < Hq * kScoreTB; o += kScoreThreads) {
-        int h = o / kScoreTB, tl = o % kScoreTB;
-        if (tl < len) scores[(int64_t)h * S + base_tok + tl] = tile[o];
+        const int h = o / kScoreTB, tl = o % kScoreTB;
+        if (tl < len) scores[(int64_t)h * S + base_tok + tl] = tile[h * kTileLd + tl];
     }
-}
-
-static size_t score_shm(int Hq) {
-    size_t stage = (size_t)kD * kDP + (size_t)Hq * kD, tile = (size_t)Hq * kScoreTB;
-    return ((size_t)Hq * kDP + (stage > tile ? stage : tile)) * sizeof(float);
 }
 
 int64_t score_items(const int64_t* offsets_host, int B) {
@@ -193,31 +242,47 @@ int64_t score_items(const int64_t* offsets_host, int B) {
     return items;
 }
 
-hipError_t launch_score(const uint16_t* q, const float* P, const uint16_t* k_index, const int64_t* offsets_dev,
-                        const int64_t* offsets_host, int B, int Hq, int Hkv, float* scores, hipStream_t stream) {
-    int64_t items = score_items(offsets_host, B);
-    if (items == 0) return hipSuccess;
-    size_t shm = score_shm(Hq);
-    dim3 grid((unsigned)items), block(kScoreThreads);
-    switch (Hkv) {
-        case 1: hipLaunchKernelGGL(score_kernel<1>, grid, block, shm, stream, q, P, k_index, offsets_dev, B, Hq, scores); break;
-        case 2: hipLaunchKernelGGL(score_kernel<2>, grid, block, shm, stream, q, P, k_index, offsets_dev, B, Hq, scores); break;
-        case 4: hipLaunchKernelGGL(score_kernel<4>, grid, block, shm, stream, q, P, k_index, offsets_dev, B, Hq, scores); break;
-        case 8: hipLaunchKernelGGL(score_kernel<8>, grid, block, shm, stream, q, P, k_index, offsets_dev, B, Hq, scores); break;
+size_t score_workspace(int B, int Hq) {
+    WsCarver w(nullptr);
+    w.take<float>((size_t)B * Hq * kDP);
+    return w.size();
+}
+
+template <int HKV>
+static hipError_t launch_score_g(int G, dim3 grid, hipStream_t stream, const float* qp, const uint16_t* k_index,
+                                 const int64_t* offsets_dev, int B, float* scores) {
+    dim3 block(kScoreThreads);
+    switch (G) {
+        case 1: hipLaunchKernelGGL((score_kernel<HKV, 1>), grid, block, 0, stream, qp, k_index, offsets_dev, B, scores); break;
+        case 2: hipLaunchKernelGGL((score_kernel<HKV, 2>), grid, block, 0, stream, qp, k_index, offsets_dev, B, scores); break;
+        case 4: hipLaunchKernelGGL((score_kernel<HKV, 4>), grid, block, 0, stream, qp, k_index, offsets_dev, B, scores); break;
+        case 8: hipLaunchKernelGGL((score_kernel<HKV, 8>), grid, block, 0, stream, qp, k_index, offsets_dev, B, scores); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
+hipError_t launch_score(const uint16_t* q, const float* P, const uint16_t* k_index, const int64_t* offsets_dev,
+                        const int64_t* offsets_host, int B, int Hq, int Hkv, float* scores, void* ws,
+                        size_t ws_bytes, hipStream_t stream) {
+    if (score_workspace(B, Hq) > ws_bytes) return hipErrorInvalidValue;
+    float* qp = static_cast<float*>(ws);
+    hipLaunchKernelGGL(qproj_kernel, dim3(B), dim3(1024), 0, stream, q, P, Hq, qp);
+    const int64_t items = score_items(offsets_host, B);
+    if (items == 0) return hipGetLastError();
+    const dim3 grid((unsigned)items);
+    const int G = Hq / Hkv;
+    switch (Hkv) {
+        case 1: return launch_score_g<1>(G, grid, stream, qp, k_index, offsets_dev, B, scores);
+        case 2: return launch_score_g<2>(G, grid, stream, qp, k_index, offsets_dev, B, scores);
+        case 4: return launch_score_g<4>(G, grid, stream, qp, k_index, offsets_dev, B, scores);
+        case 8: return launch_score_g<8>(G, grid, stream, qp, k_index, offsets_dev, B, scores);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 }  // namespace qasi
 
 namespace qasi {
-hipError_t init_score_kernels() {
-    const int bytes = (int)score_shm(64);
-    hipError_t e = hipSuccess;
-    if ((e = hipFuncSetAttribute((const void*)score_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize, bytes))) return e;
-    if ((e = hipFuncSetAttribute((const void*)score_kernel<2>, hipFuncAttributeMaxDynamicSharedMemorySize, bytes))) return e;
-    if ((e = hipFuncSetAttribute((const void*)score_kernel<4>, hipFuncAttributeMaxDynamicSharedMemorySize, bytes))) return e;
-    return hipFuncSetAttribute((const void*)score_kernel<8>, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-}
+hipError_t init_score_kernels() { return hipSuccess; }
 }  // namespace qasi

@@ -10,8 +10,10 @@ namespace qasi {
 // ---- index and score
 hipError_t launch_index_append(const uint16_t* k_new, const float* P, uint16_t* k_index, int64_t pos, int64_t T,
                                int Hkv, hipStream_t stream);
+size_t score_workspace(int B, int Hq);
 hipError_t launch_score(const uint16_t* q, const float* P, const uint16_t* k_index, const int64_t* offsets_dev,
-                        const int64_t* offsets_host, int B, int Hq, int Hkv, float* scores, hipStream_t stream);
+                        const int64_t* offsets_host, int B, int Hq, int Hkv, float* scores, void* ws,
+                        size_t ws_bytes, hipStream_t stream);
 
 // ---- selection
 struct SelectConfig {

@@ -9,12 +9,21 @@
 //   ranks tokens by each head's own score under the same budget.
 //
 // Both modes need an exact order statistic per (sequence, head): theta_h = s_(r) for the
-// vote, and the boundary score of the per-head top-K.  It is found by a three-digit radix
-// select over order-preserving uint32 keys of the fp32 scores (digits 12 / 12 / 8 bits):
-//   os_hist    : per (instance, slice) LDS histogram of the top 12 bits;
-//   os_collect : sums the slice histograms, finds the top digit of the answer and copies the
-//                keys that share it (the "candidates") next to the slice;
-//   os_final   : resolves the low 20 bits among the candidates (two more digits).
+// vote, and the boundary score of the per-head top-K.  It is found on order-preserving
+// uint32 keys of the fp32 scores in two kernels:
+//   th_collect : every block of an instance first derives the same key bracket [lo, hi]
+//                from a stratified sample of the row (kRuns runs of 16 keys): a histogram
+//                over the sample's value range locates the sample order statistics kDelta
+//                ranks below and above the target's expected sample rank.  The block then
+//                counts the keys of its slice below lo, compacts the keys inside the bracket
+//                (the "candidates") next to the slice and histograms them on the top
+//                kDigit bits of key - lo;
+//   th_final   : sums the slice histograms to find the answer's top digit, gathers the
+//                candidates of that digit into LDS and finishes with a radix select over
+//                the remaining bits.  If the answer's rank is not among the candidates (or
+//                its digit holds more than kCap of them) the block runs the radix select
+//                over the whole row instead.  The result is exact either way; the sample
+//                only decides how much work it takes.
 // Ties resolve to the lowest position in the compaction kernels, which take every token
 // above the boundary and the first `need_eq` tokens equal to it in position order.
 #include "qasi_device.h"
@@ -22,16 +31,24 @@
 
 namespace qasi {
 
-constexpr int kOsSlice = 16384;     // keys per radix slice
-constexpr int kOsThreads = 1024;
-constexpr int kOsMaxSL = 1024;      // slices per instance (n up to 16M tokens)
-constexpr int kChunk = 1024;        // tokens per vote / compaction block
-constexpr int kVoteBins = 72;       // vote keys 0 .. Hq + 1 (Hq <= 64)
+constexpr int kThThreads = 1024;   // final blocks
+constexpr int kRuns = 128, kRunLen = 16;
+constexpr int kSample = kRuns * kRunLen;   // sampled keys per instance
+constexpr int kSampleBins = 2048;
+constexpr int kDelta = 96;         // bracket half-width in sample ranks
+constexpr int kDigit = 11;         // radix digit width of the final select
+constexpr int kDigitBins = 1 << kDigit;
+constexpr int kCap = 16384;        // keys of the answer's top digit resolved in LDS
+constexpr int kSlice = 8192;       // keys per collect block
+constexpr int kColThreads = 512;
+constexpr int kMaxSL = 2048;       // slices per instance (n up to 2^24 tokens)
+constexpr int kChunk = 1024;       // tokens per vote / compaction block
+constexpr int kVoteBins = 72;      // vote keys 0 .. Hq + 1 (Hq <= 64)
 
 enum : int64_t { kFlagActive = 0, kFlagTakeNone = 1, kFlagTakeAll = 2 };
 
 // state[inst * 8 + k]
-enum { kStFlag = 0, kStKey = 1, kStGt = 2, kStNeed = 3, kStD1 = 4, kStR1 = 5, kStGtBin = 6 };
+enum { kStFlag = 0, kStKey = 1, kStGt = 2, kStNeed = 3, kStLo = 4, kStHi = 5 };
 
 struct DevCfg {
     int mode;
@@ -94,232 +111,361 @@ __device__ __forceinline__ int64_t forced_before(int64_t x, int64_t n, int64_t s
     return a + b;
 }
 
-// ------------------------------------------------------------------------ os_hist
-__global__ __launch_bounds__(kOsThreads) void os_hist_kernel(const float* __restrict__ scores,
-                                                            const int64_t* __restrict__ offsets, int B, int Hq,
-                                                            DevCfg cfg, int SL, int64_t S, uint32_t* __restrict__ part1) {
-    // 4 sub-histograms (one per group of 4 waves), two 16-bit bins per word
-    __shared__ uint32_t sub[4][2048];
-    const int inst = blockIdx.y, s = blockIdx.x;
-    const int b = inst / Hq, h = inst % Hq;
-    const int64_t off = offsets[b];
-    OsInst oi = os_instance(offsets[b + 1] - off, cfg);
-    for (int i = threadIdx.x; i < 4 * 2048; i += kOsThreads) (&sub[0][0])[i] = 0;
-    __syncthreads();
-    int64_t lo = oi.beg + (int64_t)s * kOsSlice, hi = lo + kOsSlice;
-    if (hi > oi.end) hi = oi.end;
-    const bool act = oi.flag == kFlagActive && lo < hi;
-    if (act) {
-        const float* row = scores + (int64_t)h * S + off;
-        uint32_t* mine = sub[threadIdx.x >> 8];
-        for_each_f32<kOsThreads, 4>(row, lo, hi, [&](int64_t, float v, bool ok) {
-            if (ok) {
-                const uint32_t d = order_key(v) >> 20;
-                atomicAdd(&mine[d >> 1], (d & 1) ? 0x10000u : 1u);
-            }
-        });
-    }
-    __syncthreads();
-    uint32_t* dst = part1 + ((size_t)inst * SL + s) * 2048;
-    for (int i = threadIdx.x; i < 2048; i += kOsThreads) dst[i] = act ? (sub[0][i] + sub[1][i] + sub[2][i] + sub[3][i]) : 0u;
+// ---------------------------------------------------------------------- th_collect
+__device__ __forceinline__ uint32_t mix32(uint32_t x) {
+    x ^= x >> 16;
+    x *= 0x7feb352du;
+    x ^= x >> 15;
+    x *= 0x846ca68bu;
+    x ^= x >> 16;
+    return x;
 }
 
-// Finds the digit whose cumulative count (ascending) first reaches `rank` in the 4096-bin
-// LDS histogram `hist`.  Returns the digit; *below = count of keys in smaller digits.
-__device__ int find_digit_4096(const uint32_t* hist, int64_t rank, int64_t* below, int64_t* sbuf, int* tmp) {
-    constexpr int PER = 4096 / kOsThreads;   // consecutive bins owned by a thread
-    const int tid = threadIdx.x;
-    if (tid == 0) { sbuf[0] = 0; sbuf[1] = 0; }
-    __syncthreads();
-    int64_t local = 0;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) local += hist[tid * PER + i];
-    int total;
-    const int inc = block_inclusive_scan<kOsThreads>((int)local, tmp, &total);
-    const int64_t excl = inc - local;
-    if (excl < rank && rank <= inc) {
-        int64_t c = excl;
-        for (int i = 0; i < PER; ++i) {
-            const int64_t nc = c + hist[tid * PER + i];
-            if (rank <= nc) { sbuf[0] = tid * PER + i; sbuf[1] = c; break; }
-            c = nc;
-        }
-    }
-    __syncthreads();
-    const int d = (int)sbuf[0];
-    *below = sbuf[1];
-    __syncthreads();
-    return d;
+// Shift that leaves the top kDigit bits of a key offset below 2^nbits.
+__host__ __device__ __forceinline__ int top_shift(uint32_t span) {
+    int nbits = 0;
+    while (nbits < 32 && (span >> nbits) != 0u) ++nbits;
+    return nbits > kDigit ? nbits - kDigit : 0;
 }
 
-// --------------------------------------------------------------------- os_collect
-__global__ __launch_bounds__(kOsThreads) void os_collect_kernel(const float* __restrict__ scores,
-                                                               const int64_t* __restrict__ offsets, int B, int Hq,
-                                                               DevCfg cfg, int SL, int64_t S, const uint32_t* __restrict__ part1,
-                                                               uint32_t* __restrict__ cand, uint32_t* __restrict__ cand_cnt,
-                                                               int64_t* __restrict__ state) {
-    __shared__ uint32_t hist[4096];
-    __shared__ int64_t sbuf[2];
-    __shared__ int tmp[kOsThreads / 64];
+// Block (slice s, instance).  Bracket: rows of m <= kCap keys take every key ([0, 2^32 - 1]).
+// Longer rows: run j of the sample starts at a hashed position of stratum
+// [j m / kRuns, (j + 1) m / kRuns); the sample's [min, max] is cut into kSampleBins equal
+// bins; lo is the lower edge of the bin before the one holding sample rank ir - kDelta and
+// hi the upper edge of the bin after the one holding ir + kDelta (the key range's ends when
+// these leave the sample), ir the target's expected sample rank.  Every block computes
+// the same bracket from the same keys; block 0 stores it.
+// Output: cnt[(inst * SL + s) * 2] = #keys < lo, [+1] = #candidates; candidates (keys in
+// [lo, hi]) at cand[(inst * SL + s) * kSlice ...] in arbitrary order; dhist[inst][s] =
+// kDigitBins 16-bit counts of the candidates' top digit (key - lo) >> top_shift(hi - lo),
+// two per word.
+__global__ __launch_bounds__(kColThreads) void th_collect_kernel(const float* __restrict__ scores,
+                                                                const int64_t* __restrict__ offsets, int Hq,
+                                                                DevCfg cfg, int SL, int64_t S,
+                                                                int64_t* __restrict__ state,
+                                                                uint32_t* __restrict__ cand,
+                                                                uint32_t* __restrict__ cnt,
+                                                                uint32_t* __restrict__ dhist) {
+    constexpr int NW = kColThreads / 64;
+    constexpr int PT = kSlice / kColThreads;       // slice keys per thread
     __shared__ uint32_t lcnt;
+    __shared__ int wsum[NW];
+    __shared__ float wmin[NW], wmax[NW];
+    __shared__ uint32_t hist[kSampleBins];         // sample bins, then candidate digit bins
+    __shared__ int tmp[NW];
+    __shared__ int sb[2];
+    static_assert(kDigitBins <= kSampleBins, "digit histogram reuses the sample bins");
     const int inst = blockIdx.y, s = blockIdx.x;
     const int b = inst / Hq, h = inst % Hq;
     const int64_t off = offsets[b];
-    OsInst oi = os_instance(offsets[b + 1] - off, cfg);
-    if (oi.flag != kFlagActive) {
-        if (s == 0 && threadIdx.x == 0) {
-            state[inst * 8 + kStFlag] = oi.flag;
-            state[inst * 8 + kStNeed] = oi.need;
-        }
-        return;
+    const OsInst oi = os_instance(offsets[b + 1] - off, cfg);
+    int64_t* st = state + (int64_t)inst * 8;
+    if (s == 0 && threadIdx.x == 0) {
+        st[kStFlag] = oi.flag;
+        st[kStNeed] = oi.need;
     }
-    // sum the slice histograms (two 16-bit bins per word)
-    for (int i0 = threadIdx.x; i0 < 2048; i0 += 8 * kOsThreads) {
-        uint32_t a[8], c[8];
+    if (oi.flag != kFlagActive) return;
+    const int64_t m = oi.end - oi.beg;
+    const int64_t lo = oi.beg + (int64_t)s * kSlice;
+    const int64_t hi = lo + kSlice < oi.end ? lo + kSlice : oi.end;
+    const float* row = scores + (int64_t)h * S + off;
+    // the slice, in registers before the bracket is known (one memory round trip for both)
+    float xv[PT];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) { a[u] = 0; c[u] = 0; }
-        for (int k0 = 0; k0 < SL; k0 += 4) {
-            uint32_t w[4][8];
+    for (int j = 0; j < PT; ++j) {
+        const int64_t t = lo + threadIdx.x + (int64_t)j * kColThreads;
+        xv[j] = t < hi ? row[t] : 0.f;
+    }
+    uint32_t klo = 0u, khi = 0xffffffffu;
+    for (int i = threadIdx.x; i < kSampleBins; i += kColThreads) hist[i] = 0;
+    if (m > kCap) {
+        constexpr int PER = kSample / kColThreads;
+        float v[PER];
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const int i = i0 + u * kOsThreads;
-                    w[kk][u] = (k0 + kk < SL && i < 2048) ? part1[((size_t)inst * SL + k0 + kk) * 2048 + i] : 0u;
-                }
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-                for (int u = 0; u < 8; ++u) { a[u] += w[kk][u] & 0xffffu; c[u] += w[kk][u] >> 16; }
+        for (int u = 0; u < PER; ++u) {
+            const int i = threadIdx.x + u * kColThreads, j = i / kRunLen;
+            const int64_t a = (int64_t)j * m / kRuns, e = (int64_t)(j + 1) * m / kRuns;
+            const uint32_t r = mix32((uint32_t)j * 0x9e3779b9u ^ mix32((uint32_t)inst + 0x632be5abu));
+            v[u] = row[oi.beg + a + (int64_t)(r % (uint32_t)(e - a - kRunLen + 1)) + (i % kRunLen)];
         }
+        float mn = v[0], mx = v[0];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int i = i0 + u * kOsThreads;
-            if (i < 2048) { hist[2 * i] = a[u]; hist[2 * i + 1] = c[u]; }
+        for (int u = 1; u < PER; ++u) { mn = fminf(mn, v[u]); mx = fmaxf(mx, v[u]); }
+        for (int o = 32; o > 0; o >>= 1) {
+            mn = fminf(mn, __shfl_xor(mn, o, 64));
+            mx = fmaxf(mx, __shfl_xor(mx, o, 64));
         }
+        if ((threadIdx.x & 63) == 0) { wmin[threadIdx.x >> 6] = mn; wmax[threadIdx.x >> 6] = mx; }
+        __syncthreads();
+        mn = wmin[0];
+        mx = wmax[0];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) { mn = fminf(mn, wmin[w]); mx = fmaxf(mx, wmax[w]); }
+        const int64_t ir = (oi.rank - 1) * kSample / m;
+        const int64_t il = ir - kDelta, ih = ir + kDelta;
+        if (mx > mn) {
+            const float scale = (float)kSampleBins / (mx - mn);
+#pragma unroll
+            for (int u = 0; u < PER; ++u) {
+                int bin = (int)((v[u] - mn) * scale);
+                bin = bin < 0 ? 0 : (bin >= kSampleBins ? kSampleBins - 1 : bin);
+                atomicAdd(&hist[bin], 1u);
+            }
+            __syncthreads();
+            constexpr int BPT = kSampleBins / kColThreads;
+            int c = 0;
+#pragma unroll
+            for (int u = 0; u < BPT; ++u) c += (int)hist[threadIdx.x * BPT + u];
+            int tot;
+            const int inc = block_inclusive_scan<kColThreads>(c, tmp, &tot);
+            int acc = inc - c;
+#pragma unroll
+            for (int u = 0; u < BPT; ++u) {
+                const int bin = threadIdx.x * BPT + u;
+                const int nx = acc + (int)hist[bin];
+                if (acc <= il && il < nx) sb[0] = bin;      // bin holding sample rank il (0-based)
+                if (acc <= ih && ih < nx) sb[1] = bin;
+                acc = nx;
+            }
+            __syncthreads();
+            const float w = (mx - mn) / (float)kSampleBins;
+            if (il > 0) klo = order_key(mn + (float)(sb[0] - 1) * w);
+            if (ih < kSample - 1) khi = order_key(mn + (float)(sb[1] + 2) * w);
+            for (int i = threadIdx.x; i < kSampleBins; i += kColThreads) hist[i] = 0;
+        } else {
+            klo = khi = order_key(mn);
+        }
+        if (klo > khi) klo = khi;
+    }
+    if (s == 0 && threadIdx.x == 0) {
+        st[kStLo] = klo;
+        st[kStHi] = khi;
     }
     if (threadIdx.x == 0) lcnt = 0;
     __syncthreads();
-    int64_t below;
-    const int d1 = find_digit_4096(hist, oi.rank, &below, sbuf, tmp);
-    if (s == 0 && threadIdx.x == 0) {
-        int64_t m = oi.end - oi.beg;
-        state[inst * 8 + kStFlag] = kFlagActive;
-        state[inst * 8 + kStNeed] = oi.need;
-        state[inst * 8 + kStD1] = d1;
-        state[inst * 8 + kStR1] = oi.rank - below;
-        state[inst * 8 + kStGtBin] = m - below - hist[d1];
-    }
-    int64_t lo = oi.beg + (int64_t)s * kOsSlice, hi = lo + kOsSlice;
-    if (hi > oi.end) hi = oi.end;
-    const float* row = scores + (int64_t)h * S + off;
-    uint32_t* dst = cand + ((size_t)inst * SL + s) * kOsSlice;
+    const int dsh = top_shift(khi - klo);
+    uint32_t* dst = cand + ((size_t)inst * SL + s) * kSlice;
     const int lane = threadIdx.x & 63;
-    for_each_f32<kOsThreads, 4>(row, lo, hi, [&](int64_t, float v, bool ok) {
-        const uint32_t k = order_key(v);
-        const bool hit = ok && (int)(k >> 20) == d1;
+    int below = 0;
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+        const bool ok = lo + threadIdx.x + (int64_t)j * kColThreads < hi;
+        const uint32_t k = order_key(xv[j]);
+        below += (ok && k < klo) ? 1 : 0;
+        const bool hit = ok && k >= klo && k <= khi;
         const uint64_t mask = __ballot(hit);
         if (mask) {
             uint32_t basep = 0;
             const int leader = __ffsll((unsigned long long)mask) - 1;
             if (lane == leader) basep = atomicAdd(&lcnt, (uint32_t)__popcll(mask));
             basep = __shfl(basep, leader, 64);
-            if (hit) dst[basep + __popcll(mask & ((1ull << lane) - 1ull))] = k;
+            if (hit) {
+                dst[basep + __popcll(mask & ((1ull << lane) - 1ull))] = k;
+                atomicAdd(&hist[(k - klo) >> dsh], 1u);
+            }
         }
-    });
+    }
+    below = wave_sum_i(below);
+    if (lane == 0) wsum[threadIdx.x >> 6] = below;
     __syncthreads();
-    if (threadIdx.x == 0) cand_cnt[(size_t)inst * SL + s] = (lo < hi) ? lcnt : 0u;
+    uint32_t* dh = dhist + ((size_t)inst * SL + s) * (kDigitBins / 2);
+    for (int i = threadIdx.x; i < kDigitBins / 2; i += kColThreads) dh[i] = hist[2 * i] | (hist[2 * i + 1] << 16);
+    if (threadIdx.x == 0) {
+        int tot = 0;
+        for (int w = 0; w < NW; ++w) tot += wsum[w];
+        cnt[((size_t)inst * SL + s) * 2 + 0] = (uint32_t)tot;
+        cnt[((size_t)inst * SL + s) * 2 + 1] = lcnt;
+    }
 }
 
-// ----------------------------------------------------------------------- os_final
-__global__ __launch_bounds__(kOsThreads) void os_final_kernel(int B, int Hq, int SL, const uint32_t* __restrict__ cand,
-                                                             const uint32_t* __restrict__ cand_cnt,
+// ---------------------------------------------------------------------- th_final
+// Radix selection over the keys that visit(f) hands to f (f(x) once per key): returns the
+// rank-th smallest x (1-based) and adds the number of keys above it to *gt.  Digits of
+// kDigit bits from bit nbits - 1 down; every thread of the block calls it.
+template <class Visit>
+__device__ uint32_t radix_rank(Visit visit, int nbits, int64_t rank, uint32_t* hist, int* tmp, int64_t* sh,
+                               int64_t* gt) {
+    constexpr int NB = 1 << kDigit, BPT = NB / kThThreads;
+    uint64_t prefix = 0;
+    int shift = nbits;
+    while (shift > 0) {
+        const int d = shift < kDigit ? shift : kDigit;
+        shift -= d;
+        const int top = shift + d;
+        const uint32_t dmask = (1u << d) - 1u;
+        for (int i = threadIdx.x; i < NB; i += kThThreads) hist[i] = 0;
+        __syncthreads();
+        visit([&](uint32_t x) {
+            const uint64_t xx = x;
+            if ((xx >> top) == (prefix >> top)) atomicAdd(&hist[(uint32_t)(xx >> shift) & dmask], 1u);
+        });
+        __syncthreads();
+        int c = 0;
+#pragma unroll
+        for (int u = 0; u < BPT; ++u) c += (int)hist[threadIdx.x * BPT + u];
+        int total;
+        const int inc = block_inclusive_scan<kThThreads>(c, tmp, &total);
+        if (inc - c < rank && rank <= inc) {
+            int acc = inc - c;
+            for (int u = 0; u < BPT; ++u) {
+                const int bin = threadIdx.x * BPT + u;
+                const int nx = acc + (int)hist[bin];
+                if (acc < rank && rank <= nx) {
+                    sh[0] = bin;
+                    sh[1] = acc;
+                    sh[2] = total - nx;
+                }
+                acc = nx;
+            }
+        }
+        __syncthreads();
+        prefix |= (uint64_t)sh[0] << shift;
+        rank -= sh[1];
+        *gt += sh[2];
+        __syncthreads();
+    }
+    return (uint32_t)prefix;
+}
+
+// One block per instance: theta key, #keys above it (state) and theta_out.
+__global__ __launch_bounds__(kThThreads) void th_final_kernel(const float* __restrict__ scores,
+                                                             const int64_t* __restrict__ offsets, int Hq,
+                                                             DevCfg cfg, int SL, int64_t S,
+                                                             const uint32_t* __restrict__ cand,
+                                                             const uint32_t* __restrict__ cnt,
+                                                             const uint32_t* __restrict__ dhist,
                                                              int64_t* __restrict__ state, float* __restrict__ theta_out) {
-    __shared__ uint32_t hist[4096];
-    __shared__ int64_t sbuf[2];
-    __shared__ int tmp[kOsThreads / 64];
-    __shared__ uint32_t scnt[kOsMaxSL], spre[kOsMaxSL + 1];
+    static_assert(kDigitBins / 2 == kThThreads, "one word of digit bins per thread");
+    __shared__ uint32_t xs[kCap];
+    __shared__ int pre[kMaxSL + 1];
+    __shared__ uint32_t hist[kDigitBins];
+    __shared__ int tmp[kThThreads / 64];
+    __shared__ int64_t sh[4];
+    __shared__ uint32_t nd;
     const int inst = blockIdx.x;
-    int64_t* st = state + inst * 8;
-    if (st[kStFlag] != kFlagActive) {
+    int64_t* st = state + (int64_t)inst * 8;
+    const int b = inst / Hq, h = inst % Hq;
+    const int64_t off = offsets[b];
+    const OsInst oi = os_instance(offsets[b + 1] - off, cfg);
+    if (oi.flag != kFlagActive) {
         if (theta_out && threadIdx.x == 0) theta_out[inst] = 0.f;
         return;
     }
-    const uint32_t d1 = (uint32_t)st[kStD1];
-    int64_t r = st[kStR1];
-    int64_t gt = st[kStGtBin];
-    // candidate counts of all slices, and their prefix, in LDS
-    for (int k = threadIdx.x; k < SL; k += kOsThreads) scnt[k] = cand_cnt[(size_t)inst * SL + k];
-    // digit 2: bits 19..8
-    for (int i = threadIdx.x; i < 4096; i += kOsThreads) hist[i] = 0;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t acc = 0;
-        for (int k = 0; k < SL; ++k) { spre[k] = acc; acc += scnt[k]; }
-        spre[SL] = acc;
-    }
-    __syncthreads();
-    const uint32_t total = spre[SL];
-    const uint32_t* cbase = cand + (size_t)inst * SL * kOsSlice;
-    auto cand_at = [&](uint32_t gi) {   // global candidate index -> key
-        int lo2 = 0, hi2 = SL - 1;
-        while (lo2 < hi2) {
-            const int mid = (lo2 + hi2 + 1) >> 1;
-            if (spre[mid] <= gi) lo2 = mid; else hi2 = mid - 1;
+    const int64_t m = oi.end - oi.beg;
+    const uint32_t klo = (uint32_t)st[kStLo], khi = (uint32_t)st[kStHi];
+    const int nsl = (int)((m + kSlice - 1) / kSlice);
+    const int t = threadIdx.x;
+    // slice counts (two slices per thread) and the digit histogram (one word per thread)
+    const uint32_t* cs = cnt + (size_t)inst * SL * 2;
+    int c0 = 0, c1 = 0, l0 = 0, l1 = 0;
+    const int s0 = 2 * t;
+    if (s0 < nsl) { l0 = (int)cs[2 * s0]; c0 = (int)cs[2 * s0 + 1]; }
+    if (s0 + 1 < nsl) { l1 = (int)cs[2 * s0 + 2]; c1 = (int)cs[2 * s0 + 3]; }
+    uint32_t dlo = 0, dhi = 0;
+    {
+        const uint32_t* dh = dhist + (size_t)inst * SL * (kDigitBins / 2) + t;
+        int sl = 0;
+        for (; sl + 8 <= nsl; sl += 8) {
+            uint32_t w[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) w[u] = dh[(size_t)(sl + u) * (kDigitBins / 2)];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) { dlo += w[u] & 0xffffu; dhi += w[u] >> 16; }
         }
-        return cbase[(size_t)lo2 * kOsSlice + (gi - spre[lo2])];
-    };
-    for (uint32_t j0 = threadIdx.x; j0 < total; j0 += 8 * kOsThreads) {
-        uint32_t key[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) key[u] = (j0 + u * kOsThreads < total) ? cand_at(j0 + u * kOsThreads) : 0u;
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-            if (j0 + u * kOsThreads < total) atomicAdd(&hist[(key[u] >> 8) & 0xfffu], 1u);
+        for (; sl < nsl; ++sl) {
+            const uint32_t w = dh[(size_t)sl * (kDigitBins / 2)];
+            dlo += w & 0xffffu;
+            dhi += w >> 16;
+        }
     }
+    int nmid, nlo;
+    const int incl = block_inclusive_scan<kThThreads>(c0 + c1, tmp, &nmid);
+    block_inclusive_scan<kThThreads>(l0 + l1, tmp, &nlo);
+    if (s0 < nsl) pre[s0] = incl - c0 - c1;
+    if (s0 + 1 < nsl) pre[s0 + 1] = incl - c1;
+    if (t == 0) { pre[nsl] = nmid; nd = 0; }
+    hist[2 * t] = dlo;
+    hist[2 * t + 1] = dhi;
     __syncthreads();
-    int64_t below;
-    const int d2 = find_digit_4096(hist, r, &below, sbuf, tmp);
-    {
-        // candidates in digits above d2
-        int64_t tot = 0;
-        for (int i = threadIdx.x; i < 4096; i += kOsThreads)
-            if (i > d2) tot += hist[i];
-        int t32 = wave_sum_i((int)tot);
-        if ((threadIdx.x & 63) == 0) tmp[threadIdx.x >> 6] = t32;
-        __syncthreads();
-        int64_t all = 0;
-        for (int w = 0; w < kOsThreads / 64; ++w) all += tmp[w];
-        gt += all;
-        __syncthreads();
-    }
-    r -= below;
-    // digit 3: bits 7..0 among keys with prefix (d1, d2)
-    for (int i = threadIdx.x; i < 4096; i += kOsThreads) hist[i] = 0;
-    __syncthreads();
-    for (uint32_t j0 = threadIdx.x; j0 < total; j0 += 8 * kOsThreads) {
-        uint32_t key[8];
+    int64_t gt = 0;
+    uint32_t key = 0;
+    const int64_t r = oi.rank;
+    bool whole_row = !(nlo < r && r <= (int64_t)nlo + nmid);
+    if (!whole_row) {
+        gt = m - nlo - nmid;                       // keys above hi
+        int64_t rr = r - nlo;
+        if (klo == khi) {
+            key = klo;
+        } else {
+            // top digit from the summed slice histograms
+            const int dsh = top_shift(khi - klo);
+            const int cd = (int)(dlo + dhi);
+            int tot;
+            const int inc = block_inclusive_scan<kThThreads>(cd, tmp, &tot);
+            if (inc - cd < rr && rr <= inc) {
+                const int below = inc - cd;
+                const bool first = rr <= below + (int)dlo;
+                sh[0] = first ? 2 * t : 2 * t + 1;
+                sh[1] = first ? below : below + (int)dlo;
+                sh[2] = tot - (first ? below + (int)dlo : inc);
+                sh[3] = first ? dlo : dhi;
+            }
+            __syncthreads();
+            const uint32_t D = (uint32_t)sh[0];
+            rr -= sh[1];
+            gt += sh[2];
+            const int64_t nD = sh[3];
+            if (nD > kCap) {
+                whole_row = true;
+            } else {
+                // gather the candidates of digit D (low bits only) into LDS
+                const uint32_t low = dsh ? ((1u << dsh) - 1u) : 0u;
+                for (int i0 = t; i0 < nmid; i0 += 16 * kThThreads) {
+                    uint32_t v[16];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) key[u] = (j0 + u * kOsThreads < total) ? cand_at(j0 + u * kOsThreads) : 0u;
+                    for (int u = 0; u < 16; ++u) {
+                        const int i = i0 + u * kThThreads;
+                        v[u] = 0;
+                        if (i < nmid) {
+                            int a = 0, z = nsl - 1;          // last slice with pre[slice] <= i
+                            while (a < z) {
+                                const int mid = (a + z + 1) >> 1;
+                                if (pre[mid] <= i) a = mid; else z = mid - 1;
+                            }
+                            v[u] = cand[((size_t)inst * SL + a) * kSlice + (i - pre[a])];
+                        }
+                    }
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-            if (j0 + u * kOsThreads < total && (int)((key[u] >> 8) & 0xfffu) == d2) atomicAdd(&hist[key[u] & 0xffu], 1u);
+                    for (int u = 0; u < 16; ++u) {
+                        const int i = i0 + u * kThThreads;
+                        const uint32_t x = v[u] - klo;
+                        if (i < nmid && (x >> dsh) == D) xs[atomicAdd(&nd, 1u)] = x & low;
+                    }
+                }
+                __syncthreads();
+                const int cntD = (int)nd;
+                const uint32_t xl = radix_rank(
+                    [&](auto f) {
+                        for (int i = t; i < cntD; i += kThThreads) f(xs[i]);
+                    },
+                    dsh, rr, hist, tmp, sh, &gt);
+                key = klo + ((D << dsh) | xl);
+            }
+        }
     }
-    __syncthreads();
-    const int d3 = find_digit_4096(hist, r, &below, sbuf, tmp);   // bins >= 256 are empty
-    {
-        int64_t tot = 0;
-        for (int i = threadIdx.x; i < 256; i += kOsThreads)
-            if (i > d3) tot += hist[i];
-        int t32 = wave_sum_i((int)tot);
-        if ((threadIdx.x & 63) == 0) tmp[threadIdx.x >> 6] = t32;
-        __syncthreads();
-        int64_t all = 0;
-        for (int w = 0; w < kOsThreads / 64; ++w) all += tmp[w];
-        gt += all;
+    if (whole_row) {
+        // the answer lies outside the bracket or its digit overflows LDS: whole row
+        gt = 0;
+        const float* row = scores + (int64_t)h * S + off;
+        key = radix_rank(
+            [&](auto f) {
+                for_each_f32<kThThreads, 4>(row, oi.beg, oi.end, [&](int64_t, float v, bool ok) {
+                    if (ok) f(order_key(v));
+                });
+            },
+            32, r, hist, tmp, sh, &gt);
     }
-    if (threadIdx.x == 0) {
-        uint32_t key = (d1 << 20) | ((uint32_t)d2 << 8) | (uint32_t)d3;
+    if (t == 0) {
         st[kStKey] = key;
         st[kStGt] = gt;
         if (theta_out) theta_out[inst] = key_to_float(key);
@@ -401,109 +547,153 @@ __global__ __launch_bounds__(kChunk) void vote_kernel(const float* __restrict__ 
     }
 }
 
-// Sums the key histograms of the blocks of sequence b into tot[] and those of the blocks
-// before block c into bef[] (rows staged through LDS, 128 blocks at a time).
-__device__ void sum_block_hists(const uint32_t* __restrict__ hist, int64_t first, int64_t nch, int64_t c,
-                                uint32_t (*stage)[kVoteBins], uint32_t* tot, uint32_t* bef) {
-    if (threadIdx.x < kVoteBins) { tot[threadIdx.x] = 0; bef[threadIdx.x] = 0; }
-    for (int64_t k0 = 0; k0 < nch; k0 += 128) {
-        const int64_t rows = nch - k0 < 128 ? nch - k0 : 128;
+// ------------------------------------------------------------------ vote scan
+// One block per sequence.  The chunk histograms of the sequence are staged in LDS, kScanTile
+// rows at a time (one tile covers sequences of up to kScanTile * kChunk tokens, which then
+// take one pass).  From the key totals: need = K - |F|, the boundary key v* (largest key
+// whose suffix count reaches need; none when need == 0), gt = #keys above v* and
+// need_eq = need - gt.  Per chunk c: eqb(c) = #tokens with key v* in earlier chunks and
+// base(c) = forced_before(first token of c) + #keys above v* in earlier chunks
+// + min(eqb(c), need_eq), the output rank of the chunk's first selected token.
+constexpr int kScanThreads = 1024;
+constexpr int kScanTile = 256;
+
+__global__ __launch_bounds__(kScanThreads) void vote_scan_kernel(const int64_t* __restrict__ offsets, DevCfg cfg,
+                                                                const uint32_t* __restrict__ hist,
+                                                                int2* __restrict__ chunk_info,
+                                                                int64_t* __restrict__ seq_info,
+                                                                int64_t* __restrict__ count_out) {
+    constexpr int NG = kScanThreads / kVoteBins;    // row groups for the column sums
+    constexpr int V4 = kVoteBins / 4;               // uint4 per histogram row
+    __shared__ uint4 stage[kScanTile * V4];
+    __shared__ uint32_t part[NG][kVoteBins];
+    __shared__ uint32_t tot[kVoteBins];
+    __shared__ int tmp[kScanThreads / 64];
+    __shared__ int64_t sh[2];
+    const int b = blockIdx.x;
+    const int t = threadIdx.x;
+    int64_t first = 0, kpre = 0;
+    for (int i = 0; i < b; ++i) {
+        const int64_t ni = offsets[i + 1] - offsets[i];
+        first += (ni + kChunk - 1) / kChunk;
+        kpre += budget_k(ni, cfg.bnum, cfg.bden, cfg.sink, cfg.local);
+    }
+    const int64_t n = offsets[b + 1] - offsets[b];
+    const int64_t nch = (n + kChunk - 1) / kChunk;
+    const int64_t K = budget_k(n, cfg.bnum, cfg.bden, cfg.sink, cfg.local);
+    const int64_t need = K - forced_before(n, n, cfg.sink, cfg.local);
+    const uint4* hrows = reinterpret_cast<const uint4*>(hist + (size_t)first * kVoteBins);
+    auto load_tile = [&](int64_t c0, int64_t rows) {
+        for (int64_t e = t; e < rows * V4; e += kScanThreads) stage[e] = hrows[c0 * V4 + e];
+    };
+    // key totals
+    const int grp = t / kVoteBins, kb = t % kVoteBins;
+    uint32_t acc = 0;
+    for (int64_t c0 = 0; c0 < nch; c0 += kScanTile) {
+        const int64_t rows = nch - c0 < kScanTile ? nch - c0 : kScanTile;
         __syncthreads();
-        const int64_t ne = rows * kVoteBins;
-        for (int64_t e0 = threadIdx.x; e0 < ne; e0 += 16 * (int64_t)blockDim.x) {
-            uint32_t x[16];
-#pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                const int64_t e = e0 + (int64_t)u * blockDim.x;
-                x[u] = e < ne ? hist[(size_t)(first + k0) * kVoteBins + e] : 0u;
-            }
-#pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                const int64_t e = e0 + (int64_t)u * blockDim.x;
-                if (e < ne) stage[e / kVoteBins][e % kVoteBins] = x[u];
-            }
-        }
+        load_tile(c0, rows);
         __syncthreads();
-        if (threadIdx.x < kVoteBins) {
-            uint32_t a = 0, p = 0;
-            for (int64_t r = 0; r < rows; ++r) {
-                const uint32_t x = stage[r][threadIdx.x];
-                a += x;
-                if (k0 + r < c) p += x;
-            }
-            tot[threadIdx.x] += a;
-            bef[threadIdx.x] += p;
+        if (grp < NG) {
+            const uint32_t* st32 = reinterpret_cast<const uint32_t*>(stage);
+            for (int64_t r = grp; r < rows; r += NG) acc += st32[r * kVoteBins + kb];
         }
     }
+    if (grp < NG) part[grp][kb] = acc;
     __syncthreads();
+    if (t < kVoteBins) {
+        uint32_t a = 0;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) a += part[g][t];
+        tot[t] = a;
+    }
+    __syncthreads();
+    {
+        const int v = kVoteBins - 1 - t;
+        const int cv = t < kVoteBins ? (int)tot[v] : 0;
+        int all;
+        const int incl = block_inclusive_scan<kScanThreads>(cv, tmp, &all);
+        if (t == 0) { sh[0] = kVoteBins; sh[1] = 0; }
+        __syncthreads();
+        if (need > 0 && t < kVoteBins && incl >= need && incl - cv < need) { sh[0] = v; sh[1] = incl - cv; }
+        __syncthreads();
+    }
+    const int vs = (int)sh[0];
+    const int64_t need_eq = need - sh[1];
+    // per-chunk bases (the last tile is still staged when the sequence fits in one)
+    int64_t carry_gt = 0, carry_eq = 0;
+    for (int64_t c0 = 0; c0 < nch; c0 += kScanTile) {
+        const int64_t rows = nch - c0 < kScanTile ? nch - c0 : kScanTile;
+        if (nch > kScanTile) {
+            __syncthreads();
+            load_tile(c0, rows);
+            __syncthreads();
+        }
+        int above = 0, eq = 0;
+        if (t < rows) {
+            const uint4* hr = stage + (size_t)t * V4;
+#pragma unroll
+            for (int k4 = 0; k4 < V4; ++k4) {
+                const uint4 w = hr[k4];
+                const int xs4[4] = {(int)w.x, (int)w.y, (int)w.z, (int)w.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int k = 4 * k4 + e;
+                    above += k > vs ? xs4[e] : 0;
+                    eq += k == vs ? xs4[e] : 0;
+                }
+            }
+        }
+        int ta, te;
+        const int ia = block_inclusive_scan<kScanThreads>(above, tmp, &ta);
+        const int ie = block_inclusive_scan<kScanThreads>(eq, tmp, &te);
+        if (t < rows) {
+            const int64_t gtb = carry_gt + ia - above, eqb = carry_eq + ie - eq;
+            const int64_t base = forced_before((c0 + t) * kChunk, n, cfg.sink, cfg.local) + gtb +
+                                 (eqb < need_eq ? eqb : need_eq);
+            chunk_info[first + c0 + t] = make_int2((int)base, (int)eqb);
+        }
+        carry_gt += ta;
+        carry_eq += te;
+    }
+    if (t == 0) {
+        seq_info[b * 4 + 0] = kpre;
+        seq_info[b * 4 + 1] = K;
+        seq_info[b * 4 + 2] = vs;
+        seq_info[b * 4 + 3] = need_eq;
+        count_out[b] = K;
+    }
 }
 
 // ------------------------------------------------------------ vote compaction
-// One thread per token.  The boundary key v* is the largest key whose suffix count reaches
-// need = K - |F|; every non-forced token above v*, the first (need - #above) tokens equal to
-// v* in position order and every forced token are written, ascending, at their rank.
+// One thread per token: every forced token, every non-forced token above v* and the first
+// (need_eq - eqb) tokens equal to v* of the chunk, written ascending at their rank.
 __global__ __launch_bounds__(kChunk) void compact_vote_kernel(const int64_t* __restrict__ offsets, int B,
-                                                             DevCfg cfg, const uint8_t* __restrict__ keys,
-                                                             const uint32_t* __restrict__ hist,
-                                                             int32_t* __restrict__ idx_out,
-                                                             int64_t* __restrict__ count_out) {
-    __shared__ uint32_t stage[128][kVoteBins];
-    __shared__ uint32_t tot[kVoteBins], bef[kVoteBins];
-    __shared__ int64_t sh[4];
+                                                             const uint8_t* __restrict__ keys,
+                                                             const int2* __restrict__ chunk_info,
+                                                             const int64_t* __restrict__ seq_info,
+                                                             int32_t* __restrict__ idx_out) {
     __shared__ int tmp[kChunk / 64];
     int b;
     int64_t first, nch, t0, len;
     if (!find_chunk(offsets, B, blockIdx.x, b, first, nch, t0, len)) return;
-    const int64_t off = offsets[b], n = offsets[b + 1] - off;
-    const int64_t c = blockIdx.x - first;
-    sum_block_hists(hist, first, nch, c, stage, tot, bef);
-    const int64_t K = budget_k(n, cfg.bnum, cfg.bden, cfg.sink, cfg.local);
-    const int64_t need = K - forced_before(n, n, cfg.sink, cfg.local);
-    // suffix counts over the keys (thread t holds key kVoteBins - 1 - t); v* is the largest
-    // key whose suffix count reaches `need` (none when need == 0)
-    {
-        const int t = threadIdx.x;
-        const int v = kVoteBins - 1 - t;
-        const int cnt = (t < kVoteBins) ? (int)tot[v] : 0;
-        int all;
-        const int incl = block_inclusive_scan<kChunk>(cnt, tmp, &all);
-        if (t == 0) { sh[0] = kVoteBins; sh[1] = 0; }
-        __syncthreads();
-        if (need > 0 && t < kVoteBins && incl >= need && incl - cnt < need) { sh[0] = v; sh[1] = incl - cnt; }
-        __syncthreads();
-    }
-    const int vs = (int)sh[0];
-    const int64_t gt = sh[1];
-    {
-        const int t = threadIdx.x;
-        const int x = (t < kVoteBins && t > vs) ? (int)bef[t] : 0;
-        int gtb;
-        block_inclusive_scan<kChunk>(x, tmp, &gtb);
-        if (t == 0) {
-            const int64_t eqb = vs < kVoteBins ? bef[vs] : 0;
-            const int64_t need_eq = need - gt;
-            sh[1] = need_eq;
-            sh[2] = eqb;
-            sh[3] = forced_before(t0, n, cfg.sink, cfg.local) + gtb + (eqb < need_eq ? eqb : need_eq);
-            if (c == 0) count_out[b] = K;
-        }
-    }
-    __syncthreads();
-    const int64_t need_eq = sh[1], eqb = sh[2], base = sh[3];
+    const int64_t off = offsets[b];
     const int64_t i = threadIdx.x;
     const uint8_t kk = i < len ? keys[off + t0 + i] : 0;
+    const int2 ci = chunk_info[blockIdx.x];
+    const int64_t kpre = seq_info[b * 4 + 0], K = seq_info[b * 4 + 1];
+    const int vs = (int)seq_info[b * 4 + 2];
+    const int64_t need_eq = seq_info[b * 4 + 3];
     const int eqf = (i < len && kk != 255 && kk == vs) ? 1 : 0;
-    int tot_eq;
-    const int eq_rank = block_inclusive_scan<kChunk>(eqf, tmp, &tot_eq) - eqf;
+    int tot;
+    const int eq_rank = block_inclusive_scan<kChunk>(eqf, tmp, &tot) - eqf;
     int sel = 0;
     if (i < len) {
         if (kk == 255) sel = 1;
         else if (vs < kVoteBins && kk > vs) sel = 1;
-        else if (eqf) sel = (eqb + eq_rank < need_eq) ? 1 : 0;
+        else if (eqf) sel = ((int64_t)ci.y + eq_rank < need_eq) ? 1 : 0;
     }
-    int tot_sel;
-    const int64_t p = base + block_inclusive_scan<kChunk>(sel, tmp, &tot_sel) - sel;
-    const int64_t kpre = kpre_of(offsets, b, cfg);
+    const int64_t p = ci.x + block_inclusive_scan<kChunk>(sel, tmp, &tot) - sel;
     if (sel && p < K) idx_out[kpre + p] = (int32_t)(t0 + i);
 }
 
@@ -603,8 +793,9 @@ static DevCfg dev_cfg(const SelectConfig& c) {
 struct SelectLayout {
     int SL;
     int64_t nitems, Ntot;
-    uint32_t *part1, *cand, *cand_cnt, *hist, *phcnt;
-    int64_t* state;
+    uint32_t *cand, *cnt, *dhist, *hist, *phcnt;
+    int64_t *state, *seq_info;
+    int2* chunk_info;
     uint8_t *votes, *keys;
     size_t bytes;
 };
@@ -619,19 +810,21 @@ static SelectLayout select_layout(void* ws, const int64_t* offsets_host, int B, 
         if (o.end - o.beg > maxm) maxm = o.end - o.beg;
         items += (n + kChunk - 1) / kChunk;
     }
-    L.SL = (int)((maxm + kOsSlice - 1) / kOsSlice);
+    L.SL = (int)((maxm + kSlice - 1) / kSlice);
     if (L.SL < 1) L.SL = 1;
     L.nitems = items;
     L.Ntot = offsets_host[B];
     WsCarver w(ws);
     const size_t inst = (size_t)B * Hq;
-    L.part1 = w.take<uint32_t>(inst * L.SL * 2048);
-    L.cand = w.take<uint32_t>(inst * L.SL * kOsSlice);
-    L.cand_cnt = w.take<uint32_t>(inst * L.SL);
+    L.cand = w.take<uint32_t>(inst * L.SL * kSlice);
+    L.cnt = w.take<uint32_t>(inst * L.SL * 2);
+    L.dhist = w.take<uint32_t>(inst * L.SL * (kDigitBins / 2));
     L.state = w.take<int64_t>(inst * 8);
     L.votes = w.take<uint8_t>((size_t)L.Ntot + 16);
     L.keys = w.take<uint8_t>((size_t)L.Ntot + 16);
     L.hist = w.take<uint32_t>((size_t)items * kVoteBins);
+    L.chunk_info = w.take<int2>((size_t)items);
+    L.seq_info = w.take<int64_t>((size_t)B * 4);
     L.phcnt = c.mode == 1 ? w.take<uint32_t>((size_t)Hq * items * 2) : nullptr;
     L.bytes = w.size();
     return L;
@@ -645,22 +838,22 @@ hipError_t launch_select(const float* scores, int64_t S, const int64_t* offsets_
                          int B, int Hq, const SelectConfig& c, int32_t* idx_out, int64_t* count_out, float* theta_out,
                          uint8_t* votes_out, void* ws, size_t ws_bytes, hipStream_t stream) {
     SelectLayout L = select_layout(ws, offsets_host, B, Hq, c);
-    if (L.bytes > ws_bytes) return hipErrorInvalidValue;
+    if (L.bytes > ws_bytes || L.SL > kMaxSL) return hipErrorInvalidValue;
     DevCfg d = dev_cfg(c);
     const unsigned inst = (unsigned)(B * Hq);
-    hipLaunchKernelGGL(os_hist_kernel, dim3(L.SL, inst), dim3(kOsThreads), 0, stream, scores, offsets_dev, B, Hq, d,
-                       L.SL, S, L.part1);
-    hipLaunchKernelGGL(os_collect_kernel, dim3(L.SL, inst), dim3(kOsThreads), 0, stream, scores, offsets_dev, B, Hq, d,
-                       L.SL, S, L.part1, L.cand, L.cand_cnt, L.state);
-    hipLaunchKernelGGL(os_final_kernel, dim3(inst), dim3(kOsThreads), 0, stream, B, Hq, L.SL, L.cand, L.cand_cnt,
-                       L.state, c.mode == 0 ? theta_out : nullptr);
+    hipLaunchKernelGGL(th_collect_kernel, dim3(L.SL, inst), dim3(kColThreads), 0, stream, scores, offsets_dev, Hq, d,
+                       L.SL, S, L.state, L.cand, L.cnt, L.dhist);
+    hipLaunchKernelGGL(th_final_kernel, dim3(inst), dim3(kThThreads), 0, stream, scores, offsets_dev, Hq, d, L.SL, S,
+                       L.cand, L.cnt, L.dhist, L.state, c.mode == 0 ? theta_out : nullptr);
     if (L.nitems == 0) return hipGetLastError();
     if (c.mode == 0) {
         uint8_t* votes = votes_out ? votes_out : L.votes;
         hipLaunchKernelGGL(vote_kernel, dim3((unsigned)L.nitems), dim3(kChunk), 0, stream, scores, offsets_dev,
                            B, Hq, d, S, L.state, votes, L.keys, L.hist);
+        hipLaunchKernelGGL(vote_scan_kernel, dim3((unsigned)B), dim3(kScanThreads), 0, stream, offsets_dev, d, L.hist,
+                           L.chunk_info, L.seq_info, count_out);
         hipLaunchKernelGGL(compact_vote_kernel, dim3((unsigned)L.nitems), dim3(kChunk), 0, stream, offsets_dev,
-                           B, d, L.keys, L.hist, idx_out, count_out);
+                           B, L.keys, L.chunk_info, L.seq_info, idx_out);
     } else {
         hipLaunchKernelGGL(ph_count_kernel, dim3((unsigned)L.nitems, Hq), dim3(kChunk), 0, stream, scores,
                            offsets_dev, B, Hq, d, S, L.state, L.nitems, L.phcnt);

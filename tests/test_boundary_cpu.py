@@ -22,7 +22,7 @@ def header_functions():
 def test_exports_match_header():
     lib = _lib.load()
     names = header_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.SIGNATURES)
@@ -69,18 +69,27 @@ def test_index_append_validation():
 def test_score_head_validation(Hq, Hkv, code):
     L = _lib.load()
     o = _offs([0, 100])
-    assert L.ts_score(FAKE, FAKE, FAKE, FAKE, o, 1, Hq, Hkv, FAKE, None) == code
+    assert L.ts_score(FAKE, FAKE, FAKE, FAKE, o, 1, Hq, Hkv, FAKE, FAKE, 1 << 20, None) == code
     assert err()
 
 
 def test_offsets_validation():
     L = _lib.load()
-    assert L.ts_score(FAKE, FAKE, FAKE, FAKE, _offs([1, 100]), 1, 32, 8, FAKE, None) == -1
-    assert L.ts_score(FAKE, FAKE, FAKE, FAKE, _offs([0, 100, 50]), 2, 32, 8, FAKE, None) == -1
-    assert L.ts_score(FAKE, FAKE, FAKE, FAKE, _offs([0, 100]), 0, 32, 8, FAKE, None) == -1
+    assert L.ts_score(FAKE, FAKE, FAKE, FAKE, _offs([1, 100]), 1, 32, 8, FAKE, FAKE, 1 << 20, None) == -1
+    assert L.ts_score(FAKE, FAKE, FAKE, FAKE, _offs([0, 100, 50]), 2, 32, 8, FAKE, FAKE, 1 << 20, None) == -1
+    assert L.ts_score(FAKE, FAKE, FAKE, FAKE, _offs([0, 100]), 0, 32, 8, FAKE, FAKE, 1 << 20, None) == -1
     p = _params()
     assert L.ts_select(FAKE, FAKE, _offs([0, 0]), 1, 32, 8, ctypes.byref(p), FAKE, FAKE, None, None, FAKE, 1 << 40,
                        None) == -1  # empty sequence
+
+
+def test_score_workspace_validation():
+    L = _lib.load()
+    need = L.ts_score_workspace_bytes(1, 32)
+    assert need >= 32 * 32 * 4
+    assert L.ts_score_workspace_bytes(0, 32) == 0
+    assert L.ts_score(FAKE, FAKE, FAKE, FAKE, _offs([0, 100]), 1, 32, 8, FAKE, FAKE, need - 1, None) == -3
+    assert "workspace" in err()
 
 
 def test_select_validation():

@@ -50,6 +50,16 @@ def test_ragged_batch(lengths, budget, mode):
     check_staged(Step(x, mode=mode).run())
 
 
+# every (Hkv, G) pair the library instantiates, a ragged two-sequence batch that spans
+# several 512-token score blocks and ends in partial blocks
+@pytest.mark.parametrize("Hq,Hkv", [(1, 1), (2, 1), (4, 1), (8, 1), (2, 2), (4, 2), (8, 2), (16, 2), (4, 4), (8, 4),
+                                    (16, 4), (32, 4), (8, 8), (16, 8), (32, 8), (64, 8)])
+@pytest.mark.parametrize("mode", [api.MODE_VOTE, api.MODE_PER_HEAD])
+def test_head_layouts(Hq, Hkv, mode):
+    x = synth.make_decode(4, [1537, 700], Hq, Hkv, 8, False, (1, 5), 11)
+    check_staged(Step(x, mode=mode, local=64).run())
+
+
 @pytest.mark.parametrize("mode", [api.MODE_VOTE, api.MODE_PER_HEAD])
 def test_full_budget_equals_dense(mode):
     x = synth.make_decode(1, [3000], 8, 2, 16, False, (1, 1), 5)
@@ -85,6 +95,29 @@ def test_zero_query_ties_to_lowest_positions():
         check_staged(st)
         idx = st.sel["idx"].cpu().numpy()[:500]
         assert np.array_equal(idx, np.r_[0:244, 4744:5000])
+
+
+# rows longer than the LDS candidate capacity whose threshold sits in a mass of equal
+# scores: the sampled bracket collapses onto the tied key and the final kernel falls back
+# to the whole-row radix select
+@pytest.mark.parametrize("zero_frac", [1.0, 0.95])
+def test_heavy_ties_long_rows(zero_frac):
+    x = synth.make_decode(1, [40000], 8, 2, 0, False, (1, 5), 6)
+    nz = int(40000 * zero_frac)
+    rng = np.random.default_rng(6)
+    rows = rng.permutation(40000)[:nz]
+    x.K[rows] = 0                     # zero keys -> zero index rows -> scores exactly 0
+    for mode in (api.MODE_VOTE, api.MODE_PER_HEAD):
+        st = Step(x, mode=mode).run()
+        check_staged(st)
+
+
+# a row longer than one tile of the vote scan (256 chunks of 1024 tokens) and longer than
+# the LDS candidate capacity of the threshold select
+@pytest.mark.parametrize("mode", [api.MODE_VOTE, api.MODE_PER_HEAD])
+def test_long_row(mode):
+    x = synth.make_decode(3, [300000], 8, 2, 300, False, (1, 5), 9)
+    check_staged(Step(x, mode=mode).run())
 
 
 def test_median_threshold_and_vmin():
