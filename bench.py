@@ -26,6 +26,27 @@ PEAK_GBPS = 8000.0       # MI355X HBM3E peak
 METRIC = "µs/decode step + HBM GB/s (% peak), 128K ctx, 20% budget, 1 MI355X"
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+DECODE_SRC = os.path.join(ROOT, "query_aware_sparse_index_amd", "csrc", "decode.hip")
+
+
+def measured_traffic(mode, n, budget):
+    """HBM bytes per ts_sparse_decode launch from the committed counter measurement
+    (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy of known size), or None when there is
+    none for this workload or the decode source has changed since it was taken."""
+    import hashlib
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        with open(DECODE_SRC, "rb") as f:
+            digest = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("decode_hip_sha256") != digest or rec.get("mode") != mode or rec.get("budget") != budget:
+        return None
+    return rec.get("bytes_per_launch")
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -39,12 +60,70 @@ def parse():
     ap.add_argument("--no-extra", action="store_true", help="skip dense / warm / graph side measurements")
     ap.add_argument("--cpu-steps", type=int, default=10)
     ap.add_argument("--isolate", action="store_true", help="also time each call alone after a flush")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="end with three plain 256 MiB elementwise copies (torch.neg on fp32), a reference "
+                         "for the HBM byte counters")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None,
+                    help="no GPU: turn two rocprofv3 --pmc counter_collection.csv files (FETCH_SIZE, then "
+                         "WRITE_SIZE, of a --copy-probe run) into the per-launch HBM traffic record")
     ap.add_argument("--out", default=None)
     return ap.parse_args()
 
 
+PROBE_BYTES = 256 << 20
+
+
+def traffic_record(fetch_csv, write_csv, out_path, mode=0, budget=20):
+    """Per-launch HBM bytes of ts_sparse_decode from FETCH_SIZE / WRITE_SIZE (KiB per
+    dispatch), each scaled by the factor that maps the probe copy's counter onto its known
+    256 MiB.  Also returns a per-kernel table (mean KiB per dispatch, scaled bytes)."""
+    import csv
+    import hashlib
+
+    def load(path, counter):
+        rows = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r.get("Counter_Name") != counter:
+                    continue
+                rows.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return rows
+
+    fetch = load(fetch_csv, "FETCH_SIZE")
+    write = load(write_csv, "WRITE_SIZE")
+    probe = lambda d: [v for k, vs in d.items() if "neg_kernel" in k for v in vs]
+    pf, pw = probe(fetch), probe(write)
+    if not pf or not pw:
+        raise SystemExit("no probe copy (neg_kernel) in the counter files: run the profiled bench with --copy-probe")
+    f_scale = (PROBE_BYTES / 1024.0) / float(np.median(pf))
+    w_scale = (PROBE_BYTES / 1024.0) / float(np.median(pw))
+    table = {}
+    for k in sorted(set(fetch) | set(write)):
+        fk = float(np.mean(fetch.get(k, [0.0])))
+        wk = float(np.mean(write.get(k, [0.0])))
+        table[k] = {"fetch_kib": round(fk, 1), "write_kib": round(wk, 1),
+                    "bytes": int(1024 * (fk * f_scale + wk * w_scale))}
+    dec = [k for k in table if "decode_partial_kernel" in k or "decode_merge_kernel" in k]
+    with open(DECODE_SRC, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()
+    rec = {"bytes_per_launch": int(sum(table[k]["bytes"] for k in dec)),
+           "kernels": {k: table[k] for k in dec},
+           "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+           "mode": mode, "budget": budget, "decode_hip_sha256": digest}
+    with open(out_path, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    return rec, table
+
+
 def main():
     args = parse()
+    if args.traffic_from:
+        rec, table = traffic_record(args.traffic_from[0], args.traffic_from[1], TRAFFIC_FILE)
+        for k, v in table.items():
+            print(f"{v['fetch_kib']:14.1f} {v['write_kib']:14.1f} {v['bytes'] / 1e6:10.2f} MB  {k[:90]}")
+        print(json.dumps({k: v for k, v in rec.items() if k != "kernels"}))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the decode-step path of one attention layer runs on a single "
               "MI355X (see DESIGN.md for how it would shard); run with --gpus 1.", file=sys.stderr)
@@ -174,16 +253,44 @@ def main():
     k_mean = float(np.mean(ktot))
     if mode == api.MODE_VOTE:
         kv_bytes = k_mean * Hkv * 128 * 2 * 2          # one K and V row per KV head per selected token
-    else:
-        kv_bytes = k_mean * Hq * 128 * 2 * 2           # every query head reads its own list's rows
+    else:                                              # per KV head: the union of its heads' lists
+        Gq = Hq // Hkv
+        kl = int(ktot[-1])
+        lst = idx[:kl * Hq].cpu().numpy().reshape(Hq, kl)
+        kv_bytes = sum(len(np.unique(lst[g * Gq:(g + 1) * Gq])) for g in range(Hkv)) * 128 * 2 * 2
     idx_bytes = n_mean * Hkv * 32 * 2
     small = Hq * 128 * 2 + 128 * 32 * 4 + Hq * 128 * 4 + k_mean * 4
     step_bytes = idx_bytes + kv_bytes + small
     mean_us = float(step_us.mean())
     gbps = step_bytes / (mean_us * 1e-6) / 1e9
-    dec_us = float(parts["sparse_decode"].mean())
-    dec_bytes = kv_bytes + Hq * 128 * 2 + k_mean * 4
+
+    # the dominant call alone (ts_sparse_decode: gather kernel + LSE merge kernel), LLC flushed
+    # before each launch, on the stream the kernels run on; inputs of the last timed step
+    s_last = warm + steps - 1
+    (_, _), (qp_l, od_l, oh_l), ch_l, _ = calls[s_last]
+    dec_evs = []
+    for r in range(22):
+        if not args.no_flush:
+            do_flush()
+        st = stream_of()
+        a, b2 = ev(), ev()
+        a.record()
+        chk(L.ts_sparse_decode(qp_l, Kp, Vp, od_l, oh_l, idp, cnp, ch_l, mode, 1, Hq, Hkv, outp, wdp, ws_dec_n, st))
+        b2.record()
+        dec_evs.append((a, b2))
+    torch.cuda.synchronize()
+    dec_us = float(np.mean([a.elapsed_time(b2) * 1e3 for a, b2 in dec_evs[2:]]))
+    k_last = float(ktot[-1])
+    if mode == api.MODE_VOTE:
+        dec_bytes = k_last * Hkv * 128 * 2 * 2 + Hq * 128 * 2 + k_last * 4
+    else:
+        # per-head lists: a KV head's rows are needed once for the union of its G heads' lists
+        G = Hq // Hkv
+        lists = idx[:int(k_last) * Hq].cpu().numpy().reshape(Hq, int(k_last))
+        union_rows = sum(len(np.unique(lists[g * G:(g + 1) * G])) for g in range(Hkv))
+        dec_bytes = union_rows * 128 * 2 * 2 + Hq * 128 * 2 + k_last * Hq * 4
     dec_gbps = dec_bytes / (dec_us * 1e-6) / 1e9
+    traffic = measured_traffic(mode, n0 + warm + steps, args.budget)
 
     extra = {}
     if args.isolate:
@@ -265,6 +372,30 @@ def main():
             extra["graph_step_us"] = round(float(np.mean([a.elapsed_time(b) * 1e3 for a, b in g_us[3:]])), 2)
         except Exception as e:  # capture is an optional side measurement
             extra["graph_step_us"] = f"unavailable: {type(e).__name__}"
+        # SnapKV prefill-end compression at LLaMA-3-70B layer shapes (64 / 8 heads, w = 32,
+        # c = 4096, pool 3) over the same n, LLC flushed before each call
+        sx = synth.config5(n0)
+        qo_s, K_s, V_s = (torch.from_numpy(a.view(np.int16)).to(dev) for a in (sx.q_obs, sx.K, sx.V))
+        ws_s = torch.empty(api.snapkv_workspace_bytes(n0, 32, 64, 8, 4096), dtype=torch.uint8, device=dev)
+        api.snapkv_compress(qo_s, K_s, V_s, 4096, ws=ws_s)
+        sts = []
+        for i in range(12):
+            do_flush()
+            a, b = ev(), ev()
+            a.record()
+            api.snapkv_compress(qo_s, K_s, V_s, 4096, ws=ws_s)
+            b.record()
+            sts.append((a, b))
+        torch.cuda.synchronize()
+        snap_us = float(np.mean([a.elapsed_time(b) * 1e3 for a, b in sts[2:]]))
+        flop_pass = 2.0 * 64 * 32 * n0 * 128                       # one Q_obs K^T over all keys
+        snap_bytes = n0 * 8 * 128 * 2 + 2 * 4096 * 8 * 128 * 2 * 2   # K once + gather (read + write K, V)
+        extra["snapkv"] = {"workload": f"Hq=64 Hkv=8 n={n0} w=32 c=4096 pool 3", "us": round(snap_us, 2),
+                           "mfma_tflops_executed": round(2 * flop_pass / (snap_us * 1e-6) / 1e12, 1),
+                           "mfma_frac_bf16_peak": round(2 * flop_pass / (snap_us * 1e-6) / 2.5e15, 4),
+                           "algorithmic_tflops": round(flop_pass / (snap_us * 1e-6) / 1e12, 1),
+                           "algorithmic_gbps": round(snap_bytes / (snap_us * 1e-6) / 1e9, 1)}
+        del qo_s, K_s, V_s, ws_s
 
     cpu = None
     if not args.no_cpu:
@@ -313,14 +444,20 @@ def main():
         "pct_peak": round(100 * gbps / PEAK_GBPS, 1),
         "algorithmic_bytes_per_step": int(step_bytes),
         "breakdown_us": {k: round(float(v.mean()), 2) for k, v in parts.items()},
-        "roofline": {"bound": "hbm", "kernel": "ts_sparse_decode (gather decode + LSE merge)",
-                     "achieved": round(dec_gbps, 1), "peak": PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(dec_gbps / PEAK_GBPS, 4), "traffic": None,
+        "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(dec_gbps / PEAK_GBPS, 4), "traffic": traffic,
+                     "kernel": "ts_sparse_decode (decode_partial_kernel + decode_merge_kernel), alone, LLC flushed",
                      "algorithmic_bytes": int(dec_bytes), "avg_us": round(dec_us, 2)},
         "cpu_baseline": cpu,
         "wall_s_timed_loop": round(wall, 4),
     }
     res.update(extra)
+    if args.copy_probe:
+        src = torch.empty(PROBE_BYTES // 4, dtype=torch.float32, device=dev).fill_(3.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
     line = json.dumps(res)
     print(line, flush=True)
     if args.out:
