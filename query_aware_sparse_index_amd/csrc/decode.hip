@@ -147,7 +147,7 @@ __global__ __launch_bounds__(512) void decode_partial_kernel(const uint16_t* __r
     for (int hs = wid; hs < nslots; hs += NW) {
         float z = lane < len ? zb[hs * kDecCH + lane] : -INFINITY;   // kDecCH == 64
         float m = wave_max(z);
-        float e = lane < len ? exp2f(z - m) : 0.f;
+        float e = lane < len ? fast_exp2(z - m) : 0.f;
         if (lane < kDecCH) zb[hs * kDecCH + lane] = e;
         float l = wave_sum(e);
         if (lane == 0) { stat[hs * 2] = m; stat[hs * 2 + 1] = l; }
@@ -266,7 +266,7 @@ __global__ __launch_bounds__(1024) void decode_merge_kernel(const float* __restr
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             if (c0 + 64 * u < nch) {
-                const float w = exp2f(mm[u] - M);
+                const float w = fast_exp2(mm[u] - M);
                 a = fmaf(x[u], w, a);
                 l = fmaf(ll[u], w, l);
             }

@@ -77,6 +77,10 @@ __device__ __forceinline__ void for_each_f32(const float* __restrict__ row, int6
     if (threadIdx.x < hi - tail0) f(tail0 + threadIdx.x, row[tail0 + threadIdx.x], true);
 }
 
+// 2^x with one v_exp_f32 (about 1 ulp; results below 2^-126 flush to zero, exp2(-inf) = 0).
+// The library's exp2f adds a denormal rescaling around the same instruction.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Order-preserving map fp32 -> uint32 (ascending keys <=> ascending values); -0 maps to
 // the key of +0 so the two tie.
 __device__ __forceinline__ uint32_t order_key(float s) {

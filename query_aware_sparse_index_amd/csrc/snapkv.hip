@@ -16,6 +16,8 @@
 //   pass 2 (snap_pass_kernel<2>): p = 2^(s - LSE_r); the column sum over the R rows (a
 //                                 16-lane DPP butterfly per 16-row tile) gives imp[j] * R
 // Scores are kept in the log2 domain (s = q.k * log2(e)/sqrt(128)) so that exp2 is used.
+#include <utility>
+
 #include "qasi_device.h"
 #include "qasi_internal.h"
 
@@ -24,9 +26,9 @@ namespace qasi {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kSnapThreads = 256;     // 4 waves
-constexpr int kSnapNIT = 8;           // 16-key sub-tiles per wave
-constexpr int kSnapKT = 4 * 16 * kSnapNIT;   // keys per block (512)
+constexpr int kSnapThreads = 512;     // 8 waves
+constexpr int kSnapKTW = 4;           // 16-key tiles per wave, held in registers
+constexpr int kSnapKT = 8 * 16 * kSnapKTW;   // keys per block (512)
 constexpr float kSnapScale = 1.4426950408889634f / 11.313708498984761f;
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) {
@@ -35,137 +37,221 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) {
     return r;
 }
 
-// grid: x = KV head g, y = key block.  Q rows of group g: r = hh * w + t  <->  q_obs[t][g*G + hh].
-template <int PASS>
+// grid: x = KV head g, y = p < P.  The block stages Q_g in LDS once, then walks the key blocks
+// kb = p, p + P, ... of kSnapKT keys (concurrent blocks cover adjacent key ranges).  RT = R / 16
+// row tiles, R = G * w rows, row r = hh * w + t  <->  q_obs[t][g*G + hh].  In key block kb,
+// wave wid owns the key tiles kb * kSnapKT + (wid * kSnapKTW + kt) * 16, kt < kSnapKTW: their
+// A fragments (16 keys x 128 dims) sit in registers while the row tiles' B fragments stream
+// from LDS, each used for kSnapKTW MFMAs; the next key block's fragments are loaded into a
+// second register set while the current one is consumed.
+template <int PASS, int RT>
 __global__ __launch_bounds__(kSnapThreads) void snap_pass_kernel(const uint16_t* __restrict__ q_obs,
                                                                 const uint16_t* __restrict__ K, int64_t n, int w,
-                                                                int Hq, int Hkv, float2* __restrict__ pstat,
+                                                                int Hq, int Hkv, int64_t nblk,
+                                                                float2* __restrict__ pstat,
                                                                 const float* __restrict__ lse,
                                                                 float* __restrict__ imp) {
+    constexpr int R = RT * 16;
+    constexpr int NW = kSnapThreads / 64;
     extern __shared__ uint4 sQ[];   // [R][16] uint4 (128 bf16 per row), row-swizzled by (row & 15)
-    __shared__ float2 wstat[4][256];
+    __shared__ float2 wstat[(PASS == 1) ? NW : 1][(PASS == 1) ? R : 1];
+    __shared__ float2 mlst[(PASS == 1) ? NW * RT * 64 : 1];   // pass 1: running (max, sum) per lane
+    __shared__ float sL[(PASS == 2) ? R : 1];   // pass 2: LSE (log2 domain) of the rows
     const int g = blockIdx.x;
-    const int64_t kb = blockIdx.y;
-    const int G = Hq / Hkv, R = G * w, RT = R / 16;
+    const int p = blockIdx.y, P = gridDim.y;
+    const int G = Hq / Hkv;
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const int lr = lane & 15, lg = lane >> 4;
 
     // stage Q_g (R x 128 bf16) in LDS; 16-byte chunk c of row r goes to slot (c ^ (r & 15))
     for (int i = threadIdx.x; i < R * 16; i += kSnapThreads) {
-        int r = i / 16, c = i % 16;
-        int hh = r / w, t = r % w;
-        uint4 v = *reinterpret_cast<const uint4*>(q_obs + ((int64_t)t * Hq + g * G + hh) * kD + c * 8);
+        const int r = i / 16, c = i % 16;
+        const int hh = r / w, t = r % w;
+        const uint4 v = *reinterpret_cast<const uint4*>(q_obs + ((int64_t)t * Hq + g * G + hh) * kD + c * 8);
         sQ[r * 16 + (c ^ (r & 15))] = v;
     }
-    float lrow[16];   // pass 2: LSE of row c*16 + lr
-    if (PASS == 2) {
-#pragma unroll
-        for (int c = 0; c < 16; ++c) lrow[c] = (c < RT) ? lse[(int64_t)g * R + c * 16 + lr] : 0.f;
-    }
-    __syncthreads();
+    if (PASS == 2)
+        for (int r = threadIdx.x; r < R; r += kSnapThreads) sL[r] = lse[(int64_t)g * R + r];
 
-    float m[16], l[16];
+    // A fragments of key block kb: key jw(kb) + kt*16 + lr, dims 32 s + 8 lg .. +8
+    auto key0 = [&](int64_t kb) { return kb * kSnapKT + (int64_t)wid * kSnapKTW * 16; };
+    auto load = [&](bf16x8_t (&a)[kSnapKTW][4], int64_t kb) {
+        const int64_t jw = key0(kb);
 #pragma unroll
-    for (int c = 0; c < 16; ++c) { m[c] = -INFINITY; l[c] = 0.f; }
-
-    for (int it = 0; it < kSnapNIT; ++it) {
-        const int64_t j0 = kb * kSnapKT + (int64_t)(it * 4 + wid) * 16;
-        if (j0 >= n) break;
-        // A operands: key j0 + lr, dims 32 s + 8 lg .. +8
-        bf16x8_t a[4];
-        const int64_t jl = j0 + lr;
+        for (int kt = 0; kt < kSnapKTW; ++kt) {
+            const int64_t jl = jw + kt * 16 + lr;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (jl < n) v = *reinterpret_cast<const uint4*>(K + (jl * Hkv + g) * kD + s * 32 + lg * 8);
-            a[s] = as_bf16x8(v);
+            for (int s = 0; s < 4; ++s) {
+                uint4 v = make_uint4(0, 0, 0, 0);
+                if (jl < n) v = *reinterpret_cast<const uint4*>(K + (jl * Hkv + g) * kD + s * 32 + lg * 8);
+                a[kt][s] = as_bf16x8(v);
+            }
         }
-        float colsum[4] = {0.f, 0.f, 0.f, 0.f};
+    };
+
+    if (PASS == 1)
+        for (int c = 0; c < RT; ++c) mlst[(wid * RT + c) * 64 + lane] = make_float2(-INFINITY, 0.f);
+
+    // one key block: pass 1 folds its scores into (m, l), pass 2 writes its keys' importance
+    auto compute = [&](const bf16x8_t (&a)[kSnapKTW][4], int64_t kb) {
+        const int64_t jw = key0(kb);
+        const bool full = jw + kSnapKTW * 16 <= n;   // only the last key block has keys >= n
+        float colsum[(PASS == 2) ? kSnapKTW : 1][4];
 #pragma unroll
-        for (int c = 0; c < 16; ++c) {
-            if (c < RT) {
-                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-                const int r = c * 16 + lr;
+        for (int kt = 0; kt < ((PASS == 2) ? kSnapKTW : 1); ++kt)
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const int chunk = s * 4 + lg;
-                    bf16x8_t bq = as_bf16x8(sQ[r * 16 + (chunk ^ (r & 15))]);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], bq, acc, 0, 0, 0);
+            for (int i = 0; i < 4; ++i) colsum[kt][i] = 0.f;
+        // row tiles, unrolled by a divisor of RT
+        constexpr int U2 = (RT % 4 == 0 && RT > 4) ? 4 : ((RT % 2 == 0) ? 2 : 1);
+#pragma unroll(U2)
+        for (int c = 0; c < RT; ++c) {
+            const int r = c * 16 + lr;
+            bf16x8_t bq[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) bq[s] = as_bf16x8(sQ[r * 16 + ((s * 4 + lg) ^ (r & 15))]);
+            f32x4_t acc[kSnapKTW];
+#pragma unroll
+            for (int kt = 0; kt < kSnapKTW; ++kt) acc[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int kt = 0; kt < kSnapKTW; ++kt)
+                    acc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[kt][s], bq[s], acc[kt], 0, 0, 0);
+            if (!full) {
+#pragma unroll
+                for (int kt = 0; kt < kSnapKTW; ++kt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (jw + kt * 16 + lg * 4 + i >= n) acc[kt][i] = -INFINITY;
+            }
+            if (PASS == 1) {
+                // online (max, sum) of 2^(scale * dot) for row r over this lane's keys
+                float mx = acc[0][0];
+#pragma unroll
+                for (int kt = 0; kt < kSnapKTW; ++kt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) mx = fmaxf(mx, acc[kt][i]);
+                float2 ml = mlst[(wid * RT + c) * 64 + lane];
+                const float mn = fmaxf(ml.x, mx * kSnapScale);
+                if (mn != -INFINITY) {
+                    float e = 0.f;
+#pragma unroll
+                    for (int kt = 0; kt < kSnapKTW; ++kt)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) e += fast_exp2(fmaf(acc[kt][i], kSnapScale, -mn));
+                    ml.y = ml.y * fast_exp2(ml.x - mn) + e;
+                    ml.x = mn;
+                    mlst[(wid * RT + c) * 64 + lane] = ml;
                 }
-                float sv[4];
+            } else {
+                const float lr_c = sL[r];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int64_t j = j0 + lg * 4 + i;
-                    sv[i] = (j < n) ? acc[i] * kSnapScale : -INFINITY;
-                }
-                if (PASS == 1) {
-                    float mx = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-                    float mn = fmaxf(m[c], mx);
-                    if (mn != -INFINITY) {
-                        float e = exp2f(sv[0] - mn) + exp2f(sv[1] - mn) + exp2f(sv[2] - mn) + exp2f(sv[3] - mn);
-                        l[c] = l[c] * exp2f(m[c] - mn) + e;
-                        m[c] = mn;
-                    }
-                } else {
+                for (int kt = 0; kt < kSnapKTW; ++kt)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) colsum[i] += exp2f(sv[i] - lrow[c]);
-                }
+                    for (int i = 0; i < 4; ++i) colsum[kt][i] += fast_exp2(fmaf(acc[kt][i], kSnapScale, -lr_c));
             }
         }
         if (PASS == 2) {
+            // column sums over the 16 rows of each lane group (DPP butterfly); lane lr == i writes
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float s = sum_row16(colsum[i]);
-                const int64_t j = j0 + lg * 4 + i;
-                if (lr == i && j < n) imp[(int64_t)g * n + j] = s / (float)R;
-            }
-        }
-    }
-    if (PASS == 1) {
-        // combine the 4 lane groups (same rows, different keys), then the 4 waves
+            for (int kt = 0; kt < kSnapKTW; ++kt)
 #pragma unroll
-        for (int c = 0; c < 16; ++c) {
-            if (c < RT) {
-#pragma unroll
-                for (int o = 16; o <= 32; o <<= 1) {
-                    float m2 = __shfl_xor(m[c], o, 64), l2 = __shfl_xor(l[c], o, 64);
-                    float mn = fmaxf(m[c], m2);
-                    if (mn != -INFINITY) {
-                        l[c] = l[c] * exp2f(m[c] - mn) + l2 * exp2f(m2 - mn);
-                        m[c] = mn;
-                    }
+                for (int i = 0; i < 4; ++i) {
+                    const float v = sum_row16(colsum[kt][i]);
+                    const int64_t j = jw + kt * 16 + lg * 4 + i;
+                    if (lr == i && j < n) imp[(int64_t)g * n + j] = v / (float)R;
                 }
-                if (lg == 0) wstat[wid][c * 16 + lr] = make_float2(m[c], l[c]);
+        }
+    };
+
+    bf16x8_t a0[kSnapKTW][4], a1[kSnapKTW][4];
+    if (p < nblk) load(a0, p);
+    __syncthreads();
+    for (int64_t kb = p; kb < nblk; kb += 2 * (int64_t)P) {
+        if (kb + P < nblk) load(a1, kb + P);
+        compute(a0, kb);
+        if (kb + P >= nblk) break;
+        if (kb + 2 * (int64_t)P < nblk) load(a0, kb + 2 * (int64_t)P);
+        compute(a1, kb + P);
+    }
+
+    if (PASS == 1) {
+        // combine the 4 lane groups (same rows, different keys), then the waves
+        for (int c = 0; c < RT; ++c) {
+            const float2 ml = mlst[(wid * RT + c) * 64 + lane];
+            float mc = ml.x, lc = ml.y;
+#pragma unroll
+            for (int o = 16; o <= 32; o <<= 1) {
+                const float m2 = __shfl_xor(mc, o, 64), l2 = __shfl_xor(lc, o, 64);
+                const float mn = fmaxf(mc, m2);
+                if (mn != -INFINITY) {
+                    lc = lc * fast_exp2(mc - mn) + l2 * fast_exp2(m2 - mn);
+                    mc = mn;
+                }
             }
+            if (lg == 0) wstat[wid][c * 16 + lr] = make_float2(mc, lc);
         }
         __syncthreads();
         for (int r = threadIdx.x; r < R; r += kSnapThreads) {
             float M = -INFINITY, L = 0.f;
-            for (int wv = 0; wv < 4; ++wv) {
-                float2 v = wstat[wv][r];
-                float mn = fmaxf(M, v.x);
+#pragma unroll
+            for (int wv = 0; wv < NW; ++wv) {
+                const float2 v = wstat[wv][r];
+                const float mn = fmaxf(M, v.x);
                 if (mn != -INFINITY) {
-                    L = L * exp2f(M - mn) + v.y * exp2f(v.x - mn);
+                    L = L * fast_exp2(M - mn) + v.y * fast_exp2(v.x - mn);
                     M = mn;
                 }
             }
-            pstat[((int64_t)g * gridDim.y + kb) * R + r] = make_float2(M, L);
+            pstat[((int64_t)g * P + p) * R + r] = make_float2(M, L);
         }
     }
 }
 
-__global__ void snap_lse_kernel(const float2* __restrict__ pstat, int64_t nblk, int R, int Hkv, float* __restrict__ lse) {
-    const int gr = blockIdx.x * blockDim.x + threadIdx.x;
-    if (gr >= Hkv * R) return;
-    const int g = gr / R, r = gr % R;
-    float M = -INFINITY;
-    for (int64_t k = 0; k < nblk; ++k) M = fmaxf(M, pstat[((int64_t)g * nblk + k) * R + r].x);
-    float L = 0.f;
-    for (int64_t k = 0; k < nblk; ++k) {
-        float2 v = pstat[((int64_t)g * nblk + k) * R + r];
-        if (v.x != -INFINITY) L += v.y * exp2f(v.x - M);
+// lse[g][r] = M + log2(L) over the pass-1 blocks' (M, L) (nblk of them per KV head).  Block = (g, 64-row slice); its 256 threads
+// are (quarter q < 4, row): each walks every 4th block with 8 loads in flight, then the
+// quarters are merged in LDS.
+__global__ __launch_bounds__(256) void snap_lse_kernel(const float2* __restrict__ pstat, int64_t nblk, int R, int Hkv,
+                                                      float* __restrict__ lse) {
+    __shared__ float2 part[4][64];
+    const int nrb = (R + 63) / 64;
+    const int rb = blockIdx.x % nrb;
+    const int g = blockIdx.x / nrb;
+    const int rl = threadIdx.x & 63, qq = threadIdx.x >> 6;
+    const int r = rb * 64 + rl;
+    float M = -INFINITY, L = 0.f;
+    if (r < R) {
+        for (int64_t k0 = qq; k0 < nblk; k0 += 4 * 8) {
+            float2 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int64_t k = k0 + 4 * u;
+                v[u] = k < nblk ? pstat[((int64_t)g * nblk + k) * R + r] : make_float2(-INFINITY, 0.f);
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const float mn = fmaxf(M, v[u].x);
+                if (mn != -INFINITY) {
+                    L = L * fast_exp2(M - mn) + v[u].y * fast_exp2(v[u].x - mn);
+                    M = mn;
+                }
+            }
+        }
     }
-    lse[gr] = M + log2f(L);
+    part[qq][rl] = make_float2(M, L);
+    __syncthreads();
+    if (qq == 0 && r < R) {
+#pragma unroll
+        for (int u = 1; u < 4; ++u) {
+            const float2 v = part[u][rl];
+            const float mn = fmaxf(M, v.x);
+            if (mn != -INFINITY) {
+                L = L * fast_exp2(M - mn) + v.y * fast_exp2(v.x - mn);
+                M = mn;
+            }
+        }
+        lse[(int64_t)g * R + r] = M + log2f(L);
+    }
 }
 
 // pooled[g][j] = ((imp[j-1] + imp[j]) + imp[j+1]) / 3, zero outside [0, n); written with row
@@ -199,8 +285,14 @@ __global__ void snap_gather_kernel(const uint16_t* __restrict__ K, const uint16_
     *reinterpret_cast<uint4*>(V_out + dst) = *reinterpret_cast<const uint4*>(V + src);
 }
 
+// one pass block per CU: 256 / Hkv per KV head, at most one per key block
+static int64_t snap_blocks_per_head(int Hkv, int64_t nblk) {
+    int64_t p = 256 / Hkv;
+    return p < nblk ? p : (nblk > 0 ? nblk : 1);
+}
+
 struct SnapLayout {
-    int64_t nblk;
+    int64_t nblk, P;
     float2* pstat;
     float *lse, *imp, *pooled;
     void* sel_ws;
@@ -211,8 +303,9 @@ static SnapLayout snap_layout(void* ws, int64_t n, int w, int Hq, int Hkv, int64
     SnapLayout L;
     const int R = (Hq / Hkv) * w;
     L.nblk = (n + kSnapKT - 1) / kSnapKT;
+    L.P = snap_blocks_per_head(Hkv, L.nblk);
     WsCarver wc(ws);
-    L.pstat = wc.take<float2>((size_t)Hkv * L.nblk * R);
+    L.pstat = wc.take<float2>((size_t)Hkv * L.P * R);
     L.lse = wc.take<float>((size_t)Hkv * R);
     L.imp = wc.take<float>((size_t)Hkv * n);
     L.pooled = wc.take<float>((size_t)Hkv * score_stride(n));
@@ -221,6 +314,45 @@ static SnapLayout snap_layout(void* ws, int64_t n, int w, int Hq, int Hkv, int64
     L.sel_ws = wc.take<char>(L.sel_bytes);
     L.bytes = wc.size();
     return L;
+}
+
+template <int PASS, int RT>
+static hipError_t launch_pass_rt(dim3 grid, size_t shq, hipStream_t stream, const uint16_t* q_obs, const uint16_t* K,
+                                 int64_t n, int w, int Hq, int Hkv, int64_t nblk, float2* pstat, const float* lse,
+                                 float* imp) {
+    hipLaunchKernelGGL((snap_pass_kernel<PASS, RT>), grid, dim3(kSnapThreads), shq, stream, q_obs, K, n, w, Hq, Hkv,
+                       nblk, pstat, lse, imp);
+    return hipGetLastError();
+}
+
+template <int PASS, int... RTS>
+static hipError_t dispatch_pass(int rt, std::integer_sequence<int, RTS...>, dim3 grid, size_t shq, hipStream_t stream,
+                                const uint16_t* q_obs, const uint16_t* K, int64_t n, int w, int Hq, int Hkv,
+                                int64_t nblk, float2* pstat, const float* lse, float* imp) {
+    hipError_t e = hipErrorInvalidValue;
+    ((rt == RTS + 1
+          ? (e = launch_pass_rt<PASS, RTS + 1>(grid, shq, stream, q_obs, K, n, w, Hq, Hkv, nblk, pstat, lse, imp), 0)
+          : 0),
+     ...);
+    return e;
+}
+
+template <int PASS>
+static hipError_t launch_snap_pass(int rt, dim3 grid, size_t shq, hipStream_t stream, const uint16_t* q_obs,
+                                   const uint16_t* K, int64_t n, int w, int Hq, int Hkv, int64_t nblk, float2* pstat,
+                                   const float* lse, float* imp) {
+    return dispatch_pass<PASS>(rt, std::make_integer_sequence<int, 16>{}, grid, shq, stream, q_obs, K, n, w, Hq, Hkv,
+                               nblk, pstat, lse, imp);
+}
+
+template <int... RTS>
+static hipError_t set_lds_all(int bytes, std::integer_sequence<int, RTS...>) {
+    hipError_t e = hipSuccess;
+    ((e == hipSuccess ? (e = hipFuncSetAttribute((const void*)snap_pass_kernel<1, RTS + 1>,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, bytes)) : e), ...);
+    ((e == hipSuccess ? (e = hipFuncSetAttribute((const void*)snap_pass_kernel<2, RTS + 1>,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, bytes)) : e), ...);
+    return e;
 }
 
 size_t snapkv_workspace(int64_t n, int w, int Hq, int Hkv, int64_t c) {
@@ -236,18 +368,19 @@ hipError_t launch_snapkv(const uint16_t* q_obs, const uint16_t* K, const uint16_
     float* imp = imp_out ? imp_out : L.imp;
     float* pooled = L.pooled;
     const size_t shq = (size_t)R * kD * 2;
-    dim3 grid(Hkv, (unsigned)L.nblk);
-    hipLaunchKernelGGL(snap_pass_kernel<1>, grid, dim3(kSnapThreads), shq, stream, q_obs, K, n, w, Hq, Hkv, L.pstat,
-                       nullptr, nullptr);
-    hipLaunchKernelGGL(snap_lse_kernel, dim3((Hkv * R + 255) / 256), dim3(256), 0, stream, L.pstat, L.nblk, R, Hkv,
-                       L.lse);
-    hipLaunchKernelGGL(snap_pass_kernel<2>, grid, dim3(kSnapThreads), shq, stream, q_obs, K, n, w, Hq, Hkv, nullptr,
-                       L.lse, imp);
+    dim3 grid(Hkv, (unsigned)L.P);
+    hipError_t e = launch_snap_pass<1>(R / 16, grid, shq, stream, q_obs, K, n, w, Hq, Hkv, L.nblk, L.pstat, nullptr,
+                                       nullptr);
+    if (e != hipSuccess) return e;
+    const int rblk = (R + 63) / 64;
+    hipLaunchKernelGGL(snap_lse_kernel, dim3(Hkv * rblk), dim3(256), 0, stream, L.pstat, L.P, R, Hkv, L.lse);
+    e = launch_snap_pass<2>(R / 16, grid, shq, stream, q_obs, K, n, w, Hq, Hkv, L.nblk, nullptr, L.lse, imp);
+    if (e != hipSuccess) return e;
     const int64_t tot = n * Hkv;
     hipLaunchKernelGGL(snap_pool_kernel, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, stream, imp, n, Hkv,
                        score_stride(n), pooled, pooled_out);
     const int64_t ce = c < n ? c : n;
-    hipError_t e = launch_rows_topk(pooled, score_stride(n), Hkv, n, ce, idx_out, L.sel_ws, L.sel_bytes, stream);
+    e = launch_rows_topk(pooled, score_stride(n), Hkv, n, ce, idx_out, L.sel_ws, L.sel_bytes, stream);
     if (e != hipSuccess) return e;
     const int64_t pieces = ce * Hkv * 16;
     hipLaunchKernelGGL(snap_gather_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, stream, K, V, idx_out,
@@ -258,10 +391,5 @@ hipError_t launch_snapkv(const uint16_t* q_obs, const uint16_t* K, const uint16_
 }  // namespace qasi
 
 namespace qasi {
-hipError_t init_snap_kernels() {
-    const int bytes = 256 * kD * 2;
-    hipError_t e = hipFuncSetAttribute((const void*)snap_pass_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-    if (e != hipSuccess) return e;
-    return hipFuncSetAttribute((const void*)snap_pass_kernel<2>, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-}
+hipError_t init_snap_kernels() { return set_lds_all(256 * kD * 2, std::make_integer_sequence<int, 16>{}); }
 }  // namespace qasi

@@ -59,6 +59,20 @@ def test_snapkv_small(n, w, Hq, Hkv, c):
     print("rel err", float(np.max(err / ref)))
 
 
+# row-tile counts R / 16 other than 1, 2 and 16 (each is its own kernel instantiation), on a
+# sequence whose last key block and last 16-key tile are partial
+@pytest.mark.parametrize("w,Hq,Hkv", [(12, 16, 4), (10, 64, 8), (24, 32, 8), (14, 64, 8), (22, 64, 8), (24, 64, 8),
+                                      (26, 64, 8), (30, 64, 8)])
+def test_snapkv_row_tiles(w, Hq, Hkv):
+    x = synth.make_snap(12, 1500, w, Hq, Hkv, 20, 200)
+    r = _run(x)
+    imp = f64(r["importance"])
+    ref = O.snapkv_importance(x.q_obs, x.K, Hq, Hkv)
+    err = np.abs(imp - ref)
+    assert np.all(err <= 3e-4 * ref + 1e-10), f"importance error max rel {np.max(err / (ref + 1e-30))}"
+    _check_selection(x, r)
+
+
 def test_snapkv_full_size_c5():
     x = synth.config5()
     r = _run(x)
