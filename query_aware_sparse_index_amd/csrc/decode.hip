@@ -144,12 +144,26 @@ __global__ __launch_bounds__(512) void decode_partial_kernel(const uint16_t* __r
 
     // phase 2: per-head max, exponentials and sums
     const int nslots = (MODE == 1) ? G : Hq;
+    constexpr int EPL = (kDecCH + 63) / 64;   // entries per lane
     for (int hs = wid; hs < nslots; hs += NW) {
-        float z = lane < len ? zb[hs * kDecCH + lane] : -INFINITY;   // kDecCH == 64
-        float m = wave_max(z);
-        float e = lane < len ? fast_exp2(z - m) : 0.f;
-        if (lane < kDecCH) zb[hs * kDecCH + lane] = e;
-        float l = wave_sum(e);
+        float z[EPL];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            const int i = lane + 64 * e;
+            z[e] = i < len ? zb[hs * kDecCH + i] : -INFINITY;
+            mx = fmaxf(mx, z[e]);
+        }
+        const float m = wave_max(mx);
+        float l = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+            const int i = lane + 64 * e;
+            const float ev = i < len ? fast_exp2(z[e] - m) : 0.f;
+            if (i < kDecCH) zb[hs * kDecCH + i] = ev;
+            l += ev;
+        }
+        l = wave_sum(l);
         if (lane == 0) { stat[hs * 2] = m; stat[hs * 2 + 1] = l; }
     }
     __syncthreads();
@@ -229,12 +243,15 @@ __global__ __launch_bounds__(512) void decode_partial_kernel(const uint16_t* __r
 }
 
 // Merge of the chunk partials of each (sequence, head).  Block = (b * Hq + h, 16-dim slice);
-// its 1024 threads are (chunk group cg < 64, dim dl < 16): each thread walks every 64th chunk
-// of the sequence with independent loads, then the 64 groups are summed in LDS.
+// its 1024 threads are (chunk group cg < 64, dim dl < 16).  Every thread first requests its
+// chunks' (m, l) and acc values (8 chunks in flight, every 64th chunk of the sequence), then
+// the block takes the maximum M of all chunk maxima, and the weighted sums
+// sum_c acc_c 2^(m_c - M) and sum_c l_c 2^(m_c - M) are reduced over the 64 groups in LDS.
 __global__ __launch_bounds__(1024) void decode_merge_kernel(const float* __restrict__ part_acc,
                                                            const float2* __restrict__ part_ml,
                                                            const int64_t* __restrict__ counts, int B, int Hq,
                                                            float* __restrict__ out) {
+    constexpr int U = 8;
     __shared__ float sa[64][17];
     __shared__ float sl[64];
     __shared__ float smax[16];
@@ -242,34 +259,44 @@ __global__ __launch_bounds__(1024) void decode_merge_kernel(const float* __restr
     int64_t first = 0;
     for (int i = 0; i < b; ++i) first += (counts[i] + kDecCH - 1) / kDecCH;
     const int64_t nch = (counts[b] + kDecCH - 1) / kDecCH;
-    float M = -INFINITY;
-    for (int64_t c = threadIdx.x; c < nch; c += 1024) M = fmaxf(M, part_ml[(first + c) * Hq + h].x);
-    M = wave_max(M);
-    if ((threadIdx.x & 63) == 0) smax[threadIdx.x >> 6] = M;
-    __syncthreads();
-    M = smax[0];
-#pragma unroll
-    for (int w = 1; w < 16; ++w) M = fmaxf(M, smax[w]);
     const int cg = threadIdx.x >> 4, dl = threadIdx.x & 15, d = ds * 16 + dl;
     float a = 0.f, l = 0.f;
-    for (int64_t c0 = cg; c0 < nch; c0 += 64 * 8) {
-        float x[8], mm[8], ll[8];
+    float M = -INFINITY;
+    for (int64_t c0 = cg; c0 - cg < nch; c0 += 64 * U) {
+        float x[U], mm[U], ll[U];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < U; ++u) {
             const int64_t c = c0 + 64 * u;
             const int64_t slot = (first + (c < nch ? c : 0)) * Hq + h;
             x[u] = part_acc[slot * kD + d];
             const float2 ml = part_ml[slot];
-            mm[u] = ml.x;
+            mm[u] = c < nch ? ml.x : -INFINITY;
             ll[u] = ml.y;
         }
+        // the block-wide maximum over every chunk seen so far
+        float mx = -INFINITY;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            if (c0 + 64 * u < nch) {
-                const float w = fast_exp2(mm[u] - M);
-                a = fmaf(x[u], w, a);
-                l = fmaf(ll[u], w, l);
+        for (int u = 0; u < U; ++u) mx = fmaxf(mx, mm[u]);
+        mx = wave_max(mx);
+        __syncthreads();
+        if ((threadIdx.x & 63) == 0) smax[threadIdx.x >> 6] = mx;
+        __syncthreads();
+        float Mn = M;
+#pragma unroll
+        for (int w = 0; w < 16; ++w) Mn = fmaxf(Mn, smax[w]);
+        if (Mn != -INFINITY) {
+            const float rs = fast_exp2(M - Mn);     // rescale what was summed under M
+            a *= rs;
+            l *= rs;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (c0 + 64 * u < nch) {
+                    const float w = fast_exp2(mm[u] - Mn);
+                    a = fmaf(x[u], w, a);
+                    l = fmaf(ll[u], w, l);
+                }
             }
+            M = Mn;
         }
     }
     sa[cg][dl] = a;

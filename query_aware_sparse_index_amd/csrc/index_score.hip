@@ -72,8 +72,12 @@ hipError_t launch_index_append(const uint16_t* k_new, const float* P, uint16_t* 
 //                  whole scores.  Scores are staged in a padded LDS tile [Hq][kScoreTB + 1]
 //                  (conflict-free) and written row by row into scores[h * S + t].
 // ---------------------------------------------------------------------------------------
-constexpr int kScoreThreads = 512;
-constexpr int kScoreTB = 128;
+constexpr int kScoreTB = 64;
+// block size: at most 512 threads and at least two token rows per lane (4 lanes per KV head)
+template <int HKV>
+constexpr int score_threads() {
+    return kScoreTB * 4 * HKV / 2 < 512 ? kScoreTB * 4 * HKV / 2 : 512;
+}
 constexpr int kTileLd = kScoreTB + 1;
 
 __device__ __forceinline__ bool find_item(const int64_t* __restrict__ offsets, int B, int64_t item, int tb, int& b,
@@ -160,14 +164,16 @@ __device__ __forceinline__ void quad_transpose_sum(float (&v)[G], int part) {
 }
 
 template <int HKV, int G>
-__global__ __launch_bounds__(kScoreThreads) void score_kernel(const float* __restrict__ qp,
+__global__ __launch_bounds__(score_threads<HKV>()) void score_kernel(const float* __restrict__ qp,
                                                              const uint16_t* __restrict__ k_index,
                                                              const int64_t* __restrict__ offsets, int B,
                                                              float* __restrict__ scores) {
+    constexpr int NT = score_threads<HKV>();
     constexpr int Hq = HKV * G;
     constexpr int LPT = 4 * HKV;          // lanes per token
     constexpr int TPW = 64 / LPT;         // tokens per wave per load
-    constexpr int TPB = TPW * (kScoreThreads / 64);  // tokens per block per load
+    constexpr int TPB = TPW * (NT / 64);  // tokens per block per load
+    static_assert(NT % 64 == 0 && kScoreTB % TPB == 0, "whole waves, whole passes over the tile");
     constexpr int ITERS = kScoreTB / TPB;
     constexpr int UNR = ITERS < 8 ? ITERS : 8;
     constexpr int NOUT = G >= 4 ? G / 4 : 1;          // complete heads per lane
@@ -230,7 +236,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_kernel(const float* __res
         }
     }
     __syncthreads();
-    for (int o = threadIdx.x; o < Hq * kScoreTB; o += kScoreThreads) {
+    for (int o = threadIdx.x; o < Hq * kScoreTB; o += NT) {
         const int h = o / kScoreTB, tl = o % kScoreTB;
         if (tl < len) scores[(int64_t)h * S + base_tok + tl] = tile[h * kTileLd + tl];
     }
@@ -251,7 +257,7 @@ size_t score_workspace(int B, int Hq) {
 template <int HKV>
 static hipError_t launch_score_g(int G, dim3 grid, hipStream_t stream, const float* qp, const uint16_t* k_index,
                                  const int64_t* offsets_dev, int B, float* scores) {
-    dim3 block(kScoreThreads);
+    dim3 block(score_threads<HKV>());
     switch (G) {
         case 1: hipLaunchKernelGGL((score_kernel<HKV, 1>), grid, block, 0, stream, qp, k_index, offsets_dev, B, scores); break;
         case 2: hipLaunchKernelGGL((score_kernel<HKV, 2>), grid, block, 0, stream, qp, k_index, offsets_dev, B, scores); break;

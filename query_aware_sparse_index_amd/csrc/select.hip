@@ -10,14 +10,14 @@
 //
 // Both modes need an exact order statistic per (sequence, head): theta_h = s_(r) for the
 // vote, and the boundary score of the per-head top-K.  It is found on order-preserving
-// uint32 keys of the fp32 scores in two kernels:
-//   th_collect : every block of an instance first derives the same key bracket [lo, hi]
-//                from a stratified sample of the row (kRuns runs of 16 keys): a histogram
-//                over the sample's value range locates the sample order statistics kDelta
-//                ranks below and above the target's expected sample rank.  The block then
-//                counts the keys of its slice below lo, compacts the keys inside the bracket
-//                (the "candidates") next to the slice and histograms them on the top
-//                kDigit bits of key - lo;
+// uint32 keys of the fp32 scores in three kernels:
+//   th_bracket : a key bracket [lo, hi] per instance from a stratified sample of the row
+//                (kRuns runs of 16 keys): a histogram over the sample's value range locates
+//                the sample order statistics kDelta ranks below and above the target's
+//                expected sample rank;
+//   th_collect : per slice of the row, counts the keys below lo, compacts the keys inside
+//                the bracket (the "candidates") next to the slice and histograms them on the
+//                top kDigit bits of key - lo;
 //   th_final   : sums the slice histograms to find the answer's top digit, gathers the
 //                candidates of that digit into LDS and finishes with a radix select over
 //                the remaining bits.  If the answer's rank is not among the candidates (or
@@ -128,153 +128,193 @@ __host__ __device__ __forceinline__ int top_shift(uint32_t span) {
     return nbits > kDigit ? nbits - kDigit : 0;
 }
 
-// Block (slice s, instance).  Bracket: rows of m <= kCap keys take every key ([0, 2^32 - 1]).
-// Longer rows: run j of the sample starts at a hashed position of stratum
-// [j m / kRuns, (j + 1) m / kRuns); the sample's [min, max] is cut into kSampleBins equal
-// bins; lo is the lower edge of the bin before the one holding sample rank ir - kDelta and
-// hi the upper edge of the bin after the one holding ir + kDelta (the key range's ends when
-// these leave the sample), ir the target's expected sample rank.  Every block computes
-// the same bracket from the same keys; block 0 stores it.
-// Output: cnt[(inst * SL + s) * 2] = #keys < lo, [+1] = #candidates; candidates (keys in
-// [lo, hi]) at cand[(inst * SL + s) * kSlice ...] in arbitrary order; dhist[inst][s] =
-// kDigitBins 16-bit counts of the candidates' top digit (key - lo) >> top_shift(hi - lo),
-// two per word.
-__global__ __launch_bounds__(kColThreads) void th_collect_kernel(const float* __restrict__ scores,
+// One block per instance: flag, need and the key bracket [lo, hi] in the instance's state.
+// Rows of m <= kCap keys take every key ([0, 2^32 - 1]).  Longer rows: run j of the sample
+// starts at a hashed position of stratum [j m / kRuns, (j + 1) m / kRuns); the sample's
+// [min, max] is cut into kSampleBins equal bins; lo is the lower edge of the bin before the
+// one holding sample rank ir - kDelta and hi the upper edge of the bin after the one holding
+// ir + kDelta (the key range's ends when these leave the sample), ir the target's expected
+// sample rank.
+__global__ __launch_bounds__(kColThreads) void th_bracket_kernel(const float* __restrict__ scores,
                                                                 const int64_t* __restrict__ offsets, int Hq,
-                                                                DevCfg cfg, int SL, int64_t S,
-                                                                int64_t* __restrict__ state,
-                                                                uint32_t* __restrict__ cand,
-                                                                uint32_t* __restrict__ cnt,
-                                                                uint32_t* __restrict__ dhist) {
+                                                                DevCfg cfg, int64_t S, int64_t* __restrict__ state) {
     constexpr int NW = kColThreads / 64;
-    constexpr int PT = kSlice / kColThreads;       // slice keys per thread
-    __shared__ uint32_t lcnt;
-    __shared__ int wsum[NW];
     __shared__ float wmin[NW], wmax[NW];
-    __shared__ uint32_t hist[kSampleBins];         // sample bins, then candidate digit bins
+    __shared__ uint32_t hist[kSampleBins];
     __shared__ int tmp[NW];
     __shared__ int sb[2];
-    static_assert(kDigitBins <= kSampleBins, "digit histogram reuses the sample bins");
-    const int inst = blockIdx.y, s = blockIdx.x;
+    const int inst = blockIdx.x;
     const int b = inst / Hq, h = inst % Hq;
     const int64_t off = offsets[b];
     const OsInst oi = os_instance(offsets[b + 1] - off, cfg);
     int64_t* st = state + (int64_t)inst * 8;
-    if (s == 0 && threadIdx.x == 0) {
+    const int64_t m = oi.end - oi.beg;
+    if (oi.flag != kFlagActive || m <= kCap) {
+        if (threadIdx.x == 0) {
+            st[kStFlag] = oi.flag;
+            st[kStNeed] = oi.need;
+            st[kStLo] = 0;
+            st[kStHi] = 0xffffffffll;
+        }
+        return;
+    }
+    const float* row = scores + (int64_t)h * S + off;
+    constexpr int PER = kSample / kColThreads;
+    float v[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+        const int i = threadIdx.x + u * kColThreads, j = i / kRunLen;
+        const int64_t a = (int64_t)j * m / kRuns, e = (int64_t)(j + 1) * m / kRuns;
+        const uint32_t r = mix32((uint32_t)j * 0x9e3779b9u ^ mix32((uint32_t)inst + 0x632be5abu));
+        v[u] = row[oi.beg + a + (int64_t)(r % (uint32_t)(e - a - kRunLen + 1)) + (i % kRunLen)];
+    }
+    for (int i = threadIdx.x; i < kSampleBins; i += kColThreads) hist[i] = 0;
+    float mn = v[0], mx = v[0];
+#pragma unroll
+    for (int u = 1; u < PER; ++u) { mn = fminf(mn, v[u]); mx = fmaxf(mx, v[u]); }
+    for (int o = 32; o > 0; o >>= 1) {
+        mn = fminf(mn, __shfl_xor(mn, o, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    }
+    if ((threadIdx.x & 63) == 0) { wmin[threadIdx.x >> 6] = mn; wmax[threadIdx.x >> 6] = mx; }
+    __syncthreads();
+    mn = wmin[0];
+    mx = wmax[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) { mn = fminf(mn, wmin[w]); mx = fmaxf(mx, wmax[w]); }
+    const int64_t ir = (oi.rank - 1) * kSample / m;
+    const int64_t il = ir - kDelta, ih = ir + kDelta;
+    uint32_t klo = 0u, khi = 0xffffffffu;
+    if (mx > mn) {
+        const float scale = (float)kSampleBins / (mx - mn);
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            int bin = (int)((v[u] - mn) * scale);
+            bin = bin < 0 ? 0 : (bin >= kSampleBins ? kSampleBins - 1 : bin);
+            atomicAdd(&hist[bin], 1u);
+        }
+        __syncthreads();
+        constexpr int BPT = kSampleBins / kColThreads;
+        int c = 0;
+#pragma unroll
+        for (int u = 0; u < BPT; ++u) c += (int)hist[threadIdx.x * BPT + u];
+        int tot;
+        const int inc = block_inclusive_scan<kColThreads>(c, tmp, &tot);
+        int acc = inc - c;
+#pragma unroll
+        for (int u = 0; u < BPT; ++u) {
+            const int bin = threadIdx.x * BPT + u;
+            const int nx = acc + (int)hist[bin];
+            if (acc <= il && il < nx) sb[0] = bin;      // bin holding sample rank il (0-based)
+            if (acc <= ih && ih < nx) sb[1] = bin;
+            acc = nx;
+        }
+        __syncthreads();
+        const float w = (mx - mn) / (float)kSampleBins;
+        if (il > 0) klo = order_key(mn + (float)(sb[0] - 1) * w);
+        if (ih < kSample - 1) khi = order_key(mn + (float)(sb[1] + 2) * w);
+    } else {
+        klo = khi = order_key(mn);
+    }
+    if (klo > khi) klo = khi;
+    if (threadIdx.x == 0) {
         st[kStFlag] = oi.flag;
         st[kStNeed] = oi.need;
+        st[kStLo] = klo;
+        st[kStHi] = khi;
     }
+}
+
+// Block (slice s, instance): cnt[(inst * SL + s) * 2] = #keys < lo, [+1] = #candidates;
+// the candidates (keys in [lo, hi]) at cand[(inst * SL + s) * kSlice ...], grouped by their top
+// digit (key - lo) >> top_shift(hi - lo) in ascending digit order (any order inside a digit);
+// dpre[inst][s][d] = number of the slice's candidates with digit < d, d = 0 .. kDigitBins,
+// as 16-bit values.
+constexpr int kPreWords = kDigitBins / 2 + 1;   // 16-bit prefix values 0 .. kDigitBins, two per word
+__global__ __launch_bounds__(kColThreads) void th_collect_kernel(const float* __restrict__ scores,
+                                                                const int64_t* __restrict__ offsets, int Hq,
+                                                                DevCfg cfg, int SL, int64_t S,
+                                                                const int64_t* __restrict__ state,
+                                                                uint32_t* __restrict__ cand,
+                                                                uint32_t* __restrict__ cnt,
+                                                                uint32_t* __restrict__ dpre) {
+    constexpr int NW = kColThreads / 64;
+    constexpr int PT = kSlice / kColThreads;       // slice keys per thread
+    constexpr int BPT = kDigitBins / kColThreads;  // digit bins per thread in the scan
+    __shared__ int wsum[NW];
+    __shared__ int tmp[NW];
+    __shared__ uint32_t hist[kDigitBins];          // counts, then the running cursor per digit
+    const int inst = blockIdx.y, s = blockIdx.x;
+    const int b = inst / Hq, h = inst % Hq;
+    const int64_t off = offsets[b];
+    const OsInst oi = os_instance(offsets[b + 1] - off, cfg);
     if (oi.flag != kFlagActive) return;
-    const int64_t m = oi.end - oi.beg;
     const int64_t lo = oi.beg + (int64_t)s * kSlice;
     const int64_t hi = lo + kSlice < oi.end ? lo + kSlice : oi.end;
     const float* row = scores + (int64_t)h * S + off;
-    // the slice, in registers before the bracket is known (one memory round trip for both)
+    // the slice and the bracket in one memory round trip
     float xv[PT];
 #pragma unroll
     for (int j = 0; j < PT; ++j) {
         const int64_t t = lo + threadIdx.x + (int64_t)j * kColThreads;
         xv[j] = t < hi ? row[t] : 0.f;
     }
-    uint32_t klo = 0u, khi = 0xffffffffu;
-    for (int i = threadIdx.x; i < kSampleBins; i += kColThreads) hist[i] = 0;
-    if (m > kCap) {
-        constexpr int PER = kSample / kColThreads;
-        float v[PER];
-#pragma unroll
-        for (int u = 0; u < PER; ++u) {
-            const int i = threadIdx.x + u * kColThreads, j = i / kRunLen;
-            const int64_t a = (int64_t)j * m / kRuns, e = (int64_t)(j + 1) * m / kRuns;
-            const uint32_t r = mix32((uint32_t)j * 0x9e3779b9u ^ mix32((uint32_t)inst + 0x632be5abu));
-            v[u] = row[oi.beg + a + (int64_t)(r % (uint32_t)(e - a - kRunLen + 1)) + (i % kRunLen)];
-        }
-        float mn = v[0], mx = v[0];
-#pragma unroll
-        for (int u = 1; u < PER; ++u) { mn = fminf(mn, v[u]); mx = fmaxf(mx, v[u]); }
-        for (int o = 32; o > 0; o >>= 1) {
-            mn = fminf(mn, __shfl_xor(mn, o, 64));
-            mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-        }
-        if ((threadIdx.x & 63) == 0) { wmin[threadIdx.x >> 6] = mn; wmax[threadIdx.x >> 6] = mx; }
-        __syncthreads();
-        mn = wmin[0];
-        mx = wmax[0];
-#pragma unroll
-        for (int w = 1; w < NW; ++w) { mn = fminf(mn, wmin[w]); mx = fmaxf(mx, wmax[w]); }
-        const int64_t ir = (oi.rank - 1) * kSample / m;
-        const int64_t il = ir - kDelta, ih = ir + kDelta;
-        if (mx > mn) {
-            const float scale = (float)kSampleBins / (mx - mn);
-#pragma unroll
-            for (int u = 0; u < PER; ++u) {
-                int bin = (int)((v[u] - mn) * scale);
-                bin = bin < 0 ? 0 : (bin >= kSampleBins ? kSampleBins - 1 : bin);
-                atomicAdd(&hist[bin], 1u);
-            }
-            __syncthreads();
-            constexpr int BPT = kSampleBins / kColThreads;
-            int c = 0;
-#pragma unroll
-            for (int u = 0; u < BPT; ++u) c += (int)hist[threadIdx.x * BPT + u];
-            int tot;
-            const int inc = block_inclusive_scan<kColThreads>(c, tmp, &tot);
-            int acc = inc - c;
-#pragma unroll
-            for (int u = 0; u < BPT; ++u) {
-                const int bin = threadIdx.x * BPT + u;
-                const int nx = acc + (int)hist[bin];
-                if (acc <= il && il < nx) sb[0] = bin;      // bin holding sample rank il (0-based)
-                if (acc <= ih && ih < nx) sb[1] = bin;
-                acc = nx;
-            }
-            __syncthreads();
-            const float w = (mx - mn) / (float)kSampleBins;
-            if (il > 0) klo = order_key(mn + (float)(sb[0] - 1) * w);
-            if (ih < kSample - 1) khi = order_key(mn + (float)(sb[1] + 2) * w);
-            for (int i = threadIdx.x; i < kSampleBins; i += kColThreads) hist[i] = 0;
-        } else {
-            klo = khi = order_key(mn);
-        }
-        if (klo > khi) klo = khi;
-    }
-    if (s == 0 && threadIdx.x == 0) {
-        st[kStLo] = klo;
-        st[kStHi] = khi;
-    }
-    if (threadIdx.x == 0) lcnt = 0;
+    const int64_t* st = state + (int64_t)inst * 8;
+    const uint32_t klo = (uint32_t)st[kStLo], khi = (uint32_t)st[kStHi];
+    for (int i = threadIdx.x; i < kDigitBins; i += kColThreads) hist[i] = 0;
     __syncthreads();
     const int dsh = top_shift(khi - klo);
-    uint32_t* dst = cand + ((size_t)inst * SL + s) * kSlice;
-    const int lane = threadIdx.x & 63;
+    // classify: keys below the bracket are counted, candidates are counted per digit
     int below = 0;
+    uint32_t hitmask = 0;
 #pragma unroll
     for (int j = 0; j < PT; ++j) {
         const bool ok = lo + threadIdx.x + (int64_t)j * kColThreads < hi;
         const uint32_t k = order_key(xv[j]);
         below += (ok && k < klo) ? 1 : 0;
-        const bool hit = ok && k >= klo && k <= khi;
-        const uint64_t mask = __ballot(hit);
-        if (mask) {
-            uint32_t basep = 0;
-            const int leader = __ffsll((unsigned long long)mask) - 1;
-            if (lane == leader) basep = atomicAdd(&lcnt, (uint32_t)__popcll(mask));
-            basep = __shfl(basep, leader, 64);
-            if (hit) {
-                dst[basep + __popcll(mask & ((1ull << lane) - 1ull))] = k;
-                atomicAdd(&hist[(k - klo) >> dsh], 1u);
-            }
+        if (ok && k >= klo && k <= khi) {
+            hitmask |= 1u << j;
+            atomicAdd(&hist[(k - klo) >> dsh], 1u);
         }
     }
     below = wave_sum_i(below);
-    if (lane == 0) wsum[threadIdx.x >> 6] = below;
+    if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = below;
     __syncthreads();
-    uint32_t* dh = dhist + ((size_t)inst * SL + s) * (kDigitBins / 2);
-    for (int i = threadIdx.x; i < kDigitBins / 2; i += kColThreads) dh[i] = hist[2 * i] | (hist[2 * i + 1] << 16);
+    // exclusive prefix over the digits (BPT consecutive bins per thread)
+    uint32_t c[BPT];
+    int csum = 0;
+#pragma unroll
+    for (int u = 0; u < BPT; ++u) { c[u] = hist[threadIdx.x * BPT + u]; csum += (int)c[u]; }
+    int total;
+    const int incl = block_inclusive_scan<kColThreads>(csum, tmp, &total);
+    uint32_t* dp = dpre + ((size_t)inst * SL + s) * kPreWords;
+    {
+        uint32_t acc = (uint32_t)(incl - csum);
+        uint32_t pre[BPT];
+#pragma unroll
+        for (int u = 0; u < BPT; ++u) { pre[u] = acc; acc += c[u]; }
+        static_assert(BPT % 2 == 0, "prefix values are written in pairs");
+#pragma unroll
+        for (int u = 0; u < BPT; u += 2) dp[(threadIdx.x * BPT + u) / 2] = pre[u] | (pre[u + 1] << 16);
+#pragma unroll
+        for (int u = 0; u < BPT; ++u) hist[threadIdx.x * BPT + u] = pre[u];   // cursor
+        if (threadIdx.x == 0) dp[kDigitBins / 2] = (uint32_t)total;
+    }
+    __syncthreads();
+    // scatter the candidates to their digit's range
+    uint32_t* dst = cand + ((size_t)inst * SL + s) * kSlice;
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+        if (hitmask & (1u << j)) {
+            const uint32_t k = order_key(xv[j]);
+            dst[atomicAdd(&hist[(k - klo) >> dsh], 1u)] = k;
+        }
+    }
     if (threadIdx.x == 0) {
-        int tot = 0;
-        for (int w = 0; w < NW; ++w) tot += wsum[w];
-        cnt[((size_t)inst * SL + s) * 2 + 0] = (uint32_t)tot;
-        cnt[((size_t)inst * SL + s) * 2 + 1] = lcnt;
+        int tb = 0;
+        for (int w = 0; w < NW; ++w) tb += wsum[w];
+        cnt[((size_t)inst * SL + s) * 2 + 0] = (uint32_t)tb;
+        cnt[((size_t)inst * SL + s) * 2 + 1] = (uint32_t)total;
     }
 }
 
@@ -333,11 +373,10 @@ __global__ __launch_bounds__(kThThreads) void th_final_kernel(const float* __res
                                                              DevCfg cfg, int SL, int64_t S,
                                                              const uint32_t* __restrict__ cand,
                                                              const uint32_t* __restrict__ cnt,
-                                                             const uint32_t* __restrict__ dhist,
+                                                             const uint32_t* __restrict__ dpre,
                                                              int64_t* __restrict__ state, float* __restrict__ theta_out) {
-    static_assert(kDigitBins / 2 == kThThreads, "one word of digit bins per thread");
+    static_assert(kDigitBins / 2 == kThThreads, "one pair of digit bins per thread");
     __shared__ uint32_t xs[kCap];
-    __shared__ int pre[kMaxSL + 1];
     __shared__ uint32_t hist[kDigitBins];
     __shared__ int tmp[kThThreads / 64];
     __shared__ int64_t sh[4];
@@ -355,38 +394,44 @@ __global__ __launch_bounds__(kThThreads) void th_final_kernel(const float* __res
     const uint32_t klo = (uint32_t)st[kStLo], khi = (uint32_t)st[kStHi];
     const int nsl = (int)((m + kSlice - 1) / kSlice);
     const int t = threadIdx.x;
-    // slice counts (two slices per thread) and the digit histogram (one word per thread)
+    // keys below the bracket and candidates: two slices per thread
     const uint32_t* cs = cnt + (size_t)inst * SL * 2;
-    int c0 = 0, c1 = 0, l0 = 0, l1 = 0;
-    const int s0 = 2 * t;
-    if (s0 < nsl) { l0 = (int)cs[2 * s0]; c0 = (int)cs[2 * s0 + 1]; }
-    if (s0 + 1 < nsl) { l1 = (int)cs[2 * s0 + 2]; c1 = (int)cs[2 * s0 + 3]; }
+    int lsum = 0, csum = 0;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int sl = 2 * t + u;
+        if (sl < nsl) { lsum += (int)cs[2 * sl]; csum += (int)cs[2 * sl + 1]; }
+    }
+    // candidates per digit pair (2t, 2t+1), summed over the slices from their prefixes
     uint32_t dlo = 0, dhi = 0;
     {
-        const uint32_t* dh = dhist + (size_t)inst * SL * (kDigitBins / 2) + t;
+        const uint32_t* dp = dpre + (size_t)inst * SL * kPreWords;
         int sl = 0;
-        for (; sl + 8 <= nsl; sl += 8) {
-            uint32_t w[8];
+        for (; sl + 4 <= nsl; sl += 4) {
+            uint32_t w0[4], w1[4];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) w[u] = dh[(size_t)(sl + u) * (kDigitBins / 2)];
+            for (int u = 0; u < 4; ++u) {
+                w0[u] = dp[(size_t)(sl + u) * kPreWords + t];
+                w1[u] = dp[(size_t)(sl + u) * kPreWords + t + 1];
+            }
 #pragma unroll
-            for (int u = 0; u < 8; ++u) { dlo += w[u] & 0xffffu; dhi += w[u] >> 16; }
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t p0 = w0[u] & 0xffffu, p1 = w0[u] >> 16, p2 = w1[u] & 0xffffu;
+                dlo += p1 - p0;
+                dhi += p2 - p1;
+            }
         }
         for (; sl < nsl; ++sl) {
-            const uint32_t w = dh[(size_t)sl * (kDigitBins / 2)];
-            dlo += w & 0xffffu;
-            dhi += w >> 16;
+            const uint32_t w0 = dp[(size_t)sl * kPreWords + t], w1 = dp[(size_t)sl * kPreWords + t + 1];
+            const uint32_t p0 = w0 & 0xffffu, p1 = w0 >> 16, p2 = w1 & 0xffffu;
+            dlo += p1 - p0;
+            dhi += p2 - p1;
         }
     }
     int nmid, nlo;
-    const int incl = block_inclusive_scan<kThThreads>(c0 + c1, tmp, &nmid);
-    block_inclusive_scan<kThThreads>(l0 + l1, tmp, &nlo);
-    if (s0 < nsl) pre[s0] = incl - c0 - c1;
-    if (s0 + 1 < nsl) pre[s0 + 1] = incl - c1;
-    if (t == 0) { pre[nsl] = nmid; nd = 0; }
-    hist[2 * t] = dlo;
-    hist[2 * t + 1] = dhi;
-    __syncthreads();
+    block_inclusive_scan<kThThreads>(csum, tmp, &nmid);
+    block_inclusive_scan<kThThreads>(lsum, tmp, &nlo);
+    if (t == 0) nd = 0;
     int64_t gt = 0;
     uint32_t key = 0;
     const int64_t r = oi.rank;
@@ -397,7 +442,7 @@ __global__ __launch_bounds__(kThThreads) void th_final_kernel(const float* __res
         if (klo == khi) {
             key = klo;
         } else {
-            // top digit from the summed slice histograms
+            // the answer's top digit from the summed histograms
             const int dsh = top_shift(khi - klo);
             const int cd = (int)(dlo + dhi);
             int tot;
@@ -418,28 +463,16 @@ __global__ __launch_bounds__(kThThreads) void th_final_kernel(const float* __res
             if (nD > kCap) {
                 whole_row = true;
             } else {
-                // gather the candidates of digit D (low bits only) into LDS
+                // copy digit D's candidates of every slice (their low bits) into LDS
                 const uint32_t low = dsh ? ((1u << dsh) - 1u) : 0u;
-                for (int i0 = t; i0 < nmid; i0 += 16 * kThThreads) {
-                    uint32_t v[16];
-#pragma unroll
-                    for (int u = 0; u < 16; ++u) {
-                        const int i = i0 + u * kThThreads;
-                        v[u] = 0;
-                        if (i < nmid) {
-                            int a = 0, z = nsl - 1;          // last slice with pre[slice] <= i
-                            while (a < z) {
-                                const int mid = (a + z + 1) >> 1;
-                                if (pre[mid] <= i) a = mid; else z = mid - 1;
-                            }
-                            v[u] = cand[((size_t)inst * SL + a) * kSlice + (i - pre[a])];
-                        }
-                    }
-#pragma unroll
-                    for (int u = 0; u < 16; ++u) {
-                        const int i = i0 + u * kThThreads;
-                        const uint32_t x = v[u] - klo;
-                        if (i < nmid && (x >> dsh) == D) xs[atomicAdd(&nd, 1u)] = x & low;
+                const uint32_t* dp = dpre + (size_t)inst * SL * kPreWords;
+                for (int sl = t; sl < nsl; sl += kThThreads) {
+                    const uint32_t a = (dp[(size_t)sl * kPreWords + D / 2] >> (16 * (D & 1))) & 0xffffu;
+                    const uint32_t e = (dp[(size_t)sl * kPreWords + (D + 1) / 2] >> (16 * ((D + 1) & 1))) & 0xffffu;
+                    if (e > a) {
+                        const uint32_t base = atomicAdd(&nd, e - a);
+                        const uint32_t* src = cand + ((size_t)inst * SL + sl) * kSlice;
+                        for (uint32_t q = a; q < e; ++q) xs[base + (q - a)] = (src[q] - klo) & low;
                     }
                 }
                 __syncthreads();
@@ -514,20 +547,26 @@ __global__ __launch_bounds__(kChunk) void vote_kernel(const float* __restrict__ 
     int64_t first, nch, t0, len;
     if (!find_chunk(offsets, B, blockIdx.x, b, first, nch, t0, len)) return;
     const int64_t off = offsets[b], n = offsets[b + 1] - off;
-    for (int h = threadIdx.x; h < Hq; h += kChunk) th[h] = key_to_float((uint32_t)state[((int64_t)b * Hq + h) * 8 + kStKey]);
-    for (int i = threadIdx.x; i < (kChunk / 64) * kVoteBins; i += kChunk) (&lh[0][0])[i] = 0;
-    __syncthreads();
     const int64_t i = threadIdx.x;
     const int64_t t = t0 + i;
+    // this token's first 32 scores are requested before the thresholds are staged, so both
+    // arrive in one memory round trip
+    const float* col = scores + off + (i < len ? t : t0);
+    float sv[32];
+#pragma unroll
+    for (int u = 0; u < 32; ++u) sv[u] = col[(int64_t)(u < Hq ? u : Hq - 1) * S];
+    for (int h = threadIdx.x; h < Hq; h += kChunk) th[h] = key_to_float((uint32_t)state[((int64_t)b * Hq + h) * 8 + kStKey]);
+    for (int k = threadIdx.x; k < (kChunk / 64) * kVoteBins; k += kChunk) (&lh[0][0])[k] = 0;
+    __syncthreads();
     if (i < len) {
-        const float* col = scores + off + t;
         int v = 0;
-        for (int h0 = 0; h0 < Hq; h0 += 16) {
-            float sv[16];
 #pragma unroll
-            for (int u = 0; u < 16; ++u) sv[u] = (h0 + u < Hq) ? col[(int64_t)(h0 + u) * S] : 0.f;
+        for (int u = 0; u < 32; ++u) v += (u < Hq && sv[u] > th[u]) ? 1 : 0;
+        for (int h0 = 32; h0 < Hq; h0 += 32) {
 #pragma unroll
-            for (int u = 0; u < 16; ++u) v += (h0 + u < Hq && sv[u] > th[h0 + u]) ? 1 : 0;
+            for (int u = 0; u < 32; ++u) sv[u] = col[(int64_t)(h0 + u < Hq ? h0 + u : Hq - 1) * S];
+#pragma unroll
+            for (int u = 0; u < 32; ++u) v += (h0 + u < Hq && sv[u] > th[h0 + u]) ? 1 : 0;
         }
         votes[off + t] = (uint8_t)v;
         uint8_t key;
@@ -818,7 +857,7 @@ static SelectLayout select_layout(void* ws, const int64_t* offsets_host, int B, 
     const size_t inst = (size_t)B * Hq;
     L.cand = w.take<uint32_t>(inst * L.SL * kSlice);
     L.cnt = w.take<uint32_t>(inst * L.SL * 2);
-    L.dhist = w.take<uint32_t>(inst * L.SL * (kDigitBins / 2));
+    L.dhist = w.take<uint32_t>(inst * L.SL * kPreWords);
     L.state = w.take<int64_t>(inst * 8);
     L.votes = w.take<uint8_t>((size_t)L.Ntot + 16);
     L.keys = w.take<uint8_t>((size_t)L.Ntot + 16);
@@ -841,6 +880,8 @@ hipError_t launch_select(const float* scores, int64_t S, const int64_t* offsets_
     if (L.bytes > ws_bytes || L.SL > kMaxSL) return hipErrorInvalidValue;
     DevCfg d = dev_cfg(c);
     const unsigned inst = (unsigned)(B * Hq);
+    hipLaunchKernelGGL(th_bracket_kernel, dim3(inst), dim3(kColThreads), 0, stream, scores, offsets_dev, Hq, d, S,
+                       L.state);
     hipLaunchKernelGGL(th_collect_kernel, dim3(L.SL, inst), dim3(kColThreads), 0, stream, scores, offsets_dev, Hq, d,
                        L.SL, S, L.state, L.cand, L.cnt, L.dhist);
     hipLaunchKernelGGL(th_final_kernel, dim3(inst), dim3(kThThreads), 0, stream, scores, offsets_dev, Hq, d, L.SL, S,
