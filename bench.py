@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--n", type=int, default=131072)
     ap.add_argument("--budget", type=int, default=20, help="percent (5, 10, 15, 20, 30)")
     ap.add_argument("--mode", choices=["vote", "per-head"], default="vote")
+    ap.add_argument("--workload", choices=["long", "ragged"], default="long",
+                    help="long: one sequence of --n tokens (the headline); ragged: a batch of 16 sequences of "
+                         "16K-64K tokens at a 15%% budget")
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip dense / warm / graph side measurements")
@@ -116,6 +119,104 @@ def traffic_record(fetch_csv, write_csv, out_path, mode=0, budget=20):
     return rec, table
 
 
+def bench_ragged(args, torch, api, synth, dev):
+    """Ragged batch (Mistral-7B layer shapes, 16 sequences of 16K-64K tokens, 15 % budget): a
+    step appends the index row of each sequence's newest token (one ts_index_append per
+    sequence), then ts_score + ts_select + ts_sparse_decode over the packed batch.  Inputs
+    resident in HBM, LLC flushed before each step, events on the launch stream."""
+    import ctypes
+    from query_aware_sparse_index_amd import _lib
+    L = _lib.load()
+    mode = api.MODE_VOTE if args.mode == "vote" else api.MODE_PER_HEAD
+    print("bench: building the ragged batch", file=sys.stderr, flush=True)
+    x = synth.config4()
+    Hq, Hkv = x.Hq, x.Hkv
+    offs = api.Offsets(x.offsets, dev)
+    lens = [int(v) for v in np.diff(x.offsets)]
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+    q, K, V = t(x.q), t(x.K), t(x.V)
+    P = torch.from_numpy(x.P).to(dev)
+    kidx = torch.empty((offs.ntot, Hkv, 32), dtype=torch.int16, device=dev)
+    api.index_append(K, P, kidx, 0)
+    p = api.params(mode, x.budget)
+    ks = [api.budget_tokens(n, p) for n in lens]
+    scores = torch.empty((Hq, api.score_stride(offs)), dtype=torch.float32, device=dev)
+    idx = torch.empty(sum(ks) * (Hq if mode == api.MODE_PER_HEAD else 1) + 16, dtype=torch.int32, device=dev)
+    count = torch.empty(offs.B, dtype=torch.int64, device=dev)
+    ws_sc = torch.empty(max(api.score_workspace_bytes(offs.B, Hq), 256), dtype=torch.uint8, device=dev)
+    ws_sel = torch.empty(max(api.select_workspace_bytes(offs, Hq, p), 256), dtype=torch.uint8, device=dev)
+    ws_dec = torch.empty(max(api.decode_workspace_bytes(offs, ks, Hq, Hkv, mode), 256), dtype=torch.uint8,
+                         device=dev)
+    out = torch.empty((offs.B, Hq, 128), dtype=torch.float32, device=dev)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
+    sink = torch.empty((), dtype=torch.float32, device=dev)
+    vp = lambda a: ctypes.c_void_p(a.data_ptr())
+    ch = (ctypes.c_int64 * offs.B)(*ks)
+    Kp, Vp, Pp, kip, qp, scp = vp(K), vp(V), vp(P), vp(kidx), vp(q), vp(scores)
+    row_bytes = Hkv * 128 * 2
+    pref = ctypes.byref(p)
+
+    def chk(rc):
+        if rc != 0:
+            raise RuntimeError(L.ts_last_error().decode())
+
+    def step():
+        st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        for b in range(offs.B):
+            last = offs.host_list[b + 1] - 1
+            chk(L.ts_index_append(ctypes.c_void_p(Kp.value + last * row_bytes), Pp, kip, last, 1, Hkv, st))
+        chk(L.ts_score(qp, Pp, kip, vp(offs.dev), offs.host, offs.B, Hq, Hkv, scp, vp(ws_sc), ws_sc.numel(), st))
+        chk(L.ts_select(scp, vp(offs.dev), offs.host, offs.B, Hq, Hkv, pref, vp(idx), vp(count), None, None,
+                        vp(ws_sel), ws_sel.numel(), st))
+        chk(L.ts_sparse_decode(qp, Kp, Vp, vp(offs.dev), offs.host, vp(idx), vp(count), ch, mode, offs.B, Hq, Hkv,
+                               vp(out), vp(ws_dec), ws_dec.numel(), st))
+
+    for _ in range(args.warmup):
+        torch.sum(flush.view(torch.float32), dim=0, out=sink)
+        step()
+    torch.cuda.synchronize()
+    evs = []
+    for _ in range(args.steps):
+        torch.sum(flush.view(torch.float32), dim=0, out=sink)
+        a, b2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        step()
+        b2.record()
+        evs.append((a, b2))
+    torch.cuda.synchronize()
+    us = np.array([a.elapsed_time(b2) * 1e3 for a, b2 in evs])
+    ntot = offs.ntot
+    kv_rows = sum(ks) if mode == api.MODE_VOTE else None
+    if kv_rows is None:       # per-head: union of each KV group's lists
+        G = Hq // Hkv
+        lst = idx[:sum(ks) * Hq].cpu().numpy()
+        kv_rows, base = 0, 0
+        for k in ks:
+            blk = lst[base:base + Hq * k].reshape(Hq, k)
+            kv_rows += sum(len(np.unique(blk[g * G:(g + 1) * G])) for g in range(Hkv))
+            base += Hq * k
+        step_bytes = ntot * Hkv * 64 + kv_rows * 128 * 2 * 2
+    else:
+        step_bytes = ntot * Hkv * 64 + kv_rows * Hkv * 128 * 2 * 2
+    mean = float(us.mean())
+    res = {"metric": METRIC, "value": round(mean, 2), "unit": "us/step", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(mean / 1e3, 5), "higher_is_better": False,
+           "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+           "config": {"workload": f"ragged batch of {offs.B} sequences ({min(lens)}-{max(lens)} tokens, "
+                                  f"{ntot} in total), 32 query / 8 KV heads, d=128, d'=32, budget "
+                                  f"{x.budget[0]}/{x.budget[1]}, {args.mode} mode", "B": offs.B, "Ntot": ntot,
+                      "llc": "flushed before each step"},
+           "median_us": round(float(np.median(us)), 2),
+           "hbm_gbps": round(step_bytes / (mean * 1e-6) / 1e9, 1),
+           "pct_peak": round(100 * step_bytes / (mean * 1e-6) / 1e9 / PEAK_GBPS, 1),
+           "algorithmic_bytes_per_step": int(step_bytes)}
+    line = json.dumps(res)
+    print(line, flush=True)
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(line + "\n")
+
+
 def main():
     args = parse()
     if args.traffic_from:
@@ -126,13 +227,15 @@ def main():
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the decode-step path of one attention layer runs on a single "
-              "MI355X (see DESIGN.md for how it would shard); run with --gpus 1.", file=sys.stderr)
+              "MI355X (sharding across GPUs is not built); run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
     from query_aware_sparse_index_amd import api, synth
 
     dev = torch.device("cuda:0")
+    if args.workload == "ragged":
+        return bench_ragged(args, torch, api, synth, dev)
     n0, steps, warm = args.n, args.steps, args.warmup
     total_steps = steps + warm
     mode = api.MODE_VOTE if args.mode == "vote" else api.MODE_PER_HEAD

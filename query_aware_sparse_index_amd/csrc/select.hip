@@ -506,18 +506,21 @@ __global__ __launch_bounds__(kThThreads) void th_final_kernel(const float* __res
 }
 
 // ----------------------------------------------------------------- chunk lookup
+// Work item -> (sequence b, its first item, its item count, first token, length) for chunks of CH
+// tokens numbered sequence by sequence.
+template <int CH = kChunk>
 __device__ __forceinline__ bool find_chunk(const int64_t* __restrict__ offsets, int B, int64_t item, int& b,
                                            int64_t& first, int64_t& nch, int64_t& t0, int64_t& len) {
     int64_t acc = 0;
     for (int i = 0; i < B; ++i) {
         int64_t n = offsets[i + 1] - offsets[i];
-        int64_t nb = (n + kChunk - 1) / kChunk;
+        int64_t nb = (n + CH - 1) / CH;
         if (item < acc + nb) {
             b = i;
             first = acc;
             nch = nb;
-            t0 = (item - acc) * kChunk;
-            len = n - t0 < kChunk ? n - t0 : kChunk;
+            t0 = (item - acc) * CH;
+            len = n - t0 < CH ? n - t0 : CH;
             return true;
         }
         acc += nb;
@@ -737,82 +740,220 @@ __global__ __launch_bounds__(kChunk) void compact_vote_kernel(const int64_t* __r
 }
 
 // --------------------------------------------------------- per-head compaction
-// cnt[(h * nitems + item) * 2 + {0: above, 1: equal}] for the non-forced tokens of a block.
-__global__ __launch_bounds__(kChunk) void ph_count_kernel(const float* __restrict__ scores,
+// Three kernels, each covering all heads of a token chunk at once (the heads are looped inside
+// the block, their score loads issued together):
+//   ph_count   : cnt[(h * nitems + item) * 2 + {0, 1}] = non-forced tokens of the chunk with key
+//                above / equal to theta_h (wave ballots, no atomics);
+//   ph_scan    : one wave per (sequence, head): exclusive prefix of those counts over the
+//                sequence's chunks, written in place;
+//   ph_compact : the chunk's selected tokens of every head, at their ranks: forced tokens, keys
+//                above theta_h, and the first need_eq - eqb keys equal to theta_h in position order.
+constexpr int kPhHeads = 32;   // heads handled per pass of a block (Hq <= 64 takes two)
+constexpr int kPhChunk = 256;  // tokens per per-head compaction block
+
+__global__ __launch_bounds__(kPhChunk) void ph_count_kernel(const float* __restrict__ scores,
                                                          const int64_t* __restrict__ offsets, int B, int Hq,
                                                          DevCfg cfg, int64_t S, const int64_t* __restrict__ state,
                                                          int64_t nitems, uint32_t* __restrict__ cnt) {
-    __shared__ int tmp[kChunk / 64];
+    constexpr int NW = kPhChunk / 64;
+    __shared__ uint32_t wc[kPhHeads][NW][2];
+    __shared__ uint32_t hkey[kPhHeads];
+    __shared__ bool hact[kPhHeads];
     int b;
     int64_t first, nch, t0, len;
-    if (!find_chunk(offsets, B, blockIdx.x, b, first, nch, t0, len)) return;
-    const int h = blockIdx.y;
+    if (!find_chunk<kPhChunk>(offsets, B, blockIdx.x, b, first, nch, t0, len)) return;
     const int64_t off = offsets[b], n = offsets[b + 1] - off;
-    const int64_t* st = state + ((int64_t)b * Hq + h) * 8;
-    const uint32_t ks = (uint32_t)st[kStKey];
-    const bool act = st[kStFlag] == kFlagActive;
     const int64_t i = threadIdx.x, t = t0 + i;
-    int gt = 0, eq = 0;
-    if (act && i < len && !is_forced(t, n, cfg.sink, cfg.local)) {
-        const uint32_t k = order_key(scores[(int64_t)h * S + off + t]);
-        gt = k > ks;
-        eq = k == ks;
-    }
-    int tg, te;
-    block_inclusive_scan<kChunk>(gt, tmp, &tg);
-    block_inclusive_scan<kChunk>(eq, tmp, &te);
-    if (threadIdx.x == 0) {
-        cnt[((size_t)h * nitems + blockIdx.x) * 2 + 0] = (uint32_t)tg;
-        cnt[((size_t)h * nitems + blockIdx.x) * 2 + 1] = (uint32_t)te;
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const bool in = i < len && !is_forced(t, n, cfg.sink, cfg.local);
+    const float* col = scores + off + (i < len ? t : t0);
+    for (int h0 = 0; h0 < Hq; h0 += kPhHeads) {
+        float sv[kPhHeads];
+#pragma unroll
+        for (int u = 0; u < kPhHeads; ++u) sv[u] = col[(int64_t)(h0 + u < Hq ? h0 + u : Hq - 1) * S];
+        if (threadIdx.x < kPhHeads && h0 + threadIdx.x < Hq) {
+            const int64_t* st = state + ((int64_t)b * Hq + h0 + threadIdx.x) * 8;
+            hact[threadIdx.x] = st[kStFlag] == kFlagActive;
+            hkey[threadIdx.x] = (uint32_t)st[kStKey];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < kPhHeads; ++u) {
+            const int h = h0 + u;
+            if (h >= Hq) break;
+            const bool act = hact[u];
+            const uint32_t ks = hkey[u];
+            const uint32_t k = order_key(sv[u]);
+            const uint64_t mg = __ballot(act && in && k > ks), me = __ballot(act && in && k == ks);
+            if (lane == 0) {
+                wc[u][wid][0] = (uint32_t)__popcll(mg);
+                wc[u][wid][1] = (uint32_t)__popcll(me);
+            }
+        }
+        __syncthreads();
+        const int hh = threadIdx.x >> 1, which = threadIdx.x & 1;
+        if (hh < kPhHeads && h0 + hh < Hq) {
+            uint32_t a = 0;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) a += wc[hh][w][which];
+            cnt[((size_t)(h0 + hh) * nitems + blockIdx.x) * 2 + which] = a;
+        }
+        __syncthreads();
     }
 }
 
-__global__ __launch_bounds__(kChunk) void ph_compact_kernel(const float* __restrict__ scores,
+// One wave per (sequence b, head h), four waves per block: exclusive prefix over the chunks of
+// b of the (above, equal) counts, in place.
+__global__ __launch_bounds__(256) void ph_scan_kernel(const int64_t* __restrict__ offsets, int B, int Hq,
+                                                     int64_t nitems, uint32_t* __restrict__ cnt) {
+    const int lane = threadIdx.x & 63;
+    const int64_t wv = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (wv >= (int64_t)B * Hq) return;
+    const int b = (int)(wv / Hq), h = (int)(wv % Hq);
+    int64_t first = 0;
+    for (int i = 0; i < b; ++i) first += (offsets[i + 1] - offsets[i] + kPhChunk - 1) / kPhChunk;
+    const int64_t nch = (offsets[b + 1] - offsets[b] + kPhChunk - 1) / kPhChunk;
+    uint32_t* row = cnt + ((size_t)h * nitems + first) * 2;
+    // lane l takes the PER consecutive chunks [c0 + l*PER, c0 + (l+1)*PER) of a batch of 64*PER
+    constexpr int PER = 16;
+    uint32_t carry0 = 0, carry1 = 0;
+    for (int64_t c0 = 0; c0 < nch; c0 += 64 * PER) {
+        const int64_t cl = c0 + (int64_t)lane * PER;
+        uint2 v[PER];
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int64_t c = cl + u;
+            v[u] = c < nch ? reinterpret_cast<const uint2*>(row)[c] : make_uint2(0, 0);
+        }
+        uint32_t s0 = 0, s1 = 0;
+#pragma unroll
+        for (int u = 0; u < PER; ++u) { s0 += v[u].x; s1 += v[u].y; }
+        uint32_t i0 = s0, i1 = s1;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t y0 = __shfl_up(i0, o, 64), y1 = __shfl_up(i1, o, 64);
+            if (lane >= o) { i0 += y0; i1 += y1; }
+        }
+        uint32_t a0 = carry0 + i0 - s0, a1 = carry1 + i1 - s1;
+#pragma unroll
+        for (int u = 0; u < PER; ++u) {
+            const int64_t c = cl + u;
+            if (c < nch) reinterpret_cast<uint2*>(row)[c] = make_uint2(a0, a1);
+            a0 += v[u].x;
+            a1 += v[u].y;
+        }
+        carry0 += __shfl(i0, 63, 64);
+        carry1 += __shfl(i1, 63, 64);
+    }
+}
+
+__global__ __launch_bounds__(kPhChunk) void ph_compact_kernel(const float* __restrict__ scores,
                                                            const int64_t* __restrict__ offsets, int B, int Hq,
                                                            DevCfg cfg, int64_t S, const int64_t* __restrict__ state,
-                                                           int64_t nitems, const uint32_t* __restrict__ cnt,
+                                                           int64_t nitems, const uint32_t* __restrict__ pre,
                                                            int32_t* __restrict__ idx_out,
                                                            int64_t* __restrict__ count_out) {
-    __shared__ int tmp[kChunk / 64];
+    constexpr int NW = kPhChunk / 64;
+    __shared__ uint32_t wq[kPhHeads][NW];   // per-wave counts of equal keys, then their prefix
+    __shared__ uint32_t ws[kPhHeads][NW];   // per-wave counts of selected tokens, then their prefix
+    struct HeadParams {
+        int flag, need_eq, eqb, base;
+        uint32_t key;
+    };
+    __shared__ HeadParams hp[kPhHeads];
     int b;
     int64_t first, nch, t0, len;
-    if (!find_chunk(offsets, B, blockIdx.x, b, first, nch, t0, len)) return;
-    const int h = blockIdx.y;
+    if (!find_chunk<kPhChunk>(offsets, B, blockIdx.x, b, first, nch, t0, len)) return;
     const int64_t off = offsets[b], n = offsets[b + 1] - off;
-    const int64_t c = blockIdx.x - first;
-    const int64_t* st = state + ((int64_t)b * Hq + h) * 8;
-    const int64_t flag = st[kStFlag];
-    const uint32_t ks = (uint32_t)st[kStKey];
     const int64_t K = budget_k(n, cfg.bnum, cfg.bden, cfg.sink, cfg.local);
-    const int64_t need_eq = flag == kFlagActive ? st[kStNeed] - st[kStGt] : 0;
-    // counts of the blocks before this one (one block per thread, then a block sum)
-    int gtb_i = 0, eqb_i = 0;
-    for (int64_t k = threadIdx.x; k < c; k += kChunk) {
-        gtb_i += (int)cnt[((size_t)h * nitems + first + k) * 2 + 0];
-        eqb_i += (int)cnt[((size_t)h * nitems + first + k) * 2 + 1];
-    }
-    int gtb, eqb;
-    block_inclusive_scan<kChunk>(gtb_i, tmp, &gtb);
-    block_inclusive_scan<kChunk>(eqb_i, tmp, &eqb);
-    const int64_t fb = forced_before(t0, n, cfg.sink, cfg.local);
-    int64_t base;
-    if (flag == kFlagTakeAll) base = t0;
-    else if (flag == kFlagTakeNone) base = fb;
-    else base = fb + gtb + ((int64_t)eqb < need_eq ? (int64_t)eqb : need_eq);
-    if (c == 0 && h == 0 && threadIdx.x == 0) count_out[b] = K;
-
-    const int64_t i = threadIdx.x, t = t0 + i;
-    const bool in = i < len;
-    const bool f = in && is_forced(t, n, cfg.sink, cfg.local);
-    const uint32_t kk = (in && !f) ? order_key(scores[(int64_t)h * S + off + t]) : 0u;
-    const int eqf = (in && !f && flag == kFlagActive && kk == ks) ? 1 : 0;
-    int tot;
-    const int eq_rank = block_inclusive_scan<kChunk>(eqf, tmp, &tot) - eqf;
-    int sel = in ? (f ? 1 : (flag == kFlagTakeAll ? 1 : (flag == kFlagActive && kk > ks ? 1 : 0))) : 0;
-    if (eqf) sel = ((int64_t)eqb + eq_rank < need_eq) ? 1 : 0;
-    const int64_t p = base + block_inclusive_scan<kChunk>(sel, tmp, &tot) - sel;
     const int64_t kpre = kpre_of(offsets, b, cfg);
-    if (sel && p < K) idx_out[Hq * kpre + (int64_t)h * K + p] = (int32_t)t;
+    const int64_t fb = forced_before(t0, n, cfg.sink, cfg.local);
+    if (blockIdx.x == first && threadIdx.x == 0) count_out[b] = K;
+    const int64_t i = threadIdx.x, t = t0 + i;
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const uint64_t lt = (1ull << lane) - 1ull;
+    const bool inr = i < len;
+    const bool frc = inr && is_forced(t, n, cfg.sink, cfg.local);
+    const float* col = scores + off + (inr ? t : t0);
+    // exclusive prefix over the waves of a[h][.] for the first `nh` heads (one thread per entry)
+    auto wave_prefix = [&](uint32_t (*a)[NW], int nh) {
+        __syncthreads();
+        const int hh = threadIdx.x / NW, w = threadIdx.x % NW;
+        uint32_t v = 0;
+        if (hh < nh)
+            for (int x = 0; x < w; ++x) v += a[hh][x];
+        __syncthreads();
+        if (hh < nh) a[hh][w] = v;
+        __syncthreads();
+    };
+    for (int h0 = 0; h0 < Hq; h0 += kPhHeads) {
+        const int nh = Hq - h0 < kPhHeads ? Hq - h0 : kPhHeads;
+        float sv[kPhHeads];
+#pragma unroll
+        for (int u = 0; u < kPhHeads; ++u) sv[u] = col[(int64_t)(h0 + u < Hq ? h0 + u : Hq - 1) * S];
+        // per-head parameters of this chunk, one thread per head
+        if (threadIdx.x < nh) {
+            const int h = h0 + threadIdx.x;
+            const int64_t* st = state + ((int64_t)b * Hq + h) * 8;
+            const int64_t flag = st[kStFlag];
+            const int64_t gtb = pre[((size_t)h * nitems + blockIdx.x) * 2];
+            const int64_t eqb = pre[((size_t)h * nitems + blockIdx.x) * 2 + 1];
+            int64_t base, need_eq = 0;
+            if (flag == kFlagTakeAll) base = t0;
+            else if (flag == kFlagTakeNone) base = fb;
+            else {
+                need_eq = st[kStNeed] - st[kStGt];
+                base = fb + gtb + (eqb < need_eq ? eqb : need_eq);
+            }
+            hp[threadIdx.x].flag = (int)flag;
+            hp[threadIdx.x].key = (uint32_t)st[kStKey];
+            hp[threadIdx.x].need_eq = (int)need_eq;
+            hp[threadIdx.x].eqb = (int)eqb;
+            hp[threadIdx.x].base = (int)base;
+        }
+        // pass 1: counts of the keys equal to theta_h
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < kPhHeads; ++u) {
+            if (u >= nh) break;
+            const bool act = hp[u].flag == kFlagActive;
+            const uint64_t me = __ballot(act && inr && !frc && order_key(sv[u]) == hp[u].key);
+            if (lane == 0) wq[u][wid] = (uint32_t)__popcll(me);
+        }
+        wave_prefix(wq, nh);
+        // pass 2: selection flags (bit u of selbits) and their per-wave counts
+        uint32_t selbits = 0;
+#pragma unroll
+        for (int u = 0; u < kPhHeads; ++u) {
+            if (u >= nh) break;
+            const int flag = hp[u].flag;
+            const uint32_t ks = hp[u].key;
+            const uint32_t k = order_key(sv[u]);
+            const bool eqf = flag == kFlagActive && inr && !frc && k == ks;
+            const uint64_t me = __ballot(eqf);
+            const int64_t eq_rank = (int64_t)hp[u].eqb + wq[u][wid] + __popcll(me & lt);
+            bool sel = false;
+            if (inr) {
+                if (frc || flag == kFlagTakeAll) sel = true;
+                else if (flag == kFlagActive) sel = k > ks || (eqf && eq_rank < hp[u].need_eq);
+            }
+            selbits |= (sel ? 1u : 0u) << u;
+            const uint64_t msel = __ballot(sel);
+            if (lane == 0) ws[u][wid] = (uint32_t)__popcll(msel);
+        }
+        wave_prefix(ws, nh);
+        // pass 3: write each selected token at its rank in its head's list
+#pragma unroll
+        for (int u = 0; u < kPhHeads; ++u) {
+            if (u >= nh) break;
+            const bool sel = (selbits >> u) & 1u;
+            const uint64_t msel = __ballot(sel);
+            if (!sel) continue;
+            const int64_t p = (int64_t)hp[u].base + ws[u][wid] + __popcll(msel & lt);
+            if (p < K) idx_out[Hq * kpre + (int64_t)(h0 + u) * K + p] = (int32_t)t;
+        }
+        __syncthreads();
+    }
 }
 
 // ------------------------------------------------------------------- host side
@@ -831,7 +972,7 @@ static DevCfg dev_cfg(const SelectConfig& c) {
 
 struct SelectLayout {
     int SL;
-    int64_t nitems, Ntot;
+    int64_t nitems, ph_items, Ntot;
     uint32_t *cand, *cnt, *dhist, *hist, *phcnt;
     int64_t *state, *seq_info;
     int2* chunk_info;
@@ -842,13 +983,15 @@ struct SelectLayout {
 static SelectLayout select_layout(void* ws, const int64_t* offsets_host, int B, int Hq, const SelectConfig& c) {
     SelectLayout L;
     DevCfg d = dev_cfg(c);
-    int64_t maxm = 0, items = 0;
+    int64_t maxm = 0, items = 0, ph_items = 0;
     for (int b = 0; b < B; ++b) {
         int64_t n = offsets_host[b + 1] - offsets_host[b];
         OsInst o = os_instance(n, d);
         if (o.end - o.beg > maxm) maxm = o.end - o.beg;
         items += (n + kChunk - 1) / kChunk;
+        ph_items += (n + kPhChunk - 1) / kPhChunk;
     }
+    L.ph_items = ph_items;
     L.SL = (int)((maxm + kSlice - 1) / kSlice);
     if (L.SL < 1) L.SL = 1;
     L.nitems = items;
@@ -864,7 +1007,7 @@ static SelectLayout select_layout(void* ws, const int64_t* offsets_host, int B, 
     L.hist = w.take<uint32_t>((size_t)items * kVoteBins);
     L.chunk_info = w.take<int2>((size_t)items);
     L.seq_info = w.take<int64_t>((size_t)B * 4);
-    L.phcnt = c.mode == 1 ? w.take<uint32_t>((size_t)Hq * items * 2) : nullptr;
+    L.phcnt = c.mode == 1 ? w.take<uint32_t>((size_t)Hq * ph_items * 2) : nullptr;
     L.bytes = w.size();
     return L;
 }
@@ -896,10 +1039,12 @@ hipError_t launch_select(const float* scores, int64_t S, const int64_t* offsets_
         hipLaunchKernelGGL(compact_vote_kernel, dim3((unsigned)L.nitems), dim3(kChunk), 0, stream, offsets_dev,
                            B, L.keys, L.chunk_info, L.seq_info, idx_out);
     } else {
-        hipLaunchKernelGGL(ph_count_kernel, dim3((unsigned)L.nitems, Hq), dim3(kChunk), 0, stream, scores,
-                           offsets_dev, B, Hq, d, S, L.state, L.nitems, L.phcnt);
-        hipLaunchKernelGGL(ph_compact_kernel, dim3((unsigned)L.nitems, Hq), dim3(kChunk), 0, stream, scores,
-                           offsets_dev, B, Hq, d, S, L.state, L.nitems, L.phcnt, idx_out, count_out);
+        hipLaunchKernelGGL(ph_count_kernel, dim3((unsigned)L.ph_items), dim3(kPhChunk), 0, stream, scores, offsets_dev,
+                           B, Hq, d, S, L.state, L.ph_items, L.phcnt);
+        hipLaunchKernelGGL(ph_scan_kernel, dim3((unsigned)((B * Hq + 3) / 4)), dim3(256), 0, stream, offsets_dev, B,
+                           Hq, L.ph_items, L.phcnt);
+        hipLaunchKernelGGL(ph_compact_kernel, dim3((unsigned)L.ph_items), dim3(kPhChunk), 0, stream, scores,
+                           offsets_dev, B, Hq, d, S, L.state, L.ph_items, L.phcnt, idx_out, count_out);
     }
     return hipGetLastError();
 }

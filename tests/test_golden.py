@@ -1,0 +1,57 @@
+"""The oracle and the library's host-side rules against the hand-checked fixtures in
+tests/golden/ (page parameters, a worked vote example, a worked pooling / top-c example)."""
+import ctypes
+
+import numpy as np
+
+from golden_fixtures import page_parameters, pool_example, vote_example
+from oracle import oracle as O
+from query_aware_sparse_index_amd import _lib, api, synth
+
+
+def test_page_parameters_are_the_defaults():
+    p, budgets = page_parameters()
+    assert (synth.SINK, synth.LOCAL) == (p["sink_tokens"], p["local_window"])
+    d = api.params()
+    assert (d.sink, d.local, d.v_min) == (p["sink_tokens"], p["local_window"], p["min_votes"])
+    assert (d.budget_num, d.budget_den) == (p["selection_budget_num"], p["selection_budget_den"])
+    assert synth.D == p["head_dim"] and synth.DP * p["index_dim_ratio_den"] == p["head_dim"]
+    L = _lib.load()
+    for n, K in budgets:
+        assert O.budget_tokens(n, p["selection_budget_num"], p["selection_budget_den"], p["sink_tokens"],
+                               p["local_window"]) == K
+        assert L.ts_budget_tokens(n, ctypes.byref(d)) == K
+
+
+def test_vote_example_theta_votes_selection():
+    ex = vote_example()
+    sc = ex["scores"]
+    offs = np.array([0, sc.shape[1]], np.int64)
+    th = O.theta(sc, offs, 1, 2)[0]
+    assert np.array_equal(th, ex["theta"])
+    v = O.votes(sc, th[None, :], offs)
+    assert np.array_equal(v, ex["votes"])
+    for sink, local, num, den, vmin, want in ex["selects"]:
+        idx, cnt = O.select_vote(v, offs, num, den, sink, local, vmin)
+        assert np.array_equal(idx, want), (sink, local, num, den, vmin, idx)
+        assert cnt[0] == len(want)
+
+
+def test_vote_example_per_head():
+    ex = vote_example()
+    sc = ex["scores"]
+    offs = np.array([0, sc.shape[1]], np.int64)
+    heads = ex["perhead"]
+    sink, local, num, den, _ = heads[0]
+    idx, cnt = O.select_per_head(sc, offs, num, den, sink, local)
+    K = int(cnt[0])
+    for h, (_, _, _, _, want) in heads.items():
+        assert np.array_equal(idx[h * K:(h + 1) * K], want), (h, idx[h * K:(h + 1) * K])
+
+
+def test_pool_topc_example():
+    imp, pooled, tops = pool_example()
+    got = O.avg_pool1d(imp[None, :], 3)[0]
+    assert np.array_equal(got, pooled)
+    for c, want in tops:
+        assert np.array_equal(O.topc(got[None, :], c)[0], want), (c, O.topc(got[None, :], c)[0])

@@ -169,3 +169,32 @@ def test_error_codes_on_device_calls():
     with pytest.raises(api.QasiError) as e:
         api.snapkv_compress(st.q[:1], st.K, st.V, 64, pool_kernel=5)
     assert e.value.code == -2
+
+
+# the hand-worked vote example (tests/golden/vote_worked_example.txt) fed straight to
+# ts_select; a fourth all-zero head (theta 0, no strict votes) makes the layout 4 / 1 heads
+def test_golden_vote_example_through_ts_select():
+    from golden_fixtures import vote_example
+    ex = vote_example()
+    n = ex["scores"].shape[1]
+    offs = api.Offsets([0, n], dev())
+    S = api.score_stride(offs)
+    sc = np.zeros((4, S), np.float32)
+    sc[:3, :n] = ex["scores"]
+    scores = to_dev(sc)
+    for sink, local, num, den, vmin, want in ex["selects"]:
+        p = api.params(api.MODE_VOTE, (num, den), sink, local, vmin, (1, 2))
+        sel = api.select(scores, offs, 1, p, want_theta=True, want_votes=True)
+        torch.cuda.synchronize()
+        assert np.array_equal(sel["idx"].cpu().numpy(), want)
+        assert np.array_equal(f64(sel["theta"])[0], np.r_[ex["theta"], 0.0])
+        assert np.array_equal(sel["votes"].cpu().numpy().astype(np.int32), ex["votes"])
+    sink, local, num, den, _ = ex["perhead"][0]
+    p = api.params(api.MODE_PER_HEAD, (num, den), sink, local, 1, (1, 2))
+    sel = api.select(scores, offs, 1, p)
+    torch.cuda.synchronize()
+    K = sel["counts_host"][0]
+    got = sel["idx"].cpu().numpy().reshape(4, K)
+    for h, (_, _, _, _, want) in ex["perhead"].items():
+        assert np.array_equal(got[h], want)
+    assert np.array_equal(got[3], [0, 1, 2, 3, 10, 11])
