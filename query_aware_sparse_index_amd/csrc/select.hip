@@ -589,72 +589,92 @@ __global__ __launch_bounds__(kChunk) void vote_kernel(const float* __restrict__ 
     }
 }
 
-// ------------------------------------------------------------------ vote scan
-// One block per sequence.  The chunk histograms of the sequence are staged in LDS, kScanTile
-// rows at a time (one tile covers sequences of up to kScanTile * kChunk tokens, which then
-// take one pass).  From the key totals: need = K - |F|, the boundary key v* (largest key
-// whose suffix count reaches need; none when need == 0), gt = #keys above v* and
-// need_eq = need - gt.  Per chunk c: eqb(c) = #tokens with key v* in earlier chunks and
-// base(c) = forced_before(first token of c) + #keys above v* in earlier chunks
-// + min(eqb(c), need_eq), the output rank of the chunk's first selected token.
-constexpr int kScanThreads = 1024;
+// ------------------------------------------------------------ vote compaction
+// One block per 1024-token chunk c of sequence b.  The block first stages the key histograms of
+// all chunks of b in LDS (kScanTile rows at a time) and sums them into the totals and into the
+// counts of the chunks before c.  From the totals: need = K - |F|, the boundary key v* (largest
+// key whose suffix count reaches need; none when need == 0), gt = #keys above v* and
+// need_eq = need - gt.  The chunk's first selected token then has output rank
+//   forced_before(first token of c) + #keys above v* before c + min(eqb, need_eq),
+// eqb = #keys equal to v* before c, and each token of the chunk is placed by two block scans:
+// every forced token, every non-forced token above v* and the first need_eq - eqb tokens equal
+// to v* in position order, written ascending.
 constexpr int kScanTile = 256;
 
-__global__ __launch_bounds__(kScanThreads) void vote_scan_kernel(const int64_t* __restrict__ offsets, DevCfg cfg,
-                                                                const uint32_t* __restrict__ hist,
-                                                                int2* __restrict__ chunk_info,
-                                                                int64_t* __restrict__ seq_info,
-                                                                int64_t* __restrict__ count_out) {
-    constexpr int NG = kScanThreads / kVoteBins;    // row groups for the column sums
+__global__ __launch_bounds__(kChunk) void compact_vote_kernel(const int64_t* __restrict__ offsets, int B,
+                                                             DevCfg cfg, const uint8_t* __restrict__ keys,
+                                                             const uint32_t* __restrict__ hist,
+                                                             int32_t* __restrict__ idx_out,
+                                                             int64_t* __restrict__ count_out) {
+    constexpr int NG = kChunk / kVoteBins;          // row groups for the column sums
     constexpr int V4 = kVoteBins / 4;               // uint4 per histogram row
+    constexpr int PER = (kScanTile * V4 + kChunk - 1) / kChunk;
     __shared__ uint4 stage[kScanTile * V4];
-    __shared__ uint32_t part[NG][kVoteBins];
-    __shared__ uint32_t tot[kVoteBins];
-    __shared__ int tmp[kScanThreads / 64];
+    __shared__ uint32_t part[NG][kVoteBins][2];
+    __shared__ uint32_t tot[kVoteBins], bef[kVoteBins];
+    __shared__ int tmp[kChunk / 64];
     __shared__ int64_t sh[2];
-    const int b = blockIdx.x;
+    int b;
+    int64_t first, nch, t0, len;
+    if (!find_chunk(offsets, B, blockIdx.x, b, first, nch, t0, len)) return;
     const int t = threadIdx.x;
-    int64_t first = 0, kpre = 0;
-    for (int i = 0; i < b; ++i) {
-        const int64_t ni = offsets[i + 1] - offsets[i];
-        first += (ni + kChunk - 1) / kChunk;
-        kpre += budget_k(ni, cfg.bnum, cfg.bden, cfg.sink, cfg.local);
-    }
-    const int64_t n = offsets[b + 1] - offsets[b];
-    const int64_t nch = (n + kChunk - 1) / kChunk;
-    const int64_t K = budget_k(n, cfg.bnum, cfg.bden, cfg.sink, cfg.local);
-    const int64_t need = K - forced_before(n, n, cfg.sink, cfg.local);
+    const int64_t off = offsets[b], n = offsets[b + 1] - off;
+    const int64_t c = blockIdx.x - first;
+    const uint8_t kk = t < len ? keys[off + t0 + t] : 0;
     const uint4* hrows = reinterpret_cast<const uint4*>(hist + (size_t)first * kVoteBins);
-    auto load_tile = [&](int64_t c0, int64_t rows) {
-        for (int64_t e = t; e < rows * V4; e += kScanThreads) stage[e] = hrows[c0 * V4 + e];
-    };
-    // key totals
+    // key totals over the sequence and over the chunks before c
     const int grp = t / kVoteBins, kb = t % kVoteBins;
-    uint32_t acc = 0;
-    for (int64_t c0 = 0; c0 < nch; c0 += kScanTile) {
-        const int64_t rows = nch - c0 < kScanTile ? nch - c0 : kScanTile;
-        __syncthreads();
-        load_tile(c0, rows);
+    uint32_t at = 0, ab = 0;
+    const int nchi = (int)nch, ci = (int)c;   // chunks of one sequence: < 2^14
+    for (int c0 = 0; c0 < nchi; c0 += kScanTile) {
+        const int rows = nchi - c0 < kScanTile ? nchi - c0 : kScanTile;
+        const int ne = rows * V4;
+        const uint4* src = hrows + (size_t)c0 * V4;
+        // all five loads first (clamped, unconditional), then the stores
+        static_assert(PER == 5, "staging is written out for five rows of uint4 per thread");
+        auto ld = [&](int u) {
+            const int e = t + u * kChunk;
+            return src[e < ne ? e : ne - 1];
+        };
+        const uint4 v0 = ld(0), v1 = ld(1), v2 = ld(2), v3 = ld(3), v4 = ld(4);
+        auto stv = [&](int u, const uint4& v) {
+            const int e = t + u * kChunk;
+            if (e < ne) stage[e] = v;
+        };
+        __syncthreads();                          // the previous tile has been consumed
+        stv(0, v0);
+        stv(1, v1);
+        stv(2, v2);
+        stv(3, v3);
+        stv(4, v4);
         __syncthreads();
         if (grp < NG) {
             const uint32_t* st32 = reinterpret_cast<const uint32_t*>(stage);
-            for (int64_t r = grp; r < rows; r += NG) acc += st32[r * kVoteBins + kb];
+            for (int r = grp; r < rows; r += NG) {
+                const uint32_t x = st32[r * kVoteBins + kb];
+                at += x;
+                ab += (c0 + r < ci) ? x : 0u;
+            }
         }
     }
-    if (grp < NG) part[grp][kb] = acc;
+    if (grp < NG) { part[grp][kb][0] = at; part[grp][kb][1] = ab; }
     __syncthreads();
     if (t < kVoteBins) {
-        uint32_t a = 0;
+        uint32_t a = 0, p = 0;
 #pragma unroll
-        for (int g = 0; g < NG; ++g) a += part[g][t];
+        for (int g = 0; g < NG; ++g) { a += part[g][t][0]; p += part[g][t][1]; }
         tot[t] = a;
+        bef[t] = p;
     }
     __syncthreads();
+    const int64_t K = budget_k(n, cfg.bnum, cfg.bden, cfg.sink, cfg.local);
+    const int64_t need = K - forced_before(n, n, cfg.sink, cfg.local);
     {
+        // suffix counts over the keys (thread t holds key kVoteBins - 1 - t)
         const int v = kVoteBins - 1 - t;
         const int cv = t < kVoteBins ? (int)tot[v] : 0;
         int all;
-        const int incl = block_inclusive_scan<kScanThreads>(cv, tmp, &all);
+        const int incl = block_inclusive_scan<kChunk>(cv, tmp, &all);
         if (t == 0) { sh[0] = kVoteBins; sh[1] = 0; }
         __syncthreads();
         if (need > 0 && t < kVoteBins && incl >= need && incl - cv < need) { sh[0] = v; sh[1] = incl - cv; }
@@ -662,81 +682,25 @@ __global__ __launch_bounds__(kScanThreads) void vote_scan_kernel(const int64_t* 
     }
     const int vs = (int)sh[0];
     const int64_t need_eq = need - sh[1];
-    // per-chunk bases (the last tile is still staged when the sequence fits in one)
-    int64_t carry_gt = 0, carry_eq = 0;
-    for (int64_t c0 = 0; c0 < nch; c0 += kScanTile) {
-        const int64_t rows = nch - c0 < kScanTile ? nch - c0 : kScanTile;
-        if (nch > kScanTile) {
-            __syncthreads();
-            load_tile(c0, rows);
-            __syncthreads();
-        }
-        int above = 0, eq = 0;
-        if (t < rows) {
-            const uint4* hr = stage + (size_t)t * V4;
-#pragma unroll
-            for (int k4 = 0; k4 < V4; ++k4) {
-                const uint4 w = hr[k4];
-                const int xs4[4] = {(int)w.x, (int)w.y, (int)w.z, (int)w.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int k = 4 * k4 + e;
-                    above += k > vs ? xs4[e] : 0;
-                    eq += k == vs ? xs4[e] : 0;
-                }
-            }
-        }
-        int ta, te;
-        const int ia = block_inclusive_scan<kScanThreads>(above, tmp, &ta);
-        const int ie = block_inclusive_scan<kScanThreads>(eq, tmp, &te);
-        if (t < rows) {
-            const int64_t gtb = carry_gt + ia - above, eqb = carry_eq + ie - eq;
-            const int64_t base = forced_before((c0 + t) * kChunk, n, cfg.sink, cfg.local) + gtb +
-                                 (eqb < need_eq ? eqb : need_eq);
-            chunk_info[first + c0 + t] = make_int2((int)base, (int)eqb);
-        }
-        carry_gt += ta;
-        carry_eq += te;
-    }
-    if (t == 0) {
-        seq_info[b * 4 + 0] = kpre;
-        seq_info[b * 4 + 1] = K;
-        seq_info[b * 4 + 2] = vs;
-        seq_info[b * 4 + 3] = need_eq;
-        count_out[b] = K;
-    }
-}
-
-// ------------------------------------------------------------ vote compaction
-// One thread per token: every forced token, every non-forced token above v* and the first
-// (need_eq - eqb) tokens equal to v* of the chunk, written ascending at their rank.
-__global__ __launch_bounds__(kChunk) void compact_vote_kernel(const int64_t* __restrict__ offsets, int B,
-                                                             const uint8_t* __restrict__ keys,
-                                                             const int2* __restrict__ chunk_info,
-                                                             const int64_t* __restrict__ seq_info,
-                                                             int32_t* __restrict__ idx_out) {
-    __shared__ int tmp[kChunk / 64];
-    int b;
-    int64_t first, nch, t0, len;
-    if (!find_chunk(offsets, B, blockIdx.x, b, first, nch, t0, len)) return;
-    const int64_t off = offsets[b];
-    const int64_t i = threadIdx.x;
-    const uint8_t kk = i < len ? keys[off + t0 + i] : 0;
-    const int2 ci = chunk_info[blockIdx.x];
-    const int64_t kpre = seq_info[b * 4 + 0], K = seq_info[b * 4 + 1];
-    const int vs = (int)seq_info[b * 4 + 2];
-    const int64_t need_eq = seq_info[b * 4 + 3];
-    const int eqf = (i < len && kk != 255 && kk == vs) ? 1 : 0;
-    int tot;
-    const int eq_rank = block_inclusive_scan<kChunk>(eqf, tmp, &tot) - eqf;
+    // keys above v* in the chunks before c
+    int gtb;
+    block_inclusive_scan<kChunk>((t < kVoteBins && t > vs) ? (int)bef[t] : 0, tmp, &gtb);
+    const int64_t eqb = vs < kVoteBins ? bef[vs] : 0;
+    const int64_t base = forced_before(t0, n, cfg.sink, cfg.local) + gtb + (eqb < need_eq ? eqb : need_eq);
+    if (c == 0 && t == 0) count_out[b] = K;
+    const int eqf = (t < len && kk != 255 && kk == vs) ? 1 : 0;
+    int tot_eq;
+    const int eq_rank = block_inclusive_scan<kChunk>(eqf, tmp, &tot_eq) - eqf;
     int sel = 0;
-    if (i < len) {
+    if (t < len) {
         if (kk == 255) sel = 1;
         else if (vs < kVoteBins && kk > vs) sel = 1;
-        else if (eqf) sel = ((int64_t)ci.y + eq_rank < need_eq) ? 1 : 0;
+        else if (eqf) sel = (eqb + eq_rank < need_eq) ? 1 : 0;
     }
-    const int64_t p = ci.x + block_inclusive_scan<kChunk>(sel, tmp, &tot) - sel;
-    if (sel && p < K) idx_out[kpre + p] = (int32_t)(t0 + i);
+    int tot_sel;
+    const int64_t p = base + block_inclusive_scan<kChunk>(sel, tmp, &tot_sel) - sel;
+    const int64_t kpre = kpre_of(offsets, b, cfg);
+    if (sel && p < K) idx_out[kpre + p] = (int32_t)(t0 + t);
 }
 
 // --------------------------------------------------------- per-head compaction
@@ -974,8 +938,7 @@ struct SelectLayout {
     int SL;
     int64_t nitems, ph_items, Ntot;
     uint32_t *cand, *cnt, *dhist, *hist, *phcnt;
-    int64_t *state, *seq_info;
-    int2* chunk_info;
+    int64_t* state;
     uint8_t *votes, *keys;
     size_t bytes;
 };
@@ -1005,8 +968,6 @@ static SelectLayout select_layout(void* ws, const int64_t* offsets_host, int B, 
     L.votes = w.take<uint8_t>((size_t)L.Ntot + 16);
     L.keys = w.take<uint8_t>((size_t)L.Ntot + 16);
     L.hist = w.take<uint32_t>((size_t)items * kVoteBins);
-    L.chunk_info = w.take<int2>((size_t)items);
-    L.seq_info = w.take<int64_t>((size_t)B * 4);
     L.phcnt = c.mode == 1 ? w.take<uint32_t>((size_t)Hq * ph_items * 2) : nullptr;
     L.bytes = w.size();
     return L;
@@ -1034,10 +995,8 @@ hipError_t launch_select(const float* scores, int64_t S, const int64_t* offsets_
         uint8_t* votes = votes_out ? votes_out : L.votes;
         hipLaunchKernelGGL(vote_kernel, dim3((unsigned)L.nitems), dim3(kChunk), 0, stream, scores, offsets_dev,
                            B, Hq, d, S, L.state, votes, L.keys, L.hist);
-        hipLaunchKernelGGL(vote_scan_kernel, dim3((unsigned)B), dim3(kScanThreads), 0, stream, offsets_dev, d, L.hist,
-                           L.chunk_info, L.seq_info, count_out);
         hipLaunchKernelGGL(compact_vote_kernel, dim3((unsigned)L.nitems), dim3(kChunk), 0, stream, offsets_dev,
-                           B, L.keys, L.chunk_info, L.seq_info, idx_out);
+                           B, d, L.keys, L.hist, idx_out, count_out);
     } else {
         hipLaunchKernelGGL(ph_count_kernel, dim3((unsigned)L.ph_items), dim3(kPhChunk), 0, stream, scores, offsets_dev,
                            B, Hq, d, S, L.state, L.ph_items, L.phcnt);
