@@ -10,14 +10,13 @@
 //
 // Both modes need an exact order statistic per (sequence, head): theta_h = s_(r) for the
 // vote, and the boundary score of the per-head top-K.  It is found on order-preserving
-// uint32 keys of the fp32 scores in three kernels:
-//   th_bracket : a key bracket [lo, hi] per instance from a stratified sample of the row
-//                (kRuns runs of 16 keys): a histogram over the sample's value range locates
-//                the sample order statistics kDelta ranks below and above the target's
-//                expected sample rank;
-//   th_collect : per slice of the row, counts the keys below lo, compacts the keys inside
-//                the bracket (the "candidates") next to the slice and histograms them on the
-//                top kDigit bits of key - lo;
+// uint32 keys of the fp32 scores in two kernels:
+//   th_collect : every block of an instance derives the same key bracket [lo, hi] from a
+//                stratified sample of the row (kRuns runs of 16 keys): a histogram over the
+//                sample's value range locates the sample order statistics kDelta ranks below
+//                and above the target's expected sample rank.  Then, per slice of the row, it
+//                counts the keys below lo, compacts the keys inside the bracket (the
+//                "candidates") next to the slice grouped by their top kDigit bits of key - lo;
 //   th_final   : sums the slice histograms to find the answer's top digit, gathers the
 //                candidates of that digit into LDS and finishes with a radix select over
 //                the remaining bits.  If the answer's rank is not among the candidates (or
@@ -128,38 +127,18 @@ __host__ __device__ __forceinline__ int top_shift(uint32_t span) {
     return nbits > kDigit ? nbits - kDigit : 0;
 }
 
-// One block per instance: flag, need and the key bracket [lo, hi] in the instance's state.
-// Rows of m <= kCap keys take every key ([0, 2^32 - 1]).  Longer rows: run j of the sample
-// starts at a hashed position of stratum [j m / kRuns, (j + 1) m / kRuns); the sample's
-// [min, max] is cut into kSampleBins equal bins; lo is the lower edge of the bin before the
-// one holding sample rank ir - kDelta and hi the upper edge of the bin after the one holding
-// ir + kDelta (the key range's ends when these leave the sample), ir the target's expected
-// sample rank.
-__global__ __launch_bounds__(kColThreads) void th_bracket_kernel(const float* __restrict__ scores,
-                                                                const int64_t* __restrict__ offsets, int Hq,
-                                                                DevCfg cfg, int64_t S, int64_t* __restrict__ state) {
+// Key bracket [lo, hi] of an instance whose row (m keys) is longer than kCap; every thread of
+// the block calls it and every block of the instance computes the same result.  Run j of the
+// sample starts at a hashed position of stratum [j m / kRuns, (j + 1) m / kRuns); the
+// sample's [min, max] is cut into kSampleBins equal bins; lo is the lower edge of the bin
+// before the one holding sample rank ir - kDelta and hi the upper edge of the bin after the one
+// holding ir + kDelta (the key range's ends when these leave the sample), ir the target's
+// expected sample rank.  `hist` (kSampleBins words) is left dirty.
+__device__ void sample_bracket(const float* __restrict__ row, const OsInst& oi, int inst, uint32_t* hist,
+                               float* wmin, float* wmax, int* tmp, int* sb, uint32_t& klo, uint32_t& khi) {
     constexpr int NW = kColThreads / 64;
-    __shared__ float wmin[NW], wmax[NW];
-    __shared__ uint32_t hist[kSampleBins];
-    __shared__ int tmp[NW];
-    __shared__ int sb[2];
-    const int inst = blockIdx.x;
-    const int b = inst / Hq, h = inst % Hq;
-    const int64_t off = offsets[b];
-    const OsInst oi = os_instance(offsets[b + 1] - off, cfg);
-    int64_t* st = state + (int64_t)inst * 8;
-    const int64_t m = oi.end - oi.beg;
-    if (oi.flag != kFlagActive || m <= kCap) {
-        if (threadIdx.x == 0) {
-            st[kStFlag] = oi.flag;
-            st[kStNeed] = oi.need;
-            st[kStLo] = 0;
-            st[kStHi] = 0xffffffffll;
-        }
-        return;
-    }
-    const float* row = scores + (int64_t)h * S + off;
     constexpr int PER = kSample / kColThreads;
+    const int64_t m = oi.end - oi.beg;
     float v[PER];
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
@@ -184,7 +163,8 @@ __global__ __launch_bounds__(kColThreads) void th_bracket_kernel(const float* __
     for (int w = 1; w < NW; ++w) { mn = fminf(mn, wmin[w]); mx = fmaxf(mx, wmax[w]); }
     const int64_t ir = (oi.rank - 1) * kSample / m;
     const int64_t il = ir - kDelta, ih = ir + kDelta;
-    uint32_t klo = 0u, khi = 0xffffffffu;
+    klo = 0u;
+    khi = 0xffffffffu;
     if (mx > mn) {
         const float scale = (float)kSampleBins / (mx - mn);
 #pragma unroll
@@ -217,50 +197,60 @@ __global__ __launch_bounds__(kColThreads) void th_bracket_kernel(const float* __
         klo = khi = order_key(mn);
     }
     if (klo > khi) klo = khi;
-    if (threadIdx.x == 0) {
-        st[kStFlag] = oi.flag;
-        st[kStNeed] = oi.need;
-        st[kStLo] = klo;
-        st[kStHi] = khi;
-    }
+    __syncthreads();
 }
 
-// Block (slice s, instance): cnt[(inst * SL + s) * 2] = #keys < lo, [+1] = #candidates;
+// Block (slice s, instance).  Every block derives the instance's key bracket (all keys when
+// the row has at most kCap of them, else sample_bracket); block 0 stores the flag, need and
+// bracket in the state.  Output: cnt[(inst * SL + s) * 2] = #keys < lo, [+1] = #candidates;
 // the candidates (keys in [lo, hi]) at cand[(inst * SL + s) * kSlice ...], grouped by their top
 // digit (key - lo) >> top_shift(hi - lo) in ascending digit order (any order inside a digit);
-// dpre[inst][s][d] = number of the slice's candidates with digit < d, d = 0 .. kDigitBins,
-// as 16-bit values.
+// dpre[inst][s]: the number of the slice's candidates with digit < d, d = 0 .. kDigitBins, as
+// 16-bit values (kPreWords words), followed by the count of each digit (16-bit, two per word).
 constexpr int kPreWords = kDigitBins / 2 + 1;   // 16-bit prefix values 0 .. kDigitBins, two per word
+constexpr int kDpWords = kPreWords + kDigitBins / 2 + 1;   // per slice: prefixes, then counts (two per word)
 __global__ __launch_bounds__(kColThreads) void th_collect_kernel(const float* __restrict__ scores,
                                                                 const int64_t* __restrict__ offsets, int Hq,
                                                                 DevCfg cfg, int SL, int64_t S,
-                                                                const int64_t* __restrict__ state,
+                                                                int64_t* __restrict__ state,
                                                                 uint32_t* __restrict__ cand,
                                                                 uint32_t* __restrict__ cnt,
                                                                 uint32_t* __restrict__ dpre) {
     constexpr int NW = kColThreads / 64;
     constexpr int PT = kSlice / kColThreads;       // slice keys per thread
     constexpr int BPT = kDigitBins / kColThreads;  // digit bins per thread in the scan
+    static_assert(kDigitBins == kSampleBins, "the sample and digit histograms share one array");
     __shared__ int wsum[NW];
     __shared__ int tmp[NW];
-    __shared__ uint32_t hist[kDigitBins];          // counts, then the running cursor per digit
+    __shared__ float wmin[NW], wmax[NW];
+    __shared__ int sb[2];
+    __shared__ uint32_t hist[kDigitBins];          // sample bins; then digit counts, then cursors
     const int inst = blockIdx.y, s = blockIdx.x;
     const int b = inst / Hq, h = inst % Hq;
     const int64_t off = offsets[b];
     const OsInst oi = os_instance(offsets[b + 1] - off, cfg);
+    int64_t* st = state + (int64_t)inst * 8;
+    if (s == 0 && threadIdx.x == 0) {
+        st[kStFlag] = oi.flag;
+        st[kStNeed] = oi.need;
+    }
     if (oi.flag != kFlagActive) return;
     const int64_t lo = oi.beg + (int64_t)s * kSlice;
     const int64_t hi = lo + kSlice < oi.end ? lo + kSlice : oi.end;
     const float* row = scores + (int64_t)h * S + off;
-    // the slice and the bracket in one memory round trip
+    // the slice and the sample in one memory round trip
     float xv[PT];
 #pragma unroll
     for (int j = 0; j < PT; ++j) {
         const int64_t t = lo + threadIdx.x + (int64_t)j * kColThreads;
         xv[j] = t < hi ? row[t] : 0.f;
     }
-    const int64_t* st = state + (int64_t)inst * 8;
-    const uint32_t klo = (uint32_t)st[kStLo], khi = (uint32_t)st[kStHi];
+    uint32_t klo = 0u, khi = 0xffffffffu;
+    if (oi.end - oi.beg > kCap) sample_bracket(row, oi, inst, hist, wmin, wmax, tmp, sb, klo, khi);
+    if (s == 0 && threadIdx.x == 0) {
+        st[kStLo] = klo;
+        st[kStHi] = khi;
+    }
     for (int i = threadIdx.x; i < kDigitBins; i += kColThreads) hist[i] = 0;
     __syncthreads();
     const int dsh = top_shift(khi - klo);
@@ -287,8 +277,10 @@ __global__ __launch_bounds__(kColThreads) void th_collect_kernel(const float* __
     for (int u = 0; u < BPT; ++u) { c[u] = hist[threadIdx.x * BPT + u]; csum += (int)c[u]; }
     int total;
     const int incl = block_inclusive_scan<kColThreads>(csum, tmp, &total);
-    uint32_t* dp = dpre + ((size_t)inst * SL + s) * kPreWords;
+    uint32_t* dp = dpre + ((size_t)inst * SL + s) * kDpWords;
     {
+#pragma unroll
+        for (int u = 0; u < BPT; u += 2) dp[kPreWords + (threadIdx.x * BPT + u) / 2] = c[u] | (c[u + 1] << 16);
         uint32_t acc = (uint32_t)(incl - csum);
         uint32_t pre[BPT];
 #pragma unroll
@@ -405,27 +397,19 @@ __global__ __launch_bounds__(kThThreads) void th_final_kernel(const float* __res
     // candidates per digit pair (2t, 2t+1), summed over the slices from their prefixes
     uint32_t dlo = 0, dhi = 0;
     {
-        const uint32_t* dp = dpre + (size_t)inst * SL * kPreWords;
-        int sl = 0;
-        for (; sl + 4 <= nsl; sl += 4) {
-            uint32_t w0[4], w1[4];
+        // digit pair (2t, 2t+1) counts summed over the slices, 32 slices' words in flight
+        constexpr int SLR = 32;
+        const uint32_t* dc = dpre + (size_t)inst * SL * kDpWords + kPreWords + t;
+        for (int sl0 = 0; sl0 < nsl; sl0 += SLR) {
+            uint32_t w[SLR];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                w0[u] = dp[(size_t)(sl + u) * kPreWords + t];
-                w1[u] = dp[(size_t)(sl + u) * kPreWords + t + 1];
-            }
+            for (int u = 0; u < SLR; ++u) w[u] = dc[(size_t)(sl0 + u < nsl ? sl0 + u : nsl - 1) * kDpWords];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const uint32_t p0 = w0[u] & 0xffffu, p1 = w0[u] >> 16, p2 = w1[u] & 0xffffu;
-                dlo += p1 - p0;
-                dhi += p2 - p1;
+            for (int u = 0; u < SLR; ++u) {
+                const uint32_t x = sl0 + u < nsl ? w[u] : 0u;
+                dlo += x & 0xffffu;
+                dhi += x >> 16;
             }
-        }
-        for (; sl < nsl; ++sl) {
-            const uint32_t w0 = dp[(size_t)sl * kPreWords + t], w1 = dp[(size_t)sl * kPreWords + t + 1];
-            const uint32_t p0 = w0 & 0xffffu, p1 = w0 >> 16, p2 = w1 & 0xffffu;
-            dlo += p1 - p0;
-            dhi += p2 - p1;
         }
     }
     int nmid, nlo;
@@ -465,10 +449,10 @@ __global__ __launch_bounds__(kThThreads) void th_final_kernel(const float* __res
             } else {
                 // copy digit D's candidates of every slice (their low bits) into LDS
                 const uint32_t low = dsh ? ((1u << dsh) - 1u) : 0u;
-                const uint32_t* dp = dpre + (size_t)inst * SL * kPreWords;
+                const uint32_t* dp = dpre + (size_t)inst * SL * kDpWords;
                 for (int sl = t; sl < nsl; sl += kThThreads) {
-                    const uint32_t a = (dp[(size_t)sl * kPreWords + D / 2] >> (16 * (D & 1))) & 0xffffu;
-                    const uint32_t e = (dp[(size_t)sl * kPreWords + (D + 1) / 2] >> (16 * ((D + 1) & 1))) & 0xffffu;
+                    const uint32_t a = (dp[(size_t)sl * kDpWords + D / 2] >> (16 * (D & 1))) & 0xffffu;
+                    const uint32_t e = (dp[(size_t)sl * kDpWords + (D + 1) / 2] >> (16 * ((D + 1) & 1))) & 0xffffu;
                     if (e > a) {
                         const uint32_t base = atomicAdd(&nd, e - a);
                         const uint32_t* src = cand + ((size_t)inst * SL + sl) * kSlice;
@@ -477,11 +461,33 @@ __global__ __launch_bounds__(kThThreads) void th_final_kernel(const float* __res
                 }
                 __syncthreads();
                 const int cntD = (int)nd;
-                const uint32_t xl = radix_rank(
-                    [&](auto f) {
-                        for (int i = t; i < cntD; i += kThThreads) f(xs[i]);
-                    },
-                    dsh, rr, hist, tmp, sh, &gt);
+                uint32_t xl;
+                if (cntD <= 64) {
+                    // one wave ranks the bucket: the answer x has #{< x} < rr <= #{<= x}
+                    if (t < 64) {
+                        const bool has = t < cntD;
+                        const uint32_t x = has ? xs[t] : 0xffffffffu;
+                        int less = 0, leq = 0;
+                        for (int j = 0; j < cntD; ++j) {
+                            const uint32_t y = __shfl(x, j, 64);
+                            less += y < x ? 1 : 0;
+                            leq += y <= x ? 1 : 0;
+                        }
+                        if (has && less < rr && rr <= leq) {
+                            sh[0] = x;
+                            sh[1] = cntD - leq;
+                        }
+                    }
+                    __syncthreads();
+                    xl = (uint32_t)sh[0];
+                    gt += sh[1];
+                } else {
+                    xl = radix_rank(
+                        [&](auto f) {
+                            for (int i = t; i < cntD; i += kThThreads) f(xs[i]);
+                        },
+                        dsh, rr, hist, tmp, sh, &gt);
+                }
                 key = klo + ((D << dsh) | xl);
             }
         }
@@ -963,7 +969,7 @@ static SelectLayout select_layout(void* ws, const int64_t* offsets_host, int B, 
     const size_t inst = (size_t)B * Hq;
     L.cand = w.take<uint32_t>(inst * L.SL * kSlice);
     L.cnt = w.take<uint32_t>(inst * L.SL * 2);
-    L.dhist = w.take<uint32_t>(inst * L.SL * kPreWords);
+    L.dhist = w.take<uint32_t>(inst * L.SL * kDpWords);
     L.state = w.take<int64_t>(inst * 8);
     L.votes = w.take<uint8_t>((size_t)L.Ntot + 16);
     L.keys = w.take<uint8_t>((size_t)L.Ntot + 16);
@@ -984,8 +990,6 @@ hipError_t launch_select(const float* scores, int64_t S, const int64_t* offsets_
     if (L.bytes > ws_bytes || L.SL > kMaxSL) return hipErrorInvalidValue;
     DevCfg d = dev_cfg(c);
     const unsigned inst = (unsigned)(B * Hq);
-    hipLaunchKernelGGL(th_bracket_kernel, dim3(inst), dim3(kColThreads), 0, stream, scores, offsets_dev, Hq, d, S,
-                       L.state);
     hipLaunchKernelGGL(th_collect_kernel, dim3(L.SL, inst), dim3(kColThreads), 0, stream, scores, offsets_dev, Hq, d,
                        L.SL, S, L.state, L.cand, L.cnt, L.dhist);
     hipLaunchKernelGGL(th_final_kernel, dim3(inst), dim3(kThThreads), 0, stream, scores, offsets_dev, Hq, d, L.SL, S,
