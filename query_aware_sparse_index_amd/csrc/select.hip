@@ -369,6 +369,7 @@ __global__ __launch_bounds__(kThThreads) void th_final_kernel(const float* __res
                                                              int64_t* __restrict__ state, float* __restrict__ theta_out) {
     static_assert(kDigitBins / 2 == kThThreads, "one pair of digit bins per thread");
     __shared__ uint32_t xs[kCap];
+    __shared__ int segpre[kMaxSL + 1], sega[kMaxSL];
     __shared__ uint32_t hist[kDigitBins];
     __shared__ int tmp[kThThreads / 64];
     __shared__ int64_t sh[4];
@@ -447,19 +448,73 @@ __global__ __launch_bounds__(kThThreads) void th_final_kernel(const float* __res
             if (nD > kCap) {
                 whole_row = true;
             } else {
-                // copy digit D's candidates of every slice (their low bits) into LDS
+                // copy digit D's candidates of every slice (their low bits) into LDS: the slices'
+                // segments [a_s, e_s) of their digit-sorted candidates are laid end to end
                 const uint32_t low = dsh ? ((1u << dsh) - 1u) : 0u;
                 const uint32_t* dp = dpre + (size_t)inst * SL * kDpWords;
-                for (int sl = t; sl < nsl; sl += kThThreads) {
-                    const uint32_t a = (dp[(size_t)sl * kDpWords + D / 2] >> (16 * (D & 1))) & 0xffffu;
-                    const uint32_t e = (dp[(size_t)sl * kDpWords + (D + 1) / 2] >> (16 * ((D + 1) & 1))) & 0xffffu;
-                    if (e > a) {
-                        const uint32_t base = atomicAdd(&nd, e - a);
-                        const uint32_t* src = cand + ((size_t)inst * SL + sl) * kSlice;
-                        for (uint32_t q = a; q < e; ++q) xs[base + (q - a)] = (src[q] - klo) & low;
+                auto pre_at = [&](int sl, uint32_t d) {
+                    return (dp[(size_t)sl * kDpWords + d / 2] >> (16 * (d & 1))) & 0xffffu;
+                };
+                if (nD <= 1024) {
+                    // small bucket: one thread per slice copies its few keys
+                    for (int sl = t; sl < nsl; sl += kThThreads) {
+                        const uint32_t a = pre_at(sl, D), e = pre_at(sl, D + 1);
+                        if (e > a) {
+                            const uint32_t base = atomicAdd(&nd, e - a);
+                            const uint32_t* src = cand + ((size_t)inst * SL + sl) * kSlice;
+                            for (uint32_t q = a; q < e; ++q) xs[base + (q - a)] = (src[q] - klo) & low;
+                        }
                     }
+                    __syncthreads();
+                } else {
+                    // large bucket: every thread copies keys, 16 in flight
+                    int la[2], ll[2];
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        const int sl = 2 * t + u;
+                        la[u] = 0;
+                        ll[u] = 0;
+                        if (sl < nsl) {
+                            la[u] = (int)pre_at(sl, D);
+                            ll[u] = (int)pre_at(sl, D + 1) - la[u];
+                        }
+                    }
+                    int ntot;
+                    const int sinc = block_inclusive_scan<kThThreads>(ll[0] + ll[1], tmp, &ntot);
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        const int sl = 2 * t + u;
+                        if (sl < nsl) {
+                            segpre[sl] = sinc - ll[0] - ll[1] + (u ? ll[0] : 0);
+                            sega[sl] = la[u];
+                        }
+                    }
+                    if (t == 0) segpre[nsl] = ntot;
+                    __syncthreads();
+                    for (int i0 = t; i0 < ntot; i0 += 16 * kThThreads) {
+                        uint32_t v[16];
+#pragma unroll
+                        for (int u = 0; u < 16; ++u) {
+                            const int i = i0 + u * kThThreads;
+                            v[u] = klo;
+                            if (i < ntot) {
+                                int a = 0, z = nsl - 1;          // last slice with segpre[slice] <= i
+                                while (a < z) {
+                                    const int mid = (a + z + 1) >> 1;
+                                    if (segpre[mid] <= i) a = mid; else z = mid - 1;
+                                }
+                                v[u] = cand[((size_t)inst * SL + a) * kSlice + sega[a] + (i - segpre[a])];
+                            }
+                        }
+#pragma unroll
+                        for (int u = 0; u < 16; ++u) {
+                            const int i = i0 + u * kThThreads;
+                            if (i < ntot) xs[i] = (v[u] - klo) & low;
+                        }
+                    }
+                    if (t == 0) nd = (uint32_t)ntot;
+                    __syncthreads();
                 }
-                __syncthreads();
                 const int cntD = (int)nd;
                 uint32_t xl;
                 if (cntD <= 64) {
