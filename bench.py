@@ -327,8 +327,8 @@ def main():
     torch.cuda.synchronize()
     print("bench: warm-up done", file=sys.stderr, flush=True)
 
-    # timed steps: events per step and per call; flushes between steps are not timed
-    marks = [[ev() for _ in range(5)] for _ in range(steps)]
+    # timed steps: one event pair per step; flushes between steps are not timed
+    marks = [(ev(), ev()) for _ in range(steps)]
     ktot = []
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
@@ -336,20 +336,33 @@ def main():
         s = warm + i
         if not args.no_flush:
             do_flush()
-        m = marks[i]
-        m[0].record()
-        ktot.append(step(s, m))
-        m[4].record()
+        marks[i][0].record()
+        ktot.append(step(s))
+        marks[i][1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
-    step_us = np.array([m[0].elapsed_time(m[4]) * 1e3 for m in marks])
-    parts = {
-        "index_append": np.array([m[0].elapsed_time(m[1]) * 1e3 for m in marks]),
-        "score": np.array([m[1].elapsed_time(m[2]) * 1e3 for m in marks]),
-        "select": np.array([m[2].elapsed_time(m[3]) * 1e3 for m in marks]),
-        "sparse_decode": np.array([m[3].elapsed_time(m[4]) * 1e3 for m in marks]),
-    }
+    step_us = np.array([a.elapsed_time(b) * 1e3 for a, b in marks])
     print(f"bench: timed {steps} steps, mean {step_us.mean():.1f} us", file=sys.stderr, flush=True)
+
+    # per-call breakdown in separate steps (the same inputs again): an event between two calls
+    # idles the GPU for a few microseconds, so these steps are not the timed ones
+    nb = min(steps, 30)
+    bmarks = [[ev() for _ in range(5)] for _ in range(nb)]
+    for i in range(nb):
+        if not args.no_flush:
+            do_flush()
+        m = bmarks[i]
+        m[0].record()
+        step(warm + steps - nb + i, m)
+        m[4].record()
+    torch.cuda.synchronize()
+    parts = {
+        "index_append": np.array([m[0].elapsed_time(m[1]) * 1e3 for m in bmarks]),
+        "score": np.array([m[1].elapsed_time(m[2]) * 1e3 for m in bmarks]),
+        "select": np.array([m[2].elapsed_time(m[3]) * 1e3 for m in bmarks]),
+        "sparse_decode": np.array([m[3].elapsed_time(m[4]) * 1e3 for m in bmarks]),
+    }
+    breakdown_step = float(np.mean([m[0].elapsed_time(m[4]) * 1e3 for m in bmarks]))
 
     # algorithmic bytes (what the method must move): index read + selected K/V rows
     n_mean = n0 + warm + (steps + 1) / 2.0
@@ -547,6 +560,7 @@ def main():
         "pct_peak": round(100 * gbps / PEAK_GBPS, 1),
         "algorithmic_bytes_per_step": int(step_bytes),
         "breakdown_us": {k: round(float(v.mean()), 2) for k, v in parts.items()},
+        "breakdown_step_us": round(breakdown_step, 2),
         "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": PEAK_GBPS, "unit": "GB/s",
                      "frac": round(dec_gbps / PEAK_GBPS, 4), "traffic": traffic,
                      "kernel": "ts_sparse_decode (decode_partial_kernel + decode_merge_kernel), alone, LLC flushed",

@@ -16,6 +16,7 @@
 //   pass 2 (snap_pass_kernel<2>): p = 2^(s - LSE_r); the column sum over the R rows (a
 //                                 16-lane DPP butterfly per 16-row tile) gives imp[j] * R
 // Scores are kept in the log2 domain (s = q.k * log2(e)/sqrt(128)) so that exp2 is used.
+#include <type_traits>
 #include <utility>
 
 #include "qasi_device.h"
@@ -75,17 +76,15 @@ __global__ __launch_bounds__(kSnapThreads) void snap_pass_kernel(const uint16_t*
 
     // A fragments of key block kb: key jw(kb) + kt*16 + lr, dims 32 s + 8 lg .. +8
     auto key0 = [&](int64_t kb) { return kb * kSnapKT + (int64_t)wid * kSnapKTW * 16; };
+    // keys past the end load key n - 1 (in bounds); their scores are masked in compute
     auto load = [&](bf16x8_t (&a)[kSnapKTW][4], int64_t kb) {
         const int64_t jw = key0(kb);
 #pragma unroll
         for (int kt = 0; kt < kSnapKTW; ++kt) {
-            const int64_t jl = jw + kt * 16 + lr;
+            const int64_t jl = min(jw + kt * 16 + lr, n - 1);
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                uint4 v = make_uint4(0, 0, 0, 0);
-                if (jl < n) v = *reinterpret_cast<const uint4*>(K + (jl * Hkv + g) * kD + s * 32 + lg * 8);
-                a[kt][s] = as_bf16x8(v);
-            }
+            for (int s = 0; s < 4; ++s)
+                a[kt][s] = as_bf16x8(*reinterpret_cast<const uint4*>(K + (jl * Hkv + g) * kD + s * 32 + lg * 8));
         }
     };
 
@@ -93,17 +92,19 @@ __global__ __launch_bounds__(kSnapThreads) void snap_pass_kernel(const uint16_t*
         for (int c = 0; c < RT; ++c) mlst[(wid * RT + c) * 64 + lane] = make_float2(-INFINITY, 0.f);
 
     // one key block: pass 1 folds its scores into (m, l), pass 2 writes its keys' importance
-    auto compute = [&](const bf16x8_t (&a)[kSnapKTW][4], int64_t kb) {
+    // MASK: the wave's keys reach past n (only in the last key block)
+    auto compute = [&](const bf16x8_t (&a)[kSnapKTW][4], int64_t kb, auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
         const int64_t jw = key0(kb);
-        const bool full = jw + kSnapKTW * 16 <= n;   // only the last key block has keys >= n
         float colsum[(PASS == 2) ? kSnapKTW : 1][4];
 #pragma unroll
         for (int kt = 0; kt < ((PASS == 2) ? kSnapKTW : 1); ++kt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) colsum[kt][i] = 0.f;
+
         // row tiles, unrolled by a divisor of RT
         constexpr int U2 = (RT % 4 == 0 && RT > 4) ? 4 : ((RT % 2 == 0) ? 2 : 1);
-#pragma unroll(U2)
+#pragma unroll U2
         for (int c = 0; c < RT; ++c) {
             const int r = c * 16 + lr;
             bf16x8_t bq[4];
@@ -117,7 +118,7 @@ __global__ __launch_bounds__(kSnapThreads) void snap_pass_kernel(const uint16_t*
 #pragma unroll
                 for (int kt = 0; kt < kSnapKTW; ++kt)
                     acc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[kt][s], bq[s], acc[kt], 0, 0, 0);
-            if (!full) {
+            if (MASK) {
 #pragma unroll
                 for (int kt = 0; kt < kSnapKTW; ++kt)
 #pragma unroll
@@ -133,16 +134,16 @@ __global__ __launch_bounds__(kSnapThreads) void snap_pass_kernel(const uint16_t*
                     for (int i = 0; i < 4; ++i) mx = fmaxf(mx, acc[kt][i]);
                 float2 ml = mlst[(wid * RT + c) * 64 + lane];
                 const float mn = fmaxf(ml.x, mx * kSnapScale);
-                if (mn != -INFINITY) {
-                    float e = 0.f;
+                // while every score seen is -inf, subtract 0 so that the terms are 0, not NaN
+                const float ms = (mn == -INFINITY) ? 0.f : mn;
+                float e = 0.f;
 #pragma unroll
-                    for (int kt = 0; kt < kSnapKTW; ++kt)
+                for (int kt = 0; kt < kSnapKTW; ++kt)
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) e += fast_exp2(fmaf(acc[kt][i], kSnapScale, -mn));
-                    ml.y = ml.y * fast_exp2(ml.x - mn) + e;
-                    ml.x = mn;
-                    mlst[(wid * RT + c) * 64 + lane] = ml;
-                }
+                    for (int i = 0; i < 4; ++i) e += fast_exp2(fmaf(acc[kt][i], kSnapScale, -ms));
+                ml.y = ml.y * fast_exp2(ml.x - ms) + e;
+                ml.x = mn;
+                mlst[(wid * RT + c) * 64 + lane] = ml;
             } else {
                 const float lr_c = sL[r];
 #pragma unroll
@@ -151,6 +152,7 @@ __global__ __launch_bounds__(kSnapThreads) void snap_pass_kernel(const uint16_t*
                     for (int i = 0; i < 4; ++i) colsum[kt][i] += fast_exp2(fmaf(acc[kt][i], kSnapScale, -lr_c));
             }
         }
+
         if (PASS == 2) {
             // column sums over the 16 rows of each lane group (DPP butterfly); lane lr == i writes
 #pragma unroll
@@ -164,15 +166,25 @@ __global__ __launch_bounds__(kSnapThreads) void snap_pass_kernel(const uint16_t*
         }
     };
 
+    // the wave index is uniform: read it into a scalar so that the full / masked choice is a
+    // scalar branch and the row-tile loop stays one basic block
+    const int64_t wkeys = (int64_t)__builtin_amdgcn_readfirstlane(wid) * kSnapKTW * 16 + kSnapKTW * 16;
+    auto run = [&](const bf16x8_t (&a)[kSnapKTW][4], int64_t kb) {
+        if (kb * kSnapKT + wkeys <= n)
+            compute(a, kb, std::false_type{});
+        else
+            compute(a, kb, std::true_type{});
+    };
+
     bf16x8_t a0[kSnapKTW][4], a1[kSnapKTW][4];
     if (p < nblk) load(a0, p);
     __syncthreads();
     for (int64_t kb = p; kb < nblk; kb += 2 * (int64_t)P) {
         if (kb + P < nblk) load(a1, kb + P);
-        compute(a0, kb);
+        run(a0, kb);
         if (kb + P >= nblk) break;
         if (kb + 2 * (int64_t)P < nblk) load(a0, kb + 2 * (int64_t)P);
-        compute(a1, kb + P);
+        run(a1, kb + P);
     }
 
     if (PASS == 1) {
