@@ -19,6 +19,8 @@
  *     K_index[t][g][32], where sequence b owns rows [offsets[b], offsets[b+1]).  Functions
  *     that size launches take the same offsets twice: `offsets_dev` (device, read by the
  *     kernels) and `offsets_host` (host, read synchronously to size grids; no device sync).
+ *     For a single sequence (B = 1) the kernels take the bounds, and in the decode calls the
+ *     list length, from the host copies as launch arguments, so the two copies must agree.
  *   - Token positions inside index lists are sequence-local (0 .. n_b - 1).
  *   - The caller owns every buffer.  Nothing is allocated or freed by any call; scratch
  *     comes from a caller workspace sized by the *_workspace_bytes queries.  No pointer is

@@ -23,7 +23,7 @@ namespace qasi {
 
 constexpr int kDecCH = 64;            // list entries per chunk
 constexpr float kLog2eOverSqrtD = 1.4426950408889634f / 11.313708498984761f;
-__device__ __forceinline__ bool find_list_chunk(const int64_t* __restrict__ counts, int B, int64_t item, int& b,
+__device__ __forceinline__ bool find_list_chunk(const I64Arg& counts, int B, int64_t item, int& b,
                                                 int64_t& first, int64_t& nch, int64_t& j0, int64_t& len,
                                                 int64_t& kpre) {
     int64_t acc = 0, kp = 0;
@@ -51,9 +51,9 @@ template <int G, int MODE>
 __global__ __launch_bounds__(512) void decode_partial_kernel(const uint16_t* __restrict__ q,
                                                             const uint16_t* __restrict__ K,
                                                             const uint16_t* __restrict__ V,
-                                                            const int64_t* __restrict__ offsets,
+                                                            I64Arg offsets,
                                                             const int32_t* __restrict__ idx,
-                                                            const int64_t* __restrict__ counts, int B, int Hq,
+                                                            I64Arg counts, int B, int Hq,
                                                             int Hkv, float* __restrict__ part_acc,
                                                             float2* __restrict__ part_ml) {
     constexpr int GH = (MODE == 1) ? 1 : G;          // query heads per wave
@@ -249,7 +249,7 @@ __global__ __launch_bounds__(512) void decode_partial_kernel(const uint16_t* __r
 // sum_c acc_c 2^(m_c - M) and sum_c l_c 2^(m_c - M) are reduced over the 64 groups in LDS.
 __global__ __launch_bounds__(1024) void decode_merge_kernel(const float* __restrict__ part_acc,
                                                            const float2* __restrict__ part_ml,
-                                                           const int64_t* __restrict__ counts, int B, int Hq,
+                                                           I64Arg counts, int B, int Hq,
                                                            float* __restrict__ out) {
     constexpr int U = 8;
     __shared__ float sa[64][17];
@@ -331,8 +331,8 @@ size_t decode_workspace(const int64_t* offsets_host, const int64_t* counts_host,
 
 template <int MODE>
 static hipError_t launch_partial_G(int G, dim3 grid, hipStream_t stream, const uint16_t* q, const uint16_t* K,
-                                   const uint16_t* V, const int64_t* offsets, const int32_t* idx,
-                                   const int64_t* counts, int B, int Hq, int Hkv, float* part, float2* ml) {
+                                   const uint16_t* V, const I64Arg& offsets, const int32_t* idx,
+                                   const I64Arg& counts, int B, int Hq, int Hkv, float* part, float2* ml) {
     dim3 block(MODE == 1 ? 64 * G : 512);
     switch (G) {
         case 1: hipLaunchKernelGGL((decode_partial_kernel<1, MODE>), grid, block, 0, stream, q, K, V, offsets, idx, counts, B, Hq, Hkv, part, ml); break;
@@ -345,7 +345,7 @@ static hipError_t launch_partial_G(int G, dim3 grid, hipStream_t stream, const u
 }
 
 // dense decode: counts are the sequence lengths, computed on the device into the workspace
-__global__ void lengths_kernel(const int64_t* __restrict__ offsets, int B, int64_t* __restrict__ lens) {
+__global__ void lengths_kernel(I64Arg offsets, int B, int64_t* __restrict__ lens) {
     for (int b = threadIdx.x; b < B; b += blockDim.x) lens[b] = offsets[b + 1] - offsets[b];
 }
 
@@ -360,11 +360,13 @@ hipError_t launch_sparse_decode(const uint16_t* q, const uint16_t* K, const uint
     float* part = w.take<float>((size_t)items * Hq * kD);
     float2* ml = w.take<float2>((size_t)items * Hq);
     const int G = Hq / Hkv;
+    const I64Arg offs = i64_arg(offsets_dev, offsets_host, (int64_t)B + 1);
+    const I64Arg cnts = i64_arg(counts_dev, counts_host, B);
     hipError_t e;
-    if (mode == 0) e = launch_partial_G<0>(G, dim3((unsigned)items), stream, q, K, V, offsets_dev, idx, counts_dev, B, Hq, Hkv, part, ml);
-    else e = launch_partial_G<1>(G, dim3((unsigned)items, Hkv), stream, q, K, V, offsets_dev, idx, counts_dev, B, Hq, Hkv, part, ml);
+    if (mode == 0) e = launch_partial_G<0>(G, dim3((unsigned)items), stream, q, K, V, offs, idx, cnts, B, Hq, Hkv, part, ml);
+    else e = launch_partial_G<1>(G, dim3((unsigned)items, Hkv), stream, q, K, V, offs, idx, cnts, B, Hq, Hkv, part, ml);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_merge_kernel, dim3(B * Hq, kD / 16), dim3(1024), 0, stream, part, ml, counts_dev, B, Hq, out);
+    hipLaunchKernelGGL(decode_merge_kernel, dim3(B * Hq, kD / 16), dim3(1024), 0, stream, part, ml, cnts, B, Hq, out);
     return hipGetLastError();
 }
 
@@ -378,11 +380,16 @@ hipError_t launch_dense_decode(const uint16_t* q, const uint16_t* K, const uint1
     int64_t* lens = w.take<int64_t>((size_t)B + 1);
     float* part = w.take<float>((size_t)items * Hq * kD);
     float2* ml = w.take<float2>((size_t)items * Hq);
-    hipLaunchKernelGGL(lengths_kernel, dim3(1), dim3(256), 0, stream, offsets_dev, B, lens);
-    hipError_t e = launch_partial_G<2>(Hq / Hkv, dim3((unsigned)items), stream, q, K, V, offsets_dev, nullptr, lens,
+    const I64Arg offs = i64_arg(offsets_dev, offsets_host, (int64_t)B + 1);
+    // one sequence: its length is a launch argument; otherwise the lengths are computed on
+    // the device
+    const int64_t hl = offsets_host[B] - offsets_host[0];
+    const I64Arg lns = i64_arg(lens, B == 1 ? &hl : nullptr, B);
+    if (B != 1) hipLaunchKernelGGL(lengths_kernel, dim3(1), dim3(256), 0, stream, offs, B, lens);
+    hipError_t e = launch_partial_G<2>(Hq / Hkv, dim3((unsigned)items), stream, q, K, V, offs, nullptr, lns,
                                        B, Hq, Hkv, part, ml);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_merge_kernel, dim3(B * Hq, kD / 16), dim3(1024), 0, stream, part, ml, lens, B, Hq, out);
+    hipLaunchKernelGGL(decode_merge_kernel, dim3(B * Hq, kD / 16), dim3(1024), 0, stream, part, ml, lns, B, Hq, out);
     return hipGetLastError();
 }
 

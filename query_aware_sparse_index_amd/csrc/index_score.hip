@@ -80,7 +80,7 @@ constexpr int score_threads() {
 }
 constexpr int kTileLd = kScoreTB + 1;
 
-__device__ __forceinline__ bool find_item(const int64_t* __restrict__ offsets, int B, int64_t item, int tb, int& b,
+__device__ __forceinline__ bool find_item(const I64Arg& offsets, int B, int64_t item, int tb, int& b,
                                           int64_t& t0, int64_t& len) {
     int64_t acc = 0;
     for (int i = 0; i < B; ++i) {
@@ -166,7 +166,7 @@ __device__ __forceinline__ void quad_transpose_sum(float (&v)[G], int part) {
 template <int HKV, int G>
 __global__ __launch_bounds__(score_threads<HKV>()) void score_kernel(const float* __restrict__ qp,
                                                              const uint16_t* __restrict__ k_index,
-                                                             const int64_t* __restrict__ offsets, int B,
+                                                             I64Arg offsets, int B,
                                                              float* __restrict__ scores) {
     constexpr int NT = score_threads<HKV>();
     constexpr int Hq = HKV * G;
@@ -256,13 +256,13 @@ size_t score_workspace(int B, int Hq) {
 
 template <int HKV>
 static hipError_t launch_score_g(int G, dim3 grid, hipStream_t stream, const float* qp, const uint16_t* k_index,
-                                 const int64_t* offsets_dev, int B, float* scores) {
+                                 const I64Arg& offsets, int B, float* scores) {
     dim3 block(score_threads<HKV>());
     switch (G) {
-        case 1: hipLaunchKernelGGL((score_kernel<HKV, 1>), grid, block, 0, stream, qp, k_index, offsets_dev, B, scores); break;
-        case 2: hipLaunchKernelGGL((score_kernel<HKV, 2>), grid, block, 0, stream, qp, k_index, offsets_dev, B, scores); break;
-        case 4: hipLaunchKernelGGL((score_kernel<HKV, 4>), grid, block, 0, stream, qp, k_index, offsets_dev, B, scores); break;
-        case 8: hipLaunchKernelGGL((score_kernel<HKV, 8>), grid, block, 0, stream, qp, k_index, offsets_dev, B, scores); break;
+        case 1: hipLaunchKernelGGL((score_kernel<HKV, 1>), grid, block, 0, stream, qp, k_index, offsets, B, scores); break;
+        case 2: hipLaunchKernelGGL((score_kernel<HKV, 2>), grid, block, 0, stream, qp, k_index, offsets, B, scores); break;
+        case 4: hipLaunchKernelGGL((score_kernel<HKV, 4>), grid, block, 0, stream, qp, k_index, offsets, B, scores); break;
+        case 8: hipLaunchKernelGGL((score_kernel<HKV, 8>), grid, block, 0, stream, qp, k_index, offsets, B, scores); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -278,11 +278,12 @@ hipError_t launch_score(const uint16_t* q, const float* P, const uint16_t* k_ind
     if (items == 0) return hipGetLastError();
     const dim3 grid((unsigned)items);
     const int G = Hq / Hkv;
+    const I64Arg offs = i64_arg(offsets_dev, offsets_host, (int64_t)B + 1);
     switch (Hkv) {
-        case 1: return launch_score_g<1>(G, grid, stream, qp, k_index, offsets_dev, B, scores);
-        case 2: return launch_score_g<2>(G, grid, stream, qp, k_index, offsets_dev, B, scores);
-        case 4: return launch_score_g<4>(G, grid, stream, qp, k_index, offsets_dev, B, scores);
-        case 8: return launch_score_g<8>(G, grid, stream, qp, k_index, offsets_dev, B, scores);
+        case 1: return launch_score_g<1>(G, grid, stream, qp, k_index, offs, B, scores);
+        case 2: return launch_score_g<2>(G, grid, stream, qp, k_index, offs, B, scores);
+        case 4: return launch_score_g<4>(G, grid, stream, qp, k_index, offs, B, scores);
+        case 8: return launch_score_g<8>(G, grid, stream, qp, k_index, offs, B, scores);
         default: return hipErrorInvalidValue;
     }
 }

@@ -7,6 +7,27 @@
 
 namespace qasi {
 
+// An int64 array (sequence offsets, list lengths) as a kernel argument.  For a single
+// sequence (one length, or the offsets {0, n}) the values travel in the launch arguments, so
+// that a kernel knows its bounds without a dependent global load at its start; otherwise the
+// kernels read the device copy.  The C ABI requires the host and device copies to agree.
+struct I64Arg {
+    const int64_t* dev;
+    int32_t one;      // 1: a single sequence, values in h0 (and h1)
+    int64_t h0, h1;
+    __host__ __device__ __forceinline__ int64_t operator[](int64_t i) const {
+        return one ? (i == 0 ? h0 : h1) : dev[i];
+    }
+};
+inline I64Arg i64_arg(const int64_t* dev, const int64_t* host, int64_t count) {
+    I64Arg a;
+    a.dev = dev;
+    a.one = (host && (count == 1 || count == 2)) ? 1 : 0;
+    a.h0 = a.one ? host[0] : 0;
+    a.h1 = (a.one && count == 2) ? host[1] : 0;
+    return a;
+}
+
 // ---- index and score
 hipError_t launch_index_append(const uint16_t* k_new, const float* P, uint16_t* k_index, int64_t pos, int64_t T,
                                int Hkv, hipStream_t stream);

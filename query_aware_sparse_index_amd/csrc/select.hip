@@ -210,7 +210,7 @@ __device__ void sample_bracket(const float* __restrict__ row, const OsInst& oi, 
 constexpr int kPreWords = kDigitBins / 2 + 1;   // 16-bit prefix values 0 .. kDigitBins, two per word
 constexpr int kDpWords = kPreWords + kDigitBins / 2 + 1;   // per slice: prefixes, then counts (two per word)
 __global__ __launch_bounds__(kColThreads) void th_collect_kernel(const float* __restrict__ scores,
-                                                                const int64_t* __restrict__ offsets, int Hq,
+                                                                I64Arg offsets, int Hq,
                                                                 DevCfg cfg, int SL, int64_t S,
                                                                 int64_t* __restrict__ state,
                                                                 uint32_t* __restrict__ cand,
@@ -361,7 +361,7 @@ __device__ uint32_t radix_rank(Visit visit, int nbits, int64_t rank, uint32_t* h
 
 // One block per instance: theta key, #keys above it (state) and theta_out.
 __global__ __launch_bounds__(kThThreads) void th_final_kernel(const float* __restrict__ scores,
-                                                             const int64_t* __restrict__ offsets, int Hq,
+                                                             I64Arg offsets, int Hq,
                                                              DevCfg cfg, int SL, int64_t S,
                                                              const uint32_t* __restrict__ cand,
                                                              const uint32_t* __restrict__ cnt,
@@ -570,7 +570,7 @@ __global__ __launch_bounds__(kThThreads) void th_final_kernel(const float* __res
 // Work item -> (sequence b, its first item, its item count, first token, length) for chunks of CH
 // tokens numbered sequence by sequence.
 template <int CH = kChunk>
-__device__ __forceinline__ bool find_chunk(const int64_t* __restrict__ offsets, int B, int64_t item, int& b,
+__device__ __forceinline__ bool find_chunk(const I64Arg& offsets, int B, int64_t item, int& b,
                                            int64_t& first, int64_t& nch, int64_t& t0, int64_t& len) {
     int64_t acc = 0;
     for (int i = 0; i < B; ++i) {
@@ -589,7 +589,7 @@ __device__ __forceinline__ bool find_chunk(const int64_t* __restrict__ offsets, 
     return false;
 }
 
-__device__ __forceinline__ int64_t kpre_of(const int64_t* __restrict__ offsets, int b, const DevCfg& c) {
+__device__ __forceinline__ int64_t kpre_of(const I64Arg& offsets, int b, const DevCfg& c) {
     int64_t k = 0;
     for (int i = 0; i < b; ++i) k += budget_k(offsets[i + 1] - offsets[i], c.bnum, c.bden, c.sink, c.local);
     return k;
@@ -601,7 +601,7 @@ __device__ __forceinline__ int64_t kpre_of(const int64_t* __restrict__ offsets, 
 // Vote >= v_min, else 0 (the listing's -1); forced tokens get 255.  Each block also counts
 // the keys of its non-forced tokens (one histogram per block).
 __global__ __launch_bounds__(kChunk) void vote_kernel(const float* __restrict__ scores,
-                                                     const int64_t* __restrict__ offsets, int B, int Hq,
+                                                     I64Arg offsets, int B, int Hq,
                                                      DevCfg cfg, int64_t S, const int64_t* __restrict__ state,
                                                      uint8_t* __restrict__ votes, uint8_t* __restrict__ keys,
                                                      uint32_t* __restrict__ hist) {
@@ -662,7 +662,7 @@ __global__ __launch_bounds__(kChunk) void vote_kernel(const float* __restrict__ 
 // to v* in position order, written ascending.
 constexpr int kScanTile = 256;
 
-__global__ __launch_bounds__(kChunk) void compact_vote_kernel(const int64_t* __restrict__ offsets, int B,
+__global__ __launch_bounds__(kChunk) void compact_vote_kernel(I64Arg offsets, int B,
                                                              DevCfg cfg, const uint8_t* __restrict__ keys,
                                                              const uint32_t* __restrict__ hist,
                                                              int32_t* __restrict__ idx_out,
@@ -777,7 +777,7 @@ constexpr int kPhHeads = 32;   // heads handled per pass of a block (Hq <= 64 ta
 constexpr int kPhChunk = 256;  // tokens per per-head compaction block
 
 __global__ __launch_bounds__(kPhChunk) void ph_count_kernel(const float* __restrict__ scores,
-                                                         const int64_t* __restrict__ offsets, int B, int Hq,
+                                                         I64Arg offsets, int B, int Hq,
                                                          DevCfg cfg, int64_t S, const int64_t* __restrict__ state,
                                                          int64_t nitems, uint32_t* __restrict__ cnt) {
     constexpr int NW = kPhChunk / 64;
@@ -829,7 +829,7 @@ __global__ __launch_bounds__(kPhChunk) void ph_count_kernel(const float* __restr
 
 // One wave per (sequence b, head h), four waves per block: exclusive prefix over the chunks of
 // b of the (above, equal) counts, in place.
-__global__ __launch_bounds__(256) void ph_scan_kernel(const int64_t* __restrict__ offsets, int B, int Hq,
+__global__ __launch_bounds__(256) void ph_scan_kernel(I64Arg offsets, int B, int Hq,
                                                      int64_t nitems, uint32_t* __restrict__ cnt) {
     const int lane = threadIdx.x & 63;
     const int64_t wv = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -873,7 +873,7 @@ __global__ __launch_bounds__(256) void ph_scan_kernel(const int64_t* __restrict_
 }
 
 __global__ __launch_bounds__(kPhChunk) void ph_compact_kernel(const float* __restrict__ scores,
-                                                           const int64_t* __restrict__ offsets, int B, int Hq,
+                                                           I64Arg offsets, int B, int Hq,
                                                            DevCfg cfg, int64_t S, const int64_t* __restrict__ state,
                                                            int64_t nitems, const uint32_t* __restrict__ pre,
                                                            int32_t* __restrict__ idx_out,
@@ -1045,33 +1045,30 @@ hipError_t launch_select(const float* scores, int64_t S, const int64_t* offsets_
     if (L.bytes > ws_bytes || L.SL > kMaxSL) return hipErrorInvalidValue;
     DevCfg d = dev_cfg(c);
     const unsigned inst = (unsigned)(B * Hq);
-    hipLaunchKernelGGL(th_collect_kernel, dim3(L.SL, inst), dim3(kColThreads), 0, stream, scores, offsets_dev, Hq, d,
+    const I64Arg offs = i64_arg(offsets_dev, offsets_host, (int64_t)B + 1);
+    hipLaunchKernelGGL(th_collect_kernel, dim3(L.SL, inst), dim3(kColThreads), 0, stream, scores, offs, Hq, d,
                        L.SL, S, L.state, L.cand, L.cnt, L.dhist);
-    hipLaunchKernelGGL(th_final_kernel, dim3(inst), dim3(kThThreads), 0, stream, scores, offsets_dev, Hq, d, L.SL, S,
+    hipLaunchKernelGGL(th_final_kernel, dim3(inst), dim3(kThThreads), 0, stream, scores, offs, Hq, d, L.SL, S,
                        L.cand, L.cnt, L.dhist, L.state, c.mode == 0 ? theta_out : nullptr);
     if (L.nitems == 0) return hipGetLastError();
     if (c.mode == 0) {
         uint8_t* votes = votes_out ? votes_out : L.votes;
-        hipLaunchKernelGGL(vote_kernel, dim3((unsigned)L.nitems), dim3(kChunk), 0, stream, scores, offsets_dev,
+        hipLaunchKernelGGL(vote_kernel, dim3((unsigned)L.nitems), dim3(kChunk), 0, stream, scores, offs,
                            B, Hq, d, S, L.state, votes, L.keys, L.hist);
-        hipLaunchKernelGGL(compact_vote_kernel, dim3((unsigned)L.nitems), dim3(kChunk), 0, stream, offsets_dev,
+        hipLaunchKernelGGL(compact_vote_kernel, dim3((unsigned)L.nitems), dim3(kChunk), 0, stream, offs,
                            B, d, L.keys, L.hist, idx_out, count_out);
     } else {
-        hipLaunchKernelGGL(ph_count_kernel, dim3((unsigned)L.ph_items), dim3(kPhChunk), 0, stream, scores, offsets_dev,
+        hipLaunchKernelGGL(ph_count_kernel, dim3((unsigned)L.ph_items), dim3(kPhChunk), 0, stream, scores, offs,
                            B, Hq, d, S, L.state, L.ph_items, L.phcnt);
-        hipLaunchKernelGGL(ph_scan_kernel, dim3((unsigned)((B * Hq + 3) / 4)), dim3(256), 0, stream, offsets_dev, B,
+        hipLaunchKernelGGL(ph_scan_kernel, dim3((unsigned)((B * Hq + 3) / 4)), dim3(256), 0, stream, offs, B,
                            Hq, L.ph_items, L.phcnt);
         hipLaunchKernelGGL(ph_compact_kernel, dim3((unsigned)L.ph_items), dim3(kPhChunk), 0, stream, scores,
-                           offsets_dev, B, Hq, d, S, L.state, L.ph_items, L.phcnt, idx_out, count_out);
+                           offs, B, Hq, d, S, L.state, L.ph_items, L.phcnt, idx_out, count_out);
     }
     return hipGetLastError();
 }
 
 // ------------------------------------------------------------- row-wise top-k
-__global__ void set_offsets_kernel(int64_t* o, int64_t n) {
-    if (threadIdx.x == 0) { o[0] = 0; o[1] = n; }
-}
-
 static SelectConfig rows_cfg(int64_t n, int64_t k) {
     SelectConfig c;
     c.mode = 1;
@@ -1089,7 +1086,6 @@ size_t rows_topk_workspace(int rows, int64_t n, int64_t k) {
     int64_t oh[2] = {0, n};
     WsCarver w(nullptr);
     w.take<int64_t>(4);
-    w.take<int64_t>(4);
     w.take<char>(select_workspace(oh, 1, rows, rows_cfg(n, k)));
     return w.size();
 }
@@ -1100,12 +1096,11 @@ hipError_t launch_rows_topk(const float* vals, int64_t stride, int rows, int64_t
     int64_t oh[2] = {0, n};
     SelectConfig c = rows_cfg(n, k);
     WsCarver w(ws);
-    int64_t* od = w.take<int64_t>(4);
     int64_t* cnt = w.take<int64_t>(4);
     size_t sb = select_workspace(oh, 1, rows, c);
     void* sws = w.take<char>(sb);
-    hipLaunchKernelGGL(set_offsets_kernel, dim3(1), dim3(64), 0, stream, od, n);
-    return launch_select(vals, stride, od, oh, 1, rows, c, idx_out, cnt, nullptr, nullptr, sws, sb, stream);
+    // one sequence {0, n}: the offsets travel as launch arguments, no device copy is read
+    return launch_select(vals, stride, nullptr, oh, 1, rows, c, idx_out, cnt, nullptr, nullptr, sws, sb, stream);
 }
 
 }  // namespace qasi
