@@ -22,6 +22,7 @@
 namespace qasi {
 
 constexpr int kDecCH = 64;            // list entries per chunk
+static_assert(kDecCH % 16 == 0, "the softmax phase gives each head slot one 16-lane row");
 constexpr float kLog2eOverSqrtD = 1.4426950408889634f / 11.313708498984761f;
 __device__ __forceinline__ bool find_list_chunk(const I64Arg& counts, int B, int64_t item, int& b,
                                                 int64_t& first, int64_t& nch, int64_t& j0, int64_t& len,
@@ -142,29 +143,31 @@ __global__ __launch_bounds__(512) void decode_partial_kernel(const uint16_t* __r
     }
     __syncthreads();
 
-    // phase 2: per-head max, exponentials and sums
+    // phase 2: per-head max, exponentials and sums; one 16-lane row per head slot, kDecCH / 16
+    // entries per lane, row reductions through DPP
     const int nslots = (MODE == 1) ? G : Hq;
-    constexpr int EPL = (kDecCH + 63) / 64;   // entries per lane
-    for (int hs = wid; hs < nslots; hs += NW) {
+    constexpr int EPL = kDecCH / 16;   // entries per lane
+    for (int hs = threadIdx.x >> 4; hs < nslots; hs += NW * 4) {
+        const int l16 = threadIdx.x & 15;
         float z[EPL];
         float mx = -INFINITY;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
-            const int i = lane + 64 * e;
+            const int i = l16 + 16 * e;
             z[e] = i < len ? zb[hs * kDecCH + i] : -INFINITY;
             mx = fmaxf(mx, z[e]);
         }
-        const float m = wave_max(mx);
+        const float m = max_row16(mx);
         float l = 0.f;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) {
-            const int i = lane + 64 * e;
+            const int i = l16 + 16 * e;
             const float ev = i < len ? fast_exp2(z[e] - m) : 0.f;
-            if (i < kDecCH) zb[hs * kDecCH + i] = ev;
+            zb[hs * kDecCH + i] = ev;
             l += ev;
         }
-        l = wave_sum(l);
-        if (lane == 0) { stat[hs * 2] = m; stat[hs * 2 + 1] = l; }
+        l = sum_row16(l);
+        if (l16 == 0) { stat[hs * 2] = m; stat[hs * 2 + 1] = l; }
     }
     __syncthreads();
 

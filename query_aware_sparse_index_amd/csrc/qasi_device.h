@@ -122,6 +122,15 @@ __device__ __forceinline__ float sum_row16(float v) {
     return v;
 }
 
+// Maximum over each 16-lane row (result in every lane of the row).
+__device__ __forceinline__ float max_row16(float v) {
+    v = fmaxf(v, dpp_quad_xor1(v));
+    v = fmaxf(v, dpp_quad_xor2(v));
+    v = fmaxf(v, dpp_row_half_mirror(v));
+    v = fmaxf(v, dpp_row_mirror(v));
+    return v;
+}
+
 // Wave-wide reductions (64 lanes) through shuffles.
 __device__ __forceinline__ float wave_max(float v) {
     for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
@@ -158,6 +167,42 @@ __device__ __forceinline__ int block_inclusive_scan(int v, int* tmp, int* total)
     }
     __syncthreads();
     *total = tot;
+    return x + base;
+}
+
+// Block-wide: the totals of a and b and the inclusive scan of c (returned, total in *tc), with
+// one exchange through LDS.  tmp holds 3 x NT / 64 ints.  Every thread must call it.
+template <int NT>
+__device__ __forceinline__ int block_inclusive_scan3(int a, int b, int c, int (*tmp)[NT / 64], int* ta, int* tb,
+                                                     int* tc) {
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    int x = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+        a += __shfl_xor(a, o, 64);
+        b += __shfl_xor(b, o, 64);
+    }
+    if (lane == 63) {
+        tmp[0][wid] = a;
+        tmp[1][wid] = b;
+        tmp[2][wid] = x;
+    }
+    __syncthreads();
+    int sa = 0, sb = 0, base = 0, sc = 0;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) {
+        sa += tmp[0][w];
+        sb += tmp[1][w];
+        const int v = tmp[2][w];
+        if (w < wid) base += v;
+        sc += v;
+    }
+    __syncthreads();
+    *ta = sa;
+    *tb = sb;
+    *tc = sc;
     return x + base;
 }
 

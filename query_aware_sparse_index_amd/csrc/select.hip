@@ -372,75 +372,82 @@ __global__ __launch_bounds__(kThThreads) void th_final_kernel(const float* __res
     __shared__ int segpre[kMaxSL + 1], sega[kMaxSL];
     __shared__ uint32_t hist[kDigitBins];
     __shared__ int tmp[kThThreads / 64];
+    __shared__ int tmp3[3][kThThreads / 64];
     __shared__ int64_t sh[4];
     __shared__ uint32_t nd;
     const int inst = blockIdx.x;
     int64_t* st = state + (int64_t)inst * 8;
     const int b = inst / Hq, h = inst % Hq;
-    const int64_t off = offsets[b];
-    const OsInst oi = os_instance(offsets[b + 1] - off, cfg);
-    if (oi.flag != kFlagActive) {
-        if (theta_out && threadIdx.x == 0) theta_out[inst] = 0.f;
-        return;
-    }
-    const int64_t m = oi.end - oi.beg;
-    const uint32_t klo = (uint32_t)st[kStLo], khi = (uint32_t)st[kStHi];
-    const int nsl = (int)((m + kSlice - 1) / kSlice);
     const int t = threadIdx.x;
-    // keys below the bracket and candidates: two slices per thread
+    // every global load of the prologue is issued before any is used (one memory round trip):
+    // the sequence bounds, the bracket, the slice counts of slices 2t and 2t+1 and the counts of
+    // digit pair (2t, 2t+1) in every slice (slices past the row's end hold zeros)
+    const int64_t off = offsets[b];
+    const int64_t nrow = offsets[b + 1] - off;
+    const uint32_t klo = (uint32_t)st[kStLo], khi = (uint32_t)st[kStHi];
     const uint32_t* cs = cnt + (size_t)inst * SL * 2;
-    int lsum = 0, csum = 0;
+    uint2 cp[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         const int sl = 2 * t + u;
-        if (sl < nsl) { lsum += (int)cs[2 * sl]; csum += (int)cs[2 * sl + 1]; }
+        cp[u] = reinterpret_cast<const uint2*>(cs)[sl < SL ? sl : SL - 1];
     }
-    // candidates per digit pair (2t, 2t+1), summed over the slices from their prefixes
     uint32_t dlo = 0, dhi = 0;
     {
-        // digit pair (2t, 2t+1) counts summed over the slices, 32 slices' words in flight
         constexpr int SLR = 32;
         const uint32_t* dc = dpre + (size_t)inst * SL * kDpWords + kPreWords + t;
-        for (int sl0 = 0; sl0 < nsl; sl0 += SLR) {
+        for (int sl0 = 0; sl0 < SL; sl0 += SLR) {
             uint32_t w[SLR];
 #pragma unroll
-            for (int u = 0; u < SLR; ++u) w[u] = dc[(size_t)(sl0 + u < nsl ? sl0 + u : nsl - 1) * kDpWords];
+            for (int u = 0; u < SLR; ++u) w[u] = dc[(size_t)(sl0 + u < SL ? sl0 + u : SL - 1) * kDpWords];
 #pragma unroll
             for (int u = 0; u < SLR; ++u) {
-                const uint32_t x = sl0 + u < nsl ? w[u] : 0u;
+                const uint32_t x = sl0 + u < SL ? w[u] : 0u;
                 dlo += x & 0xffffu;
                 dhi += x >> 16;
             }
         }
     }
-    int nmid, nlo;
-    block_inclusive_scan<kThThreads>(csum, tmp, &nmid);
-    block_inclusive_scan<kThThreads>(lsum, tmp, &nlo);
+    const OsInst oi = os_instance(nrow, cfg);
+    if (oi.flag != kFlagActive) {
+        if (theta_out && t == 0) theta_out[inst] = 0.f;
+        return;
+    }
+    const int64_t m = oi.end - oi.beg;
+    const int nsl = (int)((m + kSlice - 1) / kSlice);
+    int lsum = 0, csum = 0;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+        if (2 * t + u < SL) { lsum += (int)cp[u].x; csum += (int)cp[u].y; }
+    // one block scan gives the keys below the bracket (nlo), the candidates (nmid) and the
+    // inclusive digit-count prefix; from them, the answer's digit
+    const int cd = (int)(dlo + dhi);
+    int nlo, nmid, tot;
+    const int inc = block_inclusive_scan3<kThThreads>(lsum, csum, cd, tmp3, &nlo, &nmid, &tot);
     if (t == 0) nd = 0;
     int64_t gt = 0;
     uint32_t key = 0;
     const int64_t r = oi.rank;
     bool whole_row = !(nlo < r && r <= (int64_t)nlo + nmid);
+    const int dsh = top_shift(khi - klo);
+    if (!whole_row && klo != khi) {
+        const int64_t rr0 = r - nlo;
+        if (inc - cd < rr0 && rr0 <= inc) {
+            const int below = inc - cd;
+            const bool first = rr0 <= below + (int)dlo;
+            sh[0] = first ? 2 * t : 2 * t + 1;
+            sh[1] = first ? below : below + (int)dlo;
+            sh[2] = tot - (first ? below + (int)dlo : inc);
+            sh[3] = first ? dlo : dhi;
+        }
+    }
+    __syncthreads();
     if (!whole_row) {
         gt = m - nlo - nmid;                       // keys above hi
         int64_t rr = r - nlo;
         if (klo == khi) {
             key = klo;
         } else {
-            // the answer's top digit from the summed histograms
-            const int dsh = top_shift(khi - klo);
-            const int cd = (int)(dlo + dhi);
-            int tot;
-            const int inc = block_inclusive_scan<kThThreads>(cd, tmp, &tot);
-            if (inc - cd < rr && rr <= inc) {
-                const int below = inc - cd;
-                const bool first = rr <= below + (int)dlo;
-                sh[0] = first ? 2 * t : 2 * t + 1;
-                sh[1] = first ? below : below + (int)dlo;
-                sh[2] = tot - (first ? below + (int)dlo : inc);
-                sh[3] = first ? dlo : dhi;
-            }
-            __syncthreads();
             const uint32_t D = (uint32_t)sh[0];
             rr -= sh[1];
             gt += sh[2];
