@@ -5,38 +5,46 @@
 // tokens; the "output merge" of the five-step integration is the log-sum-exp merge of the
 // partial softmax results of disjoint chunks of the list.
 //
-// Work item = (sequence b, chunk of kDecCH list entries) [vote / dense] or (b, KV head g,
-// chunk) [per-head].  Items are dispatched in list order, so the chip sweeps the sorted lists
-// front to back.  A block has 8 waves (vote / dense) or G waves (per-head).  In vote mode a
-// wave is tied to a KV head g and serves the G query heads of g, so each gathered K/V row is
-// read once for the whole GQA group.  A wave is 4 rows of 16 lanes; a row takes one entry at
-// a time and lane p holds dims [8p, 8p+8) (one 16-byte load of K or V).
-//   phase 1: z = q . k * log2(e)/sqrt(128) for every entry of the chunk (row butterfly)
-//   phase 2: per-head chunk max m, p = exp2(z - m), l = sum p (LDS)
-//   phase 3: acc += p * v
-// The partial (m, l, acc[128]) of every chunk and head goes to the workspace; the merge kernel
-// combines the chunks of a sequence: out = sum_c acc_c 2^(m_c - M) / sum_c l_c 2^(m_c - M).
+// Work item (block) = (sequence b, range of EB list entries, KV head g) [vote / dense] or
+// (b, range, query head h) [per-head]; blocks of one range are adjacent, so the chip sweeps the
+// sorted lists front to back.  EB is chosen on the host so that the grid is about one round of
+// resident blocks.  A block has 4 waves; wave w takes the EW = EB / 4 entries
+// [w EW, (w+1) EW) of the range and serves the GH query heads that read KV head g (all G heads
+// of g in vote / dense mode, one head in per-head mode), so each gathered K/V row is read once
+// for the whole GQA group.  A wave works through its entries in sub-batches of 16: a wave is 4
+// rows of 16 lanes, row r takes entries 4r .. 4r+3 of the sub-batch and lane p holds dims
+// [8p, 8p+8) (one 16-byte load of K and one of V per entry).  The K and V rows of sub-batch
+// s+1 are requested before sub-batch s is computed, so every wave keeps its gathers in flight:
+//   z  = q . k * log2(e)/sqrt(128): bf16 pair dot products (exact products, fp32 sums), then a
+//        transposed butterfly over the 16 lanes of the row (DPP);
+//   online softmax per head over the sub-batches: m, l and acc = sum 2^(z - m) v, rescaled
+//        when m grows; the row sums of the accumulators use the gfx950 row swaps;
+//   the 4 waves' (m, l, acc) merge in LDS into the block's partial (M, L, A[128]) per head.
+// The merge kernel combines the ranges of a sequence: out = sum_c A_c 2^(M_c - M) /
+// sum_c L_c 2^(M_c - M).
 #include "qasi_device.h"
 #include "qasi_internal.h"
 
 namespace qasi {
 
-constexpr int kDecCH = 64;            // list entries per chunk
-static_assert(kDecCH % 16 == 0, "the softmax phase gives each head slot one 16-lane row");
+constexpr int kDecWaves = 4;                       // waves per block
+constexpr int kDecSub = 16;                        // entries per sub-batch of a wave
+constexpr int kDecMaxEW = 256;                     // entries per wave at most
 constexpr float kLog2eOverSqrtD = 1.4426950408889634f / 11.313708498984761f;
-__device__ __forceinline__ bool find_list_chunk(const I64Arg& counts, int B, int64_t item, int& b,
-                                                int64_t& first, int64_t& nch, int64_t& j0, int64_t& len,
-                                                int64_t& kpre) {
+
+// query heads served by a wave
+__host__ __device__ constexpr int dec_gh(int G, int mode) { return mode == 1 ? 1 : G; }
+
+__device__ __forceinline__ bool find_list_chunk(const I64Arg& counts, int B, int64_t item, int EB, int& b,
+                                                int64_t& j0, int64_t& len, int64_t& kpre) {
     int64_t acc = 0, kp = 0;
     for (int i = 0; i < B; ++i) {
-        int64_t n = counts[i];
-        int64_t nb = (n + kDecCH - 1) / kDecCH;
+        const int64_t n = counts[i];
+        const int64_t nb = (n + EB - 1) / EB;
         if (item < acc + nb) {
             b = i;
-            first = acc;
-            nch = nb;
-            j0 = (item - acc) * kDecCH;
-            len = n - j0 < kDecCH ? n - j0 : kDecCH;
+            j0 = (item - acc) * EB;
+            len = n - j0 < EB ? n - j0 : EB;
             kpre = kp;
             return true;
         }
@@ -46,285 +54,413 @@ __device__ __forceinline__ bool find_list_chunk(const I64Arg& counts, int B, int
     return false;
 }
 
-// MODE 0: shared list per sequence (vote); MODE 1: list per query head; MODE 2: dense
-// (the list is implicit: entry j is token j, counts are the sequence lengths).
-template <int G, int MODE>
-__global__ __launch_bounds__(512) void decode_partial_kernel(const uint16_t* __restrict__ q,
-                                                            const uint16_t* __restrict__ K,
-                                                            const uint16_t* __restrict__ V,
-                                                            I64Arg offsets,
-                                                            const int32_t* __restrict__ idx,
-                                                            I64Arg counts, int B, int Hq,
-                                                            int Hkv, float* __restrict__ part_acc,
-                                                            float2* __restrict__ part_ml) {
-    constexpr int GH = (MODE == 1) ? 1 : G;          // query heads per wave
-    constexpr int NW = (MODE == 1) ? G : 8;          // waves per block
-    __shared__ float zb[((MODE == 1) ? G : 64) * kDecCH];   // [head slot][entry]
-    __shared__ float red[NW * GH * kD];
-    __shared__ float stat[((MODE == 1) ? G : 64) * 2];
-    __shared__ int32_t tok[(MODE == 1) ? G * kDecCH : kDecCH];
+// bf16 pair dot product with fp32 accumulation: a.lo*b.lo + a.hi*b.hi + c
+typedef __bf16 __attribute__((ext_vector_type(2))) bf16x2_t;
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
+                                           false);
+}
 
-    int b;
-    int64_t first, nch, j0, len, kpre;
-    if (!find_list_chunk(counts, B, blockIdx.x, b, first, nch, j0, len, kpre)) return;
-    const int64_t off = offsets[b];
-    const int32_t nmax = (int32_t)(offsets[b + 1] - off - 1);   // list entries are clamped to [0, n_b)
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    const int row = lane >> 4, p = lane & 15;
-
-    // wave role
-    int g, sub, nsub, hbase;
-    if (MODE == 1) { g = blockIdx.y; sub = 0; nsub = 1; hbase = g * G + wid; }
-    else { g = wid % Hkv; sub = wid / Hkv; nsub = 8 / Hkv; hbase = g * G; }
-    const bool wave_on = (MODE == 1) ? true : (wid < Hkv * nsub);
-    const int hslot0 = (MODE == 1) ? wid : hbase;   // first head slot of this wave in zb/stat
-
-    // token ids of the chunk
-    if (MODE == 1) {
-        for (int i = threadIdx.x; i < G * kDecCH; i += NW * 64) {
-            int w = i / kDecCH, j = i % kDecCH;
-            int h = g * G + w;
-            int32_t t = (j < len) ? idx[Hq * kpre + (int64_t)h * counts[b] + j0 + j] : 0;
-            tok[i] = t < 0 ? 0 : (t > nmax ? nmax : t);
-        }
-    } else {
-        for (int i = threadIdx.x; i < kDecCH; i += NW * 64) {
-            int32_t t = (i < len) ? ((MODE == 2) ? (int32_t)(j0 + i) : idx[kpre + j0 + i]) : 0;
-            tok[i] = t < 0 ? 0 : (t > nmax ? nmax : t);
+// One step of a transposed butterfly inside a 16-lane row: the lane keeps the half of its N
+// values chosen by its lane bit (`upper`) and adds the partner's copy of that half; the
+// partner (a DPP lane permutation that flips that bit) keeps the other half.
+template <int N, class F>
+__device__ __forceinline__ void tstep(const float (&in)[N], float (&out)[N / 2], bool upper, F partner) {
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {
+        const float lo = in[i], hi = in[N / 2 + i];
+        out[i] = (upper ? hi : lo) + partner(upper ? lo : hi);
+    }
+}
+// Sum over the 16 lanes of a row of NV per-lane values.  NV >= 16: lane p ends with the NV/16
+// complete sums of indices p*NV/16 + s; NV < 16: lane p ends with the sum of index p / (16/NV)
+// (DUP = 16/NV neighbouring lanes hold the same sum).
+template <int NV>
+struct RowSum {
+    static constexpr int FV = NV >= 16 ? NV / 16 : 1;
+    static constexpr int DUP = NV >= 16 ? 1 : 16 / NV;
+    __device__ static __forceinline__ void run(float (&v)[NV], float (&o)[FV], int p) {
+        if constexpr (NV == 32) {
+            float a[16], b[8], c[4];
+            tstep<32>(v, a, p & 8, dpp_row_mirror);
+            tstep<16>(a, b, p & 4, dpp_row_half_mirror);
+            tstep<8>(b, c, p & 2, dpp_quad_xor2);
+            tstep<4>(c, o, p & 1, dpp_quad_xor1);
+        } else if constexpr (NV == 16) {
+            float a[8], b[4], c[2];
+            tstep<16>(v, a, p & 8, dpp_row_mirror);
+            tstep<8>(a, b, p & 4, dpp_row_half_mirror);
+            tstep<4>(b, c, p & 2, dpp_quad_xor2);
+            tstep<2>(c, o, p & 1, dpp_quad_xor1);
+        } else if constexpr (NV == 8) {
+            float a[4], b[2], c[1];
+            tstep<8>(v, a, p & 8, dpp_row_mirror);
+            tstep<4>(a, b, p & 4, dpp_row_half_mirror);
+            tstep<2>(b, c, p & 2, dpp_quad_xor2);
+            o[0] = c[0] + dpp_quad_xor1(c[0]);
+        } else {
+            static_assert(NV == 4, "4, 8, 16 or 32 values per lane");
+            float a[2], b[1];
+            tstep<4>(v, a, p & 8, dpp_row_mirror);
+            tstep<2>(a, b, p & 4, dpp_row_half_mirror);
+            const float c = b[0] + dpp_quad_xor2(b[0]);
+            o[0] = c + dpp_quad_xor1(c);
         }
     }
-
-    // queries: lane p holds dims [8p, 8p+8) of its heads, scaled into the log2 domain
-    float qr[GH][8];
+};
+// Reduction over the lanes of a row that hold one head's values (steps S0 .. S1-1 of the
+// partners xor1, xor2, half-mirror, mirror; the steps below S0 would combine duplicate lanes),
+// then over the 4 rows with the gfx950 row swaps.
+template <bool MAX>
+__device__ __forceinline__ float op2(float a, float b) { return MAX ? fmaxf(a, b) : a + b; }
+template <bool MAX, int S0, int S1>
+__device__ __forceinline__ float head_reduce(float x) {
+    if constexpr (S0 <= 0 && S1 > 0) x = op2<MAX>(x, dpp_quad_xor1(x));
+    if constexpr (S0 <= 1 && S1 > 1) x = op2<MAX>(x, dpp_quad_xor2(x));
+    if constexpr (S0 <= 2 && S1 > 2) x = op2<MAX>(x, dpp_row_half_mirror(x));
+    if constexpr (S0 <= 3 && S1 > 3) x = op2<MAX>(x, dpp_row_mirror(x));
+    auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = op2<MAX>(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
+    auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return op2<MAX>(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+}
+__host__ __device__ constexpr int ilog2c(int x) { return x <= 1 ? 0 : 1 + ilog2c(x / 2); }
+// Sum over the 4 rows of NA per-lane values, transposed: row r ends with the sums of indices
+// r*NA/4 + j, j < NA/4 (one permlane32 swap and one permlane16 swap per value pair).
+template <int NA>
+__device__ __forceinline__ void rows_tsum(const float (&v)[NA], float (&o)[NA / 4]) {
+    float w[NA / 2];
 #pragma unroll
-    for (int hh = 0; hh < GH; ++hh) {
-        const uint16_t* qh = q + ((int64_t)b * Hq + hbase + hh) * kD + p * 8;
-        uint4 w = *reinterpret_cast<const uint4*>(qh);
-        qr[hh][0] = bf16_lo(w.x) * kLog2eOverSqrtD; qr[hh][1] = bf16_hi(w.x) * kLog2eOverSqrtD;
-        qr[hh][2] = bf16_lo(w.y) * kLog2eOverSqrtD; qr[hh][3] = bf16_hi(w.y) * kLog2eOverSqrtD;
-        qr[hh][4] = bf16_lo(w.z) * kLog2eOverSqrtD; qr[hh][5] = bf16_hi(w.z) * kLog2eOverSqrtD;
-        qr[hh][6] = bf16_lo(w.w) * kLog2eOverSqrtD; qr[hh][7] = bf16_hi(w.w) * kLog2eOverSqrtD;
+    for (int j = 0; j < NA / 2; ++j) {
+        auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[j]), __float_as_uint(v[j + NA / 2]), false, false);
+        w[j] = __uint_as_float(s[0]) + __uint_as_float(s[1]);
     }
-    __syncthreads();
-
-    // entries handled by this (wave, row): i = sub + nsub * (row + 4 k)
-    const int istep = 4 * nsub;
-    const int ibeg = sub + nsub * row;
-    constexpr int UNR = 4;
-
-    // phase 1: scores
-    if (wave_on) {
-        for (int i0 = ibeg; i0 < len; i0 += UNR * istep) {
-            uint4 kv[UNR];
 #pragma unroll
-            for (int u = 0; u < UNR; ++u) {
-                int i = i0 + u * istep;
-                kv[u] = make_uint4(0, 0, 0, 0);
-                if (i < len) {
-                    int t = (MODE == 1) ? tok[wid * kDecCH + i] : tok[i];
-                    kv[u] = *reinterpret_cast<const uint4*>(K + ((off + t) * Hkv + g) * kD + p * 8);
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < UNR; ++u) {
-                int i = i0 + u * istep;
-                float kf[8] = {bf16_lo(kv[u].x), bf16_hi(kv[u].x), bf16_lo(kv[u].y), bf16_hi(kv[u].y),
-                               bf16_lo(kv[u].z), bf16_hi(kv[u].z), bf16_lo(kv[u].w), bf16_hi(kv[u].w)};
-#pragma unroll
-                for (int hh = 0; hh < GH; ++hh) {
-                    float s = 0.f;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) s = fmaf(qr[hh][e], kf[e], s);
-                    s = sum_row16(s);
-                    if (p == hh && i < len) zb[(hslot0 + hh) * kDecCH + i] = s;
-                }
-            }
-        }
-    }
-    __syncthreads();
-
-    // phase 2: per-head max, exponentials and sums; one 16-lane row per head slot, kDecCH / 16
-    // entries per lane, row reductions through DPP
-    const int nslots = (MODE == 1) ? G : Hq;
-    constexpr int EPL = kDecCH / 16;   // entries per lane
-    for (int hs = threadIdx.x >> 4; hs < nslots; hs += NW * 4) {
-        const int l16 = threadIdx.x & 15;
-        float z[EPL];
-        float mx = -INFINITY;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-            const int i = l16 + 16 * e;
-            z[e] = i < len ? zb[hs * kDecCH + i] : -INFINITY;
-            mx = fmaxf(mx, z[e]);
-        }
-        const float m = max_row16(mx);
-        float l = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-            const int i = l16 + 16 * e;
-            const float ev = i < len ? fast_exp2(z[e] - m) : 0.f;
-            zb[hs * kDecCH + i] = ev;
-            l += ev;
-        }
-        l = sum_row16(l);
-        if (l16 == 0) { stat[hs * 2] = m; stat[hs * 2 + 1] = l; }
-    }
-    __syncthreads();
-
-    // phase 3: acc += p * v
-    float acc[GH][8];
-#pragma unroll
-    for (int hh = 0; hh < GH; ++hh)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[hh][e] = 0.f;
-    if (wave_on) {
-        for (int i0 = ibeg; i0 < len; i0 += UNR * istep) {
-            uint4 vv[UNR];
-#pragma unroll
-            for (int u = 0; u < UNR; ++u) {
-                int i = i0 + u * istep;
-                vv[u] = make_uint4(0, 0, 0, 0);
-                if (i < len) {
-                    int t = (MODE == 1) ? tok[wid * kDecCH + i] : tok[i];
-                    vv[u] = *reinterpret_cast<const uint4*>(V + ((off + t) * Hkv + g) * kD + p * 8);
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < UNR; ++u) {
-                int i = i0 + u * istep;
-                if (i < len) {
-                    float vf[8] = {bf16_lo(vv[u].x), bf16_hi(vv[u].x), bf16_lo(vv[u].y), bf16_hi(vv[u].y),
-                                   bf16_lo(vv[u].z), bf16_hi(vv[u].z), bf16_lo(vv[u].w), bf16_hi(vv[u].w)};
-#pragma unroll
-                    for (int hh = 0; hh < GH; ++hh) {
-                        float pw = zb[(hslot0 + hh) * kDecCH + i];
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) acc[hh][e] = fmaf(pw, vf[e], acc[hh][e]);
-                    }
-                }
-            }
-        }
-    }
-    // reduce the 4 rows of the wave
-#pragma unroll
-    for (int hh = 0; hh < GH; ++hh)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float v = acc[hh][e];
-            v += __shfl_xor(v, 16, 64);
-            v += __shfl_xor(v, 32, 64);
-            acc[hh][e] = v;
-        }
-    if (row == 0) {
-#pragma unroll
-        for (int hh = 0; hh < GH; ++hh)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) red[(wid * GH + hh) * kD + p * 8 + e] = wave_on ? acc[hh][e] : 0.f;
-    }
-    __syncthreads();
-
-    // write the partials: (m, l, acc) per head of the block
-    if (MODE == 1) {
-        for (int o = threadIdx.x; o < G * kD; o += NW * 64) {
-            int w = o / kD, d = o % kD;
-            int h = g * G + w;
-            const int64_t slot = (int64_t)blockIdx.x * Hq + h;
-            part_acc[slot * kD + d] = red[w * kD + d];
-            if (d == 0) part_ml[slot] = make_float2(stat[w * 2], stat[w * 2 + 1]);
-        }
-    } else {
-        for (int o = threadIdx.x; o < Hq * kD; o += NW * 64) {
-            int h = o / kD, d = o % kD;
-            int gg = h / G, hh = h % G;
-            float s = 0.f;
-            for (int sb = 0; sb < nsub; ++sb) s += red[((sb * Hkv + gg) * GH + hh) * kD + d];
-            const int64_t slot = (int64_t)blockIdx.x * Hq + h;
-            part_acc[slot * kD + d] = s;
-            if (d == 0) part_ml[slot] = make_float2(stat[h * 2], stat[h * 2 + 1]);
-        }
+    for (int j = 0; j < NA / 4; ++j) {
+        auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(w[j]), __float_as_uint(w[j + NA / 4]), false, false);
+        o[j] = __uint_as_float(s[0]) + __uint_as_float(s[1]);
     }
 }
 
-// Merge of the chunk partials of each (sequence, head).  Block = (b * Hq + h, 16-dim slice);
-// its 1024 threads are (chunk group cg < 64, dim dl < 16).  Every thread first requests its
-// chunks' (m, l) and acc values (8 chunks in flight, every 64th chunk of the sequence), then
-// the block takes the maximum M of all chunk maxima, and the weighted sums
-// sum_c acc_c 2^(m_c - M) and sum_c l_c 2^(m_c - M) are reduced over the 64 groups in LDS.
-__global__ __launch_bounds__(1024) void decode_merge_kernel(const float* __restrict__ part_acc,
-                                                           const float2* __restrict__ part_ml,
-                                                           I64Arg counts, int B, int Hq,
-                                                           float* __restrict__ out) {
-    constexpr int U = 8;
-    __shared__ float sa[64][17];
-    __shared__ float sl[64];
-    __shared__ float smax[16];
-    const int bh = blockIdx.x, b = bh / Hq, h = bh % Hq, ds = blockIdx.y;
+// MODE 0: shared list per sequence (vote); MODE 1: list per query head; MODE 2: dense
+// (the list is implicit: entry j is token j, counts are the sequence lengths).
+template <int G, int MODE>
+__global__ __launch_bounds__(kDecWaves * 64) void decode_partial_kernel(const uint16_t* __restrict__ q,
+                                                                       const uint16_t* __restrict__ K,
+                                                                       const uint16_t* __restrict__ V,
+                                                                       I64Arg offsets,
+                                                                       const int32_t* __restrict__ idx,
+                                                                       I64Arg counts, int B, int Hq,
+                                                                       int Hkv, int EB, float* __restrict__ part_acc,
+                                                                       float2* __restrict__ part_ml) {
+    constexpr int GH = dec_gh(G, MODE);
+    constexpr int EPR = kDecSub / 4;               // entries per lane row and sub-batch
+    constexpr int NV = GH * EPR;                   // (head, entry) scores of a row
+    constexpr int FV = RowSum<NV>::FV;             // complete scores per lane
+    constexpr int DUP = RowSum<NV>::DUP;           // lanes holding the same score
+    constexpr int NA = GH * 8;                     // accumulators per lane
+    // reduction steps over the lanes of a row that hold one head's scores
+    constexpr int HS0 = ilog2c(DUP);
+    constexpr int HS1 = HS0 + ilog2c(EPR / FV);
+    __shared__ float s_acc[kDecWaves][GH][kD];
+    __shared__ float s_m[kDecWaves][GH], s_l[kDecWaves][GH];
+    __shared__ float4 s_p[kDecWaves][4][NV / 4];
+    __shared__ int4 s_tok[kDecWaves][kDecMaxEW / 4];
+
+    const int HW = (MODE == 1) ? Hq : Hkv;
+    const int64_t item = blockIdx.x / HW;
+    const int hw = blockIdx.x % HW;
+    int b;
+    int64_t j0, len, kpre;
+    if (!find_list_chunk(counts, B, item, EB, b, j0, len, kpre)) return;
+    const int64_t off = offsets[b];
+    const int32_t nmax = (int32_t)(offsets[b + 1] - off - 1);   // list entries are clamped to [0, n_b)
+    const int g = (MODE == 1) ? hw / G : hw;
+    const int hbase = (MODE == 1) ? hw : hw * G;                 // first query head of the wave
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int row = lane >> 4, p = lane & 15;
+    const int EW = EB / kDecWaves;
+    const int64_t wb = (int64_t)wid * EW;
+    const int wlen = len <= wb ? 0 : (len - wb < EW ? (int)(len - wb) : EW);
+    const int nsb = (wlen + kDecSub - 1) / kDecSub;
+
+    // token ids of the wave's entries into LDS (entries past the wave's end repeat its first token,
+    // so that every load of a sub-batch is issued and hits a row already requested)
+    int32_t* tok = reinterpret_cast<int32_t*>(&s_tok[wid][0]);
+    {
+        int32_t t0 = 0;
+        if (wlen > 0) {
+            const int64_t j = j0 + wb;
+            t0 = (MODE == 2) ? (int32_t)j : ((MODE == 1) ? idx[Hq * kpre + (int64_t)hw * counts[b] + j] : idx[kpre + j]);
+        }
+        for (int i = lane; i < nsb * kDecSub; i += 64) {
+            int32_t t = t0;
+            if (i < wlen) {
+                const int64_t j = j0 + wb + i;
+                t = (MODE == 2) ? (int32_t)j : ((MODE == 1) ? idx[Hq * kpre + (int64_t)hw * counts[b] + j] : idx[kpre + j]);
+            }
+            tok[i] = t < 0 ? 0 : (t > nmax ? nmax : t);
+        }
+    }
+    uint4 qv[GH];
+#pragma unroll
+    for (int hh = 0; hh < GH; ++hh) qv[hh] = ld16(q + ((int64_t)b * Hq + hbase + hh) * kD + p * 8);
+    __builtin_amdgcn_wave_barrier();
+
+    const uint16_t* Kg = K + (off * Hkv + g) * kD + p * 8;
+    const uint16_t* Vg = V + (off * Hkv + g) * kD + p * 8;
+    const int64_t rstride = (int64_t)Hkv * kD;
+    auto issue = [&](int sb, uint4 (&kb)[EPR], uint4 (&vb)[EPR]) {
+        const int4 t = s_tok[wid][(sb * kDecSub + row * EPR) / 4];
+        const int tt[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+        for (int k = 0; k < EPR; ++k) kb[k] = ld16(Kg + tt[k] * rstride);
+#pragma unroll
+        for (int k = 0; k < EPR; ++k) vb[k] = ld16(Vg + tt[k] * rstride);
+    };
+
+    float m_run = -INFINITY, l_run = 0.f;         // this lane's head (hh_l)
+    float acc[NA];
+#pragma unroll
+    for (int i = 0; i < NA; ++i) acc[i] = 0.f;
+    // this lane's scores: index i = p * FV + s (NV >= 16) or p / DUP (NV < 16), head i / EPR,
+    // entry 4 row + (i % EPR) of the sub-batch
+    const int i0 = NV >= 16 ? p * FV : p / DUP;
+    const int hh_l = i0 / EPR;
+    float4* sp4 = &s_p[wid][row][0];
+    float* sp = reinterpret_cast<float*>(sp4);
+
+    auto compute = [&](int sb, const uint4 (&kb)[EPR], const uint4 (&vb)[EPR]) {
+        float zp[NV];
+#pragma unroll
+        for (int k = 0; k < EPR; ++k)
+#pragma unroll
+            for (int hh = 0; hh < GH; ++hh) {
+                float s = dot2_bf16(qv[hh].x, kb[k].x, 0.f);
+                s = dot2_bf16(qv[hh].y, kb[k].y, s);
+                s = dot2_bf16(qv[hh].z, kb[k].z, s);
+                zp[hh * EPR + k] = dot2_bf16(qv[hh].w, kb[k].w, s);
+            }
+        float z[FV];
+        RowSum<NV>::run(zp, z, p);
+        float mx = -INFINITY;
+#pragma unroll
+        for (int s = 0; s < FV; ++s) {
+            const int e = sb * kDecSub + row * EPR + (i0 + s) % EPR;
+            z[s] = e < wlen ? z[s] * kLog2eOverSqrtD : -INFINITY;
+            mx = fmaxf(mx, z[s]);
+        }
+        const float m_new = fmaxf(m_run, head_reduce<true, HS0, HS1>(mx));
+        const float alpha = m_run == -INFINITY ? 0.f : fast_exp2(m_run - m_new);
+        float ls = 0.f;
+#pragma unroll
+        for (int s = 0; s < FV; ++s) {
+            z[s] = m_new == -INFINITY ? 0.f : fast_exp2(z[s] - m_new);
+            ls += z[s];
+        }
+        l_run = l_run * alpha + head_reduce<false, HS0, HS1>(ls);
+        m_run = m_new;
+        // the row's probabilities to every lane of the row (LDS, one wave: in order)
+        if (NV >= 16) {
+#pragma unroll
+            for (int s = 0; s < FV; ++s) sp[i0 + s] = z[s];
+        } else if (p % DUP == 0) {
+            sp[i0] = z[0];
+        }
+        __builtin_amdgcn_wave_barrier();
+        float pr[NV];
+#pragma unroll
+        for (int i = 0; i < NV / 4; ++i) {
+            const float4 x = sp4[i];
+            pr[4 * i] = x.x; pr[4 * i + 1] = x.y; pr[4 * i + 2] = x.z; pr[4 * i + 3] = x.w;
+        }
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int hh = 0; hh < GH; ++hh) {
+            // rescale factor of head hh: uniform over the wave, read from its first lane
+            const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha),
+                                                                    (hh * EPR * DUP) / FV));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[hh * 8 + e] *= a;
+        }
+#pragma unroll
+        for (int k = 0; k < EPR; ++k) {
+            const float vf[8] = {bf16_lo(vb[k].x), bf16_hi(vb[k].x), bf16_lo(vb[k].y), bf16_hi(vb[k].y),
+                                 bf16_lo(vb[k].z), bf16_hi(vb[k].z), bf16_lo(vb[k].w), bf16_hi(vb[k].w)};
+#pragma unroll
+            for (int hh = 0; hh < GH; ++hh)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[hh * 8 + e] = fmaf(pr[hh * EPR + k], vf[e], acc[hh * 8 + e]);
+        }
+    };
+
+    // two sub-batches in flight: A = even, B = odd
+    uint4 ka[EPR], va[EPR], kb2[EPR], vb2[EPR];
+    if (nsb > 0) issue(0, ka, va);
+    for (int sb = 0; sb < nsb; sb += 2) {
+        if (sb + 1 < nsb) issue(sb + 1, kb2, vb2);
+        compute(sb, ka, va);
+        if (sb + 2 < nsb) issue(sb + 2, ka, va);
+        if (sb + 1 < nsb) compute(sb + 1, kb2, vb2);
+    }
+
+    // sum over the 4 rows: row r holds accumulator indices r * NA / 4 + j
+    float ar[NA / 4];
+    rows_tsum<NA>(acc, ar);
+#pragma unroll
+    for (int j = 0; j < NA / 4; ++j) {
+        const int i = row * (NA / 4) + j;
+        s_acc[wid][i / 8][p * 8 + (i % 8)] = ar[j];
+    }
+    if (row == 0 && p == (hh_l * EPR * DUP) / FV) {
+        s_m[wid][hh_l] = m_run;
+        s_l[wid][hh_l] = l_run;
+    }
+    __syncthreads();
+    // the block's partial: merge of the waves
+    for (int o = threadIdx.x; o < GH * kD; o += kDecWaves * 64) {
+        const int hh = o / kD, d = o % kD;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, s_m[w][hh]);
+        float A = 0.f, L = 0.f;
+#pragma unroll
+        for (int w = 0; w < kDecWaves; ++w) {
+            const float mw = s_m[w][hh];
+            const float wt = mw == -INFINITY ? 0.f : fast_exp2(mw - M);
+            A = fmaf(s_acc[w][hh][d], wt, A);
+            L = fmaf(s_l[w][hh], wt, L);
+        }
+        const int64_t slot = item * Hq + hbase + hh;
+        part_acc[slot * kD + d] = A;
+        if (d == 0) part_ml[slot] = make_float2(M, L);
+    }
+}
+
+// Merge of the chunk partials of each (sequence, head).  One block per (b, h); thread
+// (cg, d) = (tid / 128, tid % 128) takes every 8th chunk of the sequence with 16 loads in
+// flight and keeps a running (M, A, L) in the log2 domain; the 8 groups then combine in LDS.
+constexpr int kMergeThreads = 1024;
+__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const float* __restrict__ part_acc,
+                                                                    const float2* __restrict__ part_ml,
+                                                                    I64Arg counts, int B, int Hq, int EB,
+                                                                    float* __restrict__ out) {
+    constexpr int NG = kMergeThreads / kD, U = 16;
+    __shared__ float sM[NG], sL[NG];
+    __shared__ float sA[NG][kD];
+    const int bh = blockIdx.x, b = bh / Hq, h = bh % Hq;
     int64_t first = 0;
-    for (int i = 0; i < b; ++i) first += (counts[i] + kDecCH - 1) / kDecCH;
-    const int64_t nch = (counts[b] + kDecCH - 1) / kDecCH;
-    const int cg = threadIdx.x >> 4, dl = threadIdx.x & 15, d = ds * 16 + dl;
-    float a = 0.f, l = 0.f;
-    float M = -INFINITY;
-    for (int64_t c0 = cg; c0 - cg < nch; c0 += 64 * U) {
+    for (int i = 0; i < b; ++i) first += (counts[i] + EB - 1) / EB;
+    const int64_t nch = (counts[b] + EB - 1) / EB;
+    const int cg = threadIdx.x / kD, d = threadIdx.x % kD;
+    float M = -INFINITY, A = 0.f, L = 0.f;
+    for (int64_t c0 = cg; c0 < nch; c0 += (int64_t)NG * U) {
         float x[U], mm[U], ll[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t c = c0 + 64 * u;
-            const int64_t slot = (first + (c < nch ? c : 0)) * Hq + h;
+            const int64_t c = c0 + (int64_t)NG * u;
+            const int64_t slot = (first + (c < nch ? c : c0)) * Hq + h;
             x[u] = part_acc[slot * kD + d];
             const float2 ml = part_ml[slot];
             mm[u] = c < nch ? ml.x : -INFINITY;
             ll[u] = ml.y;
         }
-        // the block-wide maximum over every chunk seen so far
-        float mx = -INFINITY;
-#pragma unroll
-        for (int u = 0; u < U; ++u) mx = fmaxf(mx, mm[u]);
-        mx = wave_max(mx);
-        __syncthreads();
-        if ((threadIdx.x & 63) == 0) smax[threadIdx.x >> 6] = mx;
-        __syncthreads();
         float Mn = M;
 #pragma unroll
-        for (int w = 0; w < 16; ++w) Mn = fmaxf(Mn, smax[w]);
+        for (int u = 0; u < U; ++u) Mn = fmaxf(Mn, mm[u]);
         if (Mn != -INFINITY) {
-            const float rs = fast_exp2(M - Mn);     // rescale what was summed under M
-            a *= rs;
-            l *= rs;
+            const float rs = M == -INFINITY ? 0.f : fast_exp2(M - Mn);
+            A *= rs;
+            L *= rs;
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                if (c0 + 64 * u < nch) {
-                    const float w = fast_exp2(mm[u] - Mn);
-                    a = fmaf(x[u], w, a);
-                    l = fmaf(ll[u], w, l);
-                }
+                const float w = mm[u] == -INFINITY ? 0.f : fast_exp2(mm[u] - Mn);
+                A = fmaf(x[u], w, A);
+                L = fmaf(ll[u], w, L);
             }
             M = Mn;
         }
     }
-    sa[cg][dl] = a;
-    if (dl == 0) sl[cg] = l;
+    sA[cg][d] = A;
+    if (d == 0) { sM[cg] = M; sL[cg] = L; }
     __syncthreads();
-    if (threadIdx.x < 16) {
-        float A = 0.f, L = 0.f;
-        for (int k = 0; k < 64; ++k) { A += sa[k][threadIdx.x]; L += sl[k]; }
-        out[((int64_t)b * Hq + h) * kD + ds * 16 + threadIdx.x] = A / L;
+    if (threadIdx.x < kD) {
+        float Mx = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < NG; ++k) Mx = fmaxf(Mx, sM[k]);
+        float As = 0.f, Ls = 0.f;
+#pragma unroll
+        for (int k = 0; k < NG; ++k) {
+            const float w = sM[k] == -INFINITY ? 0.f : fast_exp2(sM[k] - Mx);
+            As = fmaf(sA[k][threadIdx.x], w, As);
+            Ls = fmaf(sL[k], w, Ls);
+        }
+        out[((int64_t)b * Hq + h) * kD + threadIdx.x] = As / Ls;
     }
 }
 
-static int64_t list_items(const int64_t* counts_host, int B) {
+static int64_t list_items(const int64_t* counts_host, int B, int EB) {
     int64_t it = 0;
-    for (int b = 0; b < B; ++b) it += (counts_host[b] + kDecCH - 1) / kDecCH;
+    for (int b = 0; b < B; ++b) it += (counts_host[b] + EB - 1) / EB;
     return it;
 }
 
+// Compute units of the current device (queried once per device).
+static int device_cus() {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
+template <int MODE>
+static const void* partial_fn(int G) {
+    switch (G) {
+        case 1: return reinterpret_cast<const void*>(decode_partial_kernel<1, MODE>);
+        case 2: return reinterpret_cast<const void*>(decode_partial_kernel<2, MODE>);
+        case 4: return reinterpret_cast<const void*>(decode_partial_kernel<4, MODE>);
+        default: return reinterpret_cast<const void*>(decode_partial_kernel<8, MODE>);
+    }
+}
+// Resident blocks per compute unit of an instantiation (queried once).
+static int partial_blocks_per_cu(int G, int mode) {
+    static int cache[3][4] = {};
+    const int lg = G == 1 ? 0 : (G == 2 ? 1 : (G == 4 ? 2 : 3));
+    int& c = cache[mode][lg];
+    if (c == 0) {
+        const void* f = mode == 0 ? partial_fn<0>(G) : (mode == 1 ? partial_fn<1>(G) : partial_fn<2>(G));
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, kDecWaves * 64, 0) != hipSuccess || n <= 0) n = 2;
+        c = n;
+    }
+    return c;
+}
+
+// Entries per block: the whole work (entries x HW blocks per range) spread over one round of
+// resident blocks; a multiple of 4, at least one sub-batch per wave and at most kDecMaxEW
+// entries per wave.
+static int decode_eb(int64_t entries, int HW, int G, int mode) {
+    const int64_t target = (int64_t)partial_blocks_per_cu(G, mode) * device_cus();
+    int64_t eb = (entries * HW + target - 1) / target;
+    eb = (eb + 3) / 4 * 4;
+    if (eb < kDecWaves * kDecSub) eb = kDecWaves * kDecSub;
+    if (eb > kDecWaves * kDecMaxEW) eb = kDecWaves * kDecMaxEW;
+    return (int)eb;
+}
+
+// Workspace: the partials of at most sum_b ceil(K_b / EB) <= sum_b K_b / (kDecWaves kDecSub) + B
+// ranges (EB never falls below kDecWaves kDecSub), a bound that grows with the list lengths.
 size_t decode_workspace(const int64_t* offsets_host, const int64_t* counts_host, int B, int Hq, int Hkv, int mode) {
     (void)Hkv;
     (void)mode;
-    int64_t items = 0;
-    if (counts_host) items = list_items(counts_host, B);
-    else
-        for (int b = 0; b < B; ++b) items += (offsets_host[b + 1] - offsets_host[b] + kDecCH - 1) / kDecCH;
+    int64_t total = 0;
+    for (int b = 0; b < B; ++b) total += counts_host ? counts_host[b] : offsets_host[b + 1] - offsets_host[b];
+    const int64_t items = (total + kDecWaves * kDecSub - 1) / (kDecWaves * kDecSub) + B;
     WsCarver w(nullptr);
     w.take<int64_t>((size_t)B + 1);   // dense: per-sequence lengths
     w.take<float>((size_t)items * Hq * kD);
@@ -335,13 +471,13 @@ size_t decode_workspace(const int64_t* offsets_host, const int64_t* counts_host,
 template <int MODE>
 static hipError_t launch_partial_G(int G, dim3 grid, hipStream_t stream, const uint16_t* q, const uint16_t* K,
                                    const uint16_t* V, const I64Arg& offsets, const int32_t* idx,
-                                   const I64Arg& counts, int B, int Hq, int Hkv, float* part, float2* ml) {
-    dim3 block(MODE == 1 ? 64 * G : 512);
+                                   const I64Arg& counts, int B, int Hq, int Hkv, int EB, float* part, float2* ml) {
+    const dim3 block(kDecWaves * 64);
     switch (G) {
-        case 1: hipLaunchKernelGGL((decode_partial_kernel<1, MODE>), grid, block, 0, stream, q, K, V, offsets, idx, counts, B, Hq, Hkv, part, ml); break;
-        case 2: hipLaunchKernelGGL((decode_partial_kernel<2, MODE>), grid, block, 0, stream, q, K, V, offsets, idx, counts, B, Hq, Hkv, part, ml); break;
-        case 4: hipLaunchKernelGGL((decode_partial_kernel<4, MODE>), grid, block, 0, stream, q, K, V, offsets, idx, counts, B, Hq, Hkv, part, ml); break;
-        case 8: hipLaunchKernelGGL((decode_partial_kernel<8, MODE>), grid, block, 0, stream, q, K, V, offsets, idx, counts, B, Hq, Hkv, part, ml); break;
+        case 1: hipLaunchKernelGGL((decode_partial_kernel<1, MODE>), grid, block, 0, stream, q, K, V, offsets, idx, counts, B, Hq, Hkv, EB, part, ml); break;
+        case 2: hipLaunchKernelGGL((decode_partial_kernel<2, MODE>), grid, block, 0, stream, q, K, V, offsets, idx, counts, B, Hq, Hkv, EB, part, ml); break;
+        case 4: hipLaunchKernelGGL((decode_partial_kernel<4, MODE>), grid, block, 0, stream, q, K, V, offsets, idx, counts, B, Hq, Hkv, EB, part, ml); break;
+        case 8: hipLaunchKernelGGL((decode_partial_kernel<8, MODE>), grid, block, 0, stream, q, K, V, offsets, idx, counts, B, Hq, Hkv, EB, part, ml); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -357,19 +493,23 @@ hipError_t launch_sparse_decode(const uint16_t* q, const uint16_t* K, const uint
                                 const int64_t* counts_host, int mode, int B, int Hq, int Hkv, float* out, void* ws,
                                 size_t ws_bytes, hipStream_t stream) {
     if (decode_workspace(offsets_host, counts_host, B, Hq, Hkv, mode) > ws_bytes) return hipErrorInvalidValue;
+    const int G = Hq / Hkv;
+    int64_t total = 0;
+    for (int b = 0; b < B; ++b) total += counts_host[b];
+    const int EB = decode_eb(total, mode == 1 ? Hq : Hkv, G, mode);
     WsCarver w(ws);
     w.take<int64_t>((size_t)B + 1);
-    const int64_t items = list_items(counts_host, B);
+    const int64_t items = list_items(counts_host, B, EB);
     float* part = w.take<float>((size_t)items * Hq * kD);
     float2* ml = w.take<float2>((size_t)items * Hq);
-    const int G = Hq / Hkv;
     const I64Arg offs = i64_arg(offsets_dev, offsets_host, (int64_t)B + 1);
     const I64Arg cnts = i64_arg(counts_dev, counts_host, B);
+    if (items == 0) return hipSuccess;
     hipError_t e;
-    if (mode == 0) e = launch_partial_G<0>(G, dim3((unsigned)items), stream, q, K, V, offs, idx, cnts, B, Hq, Hkv, part, ml);
-    else e = launch_partial_G<1>(G, dim3((unsigned)items, Hkv), stream, q, K, V, offs, idx, cnts, B, Hq, Hkv, part, ml);
+    if (mode == 0) e = launch_partial_G<0>(G, dim3((unsigned)(items * Hkv)), stream, q, K, V, offs, idx, cnts, B, Hq, Hkv, EB, part, ml);
+    else e = launch_partial_G<1>(G, dim3((unsigned)(items * Hq)), stream, q, K, V, offs, idx, cnts, B, Hq, Hkv, EB, part, ml);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_merge_kernel, dim3(B * Hq, kD / 16), dim3(1024), 0, stream, part, ml, cnts, B, Hq, out);
+    hipLaunchKernelGGL(decode_merge_kernel, dim3(B * Hq), dim3(kMergeThreads), 0, stream, part, ml, cnts, B, Hq, EB, out);
     return hipGetLastError();
 }
 
@@ -377,8 +517,10 @@ hipError_t launch_dense_decode(const uint16_t* q, const uint16_t* K, const uint1
                                const int64_t* offsets_host, int B, int Hq, int Hkv, float* out, void* ws,
                                size_t ws_bytes, hipStream_t stream) {
     if (decode_workspace(offsets_host, nullptr, B, Hq, Hkv, 2) > ws_bytes) return hipErrorInvalidValue;
+    const int G = Hq / Hkv;
+    const int EB = decode_eb(offsets_host[B] - offsets_host[0], Hkv, G, 2);
     int64_t items = 0;
-    for (int b = 0; b < B; ++b) items += (offsets_host[b + 1] - offsets_host[b] + kDecCH - 1) / kDecCH;
+    for (int b = 0; b < B; ++b) items += (offsets_host[b + 1] - offsets_host[b] + EB - 1) / EB;
     WsCarver w(ws);
     int64_t* lens = w.take<int64_t>((size_t)B + 1);
     float* part = w.take<float>((size_t)items * Hq * kD);
@@ -388,11 +530,12 @@ hipError_t launch_dense_decode(const uint16_t* q, const uint16_t* K, const uint1
     // the device
     const int64_t hl = offsets_host[B] - offsets_host[0];
     const I64Arg lns = i64_arg(lens, B == 1 ? &hl : nullptr, B);
+    if (items == 0) return hipSuccess;
     if (B != 1) hipLaunchKernelGGL(lengths_kernel, dim3(1), dim3(256), 0, stream, offs, B, lens);
-    hipError_t e = launch_partial_G<2>(Hq / Hkv, dim3((unsigned)items), stream, q, K, V, offs, nullptr, lns,
-                                       B, Hq, Hkv, part, ml);
+    hipError_t e = launch_partial_G<2>(G, dim3((unsigned)(items * Hkv)), stream, q, K, V, offs, nullptr, lns, B, Hq,
+                                       Hkv, EB, part, ml);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_merge_kernel, dim3(B * Hq, kD / 16), dim3(1024), 0, stream, part, ml, lns, B, Hq, out);
+    hipLaunchKernelGGL(decode_merge_kernel, dim3(B * Hq), dim3(kMergeThreads), 0, stream, part, ml, lns, B, Hq, EB, out);
     return hipGetLastError();
 }
 
