@@ -2,8 +2,11 @@
 
 Workload: one LLaMA-3-8B-shaped attention layer (32 query / 8 KV heads, d = 128, index
 d' = 32) with n = 131072 cached tokens, a 20 % selection budget and voting mode.  A step is
-the whole hot path: ts_index_append (T = 1) + ts_score + ts_select + ts_sparse_decode,
-with the cache, the index and the step's query already resident in HBM.  The last-level
+the whole hot path: the index row of the step's new key, the index scores, the selection
+and the sparse decode, with the cache, the index and the step's query already resident in
+HBM.  By default (--path fused) it is ts_score_select (which appends the index row itself)
++ ts_sparse_decode; --path calls runs ts_index_append + ts_score + ts_select +
+ts_sparse_decode instead (the same outputs; reported beside the headline either way).  The last-level
 cache is flushed (a 512 MiB read) before every timed step, outside the timed region, so
 the figure is HBM-cold.  Time is measured with HIP events on the stream the kernels run on.
 
@@ -58,6 +61,9 @@ def parse():
     ap.add_argument("--workload", choices=["long", "ragged"], default="long",
                     help="long: one sequence of --n tokens (the headline); ragged: a batch of 16 sequences of "
                          "16K-64K tokens at a 15%% budget")
+    ap.add_argument("--path", choices=["fused", "calls"], default="fused",
+                    help="fused: ts_score_select (with the index append) + ts_sparse_decode; calls: ts_index_append + "
+                         "ts_score + ts_select + ts_sparse_decode")
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip dense / warm / graph side measurements")
@@ -160,14 +166,20 @@ def bench_ragged(args, torch, api, synth, dev):
         if rc != 0:
             raise RuntimeError(L.ts_last_error().decode())
 
+    ws_ss = torch.empty(max(api.score_select_workspace_bytes(offs, Hq, p), 256), dtype=torch.uint8, device=dev)
+
     def step():
         st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-        for b in range(offs.B):
-            last = offs.host_list[b + 1] - 1
-            chk(L.ts_index_append(ctypes.c_void_p(Kp.value + last * row_bytes), Pp, kip, last, 1, Hkv, st))
-        chk(L.ts_score(qp, Pp, kip, vp(offs.dev), offs.host, offs.B, Hq, Hkv, scp, vp(ws_sc), ws_sc.numel(), st))
-        chk(L.ts_select(scp, vp(offs.dev), offs.host, offs.B, Hq, Hkv, pref, vp(idx), vp(count), None, None,
-                        vp(ws_sel), ws_sel.numel(), st))
+        if args.path == "fused":
+            chk(L.ts_score_select(qp, Pp, kip, Kp, vp(offs.dev), offs.host, offs.B, Hq, Hkv, pref, scp, vp(idx),
+                                  vp(count), None, None, vp(ws_ss), ws_ss.numel(), st))
+        else:
+            for b in range(offs.B):
+                last = offs.host_list[b + 1] - 1
+                chk(L.ts_index_append(ctypes.c_void_p(Kp.value + last * row_bytes), Pp, kip, last, 1, Hkv, st))
+            chk(L.ts_score(qp, Pp, kip, vp(offs.dev), offs.host, offs.B, Hq, Hkv, scp, vp(ws_sc), ws_sc.numel(), st))
+            chk(L.ts_select(scp, vp(offs.dev), offs.host, offs.B, Hq, Hkv, pref, vp(idx), vp(count), None, None,
+                            vp(ws_sel), ws_sel.numel(), st))
         chk(L.ts_sparse_decode(qp, Kp, Vp, vp(offs.dev), offs.host, vp(idx), vp(count), ch, mode, offs.B, Hq, Hkv,
                                vp(out), vp(ws_dec), ws_dec.numel(), st))
 
@@ -205,6 +217,7 @@ def bench_ragged(args, torch, api, synth, dev):
            "config": {"workload": f"ragged batch of {offs.B} sequences ({min(lens)}-{max(lens)} tokens, "
                                   f"{ntot} in total), 32 query / 8 KV heads, d=128, d'=32, budget "
                                   f"{x.budget[0]}/{x.budget[1]}, {args.mode} mode", "B": offs.B, "Ntot": ntot,
+                      "path": args.path,
                       "llc": "flushed before each step"},
            "median_us": round(float(np.median(us)), 2),
            "hbm_gbps": round(step_bytes / (mean * 1e-6) / 1e9, 1),
@@ -269,6 +282,7 @@ def main():
     idx = torch.empty(kmax * (Hq if mode == api.MODE_PER_HEAD else 1) + 16, dtype=torch.int32, device=dev)
     count = torch.empty(1, dtype=torch.int64, device=dev)
     ws_sel = torch.empty(max(api.select_workspace_bytes(offs[-1], Hq, p), 256), dtype=torch.uint8, device=dev)
+    ws_ss = torch.empty(max(api.score_select_workspace_bytes(offs[-1], Hq, p), 256), dtype=torch.uint8, device=dev)
     ws_sc = torch.empty(max(api.score_workspace_bytes(1, Hq), 256), dtype=torch.uint8, device=dev)
     ws_dec = torch.empty(max(api.decode_workspace_bytes(offs[-1], [kmax], Hq, Hkv, mode), 256), dtype=torch.uint8,
                          device=dev)
@@ -300,14 +314,15 @@ def main():
         calls.append(((vp(K) .value + (n - 1) * Hkv * 128 * 2, n - 1),
                       (qp, vp(o.dev), o.host), ch, kb))
     Kp, Pp, kip, scp, idp, cnp = vp(K), vp(P), vp(kidx), vp(scores), vp(idx), vp(count)
-    Vp, outp, wsp, wdp, wsc = vp(V), vp(out), vp(ws_sel), vp(ws_dec), vp(ws_sc)
-    ws_sel_n, ws_dec_n, ws_sc_n = ws_sel.numel(), ws_dec.numel(), ws_sc.numel()
+    Vp, outp, wsp, wdp, wsc, wss = vp(V), vp(out), vp(ws_sel), vp(ws_dec), vp(ws_sc), vp(ws_ss)
+    ws_sel_n, ws_dec_n, ws_sc_n, ws_ss_n = ws_sel.numel(), ws_dec.numel(), ws_sc.numel(), ws_ss.numel()
 
     def chk(rc):
         if rc != 0:
             raise RuntimeError(L.ts_last_error().decode())
 
-    def step(s, marks=None):
+    def step_calls(s, marks=None):
+        """The four calls: ts_index_append, ts_score, ts_select, ts_sparse_decode."""
         (kaddr, pos), (qp, od, oh), ch, kb = calls[s]
         st = stream_of()
         chk(L.ts_index_append(ctypes.c_void_p(kaddr), Pp, kip, pos, 1, Hkv, st))
@@ -318,6 +333,17 @@ def main():
         if marks: marks[3].record()
         chk(L.ts_sparse_decode(qp, Kp, Vp, od, oh, idp, cnp, ch, mode, 1, Hq, Hkv, outp, wdp, ws_dec_n, st))
         return kb
+
+    def step_fused(s, marks=None):
+        """ts_score_select (appending the step's index row itself) + ts_sparse_decode."""
+        (kaddr, pos), (qp, od, oh), ch, kb = calls[s]
+        st = stream_of()
+        chk(L.ts_score_select(qp, Pp, kip, Kp, od, oh, 1, Hq, Hkv, pref, scp, idp, cnp, None, None, wss, ws_ss_n, st))
+        if marks: marks[1].record()
+        chk(L.ts_sparse_decode(qp, Kp, Vp, od, oh, idp, cnp, ch, mode, 1, Hq, Hkv, outp, wdp, ws_dec_n, st))
+        return kb
+
+    step = step_fused if args.path == "fused" else step_calls
 
     # warm-up
     for s in range(warm):
@@ -347,22 +373,31 @@ def main():
     # per-call breakdown in separate steps (the same inputs again): an event between two calls
     # idles the GPU for a few microseconds, so these steps are not the timed ones
     nb = min(steps, 30)
-    bmarks = [[ev() for _ in range(5)] for _ in range(nb)]
+    names = ["score_select", "sparse_decode"] if args.path == "fused" else \
+        ["index_append", "score", "select", "sparse_decode"]
+    bmarks = [[ev() for _ in range(len(names) + 1)] for _ in range(nb)]
     for i in range(nb):
         if not args.no_flush:
             do_flush()
         m = bmarks[i]
         m[0].record()
         step(warm + steps - nb + i, m)
-        m[4].record()
+        m[-1].record()
     torch.cuda.synchronize()
-    parts = {
-        "index_append": np.array([m[0].elapsed_time(m[1]) * 1e3 for m in bmarks]),
-        "score": np.array([m[1].elapsed_time(m[2]) * 1e3 for m in bmarks]),
-        "select": np.array([m[2].elapsed_time(m[3]) * 1e3 for m in bmarks]),
-        "sparse_decode": np.array([m[3].elapsed_time(m[4]) * 1e3 for m in bmarks]),
-    }
-    breakdown_step = float(np.mean([m[0].elapsed_time(m[4]) * 1e3 for m in bmarks]))
+    parts = {nm: np.array([m[k].elapsed_time(m[k + 1]) * 1e3 for m in bmarks]) for k, nm in enumerate(names)}
+    breakdown_step = float(np.mean([m[0].elapsed_time(m[-1]) * 1e3 for m in bmarks]))
+
+    # the other path (four separate calls, or the fused one) on the same steps, for reference
+    other = step_calls if args.path == "fused" else step_fused
+    omarks = [(ev(), ev()) for _ in range(nb)]
+    for i in range(nb):
+        if not args.no_flush:
+            do_flush()
+        omarks[i][0].record()
+        other(warm + steps - nb + i)
+        omarks[i][1].record()
+    torch.cuda.synchronize()
+    other_us = float(np.mean([a.elapsed_time(b) * 1e3 for a, b in omarks]))
 
     # algorithmic bytes (what the method must move): index read + selected K/V rows
     n_mean = n0 + warm + (steps + 1) / 2.0
@@ -559,8 +594,10 @@ def main():
         "hbm_gbps": round(gbps, 1),
         "pct_peak": round(100 * gbps / PEAK_GBPS, 1),
         "algorithmic_bytes_per_step": int(step_bytes),
+        "path": args.path,
         "breakdown_us": {k: round(float(v.mean()), 2) for k, v in parts.items()},
         "breakdown_step_us": round(breakdown_step, 2),
+        ("four_call_step_us" if args.path == "fused" else "fused_step_us"): round(other_us, 2),
         "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": PEAK_GBPS, "unit": "GB/s",
                      "frac": round(dec_gbps / PEAK_GBPS, 4), "traffic": traffic,
                      "kernel": "ts_sparse_decode (decode_partial_kernel + decode_merge_kernel), alone, LLC flushed",

@@ -136,6 +136,33 @@ int ts_select(const float* scores, const int64_t* offsets_dev, const int64_t* of
               int64_t* count_out, float* theta_out, uint8_t* votes_out, void* ws,
               size_t ws_bytes, hipStream_t stream);
 
+/* Workspace for ts_score_select. */
+size_t ts_score_select_workspace_bytes(const int64_t* offsets_host, int32_t B, int32_t Hq,
+                                       const ts_select_params* p);
+
+/* One decode step's index scores and selection in a single call: the same scores as
+ * ts_score and the same thresholds, votes and lists as ts_select on them (the outputs are
+ * identical), with fewer passes over the score array ([TS] "Query-Key Dot Product Index",
+ * "Voting Mechanism", "Token-Level Selection と Sparse Attention"; [TB] "Kernarchitektur").
+ * If K_last is non-NULL the call first appends, for every sequence b, the index row of its
+ * last token t = offsets[b+1] - 1 from K_last (the K cache, whose row t already holds the
+ * step's new key), exactly as ts_index_append(K_last + t*Hkv*128, P, k_index, t, 1, Hkv)
+ * would.
+ *   q, P, k_index, offsets: as for ts_score (k_index is written only when K_last is given)
+ *   K_last    nullable device bf16 [Ntot][Hkv][128]
+ *   p, idx_out, count_out, theta_out, votes_out: as for ts_select
+ *   scores    device fp32 [Hq][S] (written, S = ts_score_stride)
+ *   ws        device workspace of at least ts_score_select_workspace_bytes(...) bytes.
+ * Each head's order statistic is found from a key bracket taken from 2048 sampled index
+ * scores: the score pass counts, per 64-token tile, the keys below the bracket and keeps the
+ * keys inside it, and one block per (sequence, head) ranks those; when the target rank falls
+ * outside the bracket the whole row is radix-selected instead (same result).              */
+int ts_score_select(const uint16_t* q, const float* P, uint16_t* k_index, const uint16_t* K_last,
+                    const int64_t* offsets_dev, const int64_t* offsets_host, int32_t B, int32_t Hq,
+                    int32_t Hkv, const ts_select_params* p, float* scores, int32_t* idx_out,
+                    int64_t* count_out, float* theta_out, uint8_t* votes_out, void* ws,
+                    size_t ws_bytes, hipStream_t stream);
+
 /* Workspace for ts_sparse_decode (counts_host = the per-sequence list lengths) and for
  * ts_dense_decode (counts_host = NULL). */
 size_t ts_decode_workspace_bytes(const int64_t* offsets_host, const int64_t* counts_host,

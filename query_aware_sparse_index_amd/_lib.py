@@ -25,6 +25,9 @@ SIGNATURES = {
     "ts_score": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64p, _i32, _i32, _i32, _vp, _vp, _sz, _vp]),
     "ts_select_workspace_bytes": (_sz, [_i64p, _i32, _i32, _vp]),
     "ts_select": (ctypes.c_int, [_vp, _vp, _i64p, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "ts_score_select_workspace_bytes": (_sz, [_i64p, _i32, _i32, _vp]),
+    "ts_score_select": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64p, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
+                                       _vp, _sz, _vp]),
     "ts_decode_workspace_bytes": (_sz, [_i64p, _i64p, _i32, _i32, _i32, _i32]),
     "ts_sparse_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64p, _vp, _vp, _i64p, _i32, _i32, _i32, _i32, _vp,
                                         _vp, _sz, _vp]),

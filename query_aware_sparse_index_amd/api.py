@@ -126,6 +126,44 @@ def select(scores, offs: Offsets, Hkv: int, p, want_theta=False, want_votes=Fals
     return res
 
 
+def score_select_workspace_bytes(offs: Offsets, Hq: int, p) -> int:
+    return int(_lib.load().ts_score_select_workspace_bytes(offs.host, offs.B, int(Hq), ctypes.byref(p)))
+
+
+def score_select(q, P, k_index, offs: Offsets, Hkv: int, p, K_last=None, want_theta=False, want_votes=False,
+                 ws=None, scores=None, idx=None, count=None):
+    """ts_score followed by ts_select in one call (same outputs); with K_last, the index row of
+    every sequence's last token is appended from the K cache first.  Returns the select() dict
+    plus "scores"."""
+    _bf16_check(q, k_index)
+    if K_last is not None:
+        _bf16_check(K_last)
+    Hq = q.shape[1]
+    dev = q.device
+    ks = [budget_tokens(offs.host_list[b + 1] - offs.host_list[b], p) for b in range(offs.B)]
+    total = sum(ks) * (Hq if p.mode == MODE_PER_HEAD else 1)
+    if scores is None:
+        scores = torch.empty((Hq, score_stride(offs)), dtype=torch.float32, device=dev)
+    if idx is None:
+        idx = torch.empty(max(total, 4), dtype=torch.int32, device=dev)
+    if count is None:
+        count = torch.empty(offs.B, dtype=torch.int64, device=dev)
+    theta = torch.empty((offs.B, Hq), dtype=torch.float32, device=dev) if want_theta else None
+    votes = torch.empty(max(offs.ntot, 16), dtype=torch.uint8, device=dev) if want_votes else None
+    need = score_select_workspace_bytes(offs, Hq, p)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _check(_lib.load().ts_score_select(_p(q), _p(P), _p(k_index), _p(K_last), _p(offs.dev), offs.host, offs.B, Hq,
+                                       int(Hkv), ctypes.byref(p), _p(scores), _p(idx), _p(count), _p(theta),
+                                       _p(votes), _p(ws), ws.numel(), _stream()))
+    res = {"idx": idx[:total], "count": count, "counts_host": ks, "scores": scores}
+    if want_theta:
+        res["theta"] = theta
+    if want_votes:
+        res["votes"] = votes[:offs.ntot]
+    return res
+
+
 def decode_workspace_bytes(offs: Offsets, counts_host, Hq: int, Hkv: int, mode: int) -> int:
     ch = _host_i64(counts_host) if counts_host is not None else None
     return int(_lib.load().ts_decode_workspace_bytes(offs.host, ch, offs.B, int(Hq), int(Hkv), int(mode)))

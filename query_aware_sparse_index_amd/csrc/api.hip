@@ -177,6 +177,40 @@ int ts_select(const float* scores, const int64_t* offsets_dev, const int64_t* of
                       "ts_select launch");
 }
 
+size_t ts_score_select_workspace_bytes(const int64_t* offsets_host, int32_t B, int32_t Hq,
+                                       const ts_select_params* p) {
+    qasi::SelectConfig c;
+    if (!offsets_host || B <= 0 || Hq <= 0 || to_cfg(p, &c) != QASI_OK) return 0;
+    return qasi::score_select_workspace(offsets_host, B, Hq, c);
+}
+
+int ts_score_select(const uint16_t* q, const float* P, uint16_t* k_index, const uint16_t* K_last,
+                    const int64_t* offsets_dev, const int64_t* offsets_host, int32_t B, int32_t Hq, int32_t Hkv,
+                    const ts_select_params* p, float* scores, int32_t* idx_out, int64_t* count_out,
+                    float* theta_out, uint8_t* votes_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (!aligned16(q) || !aligned16(P) || !aligned16(k_index) || !aligned16(scores) || !aligned16(idx_out) ||
+        !aligned16(ws))
+        return fail(QASI_ERR_INVALID, "q, P, k_index, scores, idx_out and ws must be non-null and 16-byte aligned");
+    if (K_last && !aligned16(K_last)) return fail(QASI_ERR_INVALID, "K_last must be 16-byte aligned");
+    if (!count_out || (reinterpret_cast<uintptr_t>(count_out) & 7u))
+        return fail(QASI_ERR_INVALID, "count_out must be non-null and 8-byte aligned");
+    if (theta_out && (reinterpret_cast<uintptr_t>(theta_out) & 3u)) return fail(QASI_ERR_INVALID, "theta_out misaligned");
+    if (int r = check_heads(Hq, Hkv)) return r;
+    if (int r = check_offsets(offsets_dev, offsets_host, B, true)) return r;
+    for (int b = 0; b < B; ++b)
+        if (offsets_host[b + 1] - offsets_host[b] > ((int64_t)1 << 24))
+            return fail(QASI_ERR_UNSUPPORTED, "sequence %d longer than 2^24 tokens (selection limit)", b);
+    qasi::SelectConfig c;
+    if (int r = to_cfg(p, &c)) return r;
+    size_t need = qasi::score_select_workspace(offsets_host, B, Hq, c);
+    if (ws_bytes < need)
+        return fail(QASI_ERR_WORKSPACE, "ts_score_select needs %zu workspace bytes, got %zu", need, ws_bytes);
+    if (int r = init_once()) return r;
+    return hip_status(qasi::launch_score_select(q, P, k_index, K_last, offsets_dev, offsets_host, B, Hq, Hkv, c, scores,
+                                                idx_out, count_out, theta_out, votes_out, ws, ws_bytes, stream),
+                      "ts_score_select launch");
+}
+
 size_t ts_decode_workspace_bytes(const int64_t* offsets_host, const int64_t* counts_host, int32_t B, int32_t Hq,
                                  int32_t Hkv, int32_t mode) {
     if (!offsets_host || B <= 0 || Hq <= 0 || Hkv <= 0) return 0;

@@ -99,31 +99,36 @@ __device__ __forceinline__ bool find_item(const I64Arg& offsets, int B, int64_t 
 }
 
 // qp[(b * Hq + h) * 32 + c] = sum_j q[b][h][j] P[j][c] / sqrt(32): P and the block's
-// queries are staged in LDS with one round trip to memory, then thread (h, c) forms its
-// 128-term sum.
+// queries are staged in LDS with one round trip to memory; the sum is formed as four partial
+// sums over j in [32k, 32k + 32) (each in order) combined as ((s0 + s1) + (s2 + s3)), then
+// scaled.
 __global__ __launch_bounds__(1024) void qproj_kernel(const uint16_t* __restrict__ q, const float* __restrict__ P,
                                                     int Hq, float* __restrict__ qp) {
     __shared__ float sP[kD * kDP];
     __shared__ uint4 sq[64 * kD / 8];
+    __shared__ float spart[4][64 * kDP];
     const int b = blockIdx.x;
     const uint4* qb = reinterpret_cast<const uint4*>(q + (int64_t)b * Hq * kD);
     for (int i = threadIdx.x; i < kD * kDP / 4; i += 1024)
         reinterpret_cast<float4*>(sP)[i] = reinterpret_cast<const float4*>(P)[i];
     for (int i = threadIdx.x; i < Hq * kD / 8; i += 1024) sq[i] = qb[i];
     __syncthreads();
-    for (int o = threadIdx.x; o < Hq * kDP; o += 1024) {
-        const int h = o / kDP, c = o % kDP;
+    for (int o = threadIdx.x; o < 4 * Hq * kDP; o += 1024) {
+        const int k = o / (Hq * kDP), hc = o % (Hq * kDP), h = hc / kDP, c = hc % kDP;
         float acc = 0.f;
-#pragma unroll 4
-        for (int j8 = 0; j8 < kD / 8; ++j8) {
+#pragma unroll
+        for (int j8 = 4 * k; j8 < 4 * k + 4; ++j8) {
             const uint4 w = sq[h * (kD / 8) + j8];
             const float qv[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
                                  bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc = fmaf(qv[e], sP[(j8 * 8 + e) * kDP + c], acc);
         }
-        qp[(int64_t)b * Hq * kDP + o] = acc * 0.17677669529663688f;
+        spart[k][hc] = acc;
     }
+    __syncthreads();
+    for (int o = threadIdx.x; o < Hq * kDP; o += 1024)
+        qp[(int64_t)b * Hq * kDP + o] = ((spart[0][o] + spart[1][o]) + (spart[2][o] + spart[3][o])) * 0.17677669529663688f;
 }
 
 // Transposed quad reduction: v[hh] (hh < G) are this lane's partial sums; afterwards
@@ -163,11 +168,26 @@ __device__ __forceinline__ void quad_transpose_sum(float (&v)[G], int part) {
     }
 }
 
-template <int HKV, int G>
+// Tile classification against a key bracket (CLS): for every query head h of the tile's
+// sequence b whose instance (b, h) is active, over the tile's positions in [beg, end):
+//   tcnt[tile * Hq + h] = below | inside << 8 | offset << 16 (#keys below lo, #keys in [lo, hi],
+//                         offset of the head's keys in the tile's key run), one 128-byte line
+//                         per tile for Hq = 32;
+//   tcand[tile * kClsTile + offset + j], j < inside: the head's in-bracket keys, heads packed one
+//                         after the other, so a tile writes a few contiguous lines.
+// The bracket comes from ClsArgs::state[(b * Hq + h) * 8 + ...].
+struct ClsArgs {
+    const int64_t* state;
+    uint32_t* tcnt;
+    uint32_t* tcand;
+    int64_t ntiles;
+};
+
+template <int HKV, int G, bool CLS>
 __global__ __launch_bounds__(score_threads<HKV>()) void score_kernel(const float* __restrict__ qp,
                                                              const uint16_t* __restrict__ k_index,
                                                              I64Arg offsets, int B,
-                                                             float* __restrict__ scores) {
+                                                             float* __restrict__ scores, ClsArgs cls) {
     constexpr int NT = score_threads<HKV>();
     constexpr int Hq = HKV * G;
     constexpr int LPT = 4 * HKV;          // lanes per token
@@ -178,10 +198,26 @@ __global__ __launch_bounds__(score_threads<HKV>()) void score_kernel(const float
     constexpr int UNR = ITERS < 8 ? ITERS : 8;
     constexpr int NOUT = G >= 4 ? G / 4 : 1;          // complete heads per lane
     __shared__ float tile[Hq * kTileLd];
+    // bracket of every head of the tile's sequence (CLS): lo, hi, range [beg, end), active
+    __shared__ uint32_t s_lo[CLS ? Hq : 1], s_hi[CLS ? Hq : 1];
+    __shared__ int64_t s_beg[CLS ? Hq : 1], s_end[CLS ? Hq : 1];
+    __shared__ int s_act[CLS ? Hq : 1];
+    __shared__ uint32_t s_cnt[CLS ? Hq : 1], s_below[CLS ? Hq : 1];
 
     int b;
     int64_t t0, len;
     if (!find_item(offsets, B, blockIdx.x, kScoreTB, b, t0, len)) return;
+    // the heads' brackets (CLS)
+    if constexpr (CLS) {
+        if ((int)threadIdx.x < Hq) {
+            const int64_t* st = cls.state + ((int64_t)b * Hq + threadIdx.x) * 8;
+            s_act[threadIdx.x] = st[kStFlag] == 0;
+            s_lo[threadIdx.x] = (uint32_t)st[kStLo];
+            s_hi[threadIdx.x] = (uint32_t)st[kStHi];
+            s_beg[threadIdx.x] = st[kStBeg];
+            s_end[threadIdx.x] = st[kStEnd];
+        }
+    }
     const int64_t S = score_stride(offsets[B]);
     const int64_t base_tok = offsets[b] + t0;
 
@@ -240,6 +276,56 @@ __global__ __launch_bounds__(score_threads<HKV>()) void score_kernel(const float
         const int h = o / kScoreTB, tl = o % kScoreTB;
         if (tl < len) scores[(int64_t)h * S + base_tok + tl] = tile[h * kTileLd + tl];
     }
+    if constexpr (CLS) {
+        static_assert(kScoreTB == 64, "one wave lane per tile token");
+        // wave w takes heads w, w + NW, ...; lane = token of the tile.  Pass 1 counts, pass 2
+        // writes the keys at the heads' offsets (an exclusive scan of the counts over the heads).
+        constexpr int NW = NT / 64;
+        constexpr int HPW = (Hq + NW - 1) / NW;
+        const uint64_t lt = (1ull << lane) - 1ull;
+        uint64_t mm[HPW];
+        uint32_t key[HPW];
+#pragma unroll
+        for (int i = 0; i < HPW; ++i) {
+            const int h = wid + i * NW;
+            mm[i] = 0;
+            key[i] = 0;
+            if (h >= Hq) continue;
+            uint32_t below = 0;
+            if (s_act[h]) {                              // an active order statistic
+                const uint32_t lo = s_lo[h], hi = s_hi[h];
+                const int64_t t = t0 + lane;
+                const bool valid = lane < len && t >= s_beg[h] && t < s_end[h];
+                key[i] = order_key(tile[h * kTileLd + lane]);
+                below = (uint32_t)__popcll(__ballot(valid && key[i] < lo));
+                mm[i] = __ballot(valid && key[i] >= lo && key[i] <= hi);
+            }
+            if (lane == 0) {
+                s_cnt[h] = (uint32_t)__popcll(mm[i]);
+                s_below[h] = below;
+            }
+        }
+        __syncthreads();
+        // exclusive scan of the heads' counts (every wave, lanes < Hq)
+        uint32_t c = lane < Hq ? s_cnt[lane] : 0u;
+        uint32_t inc = c;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t y = __shfl_up(inc, o, 64);
+            if (lane >= o) inc += y;
+        }
+        const uint32_t ex = inc - c;
+        if (wid == 0 && lane < Hq)
+            cls.tcnt[(size_t)blockIdx.x * Hq + lane] = s_below[lane] | (c << 8) | (ex << 16);
+#pragma unroll
+        for (int i = 0; i < HPW; ++i) {
+            const int h = wid + i * NW;
+            if (h >= Hq) continue;
+            const uint32_t offh = __shfl(ex, h, 64);
+            if ((mm[i] >> lane) & 1ull)
+                cls.tcand[(size_t)blockIdx.x * kClsTile + offh + __popcll(mm[i] & lt)] = key[i];
+        }
+    }
 }
 
 int64_t score_items(const int64_t* offsets_host, int B) {
@@ -254,18 +340,32 @@ size_t score_workspace(int B, int Hq) {
     return w.size();
 }
 
-template <int HKV>
+template <int HKV, bool CLS>
 static hipError_t launch_score_g(int G, dim3 grid, hipStream_t stream, const float* qp, const uint16_t* k_index,
-                                 const I64Arg& offsets, int B, float* scores) {
+                                 const I64Arg& offsets, int B, float* scores, const ClsArgs& cls) {
     dim3 block(score_threads<HKV>());
     switch (G) {
-        case 1: hipLaunchKernelGGL((score_kernel<HKV, 1>), grid, block, 0, stream, qp, k_index, offsets, B, scores); break;
-        case 2: hipLaunchKernelGGL((score_kernel<HKV, 2>), grid, block, 0, stream, qp, k_index, offsets, B, scores); break;
-        case 4: hipLaunchKernelGGL((score_kernel<HKV, 4>), grid, block, 0, stream, qp, k_index, offsets, B, scores); break;
-        case 8: hipLaunchKernelGGL((score_kernel<HKV, 8>), grid, block, 0, stream, qp, k_index, offsets, B, scores); break;
+        case 1: hipLaunchKernelGGL((score_kernel<HKV, 1, CLS>), grid, block, 0, stream, qp, k_index, offsets, B, scores, cls); break;
+        case 2: hipLaunchKernelGGL((score_kernel<HKV, 2, CLS>), grid, block, 0, stream, qp, k_index, offsets, B, scores, cls); break;
+        case 4: hipLaunchKernelGGL((score_kernel<HKV, 4, CLS>), grid, block, 0, stream, qp, k_index, offsets, B, scores, cls); break;
+        case 8: hipLaunchKernelGGL((score_kernel<HKV, 8, CLS>), grid, block, 0, stream, qp, k_index, offsets, B, scores, cls); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+template <bool CLS>
+static hipError_t launch_score_tiles(const float* qp, const uint16_t* k_index, const I64Arg& offs, int64_t items,
+                                     int B, int Hq, int Hkv, float* scores, const ClsArgs& cls, hipStream_t stream) {
+    const dim3 grid((unsigned)items);
+    const int G = Hq / Hkv;
+    switch (Hkv) {
+        case 1: return launch_score_g<1, CLS>(G, grid, stream, qp, k_index, offs, B, scores, cls);
+        case 2: return launch_score_g<2, CLS>(G, grid, stream, qp, k_index, offs, B, scores, cls);
+        case 4: return launch_score_g<4, CLS>(G, grid, stream, qp, k_index, offs, B, scores, cls);
+        case 8: return launch_score_g<8, CLS>(G, grid, stream, qp, k_index, offs, B, scores, cls);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_score(const uint16_t* q, const float* P, const uint16_t* k_index, const int64_t* offsets_dev,
@@ -276,16 +376,19 @@ hipError_t launch_score(const uint16_t* q, const float* P, const uint16_t* k_ind
     hipLaunchKernelGGL(qproj_kernel, dim3(B), dim3(1024), 0, stream, q, P, Hq, qp);
     const int64_t items = score_items(offsets_host, B);
     if (items == 0) return hipGetLastError();
-    const dim3 grid((unsigned)items);
-    const int G = Hq / Hkv;
     const I64Arg offs = i64_arg(offsets_dev, offsets_host, (int64_t)B + 1);
-    switch (Hkv) {
-        case 1: return launch_score_g<1>(G, grid, stream, qp, k_index, offs, B, scores);
-        case 2: return launch_score_g<2>(G, grid, stream, qp, k_index, offs, B, scores);
-        case 4: return launch_score_g<4>(G, grid, stream, qp, k_index, offs, B, scores);
-        case 8: return launch_score_g<8>(G, grid, stream, qp, k_index, offs, B, scores);
-        default: return hipErrorInvalidValue;
-    }
+    return launch_score_tiles<false>(qp, k_index, offs, items, B, Hq, Hkv, scores, ClsArgs{}, stream);
+}
+
+// Scores plus the tile classification against the brackets in `state` (q' already in qp).
+hipError_t launch_score_classify(const float* qp, const uint16_t* k_index, const int64_t* offsets_dev,
+                                 const int64_t* offsets_host, int B, int Hq, int Hkv, float* scores,
+                                 const int64_t* state, uint32_t* tcnt, uint32_t* tcand, hipStream_t stream) {
+    const int64_t items = score_items(offsets_host, B);
+    if (items == 0) return hipSuccess;
+    const I64Arg offs = i64_arg(offsets_dev, offsets_host, (int64_t)B + 1);
+    return launch_score_tiles<true>(qp, k_index, offs, items, B, Hq, Hkv, scores, ClsArgs{state, tcnt, tcand, items},
+                                    stream);
 }
 
 }  // namespace qasi

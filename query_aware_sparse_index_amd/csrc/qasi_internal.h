@@ -36,7 +36,20 @@ hipError_t launch_score(const uint16_t* q, const float* P, const uint16_t* k_ind
                         const int64_t* offsets_host, int B, int Hq, int Hkv, float* scores, void* ws,
                         size_t ws_bytes, hipStream_t stream);
 
+// Scores plus the classification of every tile against per-instance key brackets (the fused
+// score-and-select path): q' is read from qp; see score_kernel.
+hipError_t launch_score_classify(const float* qp, const uint16_t* k_index, const int64_t* offsets_dev,
+                                 const int64_t* offsets_host, int B, int Hq, int Hkv, float* scores,
+                                 const int64_t* state, uint32_t* tcnt, uint32_t* tcand, hipStream_t stream);
+int64_t score_items(const int64_t* offsets_host, int B);
+
 // ---- selection
+// Per-instance state of an order statistic: int64 words at state[(b * Hq + h) * 8 + k].
+enum : int { kStFlag = 0, kStKey = 1, kStGt = 2, kStNeed = 3, kStLo = 4, kStHi = 5, kStBeg = 6, kStEnd = 7 };
+// Key run of a 64-token tile in the fused path's tile classification: at most 64 in-bracket
+// keys for each of at most 64 query heads.
+constexpr int kClsTile = 64 * 64;
+
 struct SelectConfig {
     int mode;
     int64_t bnum, bden, sink, local, vmin, tnum, tden;
@@ -46,6 +59,13 @@ hipError_t launch_select(const float* scores, int64_t S, const int64_t* offsets_
                          int B, int Hq, const SelectConfig& c, int32_t* idx_out, int64_t* count_out, float* theta_out,
                          uint8_t* votes_out, void* ws, size_t ws_bytes, hipStream_t stream);
 int64_t budget_tokens(int64_t n, const SelectConfig& c);
+// ts_score followed by ts_select in one pass (and, when K is given, the index row of every
+// sequence's last token appended first): identical scores, thresholds and lists.
+size_t score_select_workspace(const int64_t* offsets_host, int B, int Hq, const SelectConfig& c);
+hipError_t launch_score_select(const uint16_t* q, const float* P, uint16_t* k_index, const uint16_t* K,
+                               const int64_t* offsets_dev, const int64_t* offsets_host, int B, int Hq, int Hkv,
+                               const SelectConfig& c, float* scores, int32_t* idx_out, int64_t* count_out,
+                               float* theta_out, uint8_t* votes_out, void* ws, size_t ws_bytes, hipStream_t stream);
 // Top-k per row of a [rows][stride] fp32 array (n valid entries per row), ties to the lower
 // position, ascending output idx_out[r * k + j] (the per-head selection with no forced tokens).
 size_t rows_topk_workspace(int rows, int64_t n, int64_t k);

@@ -38,7 +38,9 @@ constexpr int kDelta = 96;         // bracket half-width in sample ranks
 constexpr int kDigit = 11;         // radix digit width of the final select
 constexpr int kDigitBins = 1 << kDigit;
 constexpr int kCap = 16384;        // keys of the answer's top digit resolved in LDS
+constexpr int kCapT = 24576;       // bracket keys ranked in LDS by the fused path's final kernel
 constexpr int kSlice = 8192;       // keys per collect block
+constexpr int kTilesPerSlice = kSlice / 64;   // 64-token tiles per slice of the fused path
 constexpr int kColThreads = 512;
 constexpr int kMaxSL = 2048;       // slices per instance (n up to 2^24 tokens)
 constexpr int kChunk = 1024;       // tokens per vote / compaction block
@@ -46,8 +48,6 @@ constexpr int kVoteBins = 72;      // vote keys 0 .. Hq + 1 (Hq <= 64)
 
 enum : int64_t { kFlagActive = 0, kFlagTakeNone = 1, kFlagTakeAll = 2 };
 
-// state[inst * 8 + k]
-enum { kStFlag = 0, kStKey = 1, kStGt = 2, kStNeed = 3, kStLo = 4, kStHi = 5 };
 
 struct DevCfg {
     int mode;
@@ -127,26 +127,44 @@ __host__ __device__ __forceinline__ int top_shift(uint32_t span) {
     return nbits > kDigit ? nbits - kDigit : 0;
 }
 
-// Key bracket [lo, hi] of an instance whose row (m keys) is longer than kCap; every thread of
-// the block calls it and every block of the instance computes the same result.  Run j of the
-// sample starts at a hashed position of stratum [j m / kRuns, (j + 1) m / kRuns); the
-// sample's [min, max] is cut into kSampleBins equal bins; lo is the lower edge of the bin
-// before the one holding sample rank ir - kDelta and hi the upper edge of the bin after the one
-// holding ir + kDelta (the key range's ends when these leave the sample), ir the target's
-// expected sample rank.  `hist` (kSampleBins words) is left dirty.
+// Position (relative to the range start) of sample i of an instance over a range of m keys:
+// run j = i / kRunLen starts at a hashed position of stratum [j m / kRuns, (j + 1) m / kRuns).
+// Needs m >= kRuns * kRunLen.
+__device__ __forceinline__ int64_t sample_pos(int i, int64_t m, int inst) {
+    const int j = i / kRunLen;
+    const int64_t a = (int64_t)j * m / kRuns, e = (int64_t)(j + 1) * m / kRuns;
+    const uint32_t r = mix32((uint32_t)j * 0x9e3779b9u ^ mix32((uint32_t)inst + 0x632be5abu));
+    return a + (int64_t)(r % (uint32_t)(e - a - kRunLen + 1)) + (i % kRunLen);
+}
+
+template <int NS, int DELTA>
+__device__ void bracket_of_sample(const float (&v)[NS / kColThreads], const OsInst& oi, uint32_t* hist,
+                                  float* wmin, float* wmax, int* tmp, int* sb, uint32_t& klo, uint32_t& khi);
+
+// Key bracket [lo, hi] of an instance whose row (m keys) is longer than kCap, from the sampled
+// scores of the row; every thread of the block calls it and every block of the instance computes
+// the same result.
 __device__ void sample_bracket(const float* __restrict__ row, const OsInst& oi, int inst, uint32_t* hist,
                                float* wmin, float* wmax, int* tmp, int* sb, uint32_t& klo, uint32_t& khi) {
-    constexpr int NW = kColThreads / 64;
     constexpr int PER = kSample / kColThreads;
     const int64_t m = oi.end - oi.beg;
     float v[PER];
 #pragma unroll
-    for (int u = 0; u < PER; ++u) {
-        const int i = threadIdx.x + u * kColThreads, j = i / kRunLen;
-        const int64_t a = (int64_t)j * m / kRuns, e = (int64_t)(j + 1) * m / kRuns;
-        const uint32_t r = mix32((uint32_t)j * 0x9e3779b9u ^ mix32((uint32_t)inst + 0x632be5abu));
-        v[u] = row[oi.beg + a + (int64_t)(r % (uint32_t)(e - a - kRunLen + 1)) + (i % kRunLen)];
-    }
+    for (int u = 0; u < PER; ++u) v[u] = row[oi.beg + sample_pos(threadIdx.x + u * kColThreads, m, inst)];
+    bracket_of_sample<kSample, kDelta>(v, oi, hist, wmin, wmax, tmp, sb, klo, khi);
+}
+
+// The bracket [klo, khi] from the NS sample values v (PER per thread): the sample's [min, max]
+// is cut into kSampleBins equal bins; lo is the lower edge of the bin before the one holding
+// sample rank ir - DELTA and hi the upper edge of the bin after the one holding ir + DELTA (the
+// key range's ends when these leave the sample), ir the target's expected sample rank.  Every
+// thread of the block calls it; `hist` (kSampleBins words) is left dirty.
+template <int NS, int DELTA>
+__device__ void bracket_of_sample(const float (&v)[NS / kColThreads], const OsInst& oi, uint32_t* hist,
+                                  float* wmin, float* wmax, int* tmp, int* sb, uint32_t& klo, uint32_t& khi) {
+    constexpr int NW = kColThreads / 64;
+    constexpr int PER = NS / kColThreads;
+    const int64_t m = oi.end - oi.beg;
     for (int i = threadIdx.x; i < kSampleBins; i += kColThreads) hist[i] = 0;
     float mn = v[0], mx = v[0];
 #pragma unroll
@@ -161,8 +179,8 @@ __device__ void sample_bracket(const float* __restrict__ row, const OsInst& oi, 
     mx = wmax[0];
 #pragma unroll
     for (int w = 1; w < NW; ++w) { mn = fminf(mn, wmin[w]); mx = fmaxf(mx, wmax[w]); }
-    const int64_t ir = (oi.rank - 1) * kSample / m;
-    const int64_t il = ir - kDelta, ih = ir + kDelta;
+    const int64_t ir = (oi.rank - 1) * NS / m;
+    const int64_t il = ir - DELTA, ih = ir + DELTA;
     klo = 0u;
     khi = 0xffffffffu;
     if (mx > mn) {
@@ -192,7 +210,7 @@ __device__ void sample_bracket(const float* __restrict__ row, const OsInst& oi, 
         __syncthreads();
         const float w = (mx - mn) / (float)kSampleBins;
         if (il > 0) klo = order_key(mn + (float)(sb[0] - 1) * w);
-        if (ih < kSample - 1) khi = order_key(mn + (float)(sb[1] + 2) * w);
+        if (ih < NS - 1) khi = order_key(mn + (float)(sb[1] + 2) * w);
     } else {
         klo = khi = order_key(mn);
     }
@@ -366,7 +384,8 @@ __global__ __launch_bounds__(kThThreads) void th_final_kernel(const float* __res
                                                              const uint32_t* __restrict__ cand,
                                                              const uint32_t* __restrict__ cnt,
                                                              const uint32_t* __restrict__ dpre,
-                                                             int64_t* __restrict__ state, float* __restrict__ theta_out) {
+                                                             int64_t* __restrict__ state, float* __restrict__ theta_out,
+                                                             int tiles) {
     static_assert(kDigitBins / 2 == kThThreads, "one pair of digit bins per thread");
     __shared__ uint32_t xs[kCap];
     __shared__ int segpre[kMaxSL + 1], sega[kMaxSL];
@@ -414,7 +433,9 @@ __global__ __launch_bounds__(kThThreads) void th_final_kernel(const float* __res
         return;
     }
     const int64_t m = oi.end - oi.beg;
-    const int nsl = (int)((m + kSlice - 1) / kSlice);
+    // slices: of the key range [beg, end), or of the sequence's tiles (tile classification)
+    const int nsl = tiles ? (int)(((nrow + 63) / 64 + kTilesPerSlice - 1) / kTilesPerSlice)
+                          : (int)((m + kSlice - 1) / kSlice);
     int lsum = 0, csum = 0;
 #pragma unroll
     for (int u = 0; u < 2; ++u)
@@ -570,6 +591,230 @@ __global__ __launch_bounds__(kThThreads) void th_final_kernel(const float* __res
         st[kStKey] = key;
         st[kStGt] = gt;
         if (theta_out) theta_out[inst] = key_to_float(key);
+    }
+}
+
+// ------------------------------------------------- fused score-and-select: prep, final
+// prep_kernel, block (b, h) of the B*Hq instance blocks: q'_{b,h} = P^T q_{b,h} / sqrt(32) in
+// the order of qproj_kernel (so the scores equal those of ts_score), then the instance's key
+// bracket from kPrepSample sampled index scores (rows longer than kCap; otherwise every key is a
+// candidate), and the instance state (flag, need, bracket, range).  When K is given, block
+// B*Hq + b first writes the index row of sequence b's last token (the token appended by this
+// decode step) exactly as index_append_kernel does; the samples never read that row.
+constexpr int kPrepThreads = kColThreads;
+constexpr int kPrepSample = 1024;  // sampled index scores per instance (runs of kRunLen tokens)
+constexpr int kPrepDelta = 48;     // bracket half-width in sample ranks (about 5 standard deviations)
+static_assert(kPrepSample % (kPrepThreads / 4) == 0 && kPrepSample % kColThreads == 0, "whole sample passes");
+__global__ __launch_bounds__(kPrepThreads) void prep_kernel(const uint16_t* __restrict__ q, const float* __restrict__ P,
+                                                           uint16_t* k_index, const uint16_t* __restrict__ K,
+                                                           I64Arg offsets, int B, int Hq, int Hkv, DevCfg cfg,
+                                                           float* __restrict__ qp, int64_t* __restrict__ state) {
+    constexpr int NW = kPrepThreads / 64;
+    constexpr int PASSES = kPrepSample / (kPrepThreads / 4);
+    __shared__ float sP[kD * kDP];
+    __shared__ float sk[8][kD];
+    __shared__ float sq[kD];
+    __shared__ float sqp[kDP];
+    __shared__ float samp[kPrepSample];
+    __shared__ float spart[4][kDP];
+    __shared__ uint32_t hist[kSampleBins];
+    __shared__ float wmin[NW], wmax[NW];
+    __shared__ int tmp[NW];
+    __shared__ int sb[2];
+    const int ninst = B * Hq;
+    const int t = threadIdx.x;
+    if ((int)blockIdx.x >= ninst) {
+        // index row of the last token of sequence b, (g, c) = (t / 32, t % 32), fp64 sum in order
+        const int b = blockIdx.x - ninst;
+        const int64_t tok = offsets[b + 1] - 1;
+        if (tok < offsets[b]) return;
+        for (int i = t; i < kD * kDP / 4; i += kPrepThreads)
+            reinterpret_cast<float4*>(sP)[i] = reinterpret_cast<const float4*>(P)[i];
+        for (int i = t; i < Hkv * kD; i += kPrepThreads) sk[i / kD][i % kD] = bf16_to_f32(K[tok * Hkv * kD + i]);
+        __syncthreads();
+        if (t < Hkv * kDP) {
+            const int g = t / kDP, c = t % kDP;
+            double acc = 0.0;
+#pragma unroll 16
+            for (int j = 0; j < kD; ++j) acc = fma((double)sk[g][j], (double)sP[j * kDP + c], acc);
+            k_index[(tok * Hkv + g) * kDP + c] = f64_to_bf16_rne(acc);
+        }
+        return;
+    }
+    const int inst = blockIdx.x, b = inst / Hq, h = inst % Hq, g = h / (Hq / Hkv);
+    const int64_t off = offsets[b], n = offsets[b + 1] - off;
+    const OsInst oi = os_instance(n, cfg);
+    // the sample range leaves out the token appended by this step
+    const int64_t send = (K && oi.end == n) ? n - 1 : oi.end;
+    const int64_t ms = send - oi.beg;
+    const bool sampled = oi.flag == kFlagActive && oi.end - oi.beg > kCap && ms >= kRuns * kRunLen;
+    static_assert(kPrepSample / kRunLen <= kRuns, "sample runs within the strata of sample_pos");
+    const int part = t & 3;
+    uint4 kv[PASSES];
+    if (sampled) {
+#pragma unroll
+        for (int u = 0; u < PASSES; ++u) {
+            const int i = u * (kPrepThreads / 4) + (t >> 2);
+            const int64_t pos = oi.beg + sample_pos(i, ms, inst);
+            kv[u] = ld16(k_index + ((off + pos) * Hkv + g) * kDP + part * 8);
+        }
+    }
+    for (int i = t; i < kD * kDP / 4; i += kPrepThreads)
+        reinterpret_cast<float4*>(sP)[i] = reinterpret_cast<const float4*>(P)[i];
+    for (int j = t; j < kD; j += kPrepThreads) sq[j] = bf16_to_f32(q[((int64_t)b * Hq + h) * kD + j]);
+    __syncthreads();
+    if (t < 4 * kDP) {
+        // partial k of q'[c] over j in [32k, 32k + 32), in order (the order of qproj_kernel)
+        const int c = t % kDP, k = t / kDP;
+        float acc = 0.f;
+#pragma unroll
+        for (int j = 32 * k; j < 32 * k + 32; ++j) acc = fmaf(sq[j], sP[j * kDP + c], acc);
+        spart[k][c] = acc;
+    }
+    __syncthreads();
+    if (t < kDP) {
+        const float acc = ((spart[0][t] + spart[1][t]) + (spart[2][t] + spart[3][t])) * 0.17677669529663688f;
+        sqp[t] = acc;
+        qp[(int64_t)inst * kDP + t] = acc;
+    }
+    __syncthreads();
+    uint32_t klo = 0u, khi = 0xffffffffu;
+    if (sampled) {
+        float qr[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qr[e] = sqp[part * 8 + e];
+#pragma unroll
+        for (int u = 0; u < PASSES; ++u) {
+            const uint4 w = kv[u];
+            const float kf[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
+                                 bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
+            float sdot = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sdot = fmaf(qr[e], kf[e], sdot);
+            sdot = sum_quad(sdot);
+            if (part == 0) samp[u * (kPrepThreads / 4) + (t >> 2)] = sdot;
+        }
+        __syncthreads();
+        float v[kPrepSample / kColThreads];
+#pragma unroll
+        for (int u = 0; u < kPrepSample / kColThreads; ++u) v[u] = samp[t + u * kColThreads];
+        bracket_of_sample<kPrepSample, kPrepDelta>(v, oi, hist, wmin, wmax, tmp, sb, klo, khi);
+    }
+    if (t == 0) {
+        int64_t* st = state + (int64_t)inst * 8;
+        st[kStFlag] = oi.flag;
+        st[kStNeed] = oi.need;
+        st[kStLo] = klo;
+        st[kStHi] = khi;
+        st[kStBeg] = oi.beg;
+        st[kStEnd] = oi.end;
+    }
+}
+
+// Block (slice s, instance): the collect step of the order statistic from the tile
+// classification of the score kernel.  Slice s of an instance is the tiles
+// [s kTilesPerSlice, (s+1) kTilesPerSlice) of its sequence (the key range of th_collect_kernel's
+// slices, cut at tile boundaries).  The block sums the tiles' counts below the bracket, loads
+// their in-bracket keys (slots < kCtS of four tiles per wave load instruction; a tile with more
+// keys has its owning thread copy the rest) and writes the same outputs as th_collect_kernel:
+// the keys grouped by their top digit, the 16-bit digit prefixes and counts, and the slice's
+// (below, inside) counts.  The bracket and the instance state come from prep_kernel.
+constexpr int kCtS = 16;
+__global__ __launch_bounds__(kColThreads) void th_collect_tiles_kernel(I64Arg offsets, int Hq, DevCfg cfg, int SL,
+                                                                      const int64_t* __restrict__ state,
+                                                                      const uint32_t* __restrict__ tcnt,
+                                                                      const uint32_t* __restrict__ tcand,
+                                                                      uint32_t* __restrict__ cand,
+                                                                      uint32_t* __restrict__ cnt,
+                                                                      uint32_t* __restrict__ dpre) {
+    constexpr int NW = kColThreads / 64;
+    constexpr int BPT = kDigitBins / kColThreads;              // digit bins per thread in the scan
+    constexpr int TPP = kColThreads / kCtS;                    // tiles per load pass
+    constexpr int PASSES = kTilesPerSlice / TPP;
+    static_assert(kTilesPerSlice <= kColThreads && kTilesPerSlice % TPP == 0, "slice tiles per block");
+    __shared__ int wsum[NW];
+    __shared__ int tmp[NW];
+    __shared__ uint32_t hist[kDigitBins];                      // digit counts, then cursors
+    __shared__ int scn[kTilesPerSlice], sof[kTilesPerSlice];
+    const int inst = blockIdx.y, s = blockIdx.x, t = threadIdx.x;
+    const int b = inst / Hq, h = inst % Hq;
+    const int64_t n = offsets[b + 1] - offsets[b];
+    const OsInst oi = os_instance(n, cfg);
+    if (oi.flag != kFlagActive) return;
+    int64_t tf = 0;
+    for (int i = 0; i < b; ++i) tf += (offsets[i + 1] - offsets[i] + 63) / 64;
+    const int64_t nt = (n + 63) / 64;
+    const int64_t* st = state + (int64_t)inst * 8;
+    const uint32_t klo = (uint32_t)st[kStLo], khi = (uint32_t)st[kStHi];
+    const int64_t a0 = (int64_t)s * kTilesPerSlice;            // first tile of the slice
+    uint32_t cw = 0;
+    if (t < kTilesPerSlice && a0 + t < nt) cw = tcnt[(size_t)(tf + a0 + t) * Hq + h];
+    const int cy = (int)((cw >> 8) & 0xffu), cof = (int)(cw >> 16);
+    for (int i = t; i < kDigitBins; i += kColThreads) hist[i] = 0;
+    if (t < kTilesPerSlice) {
+        scn[t] = cy;
+        sof[t] = cof;
+    }
+    __syncthreads();
+    const uint32_t* tk = tcand + (size_t)(tf + a0) * kClsTile;
+    // the slice's in-bracket keys: pass p, lane -> (tile p TPP + t / kCtS, slot t % kCtS)
+    const int dsh = top_shift(khi - klo);
+    uint32_t kv[PASSES];
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+        const int tl = p * TPP + t / kCtS, sl = t % kCtS;
+        kv[p] = sl < scn[tl] ? tk[(size_t)tl * kClsTile + sof[tl] + sl] : 0u;
+    }
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+        const int tl = p * TPP + t / kCtS, sl = t % kCtS;
+        if (sl < scn[tl]) atomicAdd(&hist[(kv[p] - klo) >> dsh], 1u);
+    }
+    // rare: keys past the first kCtS of a tile
+    if (t < kTilesPerSlice)
+        for (int i = kCtS; i < cy; ++i) atomicAdd(&hist[(tk[(size_t)t * kClsTile + cof + i] - klo) >> dsh], 1u);
+    const int below = wave_sum_i((int)(cw & 0xffu));
+    if ((t & 63) == 0) wsum[t >> 6] = below;
+    __syncthreads();
+    // exclusive prefix over the digits (BPT consecutive bins per thread)
+    uint32_t cc[BPT];
+    int csum = 0;
+#pragma unroll
+    for (int u = 0; u < BPT; ++u) { cc[u] = hist[t * BPT + u]; csum += (int)cc[u]; }
+    int total;
+    const int incl = block_inclusive_scan<kColThreads>(csum, tmp, &total);
+    uint32_t* dp = dpre + ((size_t)inst * SL + s) * kDpWords;
+    {
+#pragma unroll
+        for (int u = 0; u < BPT; u += 2) dp[kPreWords + (t * BPT + u) / 2] = cc[u] | (cc[u + 1] << 16);
+        uint32_t acc = (uint32_t)(incl - csum);
+        uint32_t pre[BPT];
+#pragma unroll
+        for (int u = 0; u < BPT; ++u) { pre[u] = acc; acc += cc[u]; }
+#pragma unroll
+        for (int u = 0; u < BPT; u += 2) dp[(t * BPT + u) / 2] = pre[u] | (pre[u + 1] << 16);
+#pragma unroll
+        for (int u = 0; u < BPT; ++u) hist[t * BPT + u] = pre[u];   // cursor
+        if (t == 0) dp[kDigitBins / 2] = (uint32_t)total;
+    }
+    __syncthreads();
+    // scatter the keys to their digit's range
+    uint32_t* dst = cand + ((size_t)inst * SL + s) * kSlice;
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+        const int tl = p * TPP + t / kCtS, sl = t % kCtS;
+        if (sl < scn[tl]) dst[atomicAdd(&hist[(kv[p] - klo) >> dsh], 1u)] = kv[p];
+    }
+    if (t < kTilesPerSlice)
+        for (int i = kCtS; i < cy; ++i) {
+            const uint32_t k = tk[(size_t)t * kClsTile + cof + i];
+            dst[atomicAdd(&hist[(k - klo) >> dsh], 1u)] = k;
+        }
+    if (t == 0) {
+        int tb = 0;
+        for (int w = 0; w < NW; ++w) tb += wsum[w];
+        cnt[((size_t)inst * SL + s) * 2 + 0] = (uint32_t)tb;
+        cnt[((size_t)inst * SL + s) * 2 + 1] = (uint32_t)total;
     }
 }
 
@@ -1004,34 +1249,59 @@ static DevCfg dev_cfg(const SelectConfig& c) {
 
 struct SelectLayout {
     int SL;
-    int64_t nitems, ph_items, Ntot;
+    int64_t nitems, ph_items, Ntot, ntiles;
     uint32_t *cand, *cnt, *dhist, *hist, *phcnt;
     int64_t* state;
     uint8_t *votes, *keys;
+    float* qp;          // fused path: q' per (sequence, head)
+    uint32_t* tcnt;     // fused path: per (tile, head) counts below / inside the bracket, key offset
+    uint32_t* tcand;    // fused path: per tile the heads' keys inside the bracket
     size_t bytes;
 };
 
-static SelectLayout select_layout(void* ws, const int64_t* offsets_host, int B, int Hq, const SelectConfig& c) {
+// fused: the score-and-select path (tile classification instead of the slice candidates).
+static SelectLayout select_layout(void* ws, const int64_t* offsets_host, int B, int Hq, const SelectConfig& c,
+                                  bool fused = false) {
     SelectLayout L;
     DevCfg d = dev_cfg(c);
-    int64_t maxm = 0, items = 0, ph_items = 0;
+    int64_t maxm = 0, items = 0, ph_items = 0, tiles = 0;
     for (int b = 0; b < B; ++b) {
         int64_t n = offsets_host[b + 1] - offsets_host[b];
         OsInst o = os_instance(n, d);
         if (o.end - o.beg > maxm) maxm = o.end - o.beg;
         items += (n + kChunk - 1) / kChunk;
         ph_items += (n + kPhChunk - 1) / kPhChunk;
+        tiles += (n + 63) / 64;
     }
     L.ph_items = ph_items;
     L.SL = (int)((maxm + kSlice - 1) / kSlice);
+    if (fused) {
+        // slices of whole tiles: the longest sequence's tile count
+        int64_t maxt = 0;
+        for (int b = 0; b < B; ++b) {
+            const int64_t nt = (offsets_host[b + 1] - offsets_host[b] + 63) / 64;
+            if (nt > maxt) maxt = nt;
+        }
+        L.SL = (int)((maxt + kTilesPerSlice - 1) / kTilesPerSlice);
+    }
     if (L.SL < 1) L.SL = 1;
     L.nitems = items;
+    L.ntiles = tiles;
     L.Ntot = offsets_host[B];
     WsCarver w(ws);
     const size_t inst = (size_t)B * Hq;
+    L.cand = L.cnt = L.dhist = nullptr;
+    L.qp = nullptr;
+    L.tcnt = nullptr;
+    L.tcand = nullptr;
     L.cand = w.take<uint32_t>(inst * L.SL * kSlice);
     L.cnt = w.take<uint32_t>(inst * L.SL * 2);
     L.dhist = w.take<uint32_t>(inst * L.SL * kDpWords);
+    if (fused) {
+        L.qp = w.take<float>(inst * kDP);
+        L.tcnt = w.take<uint32_t>((size_t)Hq * tiles);
+        L.tcand = w.take<uint32_t>((size_t)tiles * kClsTile);
+    }
     L.state = w.take<int64_t>(inst * 8);
     L.votes = w.take<uint8_t>((size_t)L.Ntot + 16);
     L.keys = w.take<uint8_t>((size_t)L.Ntot + 16);
@@ -1045,18 +1315,16 @@ size_t select_workspace(const int64_t* offsets_host, int B, int Hq, const Select
     return select_layout(nullptr, offsets_host, B, Hq, c).bytes;
 }
 
-hipError_t launch_select(const float* scores, int64_t S, const int64_t* offsets_dev, const int64_t* offsets_host,
-                         int B, int Hq, const SelectConfig& c, int32_t* idx_out, int64_t* count_out, float* theta_out,
-                         uint8_t* votes_out, void* ws, size_t ws_bytes, hipStream_t stream) {
-    SelectLayout L = select_layout(ws, offsets_host, B, Hq, c);
-    if (L.bytes > ws_bytes || L.SL > kMaxSL) return hipErrorInvalidValue;
+size_t score_select_workspace(const int64_t* offsets_host, int B, int Hq, const SelectConfig& c) {
+    return select_layout(nullptr, offsets_host, B, Hq, c, true).bytes;
+}
+
+// Votes and the ordered compaction (vote mode) or the per-head compaction, once the order
+// statistics are in the state.
+static hipError_t launch_select_tail(const SelectLayout& L, const float* scores, int64_t S, const I64Arg& offs,
+                                     int B, int Hq, const SelectConfig& c, int32_t* idx_out, int64_t* count_out,
+                                     uint8_t* votes_out, hipStream_t stream) {
     DevCfg d = dev_cfg(c);
-    const unsigned inst = (unsigned)(B * Hq);
-    const I64Arg offs = i64_arg(offsets_dev, offsets_host, (int64_t)B + 1);
-    hipLaunchKernelGGL(th_collect_kernel, dim3(L.SL, inst), dim3(kColThreads), 0, stream, scores, offs, Hq, d,
-                       L.SL, S, L.state, L.cand, L.cnt, L.dhist);
-    hipLaunchKernelGGL(th_final_kernel, dim3(inst), dim3(kThThreads), 0, stream, scores, offs, Hq, d, L.SL, S,
-                       L.cand, L.cnt, L.dhist, L.state, c.mode == 0 ? theta_out : nullptr);
     if (L.nitems == 0) return hipGetLastError();
     if (c.mode == 0) {
         uint8_t* votes = votes_out ? votes_out : L.votes;
@@ -1073,6 +1341,43 @@ hipError_t launch_select(const float* scores, int64_t S, const int64_t* offsets_
                            offs, B, Hq, d, S, L.state, L.ph_items, L.phcnt, idx_out, count_out);
     }
     return hipGetLastError();
+}
+
+hipError_t launch_select(const float* scores, int64_t S, const int64_t* offsets_dev, const int64_t* offsets_host,
+                         int B, int Hq, const SelectConfig& c, int32_t* idx_out, int64_t* count_out, float* theta_out,
+                         uint8_t* votes_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+    SelectLayout L = select_layout(ws, offsets_host, B, Hq, c);
+    if (L.bytes > ws_bytes || L.SL > kMaxSL) return hipErrorInvalidValue;
+    DevCfg d = dev_cfg(c);
+    const unsigned inst = (unsigned)(B * Hq);
+    const I64Arg offs = i64_arg(offsets_dev, offsets_host, (int64_t)B + 1);
+    hipLaunchKernelGGL(th_collect_kernel, dim3(L.SL, inst), dim3(kColThreads), 0, stream, scores, offs, Hq, d,
+                       L.SL, S, L.state, L.cand, L.cnt, L.dhist);
+    hipLaunchKernelGGL(th_final_kernel, dim3(inst), dim3(kThThreads), 0, stream, scores, offs, Hq, d, L.SL, S,
+                       L.cand, L.cnt, L.dhist, L.state, c.mode == 0 ? theta_out : nullptr, 0);
+    return launch_select_tail(L, scores, S, offs, B, Hq, c, idx_out, count_out, votes_out, stream);
+}
+
+hipError_t launch_score_select(const uint16_t* q, const float* P, uint16_t* k_index, const uint16_t* K,
+                               const int64_t* offsets_dev, const int64_t* offsets_host, int B, int Hq, int Hkv,
+                               const SelectConfig& c, float* scores, int32_t* idx_out, int64_t* count_out,
+                               float* theta_out, uint8_t* votes_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+    SelectLayout L = select_layout(ws, offsets_host, B, Hq, c, true);
+    if (L.bytes > ws_bytes || L.SL > kMaxSL) return hipErrorInvalidValue;
+    DevCfg d = dev_cfg(c);
+    const unsigned inst = (unsigned)(B * Hq);
+    const I64Arg offs = i64_arg(offsets_dev, offsets_host, (int64_t)B + 1);
+    const int64_t S = score_stride(offsets_host[B]);
+    hipLaunchKernelGGL(prep_kernel, dim3(inst + (K ? B : 0)), dim3(kPrepThreads), 0, stream, q, P, k_index, K, offs,
+                       B, Hq, Hkv, d, L.qp, L.state);
+    hipError_t e = launch_score_classify(L.qp, k_index, offsets_dev, offsets_host, B, Hq, Hkv, scores, L.state, L.tcnt,
+                                         L.tcand, stream);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(th_collect_tiles_kernel, dim3(L.SL, inst), dim3(kColThreads), 0, stream, offs, Hq, d, L.SL,
+                       L.state, L.tcnt, L.tcand, L.cand, L.cnt, L.dhist);
+    hipLaunchKernelGGL(th_final_kernel, dim3(inst), dim3(kThThreads), 0, stream, scores, offs, Hq, d, L.SL, S,
+                       L.cand, L.cnt, L.dhist, L.state, c.mode == 0 ? theta_out : nullptr, 1);
+    return launch_select_tail(L, scores, S, offs, B, Hq, c, idx_out, count_out, votes_out, stream);
 }
 
 // ------------------------------------------------------------- row-wise top-k

@@ -107,3 +107,37 @@ def check_staged(st: Step, decode_tol=2e-3):
     err = float(np.abs(f64(st.out) - out_ref).max())
     assert err <= decode_tol, f"decode max abs error {err}"
     return {"decode_err": err, "score_err": float(np.abs(sc - ref).max())}
+
+
+class FusedStep(Step):
+    """The same step through ts_score_select: the index of every sequence's last token is
+    appended by the call itself (K_last), the rest of the index is built beforehand."""
+
+    def run(self):
+        kidx = torch.empty((self.n, self.Hkv, 32), dtype=torch.int16, device=dev())
+        offs = self.x.offsets
+        for b in range(len(offs) - 1):
+            a, e = int(offs[b]), int(offs[b + 1])
+            if e - 1 > a:
+                api.index_append(self.K[a:e - 1], self.P, kidx[a:e - 1], 0)
+        self.kidx = kidx
+        self.sel = api.score_select(self.q, self.P, kidx, self.offs, self.Hkv, self.p, K_last=self.K,
+                                    want_theta=True, want_votes=True)
+        self.scores = self.sel["scores"]
+        self.out = api.sparse_decode(self.q, self.K, self.V, self.offs, self.sel["idx"], self.sel["count"],
+                                     self.sel["counts_host"], self.mode)
+        torch.cuda.synchronize()
+        return self
+
+
+def assert_same_step(a: Step, b: Step):
+    """Two runs of a step agree bit for bit: index, scores, thresholds, votes, lists, output."""
+    n = a.n
+    assert torch.equal(a.kidx, b.kidx), "index differs"
+    assert torch.equal(a.scores[:, :n], b.scores[:, :n]), "scores differ"
+    assert torch.equal(a.sel["count"], b.sel["count"])
+    assert torch.equal(a.sel["idx"], b.sel["idx"]), "lists differ"
+    if a.mode == api.MODE_VOTE:
+        assert torch.equal(a.sel["theta"], b.sel["theta"]), "thresholds differ"
+        assert torch.equal(a.sel["votes"], b.sel["votes"]), "votes differ"
+    assert torch.equal(a.out, b.out), "decode output differs"

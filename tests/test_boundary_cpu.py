@@ -22,7 +22,7 @@ def header_functions():
 def test_exports_match_header():
     lib = _lib.load()
     names = header_functions()
-    assert len(names) == 13, names
+    assert len(names) == 15, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.SIGNATURES)
@@ -104,6 +104,29 @@ def test_select_validation():
     assert L.ts_select(FAKE, FAKE, o, 1, 8, 2, ctypes.byref(p), FAKE, FAKE, None, None, FAKE, need - 1, None) == -3
     assert "workspace" in err()
     assert L.ts_select(FAKE, FAKE, o, 1, 8, 2, None, FAKE, FAKE, None, None, FAKE, need, None) == -1
+
+
+def test_score_select_validation():
+    L = _lib.load()
+    o = _offs([0, 4096])
+    args = lambda p, kl, ws: (FAKE, FAKE, FAKE, kl, FAKE, o, 1, 8, 2, ctypes.byref(p) if p else None, FAKE, FAKE, FAKE,
+                              None, None, FAKE, ws, None)
+    for p, code in [(_params(mode=2), -1), (_params(bden=0), -1), (_params(tn=11, td=10), -1), (_params(vmin=-1), -1)]:
+        assert L.ts_score_select(*args(p, None, 1 << 40)) == code
+    p = _params()
+    assert L.ts_score_select(*args(None, None, 1 << 40)) == -1
+    assert L.ts_score_select(*args(p, MIS, 1 << 40)) == -1
+    need = L.ts_score_select_workspace_bytes(o, 1, 8, ctypes.byref(p))
+    assert need > 0
+    assert L.ts_score_select(*args(p, FAKE, need - 1)) == -3
+    assert "workspace" in err()
+    a = list(args(p, None, need))
+    a[7], a[8] = 12, 8           # G = 1.5
+    assert L.ts_score_select(*a) == -2
+    a = list(args(p, None, need))
+    a[5] = _offs([0, 10, 5])
+    a[6] = 2
+    assert L.ts_score_select(*a) == -1
 
 
 def test_decode_validation():
