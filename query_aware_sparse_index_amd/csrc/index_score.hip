@@ -171,10 +171,11 @@ __device__ __forceinline__ void quad_transpose_sum(float (&v)[G], int part) {
 // Tile classification against a key bracket (CLS): for every query head h of the tile's
 // sequence b whose instance (b, h) is active, over the tile's positions in [beg, end):
 //   tcnt[tile * Hq + h] = below | inside << 8 | offset << 16 (#keys below lo, #keys in [lo, hi],
-//                         offset of the head's keys in the tile's key run), one 128-byte line
+//                         offset of the head's keys in the tile's key area), one 128-byte line
 //                         per tile for Hq = 32;
-//   tcand[tile * kClsTile + offset + j], j < inside: the head's in-bracket keys, heads packed one
-//                         after the other, so a tile writes a few contiguous lines.
+//   tcand[tile * kClsTile + offset + j], j < inside: the head's in-bracket keys, the heads' runs
+//                         packed one after the other (in the order they reserve them), so a tile
+//                         writes a few contiguous lines.
 // The bracket comes from ClsArgs::state[(b * Hq + h) * 8 + ...].
 struct ClsArgs {
     const int64_t* state;
@@ -187,7 +188,8 @@ template <int HKV, int G, bool CLS>
 __global__ __launch_bounds__(score_threads<HKV>()) void score_kernel(const float* __restrict__ qp,
                                                              const uint16_t* __restrict__ k_index,
                                                              I64Arg offsets, int B,
-                                                             float* __restrict__ scores, ClsArgs cls) {
+                                                             float* __restrict__ scores,
+                                                             const int64_t* __restrict__ cls_state, ClsArgs cls) {
     constexpr int NT = score_threads<HKV>();
     constexpr int Hq = HKV * G;
     constexpr int LPT = 4 * HKV;          // lanes per token
@@ -198,24 +200,28 @@ __global__ __launch_bounds__(score_threads<HKV>()) void score_kernel(const float
     constexpr int UNR = ITERS < 8 ? ITERS : 8;
     constexpr int NOUT = G >= 4 ? G / 4 : 1;          // complete heads per lane
     __shared__ float tile[Hq * kTileLd];
-    // bracket of every head of the tile's sequence (CLS): lo, hi, range [beg, end), active
-    __shared__ uint32_t s_lo[CLS ? Hq : 1], s_hi[CLS ? Hq : 1];
-    __shared__ int64_t s_beg[CLS ? Hq : 1], s_end[CLS ? Hq : 1];
-    __shared__ int s_act[CLS ? Hq : 1];
-    __shared__ uint32_t s_cnt[CLS ? Hq : 1], s_below[CLS ? Hq : 1];
+    __shared__ uint32_t s_run;
 
     int b;
     int64_t t0, len;
     if (!find_item(offsets, B, blockIdx.x, kScoreTB, b, t0, len)) return;
-    // the heads' brackets (CLS)
+    if (CLS && threadIdx.x == 0) s_run = 0;
+    // CLS: the brackets of this wave's heads wid + i NW, requested first as wave-uniform (scalar)
+    // loads so they arrive while the tile is computed
+    constexpr int NWC = score_threads<HKV>() / 64;
+    constexpr int HPW = (HKV * G + NWC - 1) / NWC;
+    const int wu = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    int64_t c_flag[CLS ? HPW : 1], c_lo[CLS ? HPW : 1], c_hi[CLS ? HPW : 1], c_beg[CLS ? HPW : 1], c_end[CLS ? HPW : 1];
     if constexpr (CLS) {
-        if ((int)threadIdx.x < Hq) {
-            const int64_t* st = cls.state + ((int64_t)b * Hq + threadIdx.x) * 8;
-            s_act[threadIdx.x] = st[kStFlag] == 0;
-            s_lo[threadIdx.x] = (uint32_t)st[kStLo];
-            s_hi[threadIdx.x] = (uint32_t)st[kStHi];
-            s_beg[threadIdx.x] = st[kStBeg];
-            s_end[threadIdx.x] = st[kStEnd];
+#pragma unroll
+        for (int i = 0; i < HPW; ++i) {
+            const int h = wu + i * NWC < HKV * G ? wu + i * NWC : HKV * G - 1;
+            const int64_t* st = cls_state + ((int64_t)b * HKV * G + h) * 8;
+            c_flag[i] = st[kStFlag];
+            c_lo[i] = st[kStLo];
+            c_hi[i] = st[kStHi];
+            c_beg[i] = st[kStBeg];
+            c_end[i] = st[kStEnd];
         }
     }
     const int64_t S = score_stride(offsets[B]);
@@ -278,52 +284,35 @@ __global__ __launch_bounds__(score_threads<HKV>()) void score_kernel(const float
     }
     if constexpr (CLS) {
         static_assert(kScoreTB == 64, "one wave lane per tile token");
-        // wave w takes heads w, w + NW, ...; lane = token of the tile.  Pass 1 counts, pass 2
-        // writes the keys at the heads' offsets (an exclusive scan of the counts over the heads).
+        // wave w takes heads w, w + NW, ...; lane = token of the tile; each head reserves its run of
+        // keys with one LDS atomic.
         constexpr int NW = NT / 64;
-        constexpr int HPW = (Hq + NW - 1) / NW;
+        static_assert(NW == NWC, "one wave count");
         const uint64_t lt = (1ull << lane) - 1ull;
-        uint64_t mm[HPW];
-        uint32_t key[HPW];
 #pragma unroll
         for (int i = 0; i < HPW; ++i) {
-            const int h = wid + i * NW;
-            mm[i] = 0;
-            key[i] = 0;
+            const int h = wu + i * NW;
             if (h >= Hq) continue;
-            uint32_t below = 0;
-            if (s_act[h]) {                              // an active order statistic
-                const uint32_t lo = s_lo[h], hi = s_hi[h];
+            uint32_t below = 0, key = 0;
+            uint64_t mm = 0;
+            if (c_flag[i] == 0) {                        // an active order statistic
+                const uint32_t lo = (uint32_t)c_lo[i], hi = (uint32_t)c_hi[i];
                 const int64_t t = t0 + lane;
-                const bool valid = lane < len && t >= s_beg[h] && t < s_end[h];
-                key[i] = order_key(tile[h * kTileLd + lane]);
-                below = (uint32_t)__popcll(__ballot(valid && key[i] < lo));
-                mm[i] = __ballot(valid && key[i] >= lo && key[i] <= hi);
+                const bool valid = lane < len && t >= c_beg[i] && t < c_end[i];
+                key = order_key(tile[h * kTileLd + lane]);
+                below = (uint32_t)__popcll(__ballot(valid && key < lo));
+                mm = __ballot(valid && key >= lo && key <= hi);
             }
+            // the head's run of keys in the tile's key area (any order of the heads)
+            const uint32_t c = (uint32_t)__popcll(mm);
+            uint32_t offh = 0;
             if (lane == 0) {
-                s_cnt[h] = (uint32_t)__popcll(mm[i]);
-                s_below[h] = below;
+                offh = c ? atomicAdd(&s_run, c) : 0u;
+                cls.tcnt[(size_t)blockIdx.x * Hq + h] = below | (c << 8) | (offh << 16);
             }
-        }
-        __syncthreads();
-        // exclusive scan of the heads' counts (every wave, lanes < Hq)
-        uint32_t c = lane < Hq ? s_cnt[lane] : 0u;
-        uint32_t inc = c;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const uint32_t y = __shfl_up(inc, o, 64);
-            if (lane >= o) inc += y;
-        }
-        const uint32_t ex = inc - c;
-        if (wid == 0 && lane < Hq)
-            cls.tcnt[(size_t)blockIdx.x * Hq + lane] = s_below[lane] | (c << 8) | (ex << 16);
-#pragma unroll
-        for (int i = 0; i < HPW; ++i) {
-            const int h = wid + i * NW;
-            if (h >= Hq) continue;
-            const uint32_t offh = __shfl(ex, h, 64);
-            if ((mm[i] >> lane) & 1ull)
-                cls.tcand[(size_t)blockIdx.x * kClsTile + offh + __popcll(mm[i] & lt)] = key[i];
+            offh = __shfl(offh, 0, 64);
+            if ((mm >> lane) & 1ull)
+                cls.tcand[(size_t)blockIdx.x * kClsTile + offh + __popcll(mm & lt)] = key;
         }
     }
 }
@@ -345,10 +334,10 @@ static hipError_t launch_score_g(int G, dim3 grid, hipStream_t stream, const flo
                                  const I64Arg& offsets, int B, float* scores, const ClsArgs& cls) {
     dim3 block(score_threads<HKV>());
     switch (G) {
-        case 1: hipLaunchKernelGGL((score_kernel<HKV, 1, CLS>), grid, block, 0, stream, qp, k_index, offsets, B, scores, cls); break;
-        case 2: hipLaunchKernelGGL((score_kernel<HKV, 2, CLS>), grid, block, 0, stream, qp, k_index, offsets, B, scores, cls); break;
-        case 4: hipLaunchKernelGGL((score_kernel<HKV, 4, CLS>), grid, block, 0, stream, qp, k_index, offsets, B, scores, cls); break;
-        case 8: hipLaunchKernelGGL((score_kernel<HKV, 8, CLS>), grid, block, 0, stream, qp, k_index, offsets, B, scores, cls); break;
+        case 1: hipLaunchKernelGGL((score_kernel<HKV, 1, CLS>), grid, block, 0, stream, qp, k_index, offsets, B, scores, cls.state, cls); break;
+        case 2: hipLaunchKernelGGL((score_kernel<HKV, 2, CLS>), grid, block, 0, stream, qp, k_index, offsets, B, scores, cls.state, cls); break;
+        case 4: hipLaunchKernelGGL((score_kernel<HKV, 4, CLS>), grid, block, 0, stream, qp, k_index, offsets, B, scores, cls.state, cls); break;
+        case 8: hipLaunchKernelGGL((score_kernel<HKV, 8, CLS>), grid, block, 0, stream, qp, k_index, offsets, B, scores, cls.state, cls); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
