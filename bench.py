@@ -58,9 +58,10 @@ def parse():
     ap.add_argument("--n", type=int, default=131072)
     ap.add_argument("--budget", type=int, default=20, help="percent (5, 10, 15, 20, 30)")
     ap.add_argument("--mode", choices=["vote", "per-head"], default="vote")
-    ap.add_argument("--workload", choices=["long", "ragged"], default="long",
+    ap.add_argument("--workload", choices=["long", "ragged", "snapkv"], default="long",
                     help="long: one sequence of --n tokens (the headline); ragged: a batch of 16 sequences of "
-                         "16K-64K tokens at a 15%% budget")
+                         "16K-64K tokens at a 15%% budget; snapkv: SnapKV prefill-end compression alone "
+                         "(LLaMA-3-70B layer shapes, n = --n, w = 32, c = 4096)")
     ap.add_argument("--path", choices=["fused", "calls"], default="fused",
                     help="fused: ts_score_select (with the index append) + ts_sparse_decode; calls: ts_index_append + "
                          "ts_score + ts_select + ts_sparse_decode")
@@ -230,6 +231,51 @@ def bench_ragged(args, torch, api, synth, dev):
             f.write(line + "\n")
 
 
+def bench_snapkv(args, torch, api, synth, dev):
+    """SnapKV prefill-end compression at LLaMA-3-70B layer shapes (64 query / 8 KV heads, d = 128,
+    w = 32, c = 4096, pool 3) over n prompt tokens: --steps calls, the LLC flushed before each,
+    events on the launch stream."""
+    n = args.n
+    print(f"bench: building SnapKV inputs n={n}", file=sys.stderr, flush=True)
+    sx = synth.config5(n)
+    qo, K, V = (torch.from_numpy(a.view(np.int16)).to(dev) for a in (sx.q_obs, sx.K, sx.V))
+    ws = torch.empty(api.snapkv_workspace_bytes(n, 32, 64, 8, 4096), dtype=torch.uint8, device=dev)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
+    sink = torch.empty((), dtype=torch.float32, device=dev)
+    for _ in range(args.warmup):
+        torch.sum(flush.view(torch.float32), dim=0, out=sink)
+        api.snapkv_compress(qo, K, V, 4096, ws=ws)
+    torch.cuda.synchronize()
+    evs = []
+    for _ in range(args.steps):
+        torch.sum(flush.view(torch.float32), dim=0, out=sink)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        api.snapkv_compress(qo, K, V, 4096, ws=ws)
+        b.record()
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+    mean = float(us.mean())
+    flop_pass = 2.0 * 64 * 32 * n * 128
+    byts = n * 8 * 128 * 2 + 2 * 4096 * 8 * 128 * 2 * 2
+    res = {"metric": "µs per SnapKV compression (LLaMA-3-70B layer, w=32, c=4096), 1 MI355X", "value": round(mean, 2),
+           "unit": "us/call", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": False,
+           "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": f"SnapKV compress, Hq=64 Hkv=8 d=128 n={n} w=32 c=4096 pool 3", "n": n,
+                      "llc": "flushed before each call"},
+           "median_us": round(float(np.median(us)), 2),
+           "mfma_tflops_executed": round(2 * flop_pass / (mean * 1e-6) / 1e12, 1),
+           "mfma_frac_bf16_peak": round(2 * flop_pass / (mean * 1e-6) / 2.5e15, 4),
+           "algorithmic_tflops": round(flop_pass / (mean * 1e-6) / 1e12, 1),
+           "algorithmic_gbps": round(byts / (mean * 1e-6) / 1e9, 1)}
+    line = json.dumps(res)
+    print(line, flush=True)
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(line + "\n")
+
+
 def main():
     args = parse()
     if args.traffic_from:
@@ -249,6 +295,8 @@ def main():
     dev = torch.device("cuda:0")
     if args.workload == "ragged":
         return bench_ragged(args, torch, api, synth, dev)
+    if args.workload == "snapkv":
+        return bench_snapkv(args, torch, api, synth, dev)
     n0, steps, warm = args.n, args.steps, args.warmup
     total_steps = steps + warm
     mode = api.MODE_VOTE if args.mode == "vote" else api.MODE_PER_HEAD
