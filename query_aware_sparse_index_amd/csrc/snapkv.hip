@@ -154,15 +154,19 @@ __global__ __launch_bounds__(kSnapThreads) void snap_pass_kernel(const uint16_t*
         }
 
         if (PASS == 2) {
-            // column sums over the 16 rows of each lane group (DPP butterfly); lane lr == i writes
+            // column sums over the 16 rows of each lane group (DPP butterfly); lane lr then keeps
+            // the sum of key tile lr / 4, key lg * 4 + lr % 4, so that the wave's 64 keys leave in
+            // one store
+            float v = 0.f;
 #pragma unroll
             for (int kt = 0; kt < kSnapKTW; ++kt)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float v = sum_row16(colsum[kt][i]);
-                    const int64_t j = jw + kt * 16 + lg * 4 + i;
-                    if (lr == i && j < n) imp[(int64_t)g * n + j] = v / (float)R;
+                    const float sv = sum_row16(colsum[kt][i]);
+                    v = (lr == kt * 4 + i) ? sv : v;
                 }
+            const int64_t j = jw + (lr >> 2) * 16 + lg * 4 + (lr & 3);
+            if (!MASK || j < n) imp[(int64_t)g * n + j] = v / (float)R;
         }
     };
 
@@ -176,14 +180,17 @@ __global__ __launch_bounds__(kSnapThreads) void snap_pass_kernel(const uint16_t*
             compute(a, kb, std::true_type{});
     };
 
+    // The loads are unconditional: a key block past the end loads key n - 1 (the clamp in
+    // load), so that every path through the loop issues the same memory operations and the
+    // waits before the MFMAs count the prefetch as still in flight instead of draining it.
     bf16x8_t a0[kSnapKTW][4], a1[kSnapKTW][4];
-    if (p < nblk) load(a0, p);
+    load(a0, p);
     __syncthreads();
     for (int64_t kb = p; kb < nblk; kb += 2 * (int64_t)P) {
-        if (kb + P < nblk) load(a1, kb + P);
+        load(a1, kb + P);
         run(a0, kb);
         if (kb + P >= nblk) break;
-        if (kb + 2 * (int64_t)P < nblk) load(a0, kb + 2 * (int64_t)P);
+        load(a0, kb + 2 * (int64_t)P);
         run(a1, kb + P);
     }
 
