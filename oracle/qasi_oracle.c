@@ -352,7 +352,7 @@ void qo_snapkv_importance(const uint16_t* q_obs, const uint16_t* K, int64_t n, i
     free(s);
 }
 
-/* [SK] "アルゴリズム", step 3: avg_pool1d(kernel, padding = kernel/2, stride 1) along the
+/* [SK] "アルゴリズム": avg_pool1d(kernel, padding = kernel/2, stride 1) along the
  * tokens, zero padding counted in the divisor (the divisor is always `kernel`).
  * kernel must be odd so the output keeps length n.  in/out are [rows][n]. */
 void qo_avg_pool1d(const double* in, int64_t rows, int64_t n, int kernel, double* out) {
@@ -369,8 +369,8 @@ void qo_avg_pool1d(const double* in, int64_t rows, int64_t n, int kernel, double
 }
 
 /* [SK] "Top-k SelectionとCluster-based Retention" eq. S = top-k(a, c) per KV head, with
- * c clipped to n (step 4 of the listing), ties to the lower index, then sorted
- * ascending (step 5).  pooled is [rows][n]; idx is [rows][min(c, n)]. */
+ * c clipped to n and the kept positions sorted ascending, as the listing of "アルゴリズム"
+ * does; ties go to the lower index.  pooled is [rows][n]; idx is [rows][min(c, n)]. */
 int64_t qo_topc(const double* pooled, int64_t rows, int64_t n, int64_t c, int32_t* idx) {
     int64_t ce = c < n ? c : n;
     for (int64_t r = 0; r < rows; ++r) {
@@ -380,7 +380,7 @@ int64_t qo_topc(const double* pooled, int64_t rows, int64_t n, int64_t c, int32_
     return ce;
 }
 
-/* [SK] listing step 5: gather the chosen K and V rows of each KV head into a compacted
+/* [SK] "アルゴリズム": gather the chosen K and V rows of each KV head into a compacted
  * cache K_out[s][g][128] = K[idx[g][s]][g][128] (bit copies). */
 void qo_gather_rows(const uint16_t* K, const uint16_t* V, int64_t n, int Hkv, const int32_t* idx,
                     int64_t ce, uint16_t* K_out, uint16_t* V_out) {
