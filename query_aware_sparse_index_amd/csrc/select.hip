@@ -1017,219 +1017,176 @@ __global__ __launch_bounds__(kChunk) void compact_vote_kernel(I64Arg offsets, in
 }
 
 // --------------------------------------------------------- per-head compaction
-// Three kernels, each covering all heads of a token chunk at once (the heads are looped inside
-// the block, their score loads issued together):
+// Three kernels over 64-token chunks, one wave per chunk (four independent waves per block, no
+// LDS and no block barriers).  A wave covers every head of its chunk: the heads' score loads
+// are issued together, lane u keeps the parameters of head h0 + u, and each head's step reads
+// them back as wave-uniform values (readlane), so the per-head work is ballots and popcounts.
 //   ph_count   : cnt[(h * nitems + item) * 2 + {0, 1}] = non-forced tokens of the chunk with key
-//                above / equal to theta_h (wave ballots, no atomics);
+//                above / equal to theta_h;
 //   ph_scan    : one wave per (sequence, head): exclusive prefix of those counts over the
 //                sequence's chunks, written in place;
 //   ph_compact : the chunk's selected tokens of every head, at their ranks: forced tokens, keys
 //                above theta_h, and the first need_eq - eqb keys equal to theta_h in position order.
-constexpr int kPhHeads = 32;   // heads handled per pass of a block (Hq <= 64 takes two)
-constexpr int kPhChunk = 256;  // tokens per per-head compaction block
+constexpr int kPhHeads = 32;   // heads handled per pass of a wave (Hq <= 64 takes two)
+constexpr int kPhChunk = 64;   // tokens per chunk: one per lane of a wave
+constexpr int kPhWaves = 4;    // independent chunk waves per block
 
-__global__ __launch_bounds__(kPhChunk) void ph_count_kernel(const float* __restrict__ scores,
-                                                         I64Arg offsets, int B, int Hq,
-                                                         DevCfg cfg, int64_t S, const int64_t* __restrict__ state,
-                                                         int64_t nitems, uint32_t* __restrict__ cnt) {
-    constexpr int NW = kPhChunk / 64;
-    __shared__ uint32_t wc[kPhHeads][NW][2];
-    __shared__ uint32_t hkey[kPhHeads];
-    __shared__ bool hact[kPhHeads];
+__device__ __forceinline__ int lane_pick(int v, int u) { return __builtin_amdgcn_readlane(v, u); }
+
+__global__ __launch_bounds__(kPhWaves * 64) void ph_count_kernel(const float* __restrict__ scores,
+                                                               I64Arg offsets, int B, int Hq,
+                                                               DevCfg cfg, int64_t S, const int64_t* __restrict__ state,
+                                                               int64_t nitems, uint32_t* __restrict__ cnt) {
+    const int lane = threadIdx.x & 63;
+    const int64_t item = (int64_t)blockIdx.x * kPhWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (item >= nitems) return;
     int b;
     int64_t first, nch, t0, len;
-    if (!find_chunk<kPhChunk>(offsets, B, blockIdx.x, b, first, nch, t0, len)) return;
+    if (!find_chunk<kPhChunk>(offsets, B, item, b, first, nch, t0, len)) return;
     const int64_t off = offsets[b], n = offsets[b + 1] - off;
-    const int64_t i = threadIdx.x, t = t0 + i;
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    const bool in = i < len && !is_forced(t, n, cfg.sink, cfg.local);
-    const float* col = scores + off + (i < len ? t : t0);
+    const int64_t t = t0 + lane;
+    const bool in = lane < len && !is_forced(t, n, cfg.sink, cfg.local);
+    const float* col = scores + off + (lane < len ? t : t0);
     for (int h0 = 0; h0 < Hq; h0 += kPhHeads) {
         float sv[kPhHeads];
 #pragma unroll
         for (int u = 0; u < kPhHeads; ++u) sv[u] = col[(int64_t)(h0 + u < Hq ? h0 + u : Hq - 1) * S];
-        if (threadIdx.x < kPhHeads && h0 + threadIdx.x < Hq) {
-            const int64_t* st = state + ((int64_t)b * Hq + h0 + threadIdx.x) * 8;
-            hact[threadIdx.x] = st[kStFlag] == kFlagActive;
-            hkey[threadIdx.x] = (uint32_t)st[kStKey];
-        }
-        __syncthreads();
+        // lane u: flag and theta key of head h0 + u
+        const int hl = h0 + (lane < kPhHeads ? lane : 0) < Hq ? h0 + (lane < kPhHeads ? lane : 0) : Hq - 1;
+        const int64_t* st = state + ((int64_t)b * Hq + hl) * 8;
+        const int lact = st[kStFlag] == kFlagActive ? 1 : 0;
+        const int lkey = (int)(uint32_t)st[kStKey];
+        uint32_t cg = 0, ce = 0;   // lane u ends with head h0 + u's counts
 #pragma unroll
         for (int u = 0; u < kPhHeads; ++u) {
-            const int h = h0 + u;
-            if (h >= Hq) break;
-            const bool act = hact[u];
-            const uint32_t ks = hkey[u];
+            if (h0 + u >= Hq) break;
+            const bool act = lane_pick(lact, u) != 0;
+            const uint32_t ks = (uint32_t)lane_pick(lkey, u);
             const uint32_t k = order_key(sv[u]);
-            const uint64_t mg = __ballot(act && in && k > ks), me = __ballot(act && in && k == ks);
-            if (lane == 0) {
-                wc[u][wid][0] = (uint32_t)__popcll(mg);
-                wc[u][wid][1] = (uint32_t)__popcll(me);
-            }
+            const uint32_t g = (uint32_t)__popcll(__ballot(act && in && k > ks));
+            const uint32_t e = (uint32_t)__popcll(__ballot(act && in && k == ks));
+            cg = lane == u ? g : cg;
+            ce = lane == u ? e : ce;
         }
-        __syncthreads();
-        const int hh = threadIdx.x >> 1, which = threadIdx.x & 1;
-        if (hh < kPhHeads && h0 + hh < Hq) {
-            uint32_t a = 0;
-#pragma unroll
-            for (int w = 0; w < NW; ++w) a += wc[hh][w][which];
-            cnt[((size_t)(h0 + hh) * nitems + blockIdx.x) * 2 + which] = a;
-        }
-        __syncthreads();
+        if (lane < kPhHeads && h0 + lane < Hq)
+            reinterpret_cast<uint2*>(cnt)[(size_t)(h0 + lane) * nitems + item] = make_uint2(cg, ce);
     }
 }
 
-// One wave per (sequence b, head h), four waves per block: exclusive prefix over the chunks of
-// b of the (above, equal) counts, in place.
-__global__ __launch_bounds__(256) void ph_scan_kernel(I64Arg offsets, int B, int Hq,
-                                                     int64_t nitems, uint32_t* __restrict__ cnt) {
-    const int lane = threadIdx.x & 63;
-    const int64_t wv = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (wv >= (int64_t)B * Hq) return;
-    const int b = (int)(wv / Hq), h = (int)(wv % Hq);
+// One block per (sequence b, head h): exclusive prefix over the chunks of b of the (above,
+// equal) counts, in place.  Thread t sums kPhScanPer consecutive chunks, a block scan places
+// the sums, and the block walks the chunks in tiles of kPhScanThreads * kPhScanPer.
+constexpr int kPhScanThreads = 256;
+constexpr int kPhScanPer = 8;
+__global__ __launch_bounds__(kPhScanThreads) void ph_scan_kernel(I64Arg offsets, int B, int Hq,
+                                                                int64_t nitems, uint32_t* __restrict__ cnt) {
+    constexpr int NW = kPhScanThreads / 64;
+    __shared__ uint32_t wt[2][NW];
+    const int64_t inst = blockIdx.x;
+    if (inst >= (int64_t)B * Hq) return;
+    const int b = (int)(inst / Hq), h = (int)(inst % Hq);
+    const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
     int64_t first = 0;
     for (int i = 0; i < b; ++i) first += (offsets[i + 1] - offsets[i] + kPhChunk - 1) / kPhChunk;
     const int64_t nch = (offsets[b + 1] - offsets[b] + kPhChunk - 1) / kPhChunk;
-    uint32_t* row = cnt + ((size_t)h * nitems + first) * 2;
-    // lane l takes the PER consecutive chunks [c0 + l*PER, c0 + (l+1)*PER) of a batch of 64*PER
-    constexpr int PER = 16;
+    uint2* row = reinterpret_cast<uint2*>(cnt) + (size_t)h * nitems + first;
     uint32_t carry0 = 0, carry1 = 0;
-    for (int64_t c0 = 0; c0 < nch; c0 += 64 * PER) {
-        const int64_t cl = c0 + (int64_t)lane * PER;
-        uint2 v[PER];
+    for (int64_t c0 = 0; c0 < nch; c0 += kPhScanThreads * kPhScanPer) {
+        const int64_t cl = c0 + (int64_t)t * kPhScanPer;
+        uint2 v[kPhScanPer];
 #pragma unroll
-        for (int u = 0; u < PER; ++u) {
-            const int64_t c = cl + u;
-            v[u] = c < nch ? reinterpret_cast<const uint2*>(row)[c] : make_uint2(0, 0);
-        }
+        for (int u = 0; u < kPhScanPer; ++u) v[u] = cl + u < nch ? row[cl + u] : make_uint2(0, 0);
         uint32_t s0 = 0, s1 = 0;
 #pragma unroll
-        for (int u = 0; u < PER; ++u) { s0 += v[u].x; s1 += v[u].y; }
+        for (int u = 0; u < kPhScanPer; ++u) { s0 += v[u].x; s1 += v[u].y; }
         uint32_t i0 = s0, i1 = s1;
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
             const uint32_t y0 = __shfl_up(i0, o, 64), y1 = __shfl_up(i1, o, 64);
             if (lane >= o) { i0 += y0; i1 += y1; }
         }
-        uint32_t a0 = carry0 + i0 - s0, a1 = carry1 + i1 - s1;
+        if (lane == 63) { wt[0][wid] = i0; wt[1][wid] = i1; }
+        __syncthreads();
+        uint32_t b0 = 0, b1 = 0, t0 = 0, t1 = 0;
 #pragma unroll
-        for (int u = 0; u < PER; ++u) {
-            const int64_t c = cl + u;
-            if (c < nch) reinterpret_cast<uint2*>(row)[c] = make_uint2(a0, a1);
+        for (int w = 0; w < NW; ++w) {
+            const uint32_t x = wt[0][w], y = wt[1][w];
+            if (w < wid) { b0 += x; b1 += y; }
+            t0 += x;
+            t1 += y;
+        }
+        __syncthreads();                      // wt is written again by the next tile
+        uint32_t a0 = carry0 + b0 + i0 - s0, a1 = carry1 + b1 + i1 - s1;
+#pragma unroll
+        for (int u = 0; u < kPhScanPer; ++u) {
+            if (cl + u < nch) row[cl + u] = make_uint2(a0, a1);
             a0 += v[u].x;
             a1 += v[u].y;
         }
-        carry0 += __shfl(i0, 63, 64);
-        carry1 += __shfl(i1, 63, 64);
+        carry0 += t0;
+        carry1 += t1;
     }
 }
 
-__global__ __launch_bounds__(kPhChunk) void ph_compact_kernel(const float* __restrict__ scores,
-                                                           I64Arg offsets, int B, int Hq,
-                                                           DevCfg cfg, int64_t S, const int64_t* __restrict__ state,
-                                                           int64_t nitems, const uint32_t* __restrict__ pre,
-                                                           int32_t* __restrict__ idx_out,
-                                                           int64_t* __restrict__ count_out) {
-    constexpr int NW = kPhChunk / 64;
-    __shared__ uint32_t wq[kPhHeads][NW];   // per-wave counts of equal keys, then their prefix
-    __shared__ uint32_t ws[kPhHeads][NW];   // per-wave counts of selected tokens, then their prefix
-    struct HeadParams {
-        int flag, need_eq, eqb, base;
-        uint32_t key;
-    };
-    __shared__ HeadParams hp[kPhHeads];
+__global__ __launch_bounds__(kPhWaves * 64) void ph_compact_kernel(const float* __restrict__ scores,
+                                                                 I64Arg offsets, int B, int Hq,
+                                                                 DevCfg cfg, int64_t S, const int64_t* __restrict__ state,
+                                                                 int64_t nitems, const uint32_t* __restrict__ pre,
+                                                                 int32_t* __restrict__ idx_out,
+                                                                 int64_t* __restrict__ count_out) {
+    const int lane = threadIdx.x & 63;
+    const int64_t item = (int64_t)blockIdx.x * kPhWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (item >= nitems) return;
     int b;
     int64_t first, nch, t0, len;
-    if (!find_chunk<kPhChunk>(offsets, B, blockIdx.x, b, first, nch, t0, len)) return;
+    if (!find_chunk<kPhChunk>(offsets, B, item, b, first, nch, t0, len)) return;
     const int64_t off = offsets[b], n = offsets[b + 1] - off;
     const int64_t K = budget_k(n, cfg.bnum, cfg.bden, cfg.sink, cfg.local);
     const int64_t kpre = kpre_of(offsets, b, cfg);
     const int64_t fb = forced_before(t0, n, cfg.sink, cfg.local);
-    if (blockIdx.x == first && threadIdx.x == 0) count_out[b] = K;
-    const int64_t i = threadIdx.x, t = t0 + i;
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    if (item == first && lane == 0) count_out[b] = K;
+    const int64_t t = t0 + lane;
     const uint64_t lt = (1ull << lane) - 1ull;
-    const bool inr = i < len;
+    const bool inr = lane < len;
     const bool frc = inr && is_forced(t, n, cfg.sink, cfg.local);
     const float* col = scores + off + (inr ? t : t0);
-    // exclusive prefix over the waves of a[h][.] for the first `nh` heads (one thread per entry)
-    auto wave_prefix = [&](uint32_t (*a)[NW], int nh) {
-        __syncthreads();
-        const int hh = threadIdx.x / NW, w = threadIdx.x % NW;
-        uint32_t v = 0;
-        if (hh < nh)
-            for (int x = 0; x < w; ++x) v += a[hh][x];
-        __syncthreads();
-        if (hh < nh) a[hh][w] = v;
-        __syncthreads();
-    };
     for (int h0 = 0; h0 < Hq; h0 += kPhHeads) {
-        const int nh = Hq - h0 < kPhHeads ? Hq - h0 : kPhHeads;
         float sv[kPhHeads];
 #pragma unroll
         for (int u = 0; u < kPhHeads; ++u) sv[u] = col[(int64_t)(h0 + u < Hq ? h0 + u : Hq - 1) * S];
-        // per-head parameters of this chunk, one thread per head
-        if (threadIdx.x < nh) {
-            const int h = h0 + threadIdx.x;
-            const int64_t* st = state + ((int64_t)b * Hq + h) * 8;
-            const int64_t flag = st[kStFlag];
-            const int64_t gtb = pre[((size_t)h * nitems + blockIdx.x) * 2];
-            const int64_t eqb = pre[((size_t)h * nitems + blockIdx.x) * 2 + 1];
-            int64_t base, need_eq = 0;
-            if (flag == kFlagTakeAll) base = t0;
-            else if (flag == kFlagTakeNone) base = fb;
-            else {
-                need_eq = st[kStNeed] - st[kStGt];
-                base = fb + gtb + (eqb < need_eq ? eqb : need_eq);
-            }
-            hp[threadIdx.x].flag = (int)flag;
-            hp[threadIdx.x].key = (uint32_t)st[kStKey];
-            hp[threadIdx.x].need_eq = (int)need_eq;
-            hp[threadIdx.x].eqb = (int)eqb;
-            hp[threadIdx.x].base = (int)base;
+        // lane u: the parameters of head h0 + u in this chunk (the list offset of the chunk's first
+        // selected token, the equal keys before the chunk and the equal keys to take in all)
+        const int hl = h0 + (lane < kPhHeads ? lane : 0) < Hq ? h0 + (lane < kPhHeads ? lane : 0) : Hq - 1;
+        const int64_t* st = state + ((int64_t)b * Hq + hl) * 8;
+        const int64_t flag = st[kStFlag];
+        const uint2 gq = reinterpret_cast<const uint2*>(pre)[(size_t)hl * nitems + item];
+        const int64_t gtb = gq.x, eqb = gq.y;
+        int64_t base, need_eq = 0;
+        if (flag == kFlagTakeAll) base = t0;
+        else if (flag == kFlagTakeNone) base = fb;
+        else {
+            need_eq = st[kStNeed] - st[kStGt];
+            base = fb + gtb + (eqb < need_eq ? eqb : need_eq);
         }
-        // pass 1: counts of the keys equal to theta_h
-        __syncthreads();
+        const int lflag = (int)flag, lkey = (int)(uint32_t)st[kStKey];
+        const int lneq = (int)need_eq, leqb = (int)eqb, lbase = (int)base;
 #pragma unroll
         for (int u = 0; u < kPhHeads; ++u) {
-            if (u >= nh) break;
-            const bool act = hp[u].flag == kFlagActive;
-            const uint64_t me = __ballot(act && inr && !frc && order_key(sv[u]) == hp[u].key);
-            if (lane == 0) wq[u][wid] = (uint32_t)__popcll(me);
-        }
-        wave_prefix(wq, nh);
-        // pass 2: selection flags (bit u of selbits) and their per-wave counts
-        uint32_t selbits = 0;
-#pragma unroll
-        for (int u = 0; u < kPhHeads; ++u) {
-            if (u >= nh) break;
-            const int flag = hp[u].flag;
-            const uint32_t ks = hp[u].key;
+            if (h0 + u >= Hq) break;
+            const int hflag = lane_pick(lflag, u);
+            const uint32_t ks = (uint32_t)lane_pick(lkey, u);
             const uint32_t k = order_key(sv[u]);
-            const bool eqf = flag == kFlagActive && inr && !frc && k == ks;
-            const uint64_t me = __ballot(eqf);
-            const int64_t eq_rank = (int64_t)hp[u].eqb + wq[u][wid] + __popcll(me & lt);
+            const bool eqf = hflag == kFlagActive && inr && !frc && k == ks;
+            const int64_t eq_rank = (int64_t)lane_pick(leqb, u) + __popcll(__ballot(eqf) & lt);
             bool sel = false;
             if (inr) {
-                if (frc || flag == kFlagTakeAll) sel = true;
-                else if (flag == kFlagActive) sel = k > ks || (eqf && eq_rank < hp[u].need_eq);
+                if (frc || hflag == kFlagTakeAll) sel = true;
+                else if (hflag == kFlagActive) sel = k > ks || (eqf && eq_rank < lane_pick(lneq, u));
             }
-            selbits |= (sel ? 1u : 0u) << u;
             const uint64_t msel = __ballot(sel);
-            if (lane == 0) ws[u][wid] = (uint32_t)__popcll(msel);
+            const int64_t p = (int64_t)lane_pick(lbase, u) + __popcll(msel & lt);
+            if (sel && p < K) idx_out[Hq * kpre + (int64_t)(h0 + u) * K + p] = (int32_t)t;
         }
-        wave_prefix(ws, nh);
-        // pass 3: write each selected token at its rank in its head's list
-#pragma unroll
-        for (int u = 0; u < kPhHeads; ++u) {
-            if (u >= nh) break;
-            const bool sel = (selbits >> u) & 1u;
-            const uint64_t msel = __ballot(sel);
-            if (!sel) continue;
-            const int64_t p = (int64_t)hp[u].base + ws[u][wid] + __popcll(msel & lt);
-            if (p < K) idx_out[Hq * kpre + (int64_t)(h0 + u) * K + p] = (int32_t)t;
-        }
-        __syncthreads();
     }
 }
 
@@ -1333,11 +1290,12 @@ static hipError_t launch_select_tail(const SelectLayout& L, const float* scores,
         hipLaunchKernelGGL(compact_vote_kernel, dim3((unsigned)L.nitems), dim3(kChunk), 0, stream, offs,
                            B, d, L.keys, L.hist, idx_out, count_out);
     } else {
-        hipLaunchKernelGGL(ph_count_kernel, dim3((unsigned)L.ph_items), dim3(kPhChunk), 0, stream, scores, offs,
+        const dim3 phg((unsigned)((L.ph_items + kPhWaves - 1) / kPhWaves));
+        hipLaunchKernelGGL(ph_count_kernel, phg, dim3(kPhWaves * 64), 0, stream, scores, offs,
                            B, Hq, d, S, L.state, L.ph_items, L.phcnt);
-        hipLaunchKernelGGL(ph_scan_kernel, dim3((unsigned)((B * Hq + 3) / 4)), dim3(256), 0, stream, offs, B,
+        hipLaunchKernelGGL(ph_scan_kernel, dim3((unsigned)(B * Hq)), dim3(kPhScanThreads), 0, stream, offs, B,
                            Hq, L.ph_items, L.phcnt);
-        hipLaunchKernelGGL(ph_compact_kernel, dim3((unsigned)L.ph_items), dim3(kPhChunk), 0, stream, scores,
+        hipLaunchKernelGGL(ph_compact_kernel, phg, dim3(kPhWaves * 64), 0, stream, scores,
                            offs, B, Hq, d, S, L.state, L.ph_items, L.phcnt, idx_out, count_out);
     }
     return hipGetLastError();
