@@ -168,8 +168,20 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_partial_kernel(const ui
     __shared__ int4 s_tok[kDecWaves][kDecMaxEW / 4];
 
     const int HW = (MODE == 1) ? Hq : Hkv;
-    const int64_t item = blockIdx.x / HW;
-    const int hw = blockIdx.x % HW;
+    int64_t item;
+    int hw;
+    if constexpr (MODE == 1) {
+        // The G blocks of one (item, KV head) pair get equal blockIdx % 8: blocks are dealt to
+        // the 8 XCDs round-robin, so the pair's heads run on one XCD, whose L2 then serves the
+        // rows their lists share.  x = (pair / 8) * 8G + j * 8 + pair % 8 for head j of the group.
+        const int64_t x = blockIdx.x;
+        const int64_t pair = (x / (8 * G)) * 8 + x % 8;
+        item = pair / Hkv;
+        hw = (int)(pair % Hkv) * G + (int)((x / 8) % G);
+    } else {
+        item = blockIdx.x / HW;
+        hw = blockIdx.x % HW;
+    }
     int b;
     int64_t j0, len, kpre;
     if (!find_list_chunk(counts, B, item, EB, b, j0, len, kpre)) return;
@@ -507,7 +519,12 @@ hipError_t launch_sparse_decode(const uint16_t* q, const uint16_t* K, const uint
     if (items == 0) return hipSuccess;
     hipError_t e;
     if (mode == 0) e = launch_partial_G<0>(G, dim3((unsigned)(items * Hkv)), stream, q, K, V, offs, idx, cnts, B, Hq, Hkv, EB, part, ml);
-    else e = launch_partial_G<1>(G, dim3((unsigned)(items * Hq)), stream, q, K, V, offs, idx, cnts, B, Hq, Hkv, EB, part, ml);
+    else {
+        // blocks of the (item, KV head) pairs in groups of 8, G heads each (see the kernel); the
+        // pairs past items * Hkv find no list chunk and return
+        const int64_t pairs = (items * Hkv + 7) / 8 * 8;
+        e = launch_partial_G<1>(G, dim3((unsigned)(pairs * G)), stream, q, K, V, offs, idx, cnts, B, Hq, Hkv, EB, part, ml);
+    }
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(decode_merge_kernel, dim3(B * Hq), dim3(kMergeThreads), 0, stream, part, ml, cnts, B, Hq, EB, out);
     return hipGetLastError();
