@@ -13,8 +13,9 @@
 // of g in vote / dense mode, one head in per-head mode), so each gathered K/V row is read once
 // for the whole GQA group.  A wave works through its entries in sub-batches of 16: a wave is 4
 // rows of 16 lanes, row r takes entries 4r .. 4r+3 of the sub-batch and lane p holds dims
-// [8p, 8p+8) (one 16-byte load of K and one of V per entry).  The K and V rows of sub-batch
-// s+1 are requested before sub-batch s is computed, so every wave keeps its gathers in flight:
+// [8p, 8p+8) (one 16-byte load of K and one of V per entry).  The source requests the K and V
+// rows of sub-batch s+1 before sub-batch s is computed; the compiler moves those loads next to
+// their use, and with every block resident the other waves of a CU cover the gather latency:
 //   z  = q . k * log2(e)/sqrt(128): bf16 pair dot products (exact products, fp32 sums), then a
 //        transposed butterfly over the 16 lanes of the row (DPP);
 //   online softmax per head over the sub-batches: m, l and acc = sum 2^(z - m) v, rescaled
@@ -306,7 +307,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_partial_kernel(const ui
         }
     };
 
-    // two sub-batches in flight: A = even, B = odd
+    // two register sets: A = even sub-batches, B = odd
     uint4 ka[EPR], va[EPR], kb2[EPR], vb2[EPR];
     if (nsb > 0) issue(0, ka, va);
     for (int sb = 0; sb < nsb; sb += 2) {
