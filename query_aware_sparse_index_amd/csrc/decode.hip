@@ -38,21 +38,14 @@ __host__ __device__ constexpr int dec_gh(int G, int mode) { return mode == 1 ? 1
 
 __device__ __forceinline__ bool find_list_chunk(const I64Arg& counts, int B, int64_t item, int EB, int& b,
                                                 int64_t& j0, int64_t& len, int64_t& kpre) {
-    int64_t acc = 0, kp = 0;
-    for (int i = 0; i < B; ++i) {
-        const int64_t n = counts[i];
-        const int64_t nb = (n + EB - 1) / EB;
-        if (item < acc + nb) {
-            b = i;
-            j0 = (item - acc) * EB;
-            len = n - j0 < EB ? n - j0 : EB;
-            kpre = kp;
-            return true;
-        }
-        acc += nb;
-        kp += n;
-    }
-    return false;
+    const SeqPos sp = wave_find_seq(B, item, (counts[0] + EB - 1) / EB, [cd = counts.dev, EB](int i) { return (cd[i] + EB - 1) / EB; });
+    if (sp.b < 0) return false;
+    b = sp.b;
+    const int64_t n = counts[b];
+    j0 = (item - sp.first) * EB;
+    len = n - j0 < EB ? n - j0 : EB;
+    kpre = wave_prefix_seq(b, [cd = counts.dev](int i) { return cd[i]; });
+    return true;
 }
 
 // bf16 pair dot product with fp32 accumulation: a.lo*b.lo + a.hi*b.hi + c
@@ -362,8 +355,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const float
     __shared__ float sM[NG], sL[NG];
     __shared__ float sA[NG][kD];
     const int bh = blockIdx.x, b = bh / Hq, h = bh % Hq;
-    int64_t first = 0;
-    for (int i = 0; i < b; ++i) first += (counts[i] + EB - 1) / EB;
+    const int64_t first = wave_prefix_seq(b, [cd = counts.dev, EB](int i) { return (cd[i] + EB - 1) / EB; });
     const int64_t nch = (counts[b] + EB - 1) / EB;
     const int cg = threadIdx.x / kD, d = threadIdx.x % kD;
     float M = -INFINITY, A = 0.f, L = 0.f;

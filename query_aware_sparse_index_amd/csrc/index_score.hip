@@ -80,22 +80,19 @@ constexpr int score_threads() {
 }
 constexpr int kTileLd = kScoreTB + 1;
 
+// item -> (sequence b, first token t0 of the item's block of tb tokens, its length); every lane
+// of the wave calls it
 __device__ __forceinline__ bool find_item(const I64Arg& offsets, int B, int64_t item, int tb, int& b,
                                           int64_t& t0, int64_t& len) {
-    int64_t acc = 0;
-    for (int i = 0; i < B; ++i) {
-        int64_t n = offsets[i + 1] - offsets[i];
-        int64_t nb = (n + tb - 1) / tb;
-        if (item < acc + nb) {
-            b = i;
-            int64_t j = item - acc;
-            t0 = j * tb;
-            len = n - t0 < tb ? n - t0 : tb;
-            return true;
-        }
-        acc += nb;
-    }
-    return false;
+    const SeqPos sp = wave_find_seq(B, item, (offsets[1] - offsets[0] + tb - 1) / tb,
+                                    [od = offsets.dev, tb](int i) { return (od[i + 1] - od[i] + tb - 1) / tb; });
+    if (sp.b < 0) return false;
+    b = sp.b;
+    // one sequence: its length from the launch arguments; more: from device memory
+    const int64_t n = B == 1 ? offsets[1] - offsets[0] : offsets.dev[b + 1] - offsets.dev[b];
+    t0 = (item - sp.first) * tb;
+    len = n - t0 < tb ? n - t0 : tb;
+    return true;
 }
 
 // qp[(b * Hq + h) * 32 + c] = sum_j q[b][h][j] P[j][c] / sqrt(32): P and the block's

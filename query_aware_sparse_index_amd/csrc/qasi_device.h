@@ -206,4 +206,69 @@ __device__ __forceinline__ int block_inclusive_scan3(int a, int b, int c, int (*
     return x + base;
 }
 
+// ---- sequence lookups for work items numbered sequence by sequence (ragged batches)
+// Every lane of a wave must call these together (converged control flow); each returns the same
+// values in every lane.  One sequence: scalar.  More: lane i % 64 loads sequence i's value (one
+// round trip for up to 64 sequences), then a wave-uniform loop reads the values back with
+// readlane (no memory or LDS round trip per sequence).
+__device__ __forceinline__ int64_t readlane_i64(int64_t v, int l) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(v >> 32), l);
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+// The sequence b holding work item `item` when sequence i owns units(i) >= 0 items: first =
+// items of the sequences before b, cnt = units(b); b = -1 when item is past the last one.
+// units0 is units(0) for a batch of one sequence (its values are launch arguments); for more,
+// units(i) is evaluated per lane and must read device memory only (a lane-varying index into
+// launch-argument values would go through scratch memory).
+struct SeqPos {
+    int64_t first, cnt;
+    int b;
+};
+template <class Units>
+__device__ __forceinline__ SeqPos wave_find_seq(int B, int64_t item, int64_t units0, Units units) {
+    SeqPos r{0, 0, -1};
+    if (B == 1) {
+        r.cnt = units0;
+        if (item < r.cnt) r.b = 0;
+        return r;
+    }
+    const int lane = threadIdx.x & 63;
+    int64_t acc = 0;
+    for (int base = 0; base < B && r.b < 0; base += 64) {
+        const int i = base + lane;
+        const int64_t u = i < B ? units(i) : 0;
+        const int lim = B - base < 64 ? B - base : 64;
+        for (int l = 0; l < lim; ++l) {
+            const int64_t ul = readlane_i64(u, l);
+            if (item < acc + ul) {
+                r.b = base + l;
+                r.first = acc;
+                r.cnt = ul;
+                break;
+            }
+            acc += ul;
+        }
+    }
+    // the values are wave-uniform: say so, so that the caller indexes with scalars
+    r.b = __builtin_amdgcn_readfirstlane(r.b);
+    r.first = readlane_i64(r.first, 0);
+    r.cnt = readlane_i64(r.cnt, 0);
+    return r;
+}
+// sum of w(i) over the sequences i < b (b > 0 only in batches of several sequences, so w reads
+// device memory)
+template <class W>
+__device__ __forceinline__ int64_t wave_prefix_seq(int b, W w) {
+    const int lane = threadIdx.x & 63;
+    int64_t acc = 0;
+    for (int base = 0; base < b; base += 64) {
+        const int i = base + lane;
+        const int64_t v = i < b ? w(i) : 0;
+        const int lim = b - base < 64 ? b - base : 64;
+        for (int l = 0; l < lim; ++l) acc += readlane_i64(v, l);
+    }
+    return acc;
+}
+
 }  // namespace qasi

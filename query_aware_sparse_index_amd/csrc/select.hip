@@ -741,8 +741,7 @@ __global__ __launch_bounds__(kColThreads) void th_collect_tiles_kernel(I64Arg of
     const int64_t n = offsets[b + 1] - offsets[b];
     const OsInst oi = os_instance(n, cfg);
     if (oi.flag != kFlagActive) return;
-    int64_t tf = 0;
-    for (int i = 0; i < b; ++i) tf += (offsets[i + 1] - offsets[i] + 63) / 64;
+    const int64_t tf = wave_prefix_seq(b, [od = offsets.dev](int i) { return (od[i + 1] - od[i] + 63) / 64; });
     const int64_t nt = (n + 63) / 64;
     const int64_t* st = state + (int64_t)inst * 8;
     const uint32_t klo = (uint32_t)st[kStLo], khi = (uint32_t)st[kStHi];
@@ -824,27 +823,22 @@ __global__ __launch_bounds__(kColThreads) void th_collect_tiles_kernel(I64Arg of
 template <int CH = kChunk>
 __device__ __forceinline__ bool find_chunk(const I64Arg& offsets, int B, int64_t item, int& b,
                                            int64_t& first, int64_t& nch, int64_t& t0, int64_t& len) {
-    int64_t acc = 0;
-    for (int i = 0; i < B; ++i) {
-        int64_t n = offsets[i + 1] - offsets[i];
-        int64_t nb = (n + CH - 1) / CH;
-        if (item < acc + nb) {
-            b = i;
-            first = acc;
-            nch = nb;
-            t0 = (item - acc) * CH;
-            len = n - t0 < CH ? n - t0 : CH;
-            return true;
-        }
-        acc += nb;
-    }
-    return false;
+    const SeqPos sp = wave_find_seq(B, item, (offsets[1] - offsets[0] + CH - 1) / CH,
+                                    [od = offsets.dev](int i) { return (od[i + 1] - od[i] + CH - 1) / CH; });
+    if (sp.b < 0) return false;
+    b = sp.b;
+    first = sp.first;
+    nch = sp.cnt;
+    // one sequence: its length from the launch arguments; more: from device memory
+    const int64_t n = B == 1 ? offsets[1] - offsets[0] : offsets.dev[b + 1] - offsets.dev[b];
+    t0 = (item - first) * CH;
+    len = n - t0 < CH ? n - t0 : CH;
+    return true;
 }
 
+// list entries of the sequences before b (every lane of the wave calls it)
 __device__ __forceinline__ int64_t kpre_of(const I64Arg& offsets, int b, const DevCfg& c) {
-    int64_t k = 0;
-    for (int i = 0; i < b; ++i) k += budget_k(offsets[i + 1] - offsets[i], c.bnum, c.bden, c.sink, c.local);
-    return k;
+    return wave_prefix_seq(b, [od = offsets.dev, c](int i) { return budget_k(od[i + 1] - od[i], c.bnum, c.bden, c.sink, c.local); });
 }
 
 // -------------------------------------------------------------------------- votes
@@ -903,26 +897,22 @@ __global__ __launch_bounds__(kChunk) void vote_kernel(const float* __restrict__ 
 }
 
 // ------------------------------------------------------------ vote compaction
-// One block per 1024-token chunk c of sequence b.  The block first stages the key histograms of
-// all chunks of b in LDS (kScanTile rows at a time) and sums them into the totals and into the
-// counts of the chunks before c.  From the totals: need = K - |F|, the boundary key v* (largest
+// One block per 1024-token chunk c of sequence b.  The block first sums the key histograms of
+// all chunks of b (read straight from memory) into the totals and into the counts of the chunks
+// before c.  From the totals: need = K - |F|, the boundary key v* (largest
 // key whose suffix count reaches need; none when need == 0), gt = #keys above v* and
 // need_eq = need - gt.  The chunk's first selected token then has output rank
 //   forced_before(first token of c) + #keys above v* before c + min(eqb, need_eq),
 // eqb = #keys equal to v* before c, and each token of the chunk is placed by two block scans:
 // every forced token, every non-forced token above v* and the first need_eq - eqb tokens equal
 // to v* in position order, written ascending.
-constexpr int kScanTile = 256;
-
 __global__ __launch_bounds__(kChunk) void compact_vote_kernel(I64Arg offsets, int B,
                                                              DevCfg cfg, const uint8_t* __restrict__ keys,
                                                              const uint32_t* __restrict__ hist,
                                                              int32_t* __restrict__ idx_out,
                                                              int64_t* __restrict__ count_out) {
     constexpr int NG = kChunk / kVoteBins;          // row groups for the column sums
-    constexpr int V4 = kVoteBins / 4;               // uint4 per histogram row
-    constexpr int PER = (kScanTile * V4 + kChunk - 1) / kChunk;
-    __shared__ uint4 stage[kScanTile * V4];
+    constexpr int RU = 8;                           // histogram rows in flight per thread
     __shared__ uint32_t part[NG][kVoteBins][2];
     __shared__ uint32_t tot[kVoteBins], bef[kVoteBins];
     __shared__ int tmp[kChunk / 64];
@@ -934,39 +924,25 @@ __global__ __launch_bounds__(kChunk) void compact_vote_kernel(I64Arg offsets, in
     const int64_t off = offsets[b], n = offsets[b + 1] - off;
     const int64_t c = blockIdx.x - first;
     const uint8_t kk = t < len ? keys[off + t0 + t] : 0;
-    const uint4* hrows = reinterpret_cast<const uint4*>(hist + (size_t)first * kVoteBins);
-    // key totals over the sequence and over the chunks before c
+    const uint32_t* hrows = hist + (size_t)first * kVoteBins;
+    // key totals over the sequence and over the chunks before c: thread (grp, kb) sums column kb
+    // of the rows grp, grp + NG, ... straight from the histograms, RU rows in flight (no LDS
+    // staging, so the block's LDS stays small and two blocks fit on a CU)
     const int grp = t / kVoteBins, kb = t % kVoteBins;
     uint32_t at = 0, ab = 0;
     const int nchi = (int)nch, ci = (int)c;   // chunks of one sequence: < 2^14
-    for (int c0 = 0; c0 < nchi; c0 += kScanTile) {
-        const int rows = nchi - c0 < kScanTile ? nchi - c0 : kScanTile;
-        const int ne = rows * V4;
-        const uint4* src = hrows + (size_t)c0 * V4;
-        // all five loads first (clamped, unconditional), then the stores
-        static_assert(PER == 5, "staging is written out for five rows of uint4 per thread");
-        auto ld = [&](int u) {
-            const int e = t + u * kChunk;
-            return src[e < ne ? e : ne - 1];
-        };
-        const uint4 v0 = ld(0), v1 = ld(1), v2 = ld(2), v3 = ld(3), v4 = ld(4);
-        auto stv = [&](int u, const uint4& v) {
-            const int e = t + u * kChunk;
-            if (e < ne) stage[e] = v;
-        };
-        __syncthreads();                          // the previous tile has been consumed
-        stv(0, v0);
-        stv(1, v1);
-        stv(2, v2);
-        stv(3, v3);
-        stv(4, v4);
-        __syncthreads();
-        if (grp < NG) {
-            const uint32_t* st32 = reinterpret_cast<const uint32_t*>(stage);
-            for (int r = grp; r < rows; r += NG) {
-                const uint32_t x = st32[r * kVoteBins + kb];
-                at += x;
-                ab += (c0 + r < ci) ? x : 0u;
+    if (grp < NG) {
+        for (int r0 = grp; r0 < nchi; r0 += NG * RU) {
+            uint32_t x[RU];
+#pragma unroll
+            for (int u = 0; u < RU; ++u) {
+                const int r = r0 + u * NG;
+                x[u] = r < nchi ? hrows[(size_t)r * kVoteBins + kb] : 0u;
+            }
+#pragma unroll
+            for (int u = 0; u < RU; ++u) {
+                at += x[u];
+                ab += (r0 + u * NG < ci) ? x[u] : 0u;
             }
         }
     }
@@ -1086,8 +1062,7 @@ __global__ __launch_bounds__(kPhScanThreads) void ph_scan_kernel(I64Arg offsets,
     if (inst >= (int64_t)B * Hq) return;
     const int b = (int)(inst / Hq), h = (int)(inst % Hq);
     const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
-    int64_t first = 0;
-    for (int i = 0; i < b; ++i) first += (offsets[i + 1] - offsets[i] + kPhChunk - 1) / kPhChunk;
+    const int64_t first = wave_prefix_seq(b, [od = offsets.dev](int i) { return (od[i + 1] - od[i] + kPhChunk - 1) / kPhChunk; });
     const int64_t nch = (offsets[b + 1] - offsets[b] + kPhChunk - 1) / kPhChunk;
     uint2* row = reinterpret_cast<uint2*>(cnt) + (size_t)h * nitems + first;
     uint32_t carry0 = 0, carry1 = 0;
