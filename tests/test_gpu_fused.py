@@ -46,6 +46,22 @@ def test_ragged(lengths, budget, mode):
     check_staged(both(x, mode=mode))
 
 
+# more sequences than the 64 lanes of a wave: every kernel's sequence lookup takes two or
+# three rounds (lane i % 64 loads sequence i), with lengths from 1 token (shorter than sink +
+# local) to several 64-token tiles mixed in one batch
+@pytest.mark.parametrize("B", [70, 130])
+@pytest.mark.parametrize("mode", [api.MODE_VOTE, api.MODE_PER_HEAD])
+def test_many_sequences(B, mode):
+    lengths = np.random.default_rng(B).integers(1, 700, size=B)
+    x = synth.make_decode(4, lengths, 8, 2, lambda n: n // 100, False, (1, 5), 13)
+    st = both(x, mode=mode, local=64)
+    check_staged(st)
+    if mode == api.MODE_VOTE:
+        dense = api.dense_decode(st.q, st.K, st.V, st.offs)
+        torch.cuda.synchronize()
+        assert np.abs(f64(dense) - O.dense_decode(x.q, x.K, x.V, x.offsets, 8, 2)).max() <= 2e-3
+
+
 @pytest.mark.parametrize("Hq,Hkv", [(1, 1), (2, 1), (4, 1), (8, 1), (2, 2), (4, 2), (8, 2), (16, 2), (4, 4), (8, 4),
                                     (16, 4), (32, 4), (8, 8), (16, 8), (32, 8), (64, 8)])
 @pytest.mark.parametrize("mode", [api.MODE_VOTE, api.MODE_PER_HEAD])
