@@ -411,6 +411,14 @@ __global__ __launch_bounds__(kThThreads) void th_final_kernel(const float* __res
         const int sl = 2 * t + u;
         cp[u] = reinterpret_cast<const uint2*>(cs)[sl < SL ? sl : SL - 1];
     }
+    // rows with more than 2 kThThreads slices: the counts of the slices past the first
+    // 2 kThThreads (one more round trip; never taken up to 2^20 tokens with tiles, 2^22 without)
+    uint32_t more_lo = 0, more_mid = 0;
+    for (int sl = 2 * kThThreads + t; sl < SL; sl += kThThreads) {
+        const uint2 c = reinterpret_cast<const uint2*>(cs)[sl];
+        more_lo += c.x;
+        more_mid += c.y;
+    }
     uint32_t dlo = 0, dhi = 0;
     {
         constexpr int SLR = 32;
@@ -436,7 +444,7 @@ __global__ __launch_bounds__(kThThreads) void th_final_kernel(const float* __res
     // slices: of the key range [beg, end), or of the sequence's tiles (tile classification)
     const int nsl = tiles ? (int)(((nrow + 63) / 64 + kTilesPerSlice - 1) / kTilesPerSlice)
                           : (int)((m + kSlice - 1) / kSlice);
-    int lsum = 0, csum = 0;
+    int lsum = (int)more_lo, csum = (int)more_mid;
 #pragma unroll
     for (int u = 0; u < 2; ++u)
         if (2 * t + u < SL) { lsum += (int)cp[u].x; csum += (int)cp[u].y; }
@@ -495,27 +503,32 @@ __global__ __launch_bounds__(kThThreads) void th_final_kernel(const float* __res
                     }
                     __syncthreads();
                 } else {
-                    // large bucket: every thread copies keys, 16 in flight
-                    int la[2], ll[2];
+                    // large bucket: every thread copies keys, 16 in flight.  The slices' segments
+                    // are laid end to end, 2 kThThreads slices per pass.
+                    int ntot = 0;
+                    for (int sl0 = 0; sl0 < nsl; sl0 += 2 * kThThreads) {
+                        int la[2], ll[2];
 #pragma unroll
-                    for (int u = 0; u < 2; ++u) {
-                        const int sl = 2 * t + u;
-                        la[u] = 0;
-                        ll[u] = 0;
-                        if (sl < nsl) {
-                            la[u] = (int)pre_at(sl, D);
-                            ll[u] = (int)pre_at(sl, D + 1) - la[u];
+                        for (int u = 0; u < 2; ++u) {
+                            const int sl = sl0 + 2 * t + u;
+                            la[u] = 0;
+                            ll[u] = 0;
+                            if (sl < nsl) {
+                                la[u] = (int)pre_at(sl, D);
+                                ll[u] = (int)pre_at(sl, D + 1) - la[u];
+                            }
                         }
-                    }
-                    int ntot;
-                    const int sinc = block_inclusive_scan<kThThreads>(ll[0] + ll[1], tmp, &ntot);
+                        int npass;
+                        const int sinc = block_inclusive_scan<kThThreads>(ll[0] + ll[1], tmp, &npass);
 #pragma unroll
-                    for (int u = 0; u < 2; ++u) {
-                        const int sl = 2 * t + u;
-                        if (sl < nsl) {
-                            segpre[sl] = sinc - ll[0] - ll[1] + (u ? ll[0] : 0);
-                            sega[sl] = la[u];
+                        for (int u = 0; u < 2; ++u) {
+                            const int sl = sl0 + 2 * t + u;
+                            if (sl < nsl) {
+                                segpre[sl] = ntot + sinc - ll[0] - ll[1] + (u ? ll[0] : 0);
+                                sega[sl] = la[u];
+                            }
                         }
+                        ntot += npass;
                     }
                     if (t == 0) segpre[nsl] = ntot;
                     __syncthreads();

@@ -37,10 +37,14 @@ def rng_for(config: int, step: int = 0) -> np.random.Generator:
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """Round fp32 to bf16 (nearest, ties to even) and return uint16 bit patterns."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    return u.astype(np.uint16)
+    """Round finite fp32 to bf16 (nearest, ties to even) and return uint16 bit patterns.
+    In uint32: the largest finite pattern plus 0x8000 stays below 2^32."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = (u >> 16) & np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += u
+    r >>= 16
+    return r.astype(np.uint16)
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
