@@ -411,8 +411,8 @@ __global__ __launch_bounds__(kThThreads) void th_final_kernel(const float* __res
         const int sl = 2 * t + u;
         cp[u] = reinterpret_cast<const uint2*>(cs)[sl < SL ? sl : SL - 1];
     }
-    // rows with more than 2 kThThreads slices: the counts of the slices past the first
-    // 2 kThThreads (one more round trip; never taken up to 2^20 tokens with tiles, 2^22 without)
+    // rows with more than 2 kThThreads slices (of 8192 keys, or 128 tiles: past 2^22 tokens):
+    // the counts of the slices past the first 2 kThThreads, one more round trip
     uint32_t more_lo = 0, more_mid = 0;
     for (int sl = 2 * kThThreads + t; sl < SL; sl += kThThreads) {
         const uint2 c = reinterpret_cast<const uint2*>(cs)[sl];

@@ -7,8 +7,6 @@ cover the bracket path (rows longer than the sample threshold), rows short enoug
 every key as a candidate, the whole-row fallback (heavy ties, rows whose bracket holds more
 keys than the LDS capacity), ragged batches, every head layout and the full-size workloads.
 """
-import functools
-
 import numpy as np
 import pytest
 import torch
@@ -62,18 +60,6 @@ def test_many_sequences(B, mode):
         dense = api.dense_decode(st.q, st.K, st.V, st.offs)
         torch.cuda.synchronize()
         assert np.abs(f64(dense) - O.dense_decode(x.q, x.K, x.V, x.offsets, 8, 2)).max() <= 2e-3
-
-
-# a row of more than 2 x 256 tile slices (2048 tokens each): the final kernel's slice counts
-# and candidate segments take more than one pass of its 256 threads
-@functools.lru_cache(maxsize=1)
-def _row_of_1_2m_tokens():
-    return synth.make_decode(4, [1_200_000], 2, 1, 1000, False, (1, 5), 17)
-
-
-@pytest.mark.parametrize("mode", [api.MODE_VOTE, api.MODE_PER_HEAD])
-def test_rows_past_512_slices(mode):
-    check_staged(both(_row_of_1_2m_tokens(), mode=mode))
 
 
 @pytest.mark.parametrize("Hq,Hkv", [(1, 1), (2, 1), (4, 1), (8, 1), (2, 2), (4, 2), (8, 2), (16, 2), (4, 4), (8, 4),
