@@ -281,35 +281,45 @@ __global__ __launch_bounds__(score_threads<HKV>()) void score_kernel(const float
     }
     if constexpr (CLS) {
         static_assert(kScoreTB == 64, "one wave lane per tile token");
-        // wave w takes heads w, w + NW, ...; lane = token of the tile; each head reserves its run of
-        // keys with one LDS atomic.
+        // wave w takes heads w, w + NW, ...; lane = token of the tile; the wave reserves the runs
+        // of keys of its heads with one LDS atomic.
         constexpr int NW = NT / 64;
         static_assert(NW == NWC, "one wave count");
         const uint64_t lt = (1ull << lane) - 1ull;
+        uint32_t below[HPW], cnt[HPW], key[HPW];
+        uint64_t mm[HPW];
+#pragma unroll
+        for (int i = 0; i < HPW; ++i) {
+            const int h = wu + i * NW;
+            below[i] = 0;
+            key[i] = 0;
+            mm[i] = 0;
+            if (h < Hq && c_flag[i] == 0) {              // an active order statistic
+                const uint32_t lo = (uint32_t)c_lo[i], hi = (uint32_t)c_hi[i];
+                const int64_t t = t0 + lane;
+                const bool valid = lane < len && t >= c_beg[i] && t < c_end[i];
+                key[i] = order_key(tile[h * kTileLd + lane]);
+                below[i] = (uint32_t)__popcll(__ballot(valid && key[i] < lo));
+                mm[i] = __ballot(valid && key[i] >= lo && key[i] <= hi);
+            }
+            cnt[i] = (uint32_t)__popcll(mm[i]);
+        }
+        // one reservation in the tile's key area for the wave's heads, whose runs follow each
+        // other (the heads of the tile in any order)
+        uint32_t tot = 0;
+#pragma unroll
+        for (int i = 0; i < HPW; ++i) tot += cnt[i];
+        uint32_t off = 0;
+        if (lane == 0 && tot) off = atomicAdd(&s_run, tot);
+        off = __builtin_amdgcn_readfirstlane(off);
 #pragma unroll
         for (int i = 0; i < HPW; ++i) {
             const int h = wu + i * NW;
             if (h >= Hq) continue;
-            uint32_t below = 0, key = 0;
-            uint64_t mm = 0;
-            if (c_flag[i] == 0) {                        // an active order statistic
-                const uint32_t lo = (uint32_t)c_lo[i], hi = (uint32_t)c_hi[i];
-                const int64_t t = t0 + lane;
-                const bool valid = lane < len && t >= c_beg[i] && t < c_end[i];
-                key = order_key(tile[h * kTileLd + lane]);
-                below = (uint32_t)__popcll(__ballot(valid && key < lo));
-                mm = __ballot(valid && key >= lo && key <= hi);
-            }
-            // the head's run of keys in the tile's key area (any order of the heads)
-            const uint32_t c = (uint32_t)__popcll(mm);
-            uint32_t offh = 0;
-            if (lane == 0) {
-                offh = c ? atomicAdd(&s_run, c) : 0u;
-                cls.tcnt[(size_t)blockIdx.x * Hq + h] = below | (c << 8) | (offh << 16);
-            }
-            offh = __shfl(offh, 0, 64);
-            if ((mm >> lane) & 1ull)
-                cls.tcand[(size_t)blockIdx.x * kClsTile + offh + __popcll(mm & lt)] = key;
+            if (lane == 0) cls.tcnt[(size_t)blockIdx.x * Hq + h] = below[i] | (cnt[i] << 8) | (off << 16);
+            if ((mm[i] >> lane) & 1ull)
+                cls.tcand[(size_t)blockIdx.x * kClsTile + off + __popcll(mm[i] & lt)] = key[i];
+            off += cnt[i];
         }
     }
 }
