@@ -30,7 +30,7 @@ namespace qasi {
 
 constexpr int kDecWaves = 4;                       // waves per block
 constexpr int kDecSub = 16;                        // entries per sub-batch of a wave
-constexpr int kDecMaxEW = 256;                     // entries per wave at most
+constexpr int kDecMaxEW = 512;                     // entries per wave at most
 constexpr float kLog2eOverSqrtD = 1.4426950408889634f / 11.313708498984761f;
 
 // query heads served by a wave
@@ -138,8 +138,12 @@ __device__ __forceinline__ void rows_tsum(const float (&v)[NA], float (&o)[NA / 
 
 // MODE 0: shared list per sequence (vote); MODE 1: list per query head; MODE 2: dense
 // (the list is implicit: entry j is token j, counts are the sequence lengths).
+// Blocks per CU to keep: 3 (12 waves) for the shared-list modes with G <= 4, whose registers fit
+// in 168 (512 / 3) per lane; no bound otherwise.
+__host__ __device__ constexpr int dec_min_blocks(int G, int mode) { return (mode != 1 && G <= 4) ? 3 : 1; }
+
 template <int G, int MODE>
-__global__ __launch_bounds__(kDecWaves * 64) void decode_partial_kernel(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(kDecWaves * 64, dec_min_blocks(G, MODE)) void decode_partial_kernel(const uint16_t* __restrict__ q,
                                                                        const uint16_t* __restrict__ K,
                                                                        const uint16_t* __restrict__ V,
                                                                        I64Arg offsets,
@@ -447,14 +451,31 @@ static int partial_blocks_per_cu(int G, int mode) {
 }
 
 // Entries per block: the whole work (entries x HW blocks per range) spread over one round of
-// resident blocks; a multiple of 4, at least one sub-batch per wave and at most kDecMaxEW
-// entries per wave.
-static int decode_eb(int64_t entries, int HW, int G, int mode) {
+// resident blocks; a multiple of 4 and at least one sub-batch per wave.  With a list shared by
+// a sequence's heads (vote mode), each sequence's last range is partial, so EB then grows (by
+// 1/16 at a time, up to kDecMaxEW entries per wave) until the ranges of all sequences fit in
+// that round.  Per-head lists and the dense decode keep EB at most 256 entries per wave: there
+// the extra round of smaller blocks measured faster (ragged per-head batch 553 against 561 us,
+// dense 128K decode 106 against 110 us).  len(b) is the list length (or, for the dense decode,
+// the sequence length) of sequence b.
+template <class Len>
+static int decode_eb(Len len, int B, int HW, int G, int mode) {
     const int64_t target = (int64_t)partial_blocks_per_cu(G, mode) * device_cus();
-    int64_t eb = (entries * HW + target - 1) / target;
-    eb = (eb + 3) / 4 * 4;
-    if (eb < kDecWaves * kDecSub) eb = kDecWaves * kDecSub;
-    if (eb > kDecWaves * kDecMaxEW) eb = kDecWaves * kDecMaxEW;
+    int64_t entries = 0;
+    for (int b = 0; b < B; ++b) entries += len(b);
+    const int64_t lo = kDecWaves * kDecSub, hi = kDecWaves * (mode == 0 ? kDecMaxEW : 256);
+    auto clampr = [&](int64_t e) {
+        e = (e + 3) / 4 * 4;
+        return e < lo ? lo : (e > hi ? hi : e);
+    };
+    int64_t eb = clampr((entries * HW + target - 1) / target);
+    auto blocks = [&](int64_t e) {
+        int64_t it = 0;
+        for (int b = 0; b < B; ++b) it += (len(b) + e - 1) / e;
+        return it * HW;
+    };
+    if (mode == 0)
+        while (eb < hi && blocks(eb) > target) eb = clampr(eb + (eb + 15) / 16);
     return (int)eb;
 }
 
@@ -501,7 +522,7 @@ hipError_t launch_sparse_decode(const uint16_t* q, const uint16_t* K, const uint
     const int G = Hq / Hkv;
     int64_t total = 0;
     for (int b = 0; b < B; ++b) total += counts_host[b];
-    const int EB = decode_eb(total, mode == 1 ? Hq : Hkv, G, mode);
+    const int EB = decode_eb([&](int b) { return counts_host[b]; }, B, mode == 1 ? Hq : Hkv, G, mode);
     WsCarver w(ws);
     w.take<int64_t>((size_t)B + 1);
     const int64_t items = list_items(counts_host, B, EB);
@@ -528,7 +549,7 @@ hipError_t launch_dense_decode(const uint16_t* q, const uint16_t* K, const uint1
                                size_t ws_bytes, hipStream_t stream) {
     if (decode_workspace(offsets_host, nullptr, B, Hq, Hkv, 2) > ws_bytes) return hipErrorInvalidValue;
     const int G = Hq / Hkv;
-    const int EB = decode_eb(offsets_host[B] - offsets_host[0], Hkv, G, 2);
+    const int EB = decode_eb([&](int b) { return offsets_host[b + 1] - offsets_host[b]; }, B, Hkv, G, 2);
     int64_t items = 0;
     for (int b = 0; b < B; ++b) items += (offsets_host[b + 1] - offsets_host[b] + EB - 1) / EB;
     WsCarver w(ws);
