@@ -427,6 +427,9 @@ __global__ __launch_bounds__(kThThreads) void th_final_kernel(const float* __res
             uint32_t w[SLR];
 #pragma unroll
             for (int u = 0; u < SLR; ++u) w[u] = dc[(size_t)(sl0 + u < SL ? sl0 + u : SL - 1) * kDpWords];
+            // every load of the batch is issued before the first sum (else the scheduler starts
+            // the sums early and the last loads wait a round trip)
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int u = 0; u < SLR; ++u) {
                 const uint32_t x = sl0 + u < SL ? w[u] : 0u;
@@ -663,18 +666,30 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const uint16_t* __re
     const bool sampled = oi.flag == kFlagActive && oi.end - oi.beg > kCap && ms >= kRuns * kRunLen;
     static_assert(kPrepSample / kRunLen <= kRuns, "sample runs within the strata of sample_pos");
     const int part = t & 3;
+    // P and q first, then the sample rows: staging P and q waits for them alone, and the
+    // samples arrive while q' is formed.  The loads and the staging are one basic block: a
+    // branch would let the compiler move the P and q loads past the sample loads, to their use.
+    // Without a sample every lane reads the start of P (the offset is multiplied by 0).
+    static_assert(kD * kDP / 4 == 2 * kPrepThreads && kD <= kPrepThreads && (kD & (kD - 1)) == 0,
+                  "two float4 of P and one q value per thread");
+    const float4* P4 = reinterpret_cast<const float4*>(P);
+    const float4 p0 = P4[t], p1 = P4[t + kPrepThreads];
+    const uint16_t qb = q[((int64_t)b * Hq + h) * kD + (t & (kD - 1))];
+    __builtin_amdgcn_sched_barrier(0);
+    const int64_t use = sampled ? 1 : 0;
+    const int64_t ms_pos = sampled ? ms : (int64_t)kRuns * kRunLen;   // a valid range either way
+    const uint16_t* sbase = sampled ? k_index : reinterpret_cast<const uint16_t*>(P);
     uint4 kv[PASSES];
-    if (sampled) {
 #pragma unroll
-        for (int u = 0; u < PASSES; ++u) {
-            const int i = u * (kPrepThreads / 4) + (t >> 2);
-            const int64_t pos = oi.beg + sample_pos(i, ms, inst);
-            kv[u] = ld16(k_index + ((off + pos) * Hkv + g) * kDP + part * 8);
-        }
+    for (int u = 0; u < PASSES; ++u) {
+        const int i = u * (kPrepThreads / 4) + (t >> 2);
+        const int64_t pos = oi.beg + sample_pos(i, ms_pos, inst);
+        kv[u] = ld16(sbase + (((off + pos) * Hkv + g) * kDP + part * 8) * use);
     }
-    for (int i = t; i < kD * kDP / 4; i += kPrepThreads)
-        reinterpret_cast<float4*>(sP)[i] = reinterpret_cast<const float4*>(P)[i];
-    for (int j = t; j < kD; j += kPrepThreads) sq[j] = bf16_to_f32(q[((int64_t)b * Hq + h) * kD + j]);
+    __builtin_amdgcn_sched_barrier(0);
+    reinterpret_cast<float4*>(sP)[t] = p0;
+    reinterpret_cast<float4*>(sP)[t + kPrepThreads] = p1;
+    sq[t & (kD - 1)] = bf16_to_f32(qb);     // threads t and t + kD store the same value
     __syncthreads();
     if (t < 4 * kDP) {
         // partial k of q'[c] over j in [32k, 32k + 32), in order (the order of qproj_kernel)
@@ -925,7 +940,7 @@ __global__ __launch_bounds__(kChunk) void compact_vote_kernel(I64Arg offsets, in
                                                              int32_t* __restrict__ idx_out,
                                                              int64_t* __restrict__ count_out) {
     constexpr int NG = kChunk / kVoteBins;          // row groups for the column sums
-    constexpr int RU = 8;                           // histogram rows in flight per thread
+    constexpr int RU = 16;                          // histogram rows in flight per thread
     __shared__ uint32_t part[NG][kVoteBins][2];
     __shared__ uint32_t tot[kVoteBins], bef[kVoteBins];
     __shared__ int tmp[kChunk / 64];
@@ -940,7 +955,9 @@ __global__ __launch_bounds__(kChunk) void compact_vote_kernel(I64Arg offsets, in
     const uint32_t* hrows = hist + (size_t)first * kVoteBins;
     // key totals over the sequence and over the chunks before c: thread (grp, kb) sums column kb
     // of the rows grp, grp + NG, ... straight from the histograms, RU rows in flight (no LDS
-    // staging, so the block's LDS stays small and two blocks fit on a CU)
+    // staging, so the block's LDS stays small and two blocks fit on a CU).  NG * RU = 224 rows
+    // per pass: one memory round trip for sequences of up to 224 chunks.  Rows past the end are
+    // loaded as the last row and not counted, so the loads need no branch.
     const int grp = t / kVoteBins, kb = t % kVoteBins;
     uint32_t at = 0, ab = 0;
     const int nchi = (int)nch, ci = (int)c;   // chunks of one sequence: < 2^14
@@ -950,11 +967,11 @@ __global__ __launch_bounds__(kChunk) void compact_vote_kernel(I64Arg offsets, in
 #pragma unroll
             for (int u = 0; u < RU; ++u) {
                 const int r = r0 + u * NG;
-                x[u] = r < nchi ? hrows[(size_t)r * kVoteBins + kb] : 0u;
+                x[u] = hrows[(size_t)(r < nchi ? r : nchi - 1) * kVoteBins + kb];
             }
 #pragma unroll
             for (int u = 0; u < RU; ++u) {
-                at += x[u];
+                at += (r0 + u * NG < nchi) ? x[u] : 0u;
                 ab += (r0 + u * NG < ci) ? x[u] : 0u;
             }
         }
