@@ -365,30 +365,37 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const float
     float M = -INFINITY, A = 0.f, L = 0.f;
     for (int64_t c0 = cg; c0 < nch; c0 += (int64_t)NG * U) {
         float x[U], mm[U], ll[U];
+        float2 ml[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t c = c0 + (int64_t)NG * u;
             const int64_t slot = (first + (c < nch ? c : c0)) * Hq + h;
             x[u] = part_acc[slot * kD + d];
-            const float2 ml = part_ml[slot];
-            mm[u] = c < nch ? ml.x : -INFINITY;
-            ll[u] = ml.y;
+            ml[u] = part_ml[slot];
         }
+        // every load of the batch is issued before the first use
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            mm[u] = c0 + (int64_t)NG * u < nch ? ml[u].x : -INFINITY;
+            ll[u] = ml[u].y;
+        }
+        // no branch on Mn: the compiler would move the x and l loads into it, behind the wait
+        // for the maxima.  Only the clamped slots past the list's end have m = -inf (every chunk
+        // holds entries), and their weights are 0; while Mn = -inf, A and L stay 0.
         float Mn = M;
 #pragma unroll
         for (int u = 0; u < U; ++u) Mn = fmaxf(Mn, mm[u]);
-        if (Mn != -INFINITY) {
-            const float rs = M == -INFINITY ? 0.f : fast_exp2(M - Mn);
-            A *= rs;
-            L *= rs;
+        const float rs = M == -INFINITY ? 0.f : fast_exp2(M - Mn);
+        A *= rs;
+        L *= rs;
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const float w = mm[u] == -INFINITY ? 0.f : fast_exp2(mm[u] - Mn);
-                A = fmaf(x[u], w, A);
-                L = fmaf(ll[u], w, L);
-            }
-            M = Mn;
+        for (int u = 0; u < U; ++u) {
+            const float w = mm[u] == -INFINITY ? 0.f : fast_exp2(mm[u] - Mn);
+            A = fmaf(x[u], w, A);
+            L = fmaf(ll[u], w, L);
         }
+        M = Mn;
     }
     sA[cg][d] = A;
     if (d == 0) { sM[cg] = M; sL[cg] = L; }
