@@ -194,7 +194,7 @@ __global__ __launch_bounds__(score_threads<HKV>()) void score_kernel(const float
     constexpr int TPB = TPW * (NT / 64);  // tokens per block per load
     static_assert(NT % 64 == 0 && kScoreTB % TPB == 0, "whole waves, whole passes over the tile");
     constexpr int ITERS = kScoreTB / TPB;
-    constexpr int UNR = ITERS < 8 ? ITERS : 8;
+    static_assert(ITERS <= 4, "the tile's rows are loaded up front");
     constexpr int NOUT = G >= 4 ? G / 4 : 1;          // complete heads per lane
     __shared__ float tile[Hq * kTileLd];
     __shared__ uint32_t s_run;
@@ -228,12 +228,14 @@ __global__ __launch_bounds__(score_threads<HKV>()) void score_kernel(const float
     const int lit = lane % LPT, g = lit / 4, part = lit % 4;
     const int slot = wid * TPW + lane / LPT;
 
-    uint4 kv[UNR];
+    // the tile's index rows, all loads in flight at once: lanes past the tile's end read its
+    // first row (their values are never used), so the loads need no branch and no merge copy
+    // (a zeroed register merged with a conditional load makes the compiler wait for it)
+    uint4 kv[ITERS];
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) {
+    for (int u = 0; u < ITERS; ++u) {
         const int tl = u * TPB + slot;
-        kv[u] = make_uint4(0, 0, 0, 0);
-        if (tl < len) kv[u] = ld16(k_index + ((base_tok + tl) * HKV + g) * kDP + part * 8);
+        kv[u] = ld16(k_index + ((base_tok + (tl < len ? tl : 0)) * HKV + g) * kDP + part * 8);
     }
     float qr[G][8];
 #pragma unroll
@@ -247,16 +249,11 @@ __global__ __launch_bounds__(score_threads<HKV>()) void score_kernel(const float
     const bool writer = (G >= 4) || (G == 2 ? part < 2 : part == 0);
     const int hrow = g * G + (G >= 4 ? part : (G == 2 ? (part & 1) : 0));
 
-    for (int it0 = 0; it0 < ITERS; it0 += UNR) {
+    {
 #pragma unroll
-        for (int u = 0; u < UNR; ++u) {
-            const int tl = (it0 + u) * TPB + slot;
+        for (int u = 0; u < ITERS; ++u) {
+            const int tl = u * TPB + slot;
             const uint4 w = kv[u];
-            if (it0 + UNR < ITERS) {
-                const int tn = (it0 + UNR + u) * TPB + slot;
-                kv[u] = make_uint4(0, 0, 0, 0);
-                if (tn < len) kv[u] = ld16(k_index + ((base_tok + tn) * HKV + g) * kDP + part * 8);
-            }
             const float kf[8] = {bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y),
                                  bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w)};
             float v[G];
