@@ -12,7 +12,8 @@
  *
  * Common conventions
  *   - d = 128 (head dimension) and d' = 32 (index dimension) are fixed; Hkv must be 1, 2,
- *     4 or 8 and G = Hq / Hkv an integer in 1..8 (query head h reads KV head h / G).
+ *     4 or 8, G = Hq / Hkv must be 1, 2, 4 or 8 (query head h reads KV head h / G) and
+ *     Hq <= 64.  Other layouts return QASI_ERR_UNSUPPORTED.
  *   - bf16 tensors are passed as uint16_t bit patterns.  All device pointers must be
  *     16-byte aligned.
  *   - Caches are token-major and packed over a ragged batch: K[t][g][128], V[t][g][128],

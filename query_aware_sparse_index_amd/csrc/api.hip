@@ -85,8 +85,9 @@ int to_cfg(const ts_select_params* p, qasi::SelectConfig* c) {
     if (p->sink < 0 || p->local < 0 || p->sink > ((int64_t)1 << 31) || p->local > ((int64_t)1 << 31))
         return fail(QASI_ERR_INVALID, "sink/local must be in [0, 2^31]");
     if (p->mode == QASI_MODE_VOTE) {
-        if (p->theta_den <= 0 || p->theta_num < 0 || p->theta_num > p->theta_den)
-            return fail(QASI_ERR_INVALID, "theta %lld/%lld must be in [0, 1]", (long long)p->theta_num, (long long)p->theta_den);
+        if (p->theta_den <= 0 || p->theta_num < 0 || p->theta_num > p->theta_den || p->theta_den > ((int64_t)1 << 31))
+            return fail(QASI_ERR_INVALID, "theta %lld/%lld must be in [0, 1] with a denominator of at most 2^31",
+                        (long long)p->theta_num, (long long)p->theta_den);
         if (p->v_min < 0) return fail(QASI_ERR_INVALID, "v_min must be >= 0");
     }
     c->mode = p->mode;
@@ -271,6 +272,8 @@ int snapkv_compress(const uint16_t* q_obs, const uint16_t* K, const uint16_t* V,
         (pooled_out && (reinterpret_cast<uintptr_t>(pooled_out) & 3u)))
         return fail(QASI_ERR_INVALID, "importance_out / pooled_out misaligned");
     if (n <= 0 || n >= ((int64_t)1 << 31)) return fail(QASI_ERR_INVALID, "n=%lld outside [1, 2^31)", (long long)n);
+    if (n > ((int64_t)1 << 24))
+        return fail(QASI_ERR_UNSUPPORTED, "n=%lld longer than 2^24 tokens (selection limit)", (long long)n);
     if (w <= 0 || c <= 0) return fail(QASI_ERR_INVALID, "w=%d and c=%lld must be positive", w, (long long)c);
     if (int r = check_heads(Hq, Hkv)) return r;
     if (pool_kernel != 3) return fail(QASI_ERR_UNSUPPORTED, "pool_kernel=%d (only 3 is built)", pool_kernel);

@@ -127,12 +127,13 @@ __host__ __device__ __forceinline__ int top_shift(uint32_t span) {
     return nbits > kDigit ? nbits - kDigit : 0;
 }
 
-// Position (relative to the range start) of sample i of an instance over a range of m keys:
-// run j = i / kRunLen starts at a hashed position of stratum [j m / kRuns, (j + 1) m / kRuns).
-// Needs m >= kRuns * kRunLen.
-__device__ __forceinline__ int64_t sample_pos(int i, int64_t m, int inst) {
+// Position (relative to the range start) of sample i of an instance over a range of m keys,
+// for a sample of `runs` runs of kRunLen keys: run j = i / kRunLen starts at a hashed position of
+// stratum [j m / runs, (j + 1) m / runs), so the runs cover the whole range.  Needs
+// m >= runs * kRunLen.
+__device__ __forceinline__ int64_t sample_pos(int i, int64_t m, int inst, int runs) {
     const int j = i / kRunLen;
-    const int64_t a = (int64_t)j * m / kRuns, e = (int64_t)(j + 1) * m / kRuns;
+    const int64_t a = (int64_t)j * m / runs, e = (int64_t)(j + 1) * m / runs;
     const uint32_t r = mix32((uint32_t)j * 0x9e3779b9u ^ mix32((uint32_t)inst + 0x632be5abu));
     return a + (int64_t)(r % (uint32_t)(e - a - kRunLen + 1)) + (i % kRunLen);
 }
@@ -150,7 +151,7 @@ __device__ void sample_bracket(const float* __restrict__ row, const OsInst& oi, 
     const int64_t m = oi.end - oi.beg;
     float v[PER];
 #pragma unroll
-    for (int u = 0; u < PER; ++u) v[u] = row[oi.beg + sample_pos(threadIdx.x + u * kColThreads, m, inst)];
+    for (int u = 0; u < PER; ++u) v[u] = row[oi.beg + sample_pos(threadIdx.x + u * kColThreads, m, inst, kRuns)];
     bracket_of_sample<kSample, kDelta>(v, oi, hist, wmin, wmax, tmp, sb, klo, khi);
 }
 
@@ -664,7 +665,8 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const uint16_t* __re
     const int64_t send = (K && oi.end == n) ? n - 1 : oi.end;
     const int64_t ms = send - oi.beg;
     const bool sampled = oi.flag == kFlagActive && oi.end - oi.beg > kCap && ms >= kRuns * kRunLen;
-    static_assert(kPrepSample / kRunLen <= kRuns, "sample runs within the strata of sample_pos");
+    constexpr int kPrepRuns = kPrepSample / kRunLen;   // one stratum of the range per run
+    static_assert(kPrepRuns <= kRuns, "a sampled range (>= kRuns kRunLen keys) holds every run");
     const int part = t & 3;
     // P and q first, then the sample rows: staging P and q waits for them alone, and the
     // samples arrive while q' is formed.  The loads and the staging are one basic block: a
@@ -683,7 +685,7 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const uint16_t* __re
 #pragma unroll
     for (int u = 0; u < PASSES; ++u) {
         const int i = u * (kPrepThreads / 4) + (t >> 2);
-        const int64_t pos = oi.beg + sample_pos(i, ms_pos, inst);
+        const int64_t pos = oi.beg + sample_pos(i, ms_pos, inst, kPrepRuns);
         kv[u] = ld16(sbase + (((off + pos) * Hkv + g) * kDP + part * 8) * use);
     }
     __builtin_amdgcn_sched_barrier(0);

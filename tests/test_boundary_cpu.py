@@ -96,7 +96,7 @@ def test_select_validation():
     L = _lib.load()
     o = _offs([0, 4096])
     for p, code in [(_params(mode=2), -1), (_params(bden=0), -1), (_params(tn=11, td=10), -1), (_params(sink=-1), -1),
-                    (_params(vmin=-1), -1)]:
+                    (_params(vmin=-1), -1), (_params(tn=1, td=(1 << 31) + 1), -1), (_params(bnum=1, bden=(1 << 31) + 1), -1)]:
         assert L.ts_select(FAKE, FAKE, o, 1, 8, 2, ctypes.byref(p), FAKE, FAKE, None, None, FAKE, 1 << 40, None) == code
     p = _params()
     need = L.ts_select_workspace_bytes(o, 1, 8, ctypes.byref(p))
@@ -154,6 +154,9 @@ def test_snapkv_validation():
     assert L.snapkv_compress(*args(1000, 64, 64, 8, 4096, 3)) == -2     # G*w = 512
     assert L.snapkv_compress(*args(0, 32, 64, 8, 4096, 3)) == -1
     assert L.snapkv_compress(*args(1000, 32, 64, 8, 0, 3)) == -1
+    # longer than the top-c selection supports: rejected before anything is enqueued
+    assert L.snapkv_compress(*args((1 << 24) + 1, 32, 64, 8, 4096, 3)) == -2
+    assert "2^24" in err()
     need = L.snapkv_workspace_bytes(1000, 32, 64, 8, 4096)
     assert need > 0
     a = list(args(1000, 32, 64, 8, 4096, 3))

@@ -1,0 +1,107 @@
+"""End-to-end selection parity (the spec rule) and the full-size budget sweep.
+
+The staged checks compare each stage with the oracle run on the GPU's own input to that stage.
+Here the GPU lists are also compared with the oracle run end to end on its own fp64 scores
+(from the same index rows, which are bit-exact): in vote mode every GPU vote must lie within
+the number of near-tied heads of the oracle's, and every token in which the lists differ must
+be such a near token or carry the oracle's boundary key; in per-head mode every differing token
+must have an oracle score within 1e-5 relative of its head's boundary score (gpu_util.check_endtoend).
+
+The sweep runs the LLaMA-3-8B-shaped layer at n = 131072 + 1 (the step's appended token) at
+every budget of the pages' sensitivity analysis (5, 10, 15, 20, 30 %) in both modes, through
+ts_score_select and ts_sparse_decode, with the staged checks, the decode of the GPU lists and
+the end-to-end rule; the ragged Mistral-7B-shaped batch runs in both modes as well.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from query_aware_sparse_index_amd import api, synth
+
+from gpu_util import FusedStep, Step, check_endtoend, check_staged, dev, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+
+
+@pytest.mark.parametrize("cfg", ["c1", "c2"])
+@pytest.mark.parametrize("mode", [api.MODE_VOTE, api.MODE_PER_HEAD])
+def test_small_configs_end_to_end(cfg, mode):
+    x = synth.config1() if cfg == "c1" else synth.config2()
+    for cls in (Step, FusedStep):
+        st = cls(x, mode=mode).run()
+        r = check_staged(st)
+        r.update(check_endtoend(st))
+        print(cfg, mode, cls.__name__, r)
+
+
+class _C3:
+    """The C3 layer after one decode step: device copies and the oracle's index, built once."""
+
+    def __init__(self):
+        x = synth.config3(20, 131072)
+        q1, k1, v1 = synth.config3_step(1, x.q, x.Hkv)
+        x.K = np.concatenate([x.K, k1])
+        x.V = np.concatenate([x.V, v1])
+        x.q = q1
+        x.offsets = np.array([0, 131073], np.int64)
+        self.x = x
+        self.index_ref = O.index_project(x.K, x.P)
+        self.q, self.K, self.V, self.P = to_dev(x.q), to_dev(x.K), to_dev(x.V), to_dev(x.P)
+        n = int(x.offsets[-1])
+        self.kidx0 = torch.empty((n, x.Hkv, 32), dtype=torch.int16, device=dev())
+        api.index_append(self.K[:n - 1], self.P, self.kidx0[:n - 1], 0)
+        torch.cuda.synchronize()
+
+
+@pytest.fixture(scope="module")
+def c3():
+    return _C3()
+
+
+class _SweepStep(FusedStep):
+    """A FusedStep on prebuilt device arrays (the index rows before the appended token)."""
+
+    def __init__(self, c3, mode, budget):
+        self.x = c3.x
+        self.Hq, self.Hkv = c3.x.Hq, c3.x.Hkv
+        self.n = int(c3.x.offsets[-1])
+        self.q, self.K, self.V, self.P = c3.q, c3.K, c3.V, c3.P
+        self.offs = api.Offsets(c3.x.offsets, dev())
+        self.p = api.params(mode, budget)
+        self.mode = mode
+        self._kidx0 = c3.kidx0
+
+    def run(self):
+        self.kidx = self._kidx0.clone()
+        self.sel = api.score_select(self.q, self.P, self.kidx, self.offs, self.Hkv, self.p, K_last=self.K,
+                                    want_theta=True, want_votes=True)
+        self.scores = self.sel["scores"]
+        self.out = api.sparse_decode(self.q, self.K, self.V, self.offs, self.sel["idx"], self.sel["count"],
+                                     self.sel["counts_host"], self.mode)
+        torch.cuda.synchronize()
+        return self
+
+
+@pytest.mark.parametrize("pct", [5, 10, 15, 20, 30])
+@pytest.mark.parametrize("mode", [api.MODE_VOTE, api.MODE_PER_HEAD])
+def test_c3_budget_sweep(c3, pct, mode):
+    st = _SweepStep(c3, mode, synth.BUDGETS[pct]).run()
+    r = check_staged(st, index_ref=c3.index_ref)
+    r.update(check_endtoend(st))
+    print("c3", pct, mode, r)
+
+
+@pytest.mark.parametrize("mode", [api.MODE_VOTE, api.MODE_PER_HEAD])
+def test_c4_end_to_end(mode):
+    x = synth.config4()
+    st = FusedStep(x, mode=mode).run()
+    r = check_staged(st)
+    r.update(check_endtoend(st))
+    print("c4", mode, r)

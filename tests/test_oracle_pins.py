@@ -455,3 +455,25 @@ def test_snapkv_single_row_is_one_softmax_and_gather_bits():
     idx = O.topc(O.avg_pool1d(imp, 3), 5)
     Ko, Vo = O.gather_rows(K, V, idx)
     assert np.array_equal(Ko[:, 0], K[idx[0], 0]) and np.array_equal(Vo[:, 0], V[idx[0], 0])
+
+
+@pytest.mark.parametrize("n,w,Hq,Hkv,groups", [(300, 4, 8, 2, None), (513, 3, 12, 4, [3, 1]), (700, 8, 64, 8, [0, 5]),
+                                               (97, 1, 1, 1, None)])
+def test_snapkv_importance_matmul_matches_loop_oracle_and_torch(n, w, Hq, Hkv, groups):
+    """The matmul form of the SnapKV importance (used as the reference at full size) equals the
+    pinned loop oracle and an independent torch-CPU fp64 softmax mean, on contiguous and
+    non-contiguous KV-group lists and on the single-row reduction (G = 1, w = 1)."""
+    x = synth.make_snap(13, n, w, Hq, Hkv, max(1, n // 50))
+    loop = O.snapkv_importance(x.q_obs, x.K, Hq, Hkv)
+    mm = O.snapkv_importance_matmul(x.q_obs, x.K, Hq, Hkv, groups=groups)
+    want = list(range(Hkv)) if groups is None else list(groups)
+    assert sorted(mm) == sorted(want)
+    G = Hq // Hkv
+    q = torch.tensor(unbf(x.q_obs), dtype=torch.float64)        # [w][Hq][D]
+    k = torch.tensor(unbf(x.K), dtype=torch.float64)            # [n][Hkv][D]
+    for g in want:
+        rows = q[:, g * G:(g + 1) * G, :].permute(1, 0, 2).reshape(-1, D)
+        ref = torch.softmax(rows @ k[:, g, :].T / np.sqrt(D), dim=-1).mean(dim=0).numpy()
+        assert np.allclose(mm[g], loop[g], rtol=1e-12, atol=1e-16), g
+        assert np.allclose(mm[g], ref, rtol=1e-12, atol=1e-16), g
+        assert abs(mm[g].sum() - 1.0) < 1e-12
