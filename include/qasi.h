@@ -189,6 +189,19 @@ int ts_sparse_decode(const uint16_t* q, const uint16_t* K, const uint16_t* V,
                      int32_t B, int32_t Hq, int32_t Hkv, float* out, void* ws, size_t ws_bytes,
                      hipStream_t stream);
 
+/* For callers that cannot allocate (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid device allocation): ts_sparse_decode without a workspace.  The split-K
+ * partials live in a static device array of the library (64 MiB on each device it runs on,
+ * held until the process ends); arguments, layouts and results are those of ts_sparse_decode.
+ * Calls whose ts_decode_workspace_bytes(offsets_host, counts_host, B, Hq, Hkv, mode) exceeds
+ * 64 MiB return QASI_ERR_WORKSPACE before anything is enqueued.  Every call on one device shares
+ * that array: calls that overlap on one device (other streams or host threads) race, so the
+ * caller must order them.  Nothing is allocated or freed by this call.                   */
+int ts_sparse_decode_noalloc(const uint16_t* q, const uint16_t* K, const uint16_t* V,
+                             const int64_t* offsets_dev, const int64_t* offsets_host, const int32_t* idx,
+                             const int64_t* counts_dev, const int64_t* counts_host, int32_t mode, int32_t B,
+                             int32_t Hq, int32_t Hkv, float* out, hipStream_t stream);
+
 /* Dense decode attention over all n_b tokens of each sequence (the comparison baseline,
  * [TS] eq. S_i = q . k_i / sqrt(d) for every cached token).  Same layouts as above.   */
 int ts_dense_decode(const uint16_t* q, const uint16_t* K, const uint16_t* V,

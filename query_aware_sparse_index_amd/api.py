@@ -184,6 +184,20 @@ def sparse_decode(q, K, V, offs: Offsets, idx, counts_dev, counts_host, mode: in
     return out
 
 
+def sparse_decode_noalloc(q, K, V, offs: Offsets, idx, counts_dev, counts_host, mode: int, out=None):
+    """ts_sparse_decode_noalloc: sparse_decode with the partials in the library's static device
+    scratch (no workspace argument).  Calls on one device must not overlap."""
+    _bf16_check(q, K, V)
+    B, Hq, _ = q.shape
+    Hkv = K.shape[1]
+    if out is None:
+        out = torch.empty((B, Hq, 128), dtype=torch.float32, device=q.device)
+    _check(_lib.load().ts_sparse_decode_noalloc(_p(q), _p(K), _p(V), _p(offs.dev), offs.host, _p(idx),
+                                                _p(counts_dev), _host_i64(counts_host), int(mode), B, Hq, Hkv,
+                                                _p(out), _stream()))
+    return out
+
+
 def dense_decode(q, K, V, offs: Offsets, ws=None, out=None):
     _bf16_check(q, K, V)
     B, Hq, _ = q.shape

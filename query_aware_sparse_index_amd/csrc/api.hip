@@ -243,6 +243,33 @@ int ts_sparse_decode(const uint16_t* q, const uint16_t* K, const uint16_t* V, co
                       "ts_sparse_decode launch");
 }
 
+int ts_sparse_decode_noalloc(const uint16_t* q, const uint16_t* K, const uint16_t* V, const int64_t* offsets_dev,
+                             const int64_t* offsets_host, const int32_t* idx, const int64_t* counts_dev,
+                             const int64_t* counts_host, int32_t mode, int32_t B, int32_t Hq, int32_t Hkv, float* out,
+                             hipStream_t stream) {
+    if (!aligned16(q) || !aligned16(K) || !aligned16(V) || !aligned16(out))
+        return fail(QASI_ERR_INVALID, "q, K, V and out must be non-null and 16-byte aligned");
+    if (!idx || (reinterpret_cast<uintptr_t>(idx) & 3u)) return fail(QASI_ERR_INVALID, "idx must be non-null and aligned");
+    if (!counts_dev || !counts_host || (reinterpret_cast<uintptr_t>(counts_dev) & 7u))
+        return fail(QASI_ERR_INVALID, "counts_dev / counts_host must be non-null (counts_dev 8-byte aligned)");
+    if (mode != QASI_MODE_VOTE && mode != QASI_MODE_PER_HEAD) return fail(QASI_ERR_INVALID, "mode=%d", mode);
+    if (int r = check_heads(Hq, Hkv)) return r;
+    if (int r = check_offsets(offsets_dev, offsets_host, B, true)) return r;
+    for (int b = 0; b < B; ++b) {
+        int64_t n = offsets_host[b + 1] - offsets_host[b];
+        if (counts_host[b] < 1 || counts_host[b] > n)
+            return fail(QASI_ERR_INVALID, "counts[%d]=%lld outside [1, n_b=%lld]", b, (long long)counts_host[b], (long long)n);
+    }
+    size_t need = qasi::decode_workspace(offsets_host, counts_host, B, Hq, Hkv, mode);
+    if (need > qasi::kNoAllocScratchBytes)
+        return fail(QASI_ERR_WORKSPACE, "ts_sparse_decode_noalloc needs %zu scratch bytes; the static scratch holds %zu",
+                    need, qasi::kNoAllocScratchBytes);
+    if (int r = init_once()) return r;
+    return hip_status(qasi::launch_sparse_decode_noalloc(q, K, V, offsets_dev, offsets_host, idx, counts_dev,
+                                                         counts_host, mode, B, Hq, Hkv, out, stream),
+                      "ts_sparse_decode_noalloc launch");
+}
+
 int ts_dense_decode(const uint16_t* q, const uint16_t* K, const uint16_t* V, const int64_t* offsets_dev,
                     const int64_t* offsets_host, int32_t B, int32_t Hq, int32_t Hkv, float* out, void* ws,
                     size_t ws_bytes, hipStream_t stream) {

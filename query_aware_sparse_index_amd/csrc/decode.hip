@@ -23,6 +23,8 @@
 //   the 4 waves' (m, l, acc) merge in LDS into the block's partial (M, L, A[128]) per head.
 // The merge kernel combines the ranges of a sequence: out = sum_c A_c 2^(M_c - M) /
 // sum_c L_c 2^(M_c - M).
+#include <mutex>
+
 #include "qasi_device.h"
 #include "qasi_internal.h"
 
@@ -549,6 +551,48 @@ hipError_t launch_sparse_decode(const uint16_t* q, const uint16_t* K, const uint
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(decode_merge_kernel, dim3(B * Hq), dim3(kMergeThreads), 0, stream, part, ml, cnts, B, Hq, EB, out);
     return hipGetLastError();
+}
+
+// ------------------------------------------------------------- no-allocation variant
+// The partials of ts_sparse_decode_noalloc live in this file-scope device array instead of a
+// caller workspace.  Each device the library runs on holds its own copy (allocated with the code
+// object, kept until the process ends).  On the host the array's name is only a stand-in for the
+// device symbol, so its device address is looked up once per device with hipGetSymbolAddress and
+// only that address is used.  Every call on one device shares the array: calls that overlap on
+// one device (different streams, or host threads) race.  Nothing in it needs to start at zero:
+// every partial slot a merge reads is written by its block in the same call.
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+static hipError_t scratch_on_current_device(void** out) {
+    static std::mutex mu;
+    static void* ptr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        ptr[dev] = p;
+    }
+    *out = ptr[dev];
+    return hipSuccess;
+}
+
+hipError_t launch_sparse_decode_noalloc(const uint16_t* q, const uint16_t* K, const uint16_t* V,
+                                        const int64_t* offsets_dev, const int64_t* offsets_host, const int32_t* idx,
+                                        const int64_t* counts_dev, const int64_t* counts_host, int mode, int B, int Hq,
+                                        int Hkv, float* out, hipStream_t stream) {
+    if (decode_workspace(offsets_host, counts_host, B, Hq, Hkv, mode) > kNoAllocScratchBytes)
+        return hipErrorInvalidValue;
+    void* ws = nullptr;
+    hipError_t e = scratch_on_current_device(&ws);
+    if (e != hipSuccess) return e;
+    return launch_sparse_decode(q, K, V, offsets_dev, offsets_host, idx, counts_dev, counts_host, mode, B, Hq, Hkv,
+                                out, ws, kNoAllocScratchBytes, stream);
 }
 
 hipError_t launch_dense_decode(const uint16_t* q, const uint16_t* K, const uint16_t* V, const int64_t* offsets_dev,

@@ -78,6 +78,14 @@ hipError_t launch_sparse_decode(const uint16_t* q, const uint16_t* K, const uint
                                 const int64_t* offsets_host, const int32_t* idx, const int64_t* counts_dev,
                                 const int64_t* counts_host, int mode,
                                 int B, int Hq, int Hkv, float* out, void* ws, size_t ws_bytes, hipStream_t stream);
+// ts_sparse_decode with its partials in the library's static device scratch (no workspace);
+// hipErrorInvalidValue when the call needs more than kNoAllocScratchBytes.
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+constexpr int kMaxDevices = 64;
+hipError_t launch_sparse_decode_noalloc(const uint16_t* q, const uint16_t* K, const uint16_t* V,
+                                        const int64_t* offsets_dev, const int64_t* offsets_host, const int32_t* idx,
+                                        const int64_t* counts_dev, const int64_t* counts_host, int mode, int B, int Hq,
+                                        int Hkv, float* out, hipStream_t stream);
 hipError_t launch_dense_decode(const uint16_t* q, const uint16_t* K, const uint16_t* V, const int64_t* offsets_dev,
                                const int64_t* offsets_host, int B, int Hq, int Hkv, float* out, void* ws,
                                size_t ws_bytes, hipStream_t stream);

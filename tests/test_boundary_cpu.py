@@ -22,7 +22,7 @@ def header_functions():
 def test_exports_match_header():
     lib = _lib.load()
     names = header_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.SIGNATURES)
@@ -143,6 +143,23 @@ def test_decode_validation():
     assert L.ts_dense_decode(FAKE, MIS, FAKE, FAKE, o, 1, 32, 8, FAKE, FAKE, ws, None) == -1
     need = L.ts_decode_workspace_bytes(o, None, 1, 32, 8, 0)
     assert L.ts_dense_decode(FAKE, FAKE, FAKE, FAKE, o, 1, 32, 8, FAKE, FAKE, need - 1, None) == -3
+
+
+def test_decode_noalloc_validation():
+    """The no-workspace decode validates like ts_sparse_decode and rejects calls whose workspace
+    need exceeds its 64 MiB static scratch, all before any HIP call."""
+    L = _lib.load()
+    o = _offs([0, 1000])
+    c_ok, c_bad0 = _offs([100]), _offs([0])
+    assert L.ts_sparse_decode_noalloc(FAKE, FAKE, FAKE, FAKE, o, FAKE, FAKE, c_bad0, 0, 1, 32, 8, FAKE, None) == -1
+    assert L.ts_sparse_decode_noalloc(FAKE, FAKE, FAKE, FAKE, o, FAKE, FAKE, c_ok, 7, 1, 32, 8, FAKE, None) == -1
+    assert L.ts_sparse_decode_noalloc(MIS, FAKE, FAKE, FAKE, o, FAKE, FAKE, c_ok, 0, 1, 32, 8, FAKE, None) == -1
+    assert L.ts_sparse_decode_noalloc(FAKE, FAKE, FAKE, FAKE, o, FAKE, FAKE, c_ok, 0, 1, 24, 8, FAKE, None) == -2
+    # 2^20 list entries at 64 query heads: the partials' bound is far above 64 MiB
+    big_o, big_c = _offs([0, 1 << 20]), _offs([1 << 20])
+    assert L.ts_decode_workspace_bytes(big_o, big_c, 1, 64, 8, 0) > (64 << 20)
+    assert L.ts_sparse_decode_noalloc(FAKE, FAKE, FAKE, FAKE, big_o, FAKE, FAKE, big_c, 0, 1, 64, 8, FAKE, None) == -3
+    assert "static scratch" in err()
 
 
 def test_snapkv_validation():
