@@ -166,17 +166,19 @@ __device__ __forceinline__ void quad_transpose_sum(float (&v)[G], int part) {
 }
 
 // Tile classification against a key bracket (CLS): for every query head h of the tile's
-// sequence b whose instance (b, h) is active, over the tile's positions in [beg, end):
-//   tcnt[tile * Hq + h] = below | inside << 8 | offset << 16 (#keys below lo, #keys in [lo, hi],
-//                         offset of the head's keys in the tile's key area), one 128-byte line
-//                         per tile for Hq = 32;
-//   tcand[tile * kClsTile + offset + j], j < inside: the head's in-bracket keys, the heads' runs
-//                         packed one after the other (in the order they reserve them), so a tile
-//                         writes a few contiguous lines.
-// The bracket comes from ClsArgs::state[(b * Hq + h) * 8 + ...].
+// sequence b whose instance (b, h) is active, over the tile's positions in [beg, end), with
+// records laid out head-major, [h][tile] (tiles numbered sequence by sequence):
+//   tinfo[h][tile] = below | inside << 8 | offset << 16 (#keys below lo, #keys in [lo, hi], offset
+//                    of the head's keys in the tile's key area);
+//   cand[h][tile][j], j < min(inside, kClsSlots): the head's first in-bracket keys (in position
+//                    order), so that one head's keys of consecutive tiles are contiguous;
+//   tcand[tile * kClsTile + offset + j - kClsSlots], kClsSlots <= j < inside: the rest (rare), the
+//                    heads' runs packed one after the other in the order they reserve them.
+// Inactive instances write zero records.  The bracket comes from state[(b * Hq + h) * 8 + ...].
 struct ClsArgs {
     const int64_t* state;
-    uint32_t* tcnt;
+    uint32_t* tinfo;
+    uint32_t* cand;
     uint32_t* tcand;
     int64_t ntiles;
 };
@@ -301,11 +303,11 @@ __global__ __launch_bounds__(score_threads<HKV>()) void score_kernel(const float
             }
             cnt[i] = (uint32_t)__popcll(mm[i]);
         }
-        // one reservation in the tile's key area for the wave's heads, whose runs follow each
-        // other (the heads of the tile in any order)
+        // one reservation in the tile's overflow area for the keys past the first kClsSlots of
+        // the wave's heads, whose runs follow each other (the heads of the tile in any order)
         uint32_t tot = 0;
 #pragma unroll
-        for (int i = 0; i < HPW; ++i) tot += cnt[i];
+        for (int i = 0; i < HPW; ++i) tot += cnt[i] > kClsSlots ? cnt[i] - kClsSlots : 0u;
         uint32_t off = 0;
         if (lane == 0 && tot) off = atomicAdd(&s_run, tot);
         off = __builtin_amdgcn_readfirstlane(off);
@@ -313,10 +315,14 @@ __global__ __launch_bounds__(score_threads<HKV>()) void score_kernel(const float
         for (int i = 0; i < HPW; ++i) {
             const int h = wu + i * NW;
             if (h >= Hq) continue;
-            if (lane == 0) cls.tcnt[(size_t)blockIdx.x * Hq + h] = below[i] | (cnt[i] << 8) | (off << 16);
-            if ((mm[i] >> lane) & 1ull)
-                cls.tcand[(size_t)blockIdx.x * kClsTile + off + __popcll(mm[i] & lt)] = key[i];
-            off += cnt[i];
+            const size_t r = (size_t)h * cls.ntiles + blockIdx.x;
+            if (lane == 0) cls.tinfo[r] = below[i] | (cnt[i] << 8) | (off << 16);
+            if ((mm[i] >> lane) & 1ull) {
+                const uint32_t j = (uint32_t)__popcll(mm[i] & lt);
+                if (j < (uint32_t)kClsSlots) cls.cand[r * kClsSlots + j] = key[i];
+                else cls.tcand[(size_t)blockIdx.x * kClsTile + off + j - kClsSlots] = key[i];
+            }
+            off += cnt[i] > kClsSlots ? cnt[i] - kClsSlots : 0u;
         }
     }
 }
@@ -376,12 +382,13 @@ hipError_t launch_score(const uint16_t* q, const float* P, const uint16_t* k_ind
 // Scores plus the tile classification against the brackets in `state` (q' already in qp).
 hipError_t launch_score_classify(const float* qp, const uint16_t* k_index, const int64_t* offsets_dev,
                                  const int64_t* offsets_host, int B, int Hq, int Hkv, float* scores,
-                                 const int64_t* state, uint32_t* tcnt, uint32_t* tcand, hipStream_t stream) {
+                                 const int64_t* state, uint32_t* tinfo, uint32_t* cand, uint32_t* tcand,
+                                 hipStream_t stream) {
     const int64_t items = score_items(offsets_host, B);
     if (items == 0) return hipSuccess;
     const I64Arg offs = i64_arg(offsets_dev, offsets_host, (int64_t)B + 1);
-    return launch_score_tiles<true>(qp, k_index, offs, items, B, Hq, Hkv, scores, ClsArgs{state, tcnt, tcand, items},
-                                    stream);
+    return launch_score_tiles<true>(qp, k_index, offs, items, B, Hq, Hkv, scores,
+                                    ClsArgs{state, tinfo, cand, tcand, items}, stream);
 }
 
 }  // namespace qasi

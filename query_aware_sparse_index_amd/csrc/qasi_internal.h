@@ -37,10 +37,11 @@ hipError_t launch_score(const uint16_t* q, const float* P, const uint16_t* k_ind
                         size_t ws_bytes, hipStream_t stream);
 
 // Scores plus the classification of every tile against per-instance key brackets (the fused
-// score-and-select path): q' is read from qp; see score_kernel.
+// score-and-select path): q' is read from qp; per (head, tile) records, see score_kernel.
 hipError_t launch_score_classify(const float* qp, const uint16_t* k_index, const int64_t* offsets_dev,
                                  const int64_t* offsets_host, int B, int Hq, int Hkv, float* scores,
-                                 const int64_t* state, uint32_t* tcnt, uint32_t* tcand, hipStream_t stream);
+                                 const int64_t* state, uint32_t* tinfo, uint32_t* cand, uint32_t* tcand,
+                                 hipStream_t stream);
 int64_t score_items(const int64_t* offsets_host, int B);
 
 // ---- selection
@@ -49,6 +50,9 @@ enum : int { kStFlag = 0, kStKey = 1, kStGt = 2, kStNeed = 3, kStLo = 4, kStHi =
 // Key run of a 64-token tile in the fused path's tile classification: at most 64 in-bracket
 // keys for each of at most 64 query heads.
 constexpr int kClsTile = 64 * 64;
+// In-bracket keys of one (head, tile) kept in the head-major slots of the tile classification;
+// the rest go to the tile's key area.
+constexpr int kClsSlots = 16;
 
 struct SelectConfig {
     int mode;

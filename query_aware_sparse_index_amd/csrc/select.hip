@@ -38,9 +38,7 @@ constexpr int kDelta = 96;         // bracket half-width in sample ranks
 constexpr int kDigit = 11;         // radix digit width of the final select
 constexpr int kDigitBins = 1 << kDigit;
 constexpr int kCap = 16384;        // keys of the answer's top digit resolved in LDS
-constexpr int kCapT = 24576;       // bracket keys ranked in LDS by the fused path's final kernel
 constexpr int kSlice = 8192;       // keys per collect block
-constexpr int kTilesPerSlice = kSlice / 64;   // 64-token tiles per slice of the fused path
 constexpr int kColThreads = 512;
 constexpr int kMaxSL = 2048;       // slices per instance (n up to 2^24 tokens)
 constexpr int kChunk = 1024;       // tokens per vote / compaction block
@@ -333,10 +331,10 @@ __global__ __launch_bounds__(kColThreads) void th_collect_kernel(const float* __
 // Radix selection over the keys that visit(f) hands to f (f(x) once per key): returns the
 // rank-th smallest x (1-based) and adds the number of keys above it to *gt.  Digits of
 // kDigit bits from bit nbits - 1 down; every thread of the block calls it.
-template <class Visit>
+template <int NT = kThThreads, class Visit>
 __device__ uint32_t radix_rank(Visit visit, int nbits, int64_t rank, uint32_t* hist, int* tmp, int64_t* sh,
                                int64_t* gt) {
-    constexpr int NB = 1 << kDigit, BPT = NB / kThThreads;
+    constexpr int NB = 1 << kDigit, BPT = NB / NT;
     uint64_t prefix = 0;
     int shift = nbits;
     while (shift > 0) {
@@ -344,7 +342,7 @@ __device__ uint32_t radix_rank(Visit visit, int nbits, int64_t rank, uint32_t* h
         shift -= d;
         const int top = shift + d;
         const uint32_t dmask = (1u << d) - 1u;
-        for (int i = threadIdx.x; i < NB; i += kThThreads) hist[i] = 0;
+        for (int i = threadIdx.x; i < NB; i += NT) hist[i] = 0;
         __syncthreads();
         visit([&](uint32_t x) {
             const uint64_t xx = x;
@@ -355,7 +353,7 @@ __device__ uint32_t radix_rank(Visit visit, int nbits, int64_t rank, uint32_t* h
 #pragma unroll
         for (int u = 0; u < BPT; ++u) c += (int)hist[threadIdx.x * BPT + u];
         int total;
-        const int inc = block_inclusive_scan<kThThreads>(c, tmp, &total);
+        const int inc = block_inclusive_scan<NT>(c, tmp, &total);
         if (inc - c < rank && rank <= inc) {
             int acc = inc - c;
             for (int u = 0; u < BPT; ++u) {
@@ -385,8 +383,7 @@ __global__ __launch_bounds__(kThThreads) void th_final_kernel(const float* __res
                                                              const uint32_t* __restrict__ cand,
                                                              const uint32_t* __restrict__ cnt,
                                                              const uint32_t* __restrict__ dpre,
-                                                             int64_t* __restrict__ state, float* __restrict__ theta_out,
-                                                             int tiles) {
+                                                             int64_t* __restrict__ state, float* __restrict__ theta_out) {
     static_assert(kDigitBins / 2 == kThThreads, "one pair of digit bins per thread");
     __shared__ uint32_t xs[kCap];
     __shared__ int segpre[kMaxSL + 1], sega[kMaxSL];
@@ -445,9 +442,7 @@ __global__ __launch_bounds__(kThThreads) void th_final_kernel(const float* __res
         return;
     }
     const int64_t m = oi.end - oi.beg;
-    // slices: of the key range [beg, end), or of the sequence's tiles (tile classification)
-    const int nsl = tiles ? (int)(((nrow + 63) / 64 + kTilesPerSlice - 1) / kTilesPerSlice)
-                          : (int)((m + kSlice - 1) / kSlice);
+    const int nsl = (int)((m + kSlice - 1) / kSlice);   // slices of the key range [beg, end)
     int lsum = (int)more_lo, csum = (int)more_mid;
 #pragma unroll
     for (int u = 0; u < 2; ++u)
@@ -738,112 +733,6 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const uint16_t* __re
         st[kStHi] = khi;
         st[kStBeg] = oi.beg;
         st[kStEnd] = oi.end;
-    }
-}
-
-// Block (slice s, instance): the collect step of the order statistic from the tile
-// classification of the score kernel.  Slice s of an instance is the tiles
-// [s kTilesPerSlice, (s+1) kTilesPerSlice) of its sequence (the key range of th_collect_kernel's
-// slices, cut at tile boundaries).  The block sums the tiles' counts below the bracket, loads
-// their in-bracket keys (slots < kCtS of four tiles per wave load instruction; a tile with more
-// keys has its owning thread copy the rest) and writes the same outputs as th_collect_kernel:
-// the keys grouped by their top digit, the 16-bit digit prefixes and counts, and the slice's
-// (below, inside) counts.  The bracket and the instance state come from prep_kernel.
-constexpr int kCtS = 16;
-__global__ __launch_bounds__(kColThreads) void th_collect_tiles_kernel(I64Arg offsets, int Hq, DevCfg cfg, int SL,
-                                                                      const int64_t* __restrict__ state,
-                                                                      const uint32_t* __restrict__ tcnt,
-                                                                      const uint32_t* __restrict__ tcand,
-                                                                      uint32_t* __restrict__ cand,
-                                                                      uint32_t* __restrict__ cnt,
-                                                                      uint32_t* __restrict__ dpre) {
-    constexpr int NW = kColThreads / 64;
-    constexpr int BPT = kDigitBins / kColThreads;              // digit bins per thread in the scan
-    constexpr int TPP = kColThreads / kCtS;                    // tiles per load pass
-    constexpr int PASSES = kTilesPerSlice / TPP;
-    static_assert(kTilesPerSlice <= kColThreads && kTilesPerSlice % TPP == 0, "slice tiles per block");
-    __shared__ int wsum[NW];
-    __shared__ int tmp[NW];
-    __shared__ uint32_t hist[kDigitBins];                      // digit counts, then cursors
-    __shared__ int scn[kTilesPerSlice], sof[kTilesPerSlice];
-    const int inst = blockIdx.y, s = blockIdx.x, t = threadIdx.x;
-    const int b = inst / Hq, h = inst % Hq;
-    const int64_t n = offsets[b + 1] - offsets[b];
-    const OsInst oi = os_instance(n, cfg);
-    if (oi.flag != kFlagActive) return;
-    const int64_t tf = wave_prefix_seq(b, [od = offsets.dev](int i) { return (od[i + 1] - od[i] + 63) / 64; });
-    const int64_t nt = (n + 63) / 64;
-    const int64_t* st = state + (int64_t)inst * 8;
-    const uint32_t klo = (uint32_t)st[kStLo], khi = (uint32_t)st[kStHi];
-    const int64_t a0 = (int64_t)s * kTilesPerSlice;            // first tile of the slice
-    uint32_t cw = 0;
-    if (t < kTilesPerSlice && a0 + t < nt) cw = tcnt[(size_t)(tf + a0 + t) * Hq + h];
-    const int cy = (int)((cw >> 8) & 0xffu), cof = (int)(cw >> 16);
-    for (int i = t; i < kDigitBins; i += kColThreads) hist[i] = 0;
-    if (t < kTilesPerSlice) {
-        scn[t] = cy;
-        sof[t] = cof;
-    }
-    __syncthreads();
-    const uint32_t* tk = tcand + (size_t)(tf + a0) * kClsTile;
-    // the slice's in-bracket keys: pass p, lane -> (tile p TPP + t / kCtS, slot t % kCtS)
-    const int dsh = top_shift(khi - klo);
-    uint32_t kv[PASSES];
-#pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-        const int tl = p * TPP + t / kCtS, sl = t % kCtS;
-        kv[p] = sl < scn[tl] ? tk[(size_t)tl * kClsTile + sof[tl] + sl] : 0u;
-    }
-#pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-        const int tl = p * TPP + t / kCtS, sl = t % kCtS;
-        if (sl < scn[tl]) atomicAdd(&hist[(kv[p] - klo) >> dsh], 1u);
-    }
-    // rare: keys past the first kCtS of a tile
-    if (t < kTilesPerSlice)
-        for (int i = kCtS; i < cy; ++i) atomicAdd(&hist[(tk[(size_t)t * kClsTile + cof + i] - klo) >> dsh], 1u);
-    const int below = wave_sum_i((int)(cw & 0xffu));
-    if ((t & 63) == 0) wsum[t >> 6] = below;
-    __syncthreads();
-    // exclusive prefix over the digits (BPT consecutive bins per thread)
-    uint32_t cc[BPT];
-    int csum = 0;
-#pragma unroll
-    for (int u = 0; u < BPT; ++u) { cc[u] = hist[t * BPT + u]; csum += (int)cc[u]; }
-    int total;
-    const int incl = block_inclusive_scan<kColThreads>(csum, tmp, &total);
-    uint32_t* dp = dpre + ((size_t)inst * SL + s) * kDpWords;
-    {
-#pragma unroll
-        for (int u = 0; u < BPT; u += 2) dp[kPreWords + (t * BPT + u) / 2] = cc[u] | (cc[u + 1] << 16);
-        uint32_t acc = (uint32_t)(incl - csum);
-        uint32_t pre[BPT];
-#pragma unroll
-        for (int u = 0; u < BPT; ++u) { pre[u] = acc; acc += cc[u]; }
-#pragma unroll
-        for (int u = 0; u < BPT; u += 2) dp[(t * BPT + u) / 2] = pre[u] | (pre[u + 1] << 16);
-#pragma unroll
-        for (int u = 0; u < BPT; ++u) hist[t * BPT + u] = pre[u];   // cursor
-        if (t == 0) dp[kDigitBins / 2] = (uint32_t)total;
-    }
-    __syncthreads();
-    // scatter the keys to their digit's range
-    uint32_t* dst = cand + ((size_t)inst * SL + s) * kSlice;
-#pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-        const int tl = p * TPP + t / kCtS, sl = t % kCtS;
-        if (sl < scn[tl]) dst[atomicAdd(&hist[(kv[p] - klo) >> dsh], 1u)] = kv[p];
-    }
-    if (t < kTilesPerSlice)
-        for (int i = kCtS; i < cy; ++i) {
-            const uint32_t k = tk[(size_t)t * kClsTile + cof + i];
-            dst[atomicAdd(&hist[(k - klo) >> dsh], 1u)] = k;
-        }
-    if (t == 0) {
-        int tb = 0;
-        for (int w = 0; w < NW; ++w) tb += wsum[w];
-        cnt[((size_t)inst * SL + s) * 2 + 0] = (uint32_t)tb;
-        cnt[((size_t)inst * SL + s) * 2 + 1] = (uint32_t)total;
     }
 }
 
@@ -1197,6 +1086,312 @@ __global__ __launch_bounds__(kPhWaves * 64) void ph_compact_kernel(const float* 
     }
 }
 
+// ------------------------------------------------------- fused path: order statistic
+// th_final2_kernel, one block per instance (sequence b, head h), after prep_kernel and the score
+// kernel's tile classification (records [h][tile] of the sequence's tiles):
+//   1. loads the records of its tiles (thread t: kF2Per consecutive tiles) with the tiles' first
+//      in-bracket keys (head-major slots, when the sequence fits one round) and sums the counts
+//      below and inside the bracket; the target rank r lies inside when
+//      #below < r <= #below + #inside;
+//   2. stages the in-bracket keys in LDS while counting them per top digit (kDigit bits of
+//      key - lo), finds the answer's digit and ranks that digit's keys (one wave when there are
+//      at most 64, else a radix select);
+// a rank outside the bracket, keys that do not fit in LDS or a sequence of more than one round
+// take the out-of-line paths: an LDS histogram of the digits over the keys in memory, or a radix
+// select over the instance's whole score row (same result).  The state gets the answer's key and
+// the number of keys above it, as th_final_kernel leaves them.
+constexpr int kF2Threads = 512;
+constexpr int kF2Per = 5;                                  // consecutive tiles per thread per round
+constexpr int kF2Round = kF2Threads * kF2Per;              // tiles per round (163840 tokens)
+constexpr int kF2Cap = 24576;                              // keys ranked in LDS
+
+struct F2Args {
+    const uint32_t* tinfo;   // [Hq][ntiles] below | inside << 8 | offset << 16
+    const uint32_t* cand;    // [Hq][ntiles][kClsSlots] first in-bracket keys
+    const uint32_t* tcand;   // [ntiles][kClsTile] the other in-bracket keys
+    int64_t ntiles;
+};
+
+// The rank-r key (1-based) of a score row over [beg, end) by a whole-row radix select; *gt gets
+// the number of keys above it.  (Out of line: the common path is register-allocated alone.)
+__device__ __noinline__ uint32_t f2_rank_row(const float* row, int64_t beg, int64_t end, int64_t r, uint32_t* hist,
+                                             int* tmp, int64_t* sh, int64_t* gt) {
+    *gt = 0;
+    return radix_rank<kF2Threads>(
+        [&](auto f) {
+            for_each_f32<kF2Threads, 4>(row, beg, end, [&](int64_t, float v, bool ok) {
+                if (ok) f(order_key(v));
+            });
+        },
+        32, r, hist, tmp, sh, gt);
+}
+
+// The in-bracket keys of the instance, f(key) once each (every thread of the block calls it).
+template <class F>
+__device__ __forceinline__ void f2_each_cand(const uint32_t* inf_h, const uint32_t* cand_h, const uint32_t* over,
+                                             int64_t nt, F f) {
+    for (int64_t r0 = 0; r0 < nt; r0 += kF2Round)
+        for (int u = 0; u < kF2Per; ++u) {
+            const int64_t T = r0 + (int64_t)kF2Per * threadIdx.x + u;
+            if (T >= nt) continue;
+            const uint32_t w = inf_h[T];
+            const int cnt = (int)((w >> 8) & 0xffu);
+            for (int j = 0; j < cnt; ++j)
+                f(j < kClsSlots ? cand_h[T * kClsSlots + j] : over[(size_t)T * kClsTile + (w >> 16) + (j - kClsSlots)]);
+        }
+}
+
+// The answer's digit D among kDigitBins digit counts in `hist` (every thread calls it): sh[0] = D,
+// sh[1] = keys below D, sh[2] = keys above D, sh[3] = keys in D.
+__device__ __forceinline__ void f2_find_digit(const uint32_t* hist, int64_t rr, int* tmp, int64_t* sh) {
+    constexpr int BPT = kDigitBins / kF2Threads;
+    const int t = threadIdx.x;
+    int c = 0;
+#pragma unroll
+    for (int u = 0; u < BPT; ++u) c += (int)hist[t * BPT + u];
+    int tot;
+    const int inc = block_inclusive_scan<kF2Threads>(c, tmp, &tot);
+    if (inc - c < rr && rr <= inc) {
+        int acc = inc - c;
+#pragma unroll
+        for (int u = 0; u < BPT; ++u) {
+            const int bin = t * BPT + u;
+            const int nx = acc + (int)hist[bin];
+            if (acc < rr && rr <= nx) {
+                sh[0] = bin;
+                sh[1] = acc;
+                sh[2] = tot - nx;
+                sh[3] = hist[bin];
+            }
+            acc = nx;
+        }
+    }
+    __syncthreads();
+}
+
+// Rank rr (1-based) of the low dsh bits among the keys x that visit(f) hands over with
+// (x >> dsh) == D; *gt gets the keys above it.  At most 64 keys: one wave ranks them from `xd`.
+template <class Visit>
+__device__ __forceinline__ uint32_t f2_rank_in_digit(Visit visit, int nD, uint32_t D, int dsh, int64_t rr,
+                                                     uint32_t* xd, uint32_t* cursor, uint32_t* hist, int* tmp,
+                                                     int64_t* sh, int64_t* gt) {
+    const int t = threadIdx.x;
+    const uint32_t low = dsh ? ((1u << dsh) - 1u) : 0u;
+    if (nD <= 64) {
+        visit([&](uint32_t x) {
+            if ((x >> dsh) == D) xd[atomicAdd(cursor, 1u)] = x & low;
+        });
+        __syncthreads();
+        if (t < 64) {
+            const bool has = t < nD;
+            const uint32_t x = has ? xd[t] : 0xffffffffu;
+            int less = 0, leq = 0;
+            for (int j = 0; j < nD; ++j) {
+                const uint32_t y = __shfl(x, j, 64);
+                less += y < x ? 1 : 0;
+                leq += y <= x ? 1 : 0;
+            }
+            if (has && less < rr && rr <= leq) {       // the answer x: #{< x} < rr <= #{<= x}
+                sh[0] = x;
+                sh[1] = nD - leq;
+            }
+        }
+        __syncthreads();
+        *gt += sh[1];
+        return (uint32_t)sh[0];
+    }
+    int64_t gin = 0;
+    const uint32_t xl = radix_rank<kF2Threads>(
+        [&](auto f) {
+            visit([&](uint32_t x) {
+                if ((x >> dsh) == D) f(x & low);
+            });
+        },
+        dsh, rr, hist, tmp, sh, &gin);
+    *gt += gin;
+    return xl;
+}
+
+// Rank rr0 among the in-bracket keys [klo, khi] read from memory (keys that do not fit in LDS,
+// sequences of more than one round): an LDS histogram of their top digit, then the digit's keys.
+// Returns false when that digit holds more than kF2Cap keys.  *gt gets the in-bracket keys above.
+__device__ __noinline__ bool f2_rank_digit(const uint32_t* inf_h, const uint32_t* cand_h, const uint32_t* over,
+                                           int64_t nt, uint32_t klo, uint32_t khi, int64_t rr0, uint32_t* xs,
+                                           uint32_t* xd, uint32_t* hist, int* tmp, int64_t* sh, uint32_t* cursor,
+                                           uint32_t* key, int64_t* gt) {
+    const int t = threadIdx.x;
+    const int dsh = top_shift(khi - klo);
+    for (int i = t; i < kDigitBins; i += kF2Threads) hist[i] = 0;
+    if (t == 0) *cursor = 0;
+    __syncthreads();
+    f2_each_cand(inf_h, cand_h, over, nt, [&](uint32_t k) { atomicAdd(&hist[(k - klo) >> dsh], 1u); });
+    __syncthreads();
+    f2_find_digit(hist, rr0, tmp, sh);
+    const uint32_t D = (uint32_t)sh[0];
+    const int64_t rr = rr0 - sh[1];
+    const int64_t gt_d = sh[2];
+    const int64_t nD = sh[3];
+    __syncthreads();
+    if (nD > kF2Cap) return false;
+    // the digit's keys (their low dsh bits) into LDS, then ranked there
+    const uint32_t low = dsh ? ((1u << dsh) - 1u) : 0u;
+    f2_each_cand(inf_h, cand_h, over, nt, [&](uint32_t k) {
+        if (((k - klo) >> dsh) == D) xs[atomicAdd(cursor, 1u)] = (k - klo) & low;
+    });
+    __syncthreads();
+    if (t == 0) *cursor = 0;
+    __syncthreads();
+    int64_t g = gt_d;
+    const uint32_t xl = f2_rank_in_digit(
+        [&](auto f) {
+            for (int i = t; i < nD; i += kF2Threads) f(xs[i]);
+        },
+        (int)nD, 0u, dsh, rr, xd, cursor, hist, tmp, sh, &g);
+    *key = klo + ((D << dsh) | xl);
+    *gt = g;
+    return true;
+}
+
+__global__ __launch_bounds__(kF2Threads) void th_final2_kernel(const float* __restrict__ scores, I64Arg offsets,
+                                                              int Hq, DevCfg cfg, int64_t S, F2Args a,
+                                                              int64_t* __restrict__ state,
+                                                              float* __restrict__ theta_out) {
+    __shared__ uint32_t xs[kF2Cap];
+    __shared__ uint32_t hist[kDigitBins];
+    __shared__ uint32_t xd[64];
+    __shared__ int tmp[kF2Threads / 64];
+    __shared__ int tmp3[3][kF2Threads / 64];
+    __shared__ int64_t sh[4];
+    __shared__ uint32_t cursor;
+    const int inst = blockIdx.x, b = inst / Hq, h = inst % Hq, t = threadIdx.x;
+    int64_t* st = state + (int64_t)inst * 8;
+    const int64_t off = offsets[b], n = offsets[b + 1] - off;
+    const OsInst oi = os_instance(n, cfg);
+    const uint32_t klo = (uint32_t)st[kStLo], khi = (uint32_t)st[kStHi];
+    const int64_t tf = wave_prefix_seq(b, [od = offsets.dev](int i) { return (od[i + 1] - od[i] + 63) / 64; });
+    const int64_t nt = (n + 63) / 64, m = oi.end - oi.beg;
+    const size_t hrow = (size_t)h * a.ntiles + tf;
+    const uint32_t* inf_h = a.tinfo + hrow;
+    const uint32_t* cand_h = a.cand + hrow * kClsSlots;
+    const uint32_t* over = a.tcand + (size_t)tf * kClsTile;      // overflow keys of the sequence's tiles
+    const bool active = oi.flag == kFlagActive;
+    const bool one = nt <= kF2Round;                   // one round: the keys load with the records
+    const int dsh = top_shift(khi - klo);
+    for (int i = t; i < kDigitBins; i += kF2Threads) hist[i] = 0;
+    if (t == 0) cursor = 0;
+
+    // ---- 1. records, first keys and counts: one memory round trip (tiles past nt read tile 0's
+    // records, in bounds, and count nothing)
+    uint32_t w[kF2Per];
+    uint32_t kv[kF2Per][kClsSlots];
+#pragma unroll
+    for (int u = 0; u < kF2Per; ++u) {
+        const int64_t T = (int64_t)kF2Per * t + u;
+        const int64_t Tc = T < nt ? T : 0;
+        w[u] = inf_h[Tc];
+        if (one) {
+            const uint4* src = reinterpret_cast<const uint4*>(cand_h + Tc * kClsSlots);
+#pragma unroll
+            for (int v = 0; v < kClsSlots / 4; ++v) {
+                const uint4 x = src[v];
+                kv[u][4 * v] = x.x;
+                kv[u][4 * v + 1] = x.y;
+                kv[u][4 * v + 2] = x.z;
+                kv[u][4 * v + 3] = x.w;
+            }
+        }
+    }
+    int lsum = 0, c0 = 0;
+#pragma unroll
+    for (int u = 0; u < kF2Per; ++u) {
+        if ((int64_t)kF2Per * t + u >= nt) w[u] = 0;
+        lsum += (int)(w[u] & 0xffu);
+        c0 += (int)((w[u] >> 8) & 0xffu);
+    }
+    int csum = c0;
+    for (int64_t r0 = kF2Round; r0 < nt; r0 += kF2Round)
+#pragma unroll
+        for (int u = 0; u < kF2Per; ++u) {
+            const int64_t T = r0 + (int64_t)kF2Per * t + u;
+            const uint32_t x = T < nt ? inf_h[T] : 0u;
+            lsum += (int)(x & 0xffu);
+            csum += (int)((x >> 8) & 0xffu);
+        }
+    int nlo = 0, nmid = 0, ctot0 = 0;
+    const int cinc0 = block_inclusive_scan3<kF2Threads>(lsum, csum, c0, tmp3, &nlo, &nmid, &ctot0);
+    const int64_t r = oi.rank;
+    bool whole_row = active && !(nlo < r && r <= (int64_t)nlo + nmid);
+    uint32_t key = 0;
+    int64_t gt = 0;
+    if (active && !whole_row) {
+        gt = m - nlo - nmid;                              // keys above the bracket
+        const int64_t rr0 = r - nlo;
+        if (klo == khi) {
+            key = klo;                                    // every in-bracket key is the answer
+        } else if (one && nmid <= kF2Cap) {
+            // ---- 2. every in-bracket key into LDS (as key - lo), counted per top digit
+            int base = cinc0 - c0;
+#pragma unroll
+            for (int u = 0; u < kF2Per; ++u) {
+                const int cnt = (int)((w[u] >> 8) & 0xffu);
+#pragma unroll
+                for (int j = 0; j < kClsSlots; ++j)
+                    if (j < cnt) {
+                        const uint32_t x = kv[u][j] - klo;
+                        xs[base + j] = x;
+                        atomicAdd(&hist[x >> dsh], 1u);
+                    }
+                // rare: more than kClsSlots keys, read in batches of 8 loads in flight
+                const uint32_t* ov = over + (size_t)((int64_t)kF2Per * t + u) * kClsTile + (w[u] >> 16) - kClsSlots;
+                for (int j0 = kClsSlots; j0 < cnt; j0 += 8) {
+                    uint32_t x8[8];
+#pragma unroll
+                    for (int v = 0; v < 8; ++v) x8[v] = ov[j0 + v < cnt ? j0 + v : j0];
+#pragma unroll
+                    for (int v = 0; v < 8; ++v)
+                        if (j0 + v < cnt) {
+                            const uint32_t x = x8[v] - klo;
+                            xs[base + j0 + v] = x;
+                            atomicAdd(&hist[x >> dsh], 1u);
+                        }
+                }
+                base += cnt;
+            }
+            __syncthreads();
+            f2_find_digit(hist, rr0, tmp, sh);
+            const uint32_t D = (uint32_t)sh[0];
+            const int64_t rr = rr0 - sh[1];
+            const int nD = (int)sh[3];
+            gt += sh[2];
+            __syncthreads();
+            const uint32_t xl = f2_rank_in_digit(
+                [&](auto f) {
+                    for (int i = t; i < nmid; i += kF2Threads) f(xs[i]);
+                },
+                nD, D, dsh, rr, xd, &cursor, hist, tmp, sh, &gt);
+            key = klo + ((D << dsh) | xl);
+        } else {
+            // ---- 2'. keys that do not fit in LDS, or more than one round: from memory
+            uint32_t kd = 0;
+            int64_t gd = 0;
+            __syncthreads();
+            if (f2_rank_digit(inf_h, cand_h, over, nt, klo, khi, rr0, xs, xd, hist, tmp, sh, &cursor, &kd, &gd)) {
+                key = kd;
+                gt += gd;
+            } else {
+                whole_row = true;
+            }
+        }
+    }
+    if (whole_row)   // the answer lies outside the bracket (or its digit overflows LDS): the whole row
+        key = f2_rank_row(scores + (int64_t)h * S + off, oi.beg, oi.end, r, hist, tmp, sh, &gt);
+    if (t == 0) {
+        st[kStKey] = key;
+        st[kStGt] = gt;
+        if (cfg.mode == 0 && theta_out) theta_out[inst] = active ? key_to_float(key) : 0.f;
+    }
+}
+
 // ------------------------------------------------------------------- host side
 static DevCfg dev_cfg(const SelectConfig& c) {
     DevCfg d;
@@ -1218,7 +1413,8 @@ struct SelectLayout {
     int64_t* state;
     uint8_t *votes, *keys;
     float* qp;          // fused path: q' per (sequence, head)
-    uint32_t* tcnt;     // fused path: per (tile, head) counts below / inside the bracket, key offset
+    uint32_t* tinfo;    // fused path: per (head, tile) counts below / inside the bracket, key offset
+    uint32_t* hcand;    // fused path: per (head, tile) the first in-bracket keys
     uint32_t* tcand;    // fused path: per tile the heads' keys inside the bracket
     size_t bytes;
 };
@@ -1239,38 +1435,32 @@ static SelectLayout select_layout(void* ws, const int64_t* offsets_host, int B, 
     }
     L.ph_items = ph_items;
     L.SL = (int)((maxm + kSlice - 1) / kSlice);
-    if (fused) {
-        // slices of whole tiles: the longest sequence's tile count
-        int64_t maxt = 0;
-        for (int b = 0; b < B; ++b) {
-            const int64_t nt = (offsets_host[b + 1] - offsets_host[b] + 63) / 64;
-            if (nt > maxt) maxt = nt;
-        }
-        L.SL = (int)((maxt + kTilesPerSlice - 1) / kTilesPerSlice);
-    }
     if (L.SL < 1) L.SL = 1;
     L.nitems = items;
     L.ntiles = tiles;
     L.Ntot = offsets_host[B];
     WsCarver w(ws);
     const size_t inst = (size_t)B * Hq;
-    L.cand = L.cnt = L.dhist = nullptr;
+    L.cand = L.cnt = L.dhist = L.phcnt = nullptr;
     L.qp = nullptr;
-    L.tcnt = nullptr;
+    L.tinfo = nullptr;
+    L.hcand = nullptr;
     L.tcand = nullptr;
-    L.cand = w.take<uint32_t>(inst * L.SL * kSlice);
-    L.cnt = w.take<uint32_t>(inst * L.SL * 2);
-    L.dhist = w.take<uint32_t>(inst * L.SL * kDpWords);
     if (fused) {
         L.qp = w.take<float>(inst * kDP);
-        L.tcnt = w.take<uint32_t>((size_t)Hq * tiles);
+        L.tinfo = w.take<uint32_t>((size_t)Hq * tiles);
+        L.hcand = w.take<uint32_t>((size_t)Hq * tiles * kClsSlots);
         L.tcand = w.take<uint32_t>((size_t)tiles * kClsTile);
+    } else {
+        L.cand = w.take<uint32_t>(inst * L.SL * kSlice);
+        L.cnt = w.take<uint32_t>(inst * L.SL * 2);
+        L.dhist = w.take<uint32_t>(inst * L.SL * kDpWords);
     }
+    L.phcnt = c.mode == 1 ? w.take<uint32_t>((size_t)Hq * ph_items * 2) : nullptr;
     L.state = w.take<int64_t>(inst * 8);
     L.votes = w.take<uint8_t>((size_t)L.Ntot + 16);
     L.keys = w.take<uint8_t>((size_t)L.Ntot + 16);
     L.hist = w.take<uint32_t>((size_t)items * kVoteBins);
-    L.phcnt = c.mode == 1 ? w.take<uint32_t>((size_t)Hq * ph_items * 2) : nullptr;
     L.bytes = w.size();
     return L;
 }
@@ -1319,7 +1509,7 @@ hipError_t launch_select(const float* scores, int64_t S, const int64_t* offsets_
     hipLaunchKernelGGL(th_collect_kernel, dim3(L.SL, inst), dim3(kColThreads), 0, stream, scores, offs, Hq, d,
                        L.SL, S, L.state, L.cand, L.cnt, L.dhist);
     hipLaunchKernelGGL(th_final_kernel, dim3(inst), dim3(kThThreads), 0, stream, scores, offs, Hq, d, L.SL, S,
-                       L.cand, L.cnt, L.dhist, L.state, c.mode == 0 ? theta_out : nullptr, 0);
+                       L.cand, L.cnt, L.dhist, L.state, c.mode == 0 ? theta_out : nullptr);
     return launch_select_tail(L, scores, S, offs, B, Hq, c, idx_out, count_out, votes_out, stream);
 }
 
@@ -1328,20 +1518,19 @@ hipError_t launch_score_select(const uint16_t* q, const float* P, uint16_t* k_in
                                const SelectConfig& c, float* scores, int32_t* idx_out, int64_t* count_out,
                                float* theta_out, uint8_t* votes_out, void* ws, size_t ws_bytes, hipStream_t stream) {
     SelectLayout L = select_layout(ws, offsets_host, B, Hq, c, true);
-    if (L.bytes > ws_bytes || L.SL > kMaxSL) return hipErrorInvalidValue;
+    if (L.bytes > ws_bytes) return hipErrorInvalidValue;
     DevCfg d = dev_cfg(c);
     const unsigned inst = (unsigned)(B * Hq);
     const I64Arg offs = i64_arg(offsets_dev, offsets_host, (int64_t)B + 1);
     const int64_t S = score_stride(offsets_host[B]);
     hipLaunchKernelGGL(prep_kernel, dim3(inst + (K ? B : 0)), dim3(kPrepThreads), 0, stream, q, P, k_index, K, offs,
                        B, Hq, Hkv, d, L.qp, L.state);
-    hipError_t e = launch_score_classify(L.qp, k_index, offsets_dev, offsets_host, B, Hq, Hkv, scores, L.state, L.tcnt,
-                                         L.tcand, stream);
+    hipError_t e = launch_score_classify(L.qp, k_index, offsets_dev, offsets_host, B, Hq, Hkv, scores, L.state, L.tinfo,
+                                         L.hcand, L.tcand, stream);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(th_collect_tiles_kernel, dim3(L.SL, inst), dim3(kColThreads), 0, stream, offs, Hq, d, L.SL,
-                       L.state, L.tcnt, L.tcand, L.cand, L.cnt, L.dhist);
-    hipLaunchKernelGGL(th_final_kernel, dim3(inst), dim3(kThThreads), 0, stream, scores, offs, Hq, d, L.SL, S,
-                       L.cand, L.cnt, L.dhist, L.state, c.mode == 0 ? theta_out : nullptr, 1);
+    const F2Args fa{L.tinfo, L.hcand, L.tcand, L.ntiles};
+    hipLaunchKernelGGL(th_final2_kernel, dim3(inst), dim3(kF2Threads), 0, stream, scores, offs, Hq, d, S, fa, L.state,
+                       theta_out);
     return launch_select_tail(L, scores, S, offs, B, Hq, c, idx_out, count_out, votes_out, stream);
 }
 
