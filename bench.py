@@ -69,6 +69,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip dense / warm / graph side measurements")
     ap.add_argument("--cpu-steps", type=int, default=10)
+    ap.add_argument("--reuse-radius", type=int, nargs="+", default=[0, 1],
+                    help="neighbour-fetch radii of the selection-reuse side measurement")
     ap.add_argument("--isolate", action="store_true", help="also time each call alone after a flush")
     ap.add_argument("--copy-probe", action="store_true",
                     help="end with three plain 256 MiB elementwise copies (torch.neg on fp32), a reference "
@@ -571,6 +573,47 @@ def main():
             extra["graph_step_us"] = round(float(np.mean([a.elapsed_time(b) * 1e3 for a, b in g_us[3:]])), 2)
         except Exception as e:  # capture is an optional side measurement
             extra["graph_step_us"] = f"unavailable: {type(e).__name__}"
+        # selection reuse with neighbour fetch: the selector (ts_score_select) runs every N steps,
+        # every step widens the last selection by +-radius and adds its forced tokens
+        # (ts_expand_selection), then decodes the widened list; mean us per step over the same
+        # flushed steps, for N = 1, 4, 8, 16
+        lists = Hq if mode == api.MODE_PER_HEAD else 1
+        cap_max = api.expand_capacity(kmax, nmax, 4, 256, max(args.reuse_radius))
+        ex_idx = torch.empty(cap_max * lists + 16, dtype=torch.int32, device=dev)
+        ex_caps = torch.empty(1, dtype=torch.int64, device=dev)
+        ex_valid = torch.empty((1, lists), dtype=torch.int64, device=dev)
+        ws_ex = torch.empty(max(api.decode_workspace_bytes(offs[-1], [cap_max], Hq, Hkv, mode), 256), dtype=torch.uint8,
+                            device=dev)
+        exp_, capp, valp, wexp = vp(ex_idx), vp(ex_caps), vp(ex_valid), vp(ws_ex)
+        extra["reuse"] = []
+        for radius in args.reuse_radius:
+            reuse = {"radius": radius, "us_per_step": {}}
+            for N in (1, 4, 8, 16):
+                r_evs, kprev = [], None
+                for i in range(min(steps, 48)):
+                    s_ = warm + i
+                    (kaddr, pos), (qp, od, oh), ch, kb = calls[s_]
+                    n_s = n0 + s_ + 1
+                    do_flush()
+                    st = stream_of()
+                    a, b2 = ev(), ev()
+                    a.record()
+                    if i % N == 0:
+                        chk(L.ts_score_select(qp, Pp, kip, Kp, od, oh, 1, Hq, Hkv, pref, scp, idp, cnp, None, None,
+                                              wss, ws_ss_n, st))
+                        kprev = (ctypes.c_int64 * 1)(kb)
+                    chk(L.ts_expand_selection(idp, cnp, kprev, od, oh, 1, lists, 4, 256, radius, exp_, capp, valp,
+                                              st))
+                    cap = api.expand_capacity(kprev[0], n_s, 4, 256, radius)
+                    chk(L.ts_sparse_decode(qp, Kp, Vp, od, oh, exp_, capp, (ctypes.c_int64 * 1)(cap), mode, 1, Hq,
+                                           Hkv, outp, wexp, ws_ex.numel(), st))
+                    b2.record()
+                    r_evs.append((a, b2))
+                torch.cuda.synchronize()
+                reuse["us_per_step"][str(N)] = round(float(np.mean([x.elapsed_time(y) * 1e3 for x, y in r_evs])), 2)
+            reuse["mean_entries_per_list"] = round(float(ex_valid.float().mean().item()), 1)
+            reuse["selected_per_list"] = int(kprev[0])
+            extra["reuse"].append(reuse)
         # SnapKV prefill-end compression at LLaMA-3-70B layer shapes (64 / 8 heads, w = 32,
         # c = 4096, pool 3) over the same n, LLC flushed before each call
         sx = synth.config5(n0)

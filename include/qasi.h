@@ -164,6 +164,33 @@ int ts_score_select(const uint16_t* q, const float* P, uint16_t* k_index, const 
                     int64_t* count_out, float* theta_out, uint8_t* votes_out, void* ws,
                     size_t ws_bytes, hipStream_t stream);
 
+/* Capacity of an expanded list (ts_expand_selection): min(n, (2 radius + 1) k_prev + sink +
+ * local); -1 if an argument is out of range. */
+int64_t ts_expand_capacity(int64_t k_prev, int64_t n, int64_t sink, int64_t local, int64_t radius);
+
+/* Selection reuse with neighbour fetch ([TB] "Inferenzstrategie", Optimierungen: the selector
+ * runs every N decode steps and the steps in between reuse its selection, widened by the
+ * spatial neighbours of the selected tokens; sink and local window are the always-kept buffers).
+ * For every list l < lists of sequence b (lists = 1 for vote-mode lists, Hq for per-head lists),
+ * with the current lengths n_b = offsets[b+1] - offsets[b]:
+ *   out = { t + d : t in prev, |d| <= radius, 0 <= t + d < n_b } U [0, min(sink, n_b))
+ *         U [max(0, n_b - local), n_b),  ascending,
+ * followed by -1 (empty slots, skipped by ts_sparse_decode) up to the list's capacity
+ * cap_b = ts_expand_capacity(counts_prev[b], n_b, sink, local, radius).
+ *   idx_prev     device int32 lists in the ts_select layout for `lists` lists per sequence with the
+ *                lengths counts_prev (sorted ascending, unique; negative entries are ignored)
+ *   counts_prev  device (counts_prev_dev) and host (counts_prev_host) int64 [B], the same values,
+ *                each at most n_b (an earlier step's lengths)
+ *   idx_out      device int32 [lists * sum_b cap_b], list l of b at lists*cpre_b + l*cap_b + j
+ *                (cpre_b = sum of the earlier capacities)
+ *   caps_out     device int64 [B] (receives cap_b: the list lengths to hand to ts_sparse_decode)
+ *   valid_out    device int64 [B][lists] (receives the number of entries before the empty slots).
+ * Pass caps_out and the host capacities as the counts of ts_sparse_decode.                */
+int ts_expand_selection(const int32_t* idx_prev, const int64_t* counts_prev_dev, const int64_t* counts_prev_host,
+                        const int64_t* offsets_dev, const int64_t* offsets_host, int32_t B, int32_t lists,
+                        int64_t sink, int64_t local, int64_t radius, int32_t* idx_out, int64_t* caps_out,
+                        int64_t* valid_out, hipStream_t stream);
+
 /* Workspace for ts_sparse_decode (counts_host = the per-sequence list lengths) and for
  * ts_dense_decode (counts_host = NULL). */
 size_t ts_decode_workspace_bytes(const int64_t* offsets_host, const int64_t* counts_host,
@@ -178,8 +205,9 @@ size_t ts_decode_workspace_bytes(const int64_t* offsets_host, const int64_t* cou
  *   q           device bf16 [B][Hq][128]
  *   K, V        device bf16 [Ntot][Hkv][128]
  *   idx         device int32 lists in the ts_select layout for `mode`; positions must be
- *               in [0, n_b) (out-of-range entries are a caller error; the kernel clamps
- *               them into range so that a bad list cannot read outside the cache)
+ *               in [0, n_b) or negative: a negative entry is an empty slot and is skipped
+ *               (positions >= n_b are a caller error; the kernel clamps them into range so
+ *               that a bad list cannot read outside the cache)
  *   counts_dev  device int64 [B] and counts_host host int64 [B]: the same list lengths
  *               (0 < count_b <= n_b; e.g. count_out of ts_select and ts_budget_tokens)
  *   out         device fp32 [B][Hq][128].                                             */
@@ -233,6 +261,22 @@ int snapkv_compress(const uint16_t* q_obs, const uint16_t* K, const uint16_t* V,
                     int32_t w, int32_t Hq, int32_t Hkv, int64_t c, int32_t pool_kernel,
                     int32_t* idx_out, uint16_t* K_out, uint16_t* V_out, float* importance_out,
                     float* pooled_out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* SnapKV cluster-based retention ([SK] "Top-k SelectionとCluster-based Retention", eq.
+ * S_final = U_{j in S} {j - k_cluster, ..., j + k_cluster}): every KV head's top-c list, as
+ * snapkv_compress writes it, widened by the k_cluster neighbours of its positions (inside
+ * [0, n)), ascending, padded with -1 to cap = ts_expand_capacity(ce, n, 0, 0, k_cluster) =
+ * min(n, (2 k_cluster + 1) ce), and the rows of the widened lists gathered:
+ *   K_out[s][g][:] = K[idx_out[g][s]][g][:] (bit copies), zero rows for the -1 slots.
+ *   idx        device int32 [Hkv][ce] (sorted ascending, unique)
+ *   K, V       device bf16 [n][Hkv][128]
+ *   idx_out    device int32 [Hkv][cap]
+ *   K_out, V_out device bf16 [cap][Hkv][128]
+ *   valid_out  device int64 [Hkv] (receives each head's number of entries before the padding).
+ * k_cluster = 0 copies the lists unchanged.                                              */
+int snapkv_retain_clusters(const int32_t* idx, int64_t n, int32_t Hkv, int64_t ce, int64_t k_cluster,
+                           const uint16_t* K, const uint16_t* V, int32_t* idx_out, uint16_t* K_out,
+                           uint16_t* V_out, int64_t* valid_out, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -78,6 +78,13 @@ def lib():
         L.qo_avg_pool1d.argtypes = [_f64p, _i64, _i64, _int, _f64p]
         L.qo_topc.restype = _i64
         L.qo_topc.argtypes = [_f64p, _i64, _i64, _i64, _i32p]
+        L.qo_expand_capacity.restype = _i64
+        L.qo_expand_capacity.argtypes = [_i64, _i64, _i64, _i64, _i64]
+        L.qo_expand_selection.restype = None
+        L.qo_expand_selection.argtypes = [_i32p, _i64p, _i64p, _int, _int, _i64, _i64, _i64, _i32p, _i64p]
+        L.qo_snapkv_retain_clusters.restype = _i64
+        L.qo_snapkv_retain_clusters.argtypes = [_u16p, _u16p, _i64, _int, _i32p, _i64, _i64, _i32p, _u16p, _u16p,
+                                                _i64p]
         L.qo_gather_rows.restype = None
         L.qo_gather_rows.argtypes = [_u16p, _u16p, _i64, _int, _i32p, _i64, _u16p, _u16p]
         _lib = L
@@ -257,3 +264,41 @@ def snapkv_importance_matmul(q_obs, K, Hq, Hkv, groups=None):
         s /= s.sum(axis=1, keepdims=True)
         out[g] = s.mean(axis=0)
     return out
+
+
+def expand_capacity(k_prev, n, sink=4, local=256, radius=1):
+    return int(lib().qo_expand_capacity(int(k_prev), int(n), int(sink), int(local), int(radius)))
+
+
+def expand_selection(prev, counts_prev, offsets, lists=1, sink=4, local=256, radius=1):
+    """Selection reuse with neighbour fetch: every list of `prev` (ts_select layout, `lists` lists
+    per sequence with lengths counts_prev) widened by +-radius, joined with the current forced
+    tokens, ascending, padded with -1 to the capacity.  Returns (idx, counts [B][lists], caps)."""
+    offsets = _c(offsets, np.int64)
+    counts_prev = _c(counts_prev, np.int64)
+    B = len(offsets) - 1
+    caps = [expand_capacity(counts_prev[b], offsets[b + 1] - offsets[b], sink, local, radius) for b in range(B)]
+    out = np.empty(max(lists * sum(caps), 1), np.int32)
+    cnt = np.empty(B * lists, np.int64)
+    prev = _c(prev, np.int32)
+    if prev.size == 0:
+        prev = np.zeros(1, np.int32)
+    lib().qo_expand_selection(prev, counts_prev, offsets, B, lists, sink, local, radius, out, cnt)
+    return out[:lists * sum(caps)], cnt.reshape(B, lists), caps
+
+
+def snapkv_retain_clusters(K, V, idx, k_cluster):
+    """Cluster-based retention: idx [Hkv][ce] widened by +-k_cluster, padded with -1, and the rows
+    gathered (zero rows for the padding).  Returns (idx_out [Hkv][cap], K_out, V_out, valid [Hkv])."""
+    K = _c(K, np.uint16)
+    V = _c(V, np.uint16)
+    n, Hkv, _ = K.shape
+    idx = _c(idx, np.int32)
+    ce = idx.shape[1]
+    cap = expand_capacity(ce, n, 0, 0, k_cluster)
+    io = np.empty((Hkv, max(cap, 1)), np.int32)
+    Ko = np.empty((max(cap, 1), Hkv, D), np.uint16)
+    Vo = np.empty((max(cap, 1), Hkv, D), np.uint16)
+    valid = np.empty(Hkv, np.int64)
+    lib().qo_snapkv_retain_clusters(K, V, n, Hkv, idx, ce, k_cluster, io, Ko, Vo, valid)
+    return io[:, :cap], Ko[:cap], Vo[:cap], valid

@@ -263,7 +263,8 @@ void qo_select_per_head(const double* scores, const int64_t* offsets, int B, int
  * which already holds the sink and local tokens, so the "output merge" of sparse and
  * local attention is one softmax over their disjoint union.  mode 0: one list per
  * sequence (idx[kpre_b + j]); mode 1: one list per query head
- * (idx[Hq*kpre_b + h*count_b + j]).  out is [B][Hq][128]. */
+ * (idx[Hq*kpre_b + h*count_b + j]).  Negative entries are empty slots (the padding of an
+ * expanded list) and are skipped.  out is [B][Hq][128]. */
 void qo_decode(const uint16_t* q, const uint16_t* K, const uint16_t* V, const int64_t* offsets,
                const int32_t* idx, const int64_t* count, int mode, int B, int Hq, int Hkv,
                double* out) {
@@ -279,6 +280,7 @@ void qo_decode(const uint16_t* q, const uint16_t* K, const uint16_t* V, const in
             double* o = out + ((int64_t)b * Hq + h) * QO_D;
             double m = -INFINITY;
             for (int64_t j = 0; j < cnt; ++j) {
+                if (list[j] < 0) continue;
                 const uint16_t* kr = K + ((offsets[b] + list[j]) * Hkv + g) * QO_D;
                 double s = 0.0;
                 for (int e = 0; e < QO_D; ++e) s += bf16_widen(qh[e]) * bf16_widen(kr[e]);
@@ -288,6 +290,7 @@ void qo_decode(const uint16_t* q, const uint16_t* K, const uint16_t* V, const in
             double l = 0.0;
             for (int e = 0; e < QO_D; ++e) o[e] = 0.0;
             for (int64_t j = 0; j < cnt; ++j) {
+                if (list[j] < 0) continue;
                 double w = exp(z[j] - m);
                 l += w;
                 const uint16_t* vr = V + ((offsets[b] + list[j]) * Hkv + g) * QO_D;
@@ -381,15 +384,87 @@ int64_t qo_topc(const double* pooled, int64_t rows, int64_t n, int64_t c, int32_
 }
 
 /* [SK] "アルゴリズム": gather the chosen K and V rows of each KV head into a compacted
- * cache K_out[s][g][128] = K[idx[g][s]][g][128] (bit copies). */
+ * cache K_out[s][g][128] = K[idx[g][s]][g][128] (bit copies).  An empty slot (idx < 0, the
+ * padding of a cluster-widened list) gets a zero row. */
 void qo_gather_rows(const uint16_t* K, const uint16_t* V, int64_t n, int Hkv, const int32_t* idx,
                     int64_t ce, uint16_t* K_out, uint16_t* V_out) {
     (void)n;
     for (int g = 0; g < Hkv; ++g)
         for (int64_t s = 0; s < ce; ++s) {
-            int64_t src = ((int64_t)idx[(int64_t)g * ce + s] * Hkv + g) * QO_D;
+            int64_t t = idx[(int64_t)g * ce + s];
             int64_t dst = (s * Hkv + g) * QO_D;
+            if (t < 0) {
+                memset(K_out + dst, 0, QO_D * sizeof(uint16_t));
+                memset(V_out + dst, 0, QO_D * sizeof(uint16_t));
+                continue;
+            }
+            int64_t src = (t * Hkv + g) * QO_D;
             memcpy(K_out + dst, K + src, QO_D * sizeof(uint16_t));
             memcpy(V_out + dst, V + src, QO_D * sizeof(uint16_t));
         }
+}
+
+/* ------------------------------------------------- selection reuse + neighbours */
+
+/* Capacity of an expanded list: min(n, (2 radius + 1) k_prev + sink + local). */
+int64_t qo_expand_capacity(int64_t k_prev, int64_t n, int64_t sink, int64_t local, int64_t radius) {
+    int64_t c = (2 * radius + 1) * k_prev + sink + local;
+    return c < n ? c : n;
+}
+
+/* [TB] "Inferenzstrategie", Optimierungen (prediction interval and neighbour fetch): the
+ * selector runs every N decode steps; in between, the last selection is reused, widened by the
+ * spatial neighbours of every selected token, and the current step's always-kept tokens are
+ * added.  For each list (one per sequence, or one per query head of a sequence): the set
+ *   { t + d : t in prev, |d| <= radius, 0 <= t + d < n } U [0, min(sink, n)) U [max(0, n - local), n)
+ * in ascending order, followed by -1 (empty slots) up to the list's capacity.  Lists are laid
+ * out like ts_select's: list l of sequence b at out[L * cpre_b + l * cap_b + j] (L lists per
+ * sequence, cpre_b = sum of the earlier sequences' capacities), the previous lists likewise with
+ * the previous counts.  count_out[b * L + l] = the number of valid entries. */
+void qo_expand_selection(const int32_t* prev, const int64_t* counts_prev, const int64_t* offsets, int B, int L,
+                         int64_t sink, int64_t local, int64_t radius, int32_t* out, int64_t* count_out) {
+    int64_t ppre = 0, cpre = 0;
+    for (int b = 0; b < B; ++b) {
+        int64_t n = offsets[b + 1] - offsets[b];
+        int64_t kp = counts_prev[b];
+        int64_t cap = qo_expand_capacity(kp, n, sink, local, radius);
+        char* take = (char*)calloc((size_t)(n > 0 ? n : 1), 1);
+        for (int l = 0; l < L; ++l) {
+            memset(take, 0, (size_t)(n > 0 ? n : 1));
+            const int32_t* p = prev + L * ppre + (int64_t)l * kp;
+            for (int64_t j = 0; j < kp; ++j)
+                for (int64_t d = -radius; d <= radius; ++d) {
+                    int64_t t = (int64_t)p[j] + d;
+                    if (t >= 0 && t < n) take[t] = 1;
+                }
+            for (int64_t t = 0; t < n; ++t)
+                if (is_forced(t, n, sink, local)) take[t] = 1;
+            int32_t* o = out + L * cpre + (int64_t)l * cap;
+            int64_t w = 0;
+            for (int64_t t = 0; t < n; ++t)
+                if (take[t]) o[w++] = (int32_t)t;
+            count_out[(int64_t)b * L + l] = w;
+            for (; w < cap; ++w) o[w] = -1;
+        }
+        free(take);
+        ppre += kp;
+        cpre += cap;
+    }
+}
+
+/* [SK] "Top-k SelectionとCluster-based Retention", eq. S_final = U_{j in S} {j - k, ..., j + k}:
+ * every KV head's top-c positions widened by their k_cluster neighbours (inside [0, n)),
+ * ascending, padded with -1 to min(n, (2 k_cluster + 1) ce); then the rows gathered as
+ * qo_gather_rows does.  idx is [Hkv][ce]; idx_out is [Hkv][cap]; valid_out[g] = the number of
+ * entries before the padding.  (The neighbour widening of the selection reuse with no
+ * always-kept tokens.)  Returns cap. */
+int64_t qo_snapkv_retain_clusters(const uint16_t* K, const uint16_t* V, int64_t n, int Hkv, const int32_t* idx,
+                                  int64_t ce, int64_t k_cluster, int32_t* idx_out, uint16_t* K_out,
+                                  uint16_t* V_out, int64_t* valid_out) {
+    int64_t offsets[2] = {0, n};
+    int64_t counts[1] = {ce};
+    int64_t cap = qo_expand_capacity(ce, n, 0, 0, k_cluster);
+    qo_expand_selection(idx, counts, offsets, 1, Hkv, 0, 0, k_cluster, idx_out, valid_out);
+    qo_gather_rows(K, V, n, Hkv, idx_out, cap, K_out, V_out);
+    return cap;
 }

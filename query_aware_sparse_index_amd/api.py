@@ -164,6 +164,30 @@ def score_select(q, P, k_index, offs: Offsets, Hkv: int, p, K_last=None, want_th
     return res
 
 
+def expand_capacity(k_prev: int, n: int, sink=4, local=256, radius=1) -> int:
+    return int(_lib.load().ts_expand_capacity(int(k_prev), int(n), int(sink), int(local), int(radius)))
+
+
+def expand_selection(idx_prev, counts_prev_dev, counts_prev_host, offs: Offsets, lists: int = 1, sink=4, local=256,
+                     radius=1, out=None, caps=None, valid=None):
+    """ts_expand_selection: the previous lists widened by +-radius plus the current forced tokens,
+    padded with -1 to their capacities.  Returns a dict with "idx", "caps" (device), "caps_host",
+    "valid" (device [B][lists])."""
+    dev = idx_prev.device
+    caps_host = [expand_capacity(counts_prev_host[b], offs.host_list[b + 1] - offs.host_list[b], sink, local, radius)
+                 for b in range(offs.B)]
+    if out is None:
+        out = torch.empty(max(lists * sum(caps_host), 4), dtype=torch.int32, device=dev)
+    if caps is None:
+        caps = torch.empty(offs.B, dtype=torch.int64, device=dev)
+    if valid is None:
+        valid = torch.empty((offs.B, lists), dtype=torch.int64, device=dev)
+    _check(_lib.load().ts_expand_selection(_p(idx_prev), _p(counts_prev_dev), _host_i64(counts_prev_host),
+                                           _p(offs.dev), offs.host, offs.B, int(lists), int(sink), int(local),
+                                           int(radius), _p(out), _p(caps), _p(valid), _stream()))
+    return {"idx": out[:lists * sum(caps_host)], "caps": caps, "caps_host": caps_host, "valid": valid}
+
+
 def decode_workspace_bytes(offs: Offsets, counts_host, Hq: int, Hkv: int, mode: int) -> int:
     ch = _host_i64(counts_host) if counts_host is not None else None
     return int(_lib.load().ts_decode_workspace_bytes(offs.host, ch, offs.B, int(Hq), int(Hkv), int(mode)))
@@ -238,3 +262,20 @@ def snapkv_compress(q_obs, K, V, c: int = 4096, pool_kernel: int = 3, want_impor
         res["importance"] = imp
         res["pooled"] = pooled
     return res
+
+
+def snapkv_retain_clusters(idx, K, V, k_cluster: int = 1):
+    """Cluster-based retention of snapkv_compress's lists idx [Hkv][ce]: widened by +-k_cluster,
+    padded with -1, rows gathered (zero rows for the padding).  Returns idx, K, V, valid."""
+    _bf16_check(K, V)
+    n, Hkv, _ = K.shape
+    ce = idx.shape[1]
+    cap = expand_capacity(ce, n, 0, 0, k_cluster)
+    dev = K.device
+    io = torch.empty((Hkv, max(cap, 1)), dtype=torch.int32, device=dev)
+    Ko = torch.empty((max(cap, 1), Hkv, 128), dtype=K.dtype, device=dev)
+    Vo = torch.empty((max(cap, 1), Hkv, 128), dtype=V.dtype, device=dev)
+    valid = torch.empty(Hkv, dtype=torch.int64, device=dev)
+    _check(_lib.load().snapkv_retain_clusters(_p(idx), int(n), int(Hkv), int(ce), int(k_cluster), _p(K), _p(V),
+                                              _p(io), _p(Ko), _p(Vo), _p(valid), _stream()))
+    return {"idx": io[:, :cap], "K": Ko[:cap], "V": Vo[:cap], "valid": valid}

@@ -212,6 +212,38 @@ int ts_score_select(const uint16_t* q, const float* P, uint16_t* k_index, const 
                       "ts_score_select launch");
 }
 
+int64_t ts_expand_capacity(int64_t k_prev, int64_t n, int64_t sink, int64_t local, int64_t radius) {
+    if (k_prev < 0 || n < 0 || sink < 0 || local < 0 || radius < 0 || radius > (1 << 20) || k_prev > n) return -1;
+    return qasi::expand_capacity(k_prev, n, sink, local, radius);
+}
+
+int ts_expand_selection(const int32_t* idx_prev, const int64_t* counts_prev_dev, const int64_t* counts_prev_host,
+                        const int64_t* offsets_dev, const int64_t* offsets_host, int32_t B, int32_t lists,
+                        int64_t sink, int64_t local, int64_t radius, int32_t* idx_out, int64_t* caps_out,
+                        int64_t* valid_out, hipStream_t stream) {
+    if (!idx_prev || (reinterpret_cast<uintptr_t>(idx_prev) & 3u) || !idx_out || (reinterpret_cast<uintptr_t>(idx_out) & 3u))
+        return fail(QASI_ERR_INVALID, "idx_prev and idx_out must be non-null and 4-byte aligned");
+    if (!counts_prev_dev || !counts_prev_host || (reinterpret_cast<uintptr_t>(counts_prev_dev) & 7u))
+        return fail(QASI_ERR_INVALID, "counts_prev_dev / counts_prev_host must be non-null (device copy 8-byte aligned)");
+    if (!caps_out || !valid_out || (reinterpret_cast<uintptr_t>(caps_out) & 7u) || (reinterpret_cast<uintptr_t>(valid_out) & 7u))
+        return fail(QASI_ERR_INVALID, "caps_out and valid_out must be non-null and 8-byte aligned");
+    if (lists < 1 || lists > 64) return fail(QASI_ERR_INVALID, "lists=%d outside [1, 64]", lists);
+    if (sink < 0 || local < 0 || sink > ((int64_t)1 << 31) || local > ((int64_t)1 << 31))
+        return fail(QASI_ERR_INVALID, "sink/local must be in [0, 2^31]");
+    if (radius < 0 || radius > (1 << 20)) return fail(QASI_ERR_INVALID, "radius=%lld outside [0, 2^20]", (long long)radius);
+    if (int r = check_offsets(offsets_dev, offsets_host, B, true)) return r;
+    for (int b = 0; b < B; ++b) {
+        const int64_t n = offsets_host[b + 1] - offsets_host[b];
+        if (counts_prev_host[b] < 0 || counts_prev_host[b] > n)
+            return fail(QASI_ERR_INVALID, "counts_prev[%d]=%lld outside [0, n_b=%lld]", b, (long long)counts_prev_host[b],
+                        (long long)n);
+    }
+    if (int r = init_once()) return r;
+    return hip_status(qasi::launch_expand(idx_prev, counts_prev_dev, counts_prev_host, offsets_dev, offsets_host, B,
+                                          lists, sink, local, radius, idx_out, caps_out, valid_out, stream),
+                      "ts_expand_selection launch");
+}
+
 size_t ts_decode_workspace_bytes(const int64_t* offsets_host, const int64_t* counts_host, int32_t B, int32_t Hq,
                                  int32_t Hkv, int32_t mode) {
     if (!offsets_host || B <= 0 || Hq <= 0 || Hkv <= 0) return 0;
@@ -313,6 +345,26 @@ int snapkv_compress(const uint16_t* q_obs, const uint16_t* K, const uint16_t* V,
     return hip_status(qasi::launch_snapkv(q_obs, K, V, n, w, Hq, Hkv, c, idx_out, K_out, V_out, importance_out,
                                           pooled_out, ws, ws_bytes, stream),
                       "snapkv_compress launch");
+}
+
+int snapkv_retain_clusters(const int32_t* idx, int64_t n, int32_t Hkv, int64_t ce, int64_t k_cluster, const uint16_t* K,
+                           const uint16_t* V, int32_t* idx_out, uint16_t* K_out, uint16_t* V_out, int64_t* valid_out,
+                           hipStream_t stream) {
+    if (!idx || (reinterpret_cast<uintptr_t>(idx) & 3u) || !idx_out || (reinterpret_cast<uintptr_t>(idx_out) & 3u))
+        return fail(QASI_ERR_INVALID, "idx and idx_out must be non-null and 4-byte aligned");
+    if (!aligned16(K) || !aligned16(V) || !aligned16(K_out) || !aligned16(V_out))
+        return fail(QASI_ERR_INVALID, "K, V, K_out and V_out must be non-null and 16-byte aligned");
+    if (!valid_out || (reinterpret_cast<uintptr_t>(valid_out) & 7u))
+        return fail(QASI_ERR_INVALID, "valid_out must be non-null and 8-byte aligned");
+    if (n <= 0 || n > ((int64_t)1 << 24)) return fail(QASI_ERR_INVALID, "n=%lld outside [1, 2^24]", (long long)n);
+    if (!hkv_ok(Hkv)) return fail(QASI_ERR_UNSUPPORTED, "Hkv=%d not in {1,2,4,8}", Hkv);
+    if (ce < 0 || ce > n) return fail(QASI_ERR_INVALID, "ce=%lld outside [0, n]", (long long)ce);
+    if (k_cluster < 0 || k_cluster > (1 << 20))
+        return fail(QASI_ERR_INVALID, "k_cluster=%lld outside [0, 2^20]", (long long)k_cluster);
+    if (int r = init_once()) return r;
+    return hip_status(qasi::launch_snapkv_clusters(idx, n, Hkv, ce, k_cluster, K, V, idx_out, K_out, V_out, valid_out,
+                                                   stream),
+                      "snapkv_retain_clusters launch");
 }
 
 }  // extern "C"

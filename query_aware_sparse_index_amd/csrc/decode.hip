@@ -197,7 +197,8 @@ __global__ __launch_bounds__(kDecWaves * 64, dec_min_blocks(G, MODE)) void decod
     const int nsb = (wlen + kDecSub - 1) / kDecSub;
 
     // token ids of the wave's entries into LDS (entries past the wave's end repeat its first token,
-    // so that every load of a sub-batch is issued and hits a row already requested)
+    // so that every load of a sub-batch is issued and hits a row already requested); negative
+    // entries are empty slots (-1): their rows are read at position 0 and their scores are -inf
     int32_t* tok = reinterpret_cast<int32_t*>(&s_tok[wid][0]);
     {
         int32_t t0 = 0;
@@ -211,7 +212,7 @@ __global__ __launch_bounds__(kDecWaves * 64, dec_min_blocks(G, MODE)) void decod
                 const int64_t j = j0 + wb + i;
                 t = (MODE == 2) ? (int32_t)j : ((MODE == 1) ? idx[Hq * kpre + (int64_t)hw * counts[b] + j] : idx[kpre + j]);
             }
-            tok[i] = t < 0 ? 0 : (t > nmax ? nmax : t);
+            tok[i] = t < 0 ? -1 : (t > nmax ? nmax : t);
         }
     }
     uint4 qv[GH];
@@ -222,9 +223,11 @@ __global__ __launch_bounds__(kDecWaves * 64, dec_min_blocks(G, MODE)) void decod
     const uint16_t* Kg = K + (off * Hkv + g) * kD + p * 8;
     const uint16_t* Vg = V + (off * Hkv + g) * kD + p * 8;
     const int64_t rstride = (int64_t)Hkv * kD;
-    auto issue = [&](int sb, uint4 (&kb)[EPR], uint4 (&vb)[EPR]) {
+    // em: bit k set when entry k of the lane's row is an empty slot
+    auto issue = [&](int sb, uint4 (&kb)[EPR], uint4 (&vb)[EPR], int& em) {
         const int4 t = s_tok[wid][(sb * kDecSub + row * EPR) / 4];
-        const int tt[4] = {t.x, t.y, t.z, t.w};
+        const int tt[4] = {t.x < 0 ? 0 : t.x, t.y < 0 ? 0 : t.y, t.z < 0 ? 0 : t.z, t.w < 0 ? 0 : t.w};
+        em = (t.x < 0 ? 1 : 0) | (t.y < 0 ? 2 : 0) | (t.z < 0 ? 4 : 0) | (t.w < 0 ? 8 : 0);
 #pragma unroll
         for (int k = 0; k < EPR; ++k) kb[k] = ld16(Kg + tt[k] * rstride);
 #pragma unroll
@@ -242,7 +245,7 @@ __global__ __launch_bounds__(kDecWaves * 64, dec_min_blocks(G, MODE)) void decod
     float4* sp4 = &s_p[wid][row][0];
     float* sp = reinterpret_cast<float*>(sp4);
 
-    auto compute = [&](int sb, const uint4 (&kb)[EPR], const uint4 (&vb)[EPR]) {
+    auto compute = [&](int sb, const uint4 (&kb)[EPR], const uint4 (&vb)[EPR], int em) {
         float zp[NV];
 #pragma unroll
         for (int k = 0; k < EPR; ++k)
@@ -258,8 +261,9 @@ __global__ __launch_bounds__(kDecWaves * 64, dec_min_blocks(G, MODE)) void decod
         float mx = -INFINITY;
 #pragma unroll
         for (int s = 0; s < FV; ++s) {
-            const int e = sb * kDecSub + row * EPR + (i0 + s) % EPR;
-            z[s] = e < wlen ? z[s] * kLog2eOverSqrtD : -INFINITY;
+            const int ke = (i0 + s) % EPR;
+            const int e = sb * kDecSub + row * EPR + ke;
+            z[s] = (e < wlen && !((em >> ke) & 1)) ? z[s] * kLog2eOverSqrtD : -INFINITY;
             mx = fmaxf(mx, z[s]);
         }
         const float m_new = fmaxf(m_run, head_reduce<true, HS0, HS1>(mx));
@@ -308,12 +312,13 @@ __global__ __launch_bounds__(kDecWaves * 64, dec_min_blocks(G, MODE)) void decod
 
     // two register sets: A = even sub-batches, B = odd
     uint4 ka[EPR], va[EPR], kb2[EPR], vb2[EPR];
-    if (nsb > 0) issue(0, ka, va);
+    int ema = 0, emb = 0;
+    if (nsb > 0) issue(0, ka, va, ema);
     for (int sb = 0; sb < nsb; sb += 2) {
-        if (sb + 1 < nsb) issue(sb + 1, kb2, vb2);
-        compute(sb, ka, va);
-        if (sb + 2 < nsb) issue(sb + 2, ka, va);
-        if (sb + 1 < nsb) compute(sb + 1, kb2, vb2);
+        if (sb + 1 < nsb) issue(sb + 1, kb2, vb2, emb);
+        compute(sb, ka, va, ema);
+        if (sb + 2 < nsb) issue(sb + 2, ka, va, ema);
+        if (sb + 1 < nsb) compute(sb + 1, kb2, vb2, emb);
     }
 
     // sum over the 4 rows: row r holds accumulator indices r * NA / 4 + j

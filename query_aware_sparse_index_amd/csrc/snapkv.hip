@@ -304,6 +304,46 @@ __global__ void snap_gather_kernel(const uint16_t* __restrict__ K, const uint16_
     *reinterpret_cast<uint4*>(V_out + dst) = *reinterpret_cast<const uint4*>(V + src);
 }
 
+// Cluster-based retention ([SK] "Top-k SelectionとCluster-based Retention", eq. S_final): the
+// widened lists come from the selection expansion kernel (no always-kept tokens); this gather
+// copies their rows and writes zero rows for the empty slots (-1) that pad a head's list to the
+// capacity.  K_out[s][g] = idx[g][s] >= 0 ? K[idx[g][s]][g] : 0; one 16-byte piece per thread.
+__global__ void snap_gather_padded_kernel(const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+                                          const int32_t* __restrict__ idx, int64_t n, int64_t cap, int Hkv,
+                                          uint16_t* __restrict__ K_out, uint16_t* __restrict__ V_out) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= cap * Hkv * 16) return;
+    const int64_t piece = i % 16, sg = i / 16;
+    const int64_t s = sg / Hkv, g = sg % Hkv;
+    const int64_t t = idx[g * cap + s];
+    const int64_t dst = (s * Hkv + g) * kD + piece * 8;
+    uint4 k = make_uint4(0, 0, 0, 0), v = make_uint4(0, 0, 0, 0);
+    if (t >= 0) {
+        const int64_t tc = t >= n ? n - 1 : t;
+        const int64_t src = (tc * Hkv + g) * kD + piece * 8;
+        k = *reinterpret_cast<const uint4*>(K + src);
+        v = *reinterpret_cast<const uint4*>(V + src);
+    }
+    *reinterpret_cast<uint4*>(K_out + dst) = k;
+    *reinterpret_cast<uint4*>(V_out + dst) = v;
+}
+
+hipError_t launch_snapkv_clusters(const int32_t* idx, int64_t n, int Hkv, int64_t ce, int64_t k_cluster,
+                                  const uint16_t* K, const uint16_t* V, int32_t* idx_out, uint16_t* K_out,
+                                  uint16_t* V_out, int64_t* valid_out, hipStream_t stream) {
+    // one sequence {0, n} with Hkv lists of ce entries: the bounds travel as launch arguments
+    const int64_t offs[2] = {0, n};
+    const int64_t cnt[1] = {ce};
+    hipError_t e = launch_expand(idx, nullptr, cnt, nullptr, offs, 1, Hkv, 0, 0, k_cluster, idx_out, nullptr,
+                                 valid_out, stream);
+    if (e != hipSuccess) return e;
+    const int64_t cap = expand_capacity(ce, n, 0, 0, k_cluster);
+    const int64_t pieces = cap * Hkv * 16;
+    hipLaunchKernelGGL(snap_gather_padded_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, stream, K, V,
+                       idx_out, n, cap, Hkv, K_out, V_out);
+    return hipGetLastError();
+}
+
 // one pass block per CU: 256 / Hkv per KV head, at most one per key block
 static int64_t snap_blocks_per_head(int Hkv, int64_t nblk) {
     int64_t p = 256 / Hkv;

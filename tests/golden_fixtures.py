@@ -69,3 +69,20 @@ def pool_example():
             lhs, rhs = line.split("->")
             tops.append((int(lhs.split("=")[1]), np.array([int(x) for x in rhs.split()], np.int32)))
     return imp, pooled, tops
+
+
+def expand_example():
+    """The worked neighbour-fetch example: n, sink, local, prev and per radius (valid, padding)."""
+    vals, cases = {}, []
+    for line in open(os.path.join(GOLDEN, "expand_example.txt")):
+        line = line.split("#")[0].strip()
+        if not line:
+            continue
+        if line.startswith("radius"):
+            head, rest = line.split("->")
+            valid, pad = rest.split("|")
+            cases.append((int(head.split()[1]), [int(x) for x in valid.split()], [int(x) for x in pad.split()]))
+        else:
+            k, v = line.split("=")
+            vals[k.strip()] = [int(x) for x in v.split()]
+    return vals["n"][0], vals["sink"][0], vals["local"][0], np.array(vals["prev"], np.int32), cases

@@ -55,3 +55,13 @@ def test_pool_topc_example():
     assert np.array_equal(got, pooled)
     for c, want in tops:
         assert np.array_equal(O.topc(got[None, :], c)[0], want), (c, O.topc(got[None, :], c)[0])
+
+
+def test_expand_example():
+    from golden_fixtures import expand_example
+    n, sink, local, prev, cases = expand_example()
+    for radius, valid, pad in cases:
+        idx, cnt, caps = O.expand_selection(prev, [len(prev)], [0, n], 1, sink, local, radius)
+        assert list(idx) == valid + pad, (radius, list(idx))
+        assert cnt[0, 0] == len(valid) and caps[0] == len(valid) + len(pad)
+        assert _lib.load().ts_expand_capacity(len(prev), n, sink, local, radius) == caps[0]

@@ -99,3 +99,19 @@ def test_snapkv_full_size_c5():
     _check_selection(x, r)
     stats.update(check_snap_endtoend(x, r, groups=[0, 5]))
     print("snapkv c5", stats)
+
+
+@pytest.mark.parametrize("k_cluster", [0, 1, 2])
+def test_snapkv_cluster_retention(k_cluster):
+    """Cluster-based retention of the GPU's top-c lists: widened lists, padding and the gathered
+    rows bit-exact against the oracle on the same lists."""
+    x = synth.make_snap(14, 5000, 8, 16, 4, 60, 400)
+    r = _run(x)
+    K, V = to_dev(x.K), to_dev(x.V)
+    c = api.snapkv_retain_clusters(r["idx"], K, V, k_cluster)
+    torch.cuda.synchronize()
+    io, Ko, Vo, valid = O.snapkv_retain_clusters(x.K, x.V, r["idx"].cpu().numpy(), k_cluster)
+    assert np.array_equal(c["idx"].cpu().numpy(), io)
+    assert np.array_equal(c["valid"].cpu().numpy(), valid)
+    assert np.array_equal(bits(c["K"]), Ko) and np.array_equal(bits(c["V"]), Vo)
+    print("cluster", k_cluster, "kept", valid.tolist(), "of capacity", io.shape[1])

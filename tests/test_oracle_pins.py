@@ -477,3 +477,95 @@ def test_snapkv_importance_matmul_matches_loop_oracle_and_torch(n, w, Hq, Hkv, g
         assert np.allclose(mm[g], loop[g], rtol=1e-12, atol=1e-16), g
         assert np.allclose(mm[g], ref, rtol=1e-12, atol=1e-16), g
         assert abs(mm[g].sum() - 1.0) < 1e-12
+
+
+# ------------------------------------------------------- selection reuse + neighbours
+
+def _expand_bruteforce(prev, n, sink, local, radius):
+    s = set(range(min(sink, n))) | set(range(max(0, n - local), n))
+    for t in prev:
+        if t < 0:
+            continue
+        s |= {t + d for d in range(-radius, radius + 1) if 0 <= t + d < n}
+    return sorted(s)
+
+
+@pytest.mark.parametrize("radius", [0, 1, 2, 5])
+def test_expand_selection_bruteforce_and_invariants(radius):
+    """Every list of a ragged batch, in the one-list and the per-head layouts, against a set built
+    by brute force; sorted, unique, holding the forced tokens and the previous tokens still in
+    range, every token within `radius` of a previous one or forced; -1 after the valid entries."""
+    rng = np.random.default_rng(radius)
+    lens = [1, 40, 700, 3000]
+    offsets = np.concatenate([[0], np.cumsum(lens)])
+    for L in (1, 3):
+        kps = [int(rng.integers(0, n + 1)) for n in lens]
+        prev = []
+        for n, k in zip(lens, kps):
+            for _ in range(L):
+                prev.append(np.sort(rng.choice(n, size=k, replace=False)))
+        # previous lists of an earlier, shorter step: entries must be < that step's length
+        idx, cnt, caps = O.expand_selection(np.concatenate(prev), kps, offsets, L, 4, 256, radius)
+        pos, li = 0, 0
+        for b, n in enumerate(lens):
+            cap = caps[b]
+            assert cap == min(n, (2 * radius + 1) * kps[b] + 4 + 256)
+            for l in range(L):
+                got = idx[pos:pos + cap]
+                want = _expand_bruteforce(prev[li], n, 4, 256, radius)
+                v = int(cnt[b, l])
+                assert v == len(want) and list(got[:v]) == want and np.all(got[v:] == -1)
+                forced = set(range(min(4, n))) | set(range(max(0, n - 256), n))
+                assert forced <= set(want) and set(prev[li].tolist()) <= set(want)
+                pv = prev[li]
+                for t in want:
+                    assert t in forced or (len(pv) and np.min(np.abs(pv - t)) <= radius)
+                pos += cap
+                li += 1
+
+
+def test_expand_selection_special_cases():
+    # radius 0: the previous list joined with the forced tokens; short rows: everything
+    prev = np.array([10, 50, 51, 300], np.int32)
+    idx, cnt, _ = O.expand_selection(prev, [4], [0, 1000], 1, 4, 256, 0)
+    assert list(idx[:cnt[0, 0]]) == [0, 1, 2, 3, 10, 50, 51, 300] + list(range(744, 1000))
+    idx, cnt, caps = O.expand_selection(np.array([1, 2], np.int32), [2], [0, 200], 1, 4, 256, 1)
+    assert caps[0] == 200 and list(idx) == list(range(200))
+    # an empty previous list keeps only the forced tokens
+    idx, cnt, _ = O.expand_selection(np.zeros(0, np.int32), [0], [0, 1000], 1, 4, 256, 3)
+    assert list(idx[:cnt[0, 0]]) == [0, 1, 2, 3] + list(range(744, 1000))
+
+
+def test_decode_skips_empty_slots():
+    """-1 entries of a list (the padding of an expanded list) contribute nothing: the decode of a
+    padded list equals the decode of its valid entries."""
+    rng = np.random.default_rng(4)
+    x = synth.make_decode(7, [500], 8, 2, 4, False, (1, 5), 0)
+    lst = np.sort(rng.choice(500, size=60, replace=False)).astype(np.int32)
+    padded = np.concatenate([lst, -np.ones(25, np.int32)])
+    a = O.decode(x.q, x.K, x.V, x.offsets, lst, np.array([60]), 0, 8, 2)
+    b = O.decode(x.q, x.K, x.V, x.offsets, padded, np.array([85]), 0, 8, 2)
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("k_cluster", [0, 1, 3])
+def test_snapkv_cluster_retention_bruteforce(k_cluster):
+    """S_final = U_{j in S} {j - k, ..., j + k} per KV head (brute-force set union), ascending,
+    padded with -1 to min(n, (2k + 1) c); rows are bit copies and the padding rows are zero."""
+    rng = np.random.default_rng(k_cluster + 10)
+    n, Hkv, c = 500, 2, 40
+    K = rng.integers(1, 60000, size=(n, Hkv, D), dtype=np.uint16)
+    V = rng.integers(1, 60000, size=(n, Hkv, D), dtype=np.uint16)
+    idx = np.stack([np.sort(rng.choice(n, size=c, replace=False)) for _ in range(Hkv)]).astype(np.int32)
+    idx[0, :3] = [0, 1, 2]                 # neighbours of the first position clip at 0
+    idx[0] = np.sort(idx[0])
+    io, Ko, Vo, valid = O.snapkv_retain_clusters(K, V, idx, k_cluster)
+    cap = min(n, (2 * k_cluster + 1) * c)
+    assert io.shape == (Hkv, cap)
+    for g in range(Hkv):
+        want = sorted({int(j) + d for j in idx[g] for d in range(-k_cluster, k_cluster + 1) if 0 <= j + d < n})
+        assert valid[g] == len(want) and list(io[g, :len(want)]) == want and np.all(io[g, len(want):] == -1)
+        assert np.array_equal(Ko[:len(want), g], K[want, g]) and np.array_equal(Vo[:len(want), g], V[want, g])
+        assert not Ko[len(want):, g].any() and not Vo[len(want):, g].any()
+    if k_cluster == 0:
+        assert np.array_equal(io, idx)
