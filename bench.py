@@ -50,6 +50,61 @@ def measured_traffic(mode, n, budget):
     return rec.get("bytes_per_launch")
 
 
+# ------------------------------------------------------------------ CPU oracle leg
+# The oracle as it stands (plain fp64 C loops, one thread per step) on the host cores: whole
+# decode steps of the benchmarked workload, first one after another in this process, then one
+# step per worker process, all at once, on min(host cores, 16) processes.  It runs before the
+# GPU is initialised, so the workers are plain forks sharing the inputs.
+_CPU = {}
+
+
+def _oracle_step(s):
+    from oracle import oracle as O
+    c = _CPU
+    n = c["n0"] + s + 1
+    kidx = np.concatenate([c["kidx"], O.index_project(c["K"][n - 1:n], c["P"])])
+    o = np.array([0, n], np.int64)
+    sc = O.score(c["Q"][s], c["P"], kidx, o, c["Hq"], c["Hkv"])
+    if c["vote"]:
+        th = O.theta(sc, o, 9, 10)
+        il, cnt = O.select_vote(O.votes(sc, th, o), o, c["bnum"], c["bden"])
+    else:
+        il, cnt = O.select_per_head(sc, o, c["bnum"], c["bden"])
+    O.decode(c["Q"][s], c["K"][:n], c["V"][:n], o, il, cnt, 0 if c["vote"] else 1, c["Hq"], c["Hkv"])
+    return s
+
+
+def cpu_baseline(x, Kh, Vh, Qh, n0, vote, bnum, bden, nseq):
+    import multiprocessing as mp
+    from oracle import oracle as O
+    O.build()
+    _CPU.update(n0=n0, K=Kh, V=Vh, Q=Qh, P=x.P, Hq=x.Hq, Hkv=x.Hkv, vote=vote, bnum=bnum, bden=bden)
+    _CPU["kidx"] = O.index_project(Kh[:n0], x.P)
+    t0 = time.perf_counter()
+    for s in range(nseq):
+        _oracle_step(s)
+    one = (time.perf_counter() - t0) / nseq
+    procs = max(1, min(os.cpu_count() or 1, 16))
+    ctx = mp.get_context("fork")
+    with ctx.Pool(procs) as pool:
+        t0 = time.perf_counter()
+        pool.map(_oracle_step, [i % len(Qh) for i in range(procs)], chunksize=1)
+        wall = time.perf_counter() - t0
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": round(wall / procs * 1e6, 1), "unit": "us/step", "cores": procs, "kind": "oracle",
+            "single_thread_us_per_step": round(one * 1e6, 1), "cpu_model": model,
+            "sample": f"{procs} whole decode steps of the benchmarked workload (n={n0}+s, fp64 C oracle, one step per "
+                      f"process on {procs} processes at once; value = wall time / steps) after {nseq} steps one "
+                      f"after another in one process (single_thread_us_per_step); {os.cpu_count()} host cores visible"}
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -68,7 +123,7 @@ def parse():
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip dense / warm / graph side measurements")
-    ap.add_argument("--cpu-steps", type=int, default=10)
+    ap.add_argument("--cpu-steps", type=int, default=3, help="oracle steps run one after another")
     ap.add_argument("--reuse-radius", type=int, nargs="+", default=[0, 1],
                     help="neighbour-fetch radii of the selection-reuse side measurement")
     ap.add_argument("--isolate", action="store_true", help="also time each call alone after a flush")
@@ -309,18 +364,25 @@ def main():
     x = synth.config3(args.budget, n0)
     Hq, Hkv = x.Hq, x.Hkv
     cap = n0 + total_steps
-    # cache arrays with room for the decode steps; the new rows are drawn per step
-    K = torch.empty((cap, Hkv, 128), dtype=torch.int16, device=dev)
-    V = torch.empty((cap, Hkv, 128), dtype=torch.int16, device=dev)
-    K[:n0] = torch.from_numpy(x.K.view(np.int16)).to(dev)
-    V[:n0] = torch.from_numpy(x.V.view(np.int16)).to(dev)
+    # host copies of the cache with room for the decode steps (the new rows are drawn per step)
+    Kh = np.empty((cap, Hkv, 128), np.uint16)
+    Vh = np.empty((cap, Hkv, 128), np.uint16)
+    Kh[:n0], Vh[:n0] = x.K, x.V
     qs = []
     for s in range(total_steps):
         q_s, k_new, v_new = synth.config3_step(s + 1, x.q, Hkv)
-        K[n0 + s] = torch.from_numpy(k_new[0].view(np.int16)).to(dev)
-        V[n0 + s] = torch.from_numpy(v_new[0].view(np.int16)).to(dev)
+        Kh[n0 + s], Vh[n0 + s] = k_new[0], v_new[0]
         qs.append(q_s)
-    Q = torch.from_numpy(np.stack(qs).view(np.int16)).to(dev)          # [steps][1][Hq][128]
+    Qh = np.stack(qs)                                                   # [steps][1][Hq][128]
+    cpu = None
+    if not args.no_cpu:
+        print("bench: timing the CPU oracle", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(x, Kh, Vh, Qh, n0, mode == api.MODE_VOTE, bnum, bden, args.cpu_steps)
+        print(f"bench: CPU oracle {cpu['single_thread_us_per_step']} us/step on one thread, {cpu['value']} us/step on "
+              f"{cpu['cores']} processes", file=sys.stderr, flush=True)
+    K = torch.from_numpy(Kh.view(np.int16)).to(dev)
+    V = torch.from_numpy(Vh.view(np.int16)).to(dev)
+    Q = torch.from_numpy(Qh.view(np.int16)).to(dev)
     P = torch.from_numpy(x.P).to(dev)
     kidx = torch.empty((cap, Hkv, 32), dtype=torch.int16, device=dev)
     api.index_append(K[:n0], P, kidx, 0)
@@ -522,6 +584,60 @@ def main():
                 iso[f"{name}{'' if flushed else '_warm'}"] = round(float(np.mean([a.elapsed_time(b2) * 1e3 for a, b2 in evs[2:]])), 2)
         extra["isolated_us"] = iso
     if not args.no_extra:
+        # measured device copy bandwidth: 1 GiB read + 1 GiB written per copy, events around 5 copies
+        csrc = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        cdst = torch.empty_like(csrc)
+        cdst.copy_(csrc)
+        cev = []
+        for _ in range(5):
+            a, b2 = ev(), ev()
+            a.record()
+            cdst.copy_(csrc)
+            b2.record()
+            cev.append((a, b2))
+        torch.cuda.synchronize()
+        copy_us = float(np.median([a.elapsed_time(b2) * 1e3 for a, b2 in cev]))
+        extra["copy_gbps"] = round(2 * (1 << 30) / (copy_us * 1e-6) / 1e9, 1)
+        del csrc, cdst
+        # the two smaller decode configurations (tiny layer at 4K tokens, the 8B-shaped layer at 32K),
+        # the same fused step (ts_score_select with the append, ts_sparse_decode), flushed, 20 steps
+        cfgs = {}
+        for name, xc in (("c1", synth.config1()), ("c2", synth.config2())):
+            nc = int(xc.offsets[-1])
+            oc = api.Offsets(xc.offsets, dev)
+            qc, Kc, Vc = (torch.from_numpy(a.view(np.int16)).to(dev) for a in (xc.q, xc.K, xc.V))
+            Pc = torch.from_numpy(xc.P).to(dev)
+            kic = torch.empty((nc, xc.Hkv, 32), dtype=torch.int16, device=dev)
+            api.index_append(Kc, Pc, kic, 0)
+            pc = api.params(api.MODE_VOTE, xc.budget)
+            kc = api.budget_tokens(nc, pc)
+            wssc = torch.empty(api.score_select_workspace_bytes(oc, xc.Hq, pc), dtype=torch.uint8, device=dev)
+            wsdc = torch.empty(api.decode_workspace_bytes(oc, [kc], xc.Hq, xc.Hkv, api.MODE_VOTE), dtype=torch.uint8,
+                               device=dev)
+            scc = torch.empty((xc.Hq, api.score_stride(oc)), dtype=torch.float32, device=dev)
+            idc = torch.empty(kc + 16, dtype=torch.int32, device=dev)
+            cnc = torch.empty(1, dtype=torch.int64, device=dev)
+            outc = torch.empty((1, xc.Hq, 128), dtype=torch.float32, device=dev)
+            pcr, chc = ctypes.byref(pc), (ctypes.c_int64 * 1)(kc)
+            cevs = []
+            for i in range(25):
+                do_flush()
+                st = stream_of()
+                a, b2 = ev(), ev()
+                a.record()
+                chk(L.ts_score_select(vp(qc), vp(Pc), vp(kic), vp(Kc), vp(oc.dev), oc.host, 1, xc.Hq, xc.Hkv, pcr,
+                                      vp(scc), vp(idc), vp(cnc), None, None, vp(wssc), wssc.numel(), st))
+                chk(L.ts_sparse_decode(vp(qc), vp(Kc), vp(Vc), vp(oc.dev), oc.host, vp(idc), vp(cnc), chc,
+                                       api.MODE_VOTE, 1, xc.Hq, xc.Hkv, vp(outc), vp(wsdc), wsdc.numel(), st))
+                b2.record()
+                cevs.append((a, b2))
+            torch.cuda.synchronize()
+            us = float(np.mean([a.elapsed_time(b2) * 1e3 for a, b2 in cevs[5:]]))
+            byts = nc * xc.Hkv * 64 + kc * xc.Hkv * 512
+            cfgs[name] = {"n": nc, "Hq": xc.Hq, "Hkv": xc.Hkv, "budget": f"{xc.budget[0]}/{xc.budget[1]}",
+                          "us_per_step": round(us, 2), "algorithmic_bytes": int(byts),
+                          "hbm_gbps": round(byts / (us * 1e-6) / 1e9, 1)}
+        extra["configs"] = cfgs
         # dense flash-decode over all n under the same protocol
         n_d = n0
         od = api.Offsets([0, n_d], dev)
@@ -584,7 +700,8 @@ def main():
         ex_valid = torch.empty((1, lists), dtype=torch.int64, device=dev)
         ws_ex = torch.empty(max(api.decode_workspace_bytes(offs[-1], [cap_max], Hq, Hkv, mode), 256), dtype=torch.uint8,
                             device=dev)
-        exp_, capp, valp, wexp = vp(ex_idx), vp(ex_caps), vp(ex_valid), vp(ws_ex)
+        wsx = torch.empty(4096, dtype=torch.uint8, device=dev)      # chunk sums of the expansion
+        exp_, capp, valp, wexp, wsxp = vp(ex_idx), vp(ex_caps), vp(ex_valid), vp(ws_ex), vp(wsx)
         extra["reuse"] = []
         for radius in args.reuse_radius:
             reuse = {"radius": radius, "us_per_step": {}}
@@ -603,7 +720,7 @@ def main():
                                               wss, ws_ss_n, st))
                         kprev = (ctypes.c_int64 * 1)(kb)
                     chk(L.ts_expand_selection(idp, cnp, kprev, od, oh, 1, lists, 4, 256, radius, exp_, capp, valp,
-                                              st))
+                                              wsxp, wsx.numel(), st))
                     cap = api.expand_capacity(kprev[0], n_s, 4, 256, radius)
                     chk(L.ts_sparse_decode(qp, Kp, Vp, od, oh, exp_, capp, (ctypes.c_int64 * 1)(cap), mode, 1, Hq,
                                            Hkv, outp, wexp, ws_ex.numel(), st))
@@ -639,31 +756,6 @@ def main():
                            "algorithmic_gbps": round(snap_bytes / (snap_us * 1e-6) / 1e9, 1)}
         del qo_s, K_s, V_s, ws_s
 
-    cpu = None
-    if not args.no_cpu:
-        from oracle import oracle as O
-        print("bench: timing the CPU oracle", file=sys.stderr, flush=True)
-        Kh, Vh = K[:n0 + args.cpu_steps].cpu().numpy().view(np.uint16), V[:n0 + args.cpu_steps].cpu().numpy().view(np.uint16)
-        kidx_h = O.index_project(Kh[:n0], x.P)
-        qs_h = Q.cpu().numpy().view(np.uint16)
-        t0 = time.perf_counter()
-        for s in range(args.cpu_steps):
-            n = n0 + s + 1
-            kidx_h = np.concatenate([kidx_h, O.index_project(Kh[n - 1:n], x.P)])
-            o = np.array([0, n], np.int64)
-            sc = O.score(qs_h[s], x.P, kidx_h, o, Hq, Hkv)
-            if mode == api.MODE_VOTE:
-                th = O.theta(sc, o, 9, 10)
-                vt = O.votes(sc, th, o)
-                il, cnt = O.select_vote(vt, o, bnum, bden)
-            else:
-                il, cnt = O.select_per_head(sc, o, bnum, bden)
-            O.decode(qs_h[s], Kh, Vh, o, il, cnt, mode, Hq, Hkv)
-        cpu_s = (time.perf_counter() - t0) / args.cpu_steps
-        cpu = {"value": round(cpu_s * 1e6, 1), "unit": "us/step", "cores": 1, "kind": "oracle",
-               "sample": f"{args.cpu_steps} full decode steps of the same workload (n={n0}+s, fp64 C oracle, "
-                         f"single thread, {os.cpu_count()} host cores visible)"}
-
     res = {
         "metric": METRIC,
         "value": round(mean_us, 2),
@@ -693,10 +785,18 @@ def main():
                      "frac": round(dec_gbps / PEAK_GBPS, 4), "traffic": traffic,
                      "kernel": "ts_sparse_decode (decode_partial_kernel + decode_merge_kernel), alone, LLC flushed",
                      "algorithmic_bytes": int(dec_bytes), "avg_us": round(dec_us, 2)},
+        # the whole step (every call of the hot path) against the same peak: the metric's own figure
+        "step_roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_GBPS, "unit": "GB/s",
+                          "frac": round(gbps / PEAK_GBPS, 4), "algorithmic_bytes": int(step_bytes),
+                          "avg_us": round(mean_us, 2)},
         "cpu_baseline": cpu,
         "wall_s_timed_loop": round(wall, 4),
     }
     res.update(extra)
+    if "copy_gbps" in extra:
+        res["roofline"]["measured_copy_gbps"] = extra["copy_gbps"]
+        res["roofline"]["frac_of_measured_copy"] = round(dec_gbps / extra["copy_gbps"], 4)
+        res["step_roofline"]["frac_of_measured_copy"] = round(gbps / extra["copy_gbps"], 4)
     if args.copy_probe:
         src = torch.empty(PROBE_BYTES // 4, dtype=torch.float32, device=dev).fill_(3.0)
         dst = torch.empty_like(src)

@@ -168,6 +168,9 @@ int ts_score_select(const uint16_t* q, const float* P, uint16_t* k_index, const 
  * local); -1 if an argument is out of range. */
 int64_t ts_expand_capacity(int64_t k_prev, int64_t n, int64_t sink, int64_t local, int64_t radius);
 
+/* Workspace for ts_expand_selection (0 if an argument is invalid). */
+size_t ts_expand_workspace_bytes(const int64_t* counts_prev_host, int32_t B, int32_t lists);
+
 /* Selection reuse with neighbour fetch ([TB] "Inferenzstrategie", Optimierungen: the selector
  * runs every N decode steps and the steps in between reuse its selection, widened by the
  * spatial neighbours of the selected tokens; sink and local window are the always-kept buffers).
@@ -184,12 +187,14 @@ int64_t ts_expand_capacity(int64_t k_prev, int64_t n, int64_t sink, int64_t loca
  *   idx_out      device int32 [lists * sum_b cap_b], list l of b at lists*cpre_b + l*cap_b + j
  *                (cpre_b = sum of the earlier capacities)
  *   caps_out     device int64 [B] (receives cap_b: the list lengths to hand to ts_sparse_decode)
- *   valid_out    device int64 [B][lists] (receives the number of entries before the empty slots).
+ *   valid_out    device int64 [B][lists] (receives the number of entries before the empty slots)
+ *   ws           device workspace of at least ts_expand_workspace_bytes(counts_prev_host, B, lists)
+ *                bytes.
  * Pass caps_out and the host capacities as the counts of ts_sparse_decode.                */
 int ts_expand_selection(const int32_t* idx_prev, const int64_t* counts_prev_dev, const int64_t* counts_prev_host,
                         const int64_t* offsets_dev, const int64_t* offsets_host, int32_t B, int32_t lists,
                         int64_t sink, int64_t local, int64_t radius, int32_t* idx_out, int64_t* caps_out,
-                        int64_t* valid_out, hipStream_t stream);
+                        int64_t* valid_out, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Workspace for ts_sparse_decode (counts_host = the per-sequence list lengths) and for
  * ts_dense_decode (counts_host = NULL). */
@@ -272,11 +277,13 @@ int snapkv_compress(const uint16_t* q_obs, const uint16_t* K, const uint16_t* V,
  *   K, V       device bf16 [n][Hkv][128]
  *   idx_out    device int32 [Hkv][cap]
  *   K_out, V_out device bf16 [cap][Hkv][128]
- *   valid_out  device int64 [Hkv] (receives each head's number of entries before the padding).
+ *   valid_out  device int64 [Hkv] (receives each head's number of entries before the padding)
+ *   ws         device workspace of at least snapkv_clusters_workspace_bytes(ce, Hkv) bytes.
  * k_cluster = 0 copies the lists unchanged.                                              */
+size_t snapkv_clusters_workspace_bytes(int64_t ce, int32_t Hkv);
 int snapkv_retain_clusters(const int32_t* idx, int64_t n, int32_t Hkv, int64_t ce, int64_t k_cluster,
                            const uint16_t* K, const uint16_t* V, int32_t* idx_out, uint16_t* K_out,
-                           uint16_t* V_out, int64_t* valid_out, hipStream_t stream);
+                           uint16_t* V_out, int64_t* valid_out, void* ws, size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

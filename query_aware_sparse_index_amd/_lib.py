@@ -29,8 +29,9 @@ SIGNATURES = {
     "ts_score_select": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64p, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
                                        _vp, _sz, _vp]),
     "ts_expand_capacity": (_i64, [_i64, _i64, _i64, _i64, _i64]),
+    "ts_expand_workspace_bytes": (_sz, [_i64p, _i32, _i32]),
     "ts_expand_selection": (ctypes.c_int, [_vp, _vp, _i64p, _vp, _i64p, _i32, _i32, _i64, _i64, _i64, _vp, _vp, _vp,
-                                           _vp]),
+                                           _vp, _sz, _vp]),
     "ts_decode_workspace_bytes": (_sz, [_i64p, _i64p, _i32, _i32, _i32, _i32]),
     "ts_sparse_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64p, _vp, _vp, _i64p, _i32, _i32, _i32, _i32, _vp,
                                         _vp, _sz, _vp]),
@@ -40,7 +41,9 @@ SIGNATURES = {
     "snapkv_workspace_bytes": (_sz, [_i64, _i32, _i32, _i32, _i64]),
     "snapkv_compress": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _i32, _vp, _vp, _vp, _vp, _vp,
                                        _vp, _sz, _vp]),
-    "snapkv_retain_clusters": (ctypes.c_int, [_vp, _i64, _i32, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "snapkv_clusters_workspace_bytes": (_sz, [_i64, _i32]),
+    "snapkv_retain_clusters": (ctypes.c_int, [_vp, _i64, _i32, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
+                                              _vp]),
 }
 
 

@@ -169,7 +169,7 @@ def expand_capacity(k_prev: int, n: int, sink=4, local=256, radius=1) -> int:
 
 
 def expand_selection(idx_prev, counts_prev_dev, counts_prev_host, offs: Offsets, lists: int = 1, sink=4, local=256,
-                     radius=1, out=None, caps=None, valid=None):
+                     radius=1, out=None, caps=None, valid=None, ws=None):
     """ts_expand_selection: the previous lists widened by +-radius plus the current forced tokens,
     padded with -1 to their capacities.  Returns a dict with "idx", "caps" (device), "caps_host",
     "valid" (device [B][lists])."""
@@ -182,9 +182,13 @@ def expand_selection(idx_prev, counts_prev_dev, counts_prev_host, offs: Offsets,
         caps = torch.empty(offs.B, dtype=torch.int64, device=dev)
     if valid is None:
         valid = torch.empty((offs.B, lists), dtype=torch.int64, device=dev)
-    _check(_lib.load().ts_expand_selection(_p(idx_prev), _p(counts_prev_dev), _host_i64(counts_prev_host),
-                                           _p(offs.dev), offs.host, offs.B, int(lists), int(sink), int(local),
-                                           int(radius), _p(out), _p(caps), _p(valid), _stream()))
+    ch = _host_i64(counts_prev_host)
+    need = int(_lib.load().ts_expand_workspace_bytes(ch, offs.B, int(lists)))
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _check(_lib.load().ts_expand_selection(_p(idx_prev), _p(counts_prev_dev), ch, _p(offs.dev), offs.host, offs.B,
+                                           int(lists), int(sink), int(local), int(radius), _p(out), _p(caps),
+                                           _p(valid), _p(ws), ws.numel(), _stream()))
     return {"idx": out[:lists * sum(caps_host)], "caps": caps, "caps_host": caps_host, "valid": valid}
 
 
@@ -276,6 +280,8 @@ def snapkv_retain_clusters(idx, K, V, k_cluster: int = 1):
     Ko = torch.empty((max(cap, 1), Hkv, 128), dtype=K.dtype, device=dev)
     Vo = torch.empty((max(cap, 1), Hkv, 128), dtype=V.dtype, device=dev)
     valid = torch.empty(Hkv, dtype=torch.int64, device=dev)
+    need = int(_lib.load().snapkv_clusters_workspace_bytes(int(ce), int(Hkv)))
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     _check(_lib.load().snapkv_retain_clusters(_p(idx), int(n), int(Hkv), int(ce), int(k_cluster), _p(K), _p(V),
-                                              _p(io), _p(Ko), _p(Vo), _p(valid), _stream()))
+                                              _p(io), _p(Ko), _p(Vo), _p(valid), _p(ws), ws.numel(), _stream()))
     return {"idx": io[:, :cap], "K": Ko[:cap], "V": Vo[:cap], "valid": valid}

@@ -217,10 +217,17 @@ int64_t ts_expand_capacity(int64_t k_prev, int64_t n, int64_t sink, int64_t loca
     return qasi::expand_capacity(k_prev, n, sink, local, radius);
 }
 
+size_t ts_expand_workspace_bytes(const int64_t* counts_prev_host, int32_t B, int32_t lists) {
+    if (!counts_prev_host || B <= 0 || lists < 1 || lists > 64) return 0;
+    for (int b = 0; b < B; ++b)
+        if (counts_prev_host[b] < 0) return 0;
+    return (size_t)qasi::expand_blocks(counts_prev_host, B, lists) * sizeof(uint32_t);
+}
+
 int ts_expand_selection(const int32_t* idx_prev, const int64_t* counts_prev_dev, const int64_t* counts_prev_host,
                         const int64_t* offsets_dev, const int64_t* offsets_host, int32_t B, int32_t lists,
                         int64_t sink, int64_t local, int64_t radius, int32_t* idx_out, int64_t* caps_out,
-                        int64_t* valid_out, hipStream_t stream) {
+                        int64_t* valid_out, void* ws, size_t ws_bytes, hipStream_t stream) {
     if (!idx_prev || (reinterpret_cast<uintptr_t>(idx_prev) & 3u) || !idx_out || (reinterpret_cast<uintptr_t>(idx_out) & 3u))
         return fail(QASI_ERR_INVALID, "idx_prev and idx_out must be non-null and 4-byte aligned");
     if (!counts_prev_dev || !counts_prev_host || (reinterpret_cast<uintptr_t>(counts_prev_dev) & 7u))
@@ -238,9 +245,13 @@ int ts_expand_selection(const int32_t* idx_prev, const int64_t* counts_prev_dev,
             return fail(QASI_ERR_INVALID, "counts_prev[%d]=%lld outside [0, n_b=%lld]", b, (long long)counts_prev_host[b],
                         (long long)n);
     }
+    if (!ws || (reinterpret_cast<uintptr_t>(ws) & 3u)) return fail(QASI_ERR_INVALID, "ws must be non-null and aligned");
+    const size_t need = (size_t)qasi::expand_blocks(counts_prev_host, B, lists) * sizeof(uint32_t);
+    if (ws_bytes < need) return fail(QASI_ERR_WORKSPACE, "ts_expand_selection needs %zu workspace bytes, got %zu", need, ws_bytes);
     if (int r = init_once()) return r;
     return hip_status(qasi::launch_expand(idx_prev, counts_prev_dev, counts_prev_host, offsets_dev, offsets_host, B,
-                                          lists, sink, local, radius, idx_out, caps_out, valid_out, stream),
+                                          lists, sink, local, radius, idx_out, caps_out, valid_out,
+                                          static_cast<uint32_t*>(ws), stream),
                       "ts_expand_selection launch");
 }
 
@@ -347,9 +358,15 @@ int snapkv_compress(const uint16_t* q_obs, const uint16_t* K, const uint16_t* V,
                       "snapkv_compress launch");
 }
 
+size_t snapkv_clusters_workspace_bytes(int64_t ce, int32_t Hkv) {
+    if (ce < 0 || Hkv <= 0 || Hkv > 64) return 0;
+    const int64_t c[1] = {ce};
+    return (size_t)qasi::expand_blocks(c, 1, Hkv) * sizeof(uint32_t);
+}
+
 int snapkv_retain_clusters(const int32_t* idx, int64_t n, int32_t Hkv, int64_t ce, int64_t k_cluster, const uint16_t* K,
                            const uint16_t* V, int32_t* idx_out, uint16_t* K_out, uint16_t* V_out, int64_t* valid_out,
-                           hipStream_t stream) {
+                           void* ws, size_t ws_bytes, hipStream_t stream) {
     if (!idx || (reinterpret_cast<uintptr_t>(idx) & 3u) || !idx_out || (reinterpret_cast<uintptr_t>(idx_out) & 3u))
         return fail(QASI_ERR_INVALID, "idx and idx_out must be non-null and 4-byte aligned");
     if (!aligned16(K) || !aligned16(V) || !aligned16(K_out) || !aligned16(V_out))
@@ -361,9 +378,14 @@ int snapkv_retain_clusters(const int32_t* idx, int64_t n, int32_t Hkv, int64_t c
     if (ce < 0 || ce > n) return fail(QASI_ERR_INVALID, "ce=%lld outside [0, n]", (long long)ce);
     if (k_cluster < 0 || k_cluster > (1 << 20))
         return fail(QASI_ERR_INVALID, "k_cluster=%lld outside [0, 2^20]", (long long)k_cluster);
+    if (!ws || (reinterpret_cast<uintptr_t>(ws) & 3u)) return fail(QASI_ERR_INVALID, "ws must be non-null and aligned");
+    const int64_t c[1] = {ce};
+    const size_t need = (size_t)qasi::expand_blocks(c, 1, Hkv) * sizeof(uint32_t);
+    if (ws_bytes < need)
+        return fail(QASI_ERR_WORKSPACE, "snapkv_retain_clusters needs %zu workspace bytes, got %zu", need, ws_bytes);
     if (int r = init_once()) return r;
     return hip_status(qasi::launch_snapkv_clusters(idx, n, Hkv, ce, k_cluster, K, V, idx_out, K_out, V_out, valid_out,
-                                                   stream),
+                                                   static_cast<uint32_t*>(ws), stream),
                       "snapkv_retain_clusters launch");
 }
 

@@ -78,10 +78,12 @@ hipError_t launch_rows_topk(const float* vals, int64_t stride, int rows, int64_t
 
 // ---- selection reuse with neighbour fetch
 int64_t expand_capacity(int64_t k_prev, int64_t n, int64_t sink, int64_t local, int64_t radius);
+// blocks of the two expansion kernels (one u32 of workspace each)
+int64_t expand_blocks(const int64_t* counts_prev_host, int B, int L);
 hipError_t launch_expand(const int32_t* prev, const int64_t* counts_prev_dev, const int64_t* counts_prev_host,
                          const int64_t* offsets_dev, const int64_t* offsets_host, int B, int L, int64_t sink,
                          int64_t local, int64_t radius, int32_t* out, int64_t* caps_out, int64_t* valid_out,
-                         hipStream_t stream);
+                         uint32_t* chunk_counts, hipStream_t stream);
 
 // ---- decode
 size_t decode_workspace(const int64_t* offsets_host, const int64_t* counts_host, int B, int Hq, int Hkv, int mode);
@@ -110,7 +112,7 @@ hipError_t launch_snapkv(const uint16_t* q_obs, const uint16_t* K, const uint16_
 // SnapKV cluster-based retention: the top-c lists widened by +-k_cluster, rows gathered
 hipError_t launch_snapkv_clusters(const int32_t* idx, int64_t n, int Hkv, int64_t ce, int64_t k_cluster,
                                   const uint16_t* K, const uint16_t* V, int32_t* idx_out, uint16_t* K_out,
-                                  uint16_t* V_out, int64_t* valid_out, hipStream_t stream);
+                                  uint16_t* V_out, int64_t* valid_out, uint32_t* chunk_counts, hipStream_t stream);
 
 // One-time per-process set-up (kernel attributes); returns the first error.
 hipError_t init_kernels();

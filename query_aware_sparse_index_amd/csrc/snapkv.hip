@@ -330,12 +330,12 @@ __global__ void snap_gather_padded_kernel(const uint16_t* __restrict__ K, const 
 
 hipError_t launch_snapkv_clusters(const int32_t* idx, int64_t n, int Hkv, int64_t ce, int64_t k_cluster,
                                   const uint16_t* K, const uint16_t* V, int32_t* idx_out, uint16_t* K_out,
-                                  uint16_t* V_out, int64_t* valid_out, hipStream_t stream) {
+                                  uint16_t* V_out, int64_t* valid_out, uint32_t* chunk_counts, hipStream_t stream) {
     // one sequence {0, n} with Hkv lists of ce entries: the bounds travel as launch arguments
     const int64_t offs[2] = {0, n};
     const int64_t cnt[1] = {ce};
     hipError_t e = launch_expand(idx, nullptr, cnt, nullptr, offs, 1, Hkv, 0, 0, k_cluster, idx_out, nullptr,
-                                 valid_out, stream);
+                                 valid_out, chunk_counts, stream);
     if (e != hipSuccess) return e;
     const int64_t cap = expand_capacity(ce, n, 0, 0, k_cluster);
     const int64_t pieces = cap * Hkv * 16;

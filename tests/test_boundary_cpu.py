@@ -22,7 +22,7 @@ def header_functions():
 def test_exports_match_header():
     lib = _lib.load()
     names = header_functions()
-    assert len(names) == 19, names
+    assert len(names) == 21, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.SIGNATURES)

@@ -85,3 +85,15 @@ def test_reuse_after_steps():
         r = _expand_and_check(st.q, K, V, x_now, offs_now, st.sel["idx"], st.sel["counts_host"], api.MODE_VOTE,
                               32, 8, 1)
         print("reuse after", g, "steps", r)
+
+
+def test_expand_empty_previous_list():
+    """A previous list with no entries keeps only the current forced tokens (no entry is read)."""
+    x = synth.make_decode(8, [3000, 2000], 8, 2, 4, False, (1, 5), 0)
+    offs = api.Offsets(x.offsets, dev())
+    prev = torch.zeros(4, dtype=torch.int32, device=dev())
+    cp = torch.zeros(2, dtype=torch.int64, device=dev())
+    ex = api.expand_selection(prev, cp, [0, 0], offs, 1, 4, 256, 2)
+    torch.cuda.synchronize()
+    ref, cnt, caps = O.expand_selection(np.zeros(0, np.int32), [0, 0], x.offsets, 1, 4, 256, 2)
+    assert np.array_equal(ex["idx"].cpu().numpy(), ref) and np.array_equal(ex["valid"].cpu().numpy(), cnt)
