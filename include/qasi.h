@@ -154,10 +154,12 @@ size_t ts_score_select_workspace_bytes(const int64_t* offsets_host, int32_t B, i
  *   p, idx_out, count_out, theta_out, votes_out: as for ts_select
  *   scores    device fp32 [Hq][S] (written, S = ts_score_stride)
  *   ws        device workspace of at least ts_score_select_workspace_bytes(...) bytes.
- * Each head's order statistic is found from a key bracket taken from 2048 sampled index
- * scores: the score pass counts, per 64-token tile, the keys below the bracket and keeps the
- * keys inside it, and one block per (sequence, head) ranks those; when the target rank falls
- * outside the bracket the whole row is radix-selected instead (same result).              */
+ * Each head's order statistic is found from a key bracket taken from 1024 sampled index
+ * scores (rows of more than 16384 candidate keys; shorter rows are ranked whole): the score pass
+ * counts, per 64-token tile, the keys below the bracket and keeps the keys inside it; blocks of
+ * up to 512 tiles histogram those keys and the last of them to finish ranks the answer's digit.
+ * When the target rank falls outside the bracket the whole row is radix-selected instead (same
+ * result).                                                                                    */
 int ts_score_select(const uint16_t* q, const float* P, uint16_t* k_index, const uint16_t* K_last,
                     const int64_t* offsets_dev, const int64_t* offsets_host, int32_t B, int32_t Hq,
                     int32_t Hkv, const ts_select_params* p, float* scores, int32_t* idx_out,

@@ -174,7 +174,8 @@ __device__ __forceinline__ void quad_transpose_sum(float (&v)[G], int part) {
 //                    order), so that one head's keys of consecutive tiles are contiguous;
 //   tcand[tile * kClsTile + offset + j - kClsSlots], kClsSlots <= j < inside: the rest (rare), the
 //                    heads' runs packed one after the other in the order they reserve them.
-// Inactive instances write zero records.  The bracket comes from state[(b * Hq + h) * 8 + ...].
+// Inactive instances, and those without a bracket (lo > hi: rows short enough to be ranked whole),
+// write zero records.  The bracket comes from state[(b * Hq + h) * 8 + ...].
 struct ClsArgs {
     const int64_t* state;
     uint32_t* tinfo;
@@ -293,8 +294,8 @@ __global__ __launch_bounds__(score_threads<HKV>()) void score_kernel(const float
             below[i] = 0;
             key[i] = 0;
             mm[i] = 0;
-            if (h < Hq && c_flag[i] == 0) {              // an active order statistic
-                const uint32_t lo = (uint32_t)c_lo[i], hi = (uint32_t)c_hi[i];
+            const uint32_t lo = (uint32_t)c_lo[i], hi = (uint32_t)c_hi[i];
+            if (h < Hq && c_flag[i] == 0 && lo <= hi) {  // an active order statistic with a bracket
                 const int64_t t = t0 + lane;
                 const bool valid = lane < len && t >= c_beg[i] && t < c_end[i];
                 key[i] = order_key(tile[h * kTileLd + lane]);

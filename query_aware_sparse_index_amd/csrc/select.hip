@@ -703,7 +703,9 @@ __global__ __launch_bounds__(kPrepThreads) void prep_kernel(const uint16_t* __re
         qp[(int64_t)inst * kDP + t] = acc;
     }
     __syncthreads();
-    uint32_t klo = 0u, khi = 0xffffffffu;
+    // no sample (rows of at most kCap keys): the empty bracket lo > hi, so that the score kernel
+    // classifies nothing and th_final2 ranks the row itself
+    uint32_t klo = 1u, khi = 0u;
     if (sampled) {
         float qr[8];
 #pragma unroll
@@ -1093,13 +1095,15 @@ __global__ __launch_bounds__(kPhWaves * 64) void ph_compact_kernel(const float* 
 //      in-bracket keys (head-major slots, when the sequence fits one round) and sums the counts
 //      below and inside the bracket; the target rank r lies inside when
 //      #below < r <= #below + #inside;
-//   2. stages the in-bracket keys in LDS while counting them per top digit (kDigit bits of
-//      key - lo), finds the answer's digit and ranks that digit's keys (one wave when there are
-//      at most 64, else a radix select);
-// a rank outside the bracket, keys that do not fit in LDS or a sequence of more than one round
-// take the out-of-line paths: an LDS histogram of the digits over the keys in memory, or a radix
-// select over the instance's whole score row (same result).  The state gets the answer's key and
-// the number of keys above it, as th_final_kernel leaves them.
+//   2. counts the in-bracket keys per top digit (kDigit bits of key - lo) in LDS, straight from
+//      the registers (the rare keys past a tile's slots are read into LDS first), finds the
+//      answer's digit and ranks that digit's keys, picked from the registers again (one wave when
+//      there are at most 64, else a radix select).
+// A row of at most kCap keys has no bracket and is ranked from the score row itself
+// (f2_short_row_rank).  A rank outside the bracket, more overflow keys than LDS holds or a
+// sequence of more than one round take the out-of-line paths: an LDS histogram of the digits
+// over the keys in memory, or a radix select over the instance's whole score row (same result).
+// The state gets the answer's key and the number of keys above it, as th_final_kernel leaves them.
 constexpr int kF2Threads = 512;
 constexpr int kF2Per = 5;                                  // consecutive tiles per thread per round
 constexpr int kF2Round = kF2Threads * kF2Per;              // tiles per round (163840 tokens)
@@ -1169,18 +1173,15 @@ __device__ __forceinline__ void f2_find_digit(const uint32_t* hist, int64_t rr, 
     __syncthreads();
 }
 
-// Rank rr (1-based) of the low dsh bits among the keys x that visit(f) hands over with
-// (x >> dsh) == D; *gt gets the keys above it.  At most 64 keys: one wave ranks them from `xd`.
+// Rank rr (1-based) among the nD keys (values below 2^nbits) that visit(f) hands over;
+// *gt gets the keys above it.  At most 64 keys: one wave ranks them from `xd`; else a radix select.
 template <class Visit>
-__device__ __forceinline__ uint32_t f2_rank_in_digit(Visit visit, int nD, uint32_t D, int dsh, int64_t rr,
-                                                     uint32_t* xd, uint32_t* cursor, uint32_t* hist, int* tmp,
-                                                     int64_t* sh, int64_t* gt) {
+__device__ __forceinline__ uint32_t f2_rank_keys(Visit visit, int nD, int nbits, int64_t rr, uint32_t* xd,
+                                                 uint32_t* cursor, uint32_t* hist, int* tmp, int64_t* sh,
+                                                 int64_t* gt) {
     const int t = threadIdx.x;
-    const uint32_t low = dsh ? ((1u << dsh) - 1u) : 0u;
     if (nD <= 64) {
-        visit([&](uint32_t x) {
-            if ((x >> dsh) == D) xd[atomicAdd(cursor, 1u)] = x & low;
-        });
+        visit([&](uint32_t x) { xd[atomicAdd(cursor, 1u)] = x; });
         __syncthreads();
         if (t < 64) {
             const bool has = t < nD;
@@ -1201,15 +1202,128 @@ __device__ __forceinline__ uint32_t f2_rank_in_digit(Visit visit, int nD, uint32
         return (uint32_t)sh[0];
     }
     int64_t gin = 0;
+    const uint32_t xl = radix_rank<kF2Threads>(visit, nbits, rr, hist, tmp, sh, &gin);
+    *gt += gin;
+    return xl;
+}
+
+// Rank rr (1-based) among the nD keys src[0 .. nD) in LDS (values below 2^nbits); *gt gets the
+// keys above it.  At most 64 keys: one wave ranks them; else a radix select.
+__device__ __forceinline__ uint32_t f2_rank_lds(const uint32_t* src, int nD, int nbits, int64_t rr, uint32_t* hist,
+                                                int* tmp, int64_t* sh, int64_t* gt) {
+    const int t = threadIdx.x;
+    if (nD <= 64) {
+        if (t < 64) {
+            const bool has = t < nD;
+            const uint32_t x = has ? src[t] : 0xffffffffu;
+            int less = 0, leq = 0;
+            for (int j = 0; j < nD; ++j) {
+                const uint32_t y = __shfl(x, j, 64);
+                less += y < x ? 1 : 0;
+                leq += y <= x ? 1 : 0;
+            }
+            if (has && less < rr && rr <= leq) {       // the answer x: #{< x} < rr <= #{<= x}
+                sh[0] = x;
+                sh[1] = nD - leq;
+            }
+        }
+        __syncthreads();
+        *gt += sh[1];
+        return (uint32_t)sh[0];
+    }
+    int64_t gin = 0;
     const uint32_t xl = radix_rank<kF2Threads>(
+        [&](auto f) {
+            for (int i = t; i < nD; i += kF2Threads) f(src[i]);
+        },
+        nbits, rr, hist, tmp, sh, &gin);
+    *gt += gin;
+    return xl;
+}
+
+// Rank rr of the low dsh bits among the keys x that visit(f) hands over with (x >> dsh) == D.
+template <class Visit>
+__device__ __forceinline__ uint32_t f2_rank_in_digit(Visit visit, int nD, uint32_t D, int dsh, int64_t rr,
+                                                     uint32_t* xd, uint32_t* cursor, uint32_t* hist, int* tmp,
+                                                     int64_t* sh, int64_t* gt) {
+    const uint32_t low = dsh ? ((1u << dsh) - 1u) : 0u;
+    return f2_rank_keys(
         [&](auto f) {
             visit([&](uint32_t x) {
                 if ((x >> dsh) == D) f(x & low);
             });
         },
-        dsh, rr, hist, tmp, sh, &gin);
-    *gt += gin;
-    return xl;
+        nD, dsh, rr, xd, cursor, hist, tmp, sh, gt);
+}
+
+// The rank-r key (1-based) of a row of at most kCap keys over [beg, end) (rows prep leaves without
+// a bracket), the row read once, coalesced, into registers.  The keys are counted in kDigitBins
+// equal-width bins of the value range [vmin, vmax]: bin(v) = floor((v - vmin) * kDigitBins /
+// (vmax - vmin)), clamped, is non-decreasing in v whatever the fp32 rounding, so every key of a
+// lower bin is smaller, and the bins spread the keys evenly where the scores are dense (the top
+// bits of the order keys would put a quarter of an octave, hundreds of keys, in one bin).  The
+// answer's bin is found from the counts and its keys are ranked exactly.  *gt gets the number of
+// keys above the answer.
+__device__ __forceinline__ uint32_t f2_short_row_rank(const float* row, int64_t beg, int64_t m, int64_t r,
+                                                      uint32_t* hist, float* red, uint32_t* xd, uint32_t* cursor,
+                                                      int* tmp, int64_t* sh, int64_t* gt) {
+    constexpr int KPT = kCap / kF2Threads;
+    constexpr int NW = kF2Threads / 64;
+    const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
+    // slot u of every thread holds key t + u kF2Threads; slots u >= nu (uniform) are not used
+    const int nu = (int)((m + kF2Threads - 1) / kF2Threads);
+    float v[KPT];
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+        const int64_t i = t + (int64_t)u * kF2Threads;
+        v[u] = u < nu ? row[beg + (i < m ? i : 0)] : 0.f;   // past the end: the first value again
+    }
+    float mn = v[0], mx = v[0];
+#pragma unroll
+    for (int u = 1; u < KPT; ++u)
+        if (u < nu) {
+            mn = fminf(mn, v[u]);
+            mx = fmaxf(mx, v[u]);
+        }
+    for (int o = 32; o > 0; o >>= 1) {
+        mn = fminf(mn, __shfl_xor(mn, o, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    }
+    for (int i = t; i < kDigitBins; i += kF2Threads) hist[i] = 0;
+    if (lane == 0) {
+        red[wid] = mn;
+        red[NW + wid] = mx;
+    }
+    __syncthreads();
+    float vmin = red[0], vmax = red[NW];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+        vmin = fminf(vmin, red[w]);
+        vmax = fmaxf(vmax, red[NW + w]);
+    }
+    const float span = vmax - vmin;
+    const float scale = (span > 0.f && span < INFINITY) ? (float)kDigitBins / span : 0.f;
+    auto bin_of = [&](float x) {
+        const float f = (x - vmin) * scale;
+        return f >= (float)(kDigitBins - 1) ? kDigitBins - 1 : (int)f;
+    };
+#pragma unroll
+    for (int u = 0; u < KPT; ++u)
+        if (u < nu && t + (int64_t)u * kF2Threads < m) atomicAdd(&hist[bin_of(v[u])], 1u);
+    __syncthreads();
+    f2_find_digit(hist, r, tmp, sh);
+    const int D = (int)sh[0];
+    const int64_t rr = r - sh[1];
+    const int nD = (int)sh[3];
+    *gt = sh[2];
+    __syncthreads();
+    return f2_rank_keys(
+        [&](auto f) {
+#pragma unroll
+            for (int u = 0; u < KPT; ++u)
+                if (u < nu && t + (int64_t)u * kF2Threads < m && bin_of(v[u]) == D) f(order_key(v[u]));
+        },
+        nD, 32, rr, xd, cursor, hist, tmp, sh, gt);
 }
 
 // Rank rr0 among the in-bracket keys [klo, khi] read from memory (keys that do not fit in LDS,
@@ -1257,28 +1371,43 @@ __global__ __launch_bounds__(kF2Threads) void th_final2_kernel(const float* __re
                                                               int64_t* __restrict__ state,
                                                               float* __restrict__ theta_out) {
     __shared__ uint32_t xs[kF2Cap];
-    __shared__ uint32_t hist[kDigitBins];
+    __shared__ uint32_t hist[kDigitBins + 64];              // the digits, then one spare bin per lane
     __shared__ uint32_t xd[64];
     __shared__ int tmp[kF2Threads / 64];
     __shared__ int tmp3[3][kF2Threads / 64];
     __shared__ int64_t sh[4];
     __shared__ uint32_t cursor;
-    const int inst = blockIdx.x, b = inst / Hq, h = inst % Hq, t = threadIdx.x;
+    const int inst = blockIdx.x, b = inst / Hq, h = inst % Hq, t = threadIdx.x, lane = t & 63;
     int64_t* st = state + (int64_t)inst * 8;
     const int64_t off = offsets[b], n = offsets[b + 1] - off;
     const OsInst oi = os_instance(n, cfg);
+    const int64_t m = oi.end - oi.beg;
+    const bool active = oi.flag == kFlagActive;
+    if (t == 0) cursor = 0;
+    if (!active || m <= kCap) {
+        // ---- no order statistic, or a row prep leaves without a bracket: ranked from the row itself
+        int64_t gt = 0;
+        uint32_t key = 0;
+        if (active)
+            key = f2_short_row_rank(scores + (int64_t)h * S + off, oi.beg, m, oi.rank, hist,
+                                    reinterpret_cast<float*>(tmp3), xd, &cursor, tmp, sh, &gt);
+        if (t == 0) {
+            st[kStKey] = key;
+            st[kStGt] = gt;
+            if (cfg.mode == 0 && theta_out) theta_out[inst] = active ? key_to_float(key) : 0.f;
+        }
+        return;
+    }
     const uint32_t klo = (uint32_t)st[kStLo], khi = (uint32_t)st[kStHi];
     const int64_t tf = wave_prefix_seq(b, [od = offsets.dev](int i) { return (od[i + 1] - od[i] + 63) / 64; });
-    const int64_t nt = (n + 63) / 64, m = oi.end - oi.beg;
+    const int64_t nt = (n + 63) / 64;
     const size_t hrow = (size_t)h * a.ntiles + tf;
     const uint32_t* inf_h = a.tinfo + hrow;
     const uint32_t* cand_h = a.cand + hrow * kClsSlots;
     const uint32_t* over = a.tcand + (size_t)tf * kClsTile;      // overflow keys of the sequence's tiles
-    const bool active = oi.flag == kFlagActive;
     const bool one = nt <= kF2Round;                   // one round: the keys load with the records
     const int dsh = top_shift(khi - klo);
-    for (int i = t; i < kDigitBins; i += kF2Threads) hist[i] = 0;
-    if (t == 0) cursor = 0;
+    for (int i = t; i < kDigitBins + 64; i += kF2Threads) hist[i] = 0;
 
     // ---- 1. records, first keys and counts: one memory round trip (tiles past nt read tile 0's
     // records, in bounds, and count nothing)
@@ -1301,14 +1430,15 @@ __global__ __launch_bounds__(kF2Threads) void th_final2_kernel(const float* __re
             }
         }
     }
-    int lsum = 0, c0 = 0;
+    int lsum = 0, csum = 0, ov0 = 0;
 #pragma unroll
     for (int u = 0; u < kF2Per; ++u) {
         if ((int64_t)kF2Per * t + u >= nt) w[u] = 0;
+        const int c = (int)((w[u] >> 8) & 0xffu);
         lsum += (int)(w[u] & 0xffu);
-        c0 += (int)((w[u] >> 8) & 0xffu);
+        csum += c;
+        ov0 += c > kClsSlots ? c - kClsSlots : 0;
     }
-    int csum = c0;
     for (int64_t r0 = kF2Round; r0 < nt; r0 += kF2Round)
 #pragma unroll
         for (int u = 0; u < kF2Per; ++u) {
@@ -1317,69 +1447,96 @@ __global__ __launch_bounds__(kF2Threads) void th_final2_kernel(const float* __re
             lsum += (int)(x & 0xffu);
             csum += (int)((x >> 8) & 0xffu);
         }
-    int nlo = 0, nmid = 0, ctot0 = 0;
-    const int cinc0 = block_inclusive_scan3<kF2Threads>(lsum, csum, c0, tmp3, &nlo, &nmid, &ctot0);
+    int nlo = 0, nmid = 0, novf = 0;
+    const int oinc = block_inclusive_scan3<kF2Threads>(lsum, csum, ov0, tmp3, &nlo, &nmid, &novf);
     const int64_t r = oi.rank;
-    bool whole_row = active && !(nlo < r && r <= (int64_t)nlo + nmid);
+    bool whole_row = !(nlo < r && r <= (int64_t)nlo + nmid);
     uint32_t key = 0;
     int64_t gt = 0;
-    if (active && !whole_row) {
+    if (!whole_row) {
         gt = m - nlo - nmid;                              // keys above the bracket
         const int64_t rr0 = r - nlo;
         if (klo == khi) {
             key = klo;                                    // every in-bracket key is the answer
-        } else if (one && nmid <= kF2Cap) {
-            // ---- 2. every in-bracket key into LDS (as key - lo), counted per top digit
-            int base = cinc0 - c0;
-#pragma unroll
-            for (int u = 0; u < kF2Per; ++u) {
-                const int cnt = (int)((w[u] >> 8) & 0xffu);
-#pragma unroll
-                for (int j = 0; j < kClsSlots; ++j)
-                    if (j < cnt) {
-                        const uint32_t x = kv[u][j] - klo;
-                        xs[base + j] = x;
-                        atomicAdd(&hist[x >> dsh], 1u);
-                    }
-                // rare: more than kClsSlots keys, read in batches of 8 loads in flight
-                const uint32_t* ov = over + (size_t)((int64_t)kF2Per * t + u) * kClsTile + (w[u] >> 16) - kClsSlots;
-                for (int j0 = kClsSlots; j0 < cnt; j0 += 8) {
-                    uint32_t x8[8];
-#pragma unroll
-                    for (int v = 0; v < 8; ++v) x8[v] = ov[j0 + v < cnt ? j0 + v : j0];
-#pragma unroll
-                    for (int v = 0; v < 8; ++v)
-                        if (j0 + v < cnt) {
-                            const uint32_t x = x8[v] - klo;
-                            xs[base + j0 + v] = x;
-                            atomicAdd(&hist[x >> dsh], 1u);
-                        }
-                }
-                base += cnt;
-            }
-            __syncthreads();
-            f2_find_digit(hist, rr0, tmp, sh);
-            const uint32_t D = (uint32_t)sh[0];
-            const int64_t rr = rr0 - sh[1];
-            const int nD = (int)sh[3];
-            gt += sh[2];
-            __syncthreads();
-            const uint32_t xl = f2_rank_in_digit(
-                [&](auto f) {
-                    for (int i = t; i < nmid; i += kF2Threads) f(xs[i]);
-                },
-                nD, D, dsh, rr, xd, &cursor, hist, tmp, sh, &gt);
-            key = klo + ((D << dsh) | xl);
         } else {
-            // ---- 2'. keys that do not fit in LDS, or more than one round: from memory
-            uint32_t kd = 0;
-            int64_t gd = 0;
-            __syncthreads();
-            if (f2_rank_digit(inf_h, cand_h, over, nt, klo, khi, rr0, xs, xd, hist, tmp, sh, &cursor, &kd, &gd)) {
-                key = kd;
-                gt += gd;
-            } else {
-                whole_row = true;
+            // in LDS when one round holds the sequence and the overflow keys fit; else from memory
+            bool from_mem = !(one && novf <= kF2Cap);
+            if (!from_mem) {
+                // ---- 2. the keys past the tiles' slots (rare) into LDS, batches of 8 loads in
+                // flight, counted per digit as they arrive; the slots' keys counted from the
+                // registers (a key past the tile's count goes to the lane's spare bin, so every
+                // atomic is unconditional)
+                int base = oinc - ov0;
+#pragma unroll
+                for (int u = 0; u < kF2Per; ++u) {
+                    const int cnt = (int)((w[u] >> 8) & 0xffu);
+                    const uint32_t* ov = over + (size_t)((int64_t)kF2Per * t + u) * kClsTile + (w[u] >> 16);
+                    for (int j0 = kClsSlots; j0 < cnt; j0 += 8) {
+                        uint32_t x8[8];
+#pragma unroll
+                        for (int v = 0; v < 8; ++v) x8[v] = ov[(j0 + v < cnt ? j0 + v : j0) - kClsSlots];
+#pragma unroll
+                        for (int v = 0; v < 8; ++v)
+                            if (j0 + v < cnt) {
+                                const uint32_t x = x8[v] - klo;
+                                xs[base + j0 + v - kClsSlots] = x;
+                                atomicAdd(&hist[x >> dsh], 1u);
+                            }
+                    }
+                    base += cnt > kClsSlots ? cnt - kClsSlots : 0;
+                }
+#pragma unroll
+                for (int u = 0; u < kF2Per; ++u) {
+                    const int cnt = (int)((w[u] >> 8) & 0xffu);
+#pragma unroll
+                    for (int j = 0; j < kClsSlots; ++j)
+                        atomicAdd(&hist[j < cnt ? (kv[u][j] - klo) >> dsh : (uint32_t)(kDigitBins + lane)], 1u);
+                }
+                __syncthreads();
+                f2_find_digit(hist, rr0, tmp, sh);
+                const uint32_t D = (uint32_t)sh[0];
+                const int64_t rr = rr0 - sh[1];
+                const int nD = (int)sh[3];
+                const int64_t gt_d = sh[2];
+                __syncthreads();
+                if (nD > 64 && novf + nD > kF2Cap) {
+                    from_mem = true;                      // the digit does not fit beside the overflow keys
+                } else {
+                    // the digit's keys (low bits) into LDS: xd for at most 64, else after the
+                    // overflow keys; then ranked there
+                    const uint32_t low = dsh ? ((1u << dsh) - 1u) : 0u;
+                    uint32_t* dst = nD <= 64 ? xd : xs + novf;
+#pragma unroll
+                    for (int u = 0; u < kF2Per; ++u) {
+                        const int cnt = (int)((w[u] >> 8) & 0xffu);
+#pragma unroll
+                        for (int j = 0; j < kClsSlots; ++j) {
+                            const uint32_t x = kv[u][j] - klo;
+                            if (j < cnt && (x >> dsh) == D) dst[atomicAdd(&cursor, 1u)] = x & low;
+                        }
+                    }
+                    for (int i = t; i < novf; i += kF2Threads) {
+                        const uint32_t x = xs[i];
+                        if ((x >> dsh) == D) dst[atomicAdd(&cursor, 1u)] = x & low;
+                    }
+                    __syncthreads();
+                    gt += gt_d;
+                    const uint32_t xl = f2_rank_lds(dst, nD, dsh, rr, hist, tmp, sh, &gt);
+                    key = klo + ((D << dsh) | xl);
+                }
+            }
+            if (from_mem) {
+                // ---- 2'. from memory: an LDS histogram of the in-bracket keys' digits, then the
+                // digit's keys
+                uint32_t kd = 0;
+                int64_t gd = 0;
+                __syncthreads();
+                if (f2_rank_digit(inf_h, cand_h, over, nt, klo, khi, rr0, xs, xd, hist, tmp, sh, &cursor, &kd, &gd)) {
+                    key = kd;
+                    gt += gd;
+                } else {
+                    whole_row = true;
+                }
             }
         }
     }
@@ -1388,7 +1545,7 @@ __global__ __launch_bounds__(kF2Threads) void th_final2_kernel(const float* __re
     if (t == 0) {
         st[kStKey] = key;
         st[kStGt] = gt;
-        if (cfg.mode == 0 && theta_out) theta_out[inst] = active ? key_to_float(key) : 0.f;
+        if (cfg.mode == 0 && theta_out) theta_out[inst] = key_to_float(key);
     }
 }
 

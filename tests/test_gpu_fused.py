@@ -101,6 +101,19 @@ def test_heavy_ties(zero_frac):
         check_staged(both(x, mode=mode))
 
 
+# rows of few distinct keys: the bracket around the threshold holds whole runs of tied keys, so
+# tiles hold more in-bracket keys than their slots (the overflow keys go through LDS, or through
+# memory when more than fit), and the answer's digit holds hundreds of keys (radix select in LDS)
+@pytest.mark.parametrize("n, distinct", [(40000, 12), (40000, 150), (40000, 2000), (80000, 3)])
+def test_bracket_paths(n, distinct):
+    x = synth.make_decode(1, [n], 8, 2, 0, False, (1, 5), 8)
+    rng = np.random.default_rng(distinct)
+    base = x.K[rng.permutation(n)[:distinct]]
+    x.K = np.ascontiguousarray(base[rng.integers(0, distinct, n)])
+    for mode in (api.MODE_VOTE, api.MODE_PER_HEAD):
+        check_staged(both(x, mode=mode))
+
+
 @pytest.mark.parametrize("mode", [api.MODE_VOTE, api.MODE_PER_HEAD])
 def test_long_row(mode):
     x = synth.make_decode(3, [300000], 8, 2, 300, False, (1, 5), 9)
