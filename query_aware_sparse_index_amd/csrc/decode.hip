@@ -468,16 +468,17 @@ static int partial_blocks_per_cu(int G, int mode) {
 // resident blocks; a multiple of 4 and at least one sub-batch per wave.  With a list shared by
 // a sequence's heads (vote mode), each sequence's last range is partial, so EB then grows (by
 // 1/16 at a time, up to kDecMaxEW entries per wave) until the ranges of all sequences fit in
-// that round.  Per-head lists and the dense decode keep EB at most 256 entries per wave: there
-// the extra round of smaller blocks measured faster (ragged per-head batch 553 against 561 us,
-// dense 128K decode 106 against 110 us).  len(b) is the list length (or, for the dense decode,
-// the sequence length) of sequence b.
+// that round.  The dense decode keeps EB at most 256 entries per wave and per-head lists at most
+// 64: there several rounds of smaller blocks measured faster, the blocks that finish early taking
+// the next ones (dense 128K decode 106 against 110 us; per-head lists at 128K tokens and 20 %,
+// 69.7 against 80.8 us with 256 entries per wave).  len(b) is the list length (or, for the dense
+// decode, the sequence length) of sequence b.
 template <class Len>
 static int decode_eb(Len len, int B, int HW, int G, int mode) {
     const int64_t target = (int64_t)partial_blocks_per_cu(G, mode) * device_cus();
     int64_t entries = 0;
     for (int b = 0; b < B; ++b) entries += len(b);
-    const int64_t lo = kDecWaves * kDecSub, hi = kDecWaves * (mode == 0 ? kDecMaxEW : 256);
+    const int64_t lo = kDecWaves * kDecSub, hi = kDecWaves * (mode == 0 ? kDecMaxEW : (mode == 1 ? 64 : 256));
     auto clampr = [&](int64_t e) {
         e = (e + 3) / 4 * 4;
         return e < lo ? lo : (e > hi ? hi : e);

@@ -70,11 +70,12 @@ hipError_t launch_score_select(const uint16_t* q, const float* P, uint16_t* k_in
                                const int64_t* offsets_dev, const int64_t* offsets_host, int B, int Hq, int Hkv,
                                const SelectConfig& c, float* scores, int32_t* idx_out, int64_t* count_out,
                                float* theta_out, uint8_t* votes_out, void* ws, size_t ws_bytes, hipStream_t stream);
-// Top-k per row of a [rows][stride] fp32 array (n valid entries per row), ties to the lower
-// position, ascending output idx_out[r * k + j] (the per-head selection with no forced tokens).
-size_t rows_topk_workspace(int rows, int64_t n, int64_t k);
-hipError_t launch_rows_topk(const float* vals, int64_t stride, int rows, int64_t n, int64_t k, int32_t* idx_out,
-                            void* ws, size_t ws_bytes, hipStream_t stream);
+// SnapKV top-c of `rows` importance rows imp[rows][n]: pooled[r * ps + j] (and, when non-null,
+// pooled_out[r * n + j]) = avg_pool1d(3) of the row, then the top min(c, n) positions per row,
+// ties to the lower position, ascending in idx_out[r * min(c, n) + j].
+size_t snap_topc_workspace(int rows, int64_t n);
+hipError_t launch_snap_topc(const float* imp, int64_t n, int rows, int64_t c, float* pooled, int64_t ps,
+                            float* pooled_out, int32_t* idx_out, void* ws, size_t ws_bytes, hipStream_t stream);
 
 // ---- selection reuse with neighbour fetch
 int64_t expand_capacity(int64_t k_prev, int64_t n, int64_t sink, int64_t local, int64_t radius);

@@ -136,7 +136,7 @@ __device__ __forceinline__ int64_t sample_pos(int i, int64_t m, int inst, int ru
     return a + (int64_t)(r % (uint32_t)(e - a - kRunLen + 1)) + (i % kRunLen);
 }
 
-template <int NS, int DELTA>
+template <int NS, int DELTA, bool KEYBINS = false>
 __device__ void bracket_of_sample(const float (&v)[NS / kColThreads], const OsInst& oi, uint32_t* hist,
                                   float* wmin, float* wmax, int* tmp, int* sb, uint32_t& klo, uint32_t& khi);
 
@@ -158,7 +158,12 @@ __device__ void sample_bracket(const float* __restrict__ row, const OsInst& oi, 
 // sample rank ir - DELTA and hi the upper edge of the bin after the one holding ir + DELTA (the
 // key range's ends when these leave the sample), ir the target's expected sample rank.  Every
 // thread of the block calls it; `hist` (kSampleBins words) is left dirty.
-template <int NS, int DELTA>
+// The sample's ranks il, ih = ir -+ DELTA around the target rank ir are located in kSampleBins
+// bins of the sample range: equal-width value bins, or (KEYBINS) equal-width bins of the order
+// keys, which spread heavy-tailed positive values (such as mean attention probabilities) over
+// their octaves.  With KEYBINS an upper rank past the sample keeps the bin of the sample's maximum
+// (keys above the bracket are counted, not ranked).
+template <int NS, int DELTA, bool KEYBINS>
 __device__ void bracket_of_sample(const float (&v)[NS / kColThreads], const OsInst& oi, uint32_t* hist,
                                   float* wmin, float* wmax, int* tmp, int* sb, uint32_t& klo, uint32_t& khi) {
     constexpr int NW = kColThreads / 64;
@@ -182,7 +187,33 @@ __device__ void bracket_of_sample(const float (&v)[NS / kColThreads], const OsIn
     const int64_t il = ir - DELTA, ih = ir + DELTA;
     klo = 0u;
     khi = 0xffffffffu;
-    if (mx > mn) {
+    if (KEYBINS && mx > mn) {
+        const uint32_t kmn = order_key(mn), kmx = order_key(mx);
+        const int sh = top_shift(kmx - kmn);
+        const int64_t ihc = ih < NS - 1 ? ih : NS - 1;
+#pragma unroll
+        for (int u = 0; u < PER; ++u) atomicAdd(&hist[(order_key(v[u]) - kmn) >> sh], 1u);
+        __syncthreads();
+        constexpr int BPT = kSampleBins / kColThreads;
+        int c = 0;
+#pragma unroll
+        for (int u = 0; u < BPT; ++u) c += (int)hist[threadIdx.x * BPT + u];
+        int tot;
+        const int inc = block_inclusive_scan<kColThreads>(c, tmp, &tot);
+        int acc = inc - c;
+#pragma unroll
+        for (int u = 0; u < BPT; ++u) {
+            const int bin = threadIdx.x * BPT + u;
+            const int nx = acc + (int)hist[bin];
+            if (acc <= il && il < nx) sb[0] = bin;
+            if (acc <= ihc && ihc < nx) sb[1] = bin;
+            acc = nx;
+        }
+        __syncthreads();
+        if (il > 0) klo = kmn + ((uint32_t)(sb[0] > 0 ? sb[0] - 1 : 0) << sh);
+        const uint64_t hk = (uint64_t)kmn + ((uint64_t)(sb[1] + 2) << sh) - 1;
+        khi = hk < 0xffffffffull ? (uint32_t)hk : 0xffffffffu;
+    } else if (mx > mn) {
         const float scale = (float)kSampleBins / (mx - mn);
 #pragma unroll
         for (int u = 0; u < PER; ++u) {
@@ -1112,9 +1143,46 @@ constexpr int kF2Cap = 24576;                              // keys ranked in LDS
 struct F2Args {
     const uint32_t* tinfo;   // [Hq][ntiles] below | inside << 8 | offset << 16
     const uint32_t* cand;    // [Hq][ntiles][kClsSlots] first in-bracket keys
-    const uint32_t* tcand;   // [ntiles][kClsTile] the other in-bracket keys
+    const uint32_t* tcand;   // [ntiles][tstride] the other in-bracket keys
     int64_t ntiles;
+    int64_t tstride;         // u32 words per tile in tcand
+    uint2* phpre;            // nullable [Hq][ntiles]: per 64-token chunk, the (above, equal) key counts
+                             // of the chunks before it in the sequence (the per-head compaction's input)
 };
+
+// Per-chunk (above, equal) counts of the keys of a score row at positions [beg, end) against the
+// key ks, as exclusive prefixes over the sequence's nt chunks of 64 tokens, into pre[0 .. nt).
+// Thread t takes a contiguous run of chunks; the counts go to `pre` first and are turned into
+// prefixes in place.  (Out of line: used only after the rare whole-row and from-memory paths.)
+__device__ __noinline__ void f2_prefix_from_row(const float* row, int64_t nt, int64_t beg, int64_t end, uint32_t ks,
+                                                uint2* pre, int* tmp) {
+    const int t = threadIdx.x;
+    const int64_t per = (nt + kF2Threads - 1) / kF2Threads;
+    const int64_t c0 = (int64_t)t * per, c1 = c0 + per < nt ? c0 + per : nt;
+    int sg = 0, se = 0;
+    for (int64_t c = c0; c < c1; ++c) {
+        const int64_t a = 64 * c > beg ? 64 * c : beg, e = 64 * c + 64 < end ? 64 * c + 64 : end;
+        uint32_t g = 0, q = 0;
+        for (int64_t i = a; i < e; ++i) {
+            const uint32_t k = order_key(row[i]);
+            g += k > ks ? 1u : 0u;
+            q += k == ks ? 1u : 0u;
+        }
+        pre[c] = make_uint2(g, q);
+        sg += (int)g;
+        se += (int)q;
+    }
+    int tg = 0, te = 0;
+    const int ig = block_inclusive_scan<kF2Threads>(sg, tmp, &tg);
+    const int ie = block_inclusive_scan<kF2Threads>(se, tmp, &te);
+    uint32_t ag = (uint32_t)(ig - sg), ae = (uint32_t)(ie - se);
+    for (int64_t c = c0; c < c1; ++c) {
+        const uint2 v = pre[c];
+        pre[c] = make_uint2(ag, ae);
+        ag += v.x;
+        ae += v.y;
+    }
+}
 
 // The rank-r key (1-based) of a score row over [beg, end) by a whole-row radix select; *gt gets
 // the number of keys above it.  (Out of line: the common path is register-allocated alone.)
@@ -1133,7 +1201,7 @@ __device__ __noinline__ uint32_t f2_rank_row(const float* row, int64_t beg, int6
 // The in-bracket keys of the instance, f(key) once each (every thread of the block calls it).
 template <class F>
 __device__ __forceinline__ void f2_each_cand(const uint32_t* inf_h, const uint32_t* cand_h, const uint32_t* over,
-                                             int64_t nt, F f) {
+                                             int64_t nt, int64_t tstride, F f) {
     for (int64_t r0 = 0; r0 < nt; r0 += kF2Round)
         for (int u = 0; u < kF2Per; ++u) {
             const int64_t T = r0 + (int64_t)kF2Per * threadIdx.x + u;
@@ -1141,7 +1209,7 @@ __device__ __forceinline__ void f2_each_cand(const uint32_t* inf_h, const uint32
             const uint32_t w = inf_h[T];
             const int cnt = (int)((w >> 8) & 0xffu);
             for (int j = 0; j < cnt; ++j)
-                f(j < kClsSlots ? cand_h[T * kClsSlots + j] : over[(size_t)T * kClsTile + (w >> 16) + (j - kClsSlots)]);
+                f(j < kClsSlots ? cand_h[T * kClsSlots + j] : over[(size_t)T * tstride + (w >> 16) + (j - kClsSlots)]);
         }
 }
 
@@ -1266,7 +1334,7 @@ __device__ __forceinline__ uint32_t f2_rank_in_digit(Visit visit, int nD, uint32
 // keys above the answer.
 __device__ __forceinline__ uint32_t f2_short_row_rank(const float* row, int64_t beg, int64_t m, int64_t r,
                                                       uint32_t* hist, float* red, uint32_t* xd, uint32_t* cursor,
-                                                      int* tmp, int64_t* sh, int64_t* gt) {
+                                                      int* tmp, int64_t* sh, int64_t* gt, uint2* pre, int64_t nt) {
     constexpr int KPT = kCap / kF2Threads;
     constexpr int NW = kF2Threads / 64;
     const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
@@ -1317,20 +1385,47 @@ __device__ __forceinline__ uint32_t f2_short_row_rank(const float* row, int64_t 
     const int nD = (int)sh[3];
     *gt = sh[2];
     __syncthreads();
-    return f2_rank_keys(
+    const uint32_t ks = f2_rank_keys(
         [&](auto f) {
 #pragma unroll
             for (int u = 0; u < KPT; ++u)
                 if (u < nu && t + (int64_t)u * kF2Threads < m && bin_of(v[u]) == D) f(order_key(v[u]));
         },
         nD, 32, rr, xd, cursor, hist, tmp, sh, gt);
+    if (pre) {
+        // per-chunk (above, equal) counts of the row's keys against the answer: the row's chunks
+        // cb .. cb + nc - 1 (at most 258) counted in LDS (above in hist[c], equal in hist[512 + c]),
+        // then exclusive prefixes over the sequence's nt chunks
+        const int64_t cb = beg >> 6;
+        const int nc = (int)(((beg + m - 1) >> 6) - cb + 1);
+        __syncthreads();
+        for (int i = t; i < 1024; i += kF2Threads) hist[i] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < KPT; ++u)
+            if (u < nu && t + (int64_t)u * kF2Threads < m) {
+                const uint32_t k = order_key(v[u]);
+                const int c = (int)(((beg + t + (int64_t)u * kF2Threads) >> 6) - cb);
+                if (k > ks) atomicAdd(&hist[c], 1u);
+                else if (k == ks) atomicAdd(&hist[512 + c], 1u);
+            }
+        __syncthreads();
+        const int cg = t < nc ? (int)hist[t] : 0, ce = t < nc ? (int)hist[512 + t] : 0;
+        int tg = 0, te = 0;
+        const int ig = block_inclusive_scan<kF2Threads>(cg, tmp, &tg);
+        const int ie = block_inclusive_scan<kF2Threads>(ce, tmp, &te);
+        if (t < nc) pre[cb + t] = make_uint2((uint32_t)(ig - cg), (uint32_t)(ie - ce));
+        for (int64_t c = t; c < cb; c += kF2Threads) pre[c] = make_uint2(0u, 0u);
+        for (int64_t c = cb + nc + t; c < nt; c += kF2Threads) pre[c] = make_uint2((uint32_t)tg, (uint32_t)te);
+    }
+    return ks;
 }
 
 // Rank rr0 among the in-bracket keys [klo, khi] read from memory (keys that do not fit in LDS,
 // sequences of more than one round): an LDS histogram of their top digit, then the digit's keys.
 // Returns false when that digit holds more than kF2Cap keys.  *gt gets the in-bracket keys above.
 __device__ __noinline__ bool f2_rank_digit(const uint32_t* inf_h, const uint32_t* cand_h, const uint32_t* over,
-                                           int64_t nt, uint32_t klo, uint32_t khi, int64_t rr0, uint32_t* xs,
+                                           int64_t nt, int64_t tstride, uint32_t klo, uint32_t khi, int64_t rr0, uint32_t* xs,
                                            uint32_t* xd, uint32_t* hist, int* tmp, int64_t* sh, uint32_t* cursor,
                                            uint32_t* key, int64_t* gt) {
     const int t = threadIdx.x;
@@ -1338,7 +1433,7 @@ __device__ __noinline__ bool f2_rank_digit(const uint32_t* inf_h, const uint32_t
     for (int i = t; i < kDigitBins; i += kF2Threads) hist[i] = 0;
     if (t == 0) *cursor = 0;
     __syncthreads();
-    f2_each_cand(inf_h, cand_h, over, nt, [&](uint32_t k) { atomicAdd(&hist[(k - klo) >> dsh], 1u); });
+    f2_each_cand(inf_h, cand_h, over, nt, tstride, [&](uint32_t k) { atomicAdd(&hist[(k - klo) >> dsh], 1u); });
     __syncthreads();
     f2_find_digit(hist, rr0, tmp, sh);
     const uint32_t D = (uint32_t)sh[0];
@@ -1349,7 +1444,7 @@ __device__ __noinline__ bool f2_rank_digit(const uint32_t* inf_h, const uint32_t
     if (nD > kF2Cap) return false;
     // the digit's keys (their low dsh bits) into LDS, then ranked there
     const uint32_t low = dsh ? ((1u << dsh) - 1u) : 0u;
-    f2_each_cand(inf_h, cand_h, over, nt, [&](uint32_t k) {
+    f2_each_cand(inf_h, cand_h, over, nt, tstride, [&](uint32_t k) {
         if (((k - klo) >> dsh) == D) xs[atomicAdd(cursor, 1u)] = (k - klo) & low;
     });
     __syncthreads();
@@ -1366,6 +1461,8 @@ __device__ __noinline__ bool f2_rank_digit(const uint32_t* inf_h, const uint32_t
     return true;
 }
 
+// PRE: also the per-chunk prefixes of the per-head compaction (a.phpre).
+template <bool PRE>
 __global__ __launch_bounds__(kF2Threads) void th_final2_kernel(const float* __restrict__ scores, I64Arg offsets,
                                                               int Hq, DevCfg cfg, int64_t S, F2Args a,
                                                               int64_t* __restrict__ state,
@@ -1373,6 +1470,7 @@ __global__ __launch_bounds__(kF2Threads) void th_final2_kernel(const float* __re
     __shared__ uint32_t xs[kF2Cap];
     __shared__ uint32_t hist[kDigitBins + 64];              // the digits, then one spare bin per lane
     __shared__ uint32_t xd[64];
+    __shared__ uint16_t xdt[64];                             // the tile (in the sequence) of each xd key
     __shared__ int tmp[kF2Threads / 64];
     __shared__ int tmp3[3][kF2Threads / 64];
     __shared__ int64_t sh[4];
@@ -1388,9 +1486,14 @@ __global__ __launch_bounds__(kF2Threads) void th_final2_kernel(const float* __re
         // ---- no order statistic, or a row prep leaves without a bracket: ranked from the row itself
         int64_t gt = 0;
         uint32_t key = 0;
-        if (active)
+        if (active) {
+            uint2* pre = nullptr;
+            if (PRE)
+                pre = a.phpre + (size_t)h * a.ntiles +
+                      wave_prefix_seq(b, [od = offsets.dev](int i) { return (od[i + 1] - od[i] + 63) / 64; });
             key = f2_short_row_rank(scores + (int64_t)h * S + off, oi.beg, m, oi.rank, hist,
-                                    reinterpret_cast<float*>(tmp3), xd, &cursor, tmp, sh, &gt);
+                                    reinterpret_cast<float*>(tmp3), xd, &cursor, tmp, sh, &gt, pre, (n + 63) / 64);
+        }
         if (t == 0) {
             st[kStKey] = key;
             st[kStGt] = gt;
@@ -1398,19 +1501,16 @@ __global__ __launch_bounds__(kF2Threads) void th_final2_kernel(const float* __re
         }
         return;
     }
-    const uint32_t klo = (uint32_t)st[kStLo], khi = (uint32_t)st[kStHi];
     const int64_t tf = wave_prefix_seq(b, [od = offsets.dev](int i) { return (od[i + 1] - od[i] + 63) / 64; });
     const int64_t nt = (n + 63) / 64;
     const size_t hrow = (size_t)h * a.ntiles + tf;
     const uint32_t* inf_h = a.tinfo + hrow;
     const uint32_t* cand_h = a.cand + hrow * kClsSlots;
-    const uint32_t* over = a.tcand + (size_t)tf * kClsTile;      // overflow keys of the sequence's tiles
+    const uint32_t* over = a.tcand + (size_t)tf * a.tstride;     // overflow keys of the sequence's tiles
     const bool one = nt <= kF2Round;                   // one round: the keys load with the records
-    const int dsh = top_shift(khi - klo);
-    for (int i = t; i < kDigitBins + 64; i += kF2Threads) hist[i] = 0;
 
     // ---- 1. records, first keys and counts: one memory round trip (tiles past nt read tile 0's
-    // records, in bounds, and count nothing)
+    // records, in bounds, and count nothing); the bracket is read after these loads are issued
     uint32_t w[kF2Per];
     uint32_t kv[kF2Per][kClsSlots];
 #pragma unroll
@@ -1430,6 +1530,10 @@ __global__ __launch_bounds__(kF2Threads) void th_final2_kernel(const float* __re
             }
         }
     }
+    __builtin_amdgcn_sched_barrier(0);
+    const uint32_t klo = (uint32_t)st[kStLo], khi = (uint32_t)st[kStHi];
+    const int dsh = top_shift(khi - klo);
+    for (int i = t; i < kDigitBins + 64; i += kF2Threads) hist[i] = 0;
     int lsum = 0, csum = 0, ov0 = 0;
 #pragma unroll
     for (int u = 0; u < kF2Per; ++u) {
@@ -1453,11 +1557,20 @@ __global__ __launch_bounds__(kF2Threads) void th_final2_kernel(const float* __re
     bool whole_row = !(nlo < r && r <= (int64_t)nlo + nmid);
     uint32_t key = 0;
     int64_t gt = 0;
+    bool regs = false;                                    // tile counts below from registers
+    // per tile of this thread: keys above the answer's digit (then above the answer too), and
+    // (after the rank) the tile's keys of that digit above / equal to the answer
+    int tg[kF2Per], te[kF2Per];
+#pragma unroll
+    for (int u = 0; u < kF2Per; ++u) tg[u] = te[u] = 0;
     if (!whole_row) {
         gt = m - nlo - nmid;                              // keys above the bracket
         const int64_t rr0 = r - nlo;
         if (klo == khi) {
             key = klo;                                    // every in-bracket key is the answer
+            regs = one;
+#pragma unroll
+            for (int u = 0; u < kF2Per; ++u) te[u] = (int)((w[u] >> 8) & 0xffu);
         } else {
             // in LDS when one round holds the sequence and the overflow keys fit; else from memory
             bool from_mem = !(one && novf <= kF2Cap);
@@ -1470,7 +1583,7 @@ __global__ __launch_bounds__(kF2Threads) void th_final2_kernel(const float* __re
 #pragma unroll
                 for (int u = 0; u < kF2Per; ++u) {
                     const int cnt = (int)((w[u] >> 8) & 0xffu);
-                    const uint32_t* ov = over + (size_t)((int64_t)kF2Per * t + u) * kClsTile + (w[u] >> 16);
+                    const uint32_t* ov = over + (size_t)((int64_t)kF2Per * t + u) * a.tstride + (w[u] >> 16);
                     for (int j0 = kClsSlots; j0 < cnt; j0 += 8) {
                         uint32_t x8[8];
 #pragma unroll
@@ -1502,27 +1615,51 @@ __global__ __launch_bounds__(kF2Threads) void th_final2_kernel(const float* __re
                 if (nD > 64 && novf + nD > kF2Cap) {
                     from_mem = true;                      // the digit does not fit beside the overflow keys
                 } else {
-                    // the digit's keys (low bits) into LDS: xd for at most 64, else after the
-                    // overflow keys; then ranked there
+                    // the digit's keys (low bits) into LDS: xd (with their tiles) for at most 64,
+                    // else after the overflow keys; then ranked there.  Meanwhile each thread
+                    // counts its tiles' keys of higher digits.
                     const uint32_t low = dsh ? ((1u << dsh) - 1u) : 0u;
                     uint32_t* dst = nD <= 64 ? xd : xs + novf;
+                    int ovb = oinc - ov0;                 // this thread's overflow keys in xs
 #pragma unroll
                     for (int u = 0; u < kF2Per; ++u) {
                         const int cnt = (int)((w[u] >> 8) & 0xffu);
+                        const uint16_t T = (uint16_t)(kF2Per * t + u);
+                        auto take = [&](uint32_t x) {
+                            const uint32_t dg = x >> dsh;
+                            if (PRE) tg[u] += dg > D ? 1 : 0;
+                            if (dg == D) {
+                                const uint32_t pos = atomicAdd(&cursor, 1u);
+                                dst[pos] = x & low;
+                                if (PRE && nD <= 64) xdt[pos] = T;
+                            }
+                        };
 #pragma unroll
-                        for (int j = 0; j < kClsSlots; ++j) {
-                            const uint32_t x = kv[u][j] - klo;
-                            if (j < cnt && (x >> dsh) == D) dst[atomicAdd(&cursor, 1u)] = x & low;
-                        }
-                    }
-                    for (int i = t; i < novf; i += kF2Threads) {
-                        const uint32_t x = xs[i];
-                        if ((x >> dsh) == D) dst[atomicAdd(&cursor, 1u)] = x & low;
+                        for (int j = 0; j < kClsSlots; ++j)
+                            if (j < cnt) take(kv[u][j] - klo);
+                        for (int j = kClsSlots; j < cnt; ++j) take(xs[ovb + j - kClsSlots]);
+                        ovb += cnt > kClsSlots ? cnt - kClsSlots : 0;
                     }
                     __syncthreads();
                     gt += gt_d;
                     const uint32_t xl = f2_rank_lds(dst, nD, dsh, rr, hist, tmp, sh, &gt);
                     key = klo + ((D << dsh) | xl);
+                    if (PRE && nD <= 64) {
+                        // the digit's keys of this thread's tiles against the answer's low bits
+                        regs = true;
+                        for (int i = 0; i < nD; ++i) {
+                            const int T = xdt[i];
+                            if (T / kF2Per == t) {
+                                const uint32_t x = xd[i];
+#pragma unroll
+                                for (int u = 0; u < kF2Per; ++u)
+                                    if (T % kF2Per == u) {
+                                        tg[u] += x > xl ? 1 : 0;
+                                        te[u] += x == xl ? 1 : 0;
+                                    }
+                            }
+                        }
+                    }
                 }
             }
             if (from_mem) {
@@ -1531,7 +1668,7 @@ __global__ __launch_bounds__(kF2Threads) void th_final2_kernel(const float* __re
                 uint32_t kd = 0;
                 int64_t gd = 0;
                 __syncthreads();
-                if (f2_rank_digit(inf_h, cand_h, over, nt, klo, khi, rr0, xs, xd, hist, tmp, sh, &cursor, &kd, &gd)) {
+                if (f2_rank_digit(inf_h, cand_h, over, nt, a.tstride, klo, khi, rr0, xs, xd, hist, tmp, sh, &cursor, &kd, &gd)) {
                     key = kd;
                     gt += gd;
                 } else {
@@ -1546,6 +1683,38 @@ __global__ __launch_bounds__(kF2Threads) void th_final2_kernel(const float* __re
         st[kStKey] = key;
         st[kStGt] = gt;
         if (cfg.mode == 0 && theta_out) theta_out[inst] = key_to_float(key);
+    }
+    if (PRE) {
+        // per-chunk (above, equal) counts against the answer, as exclusive prefixes
+        uint2* pre = a.phpre + hrow;
+        if (regs && !whole_row) {
+            // from the records: a tile's keys above the bracket are above the answer, those below
+            // it below; the in-bracket ones were counted above
+            int sg = 0, se = 0;
+#pragma unroll
+            for (int u = 0; u < kF2Per; ++u) {
+                const int64_t T = (int64_t)kF2Per * t + u;
+                const int64_t pa = 64 * T > oi.beg ? 64 * T : oi.beg, pe = 64 * T + 64 < oi.end ? 64 * T + 64 : oi.end;
+                const int valid = (T < nt && pe > pa) ? (int)(pe - pa) : 0;
+                tg[u] += valid - (int)(w[u] & 0xffu) - (int)((w[u] >> 8) & 0xffu);
+                sg += tg[u];
+                se += te[u];
+            }
+            int tgs = 0, tes = 0;
+            const int ig = block_inclusive_scan<kF2Threads>(sg, tmp, &tgs);
+            const int ie = block_inclusive_scan<kF2Threads>(se, tmp, &tes);
+            uint32_t ag = (uint32_t)(ig - sg), ae = (uint32_t)(ie - se);
+#pragma unroll
+            for (int u = 0; u < kF2Per; ++u) {
+                const int64_t T = (int64_t)kF2Per * t + u;
+                if (T < nt) pre[T] = make_uint2(ag, ae);
+                ag += (uint32_t)tg[u];
+                ae += (uint32_t)te[u];
+            }
+        } else {
+            __syncthreads();
+            f2_prefix_from_row(scores + (int64_t)h * S + off, nt, oi.beg, oi.end, key, pre, tmp);
+        }
     }
 }
 
@@ -1632,9 +1801,10 @@ size_t score_select_workspace(const int64_t* offsets_host, int B, int Hq, const 
 
 // Votes and the ordered compaction (vote mode) or the per-head compaction, once the order
 // statistics are in the state.
+// prefixed: the per-head chunk prefixes are already in L.phcnt (th_final2 writes them).
 static hipError_t launch_select_tail(const SelectLayout& L, const float* scores, int64_t S, const I64Arg& offs,
                                      int B, int Hq, const SelectConfig& c, int32_t* idx_out, int64_t* count_out,
-                                     uint8_t* votes_out, hipStream_t stream) {
+                                     uint8_t* votes_out, hipStream_t stream, bool prefixed = false) {
     DevCfg d = dev_cfg(c);
     if (L.nitems == 0) return hipGetLastError();
     if (c.mode == 0) {
@@ -1645,10 +1815,12 @@ static hipError_t launch_select_tail(const SelectLayout& L, const float* scores,
                            B, d, L.keys, L.hist, idx_out, count_out);
     } else {
         const dim3 phg((unsigned)((L.ph_items + kPhWaves - 1) / kPhWaves));
-        hipLaunchKernelGGL(ph_count_kernel, phg, dim3(kPhWaves * 64), 0, stream, scores, offs,
-                           B, Hq, d, S, L.state, L.ph_items, L.phcnt);
-        hipLaunchKernelGGL(ph_scan_kernel, dim3((unsigned)(B * Hq)), dim3(kPhScanThreads), 0, stream, offs, B,
-                           Hq, L.ph_items, L.phcnt);
+        if (!prefixed) {
+            hipLaunchKernelGGL(ph_count_kernel, phg, dim3(kPhWaves * 64), 0, stream, scores, offs,
+                               B, Hq, d, S, L.state, L.ph_items, L.phcnt);
+            hipLaunchKernelGGL(ph_scan_kernel, dim3((unsigned)(B * Hq)), dim3(kPhScanThreads), 0, stream, offs, B,
+                               Hq, L.ph_items, L.phcnt);
+        }
         hipLaunchKernelGGL(ph_compact_kernel, phg, dim3(kPhWaves * 64), 0, stream, scores,
                            offs, B, Hq, d, S, L.state, L.ph_items, L.phcnt, idx_out, count_out);
     }
@@ -1685,13 +1857,32 @@ hipError_t launch_score_select(const uint16_t* q, const float* P, uint16_t* k_in
     hipError_t e = launch_score_classify(L.qp, k_index, offsets_dev, offsets_host, B, Hq, Hkv, scores, L.state, L.tinfo,
                                          L.hcand, L.tcand, stream);
     if (e != hipSuccess) return e;
-    const F2Args fa{L.tinfo, L.hcand, L.tcand, L.ntiles};
-    hipLaunchKernelGGL(th_final2_kernel, dim3(inst), dim3(kF2Threads), 0, stream, scores, offs, Hq, d, S, fa, L.state,
-                       theta_out);
-    return launch_select_tail(L, scores, S, offs, B, Hq, c, idx_out, count_out, votes_out, stream);
+    // per-head mode: th_final2 also writes the compaction's chunk prefixes (no count and scan kernels)
+    const F2Args fa{L.tinfo, L.hcand, L.tcand, L.ntiles, kClsTile,
+                    c.mode == 1 ? reinterpret_cast<uint2*>(L.phcnt) : nullptr};
+    if (c.mode == 1)
+        hipLaunchKernelGGL(th_final2_kernel<true>, dim3(inst), dim3(kF2Threads), 0, stream, scores, offs, Hq, d, S, fa,
+                           L.state, theta_out);
+    else
+        hipLaunchKernelGGL(th_final2_kernel<false>, dim3(inst), dim3(kF2Threads), 0, stream, scores, offs, Hq, d, S, fa,
+                           L.state, theta_out);
+    return launch_select_tail(L, scores, S, offs, B, Hq, c, idx_out, count_out, votes_out, stream, true);
 }
 
-// ------------------------------------------------------------- row-wise top-k
+// ------------------------------------------------------------ SnapKV top-c per row
+// [SK] "アルゴリズム": the top min(c, n) positions of each KV head's pooled importance, in
+// ascending position order; ties at the threshold go to the lower positions.  The rows are few
+// (one per KV head) and long, so instead of the general selection:
+//   snap_prep_kernel:          per row, a key bracket around the threshold from 1024 sampled
+//                              pooled values (rows of more than kCap keys), as prep_kernel does
+//                              for index scores;
+//   snap_pool_classify_kernel: pooled[j] = ((imp[j-1] + imp[j]) + imp[j+1]) / 3 (zero outside
+//                              [0, n)), written once, and each 64-key tile classified against the
+//                              bracket in the score kernel's record layout;
+//   th_final2_kernel:          the threshold key, the number of keys above it and each 64-key
+//                              chunk's prefix of (above, equal) counts;
+//   ph_compact_kernel:         the positions of the keys above the threshold and of the first
+//                              (need - #above) keys equal to it, one wave per chunk.
 static SelectConfig rows_cfg(int64_t n, int64_t k) {
     SelectConfig c;
     c.mode = 1;
@@ -1705,25 +1896,131 @@ static SelectConfig rows_cfg(int64_t n, int64_t k) {
     return c;
 }
 
-size_t rows_topk_workspace(int rows, int64_t n, int64_t k) {
-    int64_t oh[2] = {0, n};
-    WsCarver w(nullptr);
-    w.take<int64_t>(4);
-    w.take<char>(select_workspace(oh, 1, rows, rows_cfg(n, k)));
-    return w.size();
+// the pooled value at position j of a row of n importances
+__device__ __forceinline__ float pooled_at(const float* row, int64_t n, int64_t j) {
+    const float a = j > 0 ? row[j - 1] : 0.f;
+    const float c = j + 1 < n ? row[j + 1] : 0.f;
+    return ((a + row[j]) + c) / 3.0f;
 }
 
-hipError_t launch_rows_topk(const float* vals, int64_t stride, int rows, int64_t n, int64_t k, int32_t* idx_out,
-                            void* ws, size_t ws_bytes, hipStream_t stream) {
-    if (rows_topk_workspace(rows, n, k) > ws_bytes) return hipErrorInvalidValue;
-    int64_t oh[2] = {0, n};
-    SelectConfig c = rows_cfg(n, k);
+__global__ __launch_bounds__(kPrepThreads) void snap_prep_kernel(const float* __restrict__ imp, int64_t n, DevCfg cfg,
+                                                                int64_t* __restrict__ state) {
+    constexpr int NW = kPrepThreads / 64;
+    __shared__ uint32_t hist[kSampleBins];
+    __shared__ float wmin[NW], wmax[NW];
+    __shared__ int tmp[NW];
+    __shared__ int sb[2];
+    const int g = blockIdx.x, t = threadIdx.x;
+    const OsInst oi = os_instance(n, cfg);
+    const int64_t m = oi.end - oi.beg;
+    uint32_t klo = 1u, khi = 0u;                     // no bracket: the empty one (lo > hi)
+    if (oi.flag == kFlagActive && m > kCap) {
+        constexpr int kPrepRuns = kPrepSample / kRunLen;
+        const float* row = imp + (int64_t)g * n;
+        float v[kPrepSample / kColThreads];
+#pragma unroll
+        for (int u = 0; u < kPrepSample / kColThreads; ++u)
+            v[u] = pooled_at(row, n, oi.beg + sample_pos(t + u * kColThreads, m, g, kPrepRuns));
+        bracket_of_sample<kPrepSample, kPrepDelta, true>(v, oi, hist, wmin, wmax, tmp, sb, klo, khi);
+    }
+    if (t == 0) {
+        int64_t* st = state + (int64_t)g * 8;
+        st[kStFlag] = oi.flag;
+        st[kStNeed] = oi.need;
+        st[kStLo] = klo;
+        st[kStHi] = khi;
+        st[kStBeg] = oi.beg;
+        st[kStEnd] = oi.end;
+    }
+}
+
+// Block = 4 tiles of 64 keys of row g, one wave each; lane = key of the tile.  Records as the
+// score kernel's: tinfo[g][tile] = below | inside << 8 | (g * 64) << 16, the first kClsSlots
+// in-bracket keys in cand[g][tile][], the rest at tcand[tile * rows * 64 + g * 64 + j - kClsSlots].
+constexpr int kSnapTilesPerBlock = 4;
+__global__ __launch_bounds__(64 * kSnapTilesPerBlock) void snap_pool_classify_kernel(
+    const float* __restrict__ imp, int64_t n, int rows, int64_t ps, const int64_t* __restrict__ state,
+    float* __restrict__ pooled, float* __restrict__ pooled_out, uint32_t* __restrict__ tinfo,
+    uint32_t* __restrict__ cand, uint32_t* __restrict__ tcand, int64_t ntiles) {
+    const int lane = threadIdx.x & 63;
+    const int64_t tb = (ntiles + kSnapTilesPerBlock - 1) / kSnapTilesPerBlock;
+    const int g = (int)(blockIdx.x / tb);
+    const int64_t tile = (blockIdx.x % tb) * kSnapTilesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (tile >= ntiles) return;
+    const int64_t* st = state + (int64_t)g * 8;
+    const int64_t flag = st[kStFlag];
+    const uint32_t lo = (uint32_t)st[kStLo], hi = (uint32_t)st[kStHi];
+    const int64_t j = tile * 64 + lane;
+    const bool inr = j < n;
+    const float v = inr ? pooled_at(imp + (int64_t)g * n, n, j) : 0.f;
+    if (inr) {
+        pooled[(int64_t)g * ps + j] = v;
+        if (pooled_out) pooled_out[(int64_t)g * n + j] = v;
+    }
+    uint32_t below = 0;
+    uint64_t mm = 0;
+    const uint32_t key = order_key(v);
+    if (flag == kFlagActive && lo <= hi) {
+        below = (uint32_t)__popcll(__ballot(inr && key < lo));
+        mm = __ballot(inr && key >= lo && key <= hi);
+    }
+    const uint32_t cnt = (uint32_t)__popcll(mm);
+    const size_t r = (size_t)g * ntiles + tile;
+    if (lane == 0) tinfo[r] = below | (cnt << 8) | ((uint32_t)(g * 64) << 16);
+    if ((mm >> lane) & 1ull) {
+        const uint32_t jj = (uint32_t)__popcll(mm & ((1ull << lane) - 1ull));
+        if (jj < (uint32_t)kClsSlots) cand[r * kClsSlots + jj] = key;
+        else tcand[(size_t)tile * rows * 64 + g * 64 + jj - kClsSlots] = key;
+    }
+}
+
+struct SnapTopcLayout {
+    int64_t ntiles;
+    int64_t* state;
+    int64_t* count;
+    uint32_t *tinfo, *cand, *tcand;
+    uint2* pre;
+    size_t bytes;
+};
+
+static SnapTopcLayout snap_topc_layout(void* ws, int rows, int64_t n) {
+    SnapTopcLayout L;
+    L.ntiles = (n + 63) / 64;
     WsCarver w(ws);
-    int64_t* cnt = w.take<int64_t>(4);
-    size_t sb = select_workspace(oh, 1, rows, c);
-    void* sws = w.take<char>(sb);
-    // one sequence {0, n}: the offsets travel as launch arguments, no device copy is read
-    return launch_select(vals, stride, nullptr, oh, 1, rows, c, idx_out, cnt, nullptr, nullptr, sws, sb, stream);
+    L.state = w.take<int64_t>((size_t)rows * 8);
+    L.count = w.take<int64_t>(1);
+    L.pre = w.take<uint2>((size_t)rows * L.ntiles);
+    L.tinfo = w.take<uint32_t>((size_t)rows * L.ntiles);
+    L.cand = w.take<uint32_t>((size_t)rows * L.ntiles * kClsSlots);
+    L.tcand = w.take<uint32_t>((size_t)L.ntiles * rows * 64);
+    L.bytes = w.size();
+    return L;
+}
+
+size_t snap_topc_workspace(int rows, int64_t n) { return snap_topc_layout(nullptr, rows, n).bytes; }
+
+hipError_t launch_snap_topc(const float* imp, int64_t n, int rows, int64_t c, float* pooled, int64_t ps,
+                            float* pooled_out, int32_t* idx_out, void* ws, size_t ws_bytes, hipStream_t stream) {
+    SnapTopcLayout L = snap_topc_layout(ws, rows, n);
+    if (L.bytes > ws_bytes || n <= 0 || c <= 0) return hipErrorInvalidValue;
+    const int64_t ce = c < n ? c : n;
+    const DevCfg d = dev_cfg(rows_cfg(n, ce));
+    hipLaunchKernelGGL(snap_prep_kernel, dim3(rows), dim3(kPrepThreads), 0, stream, imp, n, d, L.state);
+    const int64_t tb = (L.ntiles + kSnapTilesPerBlock - 1) / kSnapTilesPerBlock;
+    hipLaunchKernelGGL(snap_pool_classify_kernel, dim3((unsigned)(tb * rows)), dim3(64 * kSnapTilesPerBlock), 0, stream,
+                       imp, n, rows, ps, L.state, pooled, pooled_out, L.tinfo, L.cand, L.tcand, L.ntiles);
+    // one sequence {0, n} of `rows` instances: the bounds travel as launch arguments
+    const int64_t oh[2] = {0, n};
+    const I64Arg offs = i64_arg(nullptr, oh, 2);
+    const F2Args fa{L.tinfo, L.cand, L.tcand, L.ntiles, (int64_t)rows * 64, L.pre};
+    hipLaunchKernelGGL(th_final2_kernel<true>, dim3(rows), dim3(kF2Threads), 0, stream, pooled, offs, rows, d, ps, fa,
+                       L.state, nullptr);
+    // the per-head compaction: the rows are the heads of one sequence with no forced tokens, so the
+    // list of row r is idx_out[r * ce ...]
+    hipLaunchKernelGGL(ph_compact_kernel, dim3((unsigned)((L.ntiles + kPhWaves - 1) / kPhWaves)), dim3(kPhWaves * 64), 0,
+                       stream, pooled, offs, 1, rows, d, ps, L.state, L.ntiles, reinterpret_cast<const uint32_t*>(L.pre),
+                       idx_out, L.count);
+    return hipGetLastError();
 }
 
 }  // namespace qasi

@@ -273,21 +273,6 @@ __global__ __launch_bounds__(256) void snap_lse_kernel(const float2* __restrict_
     }
 }
 
-// pooled[g][j] = ((imp[j-1] + imp[j]) + imp[j+1]) / 3, zero outside [0, n); written with row
-// stride `ps` into the workspace and, when requested, densely into pooled_out.
-__global__ void snap_pool_kernel(const float* __restrict__ imp, int64_t n, int Hkv, int64_t ps,
-                                 float* __restrict__ pooled, float* __restrict__ pooled_out) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= n * Hkv) return;
-    const int64_t g = i / n, j = i % n;
-    const float* row = imp + g * n;
-    float a = j > 0 ? row[j - 1] : 0.f;
-    float c = j + 1 < n ? row[j + 1] : 0.f;
-    const float v = ((a + row[j]) + c) / 3.0f;
-    pooled[g * ps + j] = v;
-    if (pooled_out) pooled_out[i] = v;
-}
-
 // K_out[s][g] = K[idx[g][s]][g]; one 16-byte piece per thread
 __global__ void snap_gather_kernel(const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                                    const int32_t* __restrict__ idx, int64_t n, int64_t ce, int Hkv,
@@ -368,8 +353,8 @@ static SnapLayout snap_layout(void* ws, int64_t n, int w, int Hq, int Hkv, int64
     L.lse = wc.take<float>((size_t)Hkv * R);
     L.imp = wc.take<float>((size_t)Hkv * n);
     L.pooled = wc.take<float>((size_t)Hkv * score_stride(n));
-    int64_t ce = c < n ? c : n;
-    L.sel_bytes = rows_topk_workspace(Hkv, n, ce);
+    (void)c;
+    L.sel_bytes = snap_topc_workspace(Hkv, n);
     L.sel_ws = wc.take<char>(L.sel_bytes);
     L.bytes = wc.size();
     return L;
@@ -435,12 +420,9 @@ hipError_t launch_snapkv(const uint16_t* q_obs, const uint16_t* K, const uint16_
     hipLaunchKernelGGL(snap_lse_kernel, dim3(Hkv * rblk), dim3(256), 0, stream, L.pstat, L.P, R, Hkv, L.lse);
     e = launch_snap_pass<2>(R / 16, grid, shq, stream, q_obs, K, n, w, Hq, Hkv, L.nblk, nullptr, L.lse, imp);
     if (e != hipSuccess) return e;
-    const int64_t tot = n * Hkv;
-    hipLaunchKernelGGL(snap_pool_kernel, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, stream, imp, n, Hkv,
-                       score_stride(n), pooled, pooled_out);
-    const int64_t ce = c < n ? c : n;
-    e = launch_rows_topk(pooled, score_stride(n), Hkv, n, ce, idx_out, L.sel_ws, L.sel_bytes, stream);
+    e = launch_snap_topc(imp, n, Hkv, c, pooled, score_stride(n), pooled_out, idx_out, L.sel_ws, L.sel_bytes, stream);
     if (e != hipSuccess) return e;
+    const int64_t ce = c < n ? c : n;
     const int64_t pieces = ce * Hkv * 16;
     hipLaunchKernelGGL(snap_gather_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, stream, K, V, idx_out,
                        n, ce, Hkv, K_out, V_out);
