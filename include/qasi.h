@@ -80,7 +80,8 @@ const char* ts_last_error(void);
 /* Row stride S of the score array: offsets[B] rounded up to a multiple of 64 (-1 if invalid). */
 int64_t ts_score_stride(const int64_t* offsets_host, int32_t B);
 
-/* K_b for one sequence of n tokens under `p` (host-only helper; -1 if p is invalid). */
+/* K_b for one sequence of n tokens under `p` (host-only helper; -1 if p is invalid or n is
+ * outside [0, 2^31]). */
 int64_t ts_budget_tokens(int64_t n, const ts_select_params* p);
 
 /* Append T tokens to the compressed key index ([TS] "Query-Key Dot Product Index": the
@@ -167,7 +168,8 @@ int ts_score_select(const uint16_t* q, const float* P, uint16_t* k_index, const 
                     size_t ws_bytes, hipStream_t stream);
 
 /* Capacity of an expanded list (ts_expand_selection): min(n, (2 radius + 1) k_prev + sink +
- * local); -1 if an argument is out of range. */
+ * local); -1 if an argument is out of range (k_prev in [0, n], n, sink and local in [0, 2^31],
+ * radius in [0, 2^20]). */
 int64_t ts_expand_capacity(int64_t k_prev, int64_t n, int64_t sink, int64_t local, int64_t radius);
 
 /* Workspace for ts_expand_selection (0 if an argument is invalid). */

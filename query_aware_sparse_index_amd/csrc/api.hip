@@ -114,7 +114,8 @@ int64_t ts_score_stride(const int64_t* offsets_host, int32_t B) {
 
 int64_t ts_budget_tokens(int64_t n, const ts_select_params* p) {
     qasi::SelectConfig c;
-    if (n < 0 || to_cfg(p, &c) != QASI_OK) return -1;
+    // n * budget_num stays below 2^62
+    if (n < 0 || n > ((int64_t)1 << 31) || to_cfg(p, &c) != QASI_OK) return -1;
     return qasi::budget_tokens(n, c);
 }
 
@@ -213,7 +214,11 @@ int ts_score_select(const uint16_t* q, const float* P, uint16_t* k_index, const 
 }
 
 int64_t ts_expand_capacity(int64_t k_prev, int64_t n, int64_t sink, int64_t local, int64_t radius) {
-    if (k_prev < 0 || n < 0 || sink < 0 || local < 0 || radius < 0 || radius > (1 << 20) || k_prev > n) return -1;
+    // (2 radius + 1) k_prev + sink + local stays below 2^62
+    const int64_t lim = (int64_t)1 << 31;
+    if (k_prev < 0 || n < 0 || n > lim || sink < 0 || sink > lim || local < 0 || local > lim || radius < 0 ||
+        radius > (1 << 20) || k_prev > n)
+        return -1;
     return qasi::expand_capacity(k_prev, n, sink, local, radius);
 }
 
