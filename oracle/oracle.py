@@ -18,6 +18,7 @@ _SRC = os.path.join(_HERE, "qasi_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 _u16p = np.ctypeslib.ndpointer(dtype=np.uint16, flags="C_CONTIGUOUS")
+_u8p = np.ctypeslib.ndpointer(np.uint8, flags="C_CONTIGUOUS")
 _f32p = np.ctypeslib.ndpointer(dtype=np.float32, flags="C_CONTIGUOUS")
 _f64p = np.ctypeslib.ndpointer(dtype=np.float64, flags="C_CONTIGUOUS")
 _i32p = np.ctypeslib.ndpointer(dtype=np.int32, flags="C_CONTIGUOUS")
@@ -87,6 +88,8 @@ def lib():
                                                 _i64p]
         L.qo_gather_rows.restype = None
         L.qo_gather_rows.argtypes = [_u16p, _u16p, _i64, _int, _i32p, _i64, _u16p, _u16p]
+        L.qo_union_lists.restype = None
+        L.qo_union_lists.argtypes = [_i32p, _i64p, _i64p, _int, _int, _int, _i32p, _u8p, _i64p]
         _lib = L
     return _lib
 
@@ -302,3 +305,22 @@ def snapkv_retain_clusters(K, V, idx, k_cluster):
     valid = np.empty(Hkv, np.int64)
     lib().qo_snapkv_retain_clusters(K, V, n, Hkv, idx, ce, k_cluster, io, Ko, Vo, valid)
     return io[:, :cap], Ko[:cap], Vo[:cap], valid
+
+
+def union_lists(idx, count, offsets, Hq, Hkv):
+    """Per-KV-group union of per-head lists (select_per_head's layout).  Returns (uidx, umask,
+    ucount [B][Hkv]): for sequence b and KV head g, the block of G*k_b entries at
+    Hq*kpre_b + g*G*k_b holds the union's tokens in ascending order, then -1; umask bit hh marks
+    the tokens head g*G+hh selected."""
+    offsets = _c(offsets, np.int64)
+    count = _c(count, np.int64)
+    B = len(offsets) - 1
+    total = Hq * int(count.sum())
+    idx = _c(idx, np.int32)
+    if idx.size == 0:
+        idx = np.zeros(1, np.int32)
+    uidx = np.empty(max(total, 1), np.int32)
+    umask = np.empty(max(total, 1), np.uint8)
+    ucount = np.empty(B * Hkv, np.int64)
+    lib().qo_union_lists(idx, count, offsets, B, Hq, Hkv, uidx, umask, ucount)
+    return uidx[:total], umask[:total], ucount.reshape(B, Hkv)

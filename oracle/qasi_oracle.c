@@ -468,3 +468,44 @@ int64_t qo_snapkv_retain_clusters(const uint16_t* K, const uint16_t* V, int64_t 
     qo_gather_rows(K, V, n, Hkv, idx_out, cap, K_out, V_out);
     return cap;
 }
+
+/* Per-KV-group union of the per-head lists (per-head mode's decode input: [TS] "主要な貢献",
+ * each head selects its own tokens; the G query heads of a KV head read the same K/V rows, so
+ * the decode reads each row of the group's union once and lets every head use the rows it
+ * selected).  idx and count are qo_select_per_head's output (idx[Hq*kpre_b + h*k_b + j],
+ * count[b] = k_b).  For sequence b and KV head g, in the block of G*k_b entries at
+ * uidx[Hq*kpre_b + g*G*k_b ...]: the tokens of the union of lists g*G .. g*G+G-1 in ascending
+ * order, then -1; umask (same layout) has bit hh set when head g*G+hh selected the token (0 for
+ * the padding); ucount[b*Hkv + g] = the union's size. */
+void qo_union_lists(const int32_t* idx, const int64_t* count, const int64_t* offsets, int B, int Hq, int Hkv,
+                    int32_t* uidx, uint8_t* umask, int64_t* ucount) {
+    const int G = Hq / Hkv;
+    int64_t kpre = 0;
+    for (int b = 0; b < B; ++b) {
+        const int64_t n = offsets[b + 1] - offsets[b], k = count[b];
+        uint8_t* mark = (uint8_t*)calloc((size_t)(n > 0 ? n : 1), 1);
+        for (int g = 0; g < Hkv; ++g) {
+            memset(mark, 0, (size_t)(n > 0 ? n : 1));
+            for (int hh = 0; hh < G; ++hh) {
+                const int32_t* list = idx + (int64_t)Hq * kpre + (int64_t)(g * G + hh) * k;
+                for (int64_t j = 0; j < k; ++j) mark[list[j]] |= (uint8_t)(1u << hh);
+            }
+            int32_t* uo = uidx + (int64_t)Hq * kpre + (int64_t)g * G * k;
+            uint8_t* mo = umask + (int64_t)Hq * kpre + (int64_t)g * G * k;
+            int64_t w = 0;
+            for (int64_t t = 0; t < n; ++t)
+                if (mark[t]) {
+                    uo[w] = (int32_t)t;
+                    mo[w] = mark[t];
+                    ++w;
+                }
+            ucount[(int64_t)b * Hkv + g] = w;
+            for (; w < (int64_t)G * k; ++w) {
+                uo[w] = -1;
+                mo[w] = 0;
+            }
+        }
+        free(mark);
+        kpre += k;
+    }
+}

@@ -37,8 +37,9 @@ def _sel_args(tokens):
 
 def vote_example():
     """-> dict(scores [3][12] float64, theta [3], votes [12], selects [(sink, local, num, den,
-    vmin, idx)], perhead {h: (sink, local, num, den, idx)})."""
-    scores, out = [], {"selects": [], "perhead": {}}
+    vmin, idx)], perhead {h: (sink, local, num, den, idx)}, union {"tokens"|"masks": (sink, local,
+    num, den, values)})."""
+    scores, out = [], {"selects": [], "perhead": {}, "union": {}}
     for line in _lines("vote_worked_example.txt"):
         lhs, rhs = line.split("->") if "->" in line else (line, None)
         if lhs.startswith("scores"):
@@ -54,6 +55,10 @@ def vote_example():
             toks = lhs.split()
             sink, local, num, den, _ = _sel_args(toks[1:-1])
             out["perhead"][int(toks[-1][1:])] = (sink, local, num, den, np.array([int(x) for x in rhs.split()], np.int32))
+        elif lhs.startswith("union"):
+            toks = lhs.split()
+            sink, local, num, den, _ = _sel_args(toks[1:-1])
+            out["union"][toks[-1]] = (sink, local, num, den, np.array([int(x) for x in rhs.split()], np.int64))
     out["scores"] = np.array(scores, np.float64)
     return out
 

@@ -49,6 +49,26 @@ def test_vote_example_per_head():
         assert np.array_equal(idx[h * K:(h + 1) * K], want), (h, idx[h * K:(h + 1) * K])
 
 
+def test_vote_example_union():
+    """The per-KV-group union of the worked example's per-head lists (one KV head for the three
+    heads), worked by hand."""
+    ex = vote_example()
+    sc = ex["scores"]
+    offs = np.array([0, sc.shape[1]], np.int64)
+    sink, local, num, den, want_t = ex["union"]["tokens"]
+    want_m = ex["union"]["masks"][-1]
+    idx, cnt = O.select_per_head(sc, offs, num, den, sink, local)
+    uidx, umask, ucount = O.union_lists(idx, cnt, offs, 3, 1)
+    n = int(ucount[0, 0])
+    assert n == len(want_t)
+    assert np.array_equal(uidx[:n], want_t) and np.array_equal(umask[:n], want_m)
+    assert np.all(uidx[n:] == -1) and np.all(umask[n:] == 0)
+    # three KV heads (G = 1): each group's union is its head's own list
+    uidx, umask, ucount = O.union_lists(idx, cnt, offs, 3, 3)
+    K = int(cnt[0])
+    assert np.array_equal(uidx, idx) and np.all(umask == 1) and np.all(ucount == K)
+
+
 def test_pool_topc_example():
     imp, pooled, tops = pool_example()
     got = O.avg_pool1d(imp[None, :], 3)[0]

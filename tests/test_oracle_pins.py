@@ -569,3 +569,47 @@ def test_snapkv_cluster_retention_bruteforce(k_cluster):
         assert not Ko[len(want):, g].any() and not Vo[len(want):, g].any()
     if k_cluster == 0:
         assert np.array_equal(io, idx)
+
+
+@pytest.mark.parametrize("Hq, Hkv", [(8, 8), (8, 4), (8, 2), (8, 1), (16, 2)])
+def test_union_lists_bruteforce(Hq, Hkv):
+    """Per-KV-group union of per-head lists: the set union of the group's lists (Python sets),
+    ascending; the mask bit of a head is set exactly when the token is in that head's list;
+    padded with -1 / 0 to G * k_b; ragged batch with a one-token sequence."""
+    rng = np.random.default_rng(Hq * 10 + Hkv)
+    G = Hq // Hkv
+    lens = [400, 1, 97]
+    ks = [60, 1, 97]
+    offs = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    idx = np.concatenate([np.sort(rng.choice(n, size=k, replace=False)) for n, k in zip(lens, ks)
+                          for _ in range(Hq)]).astype(np.int32)
+    uidx, umask, ucount = O.union_lists(idx, np.array(ks), offs, Hq, Hkv)
+    kpre = 0
+    for b, (n, k) in enumerate(zip(lens, ks)):
+        lists = [idx[Hq * kpre + h * k:Hq * kpre + (h + 1) * k] for h in range(Hq)]
+        for g in range(Hkv):
+            want = sorted(set().union(*[set(int(x) for x in lists[g * G + hh]) for hh in range(G)]))
+            blk = slice(Hq * kpre + g * G * k, Hq * kpre + (g + 1) * G * k)
+            u, m = uidx[blk], umask[blk]
+            c = int(ucount[b, g])
+            assert c == len(want) and list(u[:c]) == want
+            for j, t in enumerate(want):
+                assert m[j] == sum(1 << hh for hh in range(G) if t in set(lists[g * G + hh].tolist()))
+            assert np.all(u[c:] == -1) and np.all(m[c:] == 0)
+        kpre += k
+
+
+def test_union_lists_special_cases():
+    """Identical lists give the list with every mask bit set; disjoint lists give G * k entries with
+    one bit each; G = 1 gives the head's own list."""
+    n, k, Hq = 1000, 50, 4
+    offs = np.array([0, n], np.int64)
+    lst = np.sort(np.random.default_rng(3).choice(n, size=k, replace=False)).astype(np.int32)
+    uidx, umask, ucount = O.union_lists(np.tile(lst, Hq), np.array([k]), offs, Hq, 1)
+    assert ucount[0, 0] == k and np.array_equal(uidx[:k], lst) and np.all(umask[:k] == 15)
+    dis = np.concatenate([np.arange(h, 4 * k, 4) for h in range(Hq)]).astype(np.int32)
+    uidx, umask, ucount = O.union_lists(dis, np.array([k]), offs, Hq, 1)
+    assert ucount[0, 0] == Hq * k and np.array_equal(uidx, np.arange(4 * k))
+    assert np.array_equal(umask, np.tile(1 << np.arange(Hq), k).astype(np.uint8))
+    uidx, umask, ucount = O.union_lists(dis, np.array([k]), offs, Hq, Hq)
+    assert np.array_equal(uidx, dis) and np.all(umask == 1) and np.all(ucount == k)
