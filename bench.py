@@ -333,6 +333,90 @@ def bench_snapkv(args, torch, api, synth, dev):
             f.write(line + "\n")
 
 
+def bench_union(torch, api, L, calls, warm, steps, Hq, Hkv, kmax, offs_max, Kp, Vp, Pp, kip, pref, scp, idp, cnp,
+                wss, ws_ss_n, outp, out, ws_dec, dec_bytes, do_flush, stream_of, chk, dev):
+    """Per-head lists decoded through their per-KV-group union: ts_score_select, ts_union_lists,
+    ts_union_decode per step (LLC flushed before each step), the per-call split in separate steps,
+    each union call alone, and the largest difference from ts_sparse_decode on the same lists."""
+    import ctypes
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    vp = lambda t: ctypes.c_void_p(t.data_ptr())
+    un_idx = torch.empty(kmax * Hq + 16, dtype=torch.int32, device=dev)
+    un_msk = torch.empty(kmax * Hq + 16, dtype=torch.uint8, device=dev)
+    un_cnt = torch.empty((1, Hkv), dtype=torch.int64, device=dev)
+    ws_un = torch.empty(max(int(L.ts_union_workspace_bytes(offs_max.host, 1, Hkv)), 256), dtype=torch.uint8,
+                        device=dev)
+    ws_ud = torch.empty(max(api.decode_workspace_bytes(offs_max, [kmax], Hq, Hkv, api.MODE_UNION), 256),
+                        dtype=torch.uint8, device=dev)
+    out_u = torch.empty_like(out)
+    uip, ump, ucp, wup, wudp, oup = vp(un_idx), vp(un_msk), vp(un_cnt), vp(ws_un), vp(ws_ud), vp(out_u)
+
+    def sel(s, st):
+        (_, _), (qp, od, oh), ch, kb = calls[s]
+        chk(L.ts_score_select(qp, Pp, kip, Kp, od, oh, 1, Hq, Hkv, pref, scp, idp, cnp, None, None, wss, ws_ss_n, st))
+
+    def union(s, st):
+        (_, _), (qp, od, oh), ch, kb = calls[s]
+        chk(L.ts_union_lists(idp, cnp, ch, od, oh, 1, Hq, Hkv, uip, ump, ucp, wup, ws_un.numel(), st))
+
+    def udec(s, st):
+        (_, _), (qp, od, oh), ch, kb = calls[s]
+        chk(L.ts_union_decode(qp, Kp, Vp, od, oh, uip, ump, ucp, cnp, ch, 1, Hq, Hkv, oup, wudp, ws_ud.numel(), st))
+
+    nb = min(steps, 30)
+    whole, parts = [], []
+    for i in range(nb):
+        do_flush()
+        st = stream_of()
+        a, b = ev(), ev()
+        a.record()
+        sel(warm + i, st)
+        union(warm + i, st)
+        udec(warm + i, st)
+        b.record()
+        whole.append((a, b))
+    for i in range(nb):
+        do_flush()
+        st = stream_of()
+        m = [ev() for _ in range(4)]
+        m[0].record()
+        sel(warm + i, st)
+        m[1].record()
+        union(warm + i, st)
+        m[2].record()
+        udec(warm + i, st)
+        m[3].record()
+        parts.append(m)
+    torch.cuda.synchronize()
+    alone = {}
+    s_last = warm + steps - 1
+    st = stream_of()
+    sel(s_last, st)
+    for name, fn in (("union_lists", union), ("union_decode", udec)):
+        evs = []
+        for r in range(12):
+            do_flush()
+            a, b = ev(), ev()
+            a.record()
+            fn(s_last, st)
+            b.record()
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        alone[name] = round(float(np.mean([a.elapsed_time(b) * 1e3 for a, b in evs[2:]])), 2)
+    (_, _), (qp, od, oh), ch, kb = calls[s_last]
+    chk(L.ts_sparse_decode(qp, Kp, Vp, od, oh, idp, cnp, ch, api.MODE_PER_HEAD, 1, Hq, Hkv, outp, vp(ws_dec),
+                           ws_dec.numel(), st))
+    torch.cuda.synchronize()
+    uc = un_cnt.cpu().numpy()
+    return {"us_per_step": round(float(np.mean([a.elapsed_time(b) * 1e3 for a, b in whole])), 2),
+            "breakdown_us": {nm: round(float(np.mean([m[k].elapsed_time(m[k + 1]) * 1e3 for m in parts])), 2)
+                             for k, nm in enumerate(["score_select", "union_lists", "union_decode"])},
+            "alone_us": alone,
+            "union_rows_per_kv_head": round(float(uc.mean()), 1), "selected_per_head": int(kb),
+            "union_decode_gbps": round(dec_bytes / (alone["union_decode"] * 1e-6) / 1e9, 1),
+            "max_abs_diff_vs_sparse_decode": float((out_u - out).abs().max().item())}
+
+
 def main():
     args = parse()
     if args.traffic_from:
@@ -731,6 +815,10 @@ def main():
             reuse["mean_entries_per_list"] = round(float(ex_valid.float().mean().item()), 1)
             reuse["selected_per_list"] = int(kprev[0])
             extra["reuse"].append(reuse)
+        if mode == api.MODE_PER_HEAD:
+            extra["union"] = bench_union(torch, api, L, calls, warm, steps, Hq, Hkv, kmax, offs[-1], Kp, Vp, Pp, kip,
+                                         pref, scp, idp, cnp, wss, ws_ss_n, outp, out, ws_dec, dec_bytes, do_flush,
+                                         stream_of, chk, dev)
         # SnapKV prefill-end compression at LLaMA-3-70B layer shapes (64 / 8 heads, w = 32,
         # c = 4096, pool 3) over the same n, LLC flushed before each call
         sx = synth.config5(n0)

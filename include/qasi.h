@@ -54,6 +54,7 @@ extern "C" {
 
 #define QASI_MODE_VOTE 0
 #define QASI_MODE_PER_HEAD 1
+#define QASI_MODE_UNION 2      /* ts_decode_workspace_bytes only: the workspace of ts_union_decode */
 
 /* Selection parameters ([TS] "基本的な統合パターン", TokenSelectConfig).
  *   budget = budget_num / budget_den of the n_b cached tokens; the list length is
@@ -200,8 +201,10 @@ int ts_expand_selection(const int32_t* idx_prev, const int64_t* counts_prev_dev,
                         int64_t sink, int64_t local, int64_t radius, int32_t* idx_out, int64_t* caps_out,
                         int64_t* valid_out, void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* Workspace for ts_sparse_decode (counts_host = the per-sequence list lengths) and for
- * ts_dense_decode (counts_host = NULL). */
+/* Workspace for ts_sparse_decode (mode QASI_MODE_VOTE or QASI_MODE_PER_HEAD, counts_host = the
+ * per-sequence list lengths), for ts_union_decode (mode QASI_MODE_UNION, counts_host = the
+ * per-head list lengths) and for ts_dense_decode (counts_host = NULL).  0 if an argument is
+ * invalid. */
 size_t ts_decode_workspace_bytes(const int64_t* offsets_host, const int64_t* counts_host,
                                  int32_t B, int32_t Hq, int32_t Hkv, int32_t mode);
 
@@ -238,6 +241,50 @@ int ts_sparse_decode_noalloc(const uint16_t* q, const uint16_t* K, const uint16_
                              const int64_t* offsets_dev, const int64_t* offsets_host, const int32_t* idx,
                              const int64_t* counts_dev, const int64_t* counts_host, int32_t mode, int32_t B,
                              int32_t Hq, int32_t Hkv, float* out, hipStream_t stream);
+
+/* Workspace for ts_union_lists (0 if an argument is invalid). */
+size_t ts_union_workspace_bytes(const int64_t* offsets_host, int32_t B, int32_t Hkv);
+
+/* Per-KV-group union of per-head lists with a G-bit head mask ([TS] "主要な貢献": in per-head
+ * mode every query head selects its own tokens; the G = Hq/Hkv heads of a KV group read the same
+ * K/V rows, so their decode can gather the rows of the group's union once).  For sequence b and
+ * KV head g, with K_b = counts[b] and the heads h = g G + hh, hh < G:
+ *   U = the set union of the G lists' entries in [0, n_b) (negative entries are empty slots),
+ *   uidx[Hq kpre_b + g G K_b + j] = the j-th smallest token of U (j < |U|), then -1 up to G K_b,
+ *   umask[same]   = the byte with bit hh set when head g G + hh's list holds that token (0 past U),
+ *   ucount[b Hkv + g] = |U|,
+ * kpre_b = sum of the earlier counts (the layout of ts_select's per-head lists).
+ *   idx        device int32 per-head lists in ts_select's per-head layout, each list ascending
+ *              with its negative entries last (ts_select and ts_expand_selection produce such
+ *              lists; out-of-order lists give unspecified, in-bounds results)
+ *   counts     device (counts_dev) and host (counts_host) int64 [B], the same per-head lengths,
+ *              0 < count_b <= n_b
+ *   uidx       device int32 [Hq sum_b K_b];  umask device uint8, same shape;
+ *   ucount     device int64 [B][Hkv]
+ *   ws         device workspace of at least ts_union_workspace_bytes(offsets_host, B, Hkv) bytes.
+ * Hq/Hkv in {1, 2, 4, 8} (at most 8 mask bits).                                             */
+int ts_union_lists(const int32_t* idx, const int64_t* counts_dev, const int64_t* counts_host,
+                   const int64_t* offsets_dev, const int64_t* offsets_host, int32_t B, int32_t Hq,
+                   int32_t Hkv, int32_t* uidx, uint8_t* umask, int64_t* ucount, void* ws,
+                   size_t ws_bytes, hipStream_t stream);
+
+/* Decode attention of per-head selections read through their per-KV-group union (ts_union_lists'
+ * output): the result of ts_sparse_decode in per-head mode on the lists the union was built from
+ * (the same sets per head, summed in another order), with every K/V row of a group's union
+ * gathered once for the group's G heads; a head's score of a token outside its own list is
+ * -inf.
+ *   q, K, V, out  as for ts_sparse_decode
+ *   uidx, umask   device, ts_union_lists' layout; ucount device int64 [B][Hkv], each in
+ *                 [0, G count_b] (a larger value is taken as G count_b)
+ *   counts        device and host int64 [B]: the per-head list lengths the union was built from
+ *   ws            device workspace of at least ts_decode_workspace_bytes(offsets_host,
+ *                 counts_host, B, Hq, Hkv, QASI_MODE_UNION) bytes.
+ * A head whose list holds no token of [0, n_b) gets NaN (0/0).                           */
+int ts_union_decode(const uint16_t* q, const uint16_t* K, const uint16_t* V,
+                    const int64_t* offsets_dev, const int64_t* offsets_host, const int32_t* uidx,
+                    const uint8_t* umask, const int64_t* ucount, const int64_t* counts_dev,
+                    const int64_t* counts_host, int32_t B, int32_t Hq, int32_t Hkv, float* out,
+                    void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* Dense decode attention over all n_b tokens of each sequence (the comparison baseline,
  * [TS] eq. S_i = q . k_i / sqrt(d) for every cached token).  Same layouts as above.   */

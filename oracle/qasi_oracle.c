@@ -476,7 +476,8 @@ int64_t qo_snapkv_retain_clusters(const uint16_t* K, const uint16_t* V, int64_t 
  * count[b] = k_b).  For sequence b and KV head g, in the block of G*k_b entries at
  * uidx[Hq*kpre_b + g*G*k_b ...]: the tokens of the union of lists g*G .. g*G+G-1 in ascending
  * order, then -1; umask (same layout) has bit hh set when head g*G+hh selected the token (0 for
- * the padding); ucount[b*Hkv + g] = the union's size. */
+ * the padding); ucount[b*Hkv + g] = the union's size.  Entries outside [0, n_b) are empty slots
+ * (the -1 that pads an expanded list, qo_expand_selection) and join no union. */
 void qo_union_lists(const int32_t* idx, const int64_t* count, const int64_t* offsets, int B, int Hq, int Hkv,
                     int32_t* uidx, uint8_t* umask, int64_t* ucount) {
     const int G = Hq / Hkv;
@@ -488,7 +489,8 @@ void qo_union_lists(const int32_t* idx, const int64_t* count, const int64_t* off
             memset(mark, 0, (size_t)(n > 0 ? n : 1));
             for (int hh = 0; hh < G; ++hh) {
                 const int32_t* list = idx + (int64_t)Hq * kpre + (int64_t)(g * G + hh) * k;
-                for (int64_t j = 0; j < k; ++j) mark[list[j]] |= (uint8_t)(1u << hh);
+                for (int64_t j = 0; j < k; ++j)     /* entries outside [0, n) are empty slots */
+                    if (list[j] >= 0 && list[j] < n) mark[list[j]] |= (uint8_t)(1u << hh);
             }
             int32_t* uo = uidx + (int64_t)Hq * kpre + (int64_t)g * G * k;
             uint8_t* mo = umask + (int64_t)Hq * kpre + (int64_t)g * G * k;

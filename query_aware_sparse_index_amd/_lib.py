@@ -37,6 +37,10 @@ SIGNATURES = {
                                         _vp, _sz, _vp]),
     "ts_sparse_decode_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64p, _vp, _vp, _i64p, _i32, _i32, _i32, _i32,
                                                 _vp, _vp]),
+    "ts_union_workspace_bytes": (_sz, [_i64p, _i32, _i32]),
+    "ts_union_lists": (ctypes.c_int, [_vp, _vp, _i64p, _vp, _i64p, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "ts_union_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64p, _vp, _vp, _vp, _vp, _i64p, _i32, _i32, _i32, _vp,
+                                       _vp, _sz, _vp]),
     "ts_dense_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64p, _i32, _i32, _i32, _vp, _vp, _sz, _vp]),
     "snapkv_workspace_bytes": (_sz, [_i64, _i32, _i32, _i32, _i64]),
     "snapkv_compress": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _i32, _vp, _vp, _vp, _vp, _vp,

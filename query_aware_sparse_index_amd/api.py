@@ -15,6 +15,7 @@ from . import _lib
 
 MODE_VOTE = 0
 MODE_PER_HEAD = 1
+MODE_UNION = 2          # decode_workspace_bytes only: the workspace of union_decode
 
 
 class QasiError(RuntimeError):
@@ -223,6 +224,44 @@ def sparse_decode_noalloc(q, K, V, offs: Offsets, idx, counts_dev, counts_host, 
     _check(_lib.load().ts_sparse_decode_noalloc(_p(q), _p(K), _p(V), _p(offs.dev), offs.host, _p(idx),
                                                 _p(counts_dev), _host_i64(counts_host), int(mode), B, Hq, Hkv,
                                                 _p(out), _stream()))
+    return out
+
+
+def union_lists(idx, counts_dev, counts_host, offs: Offsets, Hq: int, Hkv: int, uidx=None, umask=None, ucount=None,
+                ws=None):
+    """ts_union_lists: per (sequence, KV head) the ascending union of the G per-head lists, the
+    per-entry head masks and the union sizes.  Returns (uidx, umask, ucount [B][Hkv])."""
+    dev = idx.device
+    total = int(Hq) * sum(int(c) for c in counts_host)
+    if uidx is None:
+        uidx = torch.empty(max(total, 4), dtype=torch.int32, device=dev)
+    if umask is None:
+        umask = torch.empty(max(total, 16), dtype=torch.uint8, device=dev)
+    if ucount is None:
+        ucount = torch.empty((offs.B, int(Hkv)), dtype=torch.int64, device=dev)
+    need = int(_lib.load().ts_union_workspace_bytes(offs.host, offs.B, int(Hkv)))
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _check(_lib.load().ts_union_lists(_p(idx), _p(counts_dev), _host_i64(counts_host), _p(offs.dev), offs.host, offs.B,
+                                      int(Hq), int(Hkv), _p(uidx), _p(umask), _p(ucount), _p(ws), ws.numel(),
+                                      _stream()))
+    return uidx[:total], umask[:total], ucount
+
+
+def union_decode(q, K, V, offs: Offsets, uidx, umask, ucount, counts_dev, counts_host, ws=None, out=None):
+    """ts_union_decode: the per-head decode of the lists a union was built from, each K/V row of
+    a group's union gathered once for its G heads."""
+    _bf16_check(q, K, V)
+    B, Hq, _ = q.shape
+    Hkv = K.shape[1]
+    if out is None:
+        out = torch.empty((B, Hq, 128), dtype=torch.float32, device=q.device)
+    need = decode_workspace_bytes(offs, counts_host, Hq, Hkv, MODE_UNION)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    _check(_lib.load().ts_union_decode(_p(q), _p(K), _p(V), _p(offs.dev), offs.host, _p(uidx), _p(umask), _p(ucount),
+                                       _p(counts_dev), _host_i64(counts_host), B, Hq, Hkv, _p(out), _p(ws),
+                                       ws.numel(), _stream()))
     return out
 
 

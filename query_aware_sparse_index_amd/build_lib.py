@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqasi.so")
-SOURCES = ["api.hip", "index_score.hip", "select.hip", "decode.hip", "snapkv.hip", "reuse.hip"]
+SOURCES = ["api.hip", "index_score.hip", "select.hip", "decode.hip", "snapkv.hip", "reuse.hip", "union.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          # packed fp32 instructions are kept out of the generated code

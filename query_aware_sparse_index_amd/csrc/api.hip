@@ -262,8 +262,10 @@ int ts_expand_selection(const int32_t* idx_prev, const int64_t* counts_prev_dev,
 
 size_t ts_decode_workspace_bytes(const int64_t* offsets_host, const int64_t* counts_host, int32_t B, int32_t Hq,
                                  int32_t Hkv, int32_t mode) {
-    if (!offsets_host || B <= 0 || Hq <= 0 || Hkv <= 0) return 0;
-    return qasi::decode_workspace(offsets_host, counts_host, B, Hq, Hkv, mode);
+    if (!offsets_host || B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv) return 0;
+    if (mode != QASI_MODE_VOTE && mode != QASI_MODE_PER_HEAD && mode != QASI_MODE_UNION) return 0;
+    if (mode == QASI_MODE_UNION && !counts_host) return 0;
+    return qasi::decode_workspace(offsets_host, counts_host, B, Hq, Hkv, mode == QASI_MODE_UNION ? 3 : mode);
 }
 
 int ts_sparse_decode(const uint16_t* q, const uint16_t* K, const uint16_t* V, const int64_t* offsets_dev,
@@ -316,6 +318,61 @@ int ts_sparse_decode_noalloc(const uint16_t* q, const uint16_t* K, const uint16_
     return hip_status(qasi::launch_sparse_decode_noalloc(q, K, V, offsets_dev, offsets_host, idx, counts_dev,
                                                          counts_host, mode, B, Hq, Hkv, out, stream),
                       "ts_sparse_decode_noalloc launch");
+}
+
+// Shared checks of per-sequence list lengths: host and device copies given, 0 < count_b <= n_b.
+static int check_counts(const int64_t* counts_dev, const int64_t* counts_host, const int64_t* offsets_host, int32_t B) {
+    if (!counts_dev || !counts_host || (reinterpret_cast<uintptr_t>(counts_dev) & 7u))
+        return fail(QASI_ERR_INVALID, "counts_dev / counts_host must be non-null (counts_dev 8-byte aligned)");
+    for (int b = 0; b < B; ++b) {
+        const int64_t n = offsets_host[b + 1] - offsets_host[b];
+        if (counts_host[b] < 1 || counts_host[b] > n)
+            return fail(QASI_ERR_INVALID, "counts[%d]=%lld outside [1, n_b=%lld]", b, (long long)counts_host[b], (long long)n);
+    }
+    return QASI_OK;
+}
+
+size_t ts_union_workspace_bytes(const int64_t* offsets_host, int32_t B, int32_t Hkv) {
+    if (!offsets_host || B <= 0 || Hkv <= 0) return 0;
+    return qasi::union_workspace(offsets_host, B, Hkv);
+}
+
+int ts_union_lists(const int32_t* idx, const int64_t* counts_dev, const int64_t* counts_host, const int64_t* offsets_dev,
+                   const int64_t* offsets_host, int32_t B, int32_t Hq, int32_t Hkv, int32_t* uidx, uint8_t* umask,
+                   int64_t* ucount, void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (!idx || (reinterpret_cast<uintptr_t>(idx) & 3u) || !uidx || (reinterpret_cast<uintptr_t>(uidx) & 3u))
+        return fail(QASI_ERR_INVALID, "idx and uidx must be non-null and 4-byte aligned");
+    if (!umask || !ucount || (reinterpret_cast<uintptr_t>(ucount) & 7u) || !aligned16(ws))
+        return fail(QASI_ERR_INVALID, "umask, ucount (8-byte aligned) and ws (16-byte aligned) must be non-null");
+    if (int r = check_heads(Hq, Hkv)) return r;
+    if (int r = check_offsets(offsets_dev, offsets_host, B, true)) return r;
+    if (int r = check_counts(counts_dev, counts_host, offsets_host, B)) return r;
+    const size_t need = qasi::union_workspace(offsets_host, B, Hkv);
+    if (ws_bytes < need) return fail(QASI_ERR_WORKSPACE, "ts_union_lists needs %zu workspace bytes, got %zu", need, ws_bytes);
+    if (int r = init_once()) return r;
+    return hip_status(qasi::launch_union(idx, counts_dev, counts_host, offsets_dev, offsets_host, B, Hq, Hkv, uidx,
+                                         umask, ucount, ws, ws_bytes, stream),
+                      "ts_union_lists launch");
+}
+
+int ts_union_decode(const uint16_t* q, const uint16_t* K, const uint16_t* V, const int64_t* offsets_dev,
+                    const int64_t* offsets_host, const int32_t* uidx, const uint8_t* umask, const int64_t* ucount,
+                    const int64_t* counts_dev, const int64_t* counts_host, int32_t B, int32_t Hq, int32_t Hkv,
+                    float* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (!aligned16(q) || !aligned16(K) || !aligned16(V) || !aligned16(out) || !aligned16(ws))
+        return fail(QASI_ERR_INVALID, "q, K, V, out and ws must be non-null and 16-byte aligned");
+    if (!uidx || (reinterpret_cast<uintptr_t>(uidx) & 3u) || !umask || !ucount ||
+        (reinterpret_cast<uintptr_t>(ucount) & 7u))
+        return fail(QASI_ERR_INVALID, "uidx (4-byte aligned), umask and ucount (8-byte aligned) must be non-null");
+    if (int r = check_heads(Hq, Hkv)) return r;
+    if (int r = check_offsets(offsets_dev, offsets_host, B, true)) return r;
+    if (int r = check_counts(counts_dev, counts_host, offsets_host, B)) return r;
+    const size_t need = qasi::decode_workspace(offsets_host, counts_host, B, Hq, Hkv, 3);
+    if (ws_bytes < need) return fail(QASI_ERR_WORKSPACE, "ts_union_decode needs %zu workspace bytes, got %zu", need, ws_bytes);
+    if (int r = init_once()) return r;
+    return hip_status(qasi::launch_union_decode(q, K, V, offsets_dev, offsets_host, uidx, umask, ucount, counts_dev,
+                                                counts_host, B, Hq, Hkv, out, ws, ws_bytes, stream),
+                      "ts_union_decode launch");
 }
 
 int ts_dense_decode(const uint16_t* q, const uint16_t* K, const uint16_t* V, const int64_t* offsets_dev,

@@ -38,12 +38,14 @@ constexpr float kLog2eOverSqrtD = 1.4426950408889634f / 11.313708498984761f;
 // query heads served by a wave
 __host__ __device__ constexpr int dec_gh(int G, int mode) { return mode == 1 ? 1 : G; }
 
-__device__ __forceinline__ bool find_list_chunk(const I64Arg& counts, int B, int64_t item, int EB, int& b,
+// lm: list entries per count (the union lists of a KV group hold G * count slots)
+__device__ __forceinline__ bool find_list_chunk(const I64Arg& counts, int B, int64_t item, int EB, int lm, int& b,
                                                 int64_t& j0, int64_t& len, int64_t& kpre) {
-    const SeqPos sp = wave_find_seq(B, item, (counts[0] + EB - 1) / EB, [cd = counts.dev, EB](int i) { return (cd[i] + EB - 1) / EB; });
+    const SeqPos sp = wave_find_seq(B, item, (lm * counts[0] + EB - 1) / EB,
+                                    [cd = counts.dev, EB, lm](int i) { return (lm * cd[i] + EB - 1) / EB; });
     if (sp.b < 0) return false;
     b = sp.b;
-    const int64_t n = counts[b];
+    const int64_t n = lm * counts[b];
     j0 = (item - sp.first) * EB;
     len = n - j0 < EB ? n - j0 : EB;
     kpre = wave_prefix_seq(b, [cd = counts.dev](int i) { return cd[i]; });
@@ -139,7 +141,10 @@ __device__ __forceinline__ void rows_tsum(const float (&v)[NA], float (&o)[NA / 
 }
 
 // MODE 0: shared list per sequence (vote); MODE 1: list per query head; MODE 2: dense
-// (the list is implicit: entry j is token j, counts are the sequence lengths).
+// (the list is implicit: entry j is token j, counts are the sequence lengths); MODE 3: the union
+// of a KV group's per-head lists (G * count slots per (sequence, KV head), padded with -1) with a
+// per-entry mask of the heads that selected the token: each gathered row is read once for the
+// group and a head's score of an entry it did not select is -inf.
 // Blocks per CU to keep: 3 (12 waves) for the shared-list modes with G <= 4, whose registers fit
 // in 168 (512 / 3) per lane; no bound otherwise.
 __host__ __device__ constexpr int dec_min_blocks(int G, int mode) { return (mode != 1 && G <= 4) ? 3 : 1; }
@@ -152,7 +157,9 @@ __global__ __launch_bounds__(kDecWaves * 64, dec_min_blocks(G, MODE)) void decod
                                                                        const int32_t* __restrict__ idx,
                                                                        I64Arg counts, int B, int Hq,
                                                                        int Hkv, int EB, float* __restrict__ part_acc,
-                                                                       float2* __restrict__ part_ml) {
+                                                                       float2* __restrict__ part_ml,
+                                                                       const uint8_t* __restrict__ umask,
+                                                                       const int64_t* __restrict__ ucount) {
     constexpr int GH = dec_gh(G, MODE);
     constexpr int EPR = kDecSub / 4;               // entries per lane row and sub-batch
     constexpr int NV = GH * EPR;                   // (head, entry) scores of a row
@@ -166,6 +173,7 @@ __global__ __launch_bounds__(kDecWaves * 64, dec_min_blocks(G, MODE)) void decod
     __shared__ float s_m[kDecWaves][GH], s_l[kDecWaves][GH];
     __shared__ float4 s_p[kDecWaves][4][NV / 4];
     __shared__ int4 s_tok[kDecWaves][kDecMaxEW / 4];
+    __shared__ uint32_t s_msk[(MODE == 3) ? kDecWaves : 1][(MODE == 3) ? kDecMaxEW / 4 : 1];   // union: head masks
 
     const int HW = (MODE == 1) ? Hq : Hkv;
     int64_t item;
@@ -184,14 +192,25 @@ __global__ __launch_bounds__(kDecWaves * 64, dec_min_blocks(G, MODE)) void decod
     }
     int b;
     int64_t j0, len, kpre;
-    if (!find_list_chunk(counts, B, item, EB, b, j0, len, kpre)) return;
+    constexpr int LM = (MODE == 3) ? G : 1;
+    if (!find_list_chunk(counts, B, item, EB, LM, b, j0, len, kpre)) return;
     const int64_t off = offsets[b];
     const int32_t nmax = (int32_t)(offsets[b + 1] - off - 1);   // list entries are clamped to [0, n_b)
     const int g = (MODE == 1) ? hw / G : hw;
     const int hbase = (MODE == 1) ? hw : hw * G;                 // first query head of the wave
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     const int row = lane >> 4, p = lane & 15;
-    const int EW = EB / kDecWaves;
+    if (MODE == 3) {
+        // the union's size is known on the device only: its entries are split evenly over the
+        // group's ceil(G K / EB) ranges (at most EB each), so that every block has work
+        const int64_t cap = (int64_t)G * counts[b];
+        int64_t uc = ucount[(int64_t)b * Hkv + hw];
+        uc = uc < 0 ? 0 : (uc > cap ? cap : uc);
+        const int64_t nch = (cap + EB - 1) / EB, c = j0 / EB;
+        j0 = uc * c / nch;
+        len = uc * (c + 1) / nch - j0;
+    }
+    const int EW = (MODE == 3) ? (int)((len + kDecWaves - 1) / kDecWaves) : EB / kDecWaves;
     const int64_t wb = (int64_t)wid * EW;
     const int wlen = len <= wb ? 0 : (len - wb < EW ? (int)(len - wb) : EW);
     const int nsb = (wlen + kDecSub - 1) / kDecSub;
@@ -201,16 +220,26 @@ __global__ __launch_bounds__(kDecWaves * 64, dec_min_blocks(G, MODE)) void decod
     // entries are empty slots (-1): their rows are read at position 0 and their scores are -inf
     int32_t* tok = reinterpret_cast<int32_t*>(&s_tok[wid][0]);
     {
+        // the list of this block: the sequence's (vote), the head's (per-head), the KV group's (union)
+        const int64_t lbase = (MODE == 1) ? Hq * kpre + (int64_t)hw * counts[b]
+                                          : ((MODE == 3) ? Hq * kpre + (int64_t)hw * G * counts[b] : kpre);
         int32_t t0 = 0;
         if (wlen > 0) {
             const int64_t j = j0 + wb;
-            t0 = (MODE == 2) ? (int32_t)j : ((MODE == 1) ? idx[Hq * kpre + (int64_t)hw * counts[b] + j] : idx[kpre + j]);
+            t0 = (MODE == 2) ? (int32_t)j : idx[lbase + j];
         }
+        uint8_t* msk = (MODE == 3) ? reinterpret_cast<uint8_t*>(&s_msk[wid][0]) : nullptr;
         for (int i = lane; i < nsb * kDecSub; i += 64) {
             int32_t t = t0;
+            uint8_t mb = 0;
             if (i < wlen) {
                 const int64_t j = j0 + wb + i;
-                t = (MODE == 2) ? (int32_t)j : ((MODE == 1) ? idx[Hq * kpre + (int64_t)hw * counts[b] + j] : idx[kpre + j]);
+                t = (MODE == 2) ? (int32_t)j : idx[lbase + j];
+                if (MODE == 3) mb = umask[lbase + j];
+            }
+            if (MODE == 3) {
+                msk[i] = mb;
+                if (i < wlen && mb == 0) t = -1;          // no head selected it: an empty slot
             }
             tok[i] = t < 0 ? -1 : (t > nmax ? nmax : t);
         }
@@ -224,8 +253,9 @@ __global__ __launch_bounds__(kDecWaves * 64, dec_min_blocks(G, MODE)) void decod
     const uint16_t* Vg = V + (off * Hkv + g) * kD + p * 8;
     const int64_t rstride = (int64_t)Hkv * kD;
     // em: bit k set when entry k of the lane's row is an empty slot
-    auto issue = [&](int sb, uint4 (&kb)[EPR], uint4 (&vb)[EPR], int& em) {
+    auto issue = [&](int sb, uint4 (&kb)[EPR], uint4 (&vb)[EPR], int& em, uint32_t& hm) {
         const int4 t = s_tok[wid][(sb * kDecSub + row * EPR) / 4];
+        if (MODE == 3) hm = s_msk[wid][(sb * kDecSub + row * EPR) / 4];
         const int tt[4] = {t.x < 0 ? 0 : t.x, t.y < 0 ? 0 : t.y, t.z < 0 ? 0 : t.z, t.w < 0 ? 0 : t.w};
         em = (t.x < 0 ? 1 : 0) | (t.y < 0 ? 2 : 0) | (t.z < 0 ? 4 : 0) | (t.w < 0 ? 8 : 0);
 #pragma unroll
@@ -245,7 +275,7 @@ __global__ __launch_bounds__(kDecWaves * 64, dec_min_blocks(G, MODE)) void decod
     float4* sp4 = &s_p[wid][row][0];
     float* sp = reinterpret_cast<float*>(sp4);
 
-    auto compute = [&](int sb, const uint4 (&kb)[EPR], const uint4 (&vb)[EPR], int em) {
+    auto compute = [&](int sb, const uint4 (&kb)[EPR], const uint4 (&vb)[EPR], int em, uint32_t hm) {
         float zp[NV];
 #pragma unroll
         for (int k = 0; k < EPR; ++k)
@@ -263,7 +293,9 @@ __global__ __launch_bounds__(kDecWaves * 64, dec_min_blocks(G, MODE)) void decod
         for (int s = 0; s < FV; ++s) {
             const int ke = (i0 + s) % EPR;
             const int e = sb * kDecSub + row * EPR + ke;
-            z[s] = (e < wlen && !((em >> ke) & 1)) ? z[s] * kLog2eOverSqrtD : -INFINITY;
+            bool use = e < wlen && !((em >> ke) & 1);
+            if (MODE == 3) use = use && ((hm >> (8 * ke + (i0 + s) / EPR)) & 1u);   // the head selected it
+            z[s] = use ? z[s] * kLog2eOverSqrtD : -INFINITY;
             mx = fmaxf(mx, z[s]);
         }
         const float m_new = fmaxf(m_run, head_reduce<true, HS0, HS1>(mx));
@@ -313,12 +345,13 @@ __global__ __launch_bounds__(kDecWaves * 64, dec_min_blocks(G, MODE)) void decod
     // two register sets: A = even sub-batches, B = odd
     uint4 ka[EPR], va[EPR], kb2[EPR], vb2[EPR];
     int ema = 0, emb = 0;
-    if (nsb > 0) issue(0, ka, va, ema);
+    uint32_t hma = 0, hmb = 0;
+    if (nsb > 0) issue(0, ka, va, ema, hma);
     for (int sb = 0; sb < nsb; sb += 2) {
-        if (sb + 1 < nsb) issue(sb + 1, kb2, vb2, emb);
-        compute(sb, ka, va, ema);
-        if (sb + 2 < nsb) issue(sb + 2, ka, va, ema);
-        if (sb + 1 < nsb) compute(sb + 1, kb2, vb2, emb);
+        if (sb + 1 < nsb) issue(sb + 1, kb2, vb2, emb, hmb);
+        compute(sb, ka, va, ema, hma);
+        if (sb + 2 < nsb) issue(sb + 2, ka, va, ema, hma);
+        if (sb + 1 < nsb) compute(sb + 1, kb2, vb2, emb, hmb);
     }
 
     // sum over the 4 rows: row r holds accumulator indices r * NA / 4 + j
@@ -360,14 +393,14 @@ __global__ __launch_bounds__(kDecWaves * 64, dec_min_blocks(G, MODE)) void decod
 constexpr int kMergeThreads = 1024;
 __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const float* __restrict__ part_acc,
                                                                     const float2* __restrict__ part_ml,
-                                                                    I64Arg counts, int B, int Hq, int EB,
+                                                                    I64Arg counts, int B, int Hq, int EB, int lm,
                                                                     float* __restrict__ out) {
     constexpr int NG = kMergeThreads / kD, U = 16;
     __shared__ float sM[NG], sL[NG];
     __shared__ float sA[NG][kD];
     const int bh = blockIdx.x, b = bh / Hq, h = bh % Hq;
-    const int64_t first = wave_prefix_seq(b, [cd = counts.dev, EB](int i) { return (cd[i] + EB - 1) / EB; });
-    const int64_t nch = (counts[b] + EB - 1) / EB;
+    const int64_t first = wave_prefix_seq(b, [cd = counts.dev, EB, lm](int i) { return (lm * cd[i] + EB - 1) / EB; });
+    const int64_t nch = (lm * counts[b] + EB - 1) / EB;
     const int cg = threadIdx.x / kD, d = threadIdx.x % kD;
     float M = -INFINITY, A = 0.f, L = 0.f;
     for (int64_t c0 = cg; c0 < nch; c0 += (int64_t)NG * U) {
@@ -388,8 +421,9 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const float
             ll[u] = ml[u].y;
         }
         // no branch on Mn: the compiler would move the x and l loads into it, behind the wait
-        // for the maxima.  Only the clamped slots past the list's end have m = -inf (every chunk
-        // holds entries), and their weights are 0; while Mn = -inf, A and L stay 0.
+        // for the maxima.  Slots with m = -inf (the clamped slots past the list's end, and in the
+        // union decode the ranges in which the head selected nothing) have weight 0 and A = L = 0;
+        // while Mn = -inf, A and L stay 0.
         float Mn = M;
 #pragma unroll
         for (int u = 0; u < U; ++u) Mn = fmaxf(Mn, mm[u]);
@@ -422,9 +456,10 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const float
     }
 }
 
-static int64_t list_items(const int64_t* counts_host, int B, int EB) {
+// ranges of EB entries over the lists (lm entries per count: G for the union lists)
+static int64_t list_items(const int64_t* counts_host, int B, int EB, int lm) {
     int64_t it = 0;
-    for (int b = 0; b < B; ++b) it += (counts_host[b] + EB - 1) / EB;
+    for (int b = 0; b < B; ++b) it += (lm * counts_host[b] + EB - 1) / EB;
     return it;
 }
 
@@ -452,11 +487,12 @@ static const void* partial_fn(int G) {
 }
 // Resident blocks per compute unit of an instantiation (queried once).
 static int partial_blocks_per_cu(int G, int mode) {
-    static int cache[3][4] = {};
+    static int cache[4][4] = {};
     const int lg = G == 1 ? 0 : (G == 2 ? 1 : (G == 4 ? 2 : 3));
     int& c = cache[mode][lg];
     if (c == 0) {
-        const void* f = mode == 0 ? partial_fn<0>(G) : (mode == 1 ? partial_fn<1>(G) : partial_fn<2>(G));
+        const void* f = mode == 0 ? partial_fn<0>(G)
+                                  : (mode == 1 ? partial_fn<1>(G) : (mode == 2 ? partial_fn<2>(G) : partial_fn<3>(G)));
         int n = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, kDecWaves * 64, 0) != hipSuccess || n <= 0) n = 2;
         c = n;
@@ -478,7 +514,7 @@ static int decode_eb(Len len, int B, int HW, int G, int mode) {
     const int64_t target = (int64_t)partial_blocks_per_cu(G, mode) * device_cus();
     int64_t entries = 0;
     for (int b = 0; b < B; ++b) entries += len(b);
-    const int64_t lo = kDecWaves * kDecSub, hi = kDecWaves * (mode == 0 ? kDecMaxEW : (mode == 1 ? 64 : 256));
+    const int64_t lo = kDecWaves * kDecSub, hi = kDecWaves * (mode == 1 ? 64 : (mode == 2 ? 256 : kDecMaxEW));
     auto clampr = [&](int64_t e) {
         e = (e + 3) / 4 * 4;
         return e < lo ? lo : (e > hi ? hi : e);
@@ -489,18 +525,18 @@ static int decode_eb(Len len, int B, int HW, int G, int mode) {
         for (int b = 0; b < B; ++b) it += (len(b) + e - 1) / e;
         return it * HW;
     };
-    if (mode == 0)
+    if (mode == 0 || mode == 3)
         while (eb < hi && blocks(eb) > target) eb = clampr(eb + (eb + 15) / 16);
     return (int)eb;
 }
 
 // Workspace: the partials of at most sum_b ceil(K_b / EB) <= sum_b K_b / (kDecWaves kDecSub) + B
-// ranges (EB never falls below kDecWaves kDecSub), a bound that grows with the list lengths.
+// ranges (EB never falls below kDecWaves kDecSub; K_b is G times the count for the union lists),
+// a bound that grows with the list lengths.
 size_t decode_workspace(const int64_t* offsets_host, const int64_t* counts_host, int B, int Hq, int Hkv, int mode) {
-    (void)Hkv;
-    (void)mode;
+    const int lm = mode == 3 ? Hq / Hkv : 1;
     int64_t total = 0;
-    for (int b = 0; b < B; ++b) total += counts_host ? counts_host[b] : offsets_host[b + 1] - offsets_host[b];
+    for (int b = 0; b < B; ++b) total += counts_host ? lm * counts_host[b] : offsets_host[b + 1] - offsets_host[b];
     const int64_t items = (total + kDecWaves * kDecSub - 1) / (kDecWaves * kDecSub) + B;
     WsCarver w(nullptr);
     w.take<int64_t>((size_t)B + 1);   // dense: per-sequence lengths
@@ -512,13 +548,14 @@ size_t decode_workspace(const int64_t* offsets_host, const int64_t* counts_host,
 template <int MODE>
 static hipError_t launch_partial_G(int G, dim3 grid, hipStream_t stream, const uint16_t* q, const uint16_t* K,
                                    const uint16_t* V, const I64Arg& offsets, const int32_t* idx,
-                                   const I64Arg& counts, int B, int Hq, int Hkv, int EB, float* part, float2* ml) {
+                                   const I64Arg& counts, int B, int Hq, int Hkv, int EB, float* part, float2* ml,
+                                   const uint8_t* umask = nullptr, const int64_t* ucount = nullptr) {
     const dim3 block(kDecWaves * 64);
     switch (G) {
-        case 1: hipLaunchKernelGGL((decode_partial_kernel<1, MODE>), grid, block, 0, stream, q, K, V, offsets, idx, counts, B, Hq, Hkv, EB, part, ml); break;
-        case 2: hipLaunchKernelGGL((decode_partial_kernel<2, MODE>), grid, block, 0, stream, q, K, V, offsets, idx, counts, B, Hq, Hkv, EB, part, ml); break;
-        case 4: hipLaunchKernelGGL((decode_partial_kernel<4, MODE>), grid, block, 0, stream, q, K, V, offsets, idx, counts, B, Hq, Hkv, EB, part, ml); break;
-        case 8: hipLaunchKernelGGL((decode_partial_kernel<8, MODE>), grid, block, 0, stream, q, K, V, offsets, idx, counts, B, Hq, Hkv, EB, part, ml); break;
+        case 1: hipLaunchKernelGGL((decode_partial_kernel<1, MODE>), grid, block, 0, stream, q, K, V, offsets, idx, counts, B, Hq, Hkv, EB, part, ml, umask, ucount); break;
+        case 2: hipLaunchKernelGGL((decode_partial_kernel<2, MODE>), grid, block, 0, stream, q, K, V, offsets, idx, counts, B, Hq, Hkv, EB, part, ml, umask, ucount); break;
+        case 4: hipLaunchKernelGGL((decode_partial_kernel<4, MODE>), grid, block, 0, stream, q, K, V, offsets, idx, counts, B, Hq, Hkv, EB, part, ml, umask, ucount); break;
+        case 8: hipLaunchKernelGGL((decode_partial_kernel<8, MODE>), grid, block, 0, stream, q, K, V, offsets, idx, counts, B, Hq, Hkv, EB, part, ml, umask, ucount); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -540,7 +577,7 @@ hipError_t launch_sparse_decode(const uint16_t* q, const uint16_t* K, const uint
     const int EB = decode_eb([&](int b) { return counts_host[b]; }, B, mode == 1 ? Hq : Hkv, G, mode);
     WsCarver w(ws);
     w.take<int64_t>((size_t)B + 1);
-    const int64_t items = list_items(counts_host, B, EB);
+    const int64_t items = list_items(counts_host, B, EB, 1);
     float* part = w.take<float>((size_t)items * Hq * kD);
     float2* ml = w.take<float2>((size_t)items * Hq);
     const I64Arg offs = i64_arg(offsets_dev, offsets_host, (int64_t)B + 1);
@@ -555,7 +592,29 @@ hipError_t launch_sparse_decode(const uint16_t* q, const uint16_t* K, const uint
         e = launch_partial_G<1>(G, dim3((unsigned)(pairs * G)), stream, q, K, V, offs, idx, cnts, B, Hq, Hkv, EB, part, ml);
     }
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_merge_kernel, dim3(B * Hq), dim3(kMergeThreads), 0, stream, part, ml, cnts, B, Hq, EB, out);
+    hipLaunchKernelGGL(decode_merge_kernel, dim3(B * Hq), dim3(kMergeThreads), 0, stream, part, ml, cnts, B, Hq, EB, 1, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_union_decode(const uint16_t* q, const uint16_t* K, const uint16_t* V, const int64_t* offsets_dev,
+                               const int64_t* offsets_host, const int32_t* uidx, const uint8_t* umask,
+                               const int64_t* ucount, const int64_t* counts_dev, const int64_t* counts_host, int B,
+                               int Hq, int Hkv, float* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (decode_workspace(offsets_host, counts_host, B, Hq, Hkv, 3) > ws_bytes) return hipErrorInvalidValue;
+    const int G = Hq / Hkv;
+    const int EB = decode_eb([&](int b) { return G * counts_host[b]; }, B, Hkv, G, 3);
+    WsCarver w(ws);
+    w.take<int64_t>((size_t)B + 1);
+    const int64_t items = list_items(counts_host, B, EB, G);
+    float* part = w.take<float>((size_t)items * Hq * kD);
+    float2* ml = w.take<float2>((size_t)items * Hq);
+    const I64Arg offs = i64_arg(offsets_dev, offsets_host, (int64_t)B + 1);
+    const I64Arg cnts = i64_arg(counts_dev, counts_host, B);
+    if (items == 0) return hipSuccess;
+    hipError_t e = launch_partial_G<3>(G, dim3((unsigned)(items * Hkv)), stream, q, K, V, offs, uidx, cnts, B, Hq, Hkv,
+                                       EB, part, ml, umask, ucount);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(decode_merge_kernel, dim3(B * Hq), dim3(kMergeThreads), 0, stream, part, ml, cnts, B, Hq, EB, G, out);
     return hipGetLastError();
 }
 
@@ -623,7 +682,7 @@ hipError_t launch_dense_decode(const uint16_t* q, const uint16_t* K, const uint1
     hipError_t e = launch_partial_G<2>(G, dim3((unsigned)(items * Hkv)), stream, q, K, V, offs, nullptr, lns, B, Hq,
                                        Hkv, EB, part, ml);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_merge_kernel, dim3(B * Hq), dim3(kMergeThreads), 0, stream, part, ml, lns, B, Hq, EB, out);
+    hipLaunchKernelGGL(decode_merge_kernel, dim3(B * Hq), dim3(kMergeThreads), 0, stream, part, ml, lns, B, Hq, EB, 1, out);
     return hipGetLastError();
 }
 

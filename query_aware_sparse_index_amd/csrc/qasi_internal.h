@@ -86,7 +86,14 @@ hipError_t launch_expand(const int32_t* prev, const int64_t* counts_prev_dev, co
                          int64_t local, int64_t radius, int32_t* out, int64_t* caps_out, int64_t* valid_out,
                          uint32_t* chunk_counts, hipStream_t stream);
 
+// ---- per-KV-group union of per-head lists with head masks
+size_t union_workspace(const int64_t* offsets_host, int B, int Hkv);
+hipError_t launch_union(const int32_t* idx, const int64_t* counts_dev, const int64_t* counts_host,
+                        const int64_t* offsets_dev, const int64_t* offsets_host, int B, int Hq, int Hkv, int32_t* uidx,
+                        uint8_t* umask, int64_t* ucount, void* ws, size_t ws_bytes, hipStream_t stream);
+
 // ---- decode
+// mode: 0 vote lists, 1 per-head lists, 2 dense (counts_host NULL), 3 union lists (G*count_b slots)
 size_t decode_workspace(const int64_t* offsets_host, const int64_t* counts_host, int B, int Hq, int Hkv, int mode);
 hipError_t launch_sparse_decode(const uint16_t* q, const uint16_t* K, const uint16_t* V, const int64_t* offsets_dev,
                                 const int64_t* offsets_host, const int32_t* idx, const int64_t* counts_dev,
@@ -100,6 +107,12 @@ hipError_t launch_sparse_decode_noalloc(const uint16_t* q, const uint16_t* K, co
                                         const int64_t* offsets_dev, const int64_t* offsets_host, const int32_t* idx,
                                         const int64_t* counts_dev, const int64_t* counts_host, int mode, int B, int Hq,
                                         int Hkv, float* out, hipStream_t stream);
+// Union decode: per (sequence, KV head) the union list (G*count_b slots) with its per-entry head
+// masks and its size on the device (the output of launch_union); mode 3 of decode_workspace.
+hipError_t launch_union_decode(const uint16_t* q, const uint16_t* K, const uint16_t* V, const int64_t* offsets_dev,
+                               const int64_t* offsets_host, const int32_t* uidx, const uint8_t* umask,
+                               const int64_t* ucount, const int64_t* counts_dev, const int64_t* counts_host, int B,
+                               int Hq, int Hkv, float* out, void* ws, size_t ws_bytes, hipStream_t stream);
 hipError_t launch_dense_decode(const uint16_t* q, const uint16_t* K, const uint16_t* V, const int64_t* offsets_dev,
                                const int64_t* offsets_host, int B, int Hq, int Hkv, float* out, void* ws,
                                size_t ws_bytes, hipStream_t stream);

@@ -108,8 +108,19 @@ int main(void) {
     EXPECT(ts_sparse_decode_noalloc(M, F, F, F, o1000, F, F, c100, 0, 1, 32, 8, F, NULL), -1);
     EXPECT(ts_sparse_decode_noalloc(F, F, F, F, o1000, F, F, c100, 0, 1, 24, 8, F, NULL), -2);
     EXPECT(ts_dense_decode(F, M, F, F, o1000, 1, 32, 8, F, F, (size_t)1 << 40, NULL), -1);
-    EXPECT(ts_dense_decode(F, F, F, F, o1000, 1, 32, 8, F, F, ts_decode_workspace_bytes(o1000, NULL, 1, 32, 8, 2) - 1,
+    EXPECT(ts_dense_decode(F, F, F, F, o1000, 1, 32, 8, F, F, ts_decode_workspace_bytes(o1000, NULL, 1, 32, 8, 0) - 1,
                            NULL), -3);
+
+    /* per-KV-group union and its decode */
+    const size_t uw = ts_union_workspace_bytes(o1000, 1, 8);
+    EXPECT(ts_union_lists(NULL, F, c100, F, o1000, 1, 32, 8, F, F, F, F, uw, NULL), -1);
+    EXPECT(ts_union_lists(F, F, c1001, F, o1000, 1, 32, 8, F, F, F, F, uw, NULL), -1);
+    EXPECT(ts_union_lists(F, F, c100, F, o1000, 1, 48, 4, F, F, F, F, uw, NULL), -2);
+    EXPECT(ts_union_lists(F, F, c100, F, o1000, 1, 32, 8, F, F, F, F, uw - 1, NULL), -3);
+    const size_t udw = ts_decode_workspace_bytes(o1000, c100, 1, 32, 8, QASI_MODE_UNION);
+    EXPECT(ts_union_decode(F, F, F, F, o1000, F, F, F, F, c0, 1, 32, 8, F, F, udw, NULL), -1);
+    EXPECT(ts_union_decode(F, F, F, F, o1000, F, F, F, F, c100, 1, 24, 8, F, F, udw, NULL), -2);
+    EXPECT(ts_union_decode(F, F, F, F, o1000, F, F, F, F, c100, 1, 32, 8, F, F, udw - 1, NULL), -3);
 
     /* SnapKV */
     EXPECT(snapkv_compress(F, F, F, 1000, 32, 64, 8, 4096, 5, F, F, F, NULL, NULL, F, (size_t)1 << 40, NULL), -2);

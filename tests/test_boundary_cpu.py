@@ -22,7 +22,7 @@ def header_functions():
 def test_exports_match_header():
     lib = _lib.load()
     names = header_functions()
-    assert len(names) == 21, names
+    assert len(names) == 24, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.SIGNATURES)
@@ -179,3 +179,34 @@ def test_snapkv_validation():
     a = list(args(1000, 32, 64, 8, 4096, 3))
     a[-2] = need - 1
     assert L.snapkv_compress(*a) == -3
+
+
+def test_union_validation():
+    """ts_union_lists / ts_union_decode reject bad pointers, head layouts, counts and short
+    workspaces before any HIP call; the union decode's workspace query needs the counts."""
+    L = _lib.load()
+    o = _offs([0, 10000])
+    c_ok, c_bad0, c_big = _offs([2000]), _offs([0]), _offs([10001])
+    ws = 1 << 40
+    u = lambda idx, ch, Hq, Hkv, uidx, um, uc, w, wsn: L.ts_union_lists(idx, FAKE, ch, FAKE, o, 1, Hq, Hkv, uidx, um,
+                                                                       uc, w, wsn, None)
+    assert u(None, c_ok, 32, 8, FAKE, FAKE, FAKE, FAKE, ws) == -1
+    assert u(FAKE, c_ok, 32, 8, MIS, FAKE, FAKE, FAKE, ws) == -1
+    assert u(FAKE, c_ok, 32, 8, FAKE, FAKE, MIS, FAKE, ws) == -1
+    assert u(FAKE, c_bad0, 32, 8, FAKE, FAKE, FAKE, FAKE, ws) == -1
+    assert u(FAKE, c_big, 32, 8, FAKE, FAKE, FAKE, FAKE, ws) == -1
+    assert u(FAKE, c_ok, 48, 4, FAKE, FAKE, FAKE, FAKE, ws) == -2          # G = 12 > 8 mask bits
+    need = L.ts_union_workspace_bytes(o, 1, 8)
+    assert need > 0 and L.ts_union_workspace_bytes(o, 0, 8) == 0
+    assert u(FAKE, c_ok, 32, 8, FAKE, FAKE, FAKE, FAKE, need - 1) == -3
+    assert "workspace" in err()
+    d = lambda ch, Hq, Hkv, uidx, wsn: L.ts_union_decode(FAKE, FAKE, FAKE, FAKE, o, uidx, FAKE, FAKE, FAKE, ch, 1, Hq,
+                                                         Hkv, FAKE, FAKE, wsn, None)
+    assert d(c_ok, 32, 8, None, ws) == -1
+    assert d(c_bad0, 32, 8, FAKE, ws) == -1
+    assert d(c_ok, 24, 8, FAKE, ws) == -2
+    assert L.ts_decode_workspace_bytes(o, None, 1, 32, 8, 2) == 0           # union mode needs the counts
+    assert L.ts_decode_workspace_bytes(o, c_ok, 1, 32, 8, 7) == 0
+    need_u = L.ts_decode_workspace_bytes(o, c_ok, 1, 32, 8, 2)
+    assert need_u > L.ts_decode_workspace_bytes(o, c_ok, 1, 32, 8, 1)      # G * count slots per group
+    assert d(c_ok, 32, 8, FAKE, need_u - 1) == -3

@@ -613,3 +613,25 @@ def test_union_lists_special_cases():
     assert np.array_equal(umask, np.tile(1 << np.arange(Hq), k).astype(np.uint8))
     uidx, umask, ucount = O.union_lists(dis, np.array([k]), offs, Hq, Hq)
     assert np.array_equal(uidx, dis) and np.all(umask == 1) and np.all(ucount == k)
+
+
+def test_union_lists_empty_slots():
+    """Lists padded with -1 (the empty slots of expanded lists) contribute only their tokens: the
+    union equals that of the lists cut at their first -1; a list of empty slots only adds nothing."""
+    n, k, Hq = 300, 40, 4
+    offs = np.array([0, n], np.int64)
+    rng = np.random.default_rng(11)
+    valid = [25, 40, 0, 7]
+    lists = []
+    for v in valid:
+        l = np.full(k, -1, np.int32)
+        l[:v] = np.sort(rng.choice(n, size=v, replace=False))
+        lists.append(l)
+    uidx, umask, ucount = O.union_lists(np.concatenate(lists), np.array([k]), offs, Hq, 1)
+    want = sorted(set().union(*[set(l[:v].tolist()) for l, v in zip(lists, valid)]))
+    c = int(ucount[0, 0])
+    assert c == len(want) and uidx[:c].tolist() == want
+    for j, t in enumerate(want):
+        assert umask[j] == sum(1 << h for h in range(Hq) if t in set(lists[h][:valid[h]].tolist()))
+    assert not any(umask[j] & 4 for j in range(c))          # head 2 holds only empty slots
+    assert np.all(uidx[c:] == -1) and np.all(umask[c:] == 0)

@@ -14,12 +14,13 @@ import subprocess
 
 import pytest
 
+from query_aware_sparse_index_amd.build_lib import SOURCES   # every source file of the library
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SAN = os.path.join(ROOT, "tests", "sanitize")
 CSRC = os.path.join(ROOT, "query_aware_sparse_index_amd", "csrc")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CLANG = "/opt/rocm/llvm/bin/clang"
-SOURCES = ["api.hip", "index_score.hip", "select.hip", "decode.hip", "snapkv.hip", "reuse.hip"]
 ENV = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=0", UBSAN_OPTIONS="print_stacktrace=1")
 
 
