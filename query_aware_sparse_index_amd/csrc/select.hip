@@ -1122,10 +1122,10 @@ __global__ __launch_bounds__(kPhWaves * 64) void ph_compact_kernel(const float* 
 // ------------------------------------------------------- fused path: order statistic
 // th_final2_kernel, one block per instance (sequence b, head h), after prep_kernel and the score
 // kernel's tile classification (records [h][tile] of the sequence's tiles):
-//   1. loads the records of its tiles (thread t: kF2Per consecutive tiles) with the tiles' first
-//      in-bracket keys (head-major slots, when the sequence fits one round) and sums the counts
-//      below and inside the bracket; the target rank r lies inside when
-//      #below < r <= #below + #inside;
+//   1. loads the records of its tiles with the tiles' first in-bracket keys (head-major slots,
+//      when the sequence fits one round; a pair of lanes per tile, eight slots each, so that a
+//      wave's loads read consecutive tiles) and sums the counts below and inside the bracket; the
+//      target rank r lies inside when #below < r <= #below + #inside;
 //   2. counts the in-bracket keys per top digit (kDigit bits of key - lo) in LDS, straight from
 //      the registers (the rare keys past a tile's slots are read into LDS first), finds the
 //      answer's digit and ranks that digit's keys, picked from the registers again (one wave when
@@ -1138,7 +1138,8 @@ __global__ __launch_bounds__(kPhWaves * 64) void ph_compact_kernel(const float* 
 constexpr int kF2Threads = 512;
 constexpr int kF2Per = 5;                                  // consecutive tiles per thread per round
 constexpr int kF2Round = kF2Threads * kF2Per;              // tiles per round (163840 tokens)
-constexpr int kF2Cap = 24576;                              // keys ranked in LDS
+constexpr int kF2Cap = 20480;                              // in-bracket keys held in LDS
+constexpr int kF2Batch = 8;                                // LDS keys read per thread before use
 
 struct F2Args {
     const uint32_t* tinfo;   // [Hq][ntiles] below | inside << 8 | offset << 16
@@ -1467,10 +1468,14 @@ __global__ __launch_bounds__(kF2Threads) void th_final2_kernel(const float* __re
                                                               int Hq, DevCfg cfg, int64_t S, F2Args a,
                                                               int64_t* __restrict__ state,
                                                               float* __restrict__ theta_out) {
-    __shared__ uint32_t xs[kF2Cap];
-    __shared__ uint32_t hist[kDigitBins + 64];              // the digits, then one spare bin per lane
+    __shared__ uint32_t xs[kF2Cap];                          // the in-bracket keys, in tile order
+    __shared__ uint16_t xt[PRE ? kF2Cap : 1];                // PRE: the tile of each key
+    __shared__ int tp[kF2Round + 1];                         // tile T's keys: xs[tp[T] .. tp[T + 1])
+    __shared__ uint32_t tc[PRE ? kF2Round : 1];              // PRE: per tile, above | equal << 16
+    __shared__ uint32_t hist[kDigitBins];
+    __shared__ uint32_t dummy[64];                           // spare words of writes that are not needed
+    __shared__ uint16_t dummyt[PRE ? 64 : 1];
     __shared__ uint32_t xd[64];
-    __shared__ uint16_t xdt[64];                             // the tile (in the sequence) of each xd key
     __shared__ int tmp[kF2Threads / 64];
     __shared__ int tmp3[3][kF2Threads / 64];
     __shared__ int64_t sh[4];
@@ -1509,31 +1514,29 @@ __global__ __launch_bounds__(kF2Threads) void th_final2_kernel(const float* __re
     const uint32_t* over = a.tcand + (size_t)tf * a.tstride;     // overflow keys of the sequence's tiles
     const bool one = nt <= kF2Round;                   // one round: the keys load with the records
 
-    // ---- 1. records, first keys and counts: one memory round trip (tiles past nt read tile 0's
-    // records, in bounds, and count nothing); the bracket is read after these loads are issued
+    // ---- 1. records and slot keys: one memory round trip.  Thread t takes the records of the
+    // kF2Per consecutive tiles kF2Per t + u; the slot keys are read in 16-byte chunks in a
+    // coalesced order (chunk g = r kF2Threads + t holds slots 4 (g % 4) .. of tile g / 4).  Tiles
+    // past nt read tile 0 (in bounds) and count nothing; the bracket is read after these loads.
+    constexpr int kChunks = kF2Round * (kClsSlots / 4) / kF2Threads;
     uint32_t w[kF2Per];
-    uint32_t kv[kF2Per][kClsSlots];
+    uint4 kc[kChunks];
 #pragma unroll
     for (int u = 0; u < kF2Per; ++u) {
         const int64_t T = (int64_t)kF2Per * t + u;
-        const int64_t Tc = T < nt ? T : 0;
-        w[u] = inf_h[Tc];
-        if (one) {
-            const uint4* src = reinterpret_cast<const uint4*>(cand_h + Tc * kClsSlots);
+        w[u] = inf_h[T < nt ? T : 0];
+    }
+    if (one) {
 #pragma unroll
-            for (int v = 0; v < kClsSlots / 4; ++v) {
-                const uint4 x = src[v];
-                kv[u][4 * v] = x.x;
-                kv[u][4 * v + 1] = x.y;
-                kv[u][4 * v + 2] = x.z;
-                kv[u][4 * v + 3] = x.w;
-            }
+        for (int r2 = 0; r2 < kChunks; ++r2) {
+            const int g = r2 * kF2Threads + t, T = g / (kClsSlots / 4);
+            kc[r2] = reinterpret_cast<const uint4*>(cand_h + (int64_t)(T < nt ? T : 0) * kClsSlots)[g % (kClsSlots / 4)];
         }
     }
     __builtin_amdgcn_sched_barrier(0);
     const uint32_t klo = (uint32_t)st[kStLo], khi = (uint32_t)st[kStHi];
     const int dsh = top_shift(khi - klo);
-    for (int i = t; i < kDigitBins + 64; i += kF2Threads) hist[i] = 0;
+    for (int i = t; i < kDigitBins; i += kF2Threads) hist[i] = 0;
     int lsum = 0, csum = 0, ov0 = 0;
 #pragma unroll
     for (int u = 0; u < kF2Per; ++u) {
@@ -1552,58 +1555,89 @@ __global__ __launch_bounds__(kF2Threads) void th_final2_kernel(const float* __re
             csum += (int)((x >> 8) & 0xffu);
         }
     int nlo = 0, nmid = 0, novf = 0;
-    const int oinc = block_inclusive_scan3<kF2Threads>(lsum, csum, ov0, tmp3, &nlo, &nmid, &novf);
+    const int cinc = block_inclusive_scan3<kF2Threads>(lsum, ov0, csum, tmp3, &nlo, &novf, &nmid);
     const int64_t r = oi.rank;
     bool whole_row = !(nlo < r && r <= (int64_t)nlo + nmid);
     uint32_t key = 0;
     int64_t gt = 0;
-    bool regs = false;                                    // tile counts below from registers
-    // per tile of this thread: keys above the answer's digit (then above the answer too), and
-    // (after the rank) the tile's keys of that digit above / equal to the answer
-    int tg[kF2Per], te[kF2Per];
-#pragma unroll
-    for (int u = 0; u < kF2Per; ++u) tg[u] = te[u] = 0;
+    bool regs = false;                 // the in-bracket keys sit in LDS in tile order (tp), or klo == khi
     if (!whole_row) {
         gt = m - nlo - nmid;                              // keys above the bracket
         const int64_t rr0 = r - nlo;
         if (klo == khi) {
             key = klo;                                    // every in-bracket key is the answer
             regs = one;
-#pragma unroll
-            for (int u = 0; u < kF2Per; ++u) te[u] = (int)((w[u] >> 8) & 0xffu);
         } else {
-            // in LDS when one round holds the sequence and the overflow keys fit; else from memory
-            bool from_mem = !(one && novf <= kF2Cap);
+            bool from_mem = !(one && nmid <= kF2Cap);
             if (!from_mem) {
-                // ---- 2. the keys past the tiles' slots (rare) into LDS, batches of 8 loads in
-                // flight, counted per digit as they arrive; the slots' keys counted from the
-                // registers (a key past the tile's count goes to the lane's spare bin, so every
-                // atomic is unconditional)
-                int base = oinc - ov0;
+                // ---- 2. the in-bracket keys (minus klo) into LDS in tile order: tile T's keys at
+                // xs[tp[T] .. tp[T + 1]), its slots' keys from the registers, the rest (rare) from
+                // memory in batches of 8 loads
+                int pos = cinc - csum;
 #pragma unroll
                 for (int u = 0; u < kF2Per; ++u) {
-                    const int cnt = (int)((w[u] >> 8) & 0xffu);
-                    const uint32_t* ov = over + (size_t)((int64_t)kF2Per * t + u) * a.tstride + (w[u] >> 16);
-                    for (int j0 = kClsSlots; j0 < cnt; j0 += 8) {
-                        uint32_t x8[8];
+                    const int64_t T = (int64_t)kF2Per * t + u;
+                    if (T < nt) tp[T] = pos;
+                    pos += (int)((w[u] >> 8) & 0xffu);
+                }
+                if (t == 0) tp[nt] = nmid;
+                if (PRE)
+                    for (int i = t; i < nt; i += kF2Threads) tc[i] = 0u;
+                __syncthreads();
+                // every chunk's table entries first (one LDS wait), then its keys: slots past the
+                // tile's count (and chunks past nt) write to a spare word instead
+                int b0[kChunks], c0[kChunks];
 #pragma unroll
-                        for (int v = 0; v < 8; ++v) x8[v] = ov[(j0 + v < cnt ? j0 + v : j0) - kClsSlots];
-#pragma unroll
-                        for (int v = 0; v < 8; ++v)
-                            if (j0 + v < cnt) {
-                                const uint32_t x = x8[v] - klo;
-                                xs[base + j0 + v - kClsSlots] = x;
-                                atomicAdd(&hist[x >> dsh], 1u);
-                            }
-                    }
-                    base += cnt > kClsSlots ? cnt - kClsSlots : 0;
+                for (int r2 = 0; r2 < kChunks; ++r2) {
+                    const int T = (r2 * kF2Threads + t) / (kClsSlots / 4);
+                    const int Tc = T < nt ? T : (int)nt;
+                    b0[r2] = tp[Tc];
+                    c0[r2] = T < nt ? tp[Tc + 1] : 0;
                 }
 #pragma unroll
-                for (int u = 0; u < kF2Per; ++u) {
-                    const int cnt = (int)((w[u] >> 8) & 0xffu);
+                for (int r2 = 0; r2 < kChunks; ++r2) {
+                    const int g = r2 * kF2Threads + t, T = g / (kClsSlots / 4), j0 = 4 * (g % (kClsSlots / 4));
+                    const int c = c0[r2] - b0[r2];
+                    const uint32_t x4[4] = {kc[r2].x, kc[r2].y, kc[r2].z, kc[r2].w};
 #pragma unroll
-                    for (int j = 0; j < kClsSlots; ++j)
-                        atomicAdd(&hist[j < cnt ? (kv[u][j] - klo) >> dsh : (uint32_t)(kDigitBins + lane)], 1u);
+                    for (int i = 0; i < 4; ++i) {
+                        const bool ok = j0 + i < c;
+                        const int at = b0[r2] + j0 + i;
+                        *(ok ? &xs[at] : &dummy[lane]) = x4[i] - klo;
+                        if (PRE) *(ok ? &xt[at] : &dummyt[lane]) = (uint16_t)T;
+                    }
+                }
+                if (novf > 0) {
+#pragma unroll
+                    for (int u = 0; u < kF2Per; ++u) {
+                        const int64_t T = (int64_t)kF2Per * t + u;
+                        const int cnt = (int)((w[u] >> 8) & 0xffu);
+                        if (cnt <= kClsSlots) continue;
+                        const uint32_t* ov = over + (size_t)T * a.tstride + (w[u] >> 16);
+                        const int tb = tp[T];
+                        for (int j0 = kClsSlots; j0 < cnt; j0 += 8) {
+                            uint32_t x8[8];
+#pragma unroll
+                            for (int v = 0; v < 8; ++v) x8[v] = ov[(j0 + v < cnt ? j0 + v : j0) - kClsSlots];
+#pragma unroll
+                            for (int v = 0; v < 8; ++v)
+                                if (j0 + v < cnt) {
+                                    xs[tb + j0 + v] = x8[v] - klo;
+                                    if (PRE) xt[tb + j0 + v] = (uint16_t)T;
+                                }
+                        }
+                    }
+                }
+                __syncthreads();
+                // ---- 3. the answer's digit, then its keys ranked (the loops over the keys read 8
+                // keys per thread before they update LDS, so that the reads overlap)
+                for (int i0 = t; i0 < nmid; i0 += kF2Batch * kF2Threads) {
+                    uint32_t x[kF2Batch];
+#pragma unroll
+                    for (int k = 0; k < kF2Batch; ++k) x[k] = xs[min(i0 + k * kF2Threads, kF2Cap - 1)];
+#pragma unroll
+                    for (int k = 0; k < kF2Batch; ++k)
+                        if (i0 + k * kF2Threads < nmid) atomicAdd(&hist[x[k] >> dsh], 1u);
                 }
                 __syncthreads();
                 f2_find_digit(hist, rr0, tmp, sh);
@@ -1612,54 +1646,25 @@ __global__ __launch_bounds__(kF2Threads) void th_final2_kernel(const float* __re
                 const int nD = (int)sh[3];
                 const int64_t gt_d = sh[2];
                 __syncthreads();
-                if (nD > 64 && novf + nD > kF2Cap) {
-                    from_mem = true;                      // the digit does not fit beside the overflow keys
+                if (nD > 64 && nmid + nD > kF2Cap) {
+                    from_mem = true;                      // the digit does not fit beside the keys
                 } else {
-                    // the digit's keys (low bits) into LDS: xd (with their tiles) for at most 64,
-                    // else after the overflow keys; then ranked there.  Meanwhile each thread
-                    // counts its tiles' keys of higher digits.
+                    // the digit's keys (low bits) into xd for at most 64, else after the keys
                     const uint32_t low = dsh ? ((1u << dsh) - 1u) : 0u;
-                    uint32_t* dst = nD <= 64 ? xd : xs + novf;
-                    int ovb = oinc - ov0;                 // this thread's overflow keys in xs
+                    uint32_t* dst = nD <= 64 ? xd : xs + nmid;
+                    for (int i0 = t; i0 < nmid; i0 += kF2Batch * kF2Threads) {
+                        uint32_t x[kF2Batch];
 #pragma unroll
-                    for (int u = 0; u < kF2Per; ++u) {
-                        const int cnt = (int)((w[u] >> 8) & 0xffu);
-                        const uint16_t T = (uint16_t)(kF2Per * t + u);
-                        auto take = [&](uint32_t x) {
-                            const uint32_t dg = x >> dsh;
-                            if (PRE) tg[u] += dg > D ? 1 : 0;
-                            if (dg == D) {
-                                const uint32_t pos = atomicAdd(&cursor, 1u);
-                                dst[pos] = x & low;
-                                if (PRE && nD <= 64) xdt[pos] = T;
-                            }
-                        };
+                        for (int k = 0; k < kF2Batch; ++k) x[k] = xs[min(i0 + k * kF2Threads, kF2Cap - 1)];
 #pragma unroll
-                        for (int j = 0; j < kClsSlots; ++j)
-                            if (j < cnt) take(kv[u][j] - klo);
-                        for (int j = kClsSlots; j < cnt; ++j) take(xs[ovb + j - kClsSlots]);
-                        ovb += cnt > kClsSlots ? cnt - kClsSlots : 0;
+                        for (int k = 0; k < kF2Batch; ++k)
+                            if (i0 + k * kF2Threads < nmid && (x[k] >> dsh) == D) dst[atomicAdd(&cursor, 1u)] = x[k] & low;
                     }
                     __syncthreads();
                     gt += gt_d;
                     const uint32_t xl = f2_rank_lds(dst, nD, dsh, rr, hist, tmp, sh, &gt);
                     key = klo + ((D << dsh) | xl);
-                    if (PRE && nD <= 64) {
-                        // the digit's keys of this thread's tiles against the answer's low bits
-                        regs = true;
-                        for (int i = 0; i < nD; ++i) {
-                            const int T = xdt[i];
-                            if (T / kF2Per == t) {
-                                const uint32_t x = xd[i];
-#pragma unroll
-                                for (int u = 0; u < kF2Per; ++u)
-                                    if (T % kF2Per == u) {
-                                        tg[u] += x > xl ? 1 : 0;
-                                        te[u] += x == xl ? 1 : 0;
-                                    }
-                            }
-                        }
-                    }
+                    regs = true;
                 }
             }
             if (from_mem) {
@@ -1689,14 +1694,43 @@ __global__ __launch_bounds__(kF2Threads) void th_final2_kernel(const float* __re
         uint2* pre = a.phpre + hrow;
         if (regs && !whole_row) {
             // from the records: a tile's keys above the bracket are above the answer, those below
-            // it below; the in-bracket ones were counted above
+            // it below; its in-bracket keys above / equal to the answer are counted per tile with
+            // one pass over the keys in LDS (all equal when klo == khi)
+            if (klo != khi) {
+                const uint32_t xa = key - klo;
+                for (int i0 = t; i0 < nmid; i0 += kF2Batch * kF2Threads) {
+                    uint32_t x[kF2Batch];
+                    uint16_t tt[kF2Batch];
+#pragma unroll
+                    for (int k = 0; k < kF2Batch; ++k) {
+                        const int i = min(i0 + k * kF2Threads, (PRE ? kF2Cap : 1) - 1);   // in bounds
+                        x[k] = xs[i];
+                        tt[k] = xt[i];
+                    }
+#pragma unroll
+                    for (int k = 0; k < kF2Batch; ++k)
+                        if (i0 + k * kF2Threads < nmid && x[k] >= xa) atomicAdd(&tc[tt[k]], x[k] > xa ? 1u : 0x10000u);
+                }
+                __syncthreads();
+            }
+            int tg[kF2Per], te[kF2Per];
             int sg = 0, se = 0;
 #pragma unroll
             for (int u = 0; u < kF2Per; ++u) {
                 const int64_t T = (int64_t)kF2Per * t + u;
+                const int cnt = (int)((w[u] >> 8) & 0xffu);
+                int g = 0, e = 0;
+                if (klo == khi) {
+                    e = cnt;
+                } else if (T < nt) {
+                    const uint32_t v = tc[T];
+                    g = (int)(v & 0xffffu);
+                    e = (int)(v >> 16);
+                }
                 const int64_t pa = 64 * T > oi.beg ? 64 * T : oi.beg, pe = 64 * T + 64 < oi.end ? 64 * T + 64 : oi.end;
                 const int valid = (T < nt && pe > pa) ? (int)(pe - pa) : 0;
-                tg[u] += valid - (int)(w[u] & 0xffu) - (int)((w[u] >> 8) & 0xffu);
+                tg[u] = g + valid - (int)(w[u] & 0xffu) - cnt;
+                te[u] = e;
                 sg += tg[u];
                 se += te[u];
             }

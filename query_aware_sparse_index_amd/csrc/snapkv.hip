@@ -183,15 +183,19 @@ __global__ __launch_bounds__(kSnapThreads) void snap_pass_kernel(const uint16_t*
     // The loads are unconditional: a key block past the end loads key n - 1 (the clamp in
     // load), so that every path through the loop issues the same memory operations and the
     // waits before the MFMAs count the prefetch as still in flight instead of draining it.
+    // Pass 2 walks the key blocks from the last one down: the keys pass 1 read last are the
+    // ones most likely still held in the last-level cache.  Steps past the end stay unmapped
+    // (their loads clamp to key n - 1).
+    auto order = [&](int64_t kb) { return (PASS == 2 && kb < nblk) ? nblk - 1 - kb : kb; };
     bf16x8_t a0[kSnapKTW][4], a1[kSnapKTW][4];
-    load(a0, p);
+    load(a0, order(p));
     __syncthreads();
     for (int64_t kb = p; kb < nblk; kb += 2 * (int64_t)P) {
-        load(a1, kb + P);
-        run(a0, kb);
+        load(a1, order(kb + P));
+        run(a0, order(kb));
         if (kb + P >= nblk) break;
-        load(a0, kb + 2 * (int64_t)P);
-        run(a1, kb + P);
+        load(a0, order(kb + 2 * (int64_t)P));
+        run(a1, order(kb + P));
     }
 
     if (PASS == 1) {
