@@ -12,8 +12,9 @@
 // from HBM (one 16-byte load per lane), the B operand a 32-dim x 16-row slice of Q_g from
 // LDS.  Lane l of the 16x16 fp32 result holds keys 4*(l/16)+i (i < 4) for row l%16.
 //   pass 1 (snap_pass_kernel<1>): per row online max / sum of 2^s over the block's keys
-//   snap_lse_kernel:             combines the per-block (m, l) into LSE_r (log2 domain)
-//   pass 2 (snap_pass_kernel<2>): p = 2^(s - LSE_r); the column sum over the R rows (a
+//   pass 2 (snap_pass_kernel<2>): each block first combines the pass-1 blocks' (m, l) of its
+//                                 rows into LSE_r (log2 domain), while its first keys load;
+//                                 then p = 2^(s - LSE_r), and the column sum over the R rows (a
 //                                 16-lane DPP butterfly per 16-row tile) gives imp[j] * R
 // Scores are kept in the log2 domain (s = q.k * log2(e)/sqrt(128)) so that exp2 is used.
 #include <type_traits>
@@ -50,7 +51,6 @@ __global__ __launch_bounds__(kSnapThreads) void snap_pass_kernel(const uint16_t*
                                                                 const uint16_t* __restrict__ K, int64_t n, int w,
                                                                 int Hq, int Hkv, int64_t nblk,
                                                                 float2* __restrict__ pstat,
-                                                                const float* __restrict__ lse,
                                                                 float* __restrict__ imp) {
     constexpr int R = RT * 16;
     constexpr int NW = kSnapThreads / 64;
@@ -71,8 +71,6 @@ __global__ __launch_bounds__(kSnapThreads) void snap_pass_kernel(const uint16_t*
         const uint4 v = *reinterpret_cast<const uint4*>(q_obs + ((int64_t)t * Hq + g * G + hh) * kD + c * 8);
         sQ[r * 16 + (c ^ (r & 15))] = v;
     }
-    if (PASS == 2)
-        for (int r = threadIdx.x; r < R; r += kSnapThreads) sL[r] = lse[(int64_t)g * R + r];
 
     // A fragments of key block kb: key jw(kb) + kt*16 + lr, dims 32 s + 8 lg .. +8
     auto key0 = [&](int64_t kb) { return kb * kSnapKT + (int64_t)wid * kSnapKTW * 16; };
@@ -189,6 +187,34 @@ __global__ __launch_bounds__(kSnapThreads) void snap_pass_kernel(const uint16_t*
     auto order = [&](int64_t kb) { return (PASS == 2 && kb < nblk) ? nblk - 1 - kb : kb; };
     bf16x8_t a0[kSnapKTW][4], a1[kSnapKTW][4];
     load(a0, order(p));
+    if (PASS == 2) {
+        // LSE_r = M + log2(L) over the P pass-1 blocks' (M, L) of row r: two lanes per row, each
+        // half of the blocks with 8 loads in flight, then the pair combined
+        static_assert(2 * R <= kSnapThreads, "two lanes per row");
+        const int r = threadIdx.x >> 1, hf = threadIdx.x & 1;
+        float M = -INFINITY, L = 0.f;
+        if (r < R)
+            for (int k0 = hf; k0 < P; k0 += 2 * 8) {
+                float2 v[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int k = k0 + 2 * u;
+                    v[u] = k < P ? pstat[((int64_t)g * P + k) * R + r] : make_float2(-INFINITY, 0.f);
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const float mn = fmaxf(M, v[u].x);
+                    if (mn != -INFINITY) {
+                        L = L * fast_exp2(M - mn) + v[u].y * fast_exp2(v[u].x - mn);
+                        M = mn;
+                    }
+                }
+            }
+        const float m2 = __shfl_xor(M, 1, 64), l2 = __shfl_xor(L, 1, 64);
+        const float mn = fmaxf(M, m2);
+        if (mn != -INFINITY) L = L * fast_exp2(M - mn) + l2 * fast_exp2(m2 - mn);
+        if (r < R && hf == 0) sL[r] = mn + log2f(L);
+    }
     __syncthreads();
     for (int64_t kb = p; kb < nblk; kb += 2 * (int64_t)P) {
         load(a1, order(kb + P));
@@ -228,52 +254,6 @@ __global__ __launch_bounds__(kSnapThreads) void snap_pass_kernel(const uint16_t*
             }
             pstat[((int64_t)g * P + p) * R + r] = make_float2(M, L);
         }
-    }
-}
-
-// lse[g][r] = M + log2(L) over the pass-1 blocks' (M, L) (nblk of them per KV head).  Block = (g, 64-row slice); its 256 threads
-// are (quarter q < 4, row): each walks every 4th block with 8 loads in flight, then the
-// quarters are merged in LDS.
-__global__ __launch_bounds__(256) void snap_lse_kernel(const float2* __restrict__ pstat, int64_t nblk, int R, int Hkv,
-                                                      float* __restrict__ lse) {
-    __shared__ float2 part[4][64];
-    const int nrb = (R + 63) / 64;
-    const int rb = blockIdx.x % nrb;
-    const int g = blockIdx.x / nrb;
-    const int rl = threadIdx.x & 63, qq = threadIdx.x >> 6;
-    const int r = rb * 64 + rl;
-    float M = -INFINITY, L = 0.f;
-    if (r < R) {
-        for (int64_t k0 = qq; k0 < nblk; k0 += 4 * 8) {
-            float2 v[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int64_t k = k0 + 4 * u;
-                v[u] = k < nblk ? pstat[((int64_t)g * nblk + k) * R + r] : make_float2(-INFINITY, 0.f);
-            }
-#pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const float mn = fmaxf(M, v[u].x);
-                if (mn != -INFINITY) {
-                    L = L * fast_exp2(M - mn) + v[u].y * fast_exp2(v[u].x - mn);
-                    M = mn;
-                }
-            }
-        }
-    }
-    part[qq][rl] = make_float2(M, L);
-    __syncthreads();
-    if (qq == 0 && r < R) {
-#pragma unroll
-        for (int u = 1; u < 4; ++u) {
-            const float2 v = part[u][rl];
-            const float mn = fmaxf(M, v.x);
-            if (mn != -INFINITY) {
-                L = L * fast_exp2(M - mn) + v.y * fast_exp2(v.x - mn);
-                M = mn;
-            }
-        }
-        lse[(int64_t)g * R + r] = M + log2f(L);
     }
 }
 
@@ -342,7 +322,7 @@ static int64_t snap_blocks_per_head(int Hkv, int64_t nblk) {
 struct SnapLayout {
     int64_t nblk, P;
     float2* pstat;
-    float *lse, *imp, *pooled;
+    float *imp, *pooled;
     void* sel_ws;
     size_t sel_bytes, bytes;
 };
@@ -354,7 +334,6 @@ static SnapLayout snap_layout(void* ws, int64_t n, int w, int Hq, int Hkv, int64
     L.P = snap_blocks_per_head(Hkv, L.nblk);
     WsCarver wc(ws);
     L.pstat = wc.take<float2>((size_t)Hkv * L.P * R);
-    L.lse = wc.take<float>((size_t)Hkv * R);
     L.imp = wc.take<float>((size_t)Hkv * n);
     L.pooled = wc.take<float>((size_t)Hkv * score_stride(n));
     (void)c;
@@ -366,20 +345,19 @@ static SnapLayout snap_layout(void* ws, int64_t n, int w, int Hq, int Hkv, int64
 
 template <int PASS, int RT>
 static hipError_t launch_pass_rt(dim3 grid, size_t shq, hipStream_t stream, const uint16_t* q_obs, const uint16_t* K,
-                                 int64_t n, int w, int Hq, int Hkv, int64_t nblk, float2* pstat, const float* lse,
-                                 float* imp) {
+                                 int64_t n, int w, int Hq, int Hkv, int64_t nblk, float2* pstat, float* imp) {
     hipLaunchKernelGGL((snap_pass_kernel<PASS, RT>), grid, dim3(kSnapThreads), shq, stream, q_obs, K, n, w, Hq, Hkv,
-                       nblk, pstat, lse, imp);
+                       nblk, pstat, imp);
     return hipGetLastError();
 }
 
 template <int PASS, int... RTS>
 static hipError_t dispatch_pass(int rt, std::integer_sequence<int, RTS...>, dim3 grid, size_t shq, hipStream_t stream,
                                 const uint16_t* q_obs, const uint16_t* K, int64_t n, int w, int Hq, int Hkv,
-                                int64_t nblk, float2* pstat, const float* lse, float* imp) {
+                                int64_t nblk, float2* pstat, float* imp) {
     hipError_t e = hipErrorInvalidValue;
     ((rt == RTS + 1
-          ? (e = launch_pass_rt<PASS, RTS + 1>(grid, shq, stream, q_obs, K, n, w, Hq, Hkv, nblk, pstat, lse, imp), 0)
+          ? (e = launch_pass_rt<PASS, RTS + 1>(grid, shq, stream, q_obs, K, n, w, Hq, Hkv, nblk, pstat, imp), 0)
           : 0),
      ...);
     return e;
@@ -388,9 +366,9 @@ static hipError_t dispatch_pass(int rt, std::integer_sequence<int, RTS...>, dim3
 template <int PASS>
 static hipError_t launch_snap_pass(int rt, dim3 grid, size_t shq, hipStream_t stream, const uint16_t* q_obs,
                                    const uint16_t* K, int64_t n, int w, int Hq, int Hkv, int64_t nblk, float2* pstat,
-                                   const float* lse, float* imp) {
+                                   float* imp) {
     return dispatch_pass<PASS>(rt, std::make_integer_sequence<int, 16>{}, grid, shq, stream, q_obs, K, n, w, Hq, Hkv,
-                               nblk, pstat, lse, imp);
+                               nblk, pstat, imp);
 }
 
 template <int... RTS>
@@ -417,12 +395,9 @@ hipError_t launch_snapkv(const uint16_t* q_obs, const uint16_t* K, const uint16_
     float* pooled = L.pooled;
     const size_t shq = (size_t)R * kD * 2;
     dim3 grid(Hkv, (unsigned)L.P);
-    hipError_t e = launch_snap_pass<1>(R / 16, grid, shq, stream, q_obs, K, n, w, Hq, Hkv, L.nblk, L.pstat, nullptr,
-                                       nullptr);
+    hipError_t e = launch_snap_pass<1>(R / 16, grid, shq, stream, q_obs, K, n, w, Hq, Hkv, L.nblk, L.pstat, nullptr);
     if (e != hipSuccess) return e;
-    const int rblk = (R + 63) / 64;
-    hipLaunchKernelGGL(snap_lse_kernel, dim3(Hkv * rblk), dim3(256), 0, stream, L.pstat, L.P, R, Hkv, L.lse);
-    e = launch_snap_pass<2>(R / 16, grid, shq, stream, q_obs, K, n, w, Hq, Hkv, L.nblk, nullptr, L.lse, imp);
+    e = launch_snap_pass<2>(R / 16, grid, shq, stream, q_obs, K, n, w, Hq, Hkv, L.nblk, L.pstat, imp);
     if (e != hipSuccess) return e;
     e = launch_snap_topc(imp, n, Hkv, c, pooled, score_stride(n), pooled_out, idx_out, L.sel_ws, L.sel_bytes, stream);
     if (e != hipSuccess) return e;
