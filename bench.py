@@ -45,9 +45,10 @@ def measured_traffic(mode, n, budget):
             digest = hashlib.sha256(f.read()).hexdigest()
     except (OSError, ValueError):
         return None
-    if rec.get("decode_hip_sha256") != digest or rec.get("mode") != mode or rec.get("budget") != budget:
-        return None
-    return rec.get("bytes_per_launch")
+    for r in rec.get("records", []):
+        if r.get("decode_hip_sha256") == digest and r.get("mode") == mode and r.get("budget") == budget:
+            return r.get("bytes_per_launch")
+    return None
 
 
 # ------------------------------------------------------------------ CPU oracle leg
@@ -177,8 +178,15 @@ def traffic_record(fetch_csv, write_csv, out_path, mode=0, budget=20):
            "kernels": {k: table[k] for k in dec},
            "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
            "mode": mode, "budget": budget, "decode_hip_sha256": digest}
+    # one record per (mode, budget): a new measurement replaces the old one of its workload
+    try:
+        with open(out_path) as f:
+            old = json.load(f).get("records", [])
+    except (OSError, ValueError):
+        old = []
+    recs = [r for r in old if (r.get("mode"), r.get("budget")) != (mode, budget)] + [rec]
     with open(out_path, "w") as f:
-        json.dump(rec, f, indent=1)
+        json.dump({"records": recs}, f, indent=1)
         f.write("\n")
     return rec, table
 
@@ -420,7 +428,8 @@ def bench_union(torch, api, L, calls, warm, steps, Hq, Hkv, kmax, offs_max, Kp, 
 def main():
     args = parse()
     if args.traffic_from:
-        rec, table = traffic_record(args.traffic_from[0], args.traffic_from[1], TRAFFIC_FILE)
+        mode = 0 if args.mode == "vote" else 1
+        rec, table = traffic_record(args.traffic_from[0], args.traffic_from[1], TRAFFIC_FILE, mode, args.budget)
         for k, v in table.items():
             print(f"{v['fetch_kib']:14.1f} {v['write_kib']:14.1f} {v['bytes'] / 1e6:10.2f} MB  {k[:90]}")
         print(json.dumps({k: v for k, v in rec.items() if k != "kernels"}))
