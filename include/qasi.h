@@ -158,15 +158,29 @@ size_t ts_score_select_workspace_bytes(const int64_t* offsets_host, int32_t B, i
  *   ws        device workspace of at least ts_score_select_workspace_bytes(...) bytes.
  * Each head's order statistic is found from a key bracket taken from 1024 sampled index
  * scores (rows of more than 16384 candidate keys; shorter rows are ranked whole): the score pass
- * counts, per 64-token tile, the keys below the bracket and keeps the keys inside it; blocks of
- * up to 512 tiles histogram those keys and the last of them to finish ranks the answer's digit.
- * When the target rank falls outside the bracket the whole row is radix-selected instead (same
- * result).                                                                                    */
+ * counts, per 64-token tile, the keys below the bracket and keeps the keys inside it; one block
+ * per (sequence, head) then ranks the kept keys.  When the target rank falls outside the
+ * bracket the whole row is radix-selected instead (same result, tens of microseconds more).   */
 int ts_score_select(const uint16_t* q, const float* P, uint16_t* k_index, const uint16_t* K_last,
                     const int64_t* offsets_dev, const int64_t* offsets_host, int32_t B, int32_t Hq,
                     int32_t Hkv, const ts_select_params* p, float* scores, int32_t* idx_out,
                     int64_t* count_out, float* theta_out, uint8_t* votes_out, void* ws,
                     size_t ws_bytes, hipStream_t stream);
+
+/* Diagnostics of ts_score_select's sampled brackets: the byte offset, in its workspace, of the
+ * per-instance records that a completed call leaves there (-1 if an argument is invalid; the
+ * arguments are those of ts_score_select_workspace_bytes).  Record i = b*Hq + h is 8 int64:
+ *   [0] flag (0: order statistic taken, 1: no token taken, 2: every candidate taken)
+ *   [1] the answer's order key (the fp32 bits of theta_h mapped to an unsigned order:
+ *       negative values bitwise inverted, others with the sign bit set; -0 counts as +0)
+ *   [2] the number of candidate keys above it      [3] per-head mode: tokens still to take
+ *   [4], [5] the sampled bracket [lo, hi] of order keys (lo > hi: no bracket, the row was ranked
+ *       whole because it holds at most 16384 candidates)
+ *   [6], [7] the candidate range [begin, end) of token positions.
+ * The bracket held, and the whole-row fallback was not taken, when lo <= [1] <= hi.  The records
+ * are only read from the workspace: the caller owns it and nothing else there is documented. */
+int64_t ts_score_select_state_offset(const int64_t* offsets_host, int32_t B, int32_t Hq,
+                                     const ts_select_params* p);
 
 /* Capacity of an expanded list (ts_expand_selection): min(n, (2 radius + 1) k_prev + sink +
  * local); -1 if an argument is out of range (k_prev in [0, n], n, sink and local in [0, 2^31],

@@ -28,6 +28,7 @@ SIGNATURES = {
     "ts_score_select_workspace_bytes": (_sz, [_i64p, _i32, _i32, _vp]),
     "ts_score_select": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64p, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
                                        _vp, _sz, _vp]),
+    "ts_score_select_state_offset": (_i64, [_i64p, _i32, _i32, _vp]),
     "ts_expand_capacity": (_i64, [_i64, _i64, _i64, _i64, _i64]),
     "ts_expand_workspace_bytes": (_sz, [_i64p, _i32, _i32]),
     "ts_expand_selection": (ctypes.c_int, [_vp, _vp, _i64p, _vp, _i64p, _i32, _i32, _i64, _i64, _i64, _vp, _vp, _vp,

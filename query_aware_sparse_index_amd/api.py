@@ -165,6 +165,17 @@ def score_select(q, P, k_index, offs: Offsets, Hkv: int, p, K_last=None, want_th
     return res
 
 
+def score_select_state(ws, offs: Offsets, Hq: int, p):
+    """ts_score_select_state_offset: the per-(sequence, head) records that a completed
+    score_select call left in its workspace `ws`, as an int64 view [B, Hq, 8] (flag, answer key,
+    keys above, need, bracket lo, bracket hi, range begin, range end)."""
+    off = int(_lib.load().ts_score_select_state_offset(offs.host, offs.B, int(Hq), ctypes.byref(p)))
+    if off < 0:
+        raise ValueError(_lib.load().ts_last_error().decode())
+    n = offs.B * int(Hq) * 8 * 8
+    return ws[off:off + n].view(torch.int64).view(offs.B, int(Hq), 8)
+
+
 def expand_capacity(k_prev: int, n: int, sink=4, local=256, radius=1) -> int:
     return int(_lib.load().ts_expand_capacity(int(k_prev), int(n), int(sink), int(local), int(radius)))
 

@@ -186,6 +186,13 @@ size_t ts_score_select_workspace_bytes(const int64_t* offsets_host, int32_t B, i
     return qasi::score_select_workspace(offsets_host, B, Hq, c);
 }
 
+int64_t ts_score_select_state_offset(const int64_t* offsets_host, int32_t B, int32_t Hq,
+                                     const ts_select_params* p) {
+    qasi::SelectConfig c;
+    if (!offsets_host || B <= 0 || Hq <= 0 || to_cfg(p, &c) != QASI_OK) return -1;
+    return (int64_t)qasi::score_select_state_offset(offsets_host, B, Hq, c);
+}
+
 int ts_score_select(const uint16_t* q, const float* P, uint16_t* k_index, const uint16_t* K_last,
                     const int64_t* offsets_dev, const int64_t* offsets_host, int32_t B, int32_t Hq, int32_t Hkv,
                     const ts_select_params* p, float* scores, int32_t* idx_out, int64_t* count_out,

@@ -66,6 +66,8 @@ int64_t budget_tokens(int64_t n, const SelectConfig& c);
 // ts_score followed by ts_select in one pass (and, when K is given, the index row of every
 // sequence's last token appended first): identical scores, thresholds and lists.
 size_t score_select_workspace(const int64_t* offsets_host, int B, int Hq, const SelectConfig& c);
+// byte offset in that workspace of the per-instance records [B * Hq][8] (kSt* fields)
+size_t score_select_state_offset(const int64_t* offsets_host, int B, int Hq, const SelectConfig& c);
 hipError_t launch_score_select(const uint16_t* q, const float* P, uint16_t* k_index, const uint16_t* K,
                                const int64_t* offsets_dev, const int64_t* offsets_host, int B, int Hq, int Hkv,
                                const SelectConfig& c, float* scores, int32_t* idx_out, int64_t* count_out,

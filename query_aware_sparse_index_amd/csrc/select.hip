@@ -1771,6 +1771,7 @@ struct SelectLayout {
     int64_t nitems, ph_items, Ntot, ntiles;
     uint32_t *cand, *cnt, *dhist, *hist, *phcnt;
     int64_t* state;
+    size_t state_off;   // byte offset of `state` in the workspace
     uint8_t *votes, *keys;
     float* qp;          // fused path: q' per (sequence, head)
     uint32_t* tinfo;    // fused path: per (head, tile) counts below / inside the bracket, key offset
@@ -1817,6 +1818,7 @@ static SelectLayout select_layout(void* ws, const int64_t* offsets_host, int B, 
         L.dhist = w.take<uint32_t>(inst * L.SL * kDpWords);
     }
     L.phcnt = c.mode == 1 ? w.take<uint32_t>((size_t)Hq * ph_items * 2) : nullptr;
+    L.state_off = w.size();
     L.state = w.take<int64_t>(inst * 8);
     L.votes = w.take<uint8_t>((size_t)L.Ntot + 16);
     L.keys = w.take<uint8_t>((size_t)L.Ntot + 16);
@@ -1831,6 +1833,10 @@ size_t select_workspace(const int64_t* offsets_host, int B, int Hq, const Select
 
 size_t score_select_workspace(const int64_t* offsets_host, int B, int Hq, const SelectConfig& c) {
     return select_layout(nullptr, offsets_host, B, Hq, c, true).bytes;
+}
+
+size_t score_select_state_offset(const int64_t* offsets_host, int B, int Hq, const SelectConfig& c) {
+    return select_layout(nullptr, offsets_host, B, Hq, c, true).state_off;
 }
 
 // Votes and the ordered compaction (vote mode) or the per-head compaction, once the order

@@ -87,6 +87,8 @@ int main(void) {
     EXPECT(ts_select(F, F, o1, 1, 8, 2, &ok, F, F, NULL, NULL, F, sel - 1, NULL), -3);
     EXPECT(ts_select(F, F, o1, 1, 8, 2, NULL, F, F, NULL, NULL, F, sel, NULL), -1);
     const size_t ssel = ts_score_select_workspace_bytes(o1, 1, 8, &ok);
+    EXPECT(ts_score_select_state_offset(o1, 1, 8, &ok) >= 0, 1);
+    EXPECT(ts_score_select_state_offset(o1, 1, 8, NULL), -1);
     EXPECT(ts_score_select(F, F, F, M, F, o1, 1, 8, 2, &ok, F, F, F, NULL, NULL, F, ssel, NULL), -1);
     EXPECT(ts_score_select(F, F, F, NULL, F, o1, 1, 8, 2, &ok, F, F, F, NULL, NULL, F, ssel - 1, NULL), -3);
     EXPECT(ts_score_select(F, F, F, NULL, F, o1, 1, 12, 8, &ok, F, F, F, NULL, NULL, F, ssel, NULL), -2);

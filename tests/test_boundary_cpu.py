@@ -22,7 +22,7 @@ def header_functions():
 def test_exports_match_header():
     lib = _lib.load()
     names = header_functions()
-    assert len(names) == 24, names
+    assert len(names) == 25, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.SIGNATURES)
@@ -210,3 +210,21 @@ def test_union_validation():
     need_u = L.ts_decode_workspace_bytes(o, c_ok, 1, 32, 8, 2)
     assert need_u > L.ts_decode_workspace_bytes(o, c_ok, 1, 32, 8, 1)      # G * count slots per group
     assert d(c_ok, 32, 8, FAKE, need_u - 1) == -3
+
+
+def test_score_select_state_offset():
+    """The bracket records sit inside the fused call's workspace, 256-byte aligned, with room for
+    B * Hq records of 8 int64; invalid arguments give -1."""
+    L = _lib.load()
+    for offs, Hq in (([0, 131072], 32), ([0, 5000, 5001, 20000], 8), ([0, 1], 4)):
+        o = _offs(offs)
+        B = len(offs) - 1
+        for mode in (0, 1):
+            p = _params(mode)
+            off = L.ts_score_select_state_offset(o, B, Hq, ctypes.byref(p))
+            ws = L.ts_score_select_workspace_bytes(o, B, Hq, ctypes.byref(p))
+            assert off >= 0 and off % 256 == 0 and off + B * Hq * 64 <= ws, (offs, Hq, mode, off, ws)
+    o = _offs([0, 100])
+    assert L.ts_score_select_state_offset(o, 0, 8, ctypes.byref(_params())) == -1
+    assert L.ts_score_select_state_offset(o, 1, 8, ctypes.byref(_params(bden=0))) == -1
+    assert L.ts_score_select_state_offset(None, 1, 8, ctypes.byref(_params())) == -1
