@@ -114,10 +114,13 @@ def parse():
     ap.add_argument("--n", type=int, default=131072)
     ap.add_argument("--budget", type=int, default=20, help="percent (5, 10, 15, 20, 30)")
     ap.add_argument("--mode", choices=["vote", "per-head"], default="vote")
-    ap.add_argument("--workload", choices=["long", "ragged", "snapkv"], default="long",
+    ap.add_argument("--workload", choices=["long", "ragged", "snapkv", "offload"], default="long",
                     help="long: one sequence of --n tokens (the headline); ragged: a batch of 16 sequences of "
                          "16K-64K tokens at a 15%% budget; snapkv: SnapKV prefill-end compression alone "
-                         "(LLaMA-3-70B layer shapes, n = --n, w = 32, c = 4096)")
+                         "(LLaMA-3-70B layer shapes, n = --n, w = 32, c = 4096); offload: the --n-token layer with "
+                         "its KV cache in pinned host memory and the newest --ring tokens in a device ring "
+                         "(selection on the GPU, sparse against dense decode across the host link)")
+    ap.add_argument("--ring", type=int, default=256, help="ring length of the offload workload (a power of two)")
     ap.add_argument("--path", choices=["fused", "calls"], default="fused",
                     help="fused: ts_score_select (with the index append) + ts_sparse_decode; calls: ts_index_append + "
                          "ts_score + ts_select + ts_sparse_decode")
@@ -341,6 +344,103 @@ def bench_snapkv(args, torch, api, synth, dev):
             f.write(line + "\n")
 
 
+def bench_offload(args, torch, api, synth, dev):
+    """The 128K-token layer (32 query / 8 KV heads) with the KV cache in pinned host memory, the
+    newest --ring tokens in a device ring, the index on the device: per call, the GPU selection
+    (ts_score_select), the sparse tiered decode of its list and the dense tiered decode, each timed
+    alone (--steps calls, LLC flushed before each), plus the whole step (selection + sparse decode)
+    and a plain host-to-device copy of 256 MiB as the host link's reference rate."""
+    n, N = args.n, args.ring
+    bnum, bden = synth.BUDGETS[args.budget]
+    print(f"bench: building offload inputs n={n} ring={N} budget={bnum}/{bden}", file=sys.stderr, flush=True)
+    x = synth.config3(args.budget, n)
+    Hq, Hkv = x.Hq, x.Hkv
+    mode = api.MODE_VOTE if args.mode == "vote" else api.MODE_PER_HEAD
+    offs = api.Offsets(x.offsets, dev)
+    Kh = torch.from_numpy(x.K.view(np.int16)).pin_memory()
+    Vh = torch.from_numpy(x.V.view(np.int16)).pin_memory()
+
+    def ring(a):
+        # slot t mod N of the device ring holds position t of the newest N
+        slots = np.empty((N,) + a.shape[1:], np.uint16)
+        slots[np.arange(n - N, n) % N] = a[n - N:]
+        return torch.from_numpy(slots.reshape(1, N, Hkv, 128).view(np.int16)).to(dev)
+
+    Kr, Vr = ring(x.K), ring(x.V)
+    P = torch.from_numpy(x.P).to(dev)
+    kidx = torch.empty((n, Hkv, 32), dtype=torch.int16, device=dev)
+    api.index_append(torch.from_numpy(x.K.view(np.int16)).to(dev), P, kidx, 0)
+    q = torch.from_numpy(x.q.view(np.int16)).to(dev)
+    p = api.params(mode, (bnum, bden))
+    vote = mode == api.MODE_VOTE
+    sel = api.score_select(q, P, kidx, offs, Hkv, p)
+    ws_sel = torch.empty(api.score_select_workspace_bytes(offs, Hq, p), dtype=torch.uint8, device=dev)
+    ch = sel["counts_host"]
+    ws_dec = torch.empty(max(api.decode_workspace_bytes(offs, ch, Hq, Hkv, mode),
+                             api.decode_workspace_bytes(offs, None, Hq, Hkv, api.MODE_VOTE)), dtype=torch.uint8, device=dev)
+    out = torch.empty((1, Hq, 128), dtype=torch.float32, device=dev)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
+    sink = torch.empty((), dtype=torch.float32, device=dev)
+
+    def sparse():
+        api.tiered_decode(q, Kh, Vh, Kr, Vr, offs, mode, sel["idx"], sel["count"], ch, ws=ws_dec, out=out)
+
+    def dense():
+        api.tiered_decode(q, Kh, Vh, Kr, Vr, offs, api.MODE_DENSE, ws=ws_dec, out=out)
+
+    def step():
+        s2 = api.score_select(q, P, kidx, offs, Hkv, p, ws=ws_sel, scores=sel["scores"], idx=sel["idx"],
+                              count=sel["count"])
+        api.tiered_decode(q, Kh, Vh, Kr, Vr, offs, mode, s2["idx"], s2["count"], ch, ws=ws_dec, out=out)
+
+    def timed(fn, steps, warm):
+        for _ in range(warm):
+            torch.sum(flush.view(torch.float32), dim=0, out=sink)
+            fn()
+        torch.cuda.synchronize()
+        evs = []
+        for _ in range(steps):
+            torch.sum(flush.view(torch.float32), dim=0, out=sink)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) * 1e3 for a, b in evs]))
+
+    steps, warm = max(3, args.steps // 10), max(1, args.warmup // 5)
+    us_sparse = timed(sparse, steps, warm)
+    print(f"bench: sparse tiered decode {us_sparse:.1f} us", file=sys.stderr, flush=True)
+    us_dense = timed(dense, max(2, steps // 2), 1)
+    print(f"bench: dense tiered decode {us_dense:.1f} us", file=sys.stderr, flush=True)
+    us_step = timed(step, steps, warm)
+    # the host link's plain copy rate: 256 MiB of pinned host memory to the device
+    hsrc = torch.empty(256 << 20, dtype=torch.uint8).pin_memory()
+    ddst = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    us_copy = timed(lambda: ddst.copy_(hsrc, non_blocking=True), 3, 1)
+    # vote mode: the list's rows older than the ring cross the host link (K and V of every KV head)
+    idx_np = sel["idx"].cpu().numpy()
+    rows_host = int((idx_np < n - N).sum()) if vote else None
+    row_bytes = Hkv * 128 * 2 * 2
+    res = {"metric": "µs per decode-step attention with the KV cache in host memory (128K ctx, 20% budget), 1 MI355X",
+           "value": round(us_step, 2), "unit": "us/step", "n_gpus": 1, "steps": steps, "warmup": warm,
+           "higher_is_better": False, "dtype": "f32", "data": "synthetic",
+           "config": {"workload": f"LLaMA-3-8B-shaped decode layer, n={n}, 32 query / 8 KV heads, KV cache in pinned "
+                                  f"host memory, newest {N} tokens in a device ring, {args.mode} mode, budget "
+                                  f"{bnum}/{bden}", "n": n, "ring": N, "mode": args.mode, "llc": "flushed before each call"},
+           "sparse_decode_us": round(us_sparse, 1), "dense_decode_us": round(us_dense, 1),
+           "dense_over_sparse": round(us_dense / us_sparse, 2),
+           "sparse_host_gbps": round(rows_host * row_bytes / (us_sparse * 1e-6) / 1e9, 1) if vote else None,
+           "dense_host_gbps": round((n - N) * row_bytes / (us_dense * 1e-6) / 1e9, 1),
+           "host_copy_gbps": round((256 << 20) / (us_copy * 1e-6) / 1e9, 1)}
+    line = json.dumps(res)
+    print(line, flush=True)
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(line + "\n")
+
+
 def bench_union(torch, api, L, calls, warm, steps, Hq, Hkv, kmax, offs_max, Kp, Vp, Pp, kip, pref, scp, idp, cnp,
                 wss, ws_ss_n, outp, out, ws_dec, dec_bytes, do_flush, stream_of, chk, dev):
     """Per-head lists decoded through their per-KV-group union: ts_score_select, ts_union_lists,
@@ -447,6 +547,8 @@ def main():
         return bench_ragged(args, torch, api, synth, dev)
     if args.workload == "snapkv":
         return bench_snapkv(args, torch, api, synth, dev)
+    if args.workload == "offload":
+        return bench_offload(args, torch, api, synth, dev)
     n0, steps, warm = args.n, args.steps, args.warmup
     total_steps = steps + warm
     mode = api.MODE_VOTE if args.mode == "vote" else api.MODE_PER_HEAD

@@ -55,6 +55,7 @@ extern "C" {
 #define QASI_MODE_VOTE 0
 #define QASI_MODE_PER_HEAD 1
 #define QASI_MODE_UNION 2      /* ts_decode_workspace_bytes only: the workspace of ts_union_decode */
+#define QASI_MODE_DENSE 3      /* ts_tiered_decode only: every position of each sequence */
 
 /* Selection parameters ([TS] "基本的な統合パターン", TokenSelectConfig).
  *   budget = budget_num / budget_den of the n_b cached tokens; the list length is
@@ -306,6 +307,39 @@ int ts_dense_decode(const uint16_t* q, const uint16_t* K, const uint16_t* V,
                     const int64_t* offsets_dev, const int64_t* offsets_host, int32_t B,
                     int32_t Hq, int32_t Hkv, float* out, void* ws, size_t ws_bytes,
                     hipStream_t stream);
+
+/* Decode over a tiered KV cache ([TB] "Inferenzstrategie": the sink, a circular buffer of the
+ * newest N tokens and the rest of the cache, from which the important tokens are read; [TB]
+ * "Hauptbeiträge" 4 and "Latenz": that rest kept in host memory, with the selection on the GPU and
+ * only the selected rows read across the host link).  The result of ts_sparse_decode
+ * (mode QASI_MODE_VOTE or QASI_MODE_PER_HEAD, same lists and counts) or ts_dense_decode
+ * (QASI_MODE_DENSE; idx and counts are not read and may be NULL) on the logical cache in which
+ * position t of sequence b is
+ *   K_ring[b][t mod N] when t >= n_b - N, else K_main[offsets[b] + t]   (V alike),
+ * up to the grouping of the split-K sums.
+ *   K_main, V_main  bf16 [Ntot][Hkv][128], the positions older than the ring (rows of the newest
+ *                   N positions are never read): device memory, or pinned host memory through the
+ *                   address ts_host_device_pointer gives (the offloaded tier)
+ *   K_ring, V_ring  device bf16 [B][N][Hkv][128]
+ *   ring_len        N, a power of two in [1, 2^20]; a sequence of at most N tokens is read from its
+ *                   ring alone
+ *   ws              workspace of at least ts_decode_workspace_bytes(offsets_host, counts_host (NULL
+ *                   for dense), B, Hq, Hkv, mode (QASI_MODE_VOTE for dense)) bytes.
+ * With a ring of N slots, the index rows of the ring's tokens can be appended N at a time ([TB]
+ * "Optimierungen", Batching): when position n_b is a multiple of N the ring holds positions
+ * [n_b - N, n_b) in slot order, so ts_index_append(K_ring + b*N*Hkv*128, P, k_index,
+ * offsets[b] + n_b - N, N, Hkv) appends all of them.                                        */
+int ts_tiered_decode(const uint16_t* q, const uint16_t* K_main, const uint16_t* V_main,
+                     const uint16_t* K_ring, const uint16_t* V_ring, int64_t ring_len,
+                     const int64_t* offsets_dev, const int64_t* offsets_host, const int32_t* idx,
+                     const int64_t* counts_dev, const int64_t* counts_host, int32_t mode, int32_t B,
+                     int32_t Hq, int32_t Hkv, float* out, void* ws, size_t ws_bytes,
+                     hipStream_t stream);
+
+/* The address kernels use for pinned host memory of the caller (hipHostMalloc, or a pinned
+ * tensor): hipHostGetDevicePointer.  QASI_ERR_HIP when `host` is not pinned host memory.  The
+ * caller keeps the memory alive while work that reads it is in flight.                      */
+int ts_host_device_pointer(const void* host, void** dev);
 
 /* Workspace for snapkv_compress. */
 size_t snapkv_workspace_bytes(int64_t n, int32_t w, int32_t Hq, int32_t Hkv, int64_t c);

@@ -43,6 +43,9 @@ SIGNATURES = {
     "ts_union_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64p, _vp, _vp, _vp, _vp, _i64p, _i32, _i32, _i32, _vp,
                                        _vp, _sz, _vp]),
     "ts_dense_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64p, _i32, _i32, _i32, _vp, _vp, _sz, _vp]),
+    "ts_tiered_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _i64p, _vp, _vp, _i64p, _i32, _i32, _i32,
+                                        _i32, _vp, _vp, _sz, _vp]),
+    "ts_host_device_pointer": (ctypes.c_int, [_vp, ctypes.POINTER(ctypes.c_void_p)]),
     "snapkv_workspace_bytes": (_sz, [_i64, _i32, _i32, _i32, _i64]),
     "snapkv_compress": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _i32, _vp, _vp, _vp, _vp, _vp,
                                        _vp, _sz, _vp]),

@@ -16,6 +16,7 @@ from . import _lib
 MODE_VOTE = 0
 MODE_PER_HEAD = 1
 MODE_UNION = 2          # decode_workspace_bytes only: the workspace of union_decode
+MODE_DENSE = 3          # tiered_decode only: every position of each sequence
 
 
 class QasiError(RuntimeError):
@@ -287,6 +288,41 @@ def dense_decode(q, K, V, offs: Offsets, ws=None, out=None):
         ws = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
     _check(_lib.load().ts_dense_decode(_p(q), _p(K), _p(V), _p(offs.dev), offs.host, B, Hq, Hkv, _p(out), _p(ws),
                                        ws.numel(), _stream()))
+    return out
+
+
+def host_device_pointer(t) -> int:
+    """ts_host_device_pointer: the address kernels use for a pinned host tensor."""
+    if t.device.type != "cpu" or not t.is_pinned():
+        raise ValueError("expected a pinned host tensor")
+    d = ctypes.c_void_p()
+    _check(_lib.load().ts_host_device_pointer(ctypes.c_void_p(t.data_ptr()), ctypes.byref(d)))
+    return int(d.value)
+
+
+def tiered_decode(q, K_main, V_main, K_ring, V_ring, offs: Offsets, mode: int, idx=None, counts_dev=None,
+                  counts_host=None, ws=None, out=None):
+    """ts_tiered_decode: K_main / V_main [Ntot][Hkv][128] on the device or pinned on the host (the
+    offloaded tier), K_ring / V_ring device [B][N][Hkv][128] holding each sequence's newest N
+    positions at slot t mod N.  mode: MODE_VOTE / MODE_PER_HEAD (with idx and counts) or
+    MODE_DENSE."""
+    _bf16_check(q, K_main, V_main, K_ring, V_ring)
+    B, Hq, _ = q.shape
+    N, Hkv = K_ring.shape[1], K_ring.shape[2]
+    dense = mode == MODE_DENSE
+    if out is None:
+        out = torch.empty((B, Hq, 128), dtype=torch.float32, device=q.device)
+    need = decode_workspace_bytes(offs, None if dense else counts_host, Hq, Hkv, MODE_VOTE if dense else mode)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+
+    def addr(t):
+        return ctypes.c_void_p(host_device_pointer(t) if t.device.type == "cpu" else t.data_ptr())
+
+    _check(_lib.load().ts_tiered_decode(_p(q), addr(K_main), addr(V_main), _p(K_ring), _p(V_ring), int(N), _p(offs.dev),
+                                        offs.host, _p(idx), _p(counts_dev),
+                                        None if dense else _host_i64(counts_host), int(mode), B, Hq, Hkv, _p(out),
+                                        _p(ws), ws.numel(), _stream()))
     return out
 
 

@@ -396,6 +396,44 @@ int ts_dense_decode(const uint16_t* q, const uint16_t* K, const uint16_t* V, con
                       "ts_dense_decode launch");
 }
 
+int ts_tiered_decode(const uint16_t* q, const uint16_t* K_main, const uint16_t* V_main, const uint16_t* K_ring,
+                     const uint16_t* V_ring, int64_t ring_len, const int64_t* offsets_dev, const int64_t* offsets_host,
+                     const int32_t* idx, const int64_t* counts_dev, const int64_t* counts_host, int32_t mode, int32_t B,
+                     int32_t Hq, int32_t Hkv, float* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (!aligned16(q) || !aligned16(K_main) || !aligned16(V_main) || !aligned16(K_ring) || !aligned16(V_ring) ||
+        !aligned16(out) || !aligned16(ws))
+        return fail(QASI_ERR_INVALID, "q, K_main, V_main, K_ring, V_ring, out and ws must be non-null and 16-byte aligned");
+    if (ring_len < 1 || ring_len > ((int64_t)1 << 20) || (ring_len & (ring_len - 1)))
+        return fail(QASI_ERR_INVALID, "ring_len=%lld is not a power of two in [1, 2^20]", (long long)ring_len);
+    if (mode != QASI_MODE_VOTE && mode != QASI_MODE_PER_HEAD && mode != QASI_MODE_DENSE)
+        return fail(QASI_ERR_INVALID, "mode=%d (vote, per-head or dense)", mode);
+    if (int r = check_heads(Hq, Hkv)) return r;
+    if (int r = check_offsets(offsets_dev, offsets_host, B, true)) return r;
+    const bool dense = mode == QASI_MODE_DENSE;
+    if (!dense) {
+        if (!idx || (reinterpret_cast<uintptr_t>(idx) & 3u)) return fail(QASI_ERR_INVALID, "idx must be non-null and aligned");
+        if (int r = check_counts(counts_dev, counts_host, offsets_host, B)) return r;
+    }
+    const size_t need = qasi::decode_workspace(offsets_host, dense ? nullptr : counts_host, B, Hq, Hkv, dense ? 2 : mode);
+    if (ws_bytes < need) return fail(QASI_ERR_WORKSPACE, "ts_tiered_decode needs %zu workspace bytes, got %zu", need, ws_bytes);
+    if (int r = init_once()) return r;
+    const qasi::DecRing ring{K_ring, V_ring, ring_len};
+    return hip_status(qasi::launch_tiered_decode(q, K_main, V_main, ring, offsets_dev, offsets_host, dense ? nullptr : idx,
+                                                 dense ? nullptr : counts_dev, dense ? nullptr : counts_host,
+                                                 dense ? 2 : mode, B, Hq, Hkv, out, ws, ws_bytes, stream),
+                      "ts_tiered_decode launch");
+}
+
+int ts_host_device_pointer(const void* host, void** dev) {
+    if (!host || !dev) return fail(QASI_ERR_INVALID, "host and dev must be non-null");
+    *dev = nullptr;
+    void* d = nullptr;
+    const hipError_t e = hipHostGetDevicePointer(&d, const_cast<void*>(host), 0);
+    if (e != hipSuccess) return hip_status(e, "hipHostGetDevicePointer (not pinned host memory?)");
+    *dev = d;
+    return QASI_OK;
+}
+
 size_t snapkv_workspace_bytes(int64_t n, int32_t w, int32_t Hq, int32_t Hkv, int64_t c) {
     if (n <= 0 || w <= 0 || Hq <= 0 || Hkv <= 0 || c <= 0 || Hq % Hkv) return 0;
     return qasi::snapkv_workspace(n, w, Hq, Hkv, c);

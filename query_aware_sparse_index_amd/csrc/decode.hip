@@ -151,7 +151,10 @@ __device__ __forceinline__ void rows_tsum(const float (&v)[NA], float (&o)[NA / 
 // decode of a 16-sequence ragged batch 112 -> 107 us, the 128K vote decode 37.2 -> 36.7 us.
 __host__ __device__ constexpr int dec_min_blocks(int G, int mode) { return (mode != 1 && G <= 4) ? 4 : 1; }
 
-template <int G, int MODE>
+// RING: positions >= n_b - N are read from slot t mod N of the sequence's ring (`ring`), the older
+// ones from K / V (a tiered cache: the newest tokens in a device ring, the rest possibly in host
+// memory mapped for the device).
+template <int G, int MODE, bool RING = false>
 __global__ __launch_bounds__(kDecWaves * 64, dec_min_blocks(G, MODE)) void decode_partial_kernel(const uint16_t* __restrict__ q,
                                                                        const uint16_t* __restrict__ K,
                                                                        const uint16_t* __restrict__ V,
@@ -161,7 +164,8 @@ __global__ __launch_bounds__(kDecWaves * 64, dec_min_blocks(G, MODE)) void decod
                                                                        int Hkv, int EB, float* __restrict__ part_acc,
                                                                        float2* __restrict__ part_ml,
                                                                        const uint8_t* __restrict__ umask,
-                                                                       const int64_t* __restrict__ ucount) {
+                                                                       const int64_t* __restrict__ ucount,
+                                                                       DecRing ring) {
     constexpr int GH = dec_gh(G, MODE);
     constexpr int EPR = kDecSub / 4;               // entries per lane row and sub-batch
     constexpr int NV = GH * EPR;                   // (head, entry) scores of a row
@@ -254,16 +258,41 @@ __global__ __launch_bounds__(kDecWaves * 64, dec_min_blocks(G, MODE)) void decod
     const uint16_t* Kg = K + (off * Hkv + g) * kD + p * 8;
     const uint16_t* Vg = V + (off * Hkv + g) * kD + p * 8;
     const int64_t rstride = (int64_t)Hkv * kD;
+    // ring: its first position (negative when the whole sequence fits in it) and slot mask; a
+    // ring slot is a row of Hkv * 128 values like a row of the main cache
+    const uint16_t* Kr = Kg;
+    const uint16_t* Vr = Vg;
+    int32_t rfirst = 0, rmask = 0;
+    if constexpr (RING) {
+        Kr = ring.K + ((int64_t)b * ring.N * Hkv + g) * kD + p * 8;
+        Vr = ring.V + ((int64_t)b * ring.N * Hkv + g) * kD + p * 8;
+        rfirst = (int32_t)((int64_t)nmax + 1 - ring.N);
+        rmask = (int32_t)ring.N - 1;
+    }
     // em: bit k set when entry k of the lane's row is an empty slot
     auto issue = [&](int sb, uint4 (&kb)[EPR], uint4 (&vb)[EPR], int& em, uint32_t& hm) {
         const int4 t = s_tok[wid][(sb * kDecSub + row * EPR) / 4];
         if (MODE == 3) hm = s_msk[wid][(sb * kDecSub + row * EPR) / 4];
         const int tt[4] = {t.x < 0 ? 0 : t.x, t.y < 0 ? 0 : t.y, t.z < 0 ? 0 : t.z, t.w < 0 ? 0 : t.w};
         em = (t.x < 0 ? 1 : 0) | (t.y < 0 ? 2 : 0) | (t.z < 0 ? 4 : 0) | (t.w < 0 ? 8 : 0);
+        if constexpr (RING) {
+            bool inr[EPR];
+            int32_t row[EPR];
 #pragma unroll
-        for (int k = 0; k < EPR; ++k) kb[k] = ld16(Kg + tt[k] * rstride);
+            for (int k = 0; k < EPR; ++k) {
+                inr[k] = tt[k] >= rfirst;
+                row[k] = inr[k] ? (tt[k] & rmask) : tt[k];
+            }
 #pragma unroll
-        for (int k = 0; k < EPR; ++k) vb[k] = ld16(Vg + tt[k] * rstride);
+            for (int k = 0; k < EPR; ++k) kb[k] = ld16((inr[k] ? Kr : Kg) + row[k] * rstride);
+#pragma unroll
+            for (int k = 0; k < EPR; ++k) vb[k] = ld16((inr[k] ? Vr : Vg) + row[k] * rstride);
+        } else {
+#pragma unroll
+            for (int k = 0; k < EPR; ++k) kb[k] = ld16(Kg + tt[k] * rstride);
+#pragma unroll
+            for (int k = 0; k < EPR; ++k) vb[k] = ld16(Vg + tt[k] * rstride);
+        }
     };
 
     float m_run = -INFINITY, l_run = 0.f;         // this lane's head (hh_l)
@@ -474,23 +503,25 @@ static int device_cus() {
     return cus[dev];
 }
 
-template <int MODE>
+template <int MODE, bool RING>
 static const void* partial_fn(int G) {
     switch (G) {
-        case 1: return reinterpret_cast<const void*>(decode_partial_kernel<1, MODE>);
-        case 2: return reinterpret_cast<const void*>(decode_partial_kernel<2, MODE>);
-        case 4: return reinterpret_cast<const void*>(decode_partial_kernel<4, MODE>);
-        default: return reinterpret_cast<const void*>(decode_partial_kernel<8, MODE>);
+        case 1: return reinterpret_cast<const void*>(decode_partial_kernel<1, MODE, RING>);
+        case 2: return reinterpret_cast<const void*>(decode_partial_kernel<2, MODE, RING>);
+        case 4: return reinterpret_cast<const void*>(decode_partial_kernel<4, MODE, RING>);
+        default: return reinterpret_cast<const void*>(decode_partial_kernel<8, MODE, RING>);
     }
 }
 // Resident blocks per compute unit of an instantiation (queried once).
-static int partial_blocks_per_cu(int G, int mode) {
-    static int cache[4][4] = {};
+static int partial_blocks_per_cu(int G, int mode, bool ring) {
+    static int cache[2][4][4] = {};
     const int lg = G == 1 ? 0 : (G == 2 ? 1 : (G == 4 ? 2 : 3));
-    int& c = cache[mode][lg];
+    int& c = cache[ring ? 1 : 0][mode][lg];
     if (c == 0) {
-        const void* f = mode == 0 ? partial_fn<0>(G)
-                                  : (mode == 1 ? partial_fn<1>(G) : (mode == 2 ? partial_fn<2>(G) : partial_fn<3>(G)));
+        const void* f = ring ? (mode == 0 ? partial_fn<0, true>(G) : (mode == 1 ? partial_fn<1, true>(G) : partial_fn<2, true>(G)))
+                             : (mode == 0 ? partial_fn<0, false>(G)
+                                          : (mode == 1 ? partial_fn<1, false>(G)
+                                                       : (mode == 2 ? partial_fn<2, false>(G) : partial_fn<3, false>(G))));
         int n = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, kDecWaves * 64, 0) != hipSuccess || n <= 0) n = 2;
         c = n;
@@ -508,8 +539,8 @@ static int partial_blocks_per_cu(int G, int mode) {
 // 69.7 against 80.8 us with 256 entries per wave).  len(b) is the list length (or, for the dense
 // decode, the sequence length) of sequence b.
 template <class Len>
-static int decode_eb(Len len, int B, int HW, int G, int mode) {
-    const int64_t target = (int64_t)partial_blocks_per_cu(G, mode) * device_cus();
+static int decode_eb(Len len, int B, int HW, int G, int mode, bool ring = false) {
+    const int64_t target = (int64_t)partial_blocks_per_cu(G, mode, ring) * device_cus();
     int64_t entries = 0;
     for (int b = 0; b < B; ++b) entries += len(b);
     const int64_t lo = kDecWaves * kDecSub, hi = kDecWaves * (mode == 1 ? 64 : (mode == 2 ? 256 : kDecMaxEW));
@@ -543,17 +574,18 @@ size_t decode_workspace(const int64_t* offsets_host, const int64_t* counts_host,
     return w.size();
 }
 
-template <int MODE>
+template <int MODE, bool RING = false>
 static hipError_t launch_partial_G(int G, dim3 grid, hipStream_t stream, const uint16_t* q, const uint16_t* K,
                                    const uint16_t* V, const I64Arg& offsets, const int32_t* idx,
                                    const I64Arg& counts, int B, int Hq, int Hkv, int EB, float* part, float2* ml,
-                                   const uint8_t* umask = nullptr, const int64_t* ucount = nullptr) {
+                                   const uint8_t* umask = nullptr, const int64_t* ucount = nullptr,
+                                   const DecRing& ring = DecRing{nullptr, nullptr, 0}) {
     const dim3 block(kDecWaves * 64);
     switch (G) {
-        case 1: hipLaunchKernelGGL((decode_partial_kernel<1, MODE>), grid, block, 0, stream, q, K, V, offsets, idx, counts, B, Hq, Hkv, EB, part, ml, umask, ucount); break;
-        case 2: hipLaunchKernelGGL((decode_partial_kernel<2, MODE>), grid, block, 0, stream, q, K, V, offsets, idx, counts, B, Hq, Hkv, EB, part, ml, umask, ucount); break;
-        case 4: hipLaunchKernelGGL((decode_partial_kernel<4, MODE>), grid, block, 0, stream, q, K, V, offsets, idx, counts, B, Hq, Hkv, EB, part, ml, umask, ucount); break;
-        case 8: hipLaunchKernelGGL((decode_partial_kernel<8, MODE>), grid, block, 0, stream, q, K, V, offsets, idx, counts, B, Hq, Hkv, EB, part, ml, umask, ucount); break;
+        case 1: hipLaunchKernelGGL((decode_partial_kernel<1, MODE, RING>), grid, block, 0, stream, q, K, V, offsets, idx, counts, B, Hq, Hkv, EB, part, ml, umask, ucount, ring); break;
+        case 2: hipLaunchKernelGGL((decode_partial_kernel<2, MODE, RING>), grid, block, 0, stream, q, K, V, offsets, idx, counts, B, Hq, Hkv, EB, part, ml, umask, ucount, ring); break;
+        case 4: hipLaunchKernelGGL((decode_partial_kernel<4, MODE, RING>), grid, block, 0, stream, q, K, V, offsets, idx, counts, B, Hq, Hkv, EB, part, ml, umask, ucount, ring); break;
+        case 8: hipLaunchKernelGGL((decode_partial_kernel<8, MODE, RING>), grid, block, 0, stream, q, K, V, offsets, idx, counts, B, Hq, Hkv, EB, part, ml, umask, ucount, ring); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -564,15 +596,14 @@ __global__ void lengths_kernel(I64Arg offsets, int B, int64_t* __restrict__ lens
     for (int b = threadIdx.x; b < B; b += blockDim.x) lens[b] = offsets[b + 1] - offsets[b];
 }
 
-hipError_t launch_sparse_decode(const uint16_t* q, const uint16_t* K, const uint16_t* V, const int64_t* offsets_dev,
-                                const int64_t* offsets_host, const int32_t* idx, const int64_t* counts_dev,
-                                const int64_t* counts_host, int mode, int B, int Hq, int Hkv, float* out, void* ws,
-                                size_t ws_bytes, hipStream_t stream) {
+// List decode (vote or per-head lists); ring: the tiered cache's ring, or null.
+static hipError_t sparse_decode(const uint16_t* q, const uint16_t* K, const uint16_t* V, const DecRing* ring,
+                                const int64_t* offsets_dev, const int64_t* offsets_host, const int32_t* idx,
+                                const int64_t* counts_dev, const int64_t* counts_host, int mode, int B, int Hq, int Hkv,
+                                float* out, void* ws, size_t ws_bytes, hipStream_t stream) {
     if (decode_workspace(offsets_host, counts_host, B, Hq, Hkv, mode) > ws_bytes) return hipErrorInvalidValue;
     const int G = Hq / Hkv;
-    int64_t total = 0;
-    for (int b = 0; b < B; ++b) total += counts_host[b];
-    const int EB = decode_eb([&](int b) { return counts_host[b]; }, B, mode == 1 ? Hq : Hkv, G, mode);
+    const int EB = decode_eb([&](int b) { return counts_host[b]; }, B, mode == 1 ? Hq : Hkv, G, mode, ring != nullptr);
     WsCarver w(ws);
     w.take<int64_t>((size_t)B + 1);
     const int64_t items = list_items(counts_host, B, EB, 1);
@@ -582,16 +613,27 @@ hipError_t launch_sparse_decode(const uint16_t* q, const uint16_t* K, const uint
     const I64Arg cnts = i64_arg(counts_dev, counts_host, B);
     if (items == 0) return hipSuccess;
     hipError_t e;
-    if (mode == 0) e = launch_partial_G<0>(G, dim3((unsigned)(items * Hkv)), stream, q, K, V, offs, idx, cnts, B, Hq, Hkv, EB, part, ml);
-    else {
-        // blocks of the (item, KV head) pairs in groups of 8, G heads each (see the kernel); the
-        // pairs past items * Hkv find no list chunk and return
-        const int64_t pairs = (items * Hkv + 7) / 8 * 8;
-        e = launch_partial_G<1>(G, dim3((unsigned)(pairs * G)), stream, q, K, V, offs, idx, cnts, B, Hq, Hkv, EB, part, ml);
+    // blocks of the (item, KV head) pairs in groups of 8, G heads each in per-head mode (see the
+    // kernel); the pairs past items * Hkv find no list chunk and return
+    const dim3 grid = mode == 0 ? dim3((unsigned)(items * Hkv)) : dim3((unsigned)((items * Hkv + 7) / 8 * 8 * G));
+    if (ring) {
+        if (mode == 0) e = launch_partial_G<0, true>(G, grid, stream, q, K, V, offs, idx, cnts, B, Hq, Hkv, EB, part, ml, nullptr, nullptr, *ring);
+        else e = launch_partial_G<1, true>(G, grid, stream, q, K, V, offs, idx, cnts, B, Hq, Hkv, EB, part, ml, nullptr, nullptr, *ring);
+    } else {
+        if (mode == 0) e = launch_partial_G<0>(G, grid, stream, q, K, V, offs, idx, cnts, B, Hq, Hkv, EB, part, ml);
+        else e = launch_partial_G<1>(G, grid, stream, q, K, V, offs, idx, cnts, B, Hq, Hkv, EB, part, ml);
     }
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(decode_merge_kernel, dim3(B * Hq), dim3(kMergeThreads), 0, stream, part, ml, cnts, B, Hq, EB, 1, out);
     return hipGetLastError();
+}
+
+hipError_t launch_sparse_decode(const uint16_t* q, const uint16_t* K, const uint16_t* V, const int64_t* offsets_dev,
+                                const int64_t* offsets_host, const int32_t* idx, const int64_t* counts_dev,
+                                const int64_t* counts_host, int mode, int B, int Hq, int Hkv, float* out, void* ws,
+                                size_t ws_bytes, hipStream_t stream) {
+    return sparse_decode(q, K, V, nullptr, offsets_dev, offsets_host, idx, counts_dev, counts_host, mode, B, Hq, Hkv,
+                         out, ws, ws_bytes, stream);
 }
 
 hipError_t launch_union_decode(const uint16_t* q, const uint16_t* K, const uint16_t* V, const int64_t* offsets_dev,
@@ -658,12 +700,12 @@ hipError_t launch_sparse_decode_noalloc(const uint16_t* q, const uint16_t* K, co
                                 out, ws, kNoAllocScratchBytes, stream);
 }
 
-hipError_t launch_dense_decode(const uint16_t* q, const uint16_t* K, const uint16_t* V, const int64_t* offsets_dev,
-                               const int64_t* offsets_host, int B, int Hq, int Hkv, float* out, void* ws,
-                               size_t ws_bytes, hipStream_t stream) {
+static hipError_t dense_decode(const uint16_t* q, const uint16_t* K, const uint16_t* V, const DecRing* ring,
+                               const int64_t* offsets_dev, const int64_t* offsets_host, int B, int Hq, int Hkv,
+                               float* out, void* ws, size_t ws_bytes, hipStream_t stream) {
     if (decode_workspace(offsets_host, nullptr, B, Hq, Hkv, 2) > ws_bytes) return hipErrorInvalidValue;
     const int G = Hq / Hkv;
-    const int EB = decode_eb([&](int b) { return offsets_host[b + 1] - offsets_host[b]; }, B, Hkv, G, 2);
+    const int EB = decode_eb([&](int b) { return offsets_host[b + 1] - offsets_host[b]; }, B, Hkv, G, 2, ring != nullptr);
     int64_t items = 0;
     for (int b = 0; b < B; ++b) items += (offsets_host[b + 1] - offsets_host[b] + EB - 1) / EB;
     WsCarver w(ws);
@@ -677,11 +719,30 @@ hipError_t launch_dense_decode(const uint16_t* q, const uint16_t* K, const uint1
     const I64Arg lns = i64_arg(lens, B == 1 ? &hl : nullptr, B);
     if (items == 0) return hipSuccess;
     if (B != 1) hipLaunchKernelGGL(lengths_kernel, dim3(1), dim3(256), 0, stream, offs, B, lens);
-    hipError_t e = launch_partial_G<2>(G, dim3((unsigned)(items * Hkv)), stream, q, K, V, offs, nullptr, lns, B, Hq,
-                                       Hkv, EB, part, ml);
+    const dim3 grid((unsigned)(items * Hkv));
+    hipError_t e = ring ? launch_partial_G<2, true>(G, grid, stream, q, K, V, offs, nullptr, lns, B, Hq, Hkv, EB, part,
+                                                    ml, nullptr, nullptr, *ring)
+                        : launch_partial_G<2>(G, grid, stream, q, K, V, offs, nullptr, lns, B, Hq, Hkv, EB, part, ml);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(decode_merge_kernel, dim3(B * Hq), dim3(kMergeThreads), 0, stream, part, ml, lns, B, Hq, EB, 1, out);
     return hipGetLastError();
+}
+
+hipError_t launch_dense_decode(const uint16_t* q, const uint16_t* K, const uint16_t* V, const int64_t* offsets_dev,
+                               const int64_t* offsets_host, int B, int Hq, int Hkv, float* out, void* ws,
+                               size_t ws_bytes, hipStream_t stream) {
+    return dense_decode(q, K, V, nullptr, offsets_dev, offsets_host, B, Hq, Hkv, out, ws, ws_bytes, stream);
+}
+
+hipError_t launch_tiered_decode(const uint16_t* q, const uint16_t* K, const uint16_t* V, const DecRing& ring,
+                                const int64_t* offsets_dev, const int64_t* offsets_host, const int32_t* idx,
+                                const int64_t* counts_dev, const int64_t* counts_host, int mode, int B, int Hq,
+                                int Hkv, float* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (ring.N < 1 || (ring.N & (ring.N - 1)) || !ring.K || !ring.V) return hipErrorInvalidValue;
+    if (mode == 2) return dense_decode(q, K, V, &ring, offsets_dev, offsets_host, B, Hq, Hkv, out, ws, ws_bytes, stream);
+    if (mode != 0 && mode != 1) return hipErrorInvalidValue;
+    return sparse_decode(q, K, V, &ring, offsets_dev, offsets_host, idx, counts_dev, counts_host, mode, B, Hq, Hkv,
+                         out, ws, ws_bytes, stream);
 }
 
 }  // namespace qasi

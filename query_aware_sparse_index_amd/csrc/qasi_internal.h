@@ -96,6 +96,13 @@ hipError_t launch_union(const int32_t* idx, const int64_t* counts_dev, const int
 
 // ---- decode
 // mode: 0 vote lists, 1 per-head lists, 2 dense (counts_host NULL), 3 union lists (G*count_b slots)
+// The newest N positions of every sequence in a ring of N slots: position t of sequence b at slot
+// t mod N of K / V [B][N][Hkv][128] (N a power of two); the older positions in the main cache.
+struct DecRing {
+    const uint16_t* K;
+    const uint16_t* V;
+    int64_t N;
+};
 size_t decode_workspace(const int64_t* offsets_host, const int64_t* counts_host, int B, int Hq, int Hkv, int mode);
 hipError_t launch_sparse_decode(const uint16_t* q, const uint16_t* K, const uint16_t* V, const int64_t* offsets_dev,
                                 const int64_t* offsets_host, const int32_t* idx, const int64_t* counts_dev,
@@ -118,6 +125,12 @@ hipError_t launch_union_decode(const uint16_t* q, const uint16_t* K, const uint1
 hipError_t launch_dense_decode(const uint16_t* q, const uint16_t* K, const uint16_t* V, const int64_t* offsets_dev,
                                const int64_t* offsets_host, int B, int Hq, int Hkv, float* out, void* ws,
                                size_t ws_bytes, hipStream_t stream);
+// Decode over a tiered cache (mode 0, 1 or 2 as above): K / V hold the positions older than the
+// ring (device memory, or host memory mapped for the device), `ring` the newest N.
+hipError_t launch_tiered_decode(const uint16_t* q, const uint16_t* K, const uint16_t* V, const DecRing& ring,
+                                const int64_t* offsets_dev, const int64_t* offsets_host, const int32_t* idx,
+                                const int64_t* counts_dev, const int64_t* counts_host, int mode, int B, int Hq,
+                                int Hkv, float* out, void* ws, size_t ws_bytes, hipStream_t stream);
 
 // ---- SnapKV
 size_t snapkv_workspace(int64_t n, int w, int Hq, int Hkv, int64_t c);

@@ -22,7 +22,7 @@ def header_functions():
 def test_exports_match_header():
     lib = _lib.load()
     names = header_functions()
-    assert len(names) == 25, names
+    assert len(names) == 27, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.SIGNATURES)
@@ -228,3 +228,31 @@ def test_score_select_state_offset():
     assert L.ts_score_select_state_offset(o, 0, 8, ctypes.byref(_params())) == -1
     assert L.ts_score_select_state_offset(o, 1, 8, ctypes.byref(_params(bden=0))) == -1
     assert L.ts_score_select_state_offset(None, 1, 8, ctypes.byref(_params())) == -1
+
+
+def test_tiered_decode_validation():
+    """ts_tiered_decode rejects a ring length that is not a power of two in [1, 2^20], the union
+    mode, null or misaligned tier pointers and a short workspace before any HIP call;
+    ts_host_device_pointer rejects null pointers."""
+    L = _lib.load()
+    o = _offs([0, 1000])
+    c = (ctypes.c_int64 * 1)(200)
+
+    def call(N=64, mode=0, Kr=FAKE, Vr=FAKE, Km=FAKE, ws_bytes=1 << 40, Hq=8, Hkv=2, idx=FAKE):
+        return L.ts_tiered_decode(FAKE, Km, FAKE, Kr, Vr, N, FAKE, o, idx, FAKE, c, mode, 1, Hq, Hkv, FAKE, FAKE,
+                                  ws_bytes, None)
+    for N in (0, 3, 96, (1 << 20) * 2, -4):
+        assert call(N=N) == -1, N
+        assert "power of two" in err()
+    assert call(mode=2) == -1                     # the union lists have their own decode
+    assert call(mode=4) == -1
+    assert call(Kr=None) == -1
+    assert call(Vr=MIS) == -1
+    assert call(Km=MIS) == -1
+    assert call(Hq=24, Hkv=8) == -2
+    assert call(idx=None) == -1                   # list modes need the lists
+    assert call(ws_bytes=16) == -3
+    assert call(mode=3, idx=None, ws_bytes=16) == -3   # dense: no lists, then the workspace check
+    d = ctypes.c_void_p()
+    assert L.ts_host_device_pointer(None, ctypes.byref(d)) == -1
+    assert L.ts_host_device_pointer(FAKE, None) == -1
