@@ -244,6 +244,16 @@ int ts_sparse_decode(const uint16_t* q, const uint16_t* K, const uint16_t* V,
                      int32_t B, int32_t Hq, int32_t Hkv, float* out, void* ws, size_t ws_bytes,
                      hipStream_t stream);
 
+/* For measurement: ts_sparse_decode, then a wait for the call's own work on `stream`, and
+ * *gather_us receives the gather kernel's duration in microseconds, taken from its dispatch
+ * start and end timestamps (the figure a kernel trace reports for it, without the merge kernel
+ * and the launch gaps).  Arguments, validation and results otherwise as for ts_sparse_decode. */
+int ts_sparse_decode_timed(const uint16_t* q, const uint16_t* K, const uint16_t* V,
+                           const int64_t* offsets_dev, const int64_t* offsets_host, const int32_t* idx,
+                           const int64_t* counts_dev, const int64_t* counts_host, int32_t mode,
+                           int32_t B, int32_t Hq, int32_t Hkv, float* out, void* ws, size_t ws_bytes,
+                           hipStream_t stream, float* gather_us);
+
 /* For callers that cannot allocate (code under HIP graph capture, tight serving loops,
  * harnesses that forbid device allocation): ts_sparse_decode without a workspace.  The split-K
  * partials live in a static device array of the library (64 MiB on each device it runs on,

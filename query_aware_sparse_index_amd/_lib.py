@@ -36,6 +36,8 @@ SIGNATURES = {
     "ts_decode_workspace_bytes": (_sz, [_i64p, _i64p, _i32, _i32, _i32, _i32]),
     "ts_sparse_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64p, _vp, _vp, _i64p, _i32, _i32, _i32, _i32, _vp,
                                         _vp, _sz, _vp]),
+    "ts_sparse_decode_timed": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64p, _vp, _vp, _i64p, _i32, _i32, _i32, _i32, _vp,
+                                              _vp, _sz, _vp, ctypes.POINTER(ctypes.c_float)]),
     "ts_sparse_decode_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64p, _vp, _vp, _i64p, _i32, _i32, _i32, _i32,
                                                 _vp, _vp]),
     "ts_union_workspace_bytes": (_sz, [_i64p, _i32, _i32]),

@@ -225,6 +225,24 @@ def sparse_decode(q, K, V, offs: Offsets, idx, counts_dev, counts_host, mode: in
     return out
 
 
+def sparse_decode_timed(q, K, V, offs: Offsets, idx, counts_dev, counts_host, mode: int, ws=None, out=None):
+    """ts_sparse_decode_timed: sparse_decode, waiting for it; returns (out, the gather kernel's
+    duration in microseconds from its dispatch timestamps)."""
+    _bf16_check(q, K, V)
+    B, Hq, _ = q.shape
+    Hkv = K.shape[1]
+    if out is None:
+        out = torch.empty((B, Hq, 128), dtype=torch.float32, device=q.device)
+    need = decode_workspace_bytes(offs, counts_host, Hq, Hkv, mode)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 256), dtype=torch.uint8, device=q.device)
+    us = ctypes.c_float()
+    _check(_lib.load().ts_sparse_decode_timed(_p(q), _p(K), _p(V), _p(offs.dev), offs.host, _p(idx), _p(counts_dev),
+                                              _host_i64(counts_host), int(mode), B, Hq, Hkv, _p(out), _p(ws),
+                                              ws.numel(), _stream(), ctypes.byref(us)))
+    return out, float(us.value)
+
+
 def sparse_decode_noalloc(q, K, V, offs: Offsets, idx, counts_dev, counts_host, mode: int, out=None):
     """ts_sparse_decode_noalloc: sparse_decode with the partials in the library's static device
     scratch (no workspace argument).  Calls on one device must not overlap."""

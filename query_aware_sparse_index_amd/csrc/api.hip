@@ -275,10 +275,11 @@ size_t ts_decode_workspace_bytes(const int64_t* offsets_host, const int64_t* cou
     return qasi::decode_workspace(offsets_host, counts_host, B, Hq, Hkv, mode == QASI_MODE_UNION ? 3 : mode);
 }
 
-int ts_sparse_decode(const uint16_t* q, const uint16_t* K, const uint16_t* V, const int64_t* offsets_dev,
-                     const int64_t* offsets_host, const int32_t* idx, const int64_t* counts_dev,
-                     const int64_t* counts_host, int32_t mode, int32_t B, int32_t Hq, int32_t Hkv, float* out, void* ws,
-                     size_t ws_bytes, hipStream_t stream) {
+// Checks shared by ts_sparse_decode and its timed variant (everything before the first HIP call).
+static int sparse_decode_checks(const uint16_t* q, const uint16_t* K, const uint16_t* V, const int64_t* offsets_dev,
+                                const int64_t* offsets_host, const int32_t* idx, const int64_t* counts_dev,
+                                const int64_t* counts_host, int32_t mode, int32_t B, int32_t Hq, int32_t Hkv,
+                                const float* out, const void* ws, size_t ws_bytes, const char* name) {
     if (!aligned16(q) || !aligned16(K) || !aligned16(V) || !aligned16(out) || !aligned16(ws))
         return fail(QASI_ERR_INVALID, "q, K, V, out and ws must be non-null and 16-byte aligned");
     if (!idx || (reinterpret_cast<uintptr_t>(idx) & 3u)) return fail(QASI_ERR_INVALID, "idx must be non-null and aligned");
@@ -293,11 +294,45 @@ int ts_sparse_decode(const uint16_t* q, const uint16_t* K, const uint16_t* V, co
             return fail(QASI_ERR_INVALID, "counts[%d]=%lld outside [1, n_b=%lld]", b, (long long)counts_host[b], (long long)n);
     }
     size_t need = qasi::decode_workspace(offsets_host, counts_host, B, Hq, Hkv, mode);
-    if (ws_bytes < need) return fail(QASI_ERR_WORKSPACE, "ts_sparse_decode needs %zu workspace bytes, got %zu", need, ws_bytes);
+    if (ws_bytes < need) return fail(QASI_ERR_WORKSPACE, "%s needs %zu workspace bytes, got %zu", name, need, ws_bytes);
+    return QASI_OK;
+}
+
+int ts_sparse_decode(const uint16_t* q, const uint16_t* K, const uint16_t* V, const int64_t* offsets_dev,
+                     const int64_t* offsets_host, const int32_t* idx, const int64_t* counts_dev,
+                     const int64_t* counts_host, int32_t mode, int32_t B, int32_t Hq, int32_t Hkv, float* out, void* ws,
+                     size_t ws_bytes, hipStream_t stream) {
+    if (int r = sparse_decode_checks(q, K, V, offsets_dev, offsets_host, idx, counts_dev, counts_host, mode, B, Hq, Hkv,
+                                     out, ws, ws_bytes, "ts_sparse_decode"))
+        return r;
     if (int r = init_once()) return r;
     return hip_status(qasi::launch_sparse_decode(q, K, V, offsets_dev, offsets_host, idx, counts_dev, counts_host, mode,
                                                  B, Hq, Hkv, out, ws, ws_bytes, stream),
                       "ts_sparse_decode launch");
+}
+
+int ts_sparse_decode_timed(const uint16_t* q, const uint16_t* K, const uint16_t* V, const int64_t* offsets_dev,
+                           const int64_t* offsets_host, const int32_t* idx, const int64_t* counts_dev,
+                           const int64_t* counts_host, int32_t mode, int32_t B, int32_t Hq, int32_t Hkv, float* out,
+                           void* ws, size_t ws_bytes, hipStream_t stream, float* gather_us) {
+    if (!gather_us) return fail(QASI_ERR_INVALID, "gather_us must be non-null");
+    if (int r = sparse_decode_checks(q, K, V, offsets_dev, offsets_host, idx, counts_dev, counts_host, mode, B, Hq, Hkv,
+                                     out, ws, ws_bytes, "ts_sparse_decode_timed"))
+        return r;
+    if (int r = init_once()) return r;
+    hipEvent_t t0 = nullptr, t1 = nullptr;
+    hipError_t e = hipEventCreate(&t0);
+    if (e == hipSuccess) e = hipEventCreate(&t1);
+    if (e == hipSuccess)
+        e = qasi::launch_sparse_decode(q, K, V, offsets_dev, offsets_host, idx, counts_dev, counts_host, mode, B, Hq, Hkv,
+                                       out, ws, ws_bytes, stream, t0, t1);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, t0, t1);
+    if (t0) (void)hipEventDestroy(t0);
+    if (t1) (void)hipEventDestroy(t1);
+    if (e == hipSuccess) *gather_us = ms * 1000.f;
+    return hip_status(e, "ts_sparse_decode_timed");
 }
 
 int ts_sparse_decode_noalloc(const uint16_t* q, const uint16_t* K, const uint16_t* V, const int64_t* offsets_dev,

@@ -23,6 +23,8 @@
 //   the 4 waves' (m, l, acc) merge in LDS into the block's partial (M, L, A[128]) per head.
 // The merge kernel combines the ranges of a sequence: out = sum_c A_c 2^(M_c - M) /
 // sum_c L_c 2^(M_c - M).
+#include <hip/hip_ext.h>
+
 #include <mutex>
 
 #include "qasi_device.h"
@@ -574,13 +576,26 @@ size_t decode_workspace(const int64_t* offsets_host, const int64_t* counts_host,
     return w.size();
 }
 
+// t0 / t1: when given, the launch records them at the kernel's start and end (its dispatch
+// timestamps), for a duration that matches a kernel trace's.
 template <int MODE, bool RING = false>
 static hipError_t launch_partial_G(int G, dim3 grid, hipStream_t stream, const uint16_t* q, const uint16_t* K,
                                    const uint16_t* V, const I64Arg& offsets, const int32_t* idx,
                                    const I64Arg& counts, int B, int Hq, int Hkv, int EB, float* part, float2* ml,
                                    const uint8_t* umask = nullptr, const int64_t* ucount = nullptr,
-                                   const DecRing& ring = DecRing{nullptr, nullptr, 0}) {
+                                   const DecRing& ring = DecRing{nullptr, nullptr, 0}, hipEvent_t t0 = nullptr,
+                                   hipEvent_t t1 = nullptr) {
     const dim3 block(kDecWaves * 64);
+    if (t0 && t1) {
+        switch (G) {
+            case 1: hipExtLaunchKernelGGL((decode_partial_kernel<1, MODE, RING>), grid, block, 0, stream, t0, t1, 0, q, K, V, offsets, idx, counts, B, Hq, Hkv, EB, part, ml, umask, ucount, ring); break;
+            case 2: hipExtLaunchKernelGGL((decode_partial_kernel<2, MODE, RING>), grid, block, 0, stream, t0, t1, 0, q, K, V, offsets, idx, counts, B, Hq, Hkv, EB, part, ml, umask, ucount, ring); break;
+            case 4: hipExtLaunchKernelGGL((decode_partial_kernel<4, MODE, RING>), grid, block, 0, stream, t0, t1, 0, q, K, V, offsets, idx, counts, B, Hq, Hkv, EB, part, ml, umask, ucount, ring); break;
+            case 8: hipExtLaunchKernelGGL((decode_partial_kernel<8, MODE, RING>), grid, block, 0, stream, t0, t1, 0, q, K, V, offsets, idx, counts, B, Hq, Hkv, EB, part, ml, umask, ucount, ring); break;
+            default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
     switch (G) {
         case 1: hipLaunchKernelGGL((decode_partial_kernel<1, MODE, RING>), grid, block, 0, stream, q, K, V, offsets, idx, counts, B, Hq, Hkv, EB, part, ml, umask, ucount, ring); break;
         case 2: hipLaunchKernelGGL((decode_partial_kernel<2, MODE, RING>), grid, block, 0, stream, q, K, V, offsets, idx, counts, B, Hq, Hkv, EB, part, ml, umask, ucount, ring); break;
@@ -596,11 +611,13 @@ __global__ void lengths_kernel(I64Arg offsets, int B, int64_t* __restrict__ lens
     for (int b = threadIdx.x; b < B; b += blockDim.x) lens[b] = offsets[b + 1] - offsets[b];
 }
 
-// List decode (vote or per-head lists); ring: the tiered cache's ring, or null.
+// List decode (vote or per-head lists); ring: the tiered cache's ring, or null; t0 / t1: events
+// recorded at the gather kernel's start and end, or null.
 static hipError_t sparse_decode(const uint16_t* q, const uint16_t* K, const uint16_t* V, const DecRing* ring,
                                 const int64_t* offsets_dev, const int64_t* offsets_host, const int32_t* idx,
                                 const int64_t* counts_dev, const int64_t* counts_host, int mode, int B, int Hq, int Hkv,
-                                float* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+                                float* out, void* ws, size_t ws_bytes, hipStream_t stream, hipEvent_t t0 = nullptr,
+                                hipEvent_t t1 = nullptr) {
     if (decode_workspace(offsets_host, counts_host, B, Hq, Hkv, mode) > ws_bytes) return hipErrorInvalidValue;
     const int G = Hq / Hkv;
     const int EB = decode_eb([&](int b) { return counts_host[b]; }, B, mode == 1 ? Hq : Hkv, G, mode, ring != nullptr);
@@ -620,8 +637,9 @@ static hipError_t sparse_decode(const uint16_t* q, const uint16_t* K, const uint
         if (mode == 0) e = launch_partial_G<0, true>(G, grid, stream, q, K, V, offs, idx, cnts, B, Hq, Hkv, EB, part, ml, nullptr, nullptr, *ring);
         else e = launch_partial_G<1, true>(G, grid, stream, q, K, V, offs, idx, cnts, B, Hq, Hkv, EB, part, ml, nullptr, nullptr, *ring);
     } else {
-        if (mode == 0) e = launch_partial_G<0>(G, grid, stream, q, K, V, offs, idx, cnts, B, Hq, Hkv, EB, part, ml);
-        else e = launch_partial_G<1>(G, grid, stream, q, K, V, offs, idx, cnts, B, Hq, Hkv, EB, part, ml);
+        const DecRing none{nullptr, nullptr, 0};
+        if (mode == 0) e = launch_partial_G<0>(G, grid, stream, q, K, V, offs, idx, cnts, B, Hq, Hkv, EB, part, ml, nullptr, nullptr, none, t0, t1);
+        else e = launch_partial_G<1>(G, grid, stream, q, K, V, offs, idx, cnts, B, Hq, Hkv, EB, part, ml, nullptr, nullptr, none, t0, t1);
     }
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(decode_merge_kernel, dim3(B * Hq), dim3(kMergeThreads), 0, stream, part, ml, cnts, B, Hq, EB, 1, out);
@@ -631,9 +649,9 @@ static hipError_t sparse_decode(const uint16_t* q, const uint16_t* K, const uint
 hipError_t launch_sparse_decode(const uint16_t* q, const uint16_t* K, const uint16_t* V, const int64_t* offsets_dev,
                                 const int64_t* offsets_host, const int32_t* idx, const int64_t* counts_dev,
                                 const int64_t* counts_host, int mode, int B, int Hq, int Hkv, float* out, void* ws,
-                                size_t ws_bytes, hipStream_t stream) {
+                                size_t ws_bytes, hipStream_t stream, hipEvent_t gather_start, hipEvent_t gather_stop) {
     return sparse_decode(q, K, V, nullptr, offsets_dev, offsets_host, idx, counts_dev, counts_host, mode, B, Hq, Hkv,
-                         out, ws, ws_bytes, stream);
+                         out, ws, ws_bytes, stream, gather_start, gather_stop);
 }
 
 hipError_t launch_union_decode(const uint16_t* q, const uint16_t* K, const uint16_t* V, const int64_t* offsets_dev,

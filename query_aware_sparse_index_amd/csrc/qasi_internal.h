@@ -104,10 +104,12 @@ struct DecRing {
     int64_t N;
 };
 size_t decode_workspace(const int64_t* offsets_host, const int64_t* counts_host, int B, int Hq, int Hkv, int mode);
+// gather_start / gather_stop (nullable): events recorded at the gather kernel's dispatch start and end
 hipError_t launch_sparse_decode(const uint16_t* q, const uint16_t* K, const uint16_t* V, const int64_t* offsets_dev,
                                 const int64_t* offsets_host, const int32_t* idx, const int64_t* counts_dev,
                                 const int64_t* counts_host, int mode,
-                                int B, int Hq, int Hkv, float* out, void* ws, size_t ws_bytes, hipStream_t stream);
+                                int B, int Hq, int Hkv, float* out, void* ws, size_t ws_bytes, hipStream_t stream,
+                                hipEvent_t gather_start = nullptr, hipEvent_t gather_stop = nullptr);
 // ts_sparse_decode with its partials in the library's static device scratch (no workspace);
 // hipErrorInvalidValue when the call needs more than kNoAllocScratchBytes.
 constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;

@@ -93,6 +93,9 @@ int main(void) {
     EXPECT(ts_tiered_decode(F, F, F, NULL, F, 64, F, o1, F, F, c100, 0, 1, 8, 2, F, F, (size_t)1 << 40, NULL), -1);
     EXPECT(ts_tiered_decode(F, F, F, F, F, 64, F, o1, NULL, NULL, NULL, 3, 1, 8, 2, F, F, 16, NULL), -3);
     EXPECT(ts_host_device_pointer(NULL, NULL), -1);
+    float gus = 0.f;
+    EXPECT(ts_sparse_decode_timed(F, F, F, F, o1, F, F, c100, 0, 1, 8, 2, F, F, 16, NULL, &gus), -3);
+    EXPECT(ts_sparse_decode_timed(F, F, F, F, o1, F, F, c100, 0, 1, 8, 2, F, F, (size_t)1 << 40, NULL, NULL), -1);
     EXPECT(ts_score_select(F, F, F, M, F, o1, 1, 8, 2, &ok, F, F, F, NULL, NULL, F, ssel, NULL), -1);
     EXPECT(ts_score_select(F, F, F, NULL, F, o1, 1, 8, 2, &ok, F, F, F, NULL, NULL, F, ssel - 1, NULL), -3);
     EXPECT(ts_score_select(F, F, F, NULL, F, o1, 1, 12, 8, &ok, F, F, F, NULL, NULL, F, ssel, NULL), -2);

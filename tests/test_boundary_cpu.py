@@ -22,7 +22,7 @@ def header_functions():
 def test_exports_match_header():
     lib = _lib.load()
     names = header_functions()
-    assert len(names) == 27, names
+    assert len(names) == 28, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.SIGNATURES)
@@ -256,3 +256,20 @@ def test_tiered_decode_validation():
     d = ctypes.c_void_p()
     assert L.ts_host_device_pointer(None, ctypes.byref(d)) == -1
     assert L.ts_host_device_pointer(FAKE, None) == -1
+
+
+def test_sparse_decode_timed_validation():
+    """ts_sparse_decode_timed validates like ts_sparse_decode, and needs somewhere to put the time."""
+    L = _lib.load()
+    o = _offs([0, 1000])
+    c = (ctypes.c_int64 * 1)(200)
+    t = ctypes.c_float()
+
+    def call(gus=ctypes.byref(t), mode=0, ws_bytes=1 << 40, K=FAKE, cnt=c):
+        return L.ts_sparse_decode_timed(FAKE, K, FAKE, FAKE, o, FAKE, FAKE, cnt, mode, 1, 8, 2, FAKE, FAKE, ws_bytes,
+                                        None, gus)
+    assert call(gus=None) == -1
+    assert call(mode=2) == -1
+    assert call(K=MIS) == -1
+    assert call(cnt=(ctypes.c_int64 * 1)(1001)) == -1
+    assert call(ws_bytes=16) == -3
