@@ -147,11 +147,15 @@ __device__ __forceinline__ void rows_tsum(const float (&v)[NA], float (&o)[NA / 
 // of a KV group's per-head lists (G * count slots per (sequence, KV head), padded with -1) with a
 // per-entry mask of the heads that selected the token: each gathered row is read once for the
 // group and a head's score of an entry it did not select is -inf.
-// Blocks per CU to keep: 4 (16 waves) for the shared-list modes with G <= 4, whose registers fit
-// in 128 (512 / 4) per lane with one sub-batch in flight per wave; no bound otherwise.  Against
-// 3 blocks with two sub-batches in flight per wave: the dense 128K decode 110 -> 102 us, the
-// decode of a 16-sequence ragged batch 112 -> 107 us, the 128K vote decode 37.2 -> 36.7 us.
-__host__ __device__ constexpr int dec_min_blocks(int G, int mode) { return (mode != 1 && G <= 4) ? 4 : 1; }
+// Blocks per CU to keep: 4 (16 waves) for the vote and dense modes with G <= 4, whose registers
+// fit in 128 (512 / 4) per lane with one sub-batch in flight per wave; 3 for the union mode with
+// G <= 4, which spills at 128 (its head masks); no bound otherwise.  Against 3 blocks with two
+// sub-batches in flight per wave: the dense 128K decode 110 -> 102 us, the decode of a
+// 16-sequence ragged batch 112 -> 107 us, the 128K vote decode 37.2 -> 36.7 us; the union decode
+// at 128K / 20 % 80.1 us with 4 blocks (7 VGPRs spilled) against 73.4 us with 3.
+__host__ __device__ constexpr int dec_min_blocks(int G, int mode) {
+    return (mode != 1 && G <= 4) ? (mode == 3 ? 3 : 4) : 1;
+}
 
 // RING: positions >= n_b - N are read from slot t mod N of the sequence's ring (`ring`), the older
 // ones from K / V (a tiered cache: the newest tokens in a device ring, the rest possibly in host
