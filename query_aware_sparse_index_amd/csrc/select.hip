@@ -1057,15 +1057,23 @@ __global__ __launch_bounds__(kPhScanThreads) void ph_scan_kernel(I64Arg offsets,
     }
 }
 
+// ph_compact_kernel: one wave per (64-token chunk, group of kPhCompactHeads heads), the groups of
+// a chunk in adjacent waves; more waves than chunks keep enough loads in flight to cover their
+// latency (at 128K tokens and 32 heads, 8192 waves instead of 2048).
+constexpr int kPhCompactHeads = 8;
 __global__ __launch_bounds__(kPhWaves * 64) void ph_compact_kernel(const float* __restrict__ scores,
                                                                  I64Arg offsets, int B, int Hq,
                                                                  DevCfg cfg, int64_t S, const int64_t* __restrict__ state,
                                                                  int64_t nitems, const uint32_t* __restrict__ pre,
                                                                  int32_t* __restrict__ idx_out,
                                                                  int64_t* __restrict__ count_out) {
+    constexpr int HPW = kPhCompactHeads;
     const int lane = threadIdx.x & 63;
-    const int64_t item = (int64_t)blockIdx.x * kPhWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (item >= nitems) return;
+    const int HG = (Hq + HPW - 1) / HPW;
+    const int64_t wv = (int64_t)blockIdx.x * kPhWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (wv >= nitems * HG) return;
+    const int64_t item = wv / HG;
+    const int h0 = (int)(wv % HG) * HPW;
     int b;
     int64_t first, nch, t0, len;
     if (!find_chunk<kPhChunk>(offsets, B, item, b, first, nch, t0, len)) return;
@@ -1073,19 +1081,19 @@ __global__ __launch_bounds__(kPhWaves * 64) void ph_compact_kernel(const float* 
     const int64_t K = budget_k(n, cfg.bnum, cfg.bden, cfg.sink, cfg.local);
     const int64_t kpre = kpre_of(offsets, b, cfg);
     const int64_t fb = forced_before(t0, n, cfg.sink, cfg.local);
-    if (item == first && lane == 0) count_out[b] = K;
+    if (item == first && h0 == 0 && lane == 0) count_out[b] = K;
     const int64_t t = t0 + lane;
     const uint64_t lt = (1ull << lane) - 1ull;
     const bool inr = lane < len;
     const bool frc = inr && is_forced(t, n, cfg.sink, cfg.local);
     const float* col = scores + off + (inr ? t : t0);
-    for (int h0 = 0; h0 < Hq; h0 += kPhHeads) {
-        float sv[kPhHeads];
+    {
+        float sv[HPW];
 #pragma unroll
-        for (int u = 0; u < kPhHeads; ++u) sv[u] = col[(int64_t)(h0 + u < Hq ? h0 + u : Hq - 1) * S];
+        for (int u = 0; u < HPW; ++u) sv[u] = col[(int64_t)(h0 + u < Hq ? h0 + u : Hq - 1) * S];
         // lane u: the parameters of head h0 + u in this chunk (the list offset of the chunk's first
         // selected token, the equal keys before the chunk and the equal keys to take in all)
-        const int hl = h0 + (lane < kPhHeads ? lane : 0) < Hq ? h0 + (lane < kPhHeads ? lane : 0) : Hq - 1;
+        const int hl = h0 + (lane < HPW ? lane : 0) < Hq ? h0 + (lane < HPW ? lane : 0) : Hq - 1;
         const int64_t* st = state + ((int64_t)b * Hq + hl) * 8;
         const int64_t flag = st[kStFlag];
         const uint2 gq = reinterpret_cast<const uint2*>(pre)[(size_t)hl * nitems + item];
@@ -1100,7 +1108,7 @@ __global__ __launch_bounds__(kPhWaves * 64) void ph_compact_kernel(const float* 
         const int lflag = (int)flag, lkey = (int)(uint32_t)st[kStKey];
         const int lneq = (int)need_eq, leqb = (int)eqb, lbase = (int)base;
 #pragma unroll
-        for (int u = 0; u < kPhHeads; ++u) {
+        for (int u = 0; u < HPW; ++u) {
             if (h0 + u >= Hq) break;
             const int hflag = lane_pick(lflag, u);
             const uint32_t ks = (uint32_t)lane_pick(lkey, u);
@@ -1855,13 +1863,15 @@ static hipError_t launch_select_tail(const SelectLayout& L, const float* scores,
                            B, d, L.keys, L.hist, idx_out, count_out);
     } else {
         const dim3 phg((unsigned)((L.ph_items + kPhWaves - 1) / kPhWaves));
+        const int64_t cw = L.ph_items * ((Hq + kPhCompactHeads - 1) / kPhCompactHeads);
+        const dim3 phcg((unsigned)((cw + kPhWaves - 1) / kPhWaves));
         if (!prefixed) {
             hipLaunchKernelGGL(ph_count_kernel, phg, dim3(kPhWaves * 64), 0, stream, scores, offs,
                                B, Hq, d, S, L.state, L.ph_items, L.phcnt);
             hipLaunchKernelGGL(ph_scan_kernel, dim3((unsigned)(B * Hq)), dim3(kPhScanThreads), 0, stream, offs, B,
                                Hq, L.ph_items, L.phcnt);
         }
-        hipLaunchKernelGGL(ph_compact_kernel, phg, dim3(kPhWaves * 64), 0, stream, scores,
+        hipLaunchKernelGGL(ph_compact_kernel, phcg, dim3(kPhWaves * 64), 0, stream, scores,
                            offs, B, Hq, d, S, L.state, L.ph_items, L.phcnt, idx_out, count_out);
     }
     return hipGetLastError();
@@ -2057,7 +2067,8 @@ hipError_t launch_snap_topc(const float* imp, int64_t n, int rows, int64_t c, fl
                        L.state, nullptr);
     // the per-head compaction: the rows are the heads of one sequence with no forced tokens, so the
     // list of row r is idx_out[r * ce ...]
-    hipLaunchKernelGGL(ph_compact_kernel, dim3((unsigned)((L.ntiles + kPhWaves - 1) / kPhWaves)), dim3(kPhWaves * 64), 0,
+    const int64_t cw = L.ntiles * ((rows + kPhCompactHeads - 1) / kPhCompactHeads);
+    hipLaunchKernelGGL(ph_compact_kernel, dim3((unsigned)((cw + kPhWaves - 1) / kPhWaves)), dim3(kPhWaves * 64), 0,
                        stream, pooled, offs, 1, rows, d, ps, L.state, L.ntiles, reinterpret_cast<const uint32_t*>(L.pre),
                        idx_out, L.count);
     return hipGetLastError();
