@@ -1057,17 +1057,18 @@ __global__ __launch_bounds__(kPhScanThreads) void ph_scan_kernel(I64Arg offsets,
     }
 }
 
-// ph_compact_kernel: one wave per (64-token chunk, group of kPhCompactHeads heads), the groups of
-// a chunk in adjacent waves; more waves than chunks keep enough loads in flight to cover their
-// latency (at 128K tokens and 32 heads, 8192 waves instead of 2048).
-constexpr int kPhCompactHeads = 8;
+// ph_compact_kernel: one wave per (64-token chunk, group of HPW heads), the groups of a chunk in
+// adjacent waves.  One sequence: 8 heads per wave, so that more waves than chunks keep enough loads
+// in flight (at 128K tokens and 32 heads 8192 waves: 11.9 us against 13.2 us with 32 heads per
+// wave).  A batch: 32 heads per wave, since every wave repeats the sequence lookup and the list
+// prefix of its chunk (16 sequences of 16K-64K tokens: 47.8 us against 64.1 us with 8).
+template <int HPW>
 __global__ __launch_bounds__(kPhWaves * 64) void ph_compact_kernel(const float* __restrict__ scores,
                                                                  I64Arg offsets, int B, int Hq,
                                                                  DevCfg cfg, int64_t S, const int64_t* __restrict__ state,
                                                                  int64_t nitems, const uint32_t* __restrict__ pre,
                                                                  int32_t* __restrict__ idx_out,
                                                                  int64_t* __restrict__ count_out) {
-    constexpr int HPW = kPhCompactHeads;
     const int lane = threadIdx.x & 63;
     const int HG = (Hq + HPW - 1) / HPW;
     const int64_t wv = (int64_t)blockIdx.x * kPhWaves + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1863,7 +1864,8 @@ static hipError_t launch_select_tail(const SelectLayout& L, const float* scores,
                            B, d, L.keys, L.hist, idx_out, count_out);
     } else {
         const dim3 phg((unsigned)((L.ph_items + kPhWaves - 1) / kPhWaves));
-        const int64_t cw = L.ph_items * ((Hq + kPhCompactHeads - 1) / kPhCompactHeads);
+        const int hpw = B == 1 ? 8 : 32;
+        const int64_t cw = L.ph_items * ((Hq + hpw - 1) / hpw);
         const dim3 phcg((unsigned)((cw + kPhWaves - 1) / kPhWaves));
         if (!prefixed) {
             hipLaunchKernelGGL(ph_count_kernel, phg, dim3(kPhWaves * 64), 0, stream, scores, offs,
@@ -1871,8 +1873,12 @@ static hipError_t launch_select_tail(const SelectLayout& L, const float* scores,
             hipLaunchKernelGGL(ph_scan_kernel, dim3((unsigned)(B * Hq)), dim3(kPhScanThreads), 0, stream, offs, B,
                                Hq, L.ph_items, L.phcnt);
         }
-        hipLaunchKernelGGL(ph_compact_kernel, phcg, dim3(kPhWaves * 64), 0, stream, scores,
-                           offs, B, Hq, d, S, L.state, L.ph_items, L.phcnt, idx_out, count_out);
+        if (hpw == 8)
+            hipLaunchKernelGGL(ph_compact_kernel<8>, phcg, dim3(kPhWaves * 64), 0, stream, scores,
+                               offs, B, Hq, d, S, L.state, L.ph_items, L.phcnt, idx_out, count_out);
+        else
+            hipLaunchKernelGGL(ph_compact_kernel<32>, phcg, dim3(kPhWaves * 64), 0, stream, scores,
+                               offs, B, Hq, d, S, L.state, L.ph_items, L.phcnt, idx_out, count_out);
     }
     return hipGetLastError();
 }
@@ -2067,8 +2073,8 @@ hipError_t launch_snap_topc(const float* imp, int64_t n, int rows, int64_t c, fl
                        L.state, nullptr);
     // the per-head compaction: the rows are the heads of one sequence with no forced tokens, so the
     // list of row r is idx_out[r * ce ...]
-    const int64_t cw = L.ntiles * ((rows + kPhCompactHeads - 1) / kPhCompactHeads);
-    hipLaunchKernelGGL(ph_compact_kernel, dim3((unsigned)((cw + kPhWaves - 1) / kPhWaves)), dim3(kPhWaves * 64), 0,
+    const int64_t cw = L.ntiles * ((rows + 7) / 8);
+    hipLaunchKernelGGL(ph_compact_kernel<8>, dim3((unsigned)((cw + kPhWaves - 1) / kPhWaves)), dim3(kPhWaves * 64), 0,
                        stream, pooled, offs, 1, rows, d, ps, L.state, L.ntiles, reinterpret_cast<const uint32_t*>(L.pre),
                        idx_out, L.count);
     return hipGetLastError();
