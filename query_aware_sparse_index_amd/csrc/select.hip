@@ -855,7 +855,8 @@ __global__ __launch_bounds__(kChunk) void vote_kernel(const float* __restrict__ 
 // key whose suffix count reaches need; none when need == 0), gt = #keys above v* and
 // need_eq = need - gt.  The chunk's first selected token then has output rank
 //   forced_before(first token of c) + #keys above v* before c + min(eqb, need_eq),
-// eqb = #keys equal to v* before c, and each token of the chunk is placed by two block scans:
+// eqb = #keys equal to v* before c.  One wave finds v*, gt and the counts before c from suffix
+// sums over the key bins (two bins per lane, from the top key down); one block scan then places
 // every forced token, every non-forced token above v* and the first need_eq - eqb tokens equal
 // to v* in position order, written ascending.
 __global__ __launch_bounds__(kChunk) void compact_vote_kernel(I64Arg offsets, int B,
@@ -868,7 +869,7 @@ __global__ __launch_bounds__(kChunk) void compact_vote_kernel(I64Arg offsets, in
     __shared__ uint32_t part[NG][kVoteBins][2];
     __shared__ uint32_t tot[kVoteBins], bef[kVoteBins];
     __shared__ int tmp[kChunk / 64];
-    __shared__ int64_t sh[2];
+    __shared__ int sh[4];
     int b;
     int64_t first, nch, t0, len;
     if (!find_chunk(offsets, B, blockIdx.x, b, first, nch, t0, len)) return;
@@ -912,36 +913,60 @@ __global__ __launch_bounds__(kChunk) void compact_vote_kernel(I64Arg offsets, in
     __syncthreads();
     const int64_t K = budget_k(n, cfg.bnum, cfg.bden, cfg.sink, cfg.local);
     const int64_t need = K - forced_before(n, n, cfg.sink, cfg.local);
-    {
-        // suffix counts over the keys (thread t holds key kVoteBins - 1 - t)
-        const int v = kVoteBins - 1 - t;
-        const int cv = t < kVoteBins ? (int)tot[v] : 0;
-        int all;
-        const int incl = block_inclusive_scan<kChunk>(cv, tmp, &all);
-        if (t == 0) { sh[0] = kVoteBins; sh[1] = 0; }
-        __syncthreads();
-        if (need > 0 && t < kVoteBins && incl >= need && incl - cv < need) { sh[0] = v; sh[1] = incl - cv; }
-        __syncthreads();
+    static_assert(kVoteBins <= 128, "two key bins per lane of one wave");
+    if (t < 64) {
+        // lane l holds bins b0 = top - 2l and b1 = b0 - 1; inclusive sums over the lanes give the
+        // suffix counts of the keys (sequence: x, chunks before c: y) above and at each bin
+        const int b0 = kVoteBins - 1 - 2 * t, b1 = b0 - 1;
+        const int c0 = b0 >= 0 ? (int)tot[b0] : 0, c1 = b1 >= 0 ? (int)tot[b1] : 0;
+        const int e0 = b0 >= 0 ? (int)bef[b0] : 0, e1 = b1 >= 0 ? (int)bef[b1] : 0;
+        int x = c0 + c1, y = e0 + e1;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int xu = __shfl_up(x, o, 64), yu = __shfl_up(y, o, 64);
+            if (t >= o) {
+                x += xu;
+                y += yu;
+            }
+        }
+        const int xa = x - c0 - c1, ya = y - e0 - e1;        // the keys above bin b0
+        // v*: the bin whose suffix count first reaches need (one lane owns it when need > 0)
+        const bool own0 = need > 0 && b0 >= 0 && xa < need && need <= xa + c0;
+        const bool own1 = need > 0 && b1 >= 0 && xa + c0 < need && need <= xa + c0 + c1;
+        const uint64_t m = __ballot(own0 || own1);
+        int vs = kVoteBins, gt = 0, gtb = 0, eqb = 0;
+        if (m) {
+            const int L = __builtin_ctzll(m);
+            vs = __builtin_amdgcn_readlane(own0 ? b0 : b1, L);
+            gt = __builtin_amdgcn_readlane(own0 ? xa : xa + c0, L);
+            gtb = __builtin_amdgcn_readlane(own0 ? ya : ya + e0, L);
+            eqb = __builtin_amdgcn_readlane(own0 ? e0 : e1, L);
+        }
+        if (t == 0) {
+            sh[0] = vs;
+            sh[1] = gt;
+            sh[2] = gtb;
+            sh[3] = eqb;
+        }
     }
-    const int vs = (int)sh[0];
+    __syncthreads();
+    const int vs = sh[0];
     const int64_t need_eq = need - sh[1];
-    // keys above v* in the chunks before c
-    int gtb;
-    block_inclusive_scan<kChunk>((t < kVoteBins && t > vs) ? (int)bef[t] : 0, tmp, &gtb);
-    const int64_t eqb = vs < kVoteBins ? bef[vs] : 0;
+    const int64_t gtb = sh[2], eqb = sh[3];
     const int64_t base = forced_before(t0, n, cfg.sink, cfg.local) + gtb + (eqb < need_eq ? eqb : need_eq);
     if (c == 0 && t == 0) count_out[b] = K;
-    const int eqf = (t < len && kk != 255 && kk == vs) ? 1 : 0;
-    int tot_eq;
-    const int eq_rank = block_inclusive_scan<kChunk>(eqf, tmp, &tot_eq) - eqf;
-    int sel = 0;
-    if (t < len) {
-        if (kk == 255) sel = 1;
-        else if (vs < kVoteBins && kk > vs) sel = 1;
-        else if (eqf) sel = (eqb + eq_rank < need_eq) ? 1 : 0;
-    }
-    int tot_sel;
-    const int64_t p = base + block_inclusive_scan<kChunk>(sel, tmp, &tot_sel) - sel;
+    // one scan: the low 16 bits count the tokens taken for sure (forced, or above v*), the high 16
+    // bits the tokens equal to v*, of which the chunk takes the first need_eq - eqb
+    const bool in = t < len;
+    const int sure = (in && (kk == 255 || (vs < kVoteBins && kk > vs))) ? 1 : 0;
+    const int eqf = (in && kk != 255 && kk == vs) ? 1 : 0;
+    const int packed = sure | (eqf << 16);
+    int tot_packed;
+    const int exc = block_inclusive_scan<kChunk>(packed, tmp, &tot_packed) - packed;
+    const int64_t quota = need_eq - eqb > 0 ? need_eq - eqb : 0;
+    const int64_t eq_before = exc >> 16;
+    const bool sel = sure || (eqf && eq_before < quota);
+    const int64_t p = base + (exc & 0xffff) + (eq_before < quota ? eq_before : quota);
     const int64_t kpre = kpre_of(offsets, b, cfg);
     if (sel && p < K) idx_out[kpre + p] = (int32_t)(t0 + t);
 }
