@@ -1954,9 +1954,9 @@ hipError_t launch_score_select(const uint16_t* q, const float* P, uint16_t* k_in
 // [SK] "アルゴリズム": the top min(c, n) positions of each KV head's pooled importance, in
 // ascending position order; ties at the threshold go to the lower positions.  The rows are few
 // (one per KV head) and long, so instead of the general selection:
-//   snap_prep_kernel:          per row, a key bracket around the threshold from 1024 sampled
+//   snap_prep_kernel:          per row, a key bracket around the threshold from 4096 sampled
 //                              pooled values (rows of more than kCap keys), as prep_kernel does
-//                              for index scores;
+//                              for index scores from 1024;
 //   snap_pool_classify_kernel: pooled[j] = ((imp[j-1] + imp[j]) + imp[j+1]) / 3 (zero outside
 //                              [0, n)), written once, and each 64-key tile classified against the
 //                              bracket in the score kernel's record layout;
@@ -1984,6 +1984,10 @@ __device__ __forceinline__ float pooled_at(const float* row, int64_t n, int64_t 
     return ((a + row[j]) + c) / 3.0f;
 }
 
+constexpr int kSnapSample = 4096;   // sampled pooled values per SnapKV row
+constexpr int kSnapDelta = 64;      // bracket half-width in sample ranks
+static_assert(kSnapSample % kColThreads == 0 && kSnapSample / kRunLen * kRunLen <= kCap,
+              "whole sample passes; a row of more than kCap keys holds every run");
 __global__ __launch_bounds__(kPrepThreads) void snap_prep_kernel(const float* __restrict__ imp, int64_t n, DevCfg cfg,
                                                                 int64_t* __restrict__ state) {
     constexpr int NW = kPrepThreads / 64;
@@ -1996,13 +2000,17 @@ __global__ __launch_bounds__(kPrepThreads) void snap_prep_kernel(const float* __
     const int64_t m = oi.end - oi.beg;
     uint32_t klo = 1u, khi = 0u;                     // no bracket: the empty one (lo > hi)
     if (oi.flag == kFlagActive && m > kCap) {
-        constexpr int kPrepRuns = kPrepSample / kRunLen;
+        // a SnapKV call has few rows (one per KV head), so each row affords 4 times the decode's
+        // sample: the bracket (+-64 of 4096 sample ranks, about 6 standard deviations at a 3 %
+        // top-c) holds about a third as many keys for the order statistic (at 131072 keys and
+        // c = 4096: its kernel 23.3 -> 19.2 us, this one 6.2 -> 8.0 us)
+        constexpr int NS = kSnapSample, kSnapRuns = NS / kRunLen;
         const float* row = imp + (int64_t)g * n;
-        float v[kPrepSample / kColThreads];
+        float v[NS / kColThreads];
 #pragma unroll
-        for (int u = 0; u < kPrepSample / kColThreads; ++u)
-            v[u] = pooled_at(row, n, oi.beg + sample_pos(t + u * kColThreads, m, g, kPrepRuns));
-        bracket_of_sample<kPrepSample, kPrepDelta, true>(v, oi, hist, wmin, wmax, tmp, sb, klo, khi);
+        for (int u = 0; u < NS / kColThreads; ++u)
+            v[u] = pooled_at(row, n, oi.beg + sample_pos(t + u * kColThreads, m, g, kSnapRuns));
+        bracket_of_sample<NS, kSnapDelta, true>(v, oi, hist, wmin, wmax, tmp, sb, klo, khi);
     }
     if (t == 0) {
         int64_t* st = state + (int64_t)g * 8;
