@@ -100,15 +100,25 @@ __global__ __launch_bounds__(kSnapThreads) void snap_pass_kernel(const uint16_t*
 #pragma unroll
             for (int i = 0; i < 4; ++i) colsum[kt][i] = 0.f;
 
-        // row tiles, unrolled by a divisor of RT
-        constexpr int U2 = (RT % 4 == 0 && RT > 4) ? 4 : ((RT % 2 == 0) ? 2 : 1);
-#pragma unroll U2
-        for (int c = 0; c < RT; ++c) {
-            const int r = c * 16 + lr;
-            bf16x8_t bq[4];
+        // (row r = 16 c + lr, so r & 15 = lr: the LDS addresses are a per-lane base plus a
+        // constant offset per tile)
+        // The per-lane bases pass through an empty register constraint once per key block: the
+        // reads of the fully unrolled row-tile loop are then not hoisted out of the key-block loop
+        // (they do not change across key blocks), which would pin all 16 tiles' fragments.
+        int qa[4];
 #pragma unroll
-            for (int s = 0; s < 4; ++s) bq[s] = as_bf16x8(sQ[r * 16 + ((s * 4 + lg) ^ (r & 15))]);
-            f32x4_t acc[kSnapKTW];
+        for (int s = 0; s < 4; ++s) {
+            qa[s] = lr * 16 + ((s * 4 + lg) ^ lr);
+            asm volatile("" : "+v"(qa[s]));
+        }
+        int la = lr;
+        asm volatile("" : "+v"(la));
+        auto tile_b = [&](int c, bf16x8_t (&bq)[4]) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) bq[s] = as_bf16x8(sQ[c * 256 + qa[s]]);
+        };
+        // the MFMAs of a row tile: 4 key tiles x 4 dim slices
+        auto tile_mma = [&](const bf16x8_t (&bq)[4], f32x4_t (&acc)[kSnapKTW]) {
 #pragma unroll
             for (int kt = 0; kt < kSnapKTW; ++kt) acc[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -116,6 +126,10 @@ __global__ __launch_bounds__(kSnapThreads) void snap_pass_kernel(const uint16_t*
 #pragma unroll
                 for (int kt = 0; kt < kSnapKTW; ++kt)
                     acc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[kt][s], bq[s], acc[kt], 0, 0, 0);
+        };
+        // the vector work on row tile c's scores; pass 1 folds them into the running (max, sum)
+        // ml of the lane's row and returns it
+        auto tile_epi = [&](int c, f32x4_t (&acc)[kSnapKTW], float2 ml) {
             if (MASK) {
 #pragma unroll
                 for (int kt = 0; kt < kSnapKTW; ++kt)
@@ -130,7 +144,6 @@ __global__ __launch_bounds__(kSnapThreads) void snap_pass_kernel(const uint16_t*
                 for (int kt = 0; kt < kSnapKTW; ++kt)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) mx = fmaxf(mx, acc[kt][i]);
-                float2 ml = mlst[(wid * RT + c) * 64 + lane];
                 const float mn = fmaxf(ml.x, mx * kSnapScale);
                 // while every score seen is -inf, subtract 0 so that the terms are 0, not NaN
                 const float ms = (mn == -INFINITY) ? 0.f : mn;
@@ -141,13 +154,70 @@ __global__ __launch_bounds__(kSnapThreads) void snap_pass_kernel(const uint16_t*
                     for (int i = 0; i < 4; ++i) e += fast_exp2(fmaf(acc[kt][i], kSnapScale, -ms));
                 ml.y = ml.y * fast_exp2(ml.x - ms) + e;
                 ml.x = mn;
-                mlst[(wid * RT + c) * 64 + lane] = ml;
             } else {
-                const float lr_c = sL[r];
+                const float lr_c = sL[c * 16 + la];
 #pragma unroll
                 for (int kt = 0; kt < kSnapKTW; ++kt)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) colsum[kt][i] += fast_exp2(fmaf(acc[kt][i], kSnapScale, -lr_c));
+            }
+            return ml;
+        };
+        // Software pipeline over the row tiles, one scheduling region per tile c: the LDS reads
+        // of tile c + 1's B fragments and tile c's running (max, sum) or LSE, tile c + 1's MFMAs,
+        // and tile c's vector work, with one MFMA issued between every few VALU instructions so
+        // that the matrix core and the vector unit of a SIMD work at the same time within one
+        // wave.
+        auto interleave = [&]() {
+            __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);   // LDS reads
+#pragma unroll
+            for (int k = 0; k < 4 * kSnapKTW; ++k) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x002, (PASS == 1) ? 4 : 3, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        f32x4_t acc[2][kSnapKTW];
+        // one region: tile c + 1's MFMAs (when it exists) into acc[nx], tile c's vector work on
+        // acc[cu]
+        auto region = [&](int c, bool next, f32x4_t (&ac)[kSnapKTW], f32x4_t (&an)[kSnapKTW]) {
+            if (next) {
+                bf16x8_t bq[4];
+                tile_b(c + 1, bq);
+                tile_mma(bq, an);
+            }
+            if constexpr (PASS == 1) {
+                float2* mp = &mlst[(wid * RT + c) * 64 + lane];
+                *mp = tile_epi(c, ac, *mp);
+            } else {
+                tile_epi(c, ac, float2{0.f, 0.f});
+            }
+            interleave();
+        };
+        {
+            bf16x8_t bq[4];
+            tile_b(0, bq);
+            tile_mma(bq, acc[0]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (PASS == 1) {
+#pragma unroll
+            for (int c = 0; c < RT; ++c) region(c, c + 1 < RT, acc[c & 1], acc[(c & 1) ^ 1]);
+        } else {
+            // pass 2 holds 16 more registers (the column sums): with a fully unrolled tile loop
+            // the compiler moves the MFMAs away from their vector work and spills, so the tiles
+            // run as a loop over pairs with the last one or two peeled
+            int c = 0;
+#pragma unroll 1
+            for (; c + 2 < RT; c += 2) {
+                region(c, true, acc[0], acc[1]);
+                region(c + 1, true, acc[1], acc[0]);
+            }
+            if (RT - c == 2) {
+                region(c, true, acc[0], acc[1]);
+                region(c + 1, false, acc[1], acc[0]);
+            } else {
+                region(c, false, acc[0], acc[1]);
             }
         }
 
