@@ -172,8 +172,9 @@ def _boundary_diff(sel_gpu, sel_ref, key_ref, forced, tol):
 
 
 def check_endtoend(st: Step):
-    """The spec rule: the GPU lists against the oracle run end to end on its own fp64
-    scores (from the same index rows, which the staged check shows to be bit-exact).
+    """End-to-end selection parity: the GPU lists against the oracle run end to end on its own
+    fp64 scores (from the same index rows, which the staged check shows to be bit-exact); lists
+    may differ only in tokens whose scores lie within 1e-5 relative of the selection boundary.
     Vote mode: every GPU vote is within #near(t) of the oracle's, where a head is near at t when
     |S_h(t) - theta_h| <= 1e-5 |theta_h| (+ the fp32 score bound as a floor), and every token in
     which the lists differ is a near token or carries the oracle's boundary key.

@@ -1,4 +1,5 @@
-"""End-to-end selection parity (the spec rule) and the full-size budget sweep.
+"""End-to-end selection parity (swaps only within 1e-5 relative of the boundary) and the
+full-size budget sweep.
 
 The staged checks compare each stage with the oracle run on the GPU's own input to that stage.
 Here the GPU lists are also compared with the oracle run end to end on its own fp64 scores
