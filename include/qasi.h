@@ -366,6 +366,8 @@ size_t snapkv_workspace_bytes(int64_t n, int32_t w, int32_t Hq, int32_t Hkv, int
  * QK^T runs on bf16 MFMA with fp32 accumulation; softmax statistics are fp32.
  *   q_obs          device bf16 [w][Hq][128] (the last w prompt queries)
  *   K, V           device bf16 [n][Hkv][128]
+ *   n              1 .. 2^24 tokens; G*w (G = Hq/Hkv) a multiple of 16 and at most 256 (the
+ *                  MFMA row tiles of a KV head's window rows); otherwise QASI_ERR_UNSUPPORTED
  *   pool_kernel    must be 3 (odd kernels keep the length; only 3 is built)
  *   idx_out        device int32 [Hkv][ce]
  *   K_out, V_out   device bf16 [ce][Hkv][128]
