@@ -987,6 +987,10 @@ constexpr int kPhChunk = 64;   // tokens per chunk: one per lane of a wave
 constexpr int kPhWaves = 4;    // independent chunk waves per block
 
 __device__ __forceinline__ int lane_pick(int v, int u) { return __builtin_amdgcn_readlane(v, u); }
+// number of set bits of the wave mask m in the lanes below this one
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
 
 __global__ __launch_bounds__(kPhWaves * 64) void ph_count_kernel(const float* __restrict__ scores,
                                                                I64Arg offsets, int B, int Hq,
@@ -1109,7 +1113,6 @@ __global__ __launch_bounds__(kPhWaves * 64) void ph_compact_kernel(const float* 
     const int64_t fb = forced_before(t0, n, cfg.sink, cfg.local);
     if (item == first && h0 == 0 && lane == 0) count_out[b] = K;
     const int64_t t = t0 + lane;
-    const uint64_t lt = (1ull << lane) - 1ull;
     const bool inr = lane < len;
     const bool frc = inr && is_forced(t, n, cfg.sink, cfg.local);
     const float* col = scores + off + (inr ? t : t0);
@@ -1117,37 +1120,44 @@ __global__ __launch_bounds__(kPhWaves * 64) void ph_compact_kernel(const float* 
         float sv[HPW];
 #pragma unroll
         for (int u = 0; u < HPW; ++u) sv[u] = col[(int64_t)(h0 + u < Hq ? h0 + u : Hq - 1) * S];
-        // lane u: the parameters of head h0 + u in this chunk (the list offset of the chunk's first
-        // selected token, the equal keys before the chunk and the equal keys to take in all)
+        // lane u: the parameters of head h0 + u in this chunk.  A token is taken when it is forced,
+        // when its key is above ks, or when it equals ks and is among the first `quota` such
+        // tokens of the chunk; base is the list offset of the chunk's first taken token.  Take-all
+        // and take-none heads are the same rule with ks = 0 and quota = 64 (every token) or
+        // ks = ~0 and quota = 0 (forced tokens only).
         const int hl = h0 + (lane < HPW ? lane : 0) < Hq ? h0 + (lane < HPW ? lane : 0) : Hq - 1;
         const int64_t* st = state + ((int64_t)b * Hq + hl) * 8;
         const int64_t flag = st[kStFlag];
         const uint2 gq = reinterpret_cast<const uint2*>(pre)[(size_t)hl * nitems + item];
         const int64_t gtb = gq.x, eqb = gq.y;
-        int64_t base, need_eq = 0;
-        if (flag == kFlagTakeAll) base = t0;
-        else if (flag == kFlagTakeNone) base = fb;
-        else {
-            need_eq = st[kStNeed] - st[kStGt];
+        int64_t base, quota;
+        uint32_t ks;
+        if (flag == kFlagTakeAll) {
+            base = t0;
+            ks = 0u;
+            quota = kPhChunk;
+        } else if (flag == kFlagTakeNone) {
+            base = fb;
+            ks = ~0u;
+            quota = 0;
+        } else {
+            const int64_t need_eq = st[kStNeed] - st[kStGt];
             base = fb + gtb + (eqb < need_eq ? eqb : need_eq);
+            ks = (uint32_t)st[kStKey];
+            quota = need_eq - eqb;
+            quota = quota < 0 ? 0 : (quota > kPhChunk ? kPhChunk : quota);
         }
-        const int lflag = (int)flag, lkey = (int)(uint32_t)st[kStKey];
-        const int lneq = (int)need_eq, leqb = (int)eqb, lbase = (int)base;
+        const int lks = (int)ks, lquota = (int)quota, lbase = (int)base;
+        const bool cand = inr && !frc;
 #pragma unroll
         for (int u = 0; u < HPW; ++u) {
             if (h0 + u >= Hq) break;
-            const int hflag = lane_pick(lflag, u);
-            const uint32_t ks = (uint32_t)lane_pick(lkey, u);
+            const uint32_t ku = (uint32_t)lane_pick(lks, u);
             const uint32_t k = order_key(sv[u]);
-            const bool eqf = hflag == kFlagActive && inr && !frc && k == ks;
-            const int64_t eq_rank = (int64_t)lane_pick(leqb, u) + __popcll(__ballot(eqf) & lt);
-            bool sel = false;
-            if (inr) {
-                if (frc || hflag == kFlagTakeAll) sel = true;
-                else if (hflag == kFlagActive) sel = k > ks || (eqf && eq_rank < lane_pick(lneq, u));
-            }
-            const uint64_t msel = __ballot(sel);
-            const int64_t p = (int64_t)lane_pick(lbase, u) + __popcll(msel & lt);
+            const bool eqf = cand && k == ku;
+            const int erank = lanes_below(__ballot(eqf));
+            const bool sel = inr && (frc || k > ku || (eqf && erank < lane_pick(lquota, u)));
+            const int64_t p = (int64_t)lane_pick(lbase, u) + lanes_below(__ballot(sel));
             if (sel && p < K) idx_out[Hq * kpre + (int64_t)(h0 + u) * K + p] = (int32_t)t;
         }
     }
