@@ -145,17 +145,25 @@ __device__ __forceinline__ int wave_sum_i(int v) {
     return v;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave in registers (DPP, no LDS crossbar): shifts
+// by 1, 2, 4 and 8 lanes within each row of 16 (lanes shifted in from outside the row add 0),
+// then lane 15 of rows 0 and 2 is added to rows 1 and 3, and lane 31 to rows 2 and 3.
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);   // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);   // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);   // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);   // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
+    return x;
+}
+
 // Inclusive prefix sum of one int per thread over a block of NT threads (NT multiple of 64,
 // at most 1024).  `tmp` holds NT/64 ints.  Returns the inclusive value; *total the sum.
 template <int NT>
 __device__ __forceinline__ int block_inclusive_scan(int v, int* tmp, int* total) {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    int x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        int y = __shfl_up(x, o, 64);
-        if (lane >= o) x += y;
-    }
+    const int x = wave_inclusive_scan(v);
     if (lane == 63) tmp[wid] = x;
     __syncthreads();
     int base = 0, tot = 0;
@@ -176,14 +184,9 @@ template <int NT>
 __device__ __forceinline__ int block_inclusive_scan3(int a, int b, int c, int (*tmp)[NT / 64], int* ta, int* tb,
                                                      int* tc) {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    int x = c;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(x, o, 64);
-        if (lane >= o) x += y;
-        a += __shfl_xor(a, o, 64);
-        b += __shfl_xor(b, o, 64);
-    }
+    const int x = wave_inclusive_scan(c);
+    a = wave_inclusive_scan(a);   // lane 63: the wave's total
+    b = wave_inclusive_scan(b);
     if (lane == 63) {
         tmp[0][wid] = a;
         tmp[1][wid] = b;

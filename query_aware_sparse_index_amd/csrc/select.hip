@@ -920,15 +920,7 @@ __global__ __launch_bounds__(kChunk) void compact_vote_kernel(I64Arg offsets, in
         const int b0 = kVoteBins - 1 - 2 * t, b1 = b0 - 1;
         const int c0 = b0 >= 0 ? (int)tot[b0] : 0, c1 = b1 >= 0 ? (int)tot[b1] : 0;
         const int e0 = b0 >= 0 ? (int)bef[b0] : 0, e1 = b1 >= 0 ? (int)bef[b1] : 0;
-        int x = c0 + c1, y = e0 + e1;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int xu = __shfl_up(x, o, 64), yu = __shfl_up(y, o, 64);
-            if (t >= o) {
-                x += xu;
-                y += yu;
-            }
-        }
+        const int x = wave_inclusive_scan(c0 + c1), y = wave_inclusive_scan(e0 + e1);
         const int xa = x - c0 - c1, ya = y - e0 - e1;        // the keys above bin b0
         // v*: the bin whose suffix count first reaches need (one lane owns it when need > 0)
         const bool own0 = need > 0 && b0 >= 0 && xa < need && need <= xa + c0;
@@ -1057,12 +1049,8 @@ __global__ __launch_bounds__(kPhScanThreads) void ph_scan_kernel(I64Arg offsets,
         uint32_t s0 = 0, s1 = 0;
 #pragma unroll
         for (int u = 0; u < kPhScanPer; ++u) { s0 += v[u].x; s1 += v[u].y; }
-        uint32_t i0 = s0, i1 = s1;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const uint32_t y0 = __shfl_up(i0, o, 64), y1 = __shfl_up(i1, o, 64);
-            if (lane >= o) { i0 += y0; i1 += y1; }
-        }
+        // (two's-complement addition: the same bits as unsigned sums)
+        const uint32_t i0 = (uint32_t)wave_inclusive_scan((int)s0), i1 = (uint32_t)wave_inclusive_scan((int)s1);
         if (lane == 63) { wt[0][wid] = i0; wt[1][wid] = i1; }
         __syncthreads();
         uint32_t b0 = 0, b1 = 0, t0 = 0, t1 = 0;
